@@ -1,0 +1,257 @@
+"""Seeded synthetic inputs for the optimizer-step workloads.
+
+This module only draws random numbers and lays out buffers; it holds none of
+the optimizer's arithmetic.  Both the HIP path's callers (tests, bench) and
+the CPU oracle's callers take their inputs from here, so the two sides see the
+same bits.
+
+Workload shapes come from the pages:
+  * toy: the two-parameter decay experiment of the page
+    "优化器：AdamW、Muon 与分布式优化器" (section "AdamW：解耦的权重衰减");
+  * two matrices 4096x1024 and 1024x4096 drawn with torch.manual_seed(0), as in
+    that page's state-size measurement (section "优化器的显存账本");
+  * a Llama-8B-shaped parameter list, a ragged 20000-tensor list and a flat
+    ZeRO-1 shard of a 70B model over 8 data-parallel ranks (the flat shard
+    layout follows "02 · Optimizer：算法与 infra" §12.1: each rank owns one
+    contiguous slice of the flat buffer, param boundaries ignored).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+# Param starts inside a flat buffer are aligned to 64 elements, the alignment
+# the DDP buffer layout uses ("02 · Optimizer：算法与 infra" §16, param_layout).
+ALIGN_ELEMS = 64
+FILL_CHUNK = 1 << 30  # elements per in-place RNG fill (bounds temporaries)
+
+
+@dataclass
+class Workload:
+    name: str
+    numels: List[int]
+    ndims: List[int]
+    param_dtype: str = "bf16"          # "bf16" or "fp32" (fp32 params are their own master)
+    lr: float = 1e-3
+    weight_decay: float = 0.1
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    mode: int = 0                      # 0 AdamW, 1 Adam + L2
+    max_norm: float = 0.0              # <= 0: no clipping
+    loss_scale: Optional[float] = None
+    steps: int = 1
+    grad_std: List[float] = field(default_factory=list)
+    master_seed: int = 0
+    grad_seed_base: int = 1000
+    inf_step: Optional[int] = None     # 1-based call index whose grads carry one +inf
+    flat: bool = False                 # one flat shard instead of a tensor list
+
+    @property
+    def numel(self) -> int:
+        return int(sum(self.numels))
+
+    @property
+    def n_tensors(self) -> int:
+        return len(self.numels)
+
+    def group_of(self, i: int) -> int:
+        """Group 0 decays, group 1 (1-D tensors: norm gains, biases) does not."""
+        return 1 if self.ndims[i] == 1 else 0
+
+    def groups(self):
+        return [(self.lr, self.weight_decay), (self.lr, 0.0)]
+
+    def inv_scale(self) -> float:
+        return 1.0 if self.loss_scale is None else float(np.float32(1.0 / self.loss_scale))
+
+
+# --------------------------------------------------------------------------
+# workload definitions
+# --------------------------------------------------------------------------
+def toy(mode: int) -> Workload:
+    return Workload("toy_2param", [2], [1], param_dtype="fp32", lr=1e-2, weight_decay=0.1,
+                    mode=mode, steps=1000, grad_std=[0.0])
+
+
+def toy_grad(k: int) -> np.ndarray:
+    """Gradient of 1-based call k: [0.01, 10] * (-1)^(k-1)."""
+    return np.ascontiguousarray(np.array([0.01, 10.0], np.float32) * np.float32((-1.0) ** (k - 1)))
+
+
+def two_matrices() -> Workload:
+    return Workload("two_matrices_8.4M", [4096 * 1024, 1024 * 4096], [2, 2], lr=1e-3,
+                    weight_decay=0.1, max_norm=1.0, steps=10, grad_std=[1e-3, 1e-3])
+
+
+def llama8b_shapes():
+    """(name, shape) of a Llama-8B-shaped parameter list: 32 layers, hidden 4096,
+    FFN 14336, 8 KV heads of 128, vocab 128256, untied embedding/head."""
+    h, f, kv, vocab, layers = 4096, 14336, 8 * 128, 128256, 32
+    out = [("embed", (vocab, h))]
+    for l in range(layers):
+        out += [(f"l{l}.q", (h, h)), (f"l{l}.k", (kv, h)), (f"l{l}.v", (kv, h)),
+                (f"l{l}.o", (h, h)), (f"l{l}.gate", (f, h)), (f"l{l}.up", (f, h)),
+                (f"l{l}.down", (h, f)), (f"l{l}.attn_norm", (h,)), (f"l{l}.mlp_norm", (h,))]
+    out += [("final_norm", (h,)), ("lm_head", (vocab, h))]
+    return out
+
+
+def llama8b() -> Workload:
+    shapes = llama8b_shapes()
+    rng = np.random.default_rng(3)
+    sig = np.exp(rng.uniform(math.log(1e-5), math.log(1e-2), size=len(shapes)))
+    return Workload("llama8b_shaped", [int(np.prod(s)) for _, s in shapes], [len(s) for _, s in shapes],
+                    lr=1e-3, weight_decay=0.1, max_norm=1.0, steps=5, grad_std=[float(x) for x in sig])
+
+
+def ragged_sizes(n: int = 20000, max_elems: int = 4 * 2 ** 20, seed: int = 4) -> List[int]:
+    rng = np.random.default_rng(seed)
+    return [max(1, int(round(math.exp(x)))) for x in rng.uniform(0.0, math.log(max_elems), size=n)]
+
+
+def ragged(n: int = 20000, max_elems: int = 4 * 2 ** 20, steps: int = 8, inf_step: int = 3) -> Workload:
+    sizes = ragged_sizes(n, max_elems)
+    return Workload(f"ragged_{n}", sizes, [2] * n, lr=1e-3, weight_decay=0.1, max_norm=1.0,
+                    loss_scale=65536.0, steps=steps, grad_std=[1e-3] * n, inf_step=inf_step)
+
+
+def zero_shard(numel: int = 8_750_000_000) -> Workload:
+    return Workload("zero1_shard_70b_over_8", [numel], [1], lr=1e-3, weight_decay=0.1, max_norm=1.0,
+                    steps=3, grad_std=[1e-4], flat=True)
+
+
+def inf_position(w: Workload) -> tuple:
+    """(tensor index, element) of the injected +inf: the last element of the
+    highest-index tensor whose size is not a multiple of 4 (so it sits on the
+    scalar tail), else the last element of the last tensor."""
+    for i in range(w.n_tensors - 1, -1, -1):
+        if w.numels[i] % 4 != 0:
+            return i, w.numels[i] - 1
+    return w.n_tensors - 1, w.numels[-1] - 1
+
+
+# --------------------------------------------------------------------------
+# buffers
+# --------------------------------------------------------------------------
+def offsets(numels: List[int], align: int = ALIGN_ELEMS):
+    """Start offset of every tensor inside one flat buffer, each aligned to
+    ``align`` elements; returns (offsets, total length)."""
+    offs, cur = [], 0
+    for n in numels:
+        offs.append(cur)
+        cur += (n + align - 1) // align * align
+    return offs, max(cur, 1)
+
+
+def fill_normal_(buf: torch.Tensor, seed: int, std: float = 1.0) -> None:
+    """In-place N(0, std) fill of a flat tensor in FILL_CHUNK slices from one
+    seeded generator on buf's device."""
+    gen = torch.Generator(device=buf.device)
+    gen.manual_seed(seed)
+    n = buf.numel()
+    for a in range(0, n, FILL_CHUNK):
+        b = min(n, a + FILL_CHUNK)
+        buf[a:b].normal_(0.0, 1.0, generator=gen)
+        if std != 1.0:
+            buf[a:b].mul_(std)
+
+
+@dataclass
+class Buffers:
+    """Flat device buffers for one workload, and the per-tensor views."""
+    workload: Workload
+    offs: List[int]
+    total: int
+    master: torch.Tensor
+    grad: torch.Tensor
+    exp_avg: torch.Tensor
+    exp_avg_sq: torch.Tensor
+    param: torch.Tensor        # bf16 buffer, or the master itself for fp32 params
+
+    def view(self, buf: torch.Tensor, i: int) -> torch.Tensor:
+        o = self.offs[i]
+        return buf[o:o + self.workload.numels[i]]
+
+    def lists(self):
+        w = self.workload
+        return ([self.view(self.param, i) for i in range(w.n_tensors)],
+                [self.view(self.master, i) for i in range(w.n_tensors)],
+                [self.view(self.grad, i) for i in range(w.n_tensors)],
+                [self.view(self.exp_avg, i) for i in range(w.n_tensors)],
+                [self.view(self.exp_avg_sq, i) for i in range(w.n_tensors)])
+
+
+def allocate(w: Workload, device) -> Buffers:
+    """Allocate flat master/grad/m/v (+bf16 param) buffers and initialise the
+    state: master N(0,1) from ``master_seed``, m = v = 0, param = bf16 cast of
+    the master (torch's cast; the param's initial value is an input)."""
+    if w.flat:
+        offs, total = [0], w.numel
+    else:
+        offs, total = offsets(w.numels)
+    f32 = dict(dtype=torch.float32, device=device)
+    master = torch.empty(total, **f32)
+    if w.name.startswith("toy"):
+        master.fill_(1.0)
+    elif w.name.startswith("two_matrices"):
+        m = two_matrix_masters()
+        master[offs[0]:offs[0] + m[0].numel()].copy_(m[0].reshape(-1))
+        master[offs[1]:offs[1] + m[1].numel()].copy_(m[1].reshape(-1))
+    else:
+        fill_normal_(master, w.master_seed)
+    grad = torch.zeros(total, **f32)
+    exp_avg = torch.zeros(total, **f32)
+    exp_avg_sq = torch.zeros(total, **f32)
+    if w.param_dtype == "fp32":
+        param = master
+    else:
+        param = torch.empty(total, dtype=torch.bfloat16, device=device)
+        for a in range(0, total, FILL_CHUNK):
+            b = min(total, a + FILL_CHUNK)
+            param[a:b].copy_(master[a:b])
+    return Buffers(w, offs, total, master, grad, exp_avg, exp_avg_sq, param)
+
+
+def two_matrix_masters():
+    """w1 = randn(4096,1024), w2 = randn(1024,4096) after torch.manual_seed(0),
+    drawn on the CPU as the page's state-size script does."""
+    g = torch.Generator().manual_seed(0)
+    w1 = torch.randn(4096, 1024, generator=g)
+    w2 = torch.randn(1024, 4096, generator=g)
+    return w1, w2
+
+
+def fill_grads_(bufs: Buffers, k: int) -> None:
+    """Stored grads of 1-based call k, written into bufs.grad in place.
+
+    toy: the page's alternating grads.  Otherwise N(0, 1) from seed
+    grad_seed_base + k over the whole flat buffer, each tensor's slice then
+    multiplied by its std, then by the loss scale (exact for powers of two);
+    at ``inf_step`` one element becomes +inf (see inf_position)."""
+    w = bufs.workload
+    if w.name.startswith("toy"):
+        bufs.grad[:2].copy_(torch.from_numpy(toy_grad(k)))
+        return
+    if w.name.startswith("two_matrices"):
+        g = torch.Generator().manual_seed(w.grad_seed_base + k)
+        for i in range(w.n_tensors):
+            cpu = torch.randn(w.numels[i], generator=g).mul_(w.grad_std[i])
+            bufs.view(bufs.grad, i).copy_(cpu)
+    else:
+        fill_normal_(bufs.grad, w.grad_seed_base + k)
+        stds = w.grad_std
+        if len(set(stds)) == 1:
+            bufs.grad.mul_(stds[0])
+        else:
+            for i in range(w.n_tensors):
+                bufs.view(bufs.grad, i).mul_(stds[i])
+    if w.loss_scale is not None:
+        bufs.grad.mul_(w.loss_scale)
+    if w.inf_step is not None and k == w.inf_step:
+        ti, e = inf_position(w)
+        bufs.grad[bufs.offs[ti] + e] = float("inf")

@@ -1,0 +1,271 @@
+"""CPU oracle for the mixed-precision AdamW step (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+and imports nothing from the product package; the product never imports it.
+
+The arithmetic lives in ``hpo_oracle.c`` (plain C loops, fp32-literal "O32"
+and binary64 "O64" variants).  This module loads it through ctypes and
+orders the steps of one optimizer step the way the pages order them:
+
+  [OPT-INFRA] "02 · Optimizer：算法与 infra"
+    §10.2  the unscale pass sets found_inf; a step with found_inf set returns
+           early: no clip, no inner step, the step counter does not advance;
+    §11.1  total norm = sqrt(sum of squared grad norms); clip coefficient
+           max_norm / (total + 1e-6), applied when below 1; clip_grad <= 0
+           turns clipping off;
+    §2,§3  the Adam/AdamW update of the fp32 master, m and v;
+    §9.2   the master is then written back to the 16-bit model params.
+  [FP32-RFC] "支持FP32优化器" §7.2: fp32 params are their own master.
+
+Parity pinning: every function here is checked in ``tests/test_oracle_pins.py``
+against values the pages print, closed forms, ``math.fsum``, torch's CPU cast
+and torch's CPU Adam/AdamW (a different op order).  NaN bit patterns of the
+bf16 write-back are not fixed by the pages ("parity unpinned": NaN is compared
+by class only).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hpo_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+ADAMW = 0
+ADAM_L2 = 1
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+             "-fno-fast-math", "-fno-finite-math-only"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile hpo_oracle.c into liboracle.so with gcc (always recompiles)."""
+    cmd = ["gcc", *GCC_FLAGS, _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+class _UpdateArgs(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_double),
+        ("wd", ctypes.c_double),
+        ("beta1", ctypes.c_double),
+        ("beta2", ctypes.c_double),
+        ("eps", ctypes.c_double),
+        ("t", ctypes.c_int64),
+        ("mode", ctypes.c_int32),
+        ("do_clip", ctypes.c_int32),
+        ("inv_scale", ctypes.c_float),
+        ("clip_C", ctypes.c_float),
+        ("clip_c64", ctypes.c_double),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, building it first only when it does not exist."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.orc_version.restype = ctypes.c_int32
+        L.orc_bf16_rne.argtypes = [ctypes.c_float]
+        L.orc_bf16_rne.restype = ctypes.c_uint16
+        L.orc_bf16_rne_array.argtypes = [P, P, I64]
+        L.orc_bf16_rne_patterns.argtypes = [ctypes.c_uint32, I64, P]
+        L.orc_any_nonfinite.argtypes = [P, I64]
+        L.orc_any_nonfinite.restype = ctypes.c_int32
+        L.orc_unscale_inplace.argtypes = [P, I64, ctypes.c_float]
+        L.orc_sumsq.argtypes = [P, I64, ctypes.c_float]
+        L.orc_sumsq.restype = ctypes.c_double
+        L.orc_clip_coeff.argtypes = [ctypes.c_double, ctypes.c_float,
+                                     ctypes.POINTER(ctypes.c_float),
+                                     ctypes.POINTER(ctypes.c_double)]
+        L.orc_clip_coeff.restype = ctypes.c_int32
+        for name in ("orc_update_f32", "orc_update_f64"):
+            fn = getattr(L, name)
+            fn.argtypes = [I64, P, P, P, P, P, ctypes.POINTER(_UpdateArgs)]
+            fn.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _f32(a: np.ndarray) -> np.ndarray:
+    assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"]
+    return a
+
+
+# --------------------------------------------------------------------------
+# elementary pieces
+# --------------------------------------------------------------------------
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), IEEE RNE (oracle definition)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_bf16_rne_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def bf16_rne_patterns(first: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.uint16)
+    lib().orc_bf16_rne_patterns(ctypes.c_uint32(first), count, _ptr(out))
+    return out
+
+
+def any_nonfinite(G: np.ndarray) -> bool:
+    G = _f32(G)
+    return bool(lib().orc_any_nonfinite(_ptr(G), G.size))
+
+
+def unscale_inplace(G: np.ndarray, inv_scale: float) -> None:
+    G = _f32(G)
+    lib().orc_unscale_inplace(_ptr(G), G.size, ctypes.c_float(inv_scale))
+
+
+def sumsq(G: np.ndarray, inv_scale: float = 1.0) -> float:
+    """sum over elements of (double)(fp32(G * inv))^2, sequential binary64."""
+    G = _f32(G)
+    return float(lib().orc_sumsq(_ptr(G), G.size, ctypes.c_float(inv_scale)))
+
+
+def clip_coeff(max_norm: float, norm32: float):
+    """Returns (applies, C as fp32 value, c64)."""
+    C = ctypes.c_float(1.0)
+    c64 = ctypes.c_double(1.0)
+    applies = lib().orc_clip_coeff(ctypes.c_double(max_norm), ctypes.c_float(norm32),
+                                   ctypes.byref(C), ctypes.byref(c64))
+    return bool(applies), float(np.float32(C.value)), float(c64.value)
+
+
+def norm_from_sumsq(n2: float):
+    """(binary64 norm, fp32 norm): sqrt in binary64, rounded once to fp32."""
+    n64 = math.sqrt(n2) if n2 >= 0 else float("nan")
+    return n64, float(np.float32(n64))
+
+
+# --------------------------------------------------------------------------
+# one whole optimizer step over a list of tensors
+# --------------------------------------------------------------------------
+@dataclass
+class Hyper:
+    """Adam hyperparameters ([OPT-INFRA] §2 defaults; §17 config fields)."""
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    mode: int = ADAMW
+
+
+@dataclass
+class OTensor:
+    """One parameter's optimizer-side state, all host numpy arrays."""
+    theta: np.ndarray                 # fp32 master (is the param for fp32 params)
+    m: np.ndarray                     # fp32 exp_avg
+    v: np.ndarray                     # fp32 exp_avg_sq
+    p: Optional[np.ndarray] = None    # uint16 bf16 bits of the model param, or None (fp32 param)
+    group: int = 0
+
+    @staticmethod
+    def fresh(theta: np.ndarray, bf16_param: bool = True, group: int = 0) -> "OTensor":
+        theta = np.ascontiguousarray(theta, dtype=np.float32).copy()
+        p = bf16_rne(theta) if bf16_param else None
+        return OTensor(theta, np.zeros_like(theta), np.zeros_like(theta), p, group)
+
+    def copy(self) -> "OTensor":
+        return OTensor(self.theta.copy(), self.m.copy(), self.v.copy(),
+                       None if self.p is None else self.p.copy(), self.group)
+
+
+@dataclass
+class StepResult:
+    applied: bool
+    found_inf: bool
+    norm32: Optional[float]
+    norm64: Optional[float]
+    clip_applied: bool = False
+    clip_C: float = 1.0
+    extra: dict = field(default_factory=dict)
+
+
+def oracle_step(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper: Hyper,
+                groups: Sequence[tuple], t: int, inv_scale: float = 1.0,
+                max_norm: float = 0.0, variant: str = "f32") -> StepResult:
+    """One full mixed-precision step, in place on ``tensors``.
+
+    ``groups[k] = (lr, weight_decay)``; ``t`` is the 1-based count of applied
+    steps including this one.  Returns the step's flags and norm; a skipped
+    step leaves every tensor bit-identical.
+    """
+    L = lib()
+    assert len(tensors) == len(grads)
+    inv32 = float(np.float32(inv_scale))
+    # a1: found_inf over the stored grads
+    found = False
+    for G in grads:
+        if G.size and any_nonfinite(G):
+            found = True
+    if found:
+        return StepResult(False, True, None, None)
+    # a2: global norm of the unscaled grads, binary64, tensors in list order
+    n2 = 0.0
+    for G in grads:
+        if G.size:
+            n2 = n2 + sumsq(G, inv32)
+    norm64, norm32 = norm_from_sumsq(n2)
+    # a3: clip coefficient from the fp32 norm
+    do_clip, C, c64 = clip_coeff(max_norm, norm32)
+    # a4 + a5: the update, one call per tensor with its group's lr / wd
+    fn = L.orc_update_f32 if variant == "f32" else L.orc_update_f64
+    for T, G in zip(tensors, grads):
+        if T.theta.size == 0:
+            continue
+        lr, wd = groups[T.group]
+        args = _UpdateArgs(lr=lr, wd=wd, beta1=hyper.beta1, beta2=hyper.beta2,
+                           eps=hyper.eps, t=t, mode=hyper.mode, do_clip=int(do_clip),
+                           inv_scale=inv32, clip_C=C, clip_c64=c64)
+        fn(T.theta.size, _ptr(_f32(T.theta)), _ptr(_f32(T.m)), _ptr(_f32(T.v)),
+           _ptr(_f32(np.ascontiguousarray(G))), _ptr(T.p), ctypes.byref(args))
+    return StepResult(True, False, norm32, norm64, do_clip, C)
+
+
+class OracleOptimizer:
+    """Keeps the applied-step counter the way the pages do: a skipped step
+    does not advance it ([OPT-INFRA] §10.2)."""
+
+    def __init__(self, tensors: List[OTensor], hyper: Hyper, groups: Sequence[tuple],
+                 max_norm: float = 0.0, variant: str = "f32"):
+        self.tensors = tensors
+        self.hyper = hyper
+        self.groups = list(groups)
+        self.max_norm = max_norm
+        self.variant = variant
+        self.t = 0  # applied steps so far
+
+    def step(self, grads: Sequence[np.ndarray], inv_scale: float = 1.0) -> StepResult:
+        r = oracle_step(self.tensors, grads, self.hyper, self.groups, self.t + 1,
+                        inv_scale, self.max_norm, self.variant)
+        if r.applied:
+            self.t += 1
+        return r

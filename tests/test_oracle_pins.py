@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names the passage it pins.  None of them re-types the oracle's
+formula: they use printed values, closed forms, exact summation
+(math.fsum), torch's CPU bf16 cast and torch's CPU Adam/AdamW (a different
+op order), brute force and invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from bounds import check_within, step_error_bounds
+from conftest import read_golden
+
+ADAMW, ADAM_L2 = 0, 1
+
+
+def _rand_state(n, seed, t_prev=3):
+    """A plausible mid-training state: theta ~ N(0,1), m ~ N(0,1e-3), v ~ (1e-3 N)^2."""
+    rng = np.random.default_rng(seed)
+    th = rng.standard_normal(n).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = ((rng.standard_normal(n) * 1e-3) ** 2).astype(np.float32)
+    G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    return th, m, v, G
+
+
+def _one_step(orc, th, m, v, G, *, lr, wd, t, mode, variant, inv=1.0, do_clip=False, C=1.0, c64=1.0,
+              b1=0.9, b2=0.999, eps=1e-8, bf16=True):
+    T = orc.OTensor(th.copy(), m.copy(), v.copy(), orc.bf16_rne(th) if bf16 else None)
+    args = orc._UpdateArgs(lr=lr, wd=wd, beta1=b1, beta2=b2, eps=eps, t=t, mode=mode,
+                           do_clip=int(do_clip), inv_scale=np.float32(inv), clip_C=C, clip_c64=c64)
+    fn = orc.lib().orc_update_f32 if variant == "f32" else orc.lib().orc_update_f64
+    import ctypes
+    fn(th.size, orc._ptr(T.theta), orc._ptr(T.m), orc._ptr(T.v), orc._ptr(np.ascontiguousarray(G)),
+       orc._ptr(T.p), ctypes.byref(args))
+    return T
+
+
+# ---------------------------------------------------------------------------
+# a4: the page's two-parameter decay experiment (printed values)
+# ---------------------------------------------------------------------------
+def _toy_run(orc, mode, steps=1000, variant="f32"):
+    T = orc.OTensor.fresh(np.ones(2, np.float32), bf16_param=False)
+    opt = orc.OracleOptimizer([T], orc.Hyper(mode=mode), [(1e-2, 0.1)], variant=variant)
+    scale = np.array([0.01, 10.0], np.float32)
+    for t in range(steps):
+        r = opt.step([np.ascontiguousarray(scale * np.float32((-1.0) ** t))])
+        assert r.applied
+    return T.theta.copy()
+
+
+@pytest.mark.parametrize("variant", ["f32", "f64"])
+def test_toy_matches_printed_values(orc, variant):
+    """Page "优化器：AdamW、Muon 与分布式优化器", AdamW section: printed results of the
+    decoupled vs L2 experiment, three decimals each."""
+    gold = read_golden("handbook_adamw_decay_toy.txt")
+    l2 = _toy_run(orc, ADAM_L2, variant=variant)
+    aw = _toy_run(orc, ADAMW, variant=variant)
+    assert [f"{x:.3f}" for x in l2] == gold["adam_l2"]
+    assert [f"{x:.3f}" for x in aw] == gold["adamw"]
+    assert f"{(1 - 1e-2 * 0.1) ** 1000:.3f}" == gold["closed_form"][0]
+    # the L2 mode's small-grad parameter is driven to (near) zero but stays positive
+    assert 0.0 < l2[0] < 5e-4
+    # decoupled decay treats both parameters alike
+    assert abs(aw[0] - aw[1]) < 1e-5
+
+
+def test_toy_o32_close_to_o64(orc):
+    """Drift between the fp32-literal and binary64 readings after 1000 steps is tiny
+    compared to the printed precision."""
+    for mode in (ADAMW, ADAM_L2):
+        a = _toy_run(orc, mode, variant="f32").astype(np.float64)
+        b = _toy_run(orc, mode, variant="f64").astype(np.float64)
+        assert np.all(np.abs(a - b) <= 1e-4 * np.maximum(np.abs(b), 1e-3))
+
+
+# ---------------------------------------------------------------------------
+# a4: closed forms
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["f32", "f64"])
+def test_zero_grad_pure_decay_closed_form(orc, variant):
+    """Zero grads, wd > 0: the update term is 0/(0+eps) = 0, so AdamW reduces to
+    theta_T = theta_0 (1 - lr wd)^T ("02 · Optimizer：算法与 infra" §3 with g = 0;
+    the handbook's 0.368 closed form)."""
+    rng = np.random.default_rng(7)
+    th0 = rng.standard_normal(1000).astype(np.float32)
+    T = orc.OTensor.fresh(th0, bf16_param=True)
+    opt = orc.OracleOptimizer([T], orc.Hyper(mode=ADAMW), [(1e-2, 0.1)], variant=variant)
+    z = np.zeros(1000, np.float32)
+    for _ in range(1000):
+        opt.step([z])
+    exact = th0.astype(np.float64) * (1 - 1e-3) ** 1000
+    # 1000 steps of 3 fp32 roundings each
+    assert np.all(np.abs(T.theta - exact) <= 3000 * 2.0 ** -24 * np.abs(exact) + 1e-30)
+    assert np.all(T.m == 0) and np.all(T.v == 0)
+    ones = orc.OTensor.fresh(np.ones(1, np.float32), bf16_param=False)
+    opt1 = orc.OracleOptimizer([ones], orc.Hyper(), [(1e-2, 0.1)], variant=variant)
+    for _ in range(1000):
+        opt1.step([np.zeros(1, np.float32)])
+    assert f"{ones.theta[0]:.3f}" == read_golden("handbook_adamw_decay_toy.txt")["closed_form"][0]
+
+
+@pytest.mark.parametrize("mode", [ADAMW, ADAM_L2])
+def test_zero_grad_no_decay_is_identity(orc, mode):
+    """Zero grads with wd = 0 from a fresh state leave master, m, v and the bf16
+    param bit-unchanged (every term of the update is exactly zero)."""
+    rng = np.random.default_rng(8)
+    th0 = rng.standard_normal(4099).astype(np.float32)
+    T = orc.OTensor.fresh(th0)
+    p0 = T.p.copy()
+    opt = orc.OracleOptimizer([T], orc.Hyper(mode=mode), [(1e-3, 0.0)], max_norm=1.0)
+    for _ in range(5):
+        opt.step([np.zeros(4099, np.float32)])
+    assert np.array_equal(T.theta.view(np.uint32), th0.view(np.uint32))
+    assert np.array_equal(T.p, p0)
+    assert not T.m.any() and not T.v.any()
+
+
+def test_first_step_closed_form(orc):
+    """Step 1 from m = v = 0: m_hat = g and v_hat = g^2 exactly, so
+    theta_1 = theta_0 - lr (g / (|g| + eps) + wd theta_0) ("02 · Optimizer：算法与 infra"
+    §2 bias correction + §3)."""
+    th, m, v, G = _rand_state(5000, 9)
+    m[:] = 0
+    v[:] = 0
+    lr, wd = 1e-3, 0.1
+    g = G.astype(np.float64)
+    exact = th.astype(np.float64) - lr * (g / (np.abs(g) + 1e-8) + wd * th.astype(np.float64))
+    T64 = _one_step(orc, th, m, v, G, lr=lr, wd=wd, t=1, mode=ADAMW, variant="f64")
+    T32 = _one_step(orc, th, m, v, G, lr=lr, wd=wd, t=1, mode=ADAMW, variant="f32")
+    # O64 rounds only the stored result
+    assert np.all(np.abs(T64.theta - exact) <= 2.0 ** -24 * np.abs(exact) * 1.0001)
+    S = np.abs(th) + lr * (1 + wd * np.abs(th))
+    assert np.all(np.abs(T32.theta - exact) <= 1e-6 * S)
+    assert np.allclose(T64.m, (0.1 * g).astype(np.float32), rtol=2 ** -23, atol=0)
+
+
+def test_constant_grad_closed_form(orc):
+    """Constant grad g: m_hat_t = g and v_hat_t = g^2 at every t, so the update is
+    s = g/(|g|+eps) and theta_T = (theta_0 + s/wd)(1 - lr wd)^T - s/wd."""
+    rng = np.random.default_rng(10)
+    th0 = rng.standard_normal(256).astype(np.float32)
+    G = (rng.standard_normal(256) * 1e-2).astype(np.float32)
+    lr, wd, steps = 1e-3, 0.1, 50
+    s = G.astype(np.float64) / (np.abs(G.astype(np.float64)) + 1e-8)
+    exact = (th0 + s / wd) * (1 - lr * wd) ** steps - s / wd
+    for variant in ("f32", "f64"):
+        T = orc.OTensor.fresh(th0)
+        opt = orc.OracleOptimizer([T], orc.Hyper(), [(lr, wd)], variant=variant)
+        for _ in range(steps):
+            opt.step([G])
+        scale = np.abs(th0) + lr * steps * (1 + wd * np.abs(th0))
+        assert np.all(np.abs(T.theta - exact) <= steps * 8 * 2.0 ** -24 * scale)
+
+
+def test_betas_zero_reduce_to_sign_like_update(orc):
+    """beta1 = beta2 = 0: m = g, v = g^2, both bias corrections are 1 at any t, so
+    the update is g/(|g| + eps) regardless of the old state."""
+    th, m, v, G = _rand_state(3000, 11)
+    lr, wd = 1e-3, 0.1
+    g = G.astype(np.float64)
+    exact = th - lr * (g / (np.abs(g) + 1e-8) + wd * th.astype(np.float64))
+    T = _one_step(orc, th, m, v, G, lr=lr, wd=wd, t=7, mode=ADAMW, variant="f64", b1=0.0, b2=0.0)
+    assert np.all(np.abs(T.theta - exact) <= 2.0 ** -24 * np.abs(exact) * 1.0001)
+    assert np.array_equal(T.m, G)
+
+
+def test_l2_with_zero_decay_equals_adamw(orc):
+    """Adam+L2 and AdamW differ only in where wd enters; with wd = 0 the two
+    modes give bit-identical state ("02 · Optimizer：算法与 infra" §3)."""
+    th, m, v, G = _rand_state(10000, 12)
+    a = _one_step(orc, th, m, v, G, lr=1e-3, wd=0.0, t=4, mode=ADAMW, variant="f32")
+    b = _one_step(orc, th, m, v, G, lr=1e-3, wd=0.0, t=4, mode=ADAM_L2, variant="f32")
+    for x, y in ((a.theta, b.theta), (a.m, b.m), (a.v, b.v), (a.p, b.p)):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def test_fp32_master_is_needed(orc):
+    """"02 · Optimizer：算法与 infra" §9.1: an update far below the weight's 16-bit
+    spacing is lost when added in 16 bits, so the update runs on an fp32 master.
+    theta_0 = 1, update lr*u = 1e-4 per step (u = 1): a bf16-only update never
+    moves 1.0 (spacing 2^-8 below 1), while the master drifts and the written-back
+    bf16 param flips to 0.99609375 exactly when the master drops below 1 - 2^-9."""
+    T = orc.OTensor.fresh(np.ones(1, np.float32))
+    opt = orc.OracleOptimizer([T], orc.Hyper(), [(1e-4, 0.0)])
+    ps = []
+    for _ in range(25):
+        opt.step([np.ones(1, np.float32)])
+        ps.append(int(T.p[0]))
+    assert ps[18] == 0x3F80  # after 19 steps: 0.9981 still rounds to 1.0
+    assert ps[19] == 0x3F7F  # after 20 steps: 0.998 < 0.998046875 -> 0.99609375
+    # the same update applied to the bf16 value itself is lost every time
+    p = torch.tensor([1.0], dtype=torch.bfloat16)
+    for _ in range(25):
+        p = (p.float() - 1e-4).to(torch.bfloat16)
+    assert p.item() == 1.0
+
+
+# ---------------------------------------------------------------------------
+# a4: O32 against the exact shadow and against torch's own AdamW / Adam
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [ADAMW, ADAM_L2])
+@pytest.mark.parametrize("t", [1, 2, 10, 1000])
+def test_o32_within_error_bound_of_o64(orc, mode, t):
+    """The fp32-literal reading stays within the rel-1e-6 propagated bound of the
+    binary64 evaluation of the same formulas, one step from the same state."""
+    th, m, v, G = _rand_state(200_000, 13 + t)
+    if t == 1:
+        m[:] = 0
+        v[:] = 0
+    lr, wd, inv, C = 1e-3, 0.1, 2.0 ** -16, 0.345
+    Gs = (G * np.float32(65536.0)).astype(np.float32)
+    kw = dict(lr=lr, wd=wd, t=t, mode=mode, inv=inv, do_clip=True, C=float(np.float32(C)), c64=C)
+    a = _one_step(orc, th, m, v, Gs, variant="f32", **kw)
+    b = _one_step(orc, th, m, v, Gs, variant="f64", **kw)
+    E_m, E_v, E_th = step_error_bounds(th, m, v, Gs, inv=inv, C=C, do_clip=True, lr=lr, wd=wd,
+                                       t=t, mode=mode)
+    check_within("m", a.m, b.m, E_m)
+    check_within("v", a.v, b.v, E_v)
+    check_within("theta", a.theta, b.theta, E_th)
+    # bf16 params within one bf16 ulp of each other
+    assert np.all(np.abs(a.p.astype(np.int32) - b.p.astype(np.int32)) <= 1)
+
+
+@pytest.mark.parametrize("mode", [ADAMW, ADAM_L2])
+def test_o32_matches_torch_cpu_optimizer_per_step(orc, mode):
+    """torch.optim.AdamW / Adam on CPU fp32 (prior art with its own op order:
+    decay first, lerp for m, addcdiv) agree with O32 per step from the same
+    state within the rel-1e-6 propagated bound."""
+    n, lr, wd = 50_000, 1e-3, 0.1
+    th, m, v, G = _rand_state(n, 21)
+    for t in (1, 2, 5, 50):
+        if t == 1:
+            m0, v0 = np.zeros_like(m), np.zeros_like(v)
+        else:
+            m0, v0 = m, v
+        a = _one_step(orc, th, m0, v0, G, lr=lr, wd=wd, t=t, mode=mode, variant="f32")
+        p = torch.nn.Parameter(torch.from_numpy(th.copy()))
+        cls = torch.optim.AdamW if mode == ADAMW else torch.optim.Adam
+        opt = cls([p], lr=lr, weight_decay=wd, betas=(0.9, 0.999), eps=1e-8, foreach=False)
+        p.grad = torch.from_numpy(G.copy())
+        opt.state[p] = {"step": torch.tensor(float(t - 1)),
+                        "exp_avg": torch.from_numpy(m0.copy()),
+                        "exp_avg_sq": torch.from_numpy(v0.copy())}
+        opt.step()
+        st = opt.state[p]
+        # both sides err, so the allowance is twice the single-implementation bound
+        E_m, E_v, E_th = step_error_bounds(th, m0, v0, G, inv=1.0, C=1.0, do_clip=False, lr=lr,
+                                           wd=wd, t=t, mode=mode)
+        check_within("m", a.m, st["exp_avg"].numpy(), 2 * E_m)
+        check_within("v", a.v, st["exp_avg_sq"].numpy(), 2 * E_v)
+        check_within("theta", a.theta, p.detach().numpy(), 2 * E_th)
+
+
+# ---------------------------------------------------------------------------
+# a1 / a6: non-finite check and the whole-step skip
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+@pytest.mark.parametrize("where", ["head", "middle", "tail"])
+def test_nonfinite_check_brute_force(orc, bad, where):
+    rng = np.random.default_rng(30)
+    G = (rng.standard_normal(10_007) * 1e-3).astype(np.float32)
+    G[:4] = [0.0, -0.0, np.float32(1e-45), np.finfo(np.float32).max]  # finite edge values
+    assert orc.any_nonfinite(G) is False
+    idx = {"head": 0, "middle": 5003, "tail": 10_006}[where]
+    G[idx] = bad
+    assert orc.any_nonfinite(G) is True
+    assert orc.any_nonfinite(G) == (not np.all(np.isfinite(G)))
+
+
+def test_skip_leaves_state_and_counter_alone(orc):
+    """"02 · Optimizer：算法与 infra" §10.2: with found_inf the step returns early,
+    runs no clip and no inner step, and the scheduler/step count does not move.
+    Sequence [g1, g_bad, g2] must equal [g1, g2]."""
+    rng = np.random.default_rng(31)
+    th0 = rng.standard_normal(777).astype(np.float32)
+    g1 = (rng.standard_normal(777) * 1e-3).astype(np.float32)
+    g2 = (rng.standard_normal(777) * 1e-3).astype(np.float32)
+    bad = g2.copy()
+    bad[776] = np.inf
+    A = orc.OTensor.fresh(th0)
+    B = orc.OTensor.fresh(th0)
+    oa = orc.OracleOptimizer([A], orc.Hyper(), [(1e-3, 0.1)], max_norm=1.0)
+    ob = orc.OracleOptimizer([B], orc.Hyper(), [(1e-3, 0.1)], max_norm=1.0)
+    oa.step([g1])
+    snap = A.copy()
+    r = oa.step([bad])
+    assert not r.applied and r.found_inf and r.norm32 is None
+    for x, y in ((A.theta, snap.theta), (A.m, snap.m), (A.v, snap.v), (A.p, snap.p)):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    assert oa.t == 1
+    oa.step([g2])
+    ob.step([g1])
+    ob.step([g2])
+    assert oa.t == ob.t == 2
+    for x, y in ((A.theta, B.theta), (A.m, B.m), (A.v, B.v), (A.p, B.p)):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def test_unscale_power_of_two_is_exact(orc):
+    """Multiplying by 2^-16 is exact for normal fp32 values, so the in-place
+    unscale recovers the unscaled grads bit for bit."""
+    rng = np.random.default_rng(32)
+    g = (rng.standard_normal(100_000) * 1e-3).astype(np.float32)
+    G = (g * np.float32(65536.0)).astype(np.float32)
+    orc.unscale_inplace(G, 2.0 ** -16)
+    assert np.array_equal(G.view(np.uint32), g.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# a2 / a3: global norm and clip
+# ---------------------------------------------------------------------------
+def test_sumsq_against_fsum(orc):
+    """"02 · Optimizer：算法与 infra" §11.1 total norm; math.fsum gives the correctly
+    rounded exact sum of the (exact) binary64 squares."""
+    rng = np.random.default_rng(40)
+    for n, std in ((1, 1.0), (1000, 1e-3), (1_000_003, 1e-2)):
+        g = (rng.standard_normal(n) * std).astype(np.float32)
+        exact = math.fsum(float(x) * float(x) for x in g.astype(np.float64))
+        got = orc.sumsq(g)
+        assert abs(got - exact) <= n * 2.0 ** -53 * exact
+
+
+def test_norm_closed_forms_and_permutation(orc):
+    c = np.float32(2.0 ** -7)
+    g = np.full(4 ** 8, c, np.float32)  # N = 65536 -> norm = c * 256 exactly
+    assert orc.norm_from_sumsq(orc.sumsq(g))[0] == float(c) * 256
+    one = np.zeros(12345, np.float32)
+    one[4321] = np.float32(-3.25)
+    assert orc.norm_from_sumsq(orc.sumsq(one))[0] == 3.25
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal(500_000) * 1e-3).astype(np.float32)
+    a, b = orc.sumsq(x), orc.sumsq(x[rng.permutation(x.size)].copy())
+    assert abs(a - b) <= x.size * 2.0 ** -53 * a
+    # unscale by 2^-16 inside the sum equals summing the unscaled copy, exactly
+    xs = (x * np.float32(65536.0)).astype(np.float32)
+    assert orc.sumsq(xs, 2.0 ** -16) == orc.sumsq(x)
+
+
+def test_clip_coefficient(orc):
+    """c = max_norm / (norm + 1e-6), applied iff c < 1; max_norm <= 0 disables."""
+    applies, C, c64 = orc.clip_coeff(1.0, 2.9)
+    assert applies and c64 == 1.0 / (float(np.float32(2.9)) + 1e-6) and C == float(np.float32(c64))
+    # post-clip norm: C * norm == max_norm * norm / (norm + 1e-6) up to fp32 rounding
+    assert abs(C * float(np.float32(2.9)) - 2.9 / (2.9 + 1e-6)) < 1e-6
+    assert orc.clip_coeff(1.0, 0.5)[0] is False            # below max_norm: untouched
+    # norm == max_norm: c = 1 / (1 + 1e-6) < 1, so the (tiny) clip applies
+    applies, C1, _ = orc.clip_coeff(1.0, 1.0)
+    assert applies and C1 == float(np.float32(1.0 / (1.0 + 1e-6)))
+    assert orc.clip_coeff(0.0, 100.0)[0] is False
+    assert orc.clip_coeff(-1.0, 100.0)[0] is False
+
+
+def test_clip_boundary_strict(orc):
+    """No clip exactly when norm + 1e-6 <= max_norm (strict '< 1' comparison)."""
+    for norm in (0.999, 0.999998, 0.999999, 1.0, 1.5):
+        n32 = float(np.float32(norm))
+        applies = orc.clip_coeff(1.0, n32)[0]
+        assert applies == (1.0 / (n32 + 1e-6) < 1.0)
+
+
+def test_full_step_clips_to_max_norm(orc):
+    """After clipping, the norm of the grads that enter the update is max_norm up
+    to the 1e-6 guard (checked through m_1 = (1 - b1) g on step 1)."""
+    rng = np.random.default_rng(42)
+    G = (rng.standard_normal(300_000) * 1e-2).astype(np.float32)
+    T = orc.OTensor.fresh(rng.standard_normal(300_000).astype(np.float32))
+    r = orc.oracle_step([T], [G], orc.Hyper(), [(1e-3, 0.1)], 1, 1.0, 1.0, "f64")
+    assert r.clip_applied and r.norm64 > 1
+    g_used = T.m.astype(np.float64) / 0.1
+    assert abs(np.sqrt(np.sum(g_used ** 2)) - r.norm64 / (r.norm64 + 1e-6)) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# a5: bf16 write-back
+# ---------------------------------------------------------------------------
+def test_bf16_rne_known_values(orc):
+    """IEEE RNE cases: ties to even, subnormals kept, overflow to inf, NaN quiet."""
+    cases = {0x3F808000: 0x3F80, 0x3F818000: 0x3F82, 0x3F808001: 0x3F81, 0x00018000: 0x0002,
+             0x7F7FFFFF: 0x7F80, 0xFF7FFFFF: 0xFF80, 0x7F800000: 0x7F80, 0x80000000: 0x8000,
+             0x00000001: 0x0000, 0x00008000: 0x0000, 0x00008001: 0x0001, 0x7F7F7FFF: 0x7F7F}
+    for bits, want in cases.items():
+        x = np.array([bits], np.uint32).view(np.float32)[0]
+        assert int(orc.bf16_rne(np.array([x]))[0]) == want, hex(bits)
+    nan = np.array([0x7FA00001, 0xFFC00000], np.uint32).view(np.float32)
+    assert [int(b) for b in orc.bf16_rne(nan)] == [0x7FC0, 0xFFC0]
+
+
+def test_bf16_rne_exhaustive_against_torch_cast(orc):
+    """All 2^32 fp32 bit patterns against torch's CPU fp32->bf16 cast (a library
+    routine).  Non-NaN results must be bit-equal; NaNs are compared by class
+    (the pages do not fix NaN encodings)."""
+    step = 1 << 28
+    base = np.arange(step, dtype=np.uint32)
+    for first in range(0, 1 << 32, step):
+        bits = base + np.uint32(first)
+        ours = orc.bf16_rne_patterns(first, step)
+        ref = torch.from_numpy(bits.view(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        isnan = ((bits & 0x7FFFFFFF) > 0x7F800000)
+        assert np.array_equal(ours[~isnan], ref[~isnan]), hex(first)
+        on = ours[isnan]
+        assert np.all(((on & 0x7FFF) > 0x7F80))
+
+
+# ---------------------------------------------------------------------------
+# ledgers
+# ---------------------------------------------------------------------------
+def test_state_bytes_per_param(orc):
+    """Page "优化器：AdamW、Muon 与分布式优化器", state-size output: AdamW holds 8 bytes of
+    optimizer state per parameter at 8.4M parameters (two fp32 moments)."""
+    gold = read_golden("handbook_optimizer_state_bytes.txt")
+    n = 4096 * 1024 + 1024 * 4096
+    Ts = [orc.OTensor.fresh(np.zeros(4096 * 1024, np.float32)), orc.OTensor.fresh(np.zeros(1024 * 4096, np.float32))]
+    state = sum(T.m.nbytes + T.v.nbytes for T in Ts)
+    assert f"{n / 1e6:.1f}" == gold["params_millions"][0]
+    assert state / n == int(gold["adamw_state_bytes_per_param"][0])
+
+
+def test_memory_ledgers():
+    gold = read_golden("memory_ledgers.txt")
+    bf16_w, bf16_g, fp32 = 2, 2, 4
+    assert bf16_w + bf16_g + 3 * fp32 == int(gold["handbook_adamw_bytes_per_param"][0])
+    assert f"{70e9 * 16 / 1e12:.1f}" == gold["handbook_70b_total_tb"][0]
+    # the layout this library steps: bf16 param + fp32 grad + fp32 master/m/v
+    assert bf16_w + fp32 + 3 * fp32 == int(gold["megatron_fp32_grad_bytes_per_param"][0])
