@@ -1,0 +1,219 @@
+"""Throughput of the full mixed-precision AdamW step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zero_shard]
+
+A step is the whole hot path over one set of synthetic inputs already
+resident in HBM: zero found_inf, the grad pass (inf/NaN check + binary64 sum
+of squares, per-chunk partials), the one-workgroup finalize (norm), the fused
+clip + AdamW + bf16 write-back pass (predicated on the device flag), and the
+8-byte read of {found_inf, norm} that decides whether the step counter moves.
+
+Default workload: one data-parallel rank's ZeRO-1 flat shard of a 70B model
+over 8 ranks -- 8.75e9 elements of fp32 grad / master / exp_avg / exp_avg_sq
+plus a bf16 param view (157.5 GB in HBM), grads N(0, 1e-4) so the norm (~9.35)
+clips to 1.0, lr 1e-3, wd 0.1.
+
+Prints ONE JSON line.  `value` is G params/s of the full step; HBM figures use
+34 algorithmic bytes per element per step (30 for the fused update, 4 for the
+grad pass).  The roofline block is for the dominant kernel (the fused update,
+30 B/elem), timed with HIP events on the stream it runs on.  cpu_baseline is
+the CPU oracle (single-threaded C, not tuned) on a bounded slice of the same
+inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "G params/s and achieved HBM GB/s (% of 8 TB/s) per full AdamW step"
+PEAK_HBM_GBPS = 8000.0
+UPDATE_BYTES = 30   # read grad, master, m, v (16); write master, m, v (12), bf16 param (2)
+GRADPASS_BYTES = 4  # read grad once
+STEP_BYTES = UPDATE_BYTES + GRADPASS_BYTES
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="zero_shard",
+                    choices=["zero_shard", "llama8b", "ragged", "two_matrices"])
+    ap.add_argument("--numel", type=int, default=None, help="override the flat shard's size")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 28,
+                    help="elements of the workload the CPU oracle steps (0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=2)
+    return ap.parse_args()
+
+
+def workload(args):
+    from mixed_precision_optimizer_amd import inputs
+    if args.workload == "zero_shard":
+        return inputs.zero_shard(args.numel) if args.numel else inputs.zero_shard()
+    if args.workload == "llama8b":
+        return inputs.llama8b()
+    if args.workload == "ragged":
+        w = inputs.ragged()
+        w.inf_step = None
+        return w
+    return inputs.two_matrices()
+
+
+def make_set(bufs):
+    from mixed_precision_optimizer_amd import hpo
+    w = bufs.workload
+    if w.flat:
+        return hpo.hpo_set_create_flat(bufs.param, bufs.master, bufs.grad, bufs.exp_avg, bufs.exp_avg_sq)
+    ps, ms, gs, m1, m2 = bufs.lists()
+    return hpo.hpo_set_create_list(ps, ms, gs, m1, m2, [w.group_of(i) for i in range(w.n_tensors)])
+
+
+def cpu_sample(bufs, n_sample):
+    """Host copy of the first n_sample elements of the initial state and the
+    step-1 grads (taken before any GPU step)."""
+    import numpy as np
+    import torch
+    n = min(n_sample, bufs.total)
+    host = lambda t: t[:n].detach().cpu().numpy().copy()
+    p = bufs.param[:n].view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    return host(bufs.master), host(bufs.exp_avg), host(bufs.exp_avg_sq), p, host(bufs.grad)
+
+
+def cpu_baseline(sample, w, steps):
+    """The oracle's full step (check, norm, clip, update, RNE) on the sample."""
+    import oracle
+    theta, m, v, p, G = sample
+    n = theta.size
+    T = oracle.OTensor(theta, m, v, p, 0)
+    O = oracle.OracleOptimizer([T], oracle.Hyper(w.beta1, w.beta2, w.eps, w.mode), w.groups(),
+                               max_norm=w.max_norm)
+    times = []
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        O.step([G], inv_scale=w.inv_scale())
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
+    gps = n / dt / 1e9
+    return {"value": round(gps, 4), "unit": "G params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} elements of the same workload (initial fp32 master/m/v, bf16 param, step-1 "
+                      f"grads), full step (inf check, binary64 norm, clip, AdamW, bf16 RNE), median of {steps} "
+                      f"steps, single-threaded C ({os.cpu_count()} host CPUs visible); "
+                      f"{STEP_BYTES * n / dt / 1e9:.2f} GB/s at 34 B/elem",
+            "ms_per_step": round(dt * 1e3, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"bench.py runs on one GPU only (got --gpus {args.gpus}); "
+                                   "the multi-GPU path (scalar all-reduces + bf16 param all-gather) is not built"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from mixed_precision_optimizer_amd import hpo, inputs
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    hpo.load()
+    w = workload(args)
+    N = w.numel
+    log(f"workload {w.name}: {N} elements, {w.n_tensors} tensors; allocating {N * 18 / 1e9:.1f} GB")
+    bufs = inputs.allocate(w, dev)
+    inputs.fill_grads_(bufs, 1)
+    torch.cuda.synchronize()
+    sample = cpu_sample(bufs, args.cpu_sample) if args.cpu_sample > 0 else None
+    hset = make_set(bufs)
+    info = hset.info()
+    log(f"set: chunk {info.chunk_elems} elements, {info.n_chunks} chunks, {info.device_bytes} B of tables")
+
+    cfg = hpo.make_cfg(w.beta1, w.beta2, w.eps, w.mode)
+    groups, n_groups = hpo.make_groups(w.groups())
+    inv = w.inv_scale()
+    buf = torch.zeros(2, dtype=torch.int32, device=dev)
+    found, norm = buf[0:1], buf[1:2].view(torch.float32)
+    host = torch.zeros(2, dtype=torch.int32, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    t_applied = 0
+
+    def step(evs=None):
+        nonlocal t_applied
+        buf.zero_()
+        if evs:
+            evs[0].record(stream)
+        hpo.hpo_grad_global_norm(hset, inv, norm, found, stream)
+        if evs:
+            evs[1].record(stream)
+        hpo.hpo_adamw_step(hset, cfg, groups, n_groups, t_applied + 1, inv, w.max_norm, norm, found, stream)
+        if evs:
+            evs[2].record(stream)
+        host.copy_(buf, non_blocking=True)
+        stream.synchronize()
+        if int(host[0]) == 0:
+            t_applied += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    norm_v = float(host[1:2].view(torch.float32)[0])
+    gradpass_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    update_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = wall * 1e3 / args.steps
+    upd = statistics.mean(update_ms)
+    gp = statistics.mean(gradpass_ms)
+    upd_gbps = UPDATE_BYTES * N / (upd * 1e-3) / 1e9
+    gp_gbps = GRADPASS_BYTES * N / (gp * 1e-3) / 1e9
+    step_gbps = STEP_BYTES * N / (ms_step * 1e-3) / 1e9
+    log(f"norm {norm_v:.6g}, applied steps {t_applied}; step {ms_step:.3f} ms, update {upd:.3f} ms "
+        f"({upd_gbps:.0f} GB/s), grad pass {gp:.3f} ms ({gp_gbps:.0f} GB/s)")
+    out = {
+        "metric": METRIC,
+        "value": round(N / (ms_step * 1e-3) / 1e9, 3),
+        "unit": "G params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "numel": N, "n_tensors": w.n_tensors, "param_dtype": w.param_dtype,
+                   "state": "fp32 master, fp32 main_grad, fp32 exp_avg/exp_avg_sq", "max_norm": w.max_norm,
+                   "lr": w.lr, "weight_decay": w.weight_decay, "loss_scale": w.loss_scale,
+                   "parallelism": "one GPU (one data-parallel rank's shard)"},
+        "hbm_full_step": {"GBps": round(step_gbps, 1), "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
+                          "bytes_per_elem": STEP_BYTES},
+        "kernels": {"adam_update": {"ms": round(upd, 4), "GBps": round(upd_gbps, 1), "bytes_per_elem": UPDATE_BYTES},
+                    "grad_pass+finalize": {"ms": round(gp, 4), "GBps": round(gp_gbps, 1),
+                                           "bytes_per_elem": GRADPASS_BYTES}},
+        "roofline": {"bound": "hbm", "achieved": round(upd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(upd_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+    hset.close()
+    if sample is not None:
+        log(f"cpu baseline on {sample[0].size} elements")
+        out["cpu_baseline"] = cpu_baseline(sample, w, args.cpu_steps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

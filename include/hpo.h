@@ -1,0 +1,225 @@
+/*
+ * hpo.h -- C ABI of libhpo: the mixed-precision AdamW optimizer step on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages):
+ *   [OPT-INFRA]  "02 · Optimizer：算法与 infra" (llm-infra-atlas, train/02_optimizer)
+ *   [HANDBOOK]   "优化器：AdamW、Muon 与分布式优化器" (ai-infra-handbooks, train/algo/optimizer)
+ *   [FP32-RFC]   "支持FP32优化器" / "AutoModels Trainer 支持 FP32 main_param 优化器"
+ *                (hyper-parallel issue)
+ *
+ * One optimizer step, in the order the pages give it ([OPT-INFRA] §10.2,
+ * §11.1, §9.2; [FP32-RFC] §8.2):
+ *   1. unscale the fp32 main grads by the loss scale and look for inf/NaN;
+ *      if any is found the whole step is skipped (no clip, no update, the
+ *      applied-step count does not move);
+ *   2. take the global L2 norm of the unscaled grads and clip them to
+ *      max_norm;
+ *   3. run Adam / AdamW on the fp32 master, exp_avg and exp_avg_sq;
+ *   4. write the master back to the 16-bit model params (bf16, round to
+ *      nearest even).
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument marked "device" is a device address on the
+ *     device that was current when the set was created; that device must be
+ *     current for every later call on the set (HPO_EDEVICE otherwise).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call that launches work is asynchronous on that stream and
+ *     returns as soon as the work is enqueued; host-side argument errors are
+ *     detected before anything is enqueued, and then nothing is.
+ *   - The caller owns (allocates, frees) every tensor and every device
+ *     result buffer.  The library never frees or resizes them.  A set holds
+ *     only its own small device tables (one 64-byte descriptor per tensor,
+ *     16 bytes per chunk, 12 bytes per chunk of reduction partials); it never
+ *     allocates per-element memory.
+ *   - The tensors of a set must stay allocated while the set exists and must
+ *     not overlap one another.  All element counts are int64.
+ *   - Return value: HPO_OK or a negative hpo_status; hpo_last_error() then
+ *     returns a message (thread-local).  No call throws or aborts.
+ *   - Two calls on the same set that run concurrently on different streams
+ *     race on the set's reduction partials; order them on one stream.
+ */
+#ifndef HPO_H
+#define HPO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HPO_ABI_VERSION 1
+/* Most parameter groups one step can take (per-group lr / weight decay). */
+#define HPO_MAX_GROUPS 16
+
+typedef enum {
+    HPO_OK = 0,
+    HPO_EINVAL = -1,  /* bad argument (null pointer, negative size, range, ...) */
+    HPO_EDTYPE = -2,  /* unsupported param dtype ([FP32-RFC] §7.2: anything but the
+                         supported float types is an error, never a silent cast) */
+    HPO_ENOMEM = -3,  /* the set's small device tables could not be allocated */
+    HPO_EHIP = -4,    /* a HIP runtime call or launch failed; message has the HIP error */
+    HPO_EDEVICE = -5  /* the current device is not the set's device */
+} hpo_status;
+
+/* dtype of the model params a set writes back to.
+ * HPO_PARAM_BF16: bf16 params, each with its own fp32 master.
+ * HPO_PARAM_FP32: fp32 params are their own master ([FP32-RFC] §7.2, native
+ *                 fp32 params): param must be NULL or equal to main_param, and
+ *                 no write-back happens.
+ * Any other value (fp16 included) is rejected with HPO_EDTYPE. */
+typedef enum { HPO_PARAM_BF16 = 0, HPO_PARAM_FP32 = 1 } hpo_param_dtype;
+
+/* Weight-decay form ([OPT-INFRA] §3): decoupled (AdamW, the default there) or
+ * an L2 term added to the gradient before the moments (Adam + L2). */
+typedef enum { HPO_ADAMW = 0, HPO_ADAM_L2 = 1 } hpo_mode;
+
+/* Adam hyperparameters ([OPT-INFRA] §2: defaults beta1 0.9, beta2 0.999,
+ * eps 1e-8; §17 config fields).  0 <= beta < 1, eps >= 0. */
+typedef struct {
+    double beta1;
+    double beta2;
+    double eps;
+    int32_t mode; /* hpo_mode */
+} hpo_adam_cfg;
+
+/* One parameter group: learning rate and weight decay.  The usual no-decay
+ * group (norm gains, biases: [HANDBOOK] AdamW section) is a group with
+ * weight_decay = 0. */
+typedef struct {
+    double lr;
+    double weight_decay;
+} hpo_group;
+
+/* Opaque handle on a set of parameters stepped together. */
+typedef struct hpo_set_* hpo_set;
+
+typedef struct {
+    int32_t n_tensors;
+    int32_t param_dtype;
+    int32_t is_flat;
+    int32_t chunk_elems;   /* elements per work chunk (one workgroup each) */
+    int64_t numel;         /* total elements over all tensors */
+    int64_t n_chunks;
+    int64_t device_bytes;  /* bytes of device memory the set itself holds */
+    int32_t device;        /* HIP device ordinal of the set */
+    int32_t n_vector;      /* tensors that take the 16-byte vector path */
+} hpo_set_info_t;
+
+/* ---------------------------------------------------------------------- */
+/* Sets                                                                    */
+/* ---------------------------------------------------------------------- */
+
+/* A set over a list of n_tensors parameters ([OPT-INFRA] §9.2: the wrapper
+ * keeps the model params, their fp32 masters and the fp32 main grads side by
+ * side).  Tensor i is the contiguous 1-D range of numel[i] elements at each
+ * of the five device pointers:
+ *   param[i]      bf16 model param (HPO_PARAM_BF16), or NULL / main_param[i]
+ *                 for HPO_PARAM_FP32;
+ *   main_param[i] fp32 master, main_grad[i] fp32 main grad (stored, i.e. still
+ *                 multiplied by the loss scale), exp_avg[i], exp_avg_sq[i] fp32.
+ * group_index[i] in [0, HPO_MAX_GROUPS) selects the tensor's hpo_group in
+ * hpo_adamw_step (NULL: every tensor is in group 0).  numel[i] may be 0;
+ * n_tensors may be 0 (then every call is a no-op and the norm is 0).
+ * Pointers need 4-byte (fp32) and 2-byte (bf16) alignment; a tensor whose
+ * pointers are not all 16-byte aligned (8-byte for bf16) is still stepped,
+ * on a slower element-at-a-time path.
+ * The host arrays are read during the call only.  The device tables are
+ * uploaded on `stream`, and the call waits for that upload to finish. */
+hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dtype,
+                               void* const* param, float* const* main_param,
+                               float* const* main_grad, float* const* exp_avg,
+                               float* const* exp_avg_sq, const int64_t* numel,
+                               const int32_t* group_index, void* stream);
+
+/* A set over one flat, contiguous range of numel elements: the ZeRO-1 shard
+ * layout of [OPT-INFRA] §12.1 (each data-parallel rank owns one contiguous
+ * slice of the flat grad/param buffers, param boundaries ignored).  One group
+ * (group 0).  Same pointer rules as one tensor of a list set. */
+hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
+                               float* main_param, float* main_grad, float* exp_avg,
+                               float* exp_avg_sq, void* stream);
+
+/* Frees the set's device tables after waiting for the device to go idle.
+ * NULL is accepted. */
+hpo_status hpo_set_destroy(hpo_set s);
+
+hpo_status hpo_set_info(hpo_set s, hpo_set_info_t* out);
+
+/* ---------------------------------------------------------------------- */
+/* The step                                                               */
+/* ---------------------------------------------------------------------- */
+
+/* Unscale and check, the pages' in-place form ([OPT-INFRA] §9.2 table, unscale
+ * row; §10.2): every main grad element G becomes fp32(G * inv_scale) in place,
+ * and *d_found_inf (device int32) is set to 1 when any stored element was inf
+ * or NaN; it is never cleared, so zero it before the first call of a step.
+ * With inv_scale == 1 the grads are only read (multiplying by 1 changes no
+ * finite value).  After this call pass inv_scale = 1 to the two calls below. */
+hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_inf, void* stream);
+
+/* Global grad norm ([OPT-INFRA] §11.1): *d_norm (device fp32) receives
+ * fp32(sqrt(sum over all elements of g^2)) with g = fp32(G * inv_scale), the
+ * squares and the sum in binary64 (per-workgroup partials, then one fixed-order
+ * sum, so the result is deterministic).  The grads are not written.
+ * d_found_inf (device int32, nullable) is set to 1 when any stored element is
+ * inf or NaN (same rule as above) -- the same read serves both.  When a
+ * non-finite value is present the norm is inf or NaN. */
+hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32_t* d_found_inf,
+                                void* stream);
+
+/* Clip + Adam/AdamW update + bf16 write-back, one fused pass
+ * ([OPT-INFRA] §11.1, §2, §3, §9.2).  For every element, with fp32 arithmetic
+ * in the order written and no fused multiply-add:
+ *   g  = G * inv_scale;  if clipping: g = g * C
+ *   Adam + L2 only:  g = g + wd * theta
+ *   m  = b1 * m + (1 - b1) * g;      v = b2 * v + (1 - b2) * (g * g)
+ *   u  = (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ *   AdamW: theta = theta - lr * (u + wd * theta);  Adam + L2: theta = theta - lr * u
+ *   bf16 sets: param = bf16_rne(theta)
+ * b1, b2, 1-b1, 1-b2, 1-b^t, eps, lr and wd are formed in binary64 on the host
+ * and rounded to fp32 once.  Clipping: when max_norm > 0, c = max_norm /
+ * ((double)*d_norm + 1e-6) is formed in binary64 on the device; it applies
+ * when c < 1, as C = fp32(c).  max_norm <= 0 turns clipping off (d_norm may
+ * then be NULL).
+ * t is the 1-based count of applied steps including this one; a skipped step
+ * must not advance it ([OPT-INFRA] §10.2).  groups[k] holds group k's lr and
+ * weight decay; n_groups must cover every group index of the set.
+ * d_found_inf (device int32, nullable): when it is non-zero at run time the
+ * whole launch does nothing (device-side skip), so the step can be enqueued
+ * before the flag is read back. */
+hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups,
+                          int32_t n_groups, int64_t t, float inv_scale, double max_norm,
+                          const float* d_norm, const int32_t* d_found_inf, void* stream);
+
+/* Master -> model copy alone: param = bf16_rne(main_param) for every element
+ * of a bf16 set ([OPT-INFRA] §9.2, the write-back row; the same conversion the
+ * step fuses).  A no-op for fp32 sets. */
+hpo_status hpo_copy_main_to_model(hpo_set s, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Host-only queries (no device needed)                                   */
+/* ---------------------------------------------------------------------- */
+
+/* The work split a list set over these sizes would use: chunk size, number
+ * of chunks (workgroups per pass) and the set's own device bytes.  Writes
+ * only the outputs given (each may be NULL). */
+hpo_status hpo_plan(int32_t n_tensors, const int64_t* numel, int32_t* out_chunk_elems,
+                    int64_t* out_n_chunks, int64_t* out_device_bytes);
+
+/* The chunk table such a list set would build: for chunk c, tensor index,
+ * first element and element count.  Each array must hold n_chunks entries
+ * as returned by hpo_plan. */
+hpo_status hpo_plan_chunks(int32_t n_tensors, const int64_t* numel, int64_t n_chunks,
+                           int32_t* out_tensor, int64_t* out_start, int32_t* out_len);
+
+const char* hpo_last_error(void);
+const char* hpo_status_string(int32_t status);
+int32_t hpo_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HPO_H */

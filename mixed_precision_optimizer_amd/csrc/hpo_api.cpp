@@ -1,0 +1,528 @@
+/*
+ * hpo_api.cpp -- host side of libhpo: argument validation, the chunk planner,
+ * set lifecycle, the per-step scalars and the C entry points of hpo.h.
+ * Host code only (compiled as plain C++ against the HIP runtime API).
+ *
+ * Sources (web pages):
+ *   [OPT-INFRA]  "02 · Optimizer：算法与 infra" (llm-infra-atlas, train/02_optimizer)
+ *   [FP32-RFC]   "支持FP32优化器" (hyper-parallel issue)
+ */
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "hpo_impl.h"
+
+struct hpo_set_ {
+    hpo::SetView view{};
+    int32_t n_tensors = 0;
+    int32_t param_dtype = 0;
+    int32_t is_flat = 0;
+    int32_t device = 0;
+    int32_t max_group = 0;   /* largest group index in the set */
+    int32_t n_vector = 0;
+    int64_t numel = 0;
+    int64_t n_chunks = 0;
+    int64_t device_bytes = 0;
+    hpo::TensorDesc* d_tensors = nullptr;
+    hpo::Chunk* d_chunks = nullptr;
+    double* d_part_sum = nullptr;
+    int32_t* d_part_flag = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hpo_status fail(hpo_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+hpo_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(HPO_EHIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+hpo_status ok()
+{
+    g_last_error.clear();
+    return HPO_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t count_chunks(const int64_t* numel, int32_t n, int64_t ch)
+{
+    int64_t c = 0;
+    for (int32_t i = 0; i < n; ++i)
+        c += (numel[i] + ch - 1) / ch;
+    return c;
+}
+
+/* Largest power-of-two chunk in [kMinChunk, kMaxChunk] that still gives at
+ * least kTargetChunks workgroups per pass; small sets get the smallest. */
+int32_t choose_chunk(const int64_t* numel, int32_t n)
+{
+    for (int64_t ch = hpo::kMaxChunk; ch >= hpo::kMinChunk; ch >>= 1)
+        if (count_chunks(numel, n, ch) >= hpo::kTargetChunks)
+            return static_cast<int32_t>(ch);
+    return hpo::kMinChunk;
+}
+
+int64_t partial_bytes(int64_t n_chunks)
+{
+    const int64_t n = n_chunks > 0 ? n_chunks : 1;
+    return n * static_cast<int64_t>(sizeof(double) + sizeof(int32_t));
+}
+
+hpo_status check_sizes(int32_t n_tensors, const int64_t* numel)
+{
+    if (n_tensors < 0)
+        return fail(HPO_EINVAL, "n_tensors must be >= 0 (got %d)", n_tensors);
+    if (n_tensors > 0 && numel == nullptr)
+        return fail(HPO_EINVAL, "numel is NULL");
+    for (int32_t i = 0; i < n_tensors; ++i)
+        if (numel[i] < 0)
+            return fail(HPO_EINVAL, "numel[%d] = %lld is negative", i, (long long)numel[i]);
+    return HPO_OK;
+}
+
+/* Pointer rules for one tensor (see hpo.h). */
+hpo_status check_tensor(int32_t i, int32_t pdt, void* param, float* master, float* grad, float* m,
+                        float* v, int64_t numel)
+{
+    if (numel == 0)
+        return HPO_OK;
+    if (!master || !grad || !m || !v)
+        return fail(HPO_EINVAL, "tensor %d: main_param, main_grad, exp_avg and exp_avg_sq must be non-NULL", i);
+    if (!aligned(master, 4) || !aligned(grad, 4) || !aligned(m, 4) || !aligned(v, 4))
+        return fail(HPO_EINVAL, "tensor %d: fp32 pointers must be 4-byte aligned", i);
+    if (pdt == HPO_PARAM_BF16) {
+        if (!param)
+            return fail(HPO_EINVAL, "tensor %d: bf16 param pointer is NULL", i);
+        if (!aligned(param, 2))
+            return fail(HPO_EINVAL, "tensor %d: bf16 param pointer must be 2-byte aligned", i);
+    } else if (param != nullptr && param != static_cast<void*>(master)) {
+        return fail(HPO_EINVAL,
+                    "tensor %d: an fp32 param is its own master, so param must be NULL or equal main_param", i);
+    }
+    return HPO_OK;
+}
+
+hpo::TensorDesc make_desc(int32_t pdt, void* param, float* master, float* grad, float* m, float* v,
+                          int64_t numel, int32_t group)
+{
+    hpo::TensorDesc d{};
+    d.param = (pdt == HPO_PARAM_FP32) ? static_cast<void*>(master) : param;
+    d.master = master;
+    d.grad = grad;
+    d.exp_avg = m;
+    d.exp_avg_sq = v;
+    d.numel = numel;
+    d.group = group;
+    const bool p_ok = (pdt == HPO_PARAM_FP32) || aligned(d.param, 8);
+    d.vec_ok = (aligned(master, 16) && aligned(grad, 16) && aligned(m, 16) && aligned(v, 16) && p_ok) ? 1 : 0;
+    return d;
+}
+
+void build_chunks(const int64_t* numel, int32_t n, int64_t ch, std::vector<hpo::Chunk>& out)
+{
+    for (int32_t i = 0; i < n; ++i)
+        for (int64_t s = 0; s < numel[i]; s += ch) {
+            hpo::Chunk c;
+            c.tensor = i;
+            c.start = s;
+            c.len = static_cast<int32_t>(numel[i] - s < ch ? numel[i] - s : ch);
+            out.push_back(c);
+        }
+}
+
+void free_set(hpo_set s)
+{
+    if (!s)
+        return;
+    if (s->d_tensors) (void)hipFree(s->d_tensors);
+    if (s->d_chunks) (void)hipFree(s->d_chunks);
+    if (s->d_part_sum) (void)hipFree(s->d_part_sum);
+    if (s->d_part_flag) (void)hipFree(s->d_part_flag);
+    delete s;
+}
+
+hpo_status alloc_partials(hpo_set s)
+{
+    const int64_t n = s->n_chunks > 0 ? s->n_chunks : 1;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->d_part_sum), n * sizeof(double));
+    if (e != hipSuccess)
+        return fail(HPO_ENOMEM, "hipMalloc of %lld reduction partials: %s", (long long)n, hipGetErrorString(e));
+    e = hipMalloc(reinterpret_cast<void**>(&s->d_part_flag), n * sizeof(int32_t));
+    if (e != hipSuccess)
+        return fail(HPO_ENOMEM, "hipMalloc of %lld flag partials: %s", (long long)n, hipGetErrorString(e));
+    s->device_bytes += partial_bytes(s->n_chunks);
+    return HPO_OK;
+}
+
+hpo_status check_set(hpo_set s)
+{
+    if (!s)
+        return fail(HPO_EINVAL, "set is NULL");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != s->device)
+        return fail(HPO_EDEVICE, "current device %d is not the set's device %d", dev, s->device);
+    return HPO_OK;
+}
+
+hipStream_t as_stream(void* stream) { return static_cast<hipStream_t>(stream); }
+
+bool is_finite(double x) { return std::isfinite(x); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t hpo_abi_version(void) { return HPO_ABI_VERSION; }
+
+const char* hpo_last_error(void) { return g_last_error.c_str(); }
+
+const char* hpo_status_string(int32_t status)
+{
+    switch (status) {
+    case HPO_OK: return "HPO_OK";
+    case HPO_EINVAL: return "HPO_EINVAL";
+    case HPO_EDTYPE: return "HPO_EDTYPE";
+    case HPO_ENOMEM: return "HPO_ENOMEM";
+    case HPO_EHIP: return "HPO_EHIP";
+    case HPO_EDEVICE: return "HPO_EDEVICE";
+    default: return "unknown hpo_status";
+    }
+}
+
+hpo_status hpo_plan(int32_t n_tensors, const int64_t* numel, int32_t* out_chunk_elems,
+                    int64_t* out_n_chunks, int64_t* out_device_bytes)
+{
+    hpo_status st = check_sizes(n_tensors, numel);
+    if (st != HPO_OK)
+        return st;
+    const int32_t ch = choose_chunk(numel, n_tensors);
+    const int64_t nc = count_chunks(numel, n_tensors, ch);
+    if (out_chunk_elems) *out_chunk_elems = ch;
+    if (out_n_chunks) *out_n_chunks = nc;
+    if (out_device_bytes)
+        *out_device_bytes = static_cast<int64_t>(n_tensors) * sizeof(hpo::TensorDesc) +
+                            nc * static_cast<int64_t>(sizeof(hpo::Chunk)) + partial_bytes(nc);
+    return ok();
+}
+
+hpo_status hpo_plan_chunks(int32_t n_tensors, const int64_t* numel, int64_t n_chunks,
+                           int32_t* out_tensor, int64_t* out_start, int32_t* out_len)
+{
+    hpo_status st = check_sizes(n_tensors, numel);
+    if (st != HPO_OK)
+        return st;
+    const int32_t ch = choose_chunk(numel, n_tensors);
+    std::vector<hpo::Chunk> chunks;
+    build_chunks(numel, n_tensors, ch, chunks);
+    if (static_cast<int64_t>(chunks.size()) != n_chunks)
+        return fail(HPO_EINVAL, "n_chunks %lld does not match the plan (%zu)", (long long)n_chunks, chunks.size());
+    if (n_chunks > 0 && (!out_tensor || !out_start || !out_len))
+        return fail(HPO_EINVAL, "output arrays must be non-NULL");
+    for (size_t c = 0; c < chunks.size(); ++c) {
+        out_tensor[c] = chunks[c].tensor;
+        out_start[c] = chunks[c].start;
+        out_len[c] = chunks[c].len;
+    }
+    return ok();
+}
+
+hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dtype,
+                               void* const* param, float* const* main_param,
+                               float* const* main_grad, float* const* exp_avg,
+                               float* const* exp_avg_sq, const int64_t* numel,
+                               const int32_t* group_index, void* stream)
+{
+    if (!out)
+        return fail(HPO_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (param_dtype != HPO_PARAM_BF16 && param_dtype != HPO_PARAM_FP32)
+        return fail(HPO_EDTYPE, "param dtype %d is not supported (bf16 = 0 with an fp32 master, or fp32 = 1)", param_dtype);
+    hpo_status st = check_sizes(n_tensors, numel);
+    if (st != HPO_OK)
+        return st;
+    if (n_tensors > 0 && (!main_param || !main_grad || !exp_avg || !exp_avg_sq))
+        return fail(HPO_EINVAL, "pointer arrays must be non-NULL");
+    if (n_tensors > 0 && param_dtype == HPO_PARAM_BF16 && !param)
+        return fail(HPO_EINVAL, "param array is NULL for a bf16 set");
+    int32_t max_group = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        void* p = param ? param[i] : nullptr;
+        st = check_tensor(i, param_dtype, p, main_param[i], main_grad[i], exp_avg[i], exp_avg_sq[i], numel[i]);
+        if (st != HPO_OK)
+            return st;
+        const int32_t g = group_index ? group_index[i] : 0;
+        if (g < 0 || g >= HPO_MAX_GROUPS)
+            return fail(HPO_EINVAL, "group_index[%d] = %d is outside [0, %d)", i, g, HPO_MAX_GROUPS);
+        if (g > max_group)
+            max_group = g;
+    }
+    const int32_t ch = choose_chunk(numel, n_tensors);
+    const int64_t nc = count_chunks(numel, n_tensors, ch);
+    if (nc > 0x7FFFFFFFLL)
+        return fail(HPO_EINVAL, "set needs %lld chunks, more than one launch can hold", (long long)nc);
+
+    hpo_set s = new (std::nothrow) hpo_set_;
+    if (!s)
+        return fail(HPO_ENOMEM, "host allocation failed");
+    hipError_t e = hipGetDevice(&s->device);
+    if (e != hipSuccess) {
+        free_set(s);
+        return hip_fail(e, "hipGetDevice");
+    }
+    s->n_tensors = n_tensors;
+    s->param_dtype = param_dtype;
+    s->is_flat = 0;
+    s->max_group = max_group;
+    s->n_chunks = nc;
+
+    std::vector<hpo::TensorDesc> descs(static_cast<size_t>(n_tensors));
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        descs[i] = make_desc(param_dtype, param ? param[i] : nullptr, main_param[i], main_grad[i], exp_avg[i],
+                             exp_avg_sq[i], numel[i], group_index ? group_index[i] : 0);
+        s->numel += numel[i];
+        s->n_vector += descs[i].vec_ok;
+    }
+    std::vector<hpo::Chunk> chunks;
+    chunks.reserve(static_cast<size_t>(nc));
+    build_chunks(numel, n_tensors, ch, chunks);
+
+    const size_t td_bytes = descs.size() * sizeof(hpo::TensorDesc);
+    const size_t ck_bytes = chunks.size() * sizeof(hpo::Chunk);
+    if (td_bytes) {
+        e = hipMalloc(reinterpret_cast<void**>(&s->d_tensors), td_bytes);
+        if (e != hipSuccess) { free_set(s); return fail(HPO_ENOMEM, "hipMalloc tensor table: %s", hipGetErrorString(e)); }
+    }
+    if (ck_bytes) {
+        e = hipMalloc(reinterpret_cast<void**>(&s->d_chunks), ck_bytes);
+        if (e != hipSuccess) { free_set(s); return fail(HPO_ENOMEM, "hipMalloc chunk table: %s", hipGetErrorString(e)); }
+    }
+    s->device_bytes = static_cast<int64_t>(td_bytes + ck_bytes);
+    st = alloc_partials(s);
+    if (st != HPO_OK) { free_set(s); return st; }
+    if (td_bytes) {
+        e = hipMemcpyAsync(s->d_tensors, descs.data(), td_bytes, hipMemcpyHostToDevice, as_stream(stream));
+        if (e != hipSuccess) { free_set(s); return hip_fail(e, "upload tensor table"); }
+    }
+    if (ck_bytes) {
+        e = hipMemcpyAsync(s->d_chunks, chunks.data(), ck_bytes, hipMemcpyHostToDevice, as_stream(stream));
+        if (e != hipSuccess) { free_set(s); return hip_fail(e, "upload chunk table"); }
+    }
+    e = hipStreamSynchronize(as_stream(stream));
+    if (e != hipSuccess) { free_set(s); return hip_fail(e, "hipStreamSynchronize after table upload"); }
+
+    s->view.tensors = s->d_tensors;
+    s->view.chunks = s->d_chunks;
+    s->view.chunk_elems = ch;
+    s->view.is_flat = 0;
+    s->view.param_dtype = param_dtype;
+    *out = s;
+    return ok();
+}
+
+hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
+                               float* main_param, float* main_grad, float* exp_avg,
+                               float* exp_avg_sq, void* stream)
+{
+    (void)stream;
+    if (!out)
+        return fail(HPO_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (param_dtype != HPO_PARAM_BF16 && param_dtype != HPO_PARAM_FP32)
+        return fail(HPO_EDTYPE, "param dtype %d is not supported (bf16 = 0 with an fp32 master, or fp32 = 1)", param_dtype);
+    hpo_status st = check_sizes(1, &numel);
+    if (st != HPO_OK)
+        return st;
+    st = check_tensor(0, param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel);
+    if (st != HPO_OK)
+        return st;
+    const int32_t ch = choose_chunk(&numel, 1);
+    const int64_t nc = count_chunks(&numel, 1, ch);
+    if (nc > 0x7FFFFFFFLL)
+        return fail(HPO_EINVAL, "set needs %lld chunks, more than one launch can hold", (long long)nc);
+
+    hpo_set s = new (std::nothrow) hpo_set_;
+    if (!s)
+        return fail(HPO_ENOMEM, "host allocation failed");
+    hipError_t e = hipGetDevice(&s->device);
+    if (e != hipSuccess) {
+        free_set(s);
+        return hip_fail(e, "hipGetDevice");
+    }
+    s->n_tensors = 1;
+    s->param_dtype = param_dtype;
+    s->is_flat = 1;
+    s->numel = numel;
+    s->n_chunks = nc;
+    s->view.flat = make_desc(param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0);
+    s->n_vector = s->view.flat.vec_ok;
+    s->view.chunk_elems = ch;
+    s->view.is_flat = 1;
+    s->view.param_dtype = param_dtype;
+    st = alloc_partials(s);
+    if (st != HPO_OK) { free_set(s); return st; }
+    *out = s;
+    return ok();
+}
+
+hpo_status hpo_set_destroy(hpo_set s)
+{
+    if (!s)
+        return ok();
+    hipError_t e = hipDeviceSynchronize();
+    free_set(s);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipDeviceSynchronize before freeing the set");
+    return ok();
+}
+
+hpo_status hpo_set_info(hpo_set s, hpo_set_info_t* out)
+{
+    if (!s || !out)
+        return fail(HPO_EINVAL, "set and out must be non-NULL");
+    out->n_tensors = s->n_tensors;
+    out->param_dtype = s->param_dtype;
+    out->is_flat = s->is_flat;
+    out->chunk_elems = static_cast<int32_t>(s->view.chunk_elems);
+    out->numel = s->numel;
+    out->n_chunks = s->n_chunks;
+    out->device_bytes = s->device_bytes;
+    out->device = s->device;
+    out->n_vector = s->n_vector;
+    return ok();
+}
+
+hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_inf, void* stream)
+{
+    hpo_status st = check_set(s);
+    if (st != HPO_OK)
+        return st;
+    if (!d_found_inf)
+        return fail(HPO_EINVAL, "d_found_inf is NULL");
+    if (!std::isfinite(inv_scale))
+        return fail(HPO_EINVAL, "inv_scale must be finite");
+    const hpo::GradPass pass = (inv_scale == 1.0f) ? hpo::GradPass::kCheck : hpo::GradPass::kUnscale;
+    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, pass, inv_scale, s->d_part_sum,
+                                         s->d_part_flag, as_stream(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "launch unscale/check pass");
+    if (s->n_chunks > 0) {
+        e = hpo::launch_finalize(nullptr, s->d_part_flag, s->n_chunks, nullptr, d_found_inf, as_stream(stream));
+        if (e != hipSuccess)
+            return hip_fail(e, "launch flag finalize");
+    }
+    return ok();
+}
+
+hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32_t* d_found_inf,
+                                void* stream)
+{
+    hpo_status st = check_set(s);
+    if (st != HPO_OK)
+        return st;
+    if (!d_norm)
+        return fail(HPO_EINVAL, "d_norm is NULL");
+    if (!std::isfinite(inv_scale))
+        return fail(HPO_EINVAL, "inv_scale must be finite");
+    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, hpo::GradPass::kNorm, inv_scale,
+                                         s->d_part_sum, s->d_part_flag, as_stream(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "launch norm pass");
+    /* with no chunks the finalizer still runs, so the norm reads 0 */
+    e = hpo::launch_finalize(s->d_part_sum, s->d_part_flag, s->n_chunks, d_norm, d_found_inf,
+                             as_stream(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "launch norm finalize");
+    return ok();
+}
+
+hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups,
+                          int32_t n_groups, int64_t t, float inv_scale, double max_norm,
+                          const float* d_norm, const int32_t* d_found_inf, void* stream)
+{
+    hpo_status st = check_set(s);
+    if (st != HPO_OK)
+        return st;
+    if (!cfg)
+        return fail(HPO_EINVAL, "cfg is NULL");
+    if (cfg->mode != HPO_ADAMW && cfg->mode != HPO_ADAM_L2)
+        return fail(HPO_EINVAL, "mode %d is neither HPO_ADAMW (0) nor HPO_ADAM_L2 (1)", cfg->mode);
+    if (!(cfg->beta1 >= 0.0 && cfg->beta1 < 1.0) || !(cfg->beta2 >= 0.0 && cfg->beta2 < 1.0))
+        return fail(HPO_EINVAL, "betas must lie in [0, 1) (got %g, %g)", cfg->beta1, cfg->beta2);
+    if (!(cfg->eps >= 0.0) || !is_finite(cfg->eps))
+        return fail(HPO_EINVAL, "eps must be finite and >= 0 (got %g)", cfg->eps);
+    if (n_groups < 1 || n_groups > HPO_MAX_GROUPS)
+        return fail(HPO_EINVAL, "n_groups must be in [1, %d] (got %d)", HPO_MAX_GROUPS, n_groups);
+    if (!groups)
+        return fail(HPO_EINVAL, "groups is NULL");
+    if (s->max_group >= n_groups)
+        return fail(HPO_EINVAL, "the set uses group %d but only %d groups were given", s->max_group, n_groups);
+    for (int32_t k = 0; k < n_groups; ++k)
+        if (!is_finite(groups[k].lr) || !is_finite(groups[k].weight_decay))
+            return fail(HPO_EINVAL, "group %d: lr and weight_decay must be finite", k);
+    if (t < 1)
+        return fail(HPO_EINVAL, "t is the 1-based count of applied steps, must be >= 1 (got %lld)", (long long)t);
+    if (!std::isfinite(inv_scale))
+        return fail(HPO_EINVAL, "inv_scale must be finite");
+    if (std::isnan(max_norm))
+        return fail(HPO_EINVAL, "max_norm is NaN");
+    if (max_norm > 0.0 && !d_norm)
+        return fail(HPO_EINVAL, "clipping (max_norm > 0) needs d_norm");
+
+    /* Per-step scalars: binary64 once, rounded to fp32 once. */
+    hpo::AdamScalars sc{};
+    sc.inv_scale = inv_scale;
+    sc.b1 = static_cast<float>(cfg->beta1);
+    sc.b2 = static_cast<float>(cfg->beta2);
+    sc.c1 = static_cast<float>(1.0 - cfg->beta1);
+    sc.c2 = static_cast<float>(1.0 - cfg->beta2);
+    sc.bc1 = static_cast<float>(1.0 - std::pow(cfg->beta1, static_cast<double>(t)));
+    sc.bc2 = static_cast<float>(1.0 - std::pow(cfg->beta2, static_cast<double>(t)));
+    sc.eps = static_cast<float>(cfg->eps);
+    sc.max_norm = max_norm;
+    sc.d_norm = d_norm;
+    sc.d_found = d_found_inf;
+    for (int32_t k = 0; k < n_groups; ++k) {
+        sc.lr[k] = static_cast<float>(groups[k].lr);
+        sc.wd[k] = static_cast<float>(groups[k].weight_decay);
+    }
+    hipError_t e = hpo::launch_adam(s->view, s->n_chunks, cfg->mode, sc, as_stream(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "launch adam update");
+    return ok();
+}
+
+hpo_status hpo_copy_main_to_model(hpo_set s, void* stream)
+{
+    hpo_status st = check_set(s);
+    if (st != HPO_OK)
+        return st;
+    if (s->param_dtype == HPO_PARAM_FP32)
+        return ok();
+    hipError_t e = hpo::launch_copy_main_to_model(s->view, s->n_chunks, as_stream(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "launch master->model copy");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+/*
+ * hpo_impl.h -- layouts shared by libhpo's host planner (hpo_api.cpp) and its
+ * gfx950 kernels (hpo_kernels.hip).  Not part of the public ABI.
+ */
+#ifndef HPO_IMPL_H
+#define HPO_IMPL_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "hpo.h"
+
+namespace hpo {
+
+/* Workgroup size of every streaming kernel: 4 wavefronts of 64 lanes. */
+constexpr int kBlock = 256;
+/* Elements one lane handles per vector access (one 16-byte fp32 load). */
+constexpr int kVec = 4;
+/* Chunk sizes the planner chooses from (powers of two, multiples of
+ * kBlock * kVec so that every chunk start keeps 16-byte alignment). */
+constexpr int kMinChunk = 1 << 12;
+constexpr int kMaxChunk = 1 << 16;
+/* Aim for at least this many workgroups per pass: 256 CUs x 8. */
+constexpr int64_t kTargetChunks = 2048;
+/* Workgroup size of the single-workgroup reduction finalizer. */
+constexpr int kFinalBlock = 1024;
+
+/* One tensor of a set, as the kernels see it (64 bytes). */
+struct TensorDesc {
+    void* param;       /* bf16 model param; == master for fp32 sets */
+    float* master;
+    float* grad;
+    float* exp_avg;
+    float* exp_avg_sq;
+    int64_t numel;
+    int32_t group;
+    int32_t vec_ok;    /* all five pointers allow 16-byte (bf16: 8-byte) access */
+    int64_t reserved;  /* pads the descriptor to 64 bytes */
+};
+static_assert(sizeof(TensorDesc) == 64, "TensorDesc layout");
+
+/* One chunk: a contiguous range of one tensor, processed by one workgroup. */
+struct Chunk {
+    int32_t tensor;
+    int32_t len;       /* <= chunk_elems */
+    int64_t start;     /* first element, a multiple of chunk_elems */
+};
+static_assert(sizeof(Chunk) == 16, "Chunk layout");
+
+/* Where a pass finds its tensors: a flat set carries its one descriptor by
+ * value and computes chunk ranges from blockIdx; a list set reads both
+ * tables from device memory. */
+struct SetView {
+    TensorDesc flat;            /* flat sets only */
+    const TensorDesc* tensors;  /* list sets only */
+    const Chunk* chunks;        /* list sets only */
+    int64_t chunk_elems;
+    int32_t is_flat;
+    int32_t param_dtype;
+};
+
+/* Per-step scalars of the update, all formed on the host in binary64 and
+ * rounded to fp32 once. */
+struct AdamScalars {
+    float inv_scale;
+    float b1, b2, c1, c2;   /* beta1, beta2, 1 - beta1, 1 - beta2 */
+    float bc1, bc2;         /* 1 - beta1^t, 1 - beta2^t */
+    float eps;
+    double max_norm;        /* <= 0: no clipping */
+    const float* d_norm;    /* device fp32 norm (read when max_norm > 0) */
+    const int32_t* d_found; /* device skip flag, nullable */
+    float lr[HPO_MAX_GROUPS];
+    float wd[HPO_MAX_GROUPS];
+};
+
+enum class GradPass : int { kNorm = 0, kCheck = 1, kUnscale = 2 };
+
+/* Launchers (hpo_kernels.hip).  Each enqueues on `stream` and returns the
+ * launch status. */
+hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, GradPass pass, float inv_scale,
+                            double* part_sum, int32_t* part_flag, hipStream_t stream);
+hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
+                           float* d_norm, int32_t* d_found, hipStream_t stream);
+hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+                       hipStream_t stream);
+hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream);
+
+}  // namespace hpo
+
+#endif /* HPO_IMPL_H */

@@ -1,0 +1,364 @@
+/*
+ * hpo_kernels.hip -- gfx950 kernels of the mixed-precision AdamW step.
+ *
+ * Sources (web pages):
+ *   [OPT-INFRA]  "02 · Optimizer：算法与 infra" (llm-infra-atlas, train/02_optimizer)
+ *   [FP32-RFC]   "支持FP32优化器" (hyper-parallel issue)
+ *
+ * The whole path is elementwise plus one global sum, so it is bound by HBM
+ * bandwidth, not by the matrix cores: no MFMA here.  Every pass walks the
+ * set's chunk table with one 256-lane workgroup (4 wavefronts of 64) per
+ * chunk of 4096..65536 contiguous elements of one tensor.  On tensors whose
+ * pointers are 16-byte aligned each lane moves 16 bytes per fp32 array per
+ * access (global_load_dwordx4), a wavefront 1 KB contiguous, and the bf16
+ * write-back is 8 bytes per lane (512 B per wavefront), so every access
+ * covers whole cache lines.  Chunk tails and unaligned tensors take an
+ * element-at-a-time path.
+ *
+ * Passes:
+ *   grad pass   one read of the stored grads: non-finite flag and binary64
+ *               sum of squares of the unscaled grads per workgroup
+ *               (wavefront shuffles, then LDS across the 4 wavefronts);
+ *               or the pages' in-place unscale.             4 or 8 B/elem
+ *   finalize    one workgroup: fixed-order sum of the partials, sqrt, flag.
+ *   adam        clip + Adam/AdamW + bf16 RNE write-back in registers:
+ *               read grad, master, m, v (16 B), write master, m, v (12 B)
+ *               and the bf16 param (2 B).                  30 B/elem
+ *   copy        master -> bf16 param alone.                 6 B/elem
+ *
+ * Floating point: the library is built with -ffp-contract=off, so every
+ * multiply and add below rounds on its own, in the order written; fp32
+ * division and sqrtf are HIP's correctly rounded ones and fp32 denormals are
+ * kept.  This reproduces, operation for operation, the formulas of
+ * [OPT-INFRA] §2 (moments, bias correction, eps outside the root) and §3
+ * (decoupled decay or the L2 term), with the clip of §11.1 in front.
+ */
+#include <hip/hip_runtime.h>
+
+#include "hpo_impl.h"
+
+namespace hpo {
+namespace {
+
+struct Range {
+    TensorDesc d;
+    int64_t start;
+    int64_t len;
+};
+
+template <bool FLAT>
+__device__ __forceinline__ Range chunk_range(const SetView& sv)
+{
+    Range r;
+    if constexpr (FLAT) {
+        r.d = sv.flat;
+        r.start = static_cast<int64_t>(blockIdx.x) * sv.chunk_elems;
+        const int64_t rem = r.d.numel - r.start;
+        r.len = rem < sv.chunk_elems ? rem : sv.chunk_elems;
+    } else {
+        const Chunk c = sv.chunks[blockIdx.x];
+        r.d = sv.tensors[c.tensor];
+        r.start = c.start;
+        r.len = c.len;
+    }
+    return r;
+}
+
+/* fp32 -> bf16 bits, IEEE round to nearest, ties to even ([OPT-INFRA] §9.2
+ * write-back; [FP32-RFC] case 1: the model param equals the bf16 image of the
+ * master after every step).  Adding 0x7FFF plus the kept part's lowest bit to
+ * the fp32 bits and dropping the low half rounds up exactly when the dropped
+ * half exceeds 0x8000, or equals it with an odd kept part; a carry ripples
+ * into the exponent (up to infinity).  NaN becomes the quiet NaN 0x7FC0 with
+ * the input's sign. */
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+}
+
+/* Binary64 sum over a workgroup of NT lanes: shuffle tree inside each
+ * wavefront, then wavefront 0 adds the per-wavefront sums in index order.
+ * The order is fixed by the lane layout alone, so results are reproducible. */
+template <int NT>
+__device__ __forceinline__ double block_sum(double x)
+{
+    constexpr int kWaves = NT / 64;
+    __shared__ double wsum[kWaves];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        x += __shfl_down(x, off, 64);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    if (lane == 0)
+        wsum[wave] = x;
+    __syncthreads();
+    double tot = 0.0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            tot += wsum[w];
+    }
+    return tot; /* valid in thread 0 */
+}
+
+/* ---------------------------------------------------------------------- */
+/* grad pass: non-finite flag + sum of squares, or in-place unscale        */
+/* ---------------------------------------------------------------------- */
+template <GradPass PASS>
+__device__ __forceinline__ void grad_elem(float& G, float inv, double& acc, int& bad)
+{
+    bad |= !__builtin_isfinite(G);
+    if constexpr (PASS == GradPass::kNorm) {
+        const double g = static_cast<double>(G * inv);
+        acc = __builtin_fma(g, g, acc); /* g*g is exact in binary64, so this is one rounding of acc + g^2 */
+    } else if constexpr (PASS == GradPass::kUnscale) {
+        G = G * inv;
+    }
+}
+
+template <bool FLAT, GradPass PASS>
+__global__ __launch_bounds__(kBlock) void k_grad_pass(SetView sv, float inv, double* part_sum,
+                                                      int32_t* part_flag)
+{
+    const Range r = chunk_range<FLAT>(sv);
+    float* __restrict__ G = r.d.grad + r.start;
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    int bad = 0;
+    int64_t done = 0;
+    if (r.d.vec_ok) {
+        const int64_t nv = r.len / kVec;
+        float4* __restrict__ G4 = reinterpret_cast<float4*>(G);
+        for (int64_t i = tid; i < nv; i += kBlock) {
+            float4 x = G4[i];
+            grad_elem<PASS>(x.x, inv, acc, bad);
+            grad_elem<PASS>(x.y, inv, acc, bad);
+            grad_elem<PASS>(x.z, inv, acc, bad);
+            grad_elem<PASS>(x.w, inv, acc, bad);
+            if constexpr (PASS == GradPass::kUnscale)
+                G4[i] = x;
+        }
+        done = nv * kVec;
+    }
+    for (int64_t i = done + tid; i < r.len; i += kBlock) {
+        float x = G[i];
+        grad_elem<PASS>(x, inv, acc, bad);
+        if constexpr (PASS == GradPass::kUnscale)
+            G[i] = x;
+    }
+    const int any_bad = __syncthreads_or(bad);
+    if constexpr (PASS == GradPass::kNorm) {
+        const double tot = block_sum<kBlock>(acc);
+        if (tid == 0)
+            part_sum[blockIdx.x] = tot;
+    }
+    if (tid == 0)
+        part_flag[blockIdx.x] = any_bad ? 1 : 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* finalize: one workgroup, fixed-order sum of the per-chunk partials       */
+/* ---------------------------------------------------------------------- */
+__global__ __launch_bounds__(kFinalBlock) void k_finalize(const double* part_sum,
+                                                          const int32_t* part_flag, int64_t n,
+                                                          float* d_norm, int32_t* d_found)
+{
+    double acc = 0.0;
+    int bad = 0;
+    for (int64_t i = threadIdx.x; i < n; i += kFinalBlock) {
+        if (d_norm != nullptr)
+            acc += part_sum[i];
+        bad |= part_flag[i];
+    }
+    const int any_bad = __syncthreads_or(bad);
+    const double tot = block_sum<kFinalBlock>(acc);
+    if (threadIdx.x == 0) {
+        if (d_norm != nullptr)
+            *d_norm = static_cast<float>(sqrt(tot));
+        if (d_found != nullptr && any_bad)
+            *d_found = 1;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* adam: clip + Adam/AdamW + bf16 write-back                              */
+/* ---------------------------------------------------------------------- */
+template <int MODE>
+__device__ __forceinline__ void adam_elem(float G, float& th, float& m, float& v,
+                                          const AdamScalars& sc, bool clip, float C, float lr,
+                                          float wd)
+{
+    float g = G * sc.inv_scale;          /* unscale ([OPT-INFRA] §10.2) */
+    if (clip)
+        g = g * C;                       /* clip ([OPT-INFRA] §11.1) */
+    if constexpr (MODE == HPO_ADAM_L2)
+        g = g + wd * th;                 /* L2 term joins the gradient ([OPT-INFRA] §3) */
+    m = sc.b1 * m + sc.c1 * g;           /* first moment ([OPT-INFRA] §2) */
+    v = sc.b2 * v + sc.c2 * (g * g);     /* raw second moment */
+    const float mh = m / sc.bc1;         /* bias corrections */
+    const float vh = v / sc.bc2;
+    const float u = mh / (sqrtf(vh) + sc.eps); /* eps outside the root */
+    if constexpr (MODE == HPO_ADAMW)
+        th = th - lr * (u + wd * th);    /* decoupled decay ([OPT-INFRA] §3) */
+    else
+        th = th - lr * u;
+}
+
+template <bool FLAT, int PDT, int MODE>
+__global__ __launch_bounds__(kBlock) void k_adam(SetView sv, AdamScalars sc)
+{
+    if (sc.d_found != nullptr && *sc.d_found != 0)
+        return; /* found_inf: the whole step is skipped ([OPT-INFRA] §10.2) */
+    bool clip = false;
+    float C = 1.0f;
+    if (sc.max_norm > 0.0) {
+        const double c = sc.max_norm / (static_cast<double>(*sc.d_norm) + 1e-6);
+        if (c < 1.0) {
+            clip = true;
+            C = static_cast<float>(c);
+        }
+    }
+    const Range r = chunk_range<FLAT>(sv);
+    const float lr = sc.lr[r.d.group];
+    const float wd = sc.wd[r.d.group];
+    const float* __restrict__ G = r.d.grad + r.start;
+    float* __restrict__ T = r.d.master + r.start;
+    float* __restrict__ M = r.d.exp_avg + r.start;
+    float* __restrict__ V = r.d.exp_avg_sq + r.start;
+    uint16_t* __restrict__ P = static_cast<uint16_t*>(r.d.param) + r.start;
+    const int tid = threadIdx.x;
+    int64_t done = 0;
+    if (r.d.vec_ok) {
+        const int64_t nv = r.len / kVec;
+        const float4* __restrict__ G4 = reinterpret_cast<const float4*>(G);
+        float4* __restrict__ T4 = reinterpret_cast<float4*>(T);
+        float4* __restrict__ M4 = reinterpret_cast<float4*>(M);
+        float4* __restrict__ V4 = reinterpret_cast<float4*>(V);
+        uint2* __restrict__ P4 = reinterpret_cast<uint2*>(P);
+        for (int64_t i = tid; i < nv; i += kBlock) {
+            const float4 g = G4[i];
+            float4 th = T4[i];
+            float4 m = M4[i];
+            float4 v = V4[i];
+            adam_elem<MODE>(g.x, th.x, m.x, v.x, sc, clip, C, lr, wd);
+            adam_elem<MODE>(g.y, th.y, m.y, v.y, sc, clip, C, lr, wd);
+            adam_elem<MODE>(g.z, th.z, m.z, v.z, sc, clip, C, lr, wd);
+            adam_elem<MODE>(g.w, th.w, m.w, v.w, sc, clip, C, lr, wd);
+            T4[i] = th;
+            M4[i] = m;
+            V4[i] = v;
+            if constexpr (PDT == HPO_PARAM_BF16)
+                P4[i] = make_uint2(pack_bf16x2(th.x, th.y), pack_bf16x2(th.z, th.w));
+        }
+        done = nv * kVec;
+    }
+    for (int64_t i = done + tid; i < r.len; i += kBlock) {
+        float th = T[i], m = M[i], v = V[i];
+        adam_elem<MODE>(G[i], th, m, v, sc, clip, C, lr, wd);
+        T[i] = th;
+        M[i] = m;
+        V[i] = v;
+        if constexpr (PDT == HPO_PARAM_BF16)
+            P[i] = static_cast<uint16_t>(bf16_rne_bits(th));
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* master -> model copy                                                   */
+/* ---------------------------------------------------------------------- */
+template <bool FLAT>
+__global__ __launch_bounds__(kBlock) void k_copy_main_to_model(SetView sv)
+{
+    const Range r = chunk_range<FLAT>(sv);
+    const float* __restrict__ T = r.d.master + r.start;
+    uint16_t* __restrict__ P = static_cast<uint16_t*>(r.d.param) + r.start;
+    const int tid = threadIdx.x;
+    int64_t done = 0;
+    if (r.d.vec_ok) {
+        const int64_t nv = r.len / kVec;
+        const float4* __restrict__ T4 = reinterpret_cast<const float4*>(T);
+        uint2* __restrict__ P4 = reinterpret_cast<uint2*>(P);
+        for (int64_t i = tid; i < nv; i += kBlock) {
+            const float4 th = T4[i];
+            P4[i] = make_uint2(pack_bf16x2(th.x, th.y), pack_bf16x2(th.z, th.w));
+        }
+        done = nv * kVec;
+    }
+    for (int64_t i = done + tid; i < r.len; i += kBlock)
+        P[i] = static_cast<uint16_t>(bf16_rne_bits(T[i]));
+}
+
+template <typename... Args>
+hipError_t launch(void (*kernel)(Args...), int64_t grid, int block, hipStream_t stream,
+                  Args... args)
+{
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<uint32_t>(grid)),
+                           dim3(block), argv, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, GradPass pass, float inv_scale,
+                            double* part_sum, int32_t* part_flag, hipStream_t stream)
+{
+    if (n_chunks == 0)
+        return hipSuccess;
+    const bool flat = sv.is_flat != 0;
+    switch (pass) {
+    case GradPass::kNorm:
+        return flat ? launch(k_grad_pass<true, GradPass::kNorm>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag)
+                    : launch(k_grad_pass<false, GradPass::kNorm>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag);
+    case GradPass::kCheck:
+        return flat ? launch(k_grad_pass<true, GradPass::kCheck>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag)
+                    : launch(k_grad_pass<false, GradPass::kCheck>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag);
+    case GradPass::kUnscale:
+        return flat ? launch(k_grad_pass<true, GradPass::kUnscale>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag)
+                    : launch(k_grad_pass<false, GradPass::kUnscale>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
+                           float* d_norm, int32_t* d_found, hipStream_t stream)
+{
+    return launch(k_finalize, 1, kFinalBlock, stream, part_sum, part_flag, n_parts, d_norm, d_found);
+}
+
+hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+                       hipStream_t stream)
+{
+    if (n_chunks == 0)
+        return hipSuccess;
+    const bool flat = sv.is_flat != 0;
+    const bool bf16 = sv.param_dtype == HPO_PARAM_BF16;
+    const bool adamw = mode == HPO_ADAMW;
+#define HPO_ADAM_LAUNCH(F, P, M) launch(k_adam<F, P, M>, n_chunks, kBlock, stream, sv, sc)
+    if (flat) {
+        if (bf16)
+            return adamw ? HPO_ADAM_LAUNCH(true, HPO_PARAM_BF16, HPO_ADAMW) : HPO_ADAM_LAUNCH(true, HPO_PARAM_BF16, HPO_ADAM_L2);
+        return adamw ? HPO_ADAM_LAUNCH(true, HPO_PARAM_FP32, HPO_ADAMW) : HPO_ADAM_LAUNCH(true, HPO_PARAM_FP32, HPO_ADAM_L2);
+    }
+    if (bf16)
+        return adamw ? HPO_ADAM_LAUNCH(false, HPO_PARAM_BF16, HPO_ADAMW) : HPO_ADAM_LAUNCH(false, HPO_PARAM_BF16, HPO_ADAM_L2);
+    return adamw ? HPO_ADAM_LAUNCH(false, HPO_PARAM_FP32, HPO_ADAMW) : HPO_ADAM_LAUNCH(false, HPO_PARAM_FP32, HPO_ADAM_L2);
+#undef HPO_ADAM_LAUNCH
+}
+
+hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream)
+{
+    if (n_chunks == 0)
+        return hipSuccess;
+    return sv.is_flat ? launch(k_copy_main_to_model<true>, n_chunks, kBlock, stream, sv)
+                      : launch(k_copy_main_to_model<false>, n_chunks, kBlock, stream, sv);
+}
+
+}  // namespace hpo

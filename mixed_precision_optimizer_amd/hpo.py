@@ -1,0 +1,300 @@
+"""ctypes binding of libhpo (include/hpo.h): argument marshalling only.
+
+Every entry point keeps its C name and argument order; torch tensors are
+accepted where the C call takes a device pointer, and `stream=None` means
+torch's current stream on the current device.  Every step of the optimizer
+runs in the HIP library; nothing here computes on the data.  If libhpo.so is
+missing the first call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhpo.so")
+
+HPO_OK, HPO_EINVAL, HPO_EDTYPE, HPO_ENOMEM, HPO_EHIP, HPO_EDEVICE = 0, -1, -2, -3, -4, -5
+HPO_PARAM_BF16, HPO_PARAM_FP32 = 0, 1
+HPO_ADAMW, HPO_ADAM_L2 = 0, 1
+HPO_MAX_GROUPS = 16
+
+
+class HpoError(RuntimeError):
+    def __init__(self, status: int, call: str, message: str):
+        super().__init__(f"{call} failed with {status}: {message}")
+        self.status = status
+
+
+class hpo_adam_cfg(ctypes.Structure):
+    _fields_ = [("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("mode", ctypes.c_int32)]
+
+
+class hpo_group(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class hpo_set_info_t(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int32), ("param_dtype", ctypes.c_int32),
+                ("is_flat", ctypes.c_int32), ("chunk_elems", ctypes.c_int32),
+                ("numel", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
+                ("device_bytes", ctypes.c_int64), ("device", ctypes.c_int32),
+                ("n_vector", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+# name -> (restype, argtypes), exactly as declared in include/hpo.h
+SIGNATURES = {
+    "hpo_set_create_list": (_I32, [ctypes.POINTER(_P), _I32, _I32, _PP, _PP, _PP, _PP, _PP,
+                                   ctypes.POINTER(_I64), ctypes.POINTER(_I32), _P]),
+    "hpo_set_create_flat": (_I32, [ctypes.POINTER(_P), _I64, _I32, _P, _P, _P, _P, _P, _P]),
+    "hpo_set_destroy": (_I32, [_P]),
+    "hpo_set_info": (_I32, [_P, ctypes.POINTER(hpo_set_info_t)]),
+    "hpo_unscale_check_inf": (_I32, [_P, ctypes.c_float, _P, _P]),
+    "hpo_grad_global_norm": (_I32, [_P, ctypes.c_float, _P, _P, _P]),
+    "hpo_adamw_step": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32,
+                              _I64, ctypes.c_float, ctypes.c_double, _P, _P, _P]),
+    "hpo_copy_main_to_model": (_I32, [_P, _P]),
+    "hpo_plan": (_I32, [_I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32), ctypes.POINTER(_I64),
+                        ctypes.POINTER(_I64)]),
+    "hpo_plan_chunks": (_I32, [_I32, ctypes.POINTER(_I64), _I64, ctypes.POINTER(_I32),
+                               ctypes.POINTER(_I64), ctypes.POINTER(_I32)]),
+    "hpo_last_error": (ctypes.c_char_p, []),
+    "hpo_status_string": (ctypes.c_char_p, [_I32]),
+    "hpo_abi_version": (_I32, []),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libhpo.so (after torch, so that both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m mixed_precision_optimizer_amd.build` "
+                               "(or __graft_entry__.build()). There is no non-HIP fallback.")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, call: str) -> None:
+    if status != HPO_OK:
+        msg = load().hpo_last_error().decode(errors="replace")
+        raise HpoError(status, call, msg)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(0)
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t: torch.Tensor, dtype, what: str, i: int) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{what}[{i}] must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{what}[{i}] must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}[{i}] must be contiguous")
+
+
+def param_dtype_code(dtype) -> int:
+    """bf16 -> HPO_PARAM_BF16, fp32 -> HPO_PARAM_FP32; other dtypes (fp16
+    included) go to the library as an unsupported code, which it rejects."""
+    if dtype == torch.bfloat16:
+        return HPO_PARAM_BF16
+    if dtype == torch.float32:
+        return HPO_PARAM_FP32
+    return 100 + {torch.float16: 0, torch.float64: 1}.get(dtype, 9)
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+class HpoSet:
+    """Owner of one hpo_set handle; keeps the tensors it points at alive."""
+
+    def __init__(self, handle: ctypes.c_void_p, keepalive):
+        self.handle = handle
+        self._keep = keepalive
+
+    def info(self) -> hpo_set_info_t:
+        return hpo_set_info(self)
+
+    def close(self) -> None:
+        if self.handle:
+            _check(load().hpo_set_destroy(self.handle), "hpo_set_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            if self.handle:
+                load().hpo_set_destroy(self.handle)
+        except Exception:
+            pass
+
+
+def hpo_set_create_list(params: Sequence[Optional[torch.Tensor]], main_params: Sequence[torch.Tensor],
+                        main_grads: Sequence[torch.Tensor], exp_avgs: Sequence[torch.Tensor],
+                        exp_avg_sqs: Sequence[torch.Tensor], group_index: Optional[Sequence[int]] = None,
+                        param_dtype: Optional[int] = None, stream=None) -> HpoSet:
+    n = len(main_params)
+    if not (len(main_grads) == len(exp_avgs) == len(exp_avg_sqs) == n):
+        raise ValueError("all per-tensor lists must have the same length")
+    if params is None:
+        params = [None] * n
+    if len(params) != n:
+        raise ValueError("params has the wrong length")
+    if param_dtype is None:
+        first = next((p for p in params if p is not None), None)
+        param_dtype = HPO_PARAM_FP32 if first is None else param_dtype_code(first.dtype)
+    numel = []
+    for i in range(n):
+        for what, lst in (("main_params", main_params), ("main_grads", main_grads),
+                          ("exp_avgs", exp_avgs), ("exp_avg_sqs", exp_avg_sqs)):
+            _require(lst[i], torch.float32, what, i)
+            if lst[i].numel() != main_params[i].numel():
+                raise ValueError(f"{what}[{i}] has {lst[i].numel()} elements, main_params[{i}] has "
+                                 f"{main_params[i].numel()}")
+        if params[i] is not None:
+            if not params[i].is_contiguous() or params[i].numel() != main_params[i].numel():
+                raise ValueError(f"params[{i}] must be contiguous with main_params[{i}]'s size")
+        numel.append(main_params[i].numel())
+    arr = lambda ts: (ctypes.c_void_p * max(n, 1))(*[(t.data_ptr() if t is not None else 0) for t in ts])
+    c_numel = (ctypes.c_int64 * max(n, 1))(*numel)
+    c_groups = None
+    if group_index is not None:
+        if len(group_index) != n:
+            raise ValueError("group_index has the wrong length")
+        c_groups = (ctypes.c_int32 * max(n, 1))(*group_index)
+    out = ctypes.c_void_p()
+    st = load().hpo_set_create_list(ctypes.byref(out), n, param_dtype, arr(params), arr(main_params),
+                                    arr(main_grads), arr(exp_avgs), arr(exp_avg_sqs), c_numel, c_groups,
+                                    _stream(stream))
+    _check(st, "hpo_set_create_list")
+    return HpoSet(out, (list(params), list(main_params), list(main_grads), list(exp_avgs), list(exp_avg_sqs)))
+
+
+def hpo_set_create_flat(param: Optional[torch.Tensor], main_param: torch.Tensor, main_grad: torch.Tensor,
+                        exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, param_dtype: Optional[int] = None,
+                        stream=None) -> HpoSet:
+    for what, t in (("main_param", main_param), ("main_grad", main_grad), ("exp_avg", exp_avg),
+                    ("exp_avg_sq", exp_avg_sq)):
+        _require(t, torch.float32, what, 0)
+        if t.numel() != main_param.numel():
+            raise ValueError(f"{what} has the wrong number of elements")
+    if param_dtype is None:
+        param_dtype = HPO_PARAM_FP32 if param is None else param_dtype_code(param.dtype)
+    if param is not None and (not param.is_contiguous() or param.numel() != main_param.numel()):
+        raise ValueError("param must be contiguous with main_param's size")
+    out = ctypes.c_void_p()
+    st = load().hpo_set_create_flat(ctypes.byref(out), main_param.numel(), param_dtype, _ptr(param),
+                                    _ptr(main_param), _ptr(main_grad), _ptr(exp_avg), _ptr(exp_avg_sq),
+                                    _stream(stream))
+    _check(st, "hpo_set_create_flat")
+    return HpoSet(out, (param, main_param, main_grad, exp_avg, exp_avg_sq))
+
+
+def hpo_set_destroy(s: HpoSet) -> None:
+    s.close()
+
+
+def hpo_set_info(s: HpoSet) -> hpo_set_info_t:
+    info = hpo_set_info_t()
+    _check(load().hpo_set_info(s.handle, ctypes.byref(info)), "hpo_set_info")
+    return info
+
+
+def hpo_unscale_check_inf(s: HpoSet, inv_scale: float, d_found_inf, stream=None) -> None:
+    _check(load().hpo_unscale_check_inf(s.handle, inv_scale, _ptr(d_found_inf), _stream(stream)),
+           "hpo_unscale_check_inf")
+
+
+def hpo_grad_global_norm(s: HpoSet, inv_scale: float, d_norm, d_found_inf=None, stream=None) -> None:
+    _check(load().hpo_grad_global_norm(s.handle, inv_scale, _ptr(d_norm), _ptr(d_found_inf), _stream(stream)),
+           "hpo_grad_global_norm")
+
+
+def make_cfg(beta1=0.9, beta2=0.999, eps=1e-8, mode=HPO_ADAMW) -> hpo_adam_cfg:
+    return hpo_adam_cfg(beta1, beta2, eps, mode)
+
+
+def make_groups(groups: Sequence[tuple]):
+    arr = (hpo_group * max(len(groups), 1))()
+    for k, (lr, wd) in enumerate(groups):
+        arr[k] = hpo_group(lr, wd)
+    return arr, len(groups)
+
+
+def hpo_adamw_step(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int], t: int,
+                   inv_scale: float, max_norm: float, d_norm=None, d_found_inf=None, stream=None) -> None:
+    """`groups` is either a ctypes hpo_group array (with n_groups) or a list of
+    (lr, weight_decay) tuples (n_groups may then be None)."""
+    if not isinstance(groups, ctypes.Array):
+        groups, n_groups = make_groups(groups)
+    _check(load().hpo_adamw_step(s.handle, ctypes.byref(cfg), groups, n_groups, t, inv_scale, max_norm,
+                                 _ptr(d_norm), _ptr(d_found_inf), _stream(stream)), "hpo_adamw_step")
+
+
+def hpo_copy_main_to_model(s: HpoSet, stream=None) -> None:
+    _check(load().hpo_copy_main_to_model(s.handle, _stream(stream)), "hpo_copy_main_to_model")
+
+
+def hpo_plan(numel: Sequence[int]):
+    """(chunk_elems, n_chunks, device_bytes) of a list set over these sizes."""
+    n = len(numel)
+    c_numel = (ctypes.c_int64 * max(n, 1))(*numel)
+    ch, nc, nb = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _check(load().hpo_plan(n, c_numel, ctypes.byref(ch), ctypes.byref(nc), ctypes.byref(nb)), "hpo_plan")
+    return ch.value, nc.value, nb.value
+
+
+def hpo_plan_chunks(numel: Sequence[int]):
+    """Chunk table of a list set over these sizes: (tensor, start, len) arrays."""
+    import numpy as np
+    _, nc, _ = hpo_plan(numel)
+    n = len(numel)
+    c_numel = (ctypes.c_int64 * max(n, 1))(*numel)
+    ten = np.empty(max(nc, 1), np.int32)
+    start = np.empty(max(nc, 1), np.int64)
+    ln = np.empty(max(nc, 1), np.int32)
+    _check(load().hpo_plan_chunks(n, c_numel, nc, ten.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                  start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                  ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))), "hpo_plan_chunks")
+    return ten[:nc], start[:nc], ln[:nc]
+
+
+def hpo_last_error() -> str:
+    return load().hpo_last_error().decode(errors="replace")
+
+
+def hpo_status_string(status: int) -> str:
+    return load().hpo_status_string(status).decode()
+
+
+def hpo_abi_version() -> int:
+    return load().hpo_abi_version()

@@ -50,6 +50,7 @@ class Workload:
     grad_seed_base: int = 1000
     inf_step: Optional[int] = None     # 1-based call index whose grads carry one +inf
     flat: bool = False                 # one flat shard instead of a tensor list
+    no_decay_1d: bool = True           # 1-D tensors go to the weight_decay = 0 group
 
     @property
     def numel(self) -> int:
@@ -61,7 +62,7 @@ class Workload:
 
     def group_of(self, i: int) -> int:
         """Group 0 decays, group 1 (1-D tensors: norm gains, biases) does not."""
-        return 1 if self.ndims[i] == 1 else 0
+        return 1 if (self.no_decay_1d and self.ndims[i] == 1) else 0
 
     def groups(self):
         return [(self.lr, self.weight_decay), (self.lr, 0.0)]
@@ -75,7 +76,7 @@ class Workload:
 # --------------------------------------------------------------------------
 def toy(mode: int) -> Workload:
     return Workload("toy_2param", [2], [1], param_dtype="fp32", lr=1e-2, weight_decay=0.1,
-                    mode=mode, steps=1000, grad_std=[0.0])
+                    mode=mode, steps=1000, grad_std=[0.0], no_decay_1d=False)
 
 
 def toy_grad(k: int) -> np.ndarray:
@@ -121,8 +122,9 @@ def ragged(n: int = 20000, max_elems: int = 4 * 2 ** 20, steps: int = 8, inf_ste
 
 
 def zero_shard(numel: int = 8_750_000_000) -> Workload:
+    # a flat shard mixes every kind of param; it is stepped as one decaying group
     return Workload("zero1_shard_70b_over_8", [numel], [1], lr=1e-3, weight_decay=0.1, max_norm=1.0,
-                    steps=3, grad_std=[1e-4], flat=True)
+                    steps=3, grad_std=[1e-4], flat=True, no_decay_1d=False)
 
 
 def inf_position(w: Workload) -> tuple:

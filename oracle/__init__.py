@@ -237,6 +237,17 @@ def oracle_step(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper: 
     # a3: clip coefficient from the fp32 norm
     do_clip, C, c64 = clip_coeff(max_norm, norm32)
     # a4 + a5: the update, one call per tensor with its group's lr / wd
+    apply_update(tensors, grads, hyper, groups, t, inv32, do_clip, C, c64, variant)
+    return StepResult(True, False, norm32, norm64, do_clip, C)
+
+
+def apply_update(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper: Hyper,
+                 groups: Sequence[tuple], t: int, inv_scale: float, do_clip: bool, C: float,
+                 c64: float, variant: str = "f32") -> None:
+    """The update + write-back of one applied step, with the clip decision
+    already taken from the global norm (used directly when only a sample of a
+    very large set is stepped on the host)."""
+    L = lib()
     fn = L.orc_update_f32 if variant == "f32" else L.orc_update_f64
     for T, G in zip(tensors, grads):
         if T.theta.size == 0:
@@ -244,10 +255,9 @@ def oracle_step(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper: 
         lr, wd = groups[T.group]
         args = _UpdateArgs(lr=lr, wd=wd, beta1=hyper.beta1, beta2=hyper.beta2,
                            eps=hyper.eps, t=t, mode=hyper.mode, do_clip=int(do_clip),
-                           inv_scale=inv32, clip_C=C, clip_c64=c64)
+                           inv_scale=float(np.float32(inv_scale)), clip_C=C, clip_c64=c64)
         fn(T.theta.size, _ptr(_f32(T.theta)), _ptr(_f32(T.m)), _ptr(_f32(T.v)),
            _ptr(_f32(np.ascontiguousarray(G))), _ptr(T.p), ctypes.byref(args))
-    return StepResult(True, False, norm32, norm64, do_clip, C)
 
 
 class OracleOptimizer:

@@ -1,0 +1,148 @@
+"""Helpers for the GPU parity tests: build hpo sets over the seeded inputs,
+read state back, and compare it with the oracle's own trajectory.
+
+Nothing here feeds GPU results into the oracle: the oracle starts from the
+seeded initial state and the seeded grads only (both produced by
+mixed_precision_optimizer_amd.inputs), and runs its own steps.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from bounds import check_within, step_error_bounds
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from mixed_precision_optimizer_amd import hpo
+    hpo.load()  # raises if libhpo.so is missing: no fallback exists
+    return hpo
+
+
+def banner(msg: str) -> None:
+    print(f"\n[gpu-test] {msg}", flush=True)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    return t.cpu().numpy().copy()
+
+
+def bf16_of(theta: np.ndarray) -> np.ndarray:
+    """torch's CPU fp32 -> bf16 cast (a library routine, not the oracle)."""
+    return torch.from_numpy(theta).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def make_set(bufs, stream=None):
+    from mixed_precision_optimizer_amd import hpo
+    w = bufs.workload
+    if w.flat:
+        return hpo.hpo_set_create_flat(None if w.param_dtype == "fp32" else bufs.param, bufs.master, bufs.grad,
+                                       bufs.exp_avg, bufs.exp_avg_sq, stream=stream,
+                                       param_dtype=hpo.HPO_PARAM_FP32 if w.param_dtype == "fp32" else hpo.HPO_PARAM_BF16)
+    ps, ms, gs, m1, m2 = bufs.lists()
+    if w.param_dtype == "fp32":
+        ps = None
+    return hpo.hpo_set_create_list(ps, ms, gs, m1, m2, [w.group_of(i) for i in range(w.n_tensors)],
+                                   param_dtype=hpo.HPO_PARAM_FP32 if w.param_dtype == "fp32" else hpo.HPO_PARAM_BF16,
+                                   stream=stream)
+
+
+def make_opt(hset, w, device=None):
+    from mixed_precision_optimizer_amd import MixedPrecisionAdamW
+    return MixedPrecisionAdamW(hset, w.groups(), beta1=w.beta1, beta2=w.beta2, eps=w.eps, mode=w.mode,
+                               max_norm=w.max_norm, loss_scale=w.loss_scale, device=device)
+
+
+def compare_tensor(tag, gpu, orc_new, orc_prev, G, *, inv, clip, C, c64, lr, wd, t, mode, bf16, stats):
+    """gpu: dict theta/m/v[/p] numpy; orc_new / orc_prev: oracle OTensor after / before the step."""
+    E_m, E_v, E_th = step_error_bounds(orc_prev.theta, orc_prev.m, orc_prev.v, G, inv=inv, C=c64, do_clip=clip,
+                                       lr=lr, wd=wd, t=t, mode=mode)
+    check_within(f"{tag} m", gpu["m"], orc_new.m, E_m)
+    check_within(f"{tag} v", gpu["v"], orc_new.v, E_v)
+    check_within(f"{tag} theta", gpu["theta"], orc_new.theta, E_th)
+    n = gpu["theta"].size
+    eq = int(np.sum(gpu["theta"].view(np.uint32) == orc_new.theta.view(np.uint32)))
+    eq += int(np.sum(gpu["m"].view(np.uint32) == orc_new.m.view(np.uint32)))
+    eq += int(np.sum(gpu["v"].view(np.uint32) == orc_new.v.view(np.uint32)))
+    stats["bit_equal"] = stats.get("bit_equal", 0) + eq
+    stats["compared"] = stats.get("compared", 0) + 3 * n
+    if bf16:
+        p = gpu["p"]
+        # the write-back of the GPU's own master is bit-exact (the pages' invariant)
+        assert np.array_equal(p, bf16_of(gpu["theta"])), f"{tag}: param != bf16(master)"
+        # and within one bf16 ulp of the oracle's param
+        d = np.abs(p.astype(np.int32) - orc_new.p.astype(np.int32))
+        assert np.all(d <= 1), f"{tag}: bf16 param more than 1 ulp from the oracle"
+
+
+def read_state(bufs, i=None, lo=0, hi=None):
+    """GPU state of tensor i (or the flat set) in element range [lo, hi)."""
+    w = bufs.workload
+    off = 0 if w.flat else bufs.offs[i]
+    n = w.numel if w.flat else w.numels[i]
+    hi = n if hi is None else hi
+    a, b = off + lo, off + hi
+    out = {"theta": to_np(bufs.master[a:b]), "m": to_np(bufs.exp_avg[a:b]), "v": to_np(bufs.exp_avg_sq[a:b])}
+    if w.param_dtype == "bf16":
+        out["p"] = to_np(bufs.param[a:b])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# full-size norms: stream the stored grads to the host and sum there
+# ---------------------------------------------------------------------------
+def oracle_sumsq_streamed(orc, grad: torch.Tensor, ranges, inv: float, chunk: int = 1 << 28,
+                          threads: int = 8) -> float:
+    """Oracle sum of squares over the given (offset, length) ranges of a flat
+    device grad buffer: each range is copied to pinned host memory in slices
+    and summed by the oracle's plain loop; slice sums are added in range order."""
+    host = [torch.empty(chunk, dtype=torch.float32, pin_memory=True) for _ in range(2)]
+    pieces = []
+    for off, n in ranges:
+        for a in range(0, n, chunk):
+            pieces.append((off + a, min(chunk, n - a)))
+    sums = [0.0] * len(pieces)
+    pool = cf.ThreadPoolExecutor(max_workers=threads)
+    futs = []
+    pending = []
+    buf_in_use = [None, None]
+    for k, (off, n) in enumerate(pieces):
+        slot = k % 2
+        if buf_in_use[slot] is not None:
+            buf_in_use[slot].result()
+        host[slot][:n].copy_(grad[off:off + n])
+        arr = host[slot][:n].numpy()
+
+        def work(arr=arr, k=k):
+            sums[k] = orc.sumsq(arr, inv)
+        fut = pool.submit(work)
+        buf_in_use[slot] = fut
+        futs.append(fut)
+    for f in futs:
+        f.result()
+    pool.shutdown()
+    total = 0.0
+    for s in sums:
+        total = total + s
+    return total
+
+
+def oracle_any_nonfinite_streamed(orc, grad: torch.Tensor, ranges, chunk: int = 1 << 28) -> bool:
+    host = torch.empty(chunk, dtype=torch.float32, pin_memory=True)
+    for off, n in ranges:
+        for a in range(0, n, chunk):
+            m = min(chunk, n - a)
+            host[:m].copy_(grad[off + a:off + a + m])
+            if orc.any_nonfinite(host[:m].numpy()):
+                return True
+    return False

@@ -1,0 +1,345 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element, on seeded inputs at sizes the oracle finishes in seconds (several
+chunks plus ragged tails), plus the edge cases of the method.
+
+The oracle runs its own trajectory from the same seeded initial state and the
+same seeded grads; the GPU state is never fed back into it.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (banner, bf16_of, compare_tensor, make_opt, make_set, read_state, require_gpu,
+                      to_np)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def H():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.lib()
+    return oracle
+
+
+def _oracle_tensors(orc, bufs):
+    """Oracle copies of the seeded initial state (taken before any GPU step)."""
+    w = bufs.workload
+    out = []
+    for i in range(w.n_tensors):
+        st = read_state(bufs, i) if not w.flat else read_state(bufs)
+        T = orc.OTensor(st["theta"], st["m"], st["v"], st.get("p"), w.group_of(i))
+        out.append(T)
+    return out
+
+
+def _grads_np(bufs):
+    w = bufs.workload
+    if w.flat:
+        return [to_np(bufs.grad[:w.numel])]
+    return [to_np(bufs.view(bufs.grad, i)) for i in range(w.n_tensors)]
+
+
+def _run_parity(H, orc, w, steps=None, stats=None, inplace=False):
+    from mixed_precision_optimizer_amd import inputs
+    stats = {} if stats is None else stats
+    bufs = inputs.allocate(w, DEV)
+    hset = make_set(bufs)
+    opt = make_opt(hset, w)
+    Ts = _oracle_tensors(orc, bufs)
+    O = orc.OracleOptimizer(Ts, orc.Hyper(w.beta1, w.beta2, w.eps, w.mode), w.groups(), max_norm=w.max_norm)
+    steps = w.steps if steps is None else steps
+    for k in range(1, steps + 1):
+        inputs.fill_grads_(bufs, k)
+        torch.cuda.synchronize()
+        G = _grads_np(bufs)
+        prev = [T.copy() for T in Ts]
+        r = O.step(G, inv_scale=w.inv_scale())
+        applied, norm = opt.step(inplace_unscale=inplace)
+        assert applied == r.applied, f"step {k}: skip decision differs"
+        assert opt.t == O.t
+        if not r.applied:
+            for i, T in enumerate(Ts):
+                st = read_state(bufs, i) if not w.flat else read_state(bufs)
+                for key in ("theta", "m", "v"):
+                    assert np.array_equal(st[key].view(np.uint32), getattr(T, key).view(np.uint32))
+                if T.p is not None:
+                    assert np.array_equal(st["p"], T.p)
+            stats.setdefault("skipped", []).append(k)
+            continue
+        assert abs(norm - r.norm64) <= 1e-5 * r.norm64, f"step {k}: norm {norm} vs {r.norm64}"
+        stats.setdefault("norm_rel", []).append(abs(norm - r.norm64) / max(r.norm64, 1e-300))
+        c64 = w.max_norm / (float(np.float32(r.norm32)) + 1e-6) if r.clip_applied else 1.0
+        for i, T in enumerate(Ts):
+            st = read_state(bufs, i) if not w.flat else read_state(bufs)
+            lr, wd = w.groups()[T.group]
+            compare_tensor(f"{w.name} step {k} tensor {i}", st, T, prev[i], G[i], inv=w.inv_scale(),
+                           clip=r.clip_applied, C=r.clip_C, c64=c64, lr=lr, wd=wd, t=O.t, mode=w.mode,
+                           bf16=w.param_dtype == "bf16", stats=stats)
+    hset.close()
+    return stats, Ts, bufs
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [0, 1])
+def test_toy_two_params_both_modes(H, orc, mode):
+    """The handbook's decay experiment on the GPU (fp32 params are their own
+    master), every step against the oracle; final values as printed."""
+    from mixed_precision_optimizer_amd import inputs
+    banner(f"toy mode={mode}")
+    w = inputs.toy(mode)
+    stats, Ts, bufs = _run_parity(H, orc, w)
+    th = to_np(bufs.master[:2])
+    want = {0: ["0.361", "0.361"], 1: ["0.000", "0.889"]}[mode]
+    assert [f"{x:.3f}" for x in th] == want
+    print(f"bit-equal {stats['bit_equal']}/{stats['compared']}")
+    assert stats["bit_equal"] == stats["compared"]
+
+
+def test_two_matrices_ten_steps(H, orc):
+    """8.4M params in two bf16 matrices, clip 1.0, 10 steps: every element,
+    every step."""
+    from mixed_precision_optimizer_amd import inputs
+    banner("two matrices 4096x1024 + 1024x4096, 10 steps")
+    w = inputs.two_matrices()
+    stats, Ts, bufs = _run_parity(H, orc, w)
+    print(f"bit-equal {stats['bit_equal']}/{stats['compared']}  norm rel {max(stats['norm_rel']):.2e}")
+    assert stats["bit_equal"] >= 0.999999 * stats["compared"]
+
+
+def _edge_workload(mode, loss_scale, inf_step=None, max_norm=1.0, steps=4):
+    from mixed_precision_optimizer_amd.inputs import Workload
+    sizes = [1, 3, 4, 5, 63, 64, 65, 255, 1023, 4095, 4096, 4097, 0, 12345, 70001, 131072, 300000, 2]
+    ndims = [1 if n in (4095, 5, 63) else 2 for n in sizes]
+    return Workload(f"edge_mode{mode}", sizes, ndims, lr=1e-3, weight_decay=0.1, mode=mode, max_norm=max_norm,
+                    loss_scale=loss_scale, steps=steps, grad_std=[1e-3 * (1 + (i % 5)) for i in range(len(sizes))],
+                    inf_step=inf_step)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_ragged_tails_groups_scale_and_skip(H, orc, mode, inplace):
+    """Ragged sizes (1 .. 300000, empty tensors, scalar tails), a no-decay
+    group, loss scale 1024, clipping, and a +inf at step 2 that skips the step
+    without moving t; both the fused and the pages' in-place unscale."""
+    banner(f"edge mode={mode} inplace={inplace}")
+    w = _edge_workload(mode, 1024.0, inf_step=2, steps=5)
+    stats, Ts, bufs = _run_parity(H, orc, w, inplace=inplace)
+    assert stats["skipped"] == [2]
+    assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.parametrize("bad", [float("inf"), float("-inf"), float("nan")])
+@pytest.mark.parametrize("where", ["head", "middle", "tail"])
+def test_nonfinite_anywhere_skips(H, orc, bad, where):
+    from mixed_precision_optimizer_amd import inputs
+    banner(f"nonfinite {bad} at {where}")
+    w = _edge_workload(0, None, steps=1)
+    bufs = inputs.allocate(w, DEV)
+    inputs.fill_grads_(bufs, 1)
+    i = {"head": 0, "middle": 13, "tail": len(w.numels) - 2}[where]
+    e = {"head": 0, "middle": w.numels[i] // 2, "tail": w.numels[i] - 1}[where]
+    bufs.grad[bufs.offs[i] + e] = bad
+    before = {k: v.clone() for k, v in (("m", bufs.master), ("a", bufs.exp_avg), ("b", bufs.exp_avg_sq),
+                                       ("p", bufs.param))}
+    hset = make_set(bufs)
+    opt = make_opt(hset, w)
+    applied, norm = opt.step()
+    assert applied is False and opt.t == 0
+    assert int(opt.found_inf.item()) == 1
+    for k, t in (("m", bufs.master), ("a", bufs.exp_avg), ("b", bufs.exp_avg_sq), ("p", bufs.param)):
+        assert torch.equal(before[k].view(torch.int16) if k == "p" else before[k].view(torch.int32),
+                           t.view(torch.int16) if k == "p" else t.view(torch.int32))
+    hset.close()
+
+
+def test_norm_matches_oracle_and_is_deterministic(H, orc):
+    from mixed_precision_optimizer_amd import inputs
+    banner("norm")
+    w = _edge_workload(0, 65536.0, steps=1)
+    bufs = inputs.allocate(w, DEV)
+    inputs.fill_grads_(bufs, 1)
+    hset = make_set(bufs)
+    norm = torch.zeros(1, dtype=torch.float32, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.hpo_grad_global_norm(hset, float(np.float32(1 / 65536)), norm, flag)
+    torch.cuda.synchronize()
+    G = [to_np(bufs.view(bufs.grad, i)) for i in range(w.n_tensors)]
+    n2 = sum(orc.sumsq(g, float(np.float32(1 / 65536))) for g in G if g.size)
+    assert abs(norm.item() - math.sqrt(n2)) <= 1e-5 * math.sqrt(n2)
+    assert norm.item() == float(np.float32(math.sqrt(n2)))  # same fp32 rounding of the same sum
+    assert flag.item() == 0
+    vals = set()
+    for _ in range(5):
+        H.hpo_grad_global_norm(hset, float(np.float32(1 / 65536)), norm, None)
+        vals.add(norm.item())
+    assert len(vals) == 1
+    hset.close()
+
+
+def test_empty_set_and_zero_sizes(H):
+    banner("empty set")
+    hset = H.hpo_set_create_list([], [], [], [], [], param_dtype=H.HPO_PARAM_BF16)
+    norm = torch.full((1,), 7.0, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.hpo_grad_global_norm(hset, 1.0, norm, flag)
+    H.hpo_adamw_step(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1, 1.0, 1.0, norm, flag)
+    H.hpo_unscale_check_inf(hset, 0.5, flag)
+    torch.cuda.synchronize()
+    assert norm.item() == 0.0 and flag.item() == 0
+    info = hset.info()
+    assert info.n_tensors == 0 and info.numel == 0 and info.n_chunks == 0
+    hset.close()
+
+
+def test_device_flag_skips_the_update(H):
+    banner("device-side skip")
+    n = 100_003
+    th = torch.randn(n, device=DEV)
+    p = th.to(torch.bfloat16)
+    g = torch.randn(n, device=DEV) * 1e-3
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    th0, p0 = th.clone(), p.clone()
+    hset = H.hpo_set_create_flat(p, th, g, m, v)
+    flag = torch.ones(1, dtype=torch.int32, device=DEV)
+    H.hpo_adamw_step(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1, 1.0, 0.0, None, flag)
+    torch.cuda.synchronize()
+    assert torch.equal(th, th0) and torch.equal(p, p0) and not m.any() and not v.any()
+    flag.zero_()
+    H.hpo_adamw_step(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1, 1.0, 0.0, None, flag)
+    torch.cuda.synchronize()
+    assert not torch.equal(th, th0)
+    hset.close()
+
+
+def test_flat_and_list_sets_agree_bitwise(H):
+    banner("flat vs list")
+    n = 1_000_001
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    base = torch.randn(n, device=DEV, generator=gen)
+    g = torch.randn(n, device=DEV, generator=gen) * 1e-2
+    outs = []
+    for kind in ("flat", "list"):
+        th = base.clone()
+        p = th.to(torch.bfloat16)
+        m = torch.zeros(n, device=DEV)
+        v = torch.zeros(n, device=DEV)
+        if kind == "flat":
+            hset = H.hpo_set_create_flat(p, th, g, m, v)
+        else:
+            hset = H.hpo_set_create_list([p], [th], [g], [m], [v])
+        norm = torch.zeros(1, device=DEV)
+        for t in (1, 2, 3):
+            H.hpo_grad_global_norm(hset, 1.0, norm, None)
+            H.hpo_adamw_step(hset, H.make_cfg(), [(1e-3, 0.1)], None, t, 1.0, 1.0, norm, None)
+        torch.cuda.synchronize()
+        outs.append((th.clone(), m.clone(), v.clone(), p.clone(), norm.item()))
+        hset.close()
+    for a, b in zip(outs[0], outs[1]):
+        if isinstance(a, float):
+            assert a == b
+        else:
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_misaligned_tensors_take_the_scalar_path(H, orc):
+    """Views that start 1..3 elements into a buffer break 16-byte alignment;
+    results must be the same bits as the aligned vector path."""
+    banner("misaligned")
+    n = 50_001
+    rng = np.random.default_rng(6)
+    th0 = rng.standard_normal(n).astype(np.float32)
+    G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    res = []
+    for shift in (0, 1, 2, 3):
+        big = [torch.zeros(n + 4, device=DEV) for _ in range(4)]
+        pb = torch.zeros(n + 4, dtype=torch.bfloat16, device=DEV)
+        th, g, m, v = (b[shift:shift + n] for b in big)
+        p = pb[shift:shift + n]
+        th.copy_(torch.from_numpy(th0))
+        g.copy_(torch.from_numpy(G))
+        hset = H.hpo_set_create_list([p], [th], [g], [m], [v])
+        assert hset.info().n_vector == (1 if shift == 0 else 0)
+        norm = torch.zeros(1, device=DEV)
+        H.hpo_grad_global_norm(hset, 1.0, norm, None)
+        H.hpo_adamw_step(hset, H.make_cfg(mode=1), [(1e-3, 0.1)], None, 1, 1.0, 1.0, norm, None)
+        torch.cuda.synchronize()
+        res.append((to_np(th), to_np(m), to_np(v), to_np(p)))
+        hset.close()
+    for r in res[1:]:
+        for a, b in zip(res[0], r):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    T = orc.OTensor.fresh(th0)
+    orc.OracleOptimizer([T], orc.Hyper(mode=1), [(1e-3, 0.1)], max_norm=1.0).step([G])
+    assert np.array_equal(res[0][0].view(np.uint32), T.theta.view(np.uint32))
+
+
+def test_fp32_param_set_has_no_writeback(H, orc):
+    banner("fp32 params")
+    n = 77_777
+    rng = np.random.default_rng(7)
+    th0 = rng.standard_normal(n).astype(np.float32)
+    G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    th = torch.from_numpy(th0).to(DEV)
+    g = torch.from_numpy(G).to(DEV)
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    hset = H.hpo_set_create_list([th], [th], [g], [m], [v])  # the param is its own master
+    assert hset.info().param_dtype == H.HPO_PARAM_FP32
+    norm = torch.zeros(1, device=DEV)
+    H.hpo_grad_global_norm(hset, 1.0, norm, None)
+    H.hpo_adamw_step(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1, 1.0, 1.0, norm, None)
+    H.hpo_copy_main_to_model(hset)  # no-op for fp32 sets
+    torch.cuda.synchronize()
+    T = orc.OTensor.fresh(th0, bf16_param=False)
+    orc.OracleOptimizer([T], orc.Hyper(), [(1e-3, 0.1)], max_norm=1.0).step([G])
+    assert np.array_equal(to_np(th).view(np.uint32), T.theta.view(np.uint32))
+    with pytest.raises(H.HpoError) as e:
+        H.hpo_set_create_list([th.clone()], [th], [g], [m], [v], param_dtype=H.HPO_PARAM_FP32)
+    assert e.value.status == H.HPO_EINVAL
+    hset.close()
+
+
+def test_fp16_params_are_rejected(H):
+    n = 64
+    th = torch.zeros(n, device=DEV)
+    with pytest.raises(H.HpoError) as e:
+        H.hpo_set_create_flat(th.half(), th, th.clone(), th.clone(), th.clone())
+    assert e.value.status == H.HPO_EDTYPE
+
+
+def test_bf16_writeback_exhaustive(H, orc):
+    """hpo_copy_main_to_model over all 2^32 fp32 bit patterns against the
+    oracle's RNE: bit-equal for every non-NaN input, NaN stays NaN."""
+    banner("exhaustive bf16 write-back")
+    step = 1 << 30
+    hset = None
+    master = torch.empty(step, dtype=torch.float32, device=DEV)
+    extra = [torch.zeros(step, dtype=torch.float32, device=DEV) for _ in range(3)]
+    param = torch.empty(step, dtype=torch.bfloat16, device=DEV)
+    hset = H.hpo_set_create_flat(param, master, *extra)
+    base = torch.arange(step, dtype=torch.int64, device=DEV)
+    for first in range(0, 1 << 32, step):
+        bits = (base + first).to(torch.int64)
+        master.view(torch.int32).copy_(torch.where(bits >= 2 ** 31, bits - 2 ** 32, bits).to(torch.int32))
+        H.hpo_copy_main_to_model(hset)
+        torch.cuda.synchronize()
+        got = to_np(param)
+        want = orc.bf16_rne_patterns(first, step)
+        u = np.arange(step, dtype=np.uint32) + np.uint32(first)
+        nan = (u & 0x7FFFFFFF) > 0x7F800000
+        assert np.array_equal(got[~nan], want[~nan]), hex(first)
+        assert np.all((got[nan] & 0x7FFF) > 0x7F80)
+        print(f"  patterns {first:#x}.. ok", flush=True)
+    hset.close()
