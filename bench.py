@@ -24,7 +24,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import statistics
 import sys
@@ -38,6 +37,37 @@ PEAK_HBM_GBPS = 8000.0
 UPDATE_BYTES = 30   # read grad, master, m, v (16); write master, m, v (12), bf16 param (2)
 GRADPASS_BYTES = 4  # read grad once
 STEP_BYTES = UPDATE_BYTES + GRADPASS_BYTES
+
+
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_hbm_traffic_zero_shard_70b_over_8.txt")
+KERNEL_SOURCES = ("mixed_precision_optimizer_amd/csrc/hpo_kernels.hip", "mixed_precision_optimizer_amd/csrc/hpo_impl.h")
+
+
+def kernel_digest():
+    """sha256[:16] over the device sources; the counter summary records the
+    digest of the kernels it measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name, numel):
+    """HBM bytes per launch of the update kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when that summary was taken on
+    another workload or on kernels that have changed since."""
+    if workload_name != "zero1_shard_70b_over_8" or numel != 8_750_000_000 or not os.path.exists(PMC_SUMMARY):
+        return None
+    digest, traffic = None, None
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if "kernel source digest" in line:
+                digest = line.rsplit(":", 1)[1].strip()
+            if line.startswith("traffic_bytes_per_launch k_adam"):
+                traffic = float(line.split()[-1])
+    return traffic if digest == kernel_digest() else None
 
 
 def log(msg):
@@ -55,7 +85,26 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=1 << 28,
                     help="elements of the workload the CPU oracle steps (0: skip)")
     ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="N",
+                    help="only run a plain device copy of N fp32 elements (known bytes: 4N read, 4N "
+                         "written) five times; used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def calibrate_copy(n):
+    import torch
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = min(a.elapsed_time(b) for a, b in evs)
+    print(json.dumps({"calibration": "device copy", "elements": n, "bytes_read": 4 * n, "bytes_written": 4 * n,
+                      "ms": round(ms, 4), "GBps": round(8 * n / ms / 1e6, 1)}), flush=True)
 
 
 def workload(args):
@@ -120,11 +169,13 @@ def main():
         print(json.dumps({"error": f"bench.py runs on one GPU only (got --gpus {args.gpus}); "
                                    "the multi-GPU path (scalar all-reduces + bf16 param all-gather) is not built"}))
         sys.exit(2)
-    import numpy as np
     import torch
 
     from mixed_precision_optimizer_amd import hpo, inputs
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     dev = torch.device("cuda", 0)
     hpo.load()
     w = workload(args)
@@ -181,6 +232,8 @@ def main():
     upd_gbps = UPDATE_BYTES * N / (upd * 1e-3) / 1e9
     gp_gbps = GRADPASS_BYTES * N / (gp * 1e-3) / 1e9
     step_gbps = STEP_BYTES * N / (ms_step * 1e-3) / 1e9
+    traffic = measured_traffic(w.name, N)
+    traffic_gb = None if traffic is None else round(traffic / 1e9, 3)
     log(f"norm {norm_v:.6g}, applied steps {t_applied}; step {ms_step:.3f} ms, update {upd:.3f} ms "
         f"({upd_gbps:.0f} GB/s), grad pass {gp:.3f} ms ({gp_gbps:.0f} GB/s)")
     out = {
@@ -206,7 +259,10 @@ def main():
                     "grad_pass+finalize": {"ms": round(gp, 4), "GBps": round(gp_gbps, 1),
                                            "bytes_per_elem": GRADPASS_BYTES}},
         "roofline": {"bound": "hbm", "achieved": round(upd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(upd_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(upd_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_gb,
+                     "traffic_unit": "GB per launch of the update kernel (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, "
+                                     "scales from a device copy of known size); algorithmic: "
+                                     f"{UPDATE_BYTES * N / 1e9:.1f} GB"},
     }
     hset.close()
     if sample is not None:

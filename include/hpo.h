@@ -30,8 +30,8 @@
  *   - The caller owns (allocates, frees) every tensor and every device
  *     result buffer.  The library never frees or resizes them.  A set holds
  *     only its own small device tables (one 64-byte descriptor per tensor,
- *     16 bytes per chunk, 12 bytes per chunk of reduction partials); it never
- *     allocates per-element memory.
+ *     16 bytes per chunk, 12 bytes per grad-pass workgroup of reduction
+ *     partials); it never allocates per-element memory.
  *   - The tensors of a set must stay allocated while the set exists and must
  *     not overlap one another.  All element counts are int64.
  *   - Return value: HPO_OK or a negative hpo_status; hpo_last_error() then
@@ -105,6 +105,9 @@ typedef struct {
     int64_t device_bytes;  /* bytes of device memory the set itself holds */
     int32_t device;        /* HIP device ordinal of the set */
     int32_t n_vector;      /* tensors that take the 16-byte vector path */
+    int32_t grad_group;    /* consecutive chunks per grad-pass workgroup */
+    int32_t reserved;
+    int64_t n_grad_parts;  /* grad-pass workgroups = binary64 partials per norm */
 } hpo_set_info_t;
 
 /* ---------------------------------------------------------------------- */

@@ -27,6 +27,8 @@ struct hpo_set_ {
     int32_t n_vector = 0;
     int64_t numel = 0;
     int64_t n_chunks = 0;
+    int32_t grad_group = 1;  /* chunks per grad-pass workgroup */
+    int64_t n_parts = 0;     /* grad-pass workgroups = reduction partials */
     int64_t device_bytes = 0;
     hpo::TensorDesc* d_tensors = nullptr;
     hpo::Chunk* d_chunks = nullptr;
@@ -80,9 +82,18 @@ int32_t choose_chunk(const int64_t* numel, int32_t n)
     return hpo::kMinChunk;
 }
 
-int64_t partial_bytes(int64_t n_chunks)
+/* Chunks per grad-pass workgroup: enough to cover kGradSpan elements. */
+int32_t grad_group_of(int32_t chunk_elems)
 {
-    const int64_t n = n_chunks > 0 ? n_chunks : 1;
+    const int64_t g = hpo::kGradSpan / chunk_elems;
+    return static_cast<int32_t>(g > 1 ? g : 1);
+}
+
+int64_t parts_of(int64_t n_chunks, int32_t group) { return (n_chunks + group - 1) / group; }
+
+int64_t partial_bytes(int64_t n_parts)
+{
+    const int64_t n = n_parts > 0 ? n_parts : 1;
     return n * static_cast<int64_t>(sizeof(double) + sizeof(int32_t));
 }
 
@@ -161,14 +172,16 @@ void free_set(hpo_set s)
 
 hpo_status alloc_partials(hpo_set s)
 {
-    const int64_t n = s->n_chunks > 0 ? s->n_chunks : 1;
+    s->grad_group = grad_group_of(static_cast<int32_t>(s->view.chunk_elems));
+    s->n_parts = parts_of(s->n_chunks, s->grad_group);
+    const int64_t n = s->n_parts > 0 ? s->n_parts : 1;
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->d_part_sum), n * sizeof(double));
     if (e != hipSuccess)
         return fail(HPO_ENOMEM, "hipMalloc of %lld reduction partials: %s", (long long)n, hipGetErrorString(e));
     e = hipMalloc(reinterpret_cast<void**>(&s->d_part_flag), n * sizeof(int32_t));
     if (e != hipSuccess)
         return fail(HPO_ENOMEM, "hipMalloc of %lld flag partials: %s", (long long)n, hipGetErrorString(e));
-    s->device_bytes += partial_bytes(s->n_chunks);
+    s->device_bytes += partial_bytes(s->n_parts);
     return HPO_OK;
 }
 
@@ -222,7 +235,8 @@ hpo_status hpo_plan(int32_t n_tensors, const int64_t* numel, int32_t* out_chunk_
     if (out_n_chunks) *out_n_chunks = nc;
     if (out_device_bytes)
         *out_device_bytes = static_cast<int64_t>(n_tensors) * sizeof(hpo::TensorDesc) +
-                            nc * static_cast<int64_t>(sizeof(hpo::Chunk)) + partial_bytes(nc);
+                            nc * static_cast<int64_t>(sizeof(hpo::Chunk)) +
+                            partial_bytes(parts_of(nc, grad_group_of(ch)));
     return ok();
 }
 
@@ -318,6 +332,7 @@ hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dt
         if (e != hipSuccess) { free_set(s); return fail(HPO_ENOMEM, "hipMalloc chunk table: %s", hipGetErrorString(e)); }
     }
     s->device_bytes = static_cast<int64_t>(td_bytes + ck_bytes);
+    s->view.chunk_elems = ch;
     st = alloc_partials(s);
     if (st != HPO_OK) { free_set(s); return st; }
     if (td_bytes) {
@@ -409,6 +424,8 @@ hpo_status hpo_set_info(hpo_set s, hpo_set_info_t* out)
     out->device_bytes = s->device_bytes;
     out->device = s->device;
     out->n_vector = s->n_vector;
+    out->grad_group = s->grad_group;
+    out->n_grad_parts = s->n_parts;
     return ok();
 }
 
@@ -422,12 +439,12 @@ hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_in
     if (!std::isfinite(inv_scale))
         return fail(HPO_EINVAL, "inv_scale must be finite");
     const hpo::GradPass pass = (inv_scale == 1.0f) ? hpo::GradPass::kCheck : hpo::GradPass::kUnscale;
-    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, pass, inv_scale, s->d_part_sum,
-                                         s->d_part_flag, as_stream(stream));
+    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, pass, inv_scale,
+                                         s->d_part_sum, s->d_part_flag, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch unscale/check pass");
     if (s->n_chunks > 0) {
-        e = hpo::launch_finalize(nullptr, s->d_part_flag, s->n_chunks, nullptr, d_found_inf, as_stream(stream));
+        e = hpo::launch_finalize(nullptr, s->d_part_flag, s->n_parts, nullptr, d_found_inf, as_stream(stream));
         if (e != hipSuccess)
             return hip_fail(e, "launch flag finalize");
     }
@@ -444,12 +461,12 @@ hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32
         return fail(HPO_EINVAL, "d_norm is NULL");
     if (!std::isfinite(inv_scale))
         return fail(HPO_EINVAL, "inv_scale must be finite");
-    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, hpo::GradPass::kNorm, inv_scale,
-                                         s->d_part_sum, s->d_part_flag, as_stream(stream));
+    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm,
+                                         inv_scale, s->d_part_sum, s->d_part_flag, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch norm pass");
     /* with no chunks the finalizer still runs, so the norm reads 0 */
-    e = hpo::launch_finalize(s->d_part_sum, s->d_part_flag, s->n_chunks, d_norm, d_found_inf,
+    e = hpo::launch_finalize(s->d_part_sum, s->d_part_flag, s->n_parts, d_norm, d_found_inf,
                              as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch norm finalize");

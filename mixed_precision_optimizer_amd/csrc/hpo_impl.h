@@ -13,16 +13,33 @@
 
 namespace hpo {
 
-/* Workgroup size of every streaming kernel: 4 wavefronts of 64 lanes. */
-constexpr int kBlock = 256;
+/* Workgroup size of every streaming kernel (default: 4 wavefronts of 64). */
+#ifndef HPO_BLOCK
+#define HPO_BLOCK 256
+#endif
+constexpr int kBlock = HPO_BLOCK;
 /* Elements one lane handles per vector access (one 16-byte fp32 load). */
 constexpr int kVec = 4;
 /* Chunk sizes the planner chooses from (powers of two, multiples of
  * kBlock * kVec so that every chunk start keeps 16-byte alignment). */
+#ifndef HPO_MAX_CHUNK_LOG2
+#define HPO_MAX_CHUNK_LOG2 14
+#endif
 constexpr int kMinChunk = 1 << 12;
-constexpr int kMaxChunk = 1 << 16;
+constexpr int kMaxChunk = 1 << HPO_MAX_CHUNK_LOG2;
 /* Aim for at least this many workgroups per pass: 256 CUs x 8. */
 constexpr int64_t kTargetChunks = 2048;
+/* Workgroup size of the grad pass (read-only streaming; 16 wavefronts). */
+#ifndef HPO_GRAD_BLOCK
+#define HPO_GRAD_BLOCK 1024
+#endif
+constexpr int kGradBlock = HPO_GRAD_BLOCK;
+/* One grad-pass workgroup covers this many elements' worth of consecutive
+ * chunks, so the number of reduction partials stays near numel / 64K. */
+#ifndef HPO_GRAD_SPAN_LOG2
+#define HPO_GRAD_SPAN_LOG2 16
+#endif
+constexpr int64_t kGradSpan = int64_t(1) << HPO_GRAD_SPAN_LOG2;
 /* Workgroup size of the single-workgroup reduction finalizer. */
 constexpr int kFinalBlock = 1024;
 
@@ -78,8 +95,10 @@ enum class GradPass : int { kNorm = 0, kCheck = 1, kUnscale = 2 };
 
 /* Launchers (hpo_kernels.hip).  Each enqueues on `stream` and returns the
  * launch status. */
-hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, GradPass pass, float inv_scale,
-                            double* part_sum, int32_t* part_flag, hipStream_t stream);
+/* The grad pass runs one workgroup per group of `grad_group` consecutive
+ * chunks (n_parts = ceil(n_chunks / grad_group) workgroups and partials). */
+hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
+                            float inv_scale, double* part_sum, int32_t* part_flag, hipStream_t stream);
 hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
                            float* d_norm, int32_t* d_found, hipStream_t stream);
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,

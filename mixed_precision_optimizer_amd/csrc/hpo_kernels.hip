@@ -6,9 +6,11 @@
  *   [FP32-RFC]   "支持FP32优化器" (hyper-parallel issue)
  *
  * The whole path is elementwise plus one global sum, so it is bound by HBM
- * bandwidth, not by the matrix cores: no MFMA here.  Every pass walks the
+ * bandwidth, not by the matrix cores: no MFMA here.  The update walks the
  * set's chunk table with one 256-lane workgroup (4 wavefronts of 64) per
- * chunk of 4096..65536 contiguous elements of one tensor.  On tensors whose
+ * chunk of 4096..16384 contiguous elements of one tensor; the read-only grad
+ * pass runs 1024-lane workgroups over groups of consecutive chunks (~64K
+ * elements each), so it leaves few reduction partials.  On tensors whose
  * pointers are 16-byte aligned each lane moves 16 bytes per fp32 array per
  * access (global_load_dwordx4), a wavefront 1 KB contiguous, and the bf16
  * write-back is 8 bytes per lane (512 B per wavefront), so every access
@@ -37,8 +39,59 @@
 
 #include "hpo_impl.h"
 
+/* Tuning knobs (compile time), defaults chosen by measurement on MI355X at
+ * 8.75e9 elements.  UNROLL: 16-byte vectors per lane per array in flight in
+ * one loop trip.  NT: streaming (nontemporal) loads / stores for data that is
+ * touched exactly once per pass -- worth about +5% on the update and +12% on
+ * the read-only grad pass, since nothing here is ever re-read from cache. */
+#ifndef HPO_ADAM_UNROLL
+#define HPO_ADAM_UNROLL 2
+#endif
+#ifndef HPO_GRAD_UNROLL
+#define HPO_GRAD_UNROLL 1
+#endif
+#ifndef HPO_NT_LOADS
+#define HPO_NT_LOADS 1
+#endif
+#ifndef HPO_NT_STORES
+#define HPO_NT_STORES 1
+#endif
+
 namespace hpo {
 namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float4 ld_stream(const float4* p)
+{
+#if HPO_NT_LOADS
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void st_stream(float4* p, float4 v)
+{
+#if HPO_NT_STORES
+    f32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(p));
+#else
+    *p = v;
+#endif
+}
+
+__device__ __forceinline__ void st_stream(uint2* p, uint2 v)
+{
+#if HPO_NT_STORES
+    u32x2_t w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+#else
+    *p = v;
+#endif
+}
 
 struct Range {
     TensorDesc d;
@@ -47,16 +100,16 @@ struct Range {
 };
 
 template <bool FLAT>
-__device__ __forceinline__ Range chunk_range(const SetView& sv)
+__device__ __forceinline__ Range chunk_range(const SetView& sv, int64_t chunk)
 {
     Range r;
     if constexpr (FLAT) {
         r.d = sv.flat;
-        r.start = static_cast<int64_t>(blockIdx.x) * sv.chunk_elems;
+        r.start = chunk * sv.chunk_elems;
         const int64_t rem = r.d.numel - r.start;
         r.len = rem < sv.chunk_elems ? rem : sv.chunk_elems;
     } else {
-        const Chunk c = sv.chunks[blockIdx.x];
+        const Chunk c = sv.chunks[chunk];
         r.d = sv.tensors[c.tensor];
         r.start = c.start;
         r.len = c.len;
@@ -124,43 +177,65 @@ __device__ __forceinline__ void grad_elem(float& G, float inv, double& acc, int&
     }
 }
 
-template <bool FLAT, GradPass PASS>
-__global__ __launch_bounds__(kBlock) void k_grad_pass(SetView sv, float inv, double* part_sum,
-                                                      int32_t* part_flag)
+template <GradPass PASS>
+__device__ __forceinline__ void grad_range(const Range& r, float inv, double& acc, int& bad)
 {
-    const Range r = chunk_range<FLAT>(sv);
     float* __restrict__ G = r.d.grad + r.start;
     const int tid = threadIdx.x;
-    double acc = 0.0;
-    int bad = 0;
     int64_t done = 0;
     if (r.d.vec_ok) {
+        constexpr int U = HPO_GRAD_UNROLL;
         const int64_t nv = r.len / kVec;
         float4* __restrict__ G4 = reinterpret_cast<float4*>(G);
-        for (int64_t i = tid; i < nv; i += kBlock) {
-            float4 x = G4[i];
-            grad_elem<PASS>(x.x, inv, acc, bad);
-            grad_elem<PASS>(x.y, inv, acc, bad);
-            grad_elem<PASS>(x.z, inv, acc, bad);
-            grad_elem<PASS>(x.w, inv, acc, bad);
-            if constexpr (PASS == GradPass::kUnscale)
-                G4[i] = x;
+        for (int64_t base = tid; base < nv; base += kGradBlock * U) {
+            float4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + static_cast<int64_t>(u) * kGradBlock;
+                if (i < nv)
+                    x[u] = ld_stream(G4 + i);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + static_cast<int64_t>(u) * kGradBlock;
+                if (i < nv) {
+                    grad_elem<PASS>(x[u].x, inv, acc, bad);
+                    grad_elem<PASS>(x[u].y, inv, acc, bad);
+                    grad_elem<PASS>(x[u].z, inv, acc, bad);
+                    grad_elem<PASS>(x[u].w, inv, acc, bad);
+                    if constexpr (PASS == GradPass::kUnscale)
+                        st_stream(G4 + i, x[u]);
+                }
+            }
         }
         done = nv * kVec;
     }
-    for (int64_t i = done + tid; i < r.len; i += kBlock) {
+    for (int64_t i = done + tid; i < r.len; i += kGradBlock) {
         float x = G[i];
         grad_elem<PASS>(x, inv, acc, bad);
         if constexpr (PASS == GradPass::kUnscale)
             G[i] = x;
     }
+}
+
+/* One workgroup per group of consecutive chunks; one partial per workgroup. */
+template <bool FLAT, GradPass PASS>
+__global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_chunks, int32_t group,
+                                                          float inv, double* part_sum, int32_t* part_flag)
+{
+    double acc = 0.0;
+    int bad = 0;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * group;
+    const int64_t c1 = c0 + group < n_chunks ? c0 + group : n_chunks;
+    for (int64_t c = c0; c < c1; ++c)
+        grad_range<PASS>(chunk_range<FLAT>(sv, c), inv, acc, bad);
     const int any_bad = __syncthreads_or(bad);
     if constexpr (PASS == GradPass::kNorm) {
-        const double tot = block_sum<kBlock>(acc);
-        if (tid == 0)
+        const double tot = block_sum<kGradBlock>(acc);
+        if (threadIdx.x == 0)
             part_sum[blockIdx.x] = tot;
     }
-    if (tid == 0)
+    if (threadIdx.x == 0)
         part_flag[blockIdx.x] = any_bad ? 1 : 0;
 }
 
@@ -171,17 +246,32 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(const double* part_sum
                                                           const int32_t* part_flag, int64_t n,
                                                           float* d_norm, int32_t* d_found)
 {
-    double acc = 0.0;
+    /* Each lane keeps kAcc independent partial sums so that kAcc loads are in
+     * flight at once; partial i always goes to the same accumulator, and the
+     * accumulators are added in a fixed tree, so the result is reproducible. */
+    constexpr int kAcc = 8;
+    double acc[kAcc];
+#pragma unroll
+    for (int k = 0; k < kAcc; ++k)
+        acc[k] = 0.0;
     int bad = 0;
-    for (int64_t i = threadIdx.x; i < n; i += kFinalBlock) {
-        if (d_norm != nullptr)
-            acc += part_sum[i];
-        bad |= part_flag[i];
+    const bool want_norm = d_norm != nullptr;
+    for (int64_t base = threadIdx.x; base < n; base += static_cast<int64_t>(kFinalBlock) * kAcc) {
+#pragma unroll
+        for (int k = 0; k < kAcc; ++k) {
+            const int64_t i = base + static_cast<int64_t>(k) * kFinalBlock;
+            if (i < n) {
+                if (want_norm)
+                    acc[k] += part_sum[i];
+                bad |= part_flag[i];
+            }
+        }
     }
+    const double mine = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     const int any_bad = __syncthreads_or(bad);
-    const double tot = block_sum<kFinalBlock>(acc);
+    const double tot = block_sum<kFinalBlock>(mine);
     if (threadIdx.x == 0) {
-        if (d_norm != nullptr)
+        if (want_norm)
             *d_norm = static_cast<float>(sqrt(tot));
         if (d_found != nullptr && any_bad)
             *d_found = 1;
@@ -226,7 +316,7 @@ __global__ __launch_bounds__(kBlock) void k_adam(SetView sv, AdamScalars sc)
             C = static_cast<float>(c);
         }
     }
-    const Range r = chunk_range<FLAT>(sv);
+    const Range r = chunk_range<FLAT>(sv, blockIdx.x);
     const float lr = sc.lr[r.d.group];
     const float wd = sc.wd[r.d.group];
     const float* __restrict__ G = r.d.grad + r.start;
@@ -243,20 +333,34 @@ __global__ __launch_bounds__(kBlock) void k_adam(SetView sv, AdamScalars sc)
         float4* __restrict__ M4 = reinterpret_cast<float4*>(M);
         float4* __restrict__ V4 = reinterpret_cast<float4*>(V);
         uint2* __restrict__ P4 = reinterpret_cast<uint2*>(P);
-        for (int64_t i = tid; i < nv; i += kBlock) {
-            const float4 g = G4[i];
-            float4 th = T4[i];
-            float4 m = M4[i];
-            float4 v = V4[i];
-            adam_elem<MODE>(g.x, th.x, m.x, v.x, sc, clip, C, lr, wd);
-            adam_elem<MODE>(g.y, th.y, m.y, v.y, sc, clip, C, lr, wd);
-            adam_elem<MODE>(g.z, th.z, m.z, v.z, sc, clip, C, lr, wd);
-            adam_elem<MODE>(g.w, th.w, m.w, v.w, sc, clip, C, lr, wd);
-            T4[i] = th;
-            M4[i] = m;
-            V4[i] = v;
-            if constexpr (PDT == HPO_PARAM_BF16)
-                P4[i] = make_uint2(pack_bf16x2(th.x, th.y), pack_bf16x2(th.z, th.w));
+        constexpr int U = HPO_ADAM_UNROLL;
+        for (int64_t base = tid; base < nv; base += kBlock * U) {
+            float4 g[U], th[U], m[U], v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + static_cast<int64_t>(u) * kBlock;
+                if (i < nv) {
+                    g[u] = ld_stream(G4 + i);
+                    th[u] = ld_stream(T4 + i);
+                    m[u] = ld_stream(M4 + i);
+                    v[u] = ld_stream(V4 + i);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + static_cast<int64_t>(u) * kBlock;
+                if (i < nv) {
+                    adam_elem<MODE>(g[u].x, th[u].x, m[u].x, v[u].x, sc, clip, C, lr, wd);
+                    adam_elem<MODE>(g[u].y, th[u].y, m[u].y, v[u].y, sc, clip, C, lr, wd);
+                    adam_elem<MODE>(g[u].z, th[u].z, m[u].z, v[u].z, sc, clip, C, lr, wd);
+                    adam_elem<MODE>(g[u].w, th[u].w, m[u].w, v[u].w, sc, clip, C, lr, wd);
+                    st_stream(T4 + i, th[u]);
+                    st_stream(M4 + i, m[u]);
+                    st_stream(V4 + i, v[u]);
+                    if constexpr (PDT == HPO_PARAM_BF16)
+                        st_stream(P4 + i, make_uint2(pack_bf16x2(th[u].x, th[u].y), pack_bf16x2(th[u].z, th[u].w)));
+                }
+            }
         }
         done = nv * kVec;
     }
@@ -277,7 +381,7 @@ __global__ __launch_bounds__(kBlock) void k_adam(SetView sv, AdamScalars sc)
 template <bool FLAT>
 __global__ __launch_bounds__(kBlock) void k_copy_main_to_model(SetView sv)
 {
-    const Range r = chunk_range<FLAT>(sv);
+    const Range r = chunk_range<FLAT>(sv, blockIdx.x);
     const float* __restrict__ T = r.d.master + r.start;
     uint16_t* __restrict__ P = static_cast<uint16_t*>(r.d.param) + r.start;
     const int tid = threadIdx.x;
@@ -307,23 +411,24 @@ hipError_t launch(void (*kernel)(Args...), int64_t grid, int block, hipStream_t 
 
 }  // namespace
 
-hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, GradPass pass, float inv_scale,
-                            double* part_sum, int32_t* part_flag, hipStream_t stream)
+hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
+                            float inv_scale, double* part_sum, int32_t* part_flag, hipStream_t stream)
 {
     if (n_chunks == 0)
         return hipSuccess;
+    const int64_t grid = (n_chunks + grad_group - 1) / grad_group;
     const bool flat = sv.is_flat != 0;
+#define HPO_GRAD_LAUNCH(F, P) \
+    launch(k_grad_pass<F, P>, grid, kGradBlock, stream, sv, n_chunks, grad_group, inv_scale, part_sum, part_flag)
     switch (pass) {
     case GradPass::kNorm:
-        return flat ? launch(k_grad_pass<true, GradPass::kNorm>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag)
-                    : launch(k_grad_pass<false, GradPass::kNorm>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag);
+        return flat ? HPO_GRAD_LAUNCH(true, GradPass::kNorm) : HPO_GRAD_LAUNCH(false, GradPass::kNorm);
     case GradPass::kCheck:
-        return flat ? launch(k_grad_pass<true, GradPass::kCheck>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag)
-                    : launch(k_grad_pass<false, GradPass::kCheck>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag);
+        return flat ? HPO_GRAD_LAUNCH(true, GradPass::kCheck) : HPO_GRAD_LAUNCH(false, GradPass::kCheck);
     case GradPass::kUnscale:
-        return flat ? launch(k_grad_pass<true, GradPass::kUnscale>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag)
-                    : launch(k_grad_pass<false, GradPass::kUnscale>, n_chunks, kBlock, stream, sv, inv_scale, part_sum, part_flag);
+        return flat ? HPO_GRAD_LAUNCH(true, GradPass::kUnscale) : HPO_GRAD_LAUNCH(false, GradPass::kUnscale);
     }
+#undef HPO_GRAD_LAUNCH
     return hipErrorInvalidValue;
 }
 

@@ -43,7 +43,8 @@ class hpo_set_info_t(ctypes.Structure):
                 ("is_flat", ctypes.c_int32), ("chunk_elems", ctypes.c_int32),
                 ("numel", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("device_bytes", ctypes.c_int64), ("device", ctypes.c_int32),
-                ("n_vector", ctypes.c_int32)]
+                ("n_vector", ctypes.c_int32), ("grad_group", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("n_grad_parts", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
