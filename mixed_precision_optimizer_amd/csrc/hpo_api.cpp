@@ -91,9 +91,10 @@ int32_t grad_group_of(int32_t chunk_elems)
 
 int64_t parts_of(int64_t n_chunks, int32_t group) { return (n_chunks + group - 1) / group; }
 
+/* First-stage partials plus the second-stage ones of large sets. */
 int64_t partial_bytes(int64_t n_parts)
 {
-    const int64_t n = n_parts > 0 ? n_parts : 1;
+    const int64_t n = (n_parts > 0 ? n_parts : 1) + hpo::stage_parts(n_parts);
     return n * static_cast<int64_t>(sizeof(double) + sizeof(int32_t));
 }
 
@@ -174,7 +175,7 @@ hpo_status alloc_partials(hpo_set s)
 {
     s->grad_group = grad_group_of(static_cast<int32_t>(s->view.chunk_elems));
     s->n_parts = parts_of(s->n_chunks, s->grad_group);
-    const int64_t n = s->n_parts > 0 ? s->n_parts : 1;
+    const int64_t n = (s->n_parts > 0 ? s->n_parts : 1) + hpo::stage_parts(s->n_parts);
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->d_part_sum), n * sizeof(double));
     if (e != hipSuccess)
         return fail(HPO_ENOMEM, "hipMalloc of %lld reduction partials: %s", (long long)n, hipGetErrorString(e));
@@ -199,6 +200,10 @@ hpo_status check_set(hpo_set s)
 }
 
 hipStream_t as_stream(void* stream) { return static_cast<hipStream_t>(stream); }
+
+/* The second-stage partials sit right after the first-stage ones. */
+double* stage_sum(hpo_set s) { return s->d_part_sum + (s->n_parts > 0 ? s->n_parts : 1); }
+int32_t* stage_flag(hpo_set s) { return s->d_part_flag + (s->n_parts > 0 ? s->n_parts : 1); }
 
 bool is_finite(double x) { return std::isfinite(x); }
 
@@ -444,7 +449,8 @@ hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_in
     if (e != hipSuccess)
         return hip_fail(e, "launch unscale/check pass");
     if (s->n_chunks > 0) {
-        e = hpo::launch_finalize(nullptr, s->d_part_flag, s->n_parts, nullptr, d_found_inf, as_stream(stream));
+        e = hpo::launch_finalize(nullptr, s->d_part_flag, s->n_parts, stage_sum(s), stage_flag(s), nullptr,
+                                 d_found_inf, as_stream(stream));
         if (e != hipSuccess)
             return hip_fail(e, "launch flag finalize");
     }
@@ -466,8 +472,8 @@ hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32
     if (e != hipSuccess)
         return hip_fail(e, "launch norm pass");
     /* with no chunks the finalizer still runs, so the norm reads 0 */
-    e = hpo::launch_finalize(s->d_part_sum, s->d_part_flag, s->n_parts, d_norm, d_found_inf,
-                             as_stream(stream));
+    e = hpo::launch_finalize(s->d_part_sum, s->d_part_flag, s->n_parts, stage_sum(s), stage_flag(s), d_norm,
+                             d_found_inf, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch norm finalize");
     return ok();

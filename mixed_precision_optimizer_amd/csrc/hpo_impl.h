@@ -40,8 +40,12 @@ constexpr int kGradBlock = HPO_GRAD_BLOCK;
 #define HPO_GRAD_SPAN_LOG2 16
 #endif
 constexpr int64_t kGradSpan = int64_t(1) << HPO_GRAD_SPAN_LOG2;
-/* Workgroup size of the single-workgroup reduction finalizer. */
+/* Workgroup size of the reduction finalizer, and the partials one
+ * workgroup folds per stage (sets with more partials reduce in two stages). */
 constexpr int kFinalBlock = 1024;
+constexpr int64_t kFinalSpan = 8192;
+/* Second-stage partials a set needs for n first-stage partials. */
+inline int64_t stage_parts(int64_t n) { return n > kFinalSpan ? (n + kFinalSpan - 1) / kFinalSpan : 0; }
 
 /* One tensor of a set, as the kernels see it (64 bytes). */
 struct TensorDesc {
@@ -99,8 +103,13 @@ enum class GradPass : int { kNorm = 0, kCheck = 1, kUnscale = 2 };
  * chunks (n_parts = ceil(n_chunks / grad_group) workgroups and partials). */
 hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
                             float inv_scale, double* part_sum, int32_t* part_flag, hipStream_t stream);
+/* Folds n_parts partials into *d_norm = fp32(sqrt(sum)) (skipped when d_norm
+ * is null, part_sum is then not read) and *d_found |= any flag; sets with
+ * more than kFinalSpan partials go through stage_sum / stage_flag
+ * (stage_parts(n_parts) entries). */
 hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
-                           float* d_norm, int32_t* d_found, hipStream_t stream);
+                           double* stage_sum, int32_t* stage_flag, float* d_norm, int32_t* d_found,
+                           hipStream_t stream);
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                        hipStream_t stream);
 hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream);

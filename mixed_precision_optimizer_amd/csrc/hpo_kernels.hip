@@ -56,6 +56,15 @@
 #ifndef HPO_NT_STORES
 #define HPO_NT_STORES 1
 #endif
+/* XCD_REMAP: workgroups are handed to the 8 XCDs round-robin by index; with
+ * the remap, XCD x works through one contiguous eighth of the chunks.
+ * ADAM_MIN_BLOCKS: second __launch_bounds__ argument of the update (0: none). */
+#ifndef HPO_XCD_REMAP
+#define HPO_XCD_REMAP 0
+#endif
+#ifndef HPO_ADAM_MIN_BLOCKS
+#define HPO_ADAM_MIN_BLOCKS 0
+#endif
 
 namespace hpo {
 namespace {
@@ -90,6 +99,22 @@ __device__ __forceinline__ void st_stream(uint2* p, uint2 v)
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
 #else
     *p = v;
+#endif
+}
+
+/* Chunk handled by this workgroup of an n-workgroup update launch. */
+__device__ __forceinline__ int64_t update_chunk(int64_t n)
+{
+#if HPO_XCD_REMAP
+    constexpr int64_t kXcd = 8;
+    const int64_t b = blockIdx.x;
+    const int64_t x = b % kXcd, k = b / kXcd;
+    const int64_t q = n / kXcd, r = n % kXcd;
+    const int64_t first = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+    return first + k;
+#else
+    (void)n;
+    return blockIdx.x;
 #endif
 }
 
@@ -242,34 +267,61 @@ __global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_
 /* ---------------------------------------------------------------------- */
 /* finalize: one workgroup, fixed-order sum of the per-chunk partials       */
 /* ---------------------------------------------------------------------- */
-__global__ __launch_bounds__(kFinalBlock) void k_finalize(const double* part_sum,
-                                                          const int32_t* part_flag, int64_t n,
-                                                          float* d_norm, int32_t* d_found)
+/* Sum of partials [lo, hi) by one workgroup: each lane keeps kAcc
+ * independent accumulators so that kAcc loads are in flight at once; partial
+ * i always lands in the same accumulator and the accumulators and lanes are
+ * combined in a fixed tree, so the result is reproducible.  Valid in lane 0. */
+__device__ __forceinline__ double reduce_partials(const double* part_sum, const int32_t* part_flag,
+                                                  int64_t lo, int64_t hi, bool want_sum, int& any_bad)
 {
-    /* Each lane keeps kAcc independent partial sums so that kAcc loads are in
-     * flight at once; partial i always goes to the same accumulator, and the
-     * accumulators are added in a fixed tree, so the result is reproducible. */
     constexpr int kAcc = 8;
     double acc[kAcc];
 #pragma unroll
     for (int k = 0; k < kAcc; ++k)
         acc[k] = 0.0;
     int bad = 0;
-    const bool want_norm = d_norm != nullptr;
-    for (int64_t base = threadIdx.x; base < n; base += static_cast<int64_t>(kFinalBlock) * kAcc) {
+    for (int64_t base = lo + threadIdx.x; base < hi; base += static_cast<int64_t>(kFinalBlock) * kAcc) {
 #pragma unroll
         for (int k = 0; k < kAcc; ++k) {
             const int64_t i = base + static_cast<int64_t>(k) * kFinalBlock;
-            if (i < n) {
-                if (want_norm)
+            if (i < hi) {
+                if (want_sum)
                     acc[k] += part_sum[i];
                 bad |= part_flag[i];
             }
         }
     }
     const double mine = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-    const int any_bad = __syncthreads_or(bad);
-    const double tot = block_sum<kFinalBlock>(mine);
+    any_bad = __syncthreads_or(bad);
+    return block_sum<kFinalBlock>(mine);
+}
+
+/* First of two reduction stages for large sets: workgroup b folds partials
+ * [b * kFinalSpan, (b + 1) * kFinalSpan) into one. */
+__global__ __launch_bounds__(kFinalBlock) void k_reduce_stage(const double* part_sum, const int32_t* part_flag,
+                                                              int64_t n, double* out_sum, int32_t* out_flag)
+{
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * kFinalSpan;
+    const int64_t hi = lo + kFinalSpan < n ? lo + kFinalSpan : n;
+    const bool want_sum = part_sum != nullptr;
+    int any_bad = 0;
+    const double tot = reduce_partials(part_sum, part_flag, lo, hi, want_sum, any_bad);
+    if (threadIdx.x == 0) {
+        if (want_sum)
+            out_sum[blockIdx.x] = tot;
+        out_flag[blockIdx.x] = any_bad ? 1 : 0;
+    }
+}
+
+/* Last stage: one workgroup over all remaining partials, then sqrt and the
+ * flag.  d_norm == nullptr: flag only (part_sum is not read). */
+__global__ __launch_bounds__(kFinalBlock) void k_finalize(const double* part_sum,
+                                                          const int32_t* part_flag, int64_t n,
+                                                          float* d_norm, int32_t* d_found)
+{
+    const bool want_norm = d_norm != nullptr;
+    int any_bad = 0;
+    const double tot = reduce_partials(part_sum, part_flag, 0, n, want_norm, any_bad);
     if (threadIdx.x == 0) {
         if (want_norm)
             *d_norm = static_cast<float>(sqrt(tot));
@@ -302,8 +354,14 @@ __device__ __forceinline__ void adam_elem(float G, float& th, float& m, float& v
         th = th - lr * u;
 }
 
+#if HPO_ADAM_MIN_BLOCKS
+#define HPO_ADAM_BOUNDS __launch_bounds__(kBlock, HPO_ADAM_MIN_BLOCKS)
+#else
+#define HPO_ADAM_BOUNDS __launch_bounds__(kBlock)
+#endif
+
 template <bool FLAT, int PDT, int MODE>
-__global__ __launch_bounds__(kBlock) void k_adam(SetView sv, AdamScalars sc)
+__global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chunks)
 {
     if (sc.d_found != nullptr && *sc.d_found != 0)
         return; /* found_inf: the whole step is skipped ([OPT-INFRA] §10.2) */
@@ -316,7 +374,7 @@ __global__ __launch_bounds__(kBlock) void k_adam(SetView sv, AdamScalars sc)
             C = static_cast<float>(c);
         }
     }
-    const Range r = chunk_range<FLAT>(sv, blockIdx.x);
+    const Range r = chunk_range<FLAT>(sv, update_chunk(n_chunks));
     const float lr = sc.lr[r.d.group];
     const float wd = sc.wd[r.d.group];
     const float* __restrict__ G = r.d.grad + r.start;
@@ -433,9 +491,21 @@ hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_gr
 }
 
 hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
-                           float* d_norm, int32_t* d_found, hipStream_t stream)
+                           double* stage_sum, int32_t* stage_flag, float* d_norm, int32_t* d_found,
+                           hipStream_t stream)
 {
-    return launch(k_finalize, 1, kFinalBlock, stream, part_sum, part_flag, n_parts, d_norm, d_found);
+    const double* ps = d_norm != nullptr ? part_sum : nullptr;
+    if (n_parts > kFinalSpan) {
+        const int64_t n_stage = (n_parts + kFinalSpan - 1) / kFinalSpan;
+        hipError_t e = launch(k_reduce_stage, n_stage, kFinalBlock, stream, ps, part_flag, n_parts,
+                              stage_sum, stage_flag);
+        if (e != hipSuccess)
+            return e;
+        ps = d_norm != nullptr ? static_cast<const double*>(stage_sum) : nullptr;
+        part_flag = stage_flag;
+        n_parts = n_stage;
+    }
+    return launch(k_finalize, 1, kFinalBlock, stream, ps, part_flag, n_parts, d_norm, d_found);
 }
 
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
@@ -446,7 +516,7 @@ hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const 
     const bool flat = sv.is_flat != 0;
     const bool bf16 = sv.param_dtype == HPO_PARAM_BF16;
     const bool adamw = mode == HPO_ADAMW;
-#define HPO_ADAM_LAUNCH(F, P, M) launch(k_adam<F, P, M>, n_chunks, kBlock, stream, sv, sc)
+#define HPO_ADAM_LAUNCH(F, P, M) launch(k_adam<F, P, M>, n_chunks, kBlock, stream, sv, sc, n_chunks)
     if (flat) {
         if (bf16)
             return adamw ? HPO_ADAM_LAUNCH(true, HPO_PARAM_BF16, HPO_ADAMW) : HPO_ADAM_LAUNCH(true, HPO_PARAM_BF16, HPO_ADAM_L2);
