@@ -80,7 +80,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zero_shard",
-                    choices=["zero_shard", "llama8b", "ragged", "two_matrices"])
+                    choices=["zero_shard", "zero_shard_ranges", "llama8b", "ragged", "two_matrices"])
     ap.add_argument("--numel", type=int, default=None, help="override the flat shard's size")
     ap.add_argument("--cpu-sample", type=int, default=1 << 28,
                     help="elements of the workload the CPU oracle steps (0: skip)")
@@ -111,6 +111,8 @@ def workload(args):
     from mixed_precision_optimizer_amd import inputs
     if args.workload == "zero_shard":
         return inputs.zero_shard(args.numel) if args.numel else inputs.zero_shard()
+    if args.workload == "zero_shard_ranges":
+        return inputs.zero_shard_ranges()
     if args.workload == "llama8b":
         return inputs.llama8b()
     if args.workload == "ragged":
@@ -123,6 +125,9 @@ def workload(args):
 def make_set(bufs):
     from mixed_precision_optimizer_amd import hpo
     w = bufs.workload
+    if w.flat and w.n_tensors > 1:
+        return hpo.hpo_set_create_flat_ranges(bufs.param, bufs.master, bufs.grad, bufs.exp_avg, bufs.exp_avg_sq,
+                                              bufs.offs, [w.group_of(i) for i in range(w.n_tensors)])
     if w.flat:
         return hpo.hpo_set_create_flat(bufs.param, bufs.master, bufs.grad, bufs.exp_avg, bufs.exp_avg_sq)
     ps, ms, gs, m1, m2 = bufs.lists()

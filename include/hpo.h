@@ -104,7 +104,7 @@ typedef struct {
     int64_t n_chunks;
     int64_t device_bytes;  /* bytes of device memory the set itself holds */
     int32_t device;        /* HIP device ordinal of the set */
-    int32_t n_vector;      /* tensors that take the 16-byte vector path */
+    int32_t n_vector;      /* tensors (ranges) whose body takes the 16-byte vector path */
     int32_t grad_group;    /* consecutive chunks per grad-pass workgroup */
     int32_t reserved;
     int64_t n_grad_parts;  /* grad-pass workgroups = binary64 partials per norm */
@@ -125,9 +125,13 @@ typedef struct {
  * group_index[i] in [0, HPO_MAX_GROUPS) selects the tensor's hpo_group in
  * hpo_adamw_step (NULL: every tensor is in group 0).  numel[i] may be 0;
  * n_tensors may be 0 (then every call is a no-op and the norm is 0).
- * Pointers need 4-byte (fp32) and 2-byte (bf16) alignment; a tensor whose
- * pointers are not all 16-byte aligned (8-byte for bf16) is still stepped,
- * on a slower element-at-a-time path.
+ * Pointers need 4-byte (fp32) and 2-byte (bf16) alignment.  Tensors whose
+ * pointers are 16-byte aligned (8-byte for bf16) take 16-byte vector
+ * accesses; a tensor whose five pointers sit at the same element offset
+ * inside a 16-byte line (a view a few elements into a flat buffer) has its
+ * first 1..3 elements stepped one at a time and the rest vectorized; any
+ * other tensor is stepped one element at a time.  Results are the same bits
+ * on every path.
  * The host arrays are read during the call only.  The device tables are
  * uploaded on `stream`, and the call waits for that upload to finish. */
 hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dtype,
@@ -143,6 +147,20 @@ hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dt
 hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
                                float* main_param, float* main_grad, float* exp_avg,
                                float* exp_avg_sq, void* stream);
+
+/* A flat ZeRO-1 shard whose elements belong to several parameter groups.
+ * The shard is cut without regard to param boundaries ([OPT-INFRA] §12.1), so
+ * one rank's slice mixes decaying weights with norm gains and biases that
+ * take no weight decay ([HANDBOOK] AdamW section).  Range k covers elements
+ * [range_start[k], range_start[k+1]) (the last one ends at numel) and uses
+ * group range_group[k] in hpo_adamw_step.  range_start[0] must be 0 and the
+ * starts strictly increasing (no empty ranges).  Pointers follow the flat
+ * set's rules; a range that does not start on a 16-byte line has its first
+ * 1..3 elements stepped one at a time and the rest vectorized. */
+hpo_status hpo_set_create_flat_ranges(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
+                                      float* main_param, float* main_grad, float* exp_avg,
+                                      float* exp_avg_sq, int32_t n_ranges, const int64_t* range_start,
+                                      const int32_t* range_group, void* stream);
 
 /* Frees the set's device tables after waiting for the device to go idle.
  * NULL is accepted. */
@@ -205,9 +223,10 @@ hpo_status hpo_copy_main_to_model(hpo_set s, void* stream);
 /* Host-only queries (no device needed)                                   */
 /* ---------------------------------------------------------------------- */
 
-/* The work split a list set over these sizes would use: chunk size, number
- * of chunks (workgroups per pass) and the set's own device bytes.  Writes
- * only the outputs given (each may be NULL). */
+/* The work split a list set over these sizes would use, for tensors whose
+ * pointers are 16-byte aligned: chunk size, number of chunks (workgroups of
+ * the update pass) and the set's own device bytes.  Writes only the outputs
+ * given (each may be NULL). */
 hpo_status hpo_plan(int32_t n_tensors, const int64_t* numel, int32_t* out_chunk_elems,
                     int64_t* out_n_chunks, int64_t* out_device_bytes);
 

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <new>
 #include <string>
 #include <vector>
@@ -148,6 +149,53 @@ hpo::TensorDesc make_desc(int32_t pdt, void* param, float* master, float* grad, 
     return d;
 }
 
+/* Position of an fp32 (bf16) pointer inside its 16-byte (8-byte) line, in
+ * elements: 0..3. */
+int32_t phase32(const void* p) { return static_cast<int32_t>((reinterpret_cast<uintptr_t>(p) / 4) % 4); }
+int32_t phase16(const void* p) { return static_cast<int32_t>((reinterpret_cast<uintptr_t>(p) / 2) % 4); }
+
+/* Appends the descriptor piece(s) of one tensor.  A tensor whose five
+ * pointers sit at the same element phase of a 16-byte line (views that start
+ * a few elements into a flat buffer, shard ranges) is split into a head of
+ * fewer than 4 elements on the element-at-a-time path and a body whose
+ * pointers are all 16-byte (bf16: 8-byte) aligned.  Returns whether the
+ * tensor's body takes the vector path. */
+bool add_pieces(std::vector<hpo::TensorDesc>& out, int32_t pdt, void* param, float* master, float* grad,
+                float* m, float* v, int64_t numel, int32_t group)
+{
+    if (numel == 0) {
+        out.push_back(make_desc(pdt, param, master, grad, m, v, 0, group));
+        return false;
+    }
+    hpo::TensorDesc d = make_desc(pdt, param, master, grad, m, v, numel, group);
+    if (d.vec_ok) {
+        out.push_back(d);
+        return true;
+    }
+    const int32_t ph = phase32(master);
+    const bool same = phase32(grad) == ph && phase32(m) == ph && phase32(v) == ph &&
+                      (pdt == HPO_PARAM_FP32 || phase16(param) == ph);
+    if (!same) {
+        out.push_back(d);
+        return false;
+    }
+    const int64_t head = std::min<int64_t>((4 - ph) % 4, numel);
+    out.push_back(make_desc(pdt, param, master, grad, m, v, head, group));
+    if (numel == head)
+        return false;
+    void* p2 = (pdt == HPO_PARAM_FP32) ? nullptr : static_cast<void*>(static_cast<uint16_t*>(param) + head);
+    hpo::TensorDesc body = make_desc(pdt, p2, master + head, grad + head, m + head, v + head, numel - head, group);
+    out.push_back(body);
+    return body.vec_ok != 0;
+}
+
+void piece_sizes(const std::vector<hpo::TensorDesc>& descs, std::vector<int64_t>& sizes)
+{
+    sizes.resize(descs.size());
+    for (size_t i = 0; i < descs.size(); ++i)
+        sizes[i] = descs[i].numel;
+}
+
 void build_chunks(const int64_t* numel, int32_t n, int64_t ch, std::vector<hpo::Chunk>& out)
 {
     for (int32_t i = 0; i < n; ++i)
@@ -266,6 +314,89 @@ hpo_status hpo_plan_chunks(int32_t n_tensors, const int64_t* numel, int64_t n_ch
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+/* Builds a table-driven set from descriptor pieces (see add_pieces). */
+hpo_status create_from_pieces(hpo_set* out, int32_t param_dtype, std::vector<hpo::TensorDesc>& descs,
+                              int32_t n_tensors, int32_t n_vector, int32_t max_group, void* stream)
+{
+    if (descs.size() > 0x7FFFFFFFu)
+        return fail(HPO_EINVAL, "too many tensor pieces");
+    std::vector<int64_t> sizes;
+    piece_sizes(descs, sizes);
+    const int32_t n_pieces = static_cast<int32_t>(descs.size());
+    const int32_t ch = choose_chunk(sizes.data(), n_pieces);
+    const int64_t nc = count_chunks(sizes.data(), n_pieces, ch);
+    if (nc > 0x7FFFFFFFLL)
+        return fail(HPO_EINVAL, "set needs %lld chunks, more than one launch can hold", (long long)nc);
+
+    hpo_set s = new (std::nothrow) hpo_set_;
+    if (!s)
+        return fail(HPO_ENOMEM, "host allocation failed");
+    hipError_t e = hipGetDevice(&s->device);
+    if (e != hipSuccess) {
+        free_set(s);
+        return hip_fail(e, "hipGetDevice");
+    }
+    s->n_tensors = n_tensors;
+    s->param_dtype = param_dtype;
+    s->is_flat = 0;
+    s->max_group = max_group;
+    s->n_chunks = nc;
+    s->n_vector = n_vector;
+    for (const auto& d : descs)
+        s->numel += d.numel;
+
+    std::vector<hpo::Chunk> chunks;
+    chunks.reserve(static_cast<size_t>(nc));
+    build_chunks(sizes.data(), n_pieces, ch, chunks);
+
+    const size_t td_bytes = descs.size() * sizeof(hpo::TensorDesc);
+    const size_t ck_bytes = chunks.size() * sizeof(hpo::Chunk);
+    if (td_bytes) {
+        e = hipMalloc(reinterpret_cast<void**>(&s->d_tensors), td_bytes);
+        if (e != hipSuccess) { free_set(s); return fail(HPO_ENOMEM, "hipMalloc tensor table: %s", hipGetErrorString(e)); }
+    }
+    if (ck_bytes) {
+        e = hipMalloc(reinterpret_cast<void**>(&s->d_chunks), ck_bytes);
+        if (e != hipSuccess) { free_set(s); return fail(HPO_ENOMEM, "hipMalloc chunk table: %s", hipGetErrorString(e)); }
+    }
+    s->device_bytes = static_cast<int64_t>(td_bytes + ck_bytes);
+    s->view.chunk_elems = ch;
+    hpo_status st = alloc_partials(s);
+    if (st != HPO_OK) { free_set(s); return st; }
+    if (td_bytes) {
+        e = hipMemcpyAsync(s->d_tensors, descs.data(), td_bytes, hipMemcpyHostToDevice, as_stream(stream));
+        if (e != hipSuccess) { free_set(s); return hip_fail(e, "upload tensor table"); }
+    }
+    if (ck_bytes) {
+        e = hipMemcpyAsync(s->d_chunks, chunks.data(), ck_bytes, hipMemcpyHostToDevice, as_stream(stream));
+        if (e != hipSuccess) { free_set(s); return hip_fail(e, "upload chunk table"); }
+    }
+    e = hipStreamSynchronize(as_stream(stream));
+    if (e != hipSuccess) { free_set(s); return hip_fail(e, "hipStreamSynchronize after table upload"); }
+
+    s->view.tensors = s->d_tensors;
+    s->view.chunks = s->d_chunks;
+    s->view.is_flat = 0;
+    s->view.param_dtype = param_dtype;
+    *out = s;
+    return ok();
+}
+
+hpo_status check_dtype(int32_t param_dtype)
+{
+    if (param_dtype != HPO_PARAM_BF16 && param_dtype != HPO_PARAM_FP32)
+        return fail(HPO_EDTYPE, "param dtype %d is not supported (bf16 = 0 with an fp32 master, or fp32 = 1)", param_dtype);
+    return HPO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dtype,
                                void* const* param, float* const* main_param,
                                float* const* main_grad, float* const* exp_avg,
@@ -275,9 +406,10 @@ hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dt
     if (!out)
         return fail(HPO_EINVAL, "out is NULL");
     *out = nullptr;
-    if (param_dtype != HPO_PARAM_BF16 && param_dtype != HPO_PARAM_FP32)
-        return fail(HPO_EDTYPE, "param dtype %d is not supported (bf16 = 0 with an fp32 master, or fp32 = 1)", param_dtype);
-    hpo_status st = check_sizes(n_tensors, numel);
+    hpo_status st = check_dtype(param_dtype);
+    if (st != HPO_OK)
+        return st;
+    st = check_sizes(n_tensors, numel);
     if (st != HPO_OK)
         return st;
     if (n_tensors > 0 && (!main_param || !main_grad || !exp_avg || !exp_avg_sq))
@@ -296,86 +428,86 @@ hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dt
         if (g > max_group)
             max_group = g;
     }
-    const int32_t ch = choose_chunk(numel, n_tensors);
-    const int64_t nc = count_chunks(numel, n_tensors, ch);
-    if (nc > 0x7FFFFFFFLL)
-        return fail(HPO_EINVAL, "set needs %lld chunks, more than one launch can hold", (long long)nc);
+    std::vector<hpo::TensorDesc> descs;
+    descs.reserve(static_cast<size_t>(n_tensors));
+    int32_t n_vector = 0;
+    for (int32_t i = 0; i < n_tensors; ++i)
+        n_vector += add_pieces(descs, param_dtype, param ? param[i] : nullptr, main_param[i], main_grad[i],
+                               exp_avg[i], exp_avg_sq[i], numel[i], group_index ? group_index[i] : 0);
+    return create_from_pieces(out, param_dtype, descs, n_tensors, n_vector, max_group, stream);
+}
 
-    hpo_set s = new (std::nothrow) hpo_set_;
-    if (!s)
-        return fail(HPO_ENOMEM, "host allocation failed");
-    hipError_t e = hipGetDevice(&s->device);
-    if (e != hipSuccess) {
-        free_set(s);
-        return hip_fail(e, "hipGetDevice");
+hpo_status hpo_set_create_flat_ranges(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
+                                      float* main_param, float* main_grad, float* exp_avg,
+                                      float* exp_avg_sq, int32_t n_ranges, const int64_t* range_start,
+                                      const int32_t* range_group, void* stream)
+{
+    if (!out)
+        return fail(HPO_EINVAL, "out is NULL");
+    *out = nullptr;
+    hpo_status st = check_dtype(param_dtype);
+    if (st != HPO_OK)
+        return st;
+    st = check_sizes(1, &numel);
+    if (st != HPO_OK)
+        return st;
+    st = check_tensor(0, param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel);
+    if (st != HPO_OK)
+        return st;
+    if (n_ranges < 1 || !range_start || !range_group)
+        return fail(HPO_EINVAL, "a flat shard with ranges needs n_ranges >= 1 and both range arrays");
+    if (range_start[0] != 0)
+        return fail(HPO_EINVAL, "range_start[0] must be 0 (got %lld)", (long long)range_start[0]);
+    int32_t max_group = 0;
+    for (int32_t k = 0; k < n_ranges; ++k) {
+        const int64_t end = k + 1 < n_ranges ? range_start[k + 1] : numel;
+        if (end <= range_start[k] || end > numel)
+            return fail(HPO_EINVAL, "range %d [%lld, %lld) is empty, unordered or past numel %lld", k,
+                        (long long)range_start[k], (long long)end, (long long)numel);
+        if (range_group[k] < 0 || range_group[k] >= HPO_MAX_GROUPS)
+            return fail(HPO_EINVAL, "range_group[%d] = %d is outside [0, %d)", k, range_group[k], HPO_MAX_GROUPS);
+        max_group = std::max(max_group, range_group[k]);
     }
-    s->n_tensors = n_tensors;
-    s->param_dtype = param_dtype;
-    s->is_flat = 0;
-    s->max_group = max_group;
-    s->n_chunks = nc;
-
-    std::vector<hpo::TensorDesc> descs(static_cast<size_t>(n_tensors));
-    for (int32_t i = 0; i < n_tensors; ++i) {
-        descs[i] = make_desc(param_dtype, param ? param[i] : nullptr, main_param[i], main_grad[i], exp_avg[i],
-                             exp_avg_sq[i], numel[i], group_index ? group_index[i] : 0);
-        s->numel += numel[i];
-        s->n_vector += descs[i].vec_ok;
+    std::vector<hpo::TensorDesc> descs;
+    descs.reserve(static_cast<size_t>(n_ranges) + 1);
+    int32_t n_vector = 0;
+    for (int32_t k = 0; k < n_ranges; ++k) {
+        const int64_t a = range_start[k];
+        const int64_t len = (k + 1 < n_ranges ? range_start[k + 1] : numel) - a;
+        void* p = (param_dtype == HPO_PARAM_FP32 || !param) ? param
+                                                             : static_cast<void*>(static_cast<uint16_t*>(param) + a);
+        n_vector += add_pieces(descs, param_dtype, p, main_param + a, main_grad + a, exp_avg + a, exp_avg_sq + a,
+                               len, range_group[k]);
     }
-    std::vector<hpo::Chunk> chunks;
-    chunks.reserve(static_cast<size_t>(nc));
-    build_chunks(numel, n_tensors, ch, chunks);
-
-    const size_t td_bytes = descs.size() * sizeof(hpo::TensorDesc);
-    const size_t ck_bytes = chunks.size() * sizeof(hpo::Chunk);
-    if (td_bytes) {
-        e = hipMalloc(reinterpret_cast<void**>(&s->d_tensors), td_bytes);
-        if (e != hipSuccess) { free_set(s); return fail(HPO_ENOMEM, "hipMalloc tensor table: %s", hipGetErrorString(e)); }
-    }
-    if (ck_bytes) {
-        e = hipMalloc(reinterpret_cast<void**>(&s->d_chunks), ck_bytes);
-        if (e != hipSuccess) { free_set(s); return fail(HPO_ENOMEM, "hipMalloc chunk table: %s", hipGetErrorString(e)); }
-    }
-    s->device_bytes = static_cast<int64_t>(td_bytes + ck_bytes);
-    s->view.chunk_elems = ch;
-    st = alloc_partials(s);
-    if (st != HPO_OK) { free_set(s); return st; }
-    if (td_bytes) {
-        e = hipMemcpyAsync(s->d_tensors, descs.data(), td_bytes, hipMemcpyHostToDevice, as_stream(stream));
-        if (e != hipSuccess) { free_set(s); return hip_fail(e, "upload tensor table"); }
-    }
-    if (ck_bytes) {
-        e = hipMemcpyAsync(s->d_chunks, chunks.data(), ck_bytes, hipMemcpyHostToDevice, as_stream(stream));
-        if (e != hipSuccess) { free_set(s); return hip_fail(e, "upload chunk table"); }
-    }
-    e = hipStreamSynchronize(as_stream(stream));
-    if (e != hipSuccess) { free_set(s); return hip_fail(e, "hipStreamSynchronize after table upload"); }
-
-    s->view.tensors = s->d_tensors;
-    s->view.chunks = s->d_chunks;
-    s->view.chunk_elems = ch;
-    s->view.is_flat = 0;
-    s->view.param_dtype = param_dtype;
-    *out = s;
-    return ok();
+    return create_from_pieces(out, param_dtype, descs, n_ranges, n_vector, max_group, stream);
 }
 
 hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
                                float* main_param, float* main_grad, float* exp_avg,
                                float* exp_avg_sq, void* stream)
 {
-    (void)stream;
     if (!out)
         return fail(HPO_EINVAL, "out is NULL");
     *out = nullptr;
-    if (param_dtype != HPO_PARAM_BF16 && param_dtype != HPO_PARAM_FP32)
-        return fail(HPO_EDTYPE, "param dtype %d is not supported (bf16 = 0 with an fp32 master, or fp32 = 1)", param_dtype);
-    hpo_status st = check_sizes(1, &numel);
+    hpo_status st = check_dtype(param_dtype);
+    if (st != HPO_OK)
+        return st;
+    st = check_sizes(1, &numel);
     if (st != HPO_OK)
         return st;
     st = check_tensor(0, param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel);
     if (st != HPO_OK)
         return st;
+    if (numel > 0 && !make_desc(param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0).vec_ok) {
+        /* a flat range that does not start on a 16-byte line: table-driven,
+         * with the head peeled off (same results, vector body) */
+        std::vector<hpo::TensorDesc> descs;
+        const int32_t nv = add_pieces(descs, param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0);
+        st = create_from_pieces(out, param_dtype, descs, 1, nv, 0, stream);
+        if (st == HPO_OK)
+            (*out)->is_flat = 1;
+        return st;
+    }
     const int32_t ch = choose_chunk(&numel, 1);
     const int64_t nc = count_chunks(&numel, 1, ch);
     if (nc > 0x7FFFFFFFLL)

@@ -57,6 +57,8 @@ SIGNATURES = {
     "hpo_set_create_list": (_I32, [ctypes.POINTER(_P), _I32, _I32, _PP, _PP, _PP, _PP, _PP,
                                    ctypes.POINTER(_I64), ctypes.POINTER(_I32), _P]),
     "hpo_set_create_flat": (_I32, [ctypes.POINTER(_P), _I64, _I32, _P, _P, _P, _P, _P, _P]),
+    "hpo_set_create_flat_ranges": (_I32, [ctypes.POINTER(_P), _I64, _I32, _P, _P, _P, _P, _P, _I32,
+                                          ctypes.POINTER(_I64), ctypes.POINTER(_I32), _P]),
     "hpo_set_destroy": (_I32, [_P]),
     "hpo_set_info": (_I32, [_P, ctypes.POINTER(hpo_set_info_t)]),
     "hpo_unscale_check_inf": (_I32, [_P, ctypes.c_float, _P, _P]),
@@ -217,6 +219,31 @@ def hpo_set_create_flat(param: Optional[torch.Tensor], main_param: torch.Tensor,
                                     _ptr(main_param), _ptr(main_grad), _ptr(exp_avg), _ptr(exp_avg_sq),
                                     _stream(stream))
     _check(st, "hpo_set_create_flat")
+    return HpoSet(out, (param, main_param, main_grad, exp_avg, exp_avg_sq))
+
+
+def hpo_set_create_flat_ranges(param: Optional[torch.Tensor], main_param: torch.Tensor, main_grad: torch.Tensor,
+                               exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, range_start: Sequence[int],
+                               range_group: Sequence[int], param_dtype: Optional[int] = None, stream=None) -> HpoSet:
+    for what, t in (("main_param", main_param), ("main_grad", main_grad), ("exp_avg", exp_avg),
+                    ("exp_avg_sq", exp_avg_sq)):
+        _require(t, torch.float32, what, 0)
+        if t.numel() != main_param.numel():
+            raise ValueError(f"{what} has the wrong number of elements")
+    if param_dtype is None:
+        param_dtype = HPO_PARAM_FP32 if param is None else param_dtype_code(param.dtype)
+    if param is not None and (not param.is_contiguous() or param.numel() != main_param.numel()):
+        raise ValueError("param must be contiguous with main_param's size")
+    if len(range_start) != len(range_group):
+        raise ValueError("range_start and range_group must have the same length")
+    k = len(range_start)
+    c_start = (ctypes.c_int64 * max(k, 1))(*range_start)
+    c_group = (ctypes.c_int32 * max(k, 1))(*range_group)
+    out = ctypes.c_void_p()
+    st = load().hpo_set_create_flat_ranges(ctypes.byref(out), main_param.numel(), param_dtype, _ptr(param),
+                                           _ptr(main_param), _ptr(main_grad), _ptr(exp_avg), _ptr(exp_avg_sq),
+                                           k, c_start, c_group, _stream(stream))
+    _check(st, "hpo_set_create_flat_ranges")
     return HpoSet(out, (param, main_param, main_grad, exp_avg, exp_avg_sq))
 
 

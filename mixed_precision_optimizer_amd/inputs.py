@@ -127,6 +127,45 @@ def zero_shard(numel: int = 8_750_000_000) -> Workload:
                     steps=3, grad_std=[1e-4], flat=True, no_decay_1d=False)
 
 
+def llama70b_shapes():
+    """(name, shape) of a Llama-70B-shaped parameter list: 80 layers, hidden
+    8192, FFN 28672, 8 KV heads of 128, vocab 128256, untied embedding/head."""
+    h, f, kv, vocab, layers = 8192, 28672, 8 * 128, 128256, 80
+    out = [("embed", (vocab, h))]
+    for l in range(layers):
+        out += [(f"l{l}.q", (h, h)), (f"l{l}.k", (kv, h)), (f"l{l}.v", (kv, h)),
+                (f"l{l}.o", (h, h)), (f"l{l}.gate", (f, h)), (f"l{l}.up", (f, h)),
+                (f"l{l}.down", (h, f)), (f"l{l}.attn_norm", (h,)), (f"l{l}.mlp_norm", (h,))]
+    out += [("final_norm", (h,)), ("lm_head", (vocab, h))]
+    return out
+
+
+def zero_shard_ranges(rank: int = 3, dp: int = 8) -> Workload:
+    """Rank `rank`'s contiguous 1/dp slice of the flat param buffer of a
+    Llama-70B-shaped model ("02 · Optimizer：算法与 infra" §12.1: the buffer is
+    split evenly by data-parallel rank without regard to param boundaries).
+    Params start on 64-element boundaries; the buffer is padded to a multiple
+    of 64 * dp.  Each range of the slice carries the group of the param it
+    belongs to (the padding after a param, that of the param before it); the
+    1-D norm gains take no weight decay."""
+    shapes = llama70b_shapes()
+    sizes = [int(np.prod(sh)) for _, sh in shapes]
+    offs, total = offsets(sizes)
+    total = (total + 64 * dp - 1) // (64 * dp) * (64 * dp)
+    shard = total // dp
+    lo, hi = rank * shard, (rank + 1) * shard
+    starts, dims = [], []
+    for (name, sh), o, n in zip(shapes, offs, sizes):
+        end = o + (n + ALIGN_ELEMS - 1) // ALIGN_ELEMS * ALIGN_ELEMS  # param + its padding
+        a, b = max(o, lo), min(end, hi)
+        if a < b:
+            starts.append(a - lo)
+            dims.append(len(sh))
+    lens = [b - a for a, b in zip(starts, starts[1:] + [shard])]
+    return Workload(f"zero1_shard_ranges_llama70b_rank{rank}_of_{dp}", lens, dims, lr=1e-3, weight_decay=0.1,
+                    max_norm=1.0, steps=3, grad_std=[1e-4] * len(lens), flat=True, no_decay_1d=True)
+
+
 def inf_position(w: Workload) -> tuple:
     """(tensor index, element) of the injected +inf: the last element of the
     highest-index tensor whose size is not a multiple of 4 (so it sits on the
@@ -193,7 +232,10 @@ def allocate(w: Workload, device) -> Buffers:
     state: master N(0,1) from ``master_seed``, m = v = 0, param = bf16 cast of
     the master (torch's cast; the param's initial value is an input)."""
     if w.flat:
-        offs, total = [0], w.numel
+        # a flat shard, possibly cut into ranges of different groups: the
+        # ranges are consecutive, with no gaps
+        offs = [int(x) for x in np.cumsum([0] + w.numels[:-1])]
+        total = w.numel
     else:
         offs, total = offsets(w.numels)
     f32 = dict(dtype=torch.float32, device=device)

@@ -8,8 +8,6 @@ mixed_precision_optimizer_amd.inputs), and runs its own steps.
 from __future__ import annotations
 
 import concurrent.futures as cf
-import math
-import os
 
 import numpy as np
 import pytest
@@ -45,6 +43,12 @@ def bf16_of(theta: np.ndarray) -> np.ndarray:
 def make_set(bufs, stream=None):
     from mixed_precision_optimizer_amd import hpo
     w = bufs.workload
+    pdt = hpo.HPO_PARAM_FP32 if w.param_dtype == "fp32" else hpo.HPO_PARAM_BF16
+    if w.flat and w.n_tensors > 1:
+        return hpo.hpo_set_create_flat_ranges(None if w.param_dtype == "fp32" else bufs.param, bufs.master, bufs.grad,
+                                              bufs.exp_avg, bufs.exp_avg_sq, bufs.offs,
+                                              [w.group_of(i) for i in range(w.n_tensors)], param_dtype=pdt,
+                                              stream=stream)
     if w.flat:
         return hpo.hpo_set_create_flat(None if w.param_dtype == "fp32" else bufs.param, bufs.master, bufs.grad,
                                        bufs.exp_avg, bufs.exp_avg_sq, stream=stream,
@@ -86,10 +90,11 @@ def compare_tensor(tag, gpu, orc_new, orc_prev, G, *, inv, clip, C, c64, lr, wd,
 
 
 def read_state(bufs, i=None, lo=0, hi=None):
-    """GPU state of tensor i (or the flat set) in element range [lo, hi)."""
+    """GPU state of tensor (or range) i, or of the whole flat set when i is
+    None, in element range [lo, hi)."""
     w = bufs.workload
-    off = 0 if w.flat else bufs.offs[i]
-    n = w.numel if w.flat else w.numels[i]
+    off = 0 if i is None else bufs.offs[i]
+    n = w.numel if i is None else w.numels[i]
     hi = n if hi is None else hi
     a, b = off + lo, off + hi
     out = {"theta": to_np(bufs.master[a:b]), "m": to_np(bufs.exp_avg[a:b]), "v": to_np(bufs.exp_avg_sq[a:b])}
@@ -101,39 +106,36 @@ def read_state(bufs, i=None, lo=0, hi=None):
 # ---------------------------------------------------------------------------
 # full-size norms: stream the stored grads to the host and sum there
 # ---------------------------------------------------------------------------
-def oracle_sumsq_streamed(orc, grad: torch.Tensor, ranges, inv: float, chunk: int = 1 << 28,
+def oracle_sumsq_streamed(orc, grad: torch.Tensor, ranges, inv: float, chunk: int = 1 << 27,
                           threads: int = 8) -> float:
     """Oracle sum of squares over the given (offset, length) ranges of a flat
-    device grad buffer: each range is copied to pinned host memory in slices
-    and summed by the oracle's plain loop; slice sums are added in range order."""
-    host = [torch.empty(chunk, dtype=torch.float32, pin_memory=True) for _ in range(2)]
+    device grad buffer: each range is copied to pinned host memory in slices,
+    each slice is summed by the oracle's plain loop (up to `threads` slices at
+    once), and the slice sums are added in range order."""
+    host = [torch.empty(chunk, dtype=torch.float32, pin_memory=True) for _ in range(threads)]
     pieces = []
     for off, n in ranges:
         for a in range(0, n, chunk):
             pieces.append((off + a, min(chunk, n - a)))
     sums = [0.0] * len(pieces)
-    pool = cf.ThreadPoolExecutor(max_workers=threads)
-    futs = []
-    pending = []
-    buf_in_use = [None, None]
-    for k, (off, n) in enumerate(pieces):
-        slot = k % 2
-        if buf_in_use[slot] is not None:
-            buf_in_use[slot].result()
-        host[slot][:n].copy_(grad[off:off + n])
-        arr = host[slot][:n].numpy()
+    busy = [None] * threads
+    with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        for k, (off, n) in enumerate(pieces):
+            slot = k % threads
+            if busy[slot] is not None:
+                busy[slot].result()
+            host[slot][:n].copy_(grad[off:off + n])
+            arr = host[slot][:n].numpy()
 
-        def work(arr=arr, k=k):
-            sums[k] = orc.sumsq(arr, inv)
-        fut = pool.submit(work)
-        buf_in_use[slot] = fut
-        futs.append(fut)
-    for f in futs:
-        f.result()
-    pool.shutdown()
+            def work(arr=arr, k=k):
+                sums[k] = orc.sumsq(arr, inv)
+            busy[slot] = pool.submit(work)
+        for f in busy:
+            if f is not None:
+                f.result()
     total = 0.0
-    for s in sums:
-        total = total + s
+    for x in sums:
+        total = total + x
     return total
 
 

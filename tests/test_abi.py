@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(H):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     lib = H.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -85,6 +85,29 @@ def test_list_validation(H):
     bad = (ctypes.c_int64 * 2)(4, -8)
     st = L.hpo_set_create_list(ctypes.byref(out), 2, 0, ptrs, ptrs, ptrs, ptrs, ptrs, bad, None, None)
     assert st == H.HPO_EINVAL and "numel[1]" in H.hpo_last_error()
+
+
+def test_flat_ranges_validation(H):
+    L = H.load()
+    out = ctypes.c_void_p()
+    P = [ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000)]
+
+    def call(n, starts, groups):
+        k = len(starts)
+        cs = (ctypes.c_int64 * max(k, 1))(*starts)
+        cg = (ctypes.c_int32 * max(k, 1))(*groups)
+        st = L.hpo_set_create_flat_ranges(ctypes.byref(out), n, 0, *P, k, cs, cg, None)
+        return st, H.hpo_last_error()
+    st, msg = call(100, [5, 50], [0, 1])
+    assert st == H.HPO_EINVAL and "range_start[0]" in msg
+    st, msg = call(100, [0, 50, 50], [0, 1, 0])
+    assert st == H.HPO_EINVAL and "range 1" in msg
+    st, msg = call(100, [0, 120], [0, 1])
+    assert st == H.HPO_EINVAL and "past numel" in msg
+    st, msg = call(100, [0, 50], [0, 16])
+    assert st == H.HPO_EINVAL and "range_group[1]" in msg
+    st, msg = call(100, [], [])
+    assert st == H.HPO_EINVAL
 
 
 def test_step_calls_reject_null_set(H):

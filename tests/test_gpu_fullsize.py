@@ -75,7 +75,7 @@ class Sample:
         self.bufs = bufs
         self.picks = picks
         w = bufs.workload
-        offs = [0] if w.flat else bufs.offs
+        offs = bufs.offs
         idx = np.concatenate([np.arange(offs[i] + lo, offs[i] + hi, dtype=np.int64) for i, lo, hi in picks])
         self.idx = torch.from_numpy(idx).to(DEV)
         self.seg = []
@@ -99,7 +99,7 @@ class Sample:
 def _ranges(bufs):
     w = bufs.workload
     if w.flat:
-        return [(0, w.numel)]
+        return [(0, w.numel)]  # a flat shard has no gaps: stream it as one range
     return [(bufs.offs[i], n) for i, n in enumerate(w.numels) if n > 0]
 
 
@@ -194,4 +194,14 @@ def test_ragged_20000_tensors_with_skip(H, orc):
     w = inputs.ragged()
     stats = _run_fullsize(H, orc, w, dict(head=256, windows_big=1, window=4096, whole_below=1024))
     assert stats["skipped"] == [3]
+    assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.timeout(900)
+def test_zero_shard_with_param_ranges_llama70b(H, orc):
+    """Rank 3 of 8 of a Llama-70B-shaped flat buffer (8.82e9 elements): 95
+    ranges, the 1-D norm gains in the no-decay group, clip 1.0, 3 steps."""
+    from mixed_precision_optimizer_amd import inputs
+    w = inputs.zero_shard_ranges()
+    stats = _run_fullsize(H, orc, w, dict(head=2048, windows_big=2, window=16384, whole_below=8192))
     assert stats["bit_equal"] == stats["compared"]

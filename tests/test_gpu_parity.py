@@ -36,7 +36,7 @@ def _oracle_tensors(orc, bufs):
     w = bufs.workload
     out = []
     for i in range(w.n_tensors):
-        st = read_state(bufs, i) if not w.flat else read_state(bufs)
+        st = read_state(bufs, i)
         T = orc.OTensor(st["theta"], st["m"], st["v"], st.get("p"), w.group_of(i))
         out.append(T)
     return out
@@ -44,8 +44,6 @@ def _oracle_tensors(orc, bufs):
 
 def _grads_np(bufs):
     w = bufs.workload
-    if w.flat:
-        return [to_np(bufs.grad[:w.numel])]
     return [to_np(bufs.view(bufs.grad, i)) for i in range(w.n_tensors)]
 
 
@@ -69,7 +67,7 @@ def _run_parity(H, orc, w, steps=None, stats=None, inplace=False):
         assert opt.t == O.t
         if not r.applied:
             for i, T in enumerate(Ts):
-                st = read_state(bufs, i) if not w.flat else read_state(bufs)
+                st = read_state(bufs, i)
                 for key in ("theta", "m", "v"):
                     assert np.array_equal(st[key].view(np.uint32), getattr(T, key).view(np.uint32))
                 if T.p is not None:
@@ -80,7 +78,7 @@ def _run_parity(H, orc, w, steps=None, stats=None, inplace=False):
         stats.setdefault("norm_rel", []).append(abs(norm - r.norm64) / max(r.norm64, 1e-300))
         c64 = w.max_norm / (float(np.float32(r.norm32)) + 1e-6) if r.clip_applied else 1.0
         for i, T in enumerate(Ts):
-            st = read_state(bufs, i) if not w.flat else read_state(bufs)
+            st = read_state(bufs, i)
             lr, wd = w.groups()[T.group]
             compare_tensor(f"{w.name} step {k} tensor {i}", st, T, prev[i], G[i], inv=w.inv_scale(),
                            clip=r.clip_applied, C=r.clip_C, c64=c64, lr=lr, wd=wd, t=O.t, mode=w.mode,
@@ -253,24 +251,28 @@ def test_flat_and_list_sets_agree_bitwise(H):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
-def test_misaligned_tensors_take_the_scalar_path(H, orc):
-    """Views that start 1..3 elements into a buffer break 16-byte alignment;
-    results must be the same bits as the aligned vector path."""
+def test_misaligned_tensors_peel_or_go_scalar(H, orc):
+    """Views that start 1..3 elements into their buffers: when all five
+    pointers share the offset, the head is peeled and the body vectorized;
+    when they do not, the whole tensor runs element by element.  Every
+    layout must give the same bits (and the oracle's)."""
     banner("misaligned")
     n = 50_001
     rng = np.random.default_rng(6)
     th0 = rng.standard_normal(n).astype(np.float32)
     G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
     res = []
-    for shift in (0, 1, 2, 3):
+    layouts = [(0, 0), (1, 1), (2, 2), (3, 3), (1, 2), (0, 3)]  # (shift of master/m/v/param, shift of grad)
+    for shift, gshift in layouts:
         big = [torch.zeros(n + 4, device=DEV) for _ in range(4)]
         pb = torch.zeros(n + 4, dtype=torch.bfloat16, device=DEV)
-        th, g, m, v = (b[shift:shift + n] for b in big)
+        th, m, v = (b[shift:shift + n] for b in big[:3])
+        g = big[3][gshift:gshift + n]
         p = pb[shift:shift + n]
         th.copy_(torch.from_numpy(th0))
         g.copy_(torch.from_numpy(G))
         hset = H.hpo_set_create_list([p], [th], [g], [m], [v])
-        assert hset.info().n_vector == (1 if shift == 0 else 0)
+        assert hset.info().n_vector == (1 if shift == gshift else 0), (shift, gshift)
         norm = torch.zeros(1, device=DEV)
         H.hpo_grad_global_norm(hset, 1.0, norm, None)
         H.hpo_adamw_step(hset, H.make_cfg(mode=1), [(1e-3, 0.1)], None, 1, 1.0, 1.0, norm, None)
@@ -283,6 +285,103 @@ def test_misaligned_tensors_take_the_scalar_path(H, orc):
     T = orc.OTensor.fresh(th0)
     orc.OracleOptimizer([T], orc.Hyper(mode=1), [(1e-3, 0.1)], max_norm=1.0).step([G])
     assert np.array_equal(res[0][0].view(np.uint32), T.theta.view(np.uint32))
+
+
+def _mini_model_layout():
+    """(sizes, ndims) of a small Llama-like model and the 64-element-aligned
+    start of each param in one flat buffer (the DDP buffer layout)."""
+    h, f, vocab, layers = 512, 1792, 3000, 3
+    shapes = [(vocab, h)]
+    for _ in range(layers):
+        shapes += [(h, h), (128, h), (128, h), (h, h), (f, h), (f, h), (h, f), (h,), (h,)]
+    shapes += [(h,), (vocab, h)]
+    sizes = [int(np.prod(s)) for s in shapes]
+    ndims = [len(s) for s in shapes]
+    from mixed_precision_optimizer_amd.inputs import offsets
+    offs, total = offsets(sizes)
+    return sizes, ndims, offs, total
+
+
+def _cuts():
+    sizes, ndims, offs, total = _mini_model_layout()
+    first_norm = next(o for o, d in zip(offs, ndims) if d == 1)
+    return [0, 1_530_001, first_norm - 1001]
+
+
+@pytest.mark.parametrize("cut", _cuts())
+def test_flat_shard_with_param_ranges(H, orc, cut):
+    """One data-parallel rank's slice of a flat param buffer, cut at an
+    arbitrary element: the ranges of 1-D params take no weight decay.  Checked
+    against the oracle (range by range, with its group) and bit for bit
+    against the same ranges given as a list set."""
+    banner(f"flat shard with ranges, cut at {cut}")
+    sizes, ndims, offs, total = _mini_model_layout()
+    shard_len = min(6_000_000, total - cut)
+    lo, hi = cut, cut + shard_len
+    starts, groups = [], []
+    for n, d, o in zip(sizes, ndims, offs):
+        a, b = max(o, lo), min(o + n, hi)
+        if a < b:
+            starts.append(a - lo)
+            groups.append(1 if d == 1 else 0)
+        # the 64-element padding after a param belongs to no param: give it the
+        # preceding param's group (its grads are zero, it is stepped harmlessly)
+    merged_s, merged_g = [], []
+    for s_, g_ in zip(starts, groups):
+        if merged_g and merged_g[-1] == g_:
+            continue
+        merged_s.append(s_)
+        merged_g.append(g_)
+    if merged_s[0] != 0:
+        merged_s[0] = 0
+    rng = np.random.default_rng(80 + cut)
+    th0 = rng.standard_normal(shard_len).astype(np.float32)
+    groups_lrwd = [(1e-3, 0.1), (1e-3, 0.0)]
+    bounds = merged_s[1:] + [shard_len]
+    results = {}
+    for kind in ("ranges", "list"):
+        th = torch.from_numpy(th0.copy()).to(DEV)
+        p = th.to(torch.bfloat16)
+        g = torch.zeros(shard_len, device=DEV)
+        m = torch.zeros(shard_len, device=DEV)
+        v = torch.zeros(shard_len, device=DEV)
+        if kind == "ranges":
+            hset = H.hpo_set_create_flat_ranges(p, th, g, m, v, merged_s, merged_g)
+        else:
+            views = lambda t: [t[a:b] for a, b in zip(merged_s, bounds)]
+            hset = H.hpo_set_create_list(views(p), views(th), views(g), views(m), views(v), merged_g)
+        from mixed_precision_optimizer_amd import MixedPrecisionAdamW
+        opt = MixedPrecisionAdamW(hset, groups_lrwd, max_norm=1.0, loss_scale=1024.0)
+        grng = np.random.default_rng(90 + cut)
+        states = []
+        for k in range(3):
+            G = (grng.standard_normal(shard_len) * 1e-3 * 1024).astype(np.float32)
+            g.copy_(torch.from_numpy(G))
+            applied, norm = opt.step()
+            assert applied
+            states.append((to_np(th), to_np(m), to_np(v), to_np(p), norm))
+        results[kind] = states
+        hset.close()
+    for a, b in zip(results["ranges"], results["list"]):
+        for x, y in zip(a[:4], b[:4]):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+        assert a[4] == b[4]
+    # oracle: one OTensor per range with its group, the same grads, every step
+    Ts = [orc.OTensor.fresh(th0[a:b], group=gid) for a, b, gid in zip(merged_s, bounds, merged_g)]
+    O = orc.OracleOptimizer(Ts, orc.Hyper(), groups_lrwd, max_norm=1.0)
+    grng = np.random.default_rng(90 + cut)
+    for k in range(3):
+        G = (grng.standard_normal(shard_len) * 1e-3 * 1024).astype(np.float32)
+        r = O.step([np.ascontiguousarray(G[a:b]) for a, b in zip(merged_s, bounds)],
+                   inv_scale=float(np.float32(1 / 1024)))
+        th_g, m_g, v_g, p_g, norm = results["ranges"][k]
+        assert abs(norm - r.norm64) <= 1e-5 * r.norm64
+        for got, key in ((th_g, "theta"), (m_g, "m"), (v_g, "v")):
+            want = np.concatenate([getattr(T, key) for T in Ts])
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (k, key)
+        assert np.array_equal(p_g, np.concatenate([T.p for T in Ts]))
+    # the no-decay ranges really took no decay: with wd = 0 they differ from a decayed step
+    assert len(set(merged_g)) == 2
 
 
 def test_fp32_param_set_has_no_writeback(H, orc):
@@ -343,3 +442,125 @@ def test_bf16_writeback_exhaustive(H, orc):
         assert np.all((got[nan] & 0x7FFF) > 0x7F80)
         print(f"  patterns {first:#x}.. ok", flush=True)
     hset.close()
+
+
+# ---------------------------------------------------------------------------
+# degenerate cases of the method, each against the oracle element by element
+# ---------------------------------------------------------------------------
+def _one_shot(H, orc, th0, G, *, mode=0, lr=1e-3, wd=0.1, b1=0.9, b2=0.999, eps=1e-8, t=1, inv=1.0,
+              max_norm=0.0, m0=None, v0=None):
+    """One step on the GPU (list set of one tensor) and in the oracle from the
+    same state; returns both states."""
+    n = th0.size
+    m0 = np.zeros(n, np.float32) if m0 is None else m0
+    v0 = np.zeros(n, np.float32) if v0 is None else v0
+    th = torch.from_numpy(th0.copy()).to(DEV)
+    p = torch.from_numpy(orc.bf16_rne(th0).view(np.int16)).to(DEV).view(torch.bfloat16)
+    g = torch.from_numpy(G.copy()).to(DEV)
+    m = torch.from_numpy(m0.copy()).to(DEV)
+    v = torch.from_numpy(v0.copy()).to(DEV)
+    hset = H.hpo_set_create_list([p], [th], [g], [m], [v])
+    norm = torch.zeros(1, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.hpo_grad_global_norm(hset, inv, norm, flag)
+    H.hpo_adamw_step(hset, H.make_cfg(b1, b2, eps, mode), [(lr, wd)], None, t, inv, max_norm, norm, None)
+    torch.cuda.synchronize()
+    gpu = {"theta": to_np(th), "m": to_np(m), "v": to_np(v), "p": to_np(p), "norm": norm.item(),
+           "flag": flag.item()}
+    hset.close()
+    T = orc.OTensor(th0.copy(), m0.copy(), v0.copy(), orc.bf16_rne(th0))
+    r = orc.oracle_step([T], [G], orc.Hyper(b1, b2, eps, mode), [(lr, wd)], t, inv, max_norm)
+    return gpu, T, r
+
+
+def _same_bits(a, b):
+    """Bit-equal, except that NaNs only need to agree as NaNs (their payload
+    is not fixed by the pages)."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if a.dtype == np.uint16:
+        an = (a & 0x7FFF) > 0x7F80
+        bn = (b & 0x7FFF) > 0x7F80
+    else:
+        an, bn = np.isnan(a), np.isnan(b)
+    assert np.array_equal(an, bn)
+    assert np.array_equal(a[~an].view(np.uint8) if a.dtype != np.uint16 else a[~an],
+                          b[~bn].view(np.uint8) if b.dtype != np.uint16 else b[~bn])
+
+
+def _check_same(gpu, T):
+    for key in ("theta", "m", "v", "p"):
+        _same_bits(gpu[key], getattr(T, key))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_degenerate_hyperparameters(H, orc, mode):
+    banner(f"degenerate hyperparameters mode={mode}")
+    rng = np.random.default_rng(70)
+    n = 40_000
+    th0 = rng.standard_normal(n).astype(np.float32)
+    G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    G[:100] = 0.0
+    m0 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v0 = ((rng.standard_normal(n) * 1e-3) ** 2).astype(np.float32)
+    cases = [dict(b1=0.0, b2=0.0, t=3), dict(eps=0.0, t=1), dict(t=1_000_000, m0=m0, v0=v0),
+             dict(lr=0.0, t=2, m0=m0, v0=v0), dict(wd=0.0, t=5, m0=m0, v0=v0), dict(b1=0.5, b2=0.5, t=2, m0=m0, v0=v0)]
+    for kw in cases:
+        gpu, T, r = _one_shot(H, orc, th0, G, mode=mode, **kw)
+        _check_same(gpu, T)
+        if kw.get("eps") == 0.0 and mode == 0:
+            # zero grad, eps = 0: 0 / (sqrt(0) + 0) -- the method itself yields NaN
+            # (in the L2 mode the grad is wd * theta, not zero)
+            assert np.isnan(T.theta[:100]).all()
+
+
+def test_extreme_values(H, orc):
+    """Huge grads (g^2 overflows fp32 in v), subnormal grads and masters,
+    masters near the bf16 overflow boundary, zeros of both signs."""
+    banner("extreme values")
+    fmax = np.finfo(np.float32).max
+    th0 = np.array([1.0, -1.0, 1e-40, -1e-40, 0.0, -0.0, fmax, -fmax, 3.3e38, 1e30, 2.0 ** -126, 5.0], np.float32)
+    G = np.array([1e30, -1e30, 1e-40, -1e-44, 0.0, -0.0, 1.0, -1.0, 1e-3, 1e20, 2.0 ** -130, 3e38], np.float32)
+    for mode in (0, 1):
+        for max_norm in (0.0, 1.0):
+            gpu, T, r = _one_shot(H, orc, th0, G, mode=mode, max_norm=max_norm)
+            _check_same(gpu, T)
+
+
+def test_clip_boundary_and_disabled(H, orc):
+    """The norm sits exactly at max_norm (the strict '< 1' test with the 1e-6
+    guard still clips by 1/(1+1e-6)); max_norm <= 0 disables clipping."""
+    banner("clip boundary")
+    G = np.zeros(4096, np.float32)
+    G[0], G[1] = 0.6, 0.8  # norm 1.0 (up to fp32 rounding of the operands)
+    th0 = np.linspace(-1, 1, 4096, dtype=np.float32)
+    for max_norm in (1.0, float(np.float32(np.sqrt(np.float32(0.6) ** 2 + np.float32(0.8) ** 2))), 0.0, -5.0, 1e9):
+        gpu, T, r = _one_shot(H, orc, th0, G, max_norm=max_norm)
+        _check_same(gpu, T)
+        assert gpu["norm"] == r.norm32
+
+
+def test_zero_grads_leave_state_alone(H, orc):
+    """Zero grads with wd = 0 from a fresh state: master, m, v and param
+    unchanged bit for bit, over several steps, both modes."""
+    banner("zero grads")
+    rng = np.random.default_rng(71)
+    n = 12_345
+    th0 = rng.standard_normal(n).astype(np.float32)
+    for mode in (0, 1):
+        th = torch.from_numpy(th0.copy()).to(DEV)
+        p = th.to(torch.bfloat16)
+        p0 = p.clone()
+        g = torch.zeros(n, device=DEV)
+        m = torch.zeros(n, device=DEV)
+        v = torch.zeros(n, device=DEV)
+        hset = H.hpo_set_create_list([p], [th], [g], [m], [v])
+        from mixed_precision_optimizer_amd import MixedPrecisionAdamW
+        opt = MixedPrecisionAdamW(hset, [(1e-3, 0.0)], mode=mode, max_norm=1.0)
+        for _ in range(4):
+            applied, norm = opt.step()
+            assert applied and norm == 0.0
+        assert np.array_equal(to_np(th).view(np.uint32), th0.view(np.uint32))
+        assert torch.equal(p.view(torch.int16), p0.view(torch.int16))
+        assert not m.any() and not v.any()
+        hset.close()
