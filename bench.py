@@ -269,6 +269,26 @@ def main():
                                      "scales from a device copy of known size); algorithmic: "
                                      f"{UPDATE_BYTES * N / 1e9:.1f} GB"},
     }
+    # the same step with the scaler, skip decision and step counter on the
+    # device: no host round trip per step (hpo_step_device); constant scale 1
+    from mixed_precision_optimizer_amd import DeviceAdamW
+    dopt = DeviceAdamW(hset, w.groups(), beta1=w.beta1, beta2=w.beta2, eps=w.eps, mode=w.mode,
+                       max_norm=w.max_norm, loss_scale=1.0 if w.loss_scale is None else w.loss_scale,
+                       dynamic=False, applied_steps=t_applied, stream=stream)
+    for _ in range(args.warmup):
+        dopt.step()
+    dopt.sync()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dopt.step()
+    torch.cuda.synchronize()
+    dev_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    dst = dopt.sync()
+    log(f"device-resident step: {dev_ms:.3f} ms ({dst.applied_steps} applied)")
+    out["device_resident_step"] = {"ms_per_step": round(dev_ms, 4), "value": round(N / (dev_ms * 1e-3) / 1e9, 3),
+                                   "unit": "G params/s",
+                                   "note": "hpo_step_device: no per-step host sync; steps re-read the state every 32"}
     hset.close()
     if sample is not None:
         log(f"cpu baseline on {sample[0].size} elements")

@@ -214,6 +214,76 @@ hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* g
                           int32_t n_groups, int64_t t, float inv_scale, double max_norm,
                           const float* d_norm, const int32_t* d_found_inf, void* stream);
 
+/* ---------------------------------------------------------------------- */
+/* Device-resident step: loss scaler, skip decision and step counter on the */
+/* device, so steps can be enqueued without a host synchronisation.         */
+/* ---------------------------------------------------------------------- */
+
+/* Most unsynchronised steps one call can account for (see hpo_step_device). */
+#define HPO_MAX_WINDOW 32
+
+/* Loss-scaler and step state kept in device memory (48 bytes, caller-owned,
+ * 8-byte aligned).  The caller multiplies its loss by loss_scale before
+ * backward ([OPT-INFRA] §10.2: the loss is scaled, the grads are unscaled
+ * before the step) and may read the struct back at any time after a sync. */
+typedef struct {
+    float loss_scale;           /* S */
+    float inv_scale;            /* fp32(1 / S), formed in binary64; what the passes multiply by */
+    int32_t growth_tracker;     /* clean steps since the last growth or non-finite step */
+    int32_t hysteresis_tracker; /* non-finite steps still tolerated before a back-off */
+    int64_t applied_steps;      /* steps applied so far = t of the last applied step */
+    int64_t skipped_steps;      /* steps skipped (non-finite grads or norm over the threshold) */
+    float grad_norm;            /* norm of the last step's unscaled grads (inf/NaN if non-finite) */
+    int32_t found_inf;          /* the last step saw an inf/NaN grad */
+    int32_t applied;            /* the last step was applied */
+    int32_t error;              /* sticky: a step's t fell outside the window it was given */
+} hpo_scaler_state;
+
+/* Scaler and skip policy ([OPT-INFRA] §10.1 scaler rules and defaults; §11.4
+ * and §17 grad_norm_skip_threshold, default off).
+ *   dynamic = 0: constant scale, never changed (an explicit loss scale).
+ *   dynamic = 1: on a step with non-finite grads the growth tracker resets and
+ *     the hysteresis tracker drops by one; once it is <= 0 the scale becomes
+ *     max(scale * backoff_factor, min_scale) (so a single spike is tolerated
+ *     when hysteresis > 1).  After growth_interval clean steps in a row the
+ *     scale is multiplied by growth_factor and both trackers reset.  The
+ *     pages' defaults: initial scale 2^32, growth 2.0, backoff 0.5, interval
+ *     1000, hysteresis 2, min scale 1.0.
+ *   A step whose grad norm exceeds grad_norm_skip_threshold is skipped too (no
+ *   update, t unchanged); it still counts as clean for the scaler, which the
+ *   pages update before the norm is taken. */
+typedef struct {
+    int32_t dynamic;
+    int32_t growth_interval;
+    int32_t hysteresis;
+    float growth_factor;
+    float backoff_factor;
+    float min_scale;
+    double grad_norm_skip_threshold; /* +inf: never */
+} hpo_scaler_cfg;
+
+/* Writes a fresh state: loss_scale, inv_scale = fp32(1/loss_scale),
+ * hysteresis_tracker = hysteresis, applied_steps as given (a resumed run),
+ * every other field 0.  Enqueued on stream (a one-lane kernel). */
+hpo_status hpo_scaler_state_init(hpo_scaler_state* d_state, float loss_scale, int32_t hysteresis,
+                                 int64_t applied_steps, void* stream);
+
+/* One whole step with everything decided on the device: the grad pass (check
+ * + norm, multiplying by d_state->inv_scale), the finalize (norm, found_inf,
+ * skip decision), the fused clip + update + write-back (run only when the
+ * step is applied, with t = applied_steps + 1), and a one-lane kernel that
+ * advances the counters and the scaler.  Nothing is read back.
+ * The bias corrections 1 - beta^t are formed on the host in binary64 and
+ * rounded to fp32 for t = t_first .. t_first + window - 1, where t_first is
+ * applied_steps + 1 as of the caller's last read of the state and window
+ * (1..HPO_MAX_WINDOW) counts the steps enqueued since that read, this one
+ * included; if the device's t falls outside, the step is not applied and
+ * d_state->error is set.  Same arithmetic, bit for bit, as the three calls
+ * above with the same scale. */
+hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                           double max_norm, const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state,
+                           int64_t t_first, int32_t window, void* stream);
+
 /* Master -> model copy alone: param = bf16_rne(main_param) for every element
  * of a bf16 set ([OPT-INFRA] §9.2, the write-back row; the same conversion the
  * step fuses).  A no-op for fp32 sets. */

@@ -5,6 +5,6 @@ libhpo.so (C ABI in include/hpo.h, HIP kernels in csrc/) does all the work;
 do.  `inputs` draws the seeded synthetic workloads.
 """
 from . import hpo  # noqa: F401
-from .optimizer import MixedPrecisionAdamW  # noqa: F401
+from .optimizer import DeviceAdamW, MixedPrecisionAdamW  # noqa: F401
 
-__all__ = ["hpo", "MixedPrecisionAdamW"]
+__all__ = ["hpo", "MixedPrecisionAdamW", "DeviceAdamW"]

@@ -576,7 +576,7 @@ hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_in
     if (!std::isfinite(inv_scale))
         return fail(HPO_EINVAL, "inv_scale must be finite");
     const hpo::GradPass pass = (inv_scale == 1.0f) ? hpo::GradPass::kCheck : hpo::GradPass::kUnscale;
-    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, pass, inv_scale,
+    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, pass, inv_scale, nullptr,
                                          s->d_part_sum, s->d_part_flag, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch unscale/check pass");
@@ -600,7 +600,7 @@ hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32
     if (!std::isfinite(inv_scale))
         return fail(HPO_EINVAL, "inv_scale must be finite");
     hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm,
-                                         inv_scale, s->d_part_sum, s->d_part_flag, as_stream(stream));
+                                         inv_scale, nullptr, s->d_part_sum, s->d_part_flag, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch norm pass");
     /* with no chunks the finalizer still runs, so the norm reads 0 */
@@ -611,9 +611,13 @@ hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32
     return ok();
 }
 
-hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups,
-                          int32_t n_groups, int64_t t, float inv_scale, double max_norm,
-                          const float* d_norm, const int32_t* d_found_inf, void* stream)
+}  // extern "C"
+
+namespace {
+
+/* Argument rules shared by the two step calls. */
+hpo_status check_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                      double max_norm)
 {
     hpo_status st = check_set(s);
     if (st != HPO_OK)
@@ -635,35 +639,130 @@ hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* g
     for (int32_t k = 0; k < n_groups; ++k)
         if (!is_finite(groups[k].lr) || !is_finite(groups[k].weight_decay))
             return fail(HPO_EINVAL, "group %d: lr and weight_decay must be finite", k);
-    if (t < 1)
-        return fail(HPO_EINVAL, "t is the 1-based count of applied steps, must be >= 1 (got %lld)", (long long)t);
-    if (!std::isfinite(inv_scale))
-        return fail(HPO_EINVAL, "inv_scale must be finite");
     if (std::isnan(max_norm))
         return fail(HPO_EINVAL, "max_norm is NaN");
-    if (max_norm > 0.0 && !d_norm)
-        return fail(HPO_EINVAL, "clipping (max_norm > 0) needs d_norm");
+    return HPO_OK;
+}
 
-    /* Per-step scalars: binary64 once, rounded to fp32 once. */
+/* 1 - beta^t, formed in binary64 and rounded once to fp32. */
+float bias_correction(double beta, int64_t t) { return static_cast<float>(1.0 - std::pow(beta, static_cast<double>(t))); }
+
+/* Per-step scalars other than t: binary64 once, rounded to fp32 once. */
+hpo::AdamScalars base_scalars(const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups, double max_norm)
+{
     hpo::AdamScalars sc{};
-    sc.inv_scale = inv_scale;
     sc.b1 = static_cast<float>(cfg->beta1);
     sc.b2 = static_cast<float>(cfg->beta2);
     sc.c1 = static_cast<float>(1.0 - cfg->beta1);
     sc.c2 = static_cast<float>(1.0 - cfg->beta2);
-    sc.bc1 = static_cast<float>(1.0 - std::pow(cfg->beta1, static_cast<double>(t)));
-    sc.bc2 = static_cast<float>(1.0 - std::pow(cfg->beta2, static_cast<double>(t)));
     sc.eps = static_cast<float>(cfg->eps);
     sc.max_norm = max_norm;
-    sc.d_norm = d_norm;
-    sc.d_found = d_found_inf;
     for (int32_t k = 0; k < n_groups; ++k) {
         sc.lr[k] = static_cast<float>(groups[k].lr);
         sc.wd[k] = static_cast<float>(groups[k].weight_decay);
     }
+    return sc;
+}
+
+}  // namespace
+
+extern "C" {
+
+hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups,
+                          int32_t n_groups, int64_t t, float inv_scale, double max_norm,
+                          const float* d_norm, const int32_t* d_found_inf, void* stream)
+{
+    hpo_status st = check_step(s, cfg, groups, n_groups, max_norm);
+    if (st != HPO_OK)
+        return st;
+    if (t < 1)
+        return fail(HPO_EINVAL, "t is the 1-based count of applied steps, must be >= 1 (got %lld)", (long long)t);
+    if (!std::isfinite(inv_scale))
+        return fail(HPO_EINVAL, "inv_scale must be finite");
+    if (max_norm > 0.0 && !d_norm)
+        return fail(HPO_EINVAL, "clipping (max_norm > 0) needs d_norm");
+    hpo::AdamScalars sc = base_scalars(cfg, groups, n_groups, max_norm);
+    sc.inv_scale = inv_scale;
+    sc.bc1 = bias_correction(cfg->beta1, t);
+    sc.bc2 = bias_correction(cfg->beta2, t);
+    sc.d_norm = d_norm;
+    sc.d_found = d_found_inf;
     hipError_t e = hpo::launch_adam(s->view, s->n_chunks, cfg->mode, sc, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch adam update");
+    return ok();
+}
+
+hpo_status hpo_scaler_state_init(hpo_scaler_state* d_state, float loss_scale, int32_t hysteresis,
+                                 int64_t applied_steps, void* stream)
+{
+    if (!d_state || !aligned(d_state, 8))
+        return fail(HPO_EINVAL, "d_state must be a non-NULL, 8-byte aligned device pointer");
+    if (!(loss_scale > 0.0f) || !std::isfinite(loss_scale))
+        return fail(HPO_EINVAL, "loss_scale must be finite and > 0 (got %g)", (double)loss_scale);
+    if (hysteresis < 1 || applied_steps < 0)
+        return fail(HPO_EINVAL, "hysteresis must be >= 1 and applied_steps >= 0");
+    hipError_t e = hpo::launch_scaler_init(d_state, loss_scale, hysteresis, applied_steps, as_stream(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "launch scaler init");
+    return ok();
+}
+
+hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                           double max_norm, const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state,
+                           int64_t t_first, int32_t window, void* stream)
+{
+    hpo_status st = check_step(s, cfg, groups, n_groups, max_norm);
+    if (st != HPO_OK)
+        return st;
+    if (!scfg)
+        return fail(HPO_EINVAL, "scfg is NULL");
+    if (!d_state || !aligned(d_state, 8))
+        return fail(HPO_EINVAL, "d_state must be a non-NULL, 8-byte aligned device pointer");
+    if (t_first < 1)
+        return fail(HPO_EINVAL, "t_first must be >= 1 (got %lld)", (long long)t_first);
+    if (window < 1 || window > HPO_MAX_WINDOW)
+        return fail(HPO_EINVAL, "window must be in [1, %d] (got %d)", HPO_MAX_WINDOW, window);
+    if (std::isnan(scfg->grad_norm_skip_threshold))
+        return fail(HPO_EINVAL, "grad_norm_skip_threshold is NaN");
+    if (scfg->dynamic) {
+        if (scfg->growth_interval < 1 || scfg->hysteresis < 1)
+            return fail(HPO_EINVAL, "growth_interval and hysteresis must be >= 1");
+        if (!(scfg->growth_factor > 0.0f) || !(scfg->backoff_factor > 0.0f) || !(scfg->min_scale > 0.0f) ||
+            !std::isfinite(scfg->growth_factor) || !std::isfinite(scfg->backoff_factor) ||
+            !std::isfinite(scfg->min_scale))
+            return fail(HPO_EINVAL, "growth_factor, backoff_factor and min_scale must be finite and > 0");
+    }
+    hpo::AdamScalars sc = base_scalars(cfg, groups, n_groups, max_norm);
+    sc.d_state = d_state;
+    sc.t_first = t_first;
+    sc.window = window;
+    for (int32_t j = 0; j < window; ++j) {
+        sc.bc1_tab[j] = bias_correction(cfg->beta1, t_first + j);
+        sc.bc2_tab[j] = bias_correction(cfg->beta2, t_first + j);
+    }
+    hpo::ScalerRule rule{};
+    rule.dynamic = scfg->dynamic ? 1 : 0;
+    rule.growth_interval = scfg->growth_interval;
+    rule.hysteresis = scfg->hysteresis;
+    rule.growth_factor = scfg->growth_factor;
+    rule.backoff_factor = scfg->backoff_factor;
+    rule.min_scale = scfg->min_scale;
+    hipStream_t strm = as_stream(stream);
+    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, 1.0f,
+                                         &d_state->inv_scale, s->d_part_sum, s->d_part_flag, strm);
+    if (e != hipSuccess)
+        return hip_fail(e, "launch norm pass");
+    e = hpo::launch_finalize_state(s->d_part_sum, s->d_part_flag, s->n_parts, stage_sum(s), stage_flag(s), d_state,
+                                   scfg->grad_norm_skip_threshold, strm);
+    if (e != hipSuccess)
+        return hip_fail(e, "launch norm finalize");
+    e = hpo::launch_adam(s->view, s->n_chunks, cfg->mode, sc, strm);
+    if (e != hipSuccess)
+        return hip_fail(e, "launch adam update");
+    e = hpo::launch_step_end(d_state, rule, t_first, window, strm);
+    if (e != hipSuccess)
+        return hip_fail(e, "launch step end");
     return ok();
 }
 

@@ -5,6 +5,7 @@
 #ifndef HPO_IMPL_H
 #define HPO_IMPL_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -93,6 +94,26 @@ struct AdamScalars {
     const int32_t* d_found; /* device skip flag, nullable */
     float lr[HPO_MAX_GROUPS];
     float wd[HPO_MAX_GROUPS];
+    /* device-resident step only: t, inv_scale, norm and the apply decision
+     * come from the state; bias corrections from the table for t_first + j */
+    const hpo_scaler_state* d_state;
+    int64_t t_first;
+    int32_t window;
+    float bc1_tab[HPO_MAX_WINDOW];
+    float bc2_tab[HPO_MAX_WINDOW];
+};
+
+static_assert(sizeof(hpo_scaler_state) == 48, "hpo_scaler_state layout");
+static_assert(offsetof(hpo_scaler_state, applied_steps) == 16, "hpo_scaler_state layout");
+
+/* Scaler rule constants for the end-of-step kernel. */
+struct ScalerRule {
+    int32_t dynamic;
+    int32_t growth_interval;
+    int32_t hysteresis;
+    float growth_factor;
+    float backoff_factor;
+    float min_scale;
 };
 
 enum class GradPass : int { kNorm = 0, kCheck = 1, kUnscale = 2 };
@@ -102,7 +123,8 @@ enum class GradPass : int { kNorm = 0, kCheck = 1, kUnscale = 2 };
 /* The grad pass runs one workgroup per group of `grad_group` consecutive
  * chunks (n_parts = ceil(n_chunks / grad_group) workgroups and partials). */
 hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
-                            float inv_scale, double* part_sum, int32_t* part_flag, hipStream_t stream);
+                            float inv_scale, const float* d_inv, double* part_sum, int32_t* part_flag,
+                            hipStream_t stream);
 /* Folds n_parts partials into *d_norm = fp32(sqrt(sum)) (skipped when d_norm
  * is null, part_sum is then not read) and *d_found |= any flag; sets with
  * more than kFinalSpan partials go through stage_sum / stage_flag
@@ -110,8 +132,17 @@ hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_gr
 hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
                            double* stage_sum, int32_t* stage_flag, float* d_norm, int32_t* d_found,
                            hipStream_t stream);
+/* Same folding, then writes the norm, found_inf and the apply decision
+ * (finite and norm <= threshold) into the device step state. */
+hipError_t launch_finalize_state(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
+                                 double* stage_sum, int32_t* stage_flag, hpo_scaler_state* st,
+                                 double threshold, hipStream_t stream);
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                        hipStream_t stream);
+hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hysteresis, int64_t applied,
+                              hipStream_t stream);
+hipError_t launch_step_end(hpo_scaler_state* st, ScalerRule rule, int64_t t_first, int32_t window,
+                           hipStream_t stream);
 hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream);
 
 }  // namespace hpo

@@ -246,8 +246,10 @@ __device__ __forceinline__ void grad_range(const Range& r, float inv, double& ac
 /* One workgroup per group of consecutive chunks; one partial per workgroup. */
 template <bool FLAT, GradPass PASS>
 __global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_chunks, int32_t group,
-                                                          float inv, double* part_sum, int32_t* part_flag)
+                                                          float inv_arg, const float* d_inv, double* part_sum,
+                                                          int32_t* part_flag)
 {
+    const float inv = d_inv != nullptr ? *d_inv : inv_arg;
     double acc = 0.0;
     int bad = 0;
     const int64_t c0 = static_cast<int64_t>(blockIdx.x) * group;
@@ -330,23 +332,47 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(const double* part_sum
     }
 }
 
+/* Last stage of the device-resident step: norm, found_inf and whether the
+ * step will be applied (finite grads, norm not above the skip threshold). */
+__global__ __launch_bounds__(kFinalBlock) void k_finalize_state(const double* part_sum, const int32_t* part_flag,
+                                                                int64_t n, hpo_scaler_state* st, double threshold)
+{
+    int any_bad = 0;
+    const double tot = reduce_partials(part_sum, part_flag, 0, n, true, any_bad);
+    if (threadIdx.x == 0) {
+        const float norm = static_cast<float>(sqrt(tot));
+        st->grad_norm = norm;
+        st->found_inf = any_bad ? 1 : 0;
+        /* the threshold test fails for a NaN norm, so "not above" is spelled out */
+        st->applied = (!any_bad && !(static_cast<double>(norm) > threshold)) ? 1 : 0;
+    }
+}
+
 /* ---------------------------------------------------------------------- */
 /* adam: clip + Adam/AdamW + bf16 write-back                              */
 /* ---------------------------------------------------------------------- */
+/* Per-step values that differ between the host-driven and the device-resident
+ * step; everything else comes straight from the (read-only) kernel arguments. */
+struct StepVals {
+    float inv_scale;
+    float bc1, bc2;  /* 1 - beta1^t, 1 - beta2^t */
+    float C;         /* clip coefficient when clip is set */
+    bool clip;
+};
+
 template <int MODE>
 __device__ __forceinline__ void adam_elem(float G, float& th, float& m, float& v,
-                                          const AdamScalars& sc, bool clip, float C, float lr,
-                                          float wd)
+                                          const AdamScalars& sc, const StepVals& k, float lr, float wd)
 {
-    float g = G * sc.inv_scale;          /* unscale ([OPT-INFRA] §10.2) */
-    if (clip)
-        g = g * C;                       /* clip ([OPT-INFRA] §11.1) */
+    float g = G * k.inv_scale;           /* unscale ([OPT-INFRA] §10.2) */
+    if (k.clip)
+        g = g * k.C;                     /* clip ([OPT-INFRA] §11.1) */
     if constexpr (MODE == HPO_ADAM_L2)
         g = g + wd * th;                 /* L2 term joins the gradient ([OPT-INFRA] §3) */
     m = sc.b1 * m + sc.c1 * g;           /* first moment ([OPT-INFRA] §2) */
     v = sc.b2 * v + sc.c2 * (g * g);     /* raw second moment */
-    const float mh = m / sc.bc1;         /* bias corrections */
-    const float vh = v / sc.bc2;
+    const float mh = m / k.bc1;          /* bias corrections */
+    const float vh = v / k.bc2;
     const float u = mh / (sqrtf(vh) + sc.eps); /* eps outside the root */
     if constexpr (MODE == HPO_ADAMW)
         th = th - lr * (u + wd * th);    /* decoupled decay ([OPT-INFRA] §3) */
@@ -360,18 +386,40 @@ __device__ __forceinline__ void adam_elem(float G, float& th, float& m, float& v
 #define HPO_ADAM_BOUNDS __launch_bounds__(kBlock)
 #endif
 
-template <bool FLAT, int PDT, int MODE>
+template <bool FLAT, int PDT, int MODE, bool DEV>
 __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chunks)
 {
-    if (sc.d_found != nullptr && *sc.d_found != 0)
-        return; /* found_inf: the whole step is skipped ([OPT-INFRA] §10.2) */
-    bool clip = false;
-    float C = 1.0f;
+    StepVals k;
+    float norm = 0.0f;
+    if constexpr (DEV) {
+        /* device-resident step: t, inv_scale, norm and the decision come
+         * from the state; the bias corrections from the host's table */
+        const hpo_scaler_state* st = sc.d_state;
+        if (!st->applied)
+            return;
+        const int64_t j = st->applied_steps + 1 - sc.t_first;
+        if (j < 0 || j >= sc.window)
+            return; /* outside the window: the end kernel records the error */
+        k.bc1 = sc.bc1_tab[j];
+        k.bc2 = sc.bc2_tab[j];
+        k.inv_scale = st->inv_scale;
+        norm = st->grad_norm;
+    } else {
+        if (sc.d_found != nullptr && *sc.d_found != 0)
+            return; /* found_inf: the whole step is skipped ([OPT-INFRA] §10.2) */
+        k.bc1 = sc.bc1;
+        k.bc2 = sc.bc2;
+        k.inv_scale = sc.inv_scale;
+        if (sc.max_norm > 0.0)
+            norm = *sc.d_norm;
+    }
+    k.clip = false;
+    k.C = 1.0f;
     if (sc.max_norm > 0.0) {
-        const double c = sc.max_norm / (static_cast<double>(*sc.d_norm) + 1e-6);
+        const double c = sc.max_norm / (static_cast<double>(norm) + 1e-6);
         if (c < 1.0) {
-            clip = true;
-            C = static_cast<float>(c);
+            k.clip = true;
+            k.C = static_cast<float>(c);
         }
     }
     const Range r = chunk_range<FLAT>(sv, update_chunk(n_chunks));
@@ -408,10 +456,10 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
             for (int u = 0; u < U; ++u) {
                 const int64_t i = base + static_cast<int64_t>(u) * kBlock;
                 if (i < nv) {
-                    adam_elem<MODE>(g[u].x, th[u].x, m[u].x, v[u].x, sc, clip, C, lr, wd);
-                    adam_elem<MODE>(g[u].y, th[u].y, m[u].y, v[u].y, sc, clip, C, lr, wd);
-                    adam_elem<MODE>(g[u].z, th[u].z, m[u].z, v[u].z, sc, clip, C, lr, wd);
-                    adam_elem<MODE>(g[u].w, th[u].w, m[u].w, v[u].w, sc, clip, C, lr, wd);
+                    adam_elem<MODE>(g[u].x, th[u].x, m[u].x, v[u].x, sc, k, lr, wd);
+                    adam_elem<MODE>(g[u].y, th[u].y, m[u].y, v[u].y, sc, k, lr, wd);
+                    adam_elem<MODE>(g[u].z, th[u].z, m[u].z, v[u].z, sc, k, lr, wd);
+                    adam_elem<MODE>(g[u].w, th[u].w, m[u].w, v[u].w, sc, k, lr, wd);
                     st_stream(T4 + i, th[u]);
                     st_stream(M4 + i, m[u]);
                     st_stream(V4 + i, v[u]);
@@ -424,7 +472,7 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
     }
     for (int64_t i = done + tid; i < r.len; i += kBlock) {
         float th = T[i], m = M[i], v = V[i];
-        adam_elem<MODE>(G[i], th, m, v, sc, clip, C, lr, wd);
+        adam_elem<MODE>(G[i], th, m, v, sc, k, lr, wd);
         T[i] = th;
         M[i] = m;
         V[i] = v;
@@ -458,6 +506,59 @@ __global__ __launch_bounds__(kBlock) void k_copy_main_to_model(SetView sv)
         P[i] = static_cast<uint16_t>(bf16_rne_bits(T[i]));
 }
 
+/* ---------------------------------------------------------------------- */
+/* device-resident step: state init and end-of-step bookkeeping            */
+/* ---------------------------------------------------------------------- */
+__global__ __launch_bounds__(64) void k_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hysteresis,
+                                                    int64_t applied)
+{
+    if (threadIdx.x == 0) {
+        hpo_scaler_state s{};
+        s.loss_scale = loss_scale;
+        s.inv_scale = static_cast<float>(1.0 / static_cast<double>(loss_scale));
+        s.hysteresis_tracker = hysteresis;
+        s.applied_steps = applied;
+        *st = s;
+    }
+}
+
+/* Counters and the dynamic loss-scale rule ([OPT-INFRA] §10.1), one lane. */
+__global__ __launch_bounds__(64) void k_step_end(hpo_scaler_state* st, ScalerRule rule, int64_t t_first,
+                                                 int32_t window)
+{
+    if (threadIdx.x != 0)
+        return;
+    hpo_scaler_state s = *st;
+    const int64_t j = s.applied_steps + 1 - t_first;
+    const bool in_window = j >= 0 && j < window;
+    if (s.applied && !in_window)
+        s.error = 1;
+    s.applied = (s.applied && in_window) ? 1 : 0;
+    if (s.applied)
+        s.applied_steps += 1;
+    else
+        s.skipped_steps += 1;
+    if (rule.dynamic) {
+        if (s.found_inf) {
+            s.growth_tracker = 0;
+            s.hysteresis_tracker -= 1;
+            if (s.hysteresis_tracker <= 0) {
+                const float backed = s.loss_scale * rule.backoff_factor;
+                s.loss_scale = backed > rule.min_scale ? backed : rule.min_scale;
+            }
+        } else {
+            s.growth_tracker += 1;
+            if (s.growth_tracker == rule.growth_interval) {
+                s.growth_tracker = 0;
+                s.hysteresis_tracker = rule.hysteresis;
+                s.loss_scale = s.loss_scale * rule.growth_factor;
+            }
+        }
+        s.inv_scale = static_cast<float>(1.0 / static_cast<double>(s.loss_scale));
+    }
+    *st = s;
+}
+
 template <typename... Args>
 hipError_t launch(void (*kernel)(Args...), int64_t grid, int block, hipStream_t stream,
                   Args... args)
@@ -470,14 +571,15 @@ hipError_t launch(void (*kernel)(Args...), int64_t grid, int block, hipStream_t 
 }  // namespace
 
 hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
-                            float inv_scale, double* part_sum, int32_t* part_flag, hipStream_t stream)
+                            float inv_scale, const float* d_inv, double* part_sum, int32_t* part_flag,
+                            hipStream_t stream)
 {
     if (n_chunks == 0)
         return hipSuccess;
     const int64_t grid = (n_chunks + grad_group - 1) / grad_group;
     const bool flat = sv.is_flat != 0;
 #define HPO_GRAD_LAUNCH(F, P) \
-    launch(k_grad_pass<F, P>, grid, kGradBlock, stream, sv, n_chunks, grad_group, inv_scale, part_sum, part_flag)
+    launch(k_grad_pass<F, P>, grid, kGradBlock, stream, sv, n_chunks, grad_group, inv_scale, d_inv, part_sum, part_flag)
     switch (pass) {
     case GradPass::kNorm:
         return flat ? HPO_GRAD_LAUNCH(true, GradPass::kNorm) : HPO_GRAD_LAUNCH(false, GradPass::kNorm);
@@ -508,15 +610,14 @@ hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int
     return launch(k_finalize, 1, kFinalBlock, stream, ps, part_flag, n_parts, d_norm, d_found);
 }
 
-hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
-                       hipStream_t stream)
+template <bool DEV>
+hipError_t launch_adam_t(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+                         hipStream_t stream)
 {
-    if (n_chunks == 0)
-        return hipSuccess;
     const bool flat = sv.is_flat != 0;
     const bool bf16 = sv.param_dtype == HPO_PARAM_BF16;
     const bool adamw = mode == HPO_ADAMW;
-#define HPO_ADAM_LAUNCH(F, P, M) launch(k_adam<F, P, M>, n_chunks, kBlock, stream, sv, sc, n_chunks)
+#define HPO_ADAM_LAUNCH(F, P, M) launch(k_adam<F, P, M, DEV>, n_chunks, kBlock, stream, sv, sc, n_chunks)
     if (flat) {
         if (bf16)
             return adamw ? HPO_ADAM_LAUNCH(true, HPO_PARAM_BF16, HPO_ADAMW) : HPO_ADAM_LAUNCH(true, HPO_PARAM_BF16, HPO_ADAM_L2);
@@ -526,6 +627,45 @@ hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const 
         return adamw ? HPO_ADAM_LAUNCH(false, HPO_PARAM_BF16, HPO_ADAMW) : HPO_ADAM_LAUNCH(false, HPO_PARAM_BF16, HPO_ADAM_L2);
     return adamw ? HPO_ADAM_LAUNCH(false, HPO_PARAM_FP32, HPO_ADAMW) : HPO_ADAM_LAUNCH(false, HPO_PARAM_FP32, HPO_ADAM_L2);
 #undef HPO_ADAM_LAUNCH
+}
+
+hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+                       hipStream_t stream)
+{
+    if (n_chunks == 0)
+        return hipSuccess;
+    return sc.d_state != nullptr ? launch_adam_t<true>(sv, n_chunks, mode, sc, stream)
+                                 : launch_adam_t<false>(sv, n_chunks, mode, sc, stream);
+}
+
+hipError_t launch_finalize_state(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
+                                 double* stage_sum, int32_t* stage_flag, hpo_scaler_state* st,
+                                 double threshold, hipStream_t stream)
+{
+    const double* ps = part_sum;
+    if (n_parts > kFinalSpan) {
+        const int64_t n_stage = (n_parts + kFinalSpan - 1) / kFinalSpan;
+        hipError_t e = launch(k_reduce_stage, n_stage, kFinalBlock, stream, ps, part_flag, n_parts,
+                              stage_sum, stage_flag);
+        if (e != hipSuccess)
+            return e;
+        ps = stage_sum;
+        part_flag = stage_flag;
+        n_parts = n_stage;
+    }
+    return launch(k_finalize_state, 1, kFinalBlock, stream, ps, part_flag, n_parts, st, threshold);
+}
+
+hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hysteresis, int64_t applied,
+                              hipStream_t stream)
+{
+    return launch(k_scaler_init, 1, 64, stream, st, loss_scale, hysteresis, applied);
+}
+
+hipError_t launch_step_end(hpo_scaler_state* st, ScalerRule rule, int64_t t_first, int32_t window,
+                           hipStream_t stream)
+{
+    return launch(k_step_end, 1, 64, stream, st, rule, t_first, window);
 }
 
 hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream)

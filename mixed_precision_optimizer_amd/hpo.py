@@ -47,6 +47,24 @@ class hpo_set_info_t(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("n_grad_parts", ctypes.c_int64)]
 
 
+class hpo_scaler_state(ctypes.Structure):
+    _fields_ = [("loss_scale", ctypes.c_float), ("inv_scale", ctypes.c_float),
+                ("growth_tracker", ctypes.c_int32), ("hysteresis_tracker", ctypes.c_int32),
+                ("applied_steps", ctypes.c_int64), ("skipped_steps", ctypes.c_int64),
+                ("grad_norm", ctypes.c_float), ("found_inf", ctypes.c_int32),
+                ("applied", ctypes.c_int32), ("error", ctypes.c_int32)]
+
+
+class hpo_scaler_cfg(ctypes.Structure):
+    _fields_ = [("dynamic", ctypes.c_int32), ("growth_interval", ctypes.c_int32),
+                ("hysteresis", ctypes.c_int32), ("growth_factor", ctypes.c_float),
+                ("backoff_factor", ctypes.c_float), ("min_scale", ctypes.c_float),
+                ("grad_norm_skip_threshold", ctypes.c_double)]
+
+
+HPO_MAX_WINDOW = 32
+SCALER_STATE_BYTES = ctypes.sizeof(hpo_scaler_state)
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -66,6 +84,9 @@ SIGNATURES = {
     "hpo_adamw_step": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32,
                               _I64, ctypes.c_float, ctypes.c_double, _P, _P, _P]),
     "hpo_copy_main_to_model": (_I32, [_P, _P]),
+    "hpo_scaler_state_init": (_I32, [_P, ctypes.c_float, _I32, _I64, _P]),
+    "hpo_step_device": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32, ctypes.c_double,
+                               ctypes.POINTER(hpo_scaler_cfg), _P, _I64, _I32, _P]),
     "hpo_plan": (_I32, [_I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32), ctypes.POINTER(_I64),
                         ctypes.POINTER(_I64)]),
     "hpo_plan_chunks": (_I32, [_I32, ctypes.POINTER(_I64), _I64, ctypes.POINTER(_I32),
@@ -286,6 +307,37 @@ def hpo_adamw_step(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int]
         groups, n_groups = make_groups(groups)
     _check(load().hpo_adamw_step(s.handle, ctypes.byref(cfg), groups, n_groups, t, inv_scale, max_norm,
                                  _ptr(d_norm), _ptr(d_found_inf), _stream(stream)), "hpo_adamw_step")
+
+
+def new_scaler_state(device=None) -> torch.Tensor:
+    """Device buffer for one hpo_scaler_state (48 bytes, 8-byte aligned)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    return torch.zeros(SCALER_STATE_BYTES // 8, dtype=torch.int64, device=dev)
+
+
+def read_scaler_state(d_state: torch.Tensor) -> hpo_scaler_state:
+    """Copies the state to the host (synchronises d_state's stream)."""
+    raw = d_state.cpu().numpy().tobytes()
+    return hpo_scaler_state.from_buffer_copy(raw)
+
+
+def make_scaler_cfg(dynamic=True, growth_interval=1000, hysteresis=2, growth_factor=2.0, backoff_factor=0.5,
+                    min_scale=1.0, grad_norm_skip_threshold=float("inf")) -> hpo_scaler_cfg:
+    return hpo_scaler_cfg(int(dynamic), growth_interval, hysteresis, growth_factor, backoff_factor, min_scale,
+                          grad_norm_skip_threshold)
+
+
+def hpo_scaler_state_init(d_state, loss_scale: float, hysteresis: int, applied_steps: int = 0, stream=None) -> None:
+    _check(load().hpo_scaler_state_init(_ptr(d_state), loss_scale, hysteresis, applied_steps, _stream(stream)),
+           "hpo_scaler_state_init")
+
+
+def hpo_step_device(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int], max_norm: float,
+                    scfg: hpo_scaler_cfg, d_state, t_first: int, window: int, stream=None) -> None:
+    if not isinstance(groups, ctypes.Array):
+        groups, n_groups = make_groups(groups)
+    _check(load().hpo_step_device(s.handle, ctypes.byref(cfg), groups, n_groups, max_norm, ctypes.byref(scfg),
+                                  _ptr(d_state), t_first, window, _stream(stream)), "hpo_step_device")
 
 
 def hpo_copy_main_to_model(s: HpoSet, stream=None) -> None:

@@ -63,3 +63,50 @@ class MixedPrecisionAdamW:
             return False, None
         self.t += 1
         return True, float(self._host[1:2].view(torch.float32)[0])
+
+
+class DeviceAdamW:
+    """Steps enqueued with no host synchronisation: the loss scaler, the skip
+    decision and the applied-step counter live in device memory
+    (hpo_step_device).  The host only tracks which t values the unsynchronised
+    steps can have; it reads the state back when that window is full, or when
+    asked (sync / state)."""
+
+    def __init__(self, hset: hpo.HpoSet, groups: Sequence[Tuple[float, float]], *, beta1: float = 0.9,
+                 beta2: float = 0.999, eps: float = 1e-8, mode: int = hpo.HPO_ADAMW, max_norm: float = 1.0,
+                 loss_scale: float = 2.0 ** 32, dynamic: bool = True, growth_interval: int = 1000,
+                 hysteresis: int = 2, growth_factor: float = 2.0, backoff_factor: float = 0.5,
+                 min_scale: float = 1.0, grad_norm_skip_threshold: float = float("inf"),
+                 applied_steps: int = 0, device=None, stream=None):
+        self.set = hset
+        self.cfg = hpo.make_cfg(beta1, beta2, eps, mode)
+        self.groups, self.n_groups = hpo.make_groups(list(groups))
+        self.max_norm = float(max_norm)
+        self.scfg = hpo.make_scaler_cfg(dynamic, growth_interval, hysteresis, growth_factor, backoff_factor,
+                                        min_scale, grad_norm_skip_threshold)
+        self.stream = torch.cuda.current_stream() if stream is None else stream
+        self.d_state = hpo.new_scaler_state(device)
+        hpo.hpo_scaler_state_init(self.d_state, loss_scale, hysteresis, applied_steps, self.stream)
+        self.t_first = applied_steps + 1   # smallest t the next step can have
+        self.pending = 0                   # steps enqueued since the last read of the state
+
+    @property
+    def loss_scale_tensor(self) -> torch.Tensor:
+        """The current loss scale as a device fp32 scalar (no sync needed)."""
+        return self.d_state.view(torch.float32)[0:1]
+
+    def step(self) -> None:
+        if self.pending == hpo.HPO_MAX_WINDOW:
+            self.sync()
+        self.pending += 1
+        hpo.hpo_step_device(self.set, self.cfg, self.groups, self.n_groups, self.max_norm, self.scfg, self.d_state,
+                            self.t_first, self.pending, self.stream)
+
+    def sync(self) -> hpo.hpo_scaler_state:
+        self.stream.synchronize()
+        st = hpo.read_scaler_state(self.d_state)
+        if st.error:
+            raise RuntimeError("a device step fell outside its bias-correction window")
+        self.t_first = st.applied_steps + 1
+        self.pending = 0
+        return st

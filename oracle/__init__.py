@@ -260,6 +260,51 @@ def apply_update(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper:
            _ptr(_f32(np.ascontiguousarray(G))), _ptr(T.p), ctypes.byref(args))
 
 
+class LossScaler:
+    """Loss scale and its update rule, [OPT-INFRA] §10.1.
+
+    Constant scaler (dynamic=False): the scale never changes.  Dynamic
+    scaler: a step with non-finite grads resets the growth tracker and takes
+    one off the hysteresis tracker; once that tracker is at or below zero the
+    scale is backed off to max(scale * backoff, min_scale).  After
+    growth_interval clean steps in a row the scale grows by growth_factor and
+    both trackers reset.  Defaults are the page's: initial 2^32, growth 2.0,
+    backoff 0.5, interval 1000, hysteresis 2, min scale 1.0.  The scale is
+    held in fp32."""
+
+    def __init__(self, scale: float = 2.0 ** 32, dynamic: bool = True, growth_factor: float = 2.0,
+                 backoff_factor: float = 0.5, growth_interval: int = 1000, hysteresis: int = 2,
+                 min_scale: float = 1.0):
+        self.scale = np.float32(scale)
+        self.dynamic = dynamic
+        self.growth_factor = np.float32(growth_factor)
+        self.backoff_factor = np.float32(backoff_factor)
+        self.growth_interval = growth_interval
+        self.hysteresis = hysteresis
+        self.min_scale = np.float32(min_scale)
+        self.growth_tracker = 0
+        self.hysteresis_tracker = hysteresis
+
+    def inv_scale(self) -> float:
+        """fp32(1 / scale), the division in binary64."""
+        return float(np.float32(1.0 / float(self.scale)))
+
+    def update(self, found_inf: bool) -> None:
+        if not self.dynamic:
+            return
+        if found_inf:
+            self.growth_tracker = 0
+            self.hysteresis_tracker -= 1
+            if self.hysteresis_tracker <= 0:
+                self.scale = max(np.float32(self.scale * self.backoff_factor), self.min_scale)
+        else:
+            self.growth_tracker += 1
+            if self.growth_tracker == self.growth_interval:
+                self.growth_tracker = 0
+                self.hysteresis_tracker = self.hysteresis
+                self.scale = np.float32(self.scale * self.growth_factor)
+
+
 class OracleOptimizer:
     """Keeps the applied-step counter the way the pages do: a skipped step
     does not advance it ([OPT-INFRA] §10.2)."""
@@ -279,3 +324,28 @@ class OracleOptimizer:
         if r.applied:
             self.t += 1
         return r
+
+    def step_scaled(self, grads: Sequence[np.ndarray], scaler: LossScaler,
+                    skip_threshold: float = math.inf) -> StepResult:
+        """One step with the loss scaler in the loop, in the pages' order
+        ([OPT-INFRA] §10.2, §11.4): unscale with the current scale and check;
+        update the scaler with found_inf; a non-finite step returns; otherwise
+        take the norm, skip when it exceeds grad_norm_skip_threshold, else
+        clip and update."""
+        inv = scaler.inv_scale()
+        found = any(G.size and any_nonfinite(G) for G in grads)
+        scaler.update(found)
+        if found:
+            return StepResult(False, True, None, None)
+        n2 = 0.0
+        for G in grads:
+            if G.size:
+                n2 = n2 + sumsq(G, inv)
+        norm64, norm32 = norm_from_sumsq(n2)
+        if norm32 > skip_threshold:
+            return StepResult(False, False, norm32, norm64, extra={"threshold_skip": True})
+        do_clip, C, c64 = clip_coeff(self.max_norm, norm32)
+        apply_update(self.tensors, grads, self.hyper, self.groups, self.t + 1, inv, do_clip, C, c64,
+                     self.variant)
+        self.t += 1
+        return StepResult(True, False, norm32, norm64, do_clip, C)

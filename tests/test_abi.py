@@ -30,13 +30,33 @@ def _declared():
 
 def test_exports_every_declared_symbol(H):
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 16
     lib = H.load()
     for n in names:
         assert hasattr(lib, n), n
         assert n in H.SIGNATURES, f"binding lacks {n}"
     assert set(H.SIGNATURES) == set(names)
     assert H.hpo_abi_version() == 1
+
+
+def test_struct_layouts(H):
+    """The ctypes mirrors have the C sizes the header fixes."""
+    assert H.SCALER_STATE_BYTES == 48
+    assert ctypes.sizeof(H.hpo_set_info_t) == 64
+    assert ctypes.sizeof(H.hpo_adam_cfg) == 32 and ctypes.sizeof(H.hpo_group) == 16
+    assert ctypes.sizeof(H.hpo_scaler_cfg) == 32
+
+
+def test_device_step_validation(H):
+    L = H.load()
+    cfg = H.make_cfg()
+    groups, n = H.make_groups([(1e-3, 0.1)])
+    scfg = H.make_scaler_cfg()
+    assert L.hpo_step_device(None, ctypes.byref(cfg), groups, n, 1.0, ctypes.byref(scfg), None, 1, 1, None) == H.HPO_EINVAL
+    assert L.hpo_scaler_state_init(None, 1.0, 1, 0, None) == H.HPO_EINVAL
+    assert L.hpo_scaler_state_init(ctypes.c_void_p(0x1004), 1.0, 1, 0, None) == H.HPO_EINVAL  # not 8-byte aligned
+    assert L.hpo_scaler_state_init(ctypes.c_void_p(0x1000), -1.0, 1, 0, None) == H.HPO_EINVAL
+    assert L.hpo_scaler_state_init(ctypes.c_void_p(0x1000), 1.0, 0, 0, None) == H.HPO_EINVAL
 
 
 def test_status_strings(H):

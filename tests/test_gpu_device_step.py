@@ -1,0 +1,154 @@
+"""GPU parity of the device-resident step (hpo_step_device): the loss scaler,
+the skip decisions and the applied-step counter live on the device and steps
+are enqueued without host synchronisation.  Compared with the oracle's
+scaled trajectory (oracle.LossScaler + OracleOptimizer.step_scaled)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import banner, require_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def H():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.lib()
+    return oracle
+
+
+SIZES = [70_001, 4096, 131_072, 3]
+GROUPS = [0, 1, 0, 1]
+INF_STEPS = {3, 4, 10, 25}
+BIG_STEP = 15          # finite grads whose norm exceeds the skip threshold
+SYNC_AFTER = {2, 9, 16, 17, 40}
+
+
+def _true_grads(k, rng_seed=500):
+    rng = np.random.default_rng(rng_seed + k)
+    gs = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for n in SIZES]
+    if k == BIG_STEP:
+        gs = [(g * np.float32(1e4)).astype(np.float32) for g in gs]
+    return gs
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_device_step_sequence_matches_oracle(H, orc, mode):
+    banner(f"device-resident step sequence, mode {mode}")
+    from mixed_precision_optimizer_amd import DeviceAdamW
+    rng = np.random.default_rng(400)
+    th0 = [rng.standard_normal(n).astype(np.float32) for n in SIZES]
+    ths = [torch.from_numpy(a.copy()).to(DEV) for a in th0]
+    ps = [t.to(torch.bfloat16) for t in ths]
+    gs = [torch.zeros(n, device=DEV) for n in SIZES]
+    ms = [torch.zeros(n, device=DEV) for n in SIZES]
+    vs = [torch.zeros(n, device=DEV) for n in SIZES]
+    hset = H.hpo_set_create_list(ps, ths, gs, ms, vs, GROUPS)
+    groups = [(1e-3, 0.1), (1e-3, 0.0)]
+    kw = dict(loss_scale=2.0 ** 16, dynamic=True, growth_interval=5, hysteresis=2, min_scale=1.0,
+              grad_norm_skip_threshold=50.0)
+    opt = DeviceAdamW(hset, groups, mode=mode, max_norm=1.0, **kw)
+    T = [orc.OTensor(a.copy(), np.zeros_like(a), np.zeros_like(a), p.view(torch.int16).cpu().numpy().view(np.uint16).copy(), g)
+         for a, p, g in zip(th0, ps, GROUPS)]
+    O = orc.OracleOptimizer(T, orc.Hyper(mode=mode), groups, max_norm=1.0)
+    sc = orc.LossScaler(scale=2.0 ** 16, dynamic=True, growth_interval=5, hysteresis=2, min_scale=1.0)
+    applied = skipped = 0
+    for k in range(1, 41):
+        true = _true_grads(k)
+        # the caller's backward: stored grads = true grads * current loss scale,
+        # taken from the device state without a sync
+        for g, t in zip(gs, true):
+            g.copy_(torch.from_numpy(t))
+            g.mul_(opt.loss_scale_tensor)
+        if k in INF_STEPS:
+            gs[2][-1] = float("inf")
+        stored = [(t * sc.scale).astype(np.float32) for t in true]
+        if k in INF_STEPS:
+            stored[2][-1] = np.inf
+        r = O.step_scaled(stored, sc, skip_threshold=50.0)
+        applied += int(r.applied)
+        skipped += int(not r.applied)
+        opt.step()
+        if k in SYNC_AFTER:
+            st = opt.sync()
+            assert st.error == 0
+            assert st.applied_steps == O.t == applied and st.skipped_steps == skipped, k
+            assert st.loss_scale == float(sc.scale) and st.inv_scale == sc.inv_scale(), k
+            assert st.growth_tracker == sc.growth_tracker and st.hysteresis_tracker == sc.hysteresis_tracker, k
+            assert bool(st.found_inf) == bool(r.found_inf) and bool(st.applied) == r.applied, k
+            if r.norm32 is not None:
+                assert st.grad_norm == r.norm32 or abs(st.grad_norm - r.norm64) <= 1e-5 * r.norm64
+            for i in range(len(SIZES)):
+                assert np.array_equal(to_np(ths[i]).view(np.uint32), T[i].theta.view(np.uint32)), (k, i)
+                assert np.array_equal(to_np(ms[i]).view(np.uint32), T[i].m.view(np.uint32)), (k, i)
+                assert np.array_equal(to_np(vs[i]).view(np.uint32), T[i].v.view(np.uint32)), (k, i)
+                assert np.array_equal(to_np(ps[i]), T[i].p), (k, i)
+    # the script exercised every branch: skips by inf and by threshold, a back-off and a growth
+    assert skipped == len(INF_STEPS) + 1 and applied == 40 - skipped
+    hset.close()
+
+
+def test_long_unsynchronised_run_uses_full_window(H, orc):
+    """More steps than one window without any explicit sync: the optimizer
+    re-reads the state every 32 steps; the result equals the oracle's."""
+    banner("device-resident step, 70 steps without explicit sync")
+    from mixed_precision_optimizer_amd import DeviceAdamW
+    n = 50_000
+    rng = np.random.default_rng(410)
+    th0 = rng.standard_normal(n).astype(np.float32)
+    th = torch.from_numpy(th0.copy()).to(DEV)
+    p = th.to(torch.bfloat16)
+    g = torch.zeros(n, device=DEV)
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    hset = H.hpo_set_create_flat(p, th, g, m, v)
+    opt = DeviceAdamW(hset, [(1e-3, 0.1)], max_norm=1.0, loss_scale=1.0, dynamic=False)
+    T = orc.OTensor.fresh(th0)
+    O = orc.OracleOptimizer([T], orc.Hyper(), [(1e-3, 0.1)], max_norm=1.0)
+    sc = orc.LossScaler(scale=1.0, dynamic=False)
+    grads = [(np.random.default_rng(420 + k).standard_normal(n) * 1e-2).astype(np.float32) for k in range(70)]
+    dev_grads = [torch.from_numpy(x).to(DEV) for x in grads]
+    for k in range(70):
+        g.copy_(dev_grads[k])
+        opt.step()
+        O.step_scaled([grads[k]], sc)
+    st = opt.sync()
+    assert st.applied_steps == 70 and st.error == 0
+    assert np.array_equal(to_np(th).view(np.uint32), T.theta.view(np.uint32))
+    assert np.array_equal(to_np(p), T.p)
+    hset.close()
+
+
+def test_window_error_is_reported_not_applied(H):
+    """A step whose device t falls outside the window the host gave is not
+    applied and sets the sticky error flag (condition forced from the host;
+    every kernel runs to completion)."""
+    banner("window error")
+    n = 4096
+    th = torch.randn(n, device=DEV)
+    p = th.to(torch.bfloat16)
+    g = torch.randn(n, device=DEV) * 1e-3
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    th0 = th.clone()
+    hset = H.hpo_set_create_flat(p, th, g, m, v)
+    d_state = H.new_scaler_state()
+    H.hpo_scaler_state_init(d_state, 1.0, 1, 0)
+    scfg = H.make_scaler_cfg(dynamic=False)
+    H.hpo_step_device(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1.0, scfg, d_state, 5, 1)  # device t = 1, window {5}
+    torch.cuda.synchronize()
+    st = H.read_scaler_state(d_state)
+    assert st.error == 1 and st.applied == 0 and st.applied_steps == 0 and st.skipped_steps == 1
+    assert torch.equal(th, th0) and not m.any()
+    with pytest.raises(H.HpoError):
+        H.hpo_step_device(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1.0, scfg, d_state, 1, 33)
+    hset.close()

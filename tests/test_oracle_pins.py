@@ -426,3 +426,75 @@ def test_memory_ledgers():
     assert f"{70e9 * 16 / 1e12:.1f}" == gold["handbook_70b_total_tb"][0]
     # the layout this library steps: bf16 param + fp32 grad + fp32 master/m/v
     assert bf16_w + fp32 + 3 * fp32 == int(gold["megatron_fp32_grad_bytes_per_param"][0])
+
+
+# ---------------------------------------------------------------------------
+# loss scaler ("02 · Optimizer：算法与 infra" §10.1)
+# ---------------------------------------------------------------------------
+def test_scaler_defaults_and_single_spike_tolerance(orc):
+    """The page's defaults (initial 2^32, growth x2, backoff x0.5, window 1000,
+    hysteresis 2) and its point that a single inf does not lower the scale."""
+    sc = orc.LossScaler()
+    assert float(sc.scale) == 2.0 ** 32 and sc.growth_interval == 1000 and sc.hysteresis == 2
+    sc.update(True)
+    assert float(sc.scale) == 2.0 ** 32           # one spike is tolerated
+    sc.update(False)
+    sc.update(True)
+    assert float(sc.scale) == 2.0 ** 31           # the second one (no growth in between) backs off
+    sc.update(True)
+    assert float(sc.scale) == 2.0 ** 30           # and every further one, until a growth resets
+    for _ in range(999):
+        sc.update(False)
+    assert float(sc.scale) == 2.0 ** 30
+    sc.update(False)                               # 1000 clean steps in a row: grow
+    assert float(sc.scale) == 2.0 ** 31 and sc.hysteresis_tracker == 2 and sc.growth_tracker == 0
+    sc.update(True)
+    assert float(sc.scale) == 2.0 ** 31           # hysteresis restored by the growth
+
+
+def test_scaler_floor_and_constant(orc):
+    sc = orc.LossScaler(scale=4.0, hysteresis=1, min_scale=1.0)
+    for _ in range(5):
+        sc.update(True)
+    assert float(sc.scale) == 1.0
+    c = orc.LossScaler(scale=65536.0, dynamic=False)
+    for f in (True, True, False) * 400:
+        c.update(f)
+    assert float(c.scale) == 65536.0 and c.inv_scale() == 2.0 ** -16
+
+
+def test_scaler_matches_torch_amp_update_at_hysteresis_one(orc):
+    """With hysteresis 1 and no floor the rule is torch's own GradScaler
+    update (torch._amp_update_scale_, a library routine) step for step."""
+    rng = np.random.default_rng(50)
+    flags = rng.random(5000) < 0.03
+    sc = orc.LossScaler(scale=2.0 ** 20, hysteresis=1, growth_interval=37, min_scale=2.0 ** -126)
+    s_t = torch.tensor([2.0 ** 20])
+    g_t = torch.tensor([0], dtype=torch.int32)
+    for f in flags:
+        sc.update(bool(f))
+        torch._amp_update_scale_(s_t, g_t, torch.tensor([1.0 if f else 0.0]), 2.0, 0.5, 37)
+        assert float(sc.scale) == float(s_t[0]) and sc.growth_tracker == int(g_t[0])
+
+
+def test_scaled_step_skips_and_counts(orc):
+    """With the scaler in the loop: a non-finite step is skipped and backs off
+    (after hysteresis), a step over grad_norm_skip_threshold is skipped but
+    counts as clean, and t only counts applied steps."""
+    rng = np.random.default_rng(51)
+    th0 = rng.standard_normal(1000).astype(np.float32)
+    T = orc.OTensor.fresh(th0)
+    O = orc.OracleOptimizer([T], orc.Hyper(), [(1e-3, 0.1)], max_norm=1.0)
+    sc = orc.LossScaler(scale=1024.0, hysteresis=1, growth_interval=2)
+    g = (rng.standard_normal(1000) * 1e-3).astype(np.float32)
+    r = O.step_scaled([g * np.float32(1024.0)], sc)
+    assert r.applied and O.t == 1
+    bad = g * np.float32(1024.0)
+    bad[5] = np.nan
+    r = O.step_scaled([bad], sc, 10.0)
+    assert not r.applied and r.found_inf and O.t == 1 and float(sc.scale) == 512.0
+    big = (g * np.float32(1e5) * np.float32(512.0)).astype(np.float32)   # unscaled norm ~3, over 1.0
+    r = O.step_scaled([big], sc, skip_threshold=1.0)
+    assert not r.applied and not r.found_inf and O.t == 1 and r.extra["threshold_skip"]
+    r = O.step_scaled([g * np.float32(512.0)], sc, skip_threshold=1.0)
+    assert r.applied and O.t == 2 and float(sc.scale) == 1024.0  # two clean steps: grown
