@@ -33,10 +33,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "G params/s and achieved HBM GB/s (% of 8 TB/s) per full AdamW step"
-PEAK_HBM_GBPS = 8000.0
-UPDATE_BYTES = 30   # read grad, master, m, v (16); write master, m, v (12), bf16 param (2)
-GRADPASS_BYTES = 4  # read grad once
-STEP_BYTES = UPDATE_BYTES + GRADPASS_BYTES
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+GRADPASS_BYTES = 4  # the grad pass reads each stored grad once
+
+
+def update_bytes(w) -> int:
+    """Algorithmic bytes per element of the fused update for a workload's
+    storage: grad and master read (8), master written (4), each moment read
+    and written at its width, the 16-bit param written (none for fp32)."""
+    mom = 2 if w.state_dtype == "bf16" else 4
+    par = 0 if w.param_dtype == "fp32" else 2
+    return 12 + 4 * mom + par
 
 
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_hbm_traffic_zero_shard_70b_over_8.txt")
@@ -82,6 +89,10 @@ def parse():
     ap.add_argument("--workload", default="zero_shard",
                     choices=["zero_shard", "zero_shard_ranges", "llama8b", "ragged", "two_matrices"])
     ap.add_argument("--numel", type=int, default=None, help="override the flat shard's size")
+    ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"],
+                    help="exp_avg / exp_avg_sq storage of the flat shard")
+    ap.add_argument("--param-dtype", default="bf16", choices=["bf16", "fp16"],
+                    help="model-param dtype of the flat shard")
     ap.add_argument("--cpu-sample", type=int, default=1 << 28,
                     help="elements of the workload the CPU oracle steps (0: skip)")
     ap.add_argument("--cpu-steps", type=int, default=2)
@@ -110,7 +121,8 @@ def calibrate_copy(n):
 def workload(args):
     from mixed_precision_optimizer_amd import inputs
     if args.workload == "zero_shard":
-        return inputs.zero_shard(args.numel) if args.numel else inputs.zero_shard()
+        return inputs.zero_shard(args.numel or 8_750_000_000, state_dtype=args.state_dtype,
+                                 param_dtype=args.param_dtype)
     if args.workload == "zero_shard_ranges":
         return inputs.zero_shard_ranges()
     if args.workload == "llama8b":
@@ -141,8 +153,9 @@ def cpu_sample(bufs, n_sample):
     import torch
     n = min(n_sample, bufs.total)
     host = lambda t: t[:n].detach().cpu().numpy().copy()
-    p = bufs.param[:n].view(torch.int16).cpu().numpy().view(np.uint16).copy()
-    return host(bufs.master), host(bufs.exp_avg), host(bufs.exp_avg_sq), p, host(bufs.grad)
+    bits = lambda t: t[:n].view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    mom = bits if bufs.exp_avg.dtype == torch.bfloat16 else host
+    return host(bufs.master), mom(bufs.exp_avg), mom(bufs.exp_avg_sq), bits(bufs.param), host(bufs.grad)
 
 
 def cpu_baseline(sample, w, steps):
@@ -150,7 +163,7 @@ def cpu_baseline(sample, w, steps):
     import oracle
     theta, m, v, p, G = sample
     n = theta.size
-    T = oracle.OTensor(theta, m, v, p, 0)
+    T = oracle.OTensor(theta, m, v, p, 0, w.param_dtype == "fp16")
     O = oracle.OracleOptimizer([T], oracle.Hyper(w.beta1, w.beta2, w.eps, w.mode), w.groups(),
                                max_norm=w.max_norm)
     times = []
@@ -164,7 +177,8 @@ def cpu_baseline(sample, w, steps):
             "sample": f"first {n} elements of the same workload (initial fp32 master/m/v, bf16 param, step-1 "
                       f"grads), full step (inf check, binary64 norm, clip, AdamW, bf16 RNE), median of {steps} "
                       f"steps, single-threaded C ({os.cpu_count()} host CPUs visible); "
-                      f"{STEP_BYTES * n / dt / 1e9:.2f} GB/s at 34 B/elem",
+                      f"{(update_bytes(w) + GRADPASS_BYTES) * n / dt / 1e9:.2f} GB/s at "
+                      f"{update_bytes(w) + GRADPASS_BYTES} B/elem",
             "ms_per_step": round(dt * 1e3, 2)}
 
 
@@ -234,9 +248,10 @@ def main():
     ms_step = wall * 1e3 / args.steps
     upd = statistics.mean(update_ms)
     gp = statistics.mean(gradpass_ms)
-    upd_gbps = UPDATE_BYTES * N / (upd * 1e-3) / 1e9
+    ub = update_bytes(w)
+    upd_gbps = ub * N / (upd * 1e-3) / 1e9
     gp_gbps = GRADPASS_BYTES * N / (gp * 1e-3) / 1e9
-    step_gbps = STEP_BYTES * N / (ms_step * 1e-3) / 1e9
+    step_gbps = (ub + GRADPASS_BYTES) * N / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(w.name, N)
     traffic_gb = None if traffic is None else round(traffic / 1e9, 3)
     log(f"norm {norm_v:.6g}, applied steps {t_applied}; step {ms_step:.3f} ms, update {upd:.3f} ms "
@@ -255,19 +270,19 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "numel": N, "n_tensors": w.n_tensors, "param_dtype": w.param_dtype,
-                   "state": "fp32 master, fp32 main_grad, fp32 exp_avg/exp_avg_sq", "max_norm": w.max_norm,
+                   "state": f"fp32 master, fp32 main_grad, {w.state_dtype} exp_avg/exp_avg_sq", "max_norm": w.max_norm,
                    "lr": w.lr, "weight_decay": w.weight_decay, "loss_scale": w.loss_scale,
                    "parallelism": "one GPU (one data-parallel rank's shard)"},
         "hbm_full_step": {"GBps": round(step_gbps, 1), "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
-                          "bytes_per_elem": STEP_BYTES},
-        "kernels": {"adam_update": {"ms": round(upd, 4), "GBps": round(upd_gbps, 1), "bytes_per_elem": UPDATE_BYTES},
+                          "bytes_per_elem": ub + GRADPASS_BYTES},
+        "kernels": {"adam_update": {"ms": round(upd, 4), "GBps": round(upd_gbps, 1), "bytes_per_elem": ub},
                     "grad_pass+finalize": {"ms": round(gp, 4), "GBps": round(gp_gbps, 1),
                                            "bytes_per_elem": GRADPASS_BYTES}},
         "roofline": {"bound": "hbm", "achieved": round(upd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(upd_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_gb,
                      "traffic_unit": "GB per launch of the update kernel (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, "
                                      "scales from a device copy of known size); algorithmic: "
-                                     f"{UPDATE_BYTES * N / 1e9:.1f} GB"},
+                                     f"{ub * N / 1e9:.1f} GB"},
     }
     # the same step with the scaler, skip decision and step counter on the
     # device: no host round trip per step (hpo_step_device); constant scale 1

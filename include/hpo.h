@@ -63,13 +63,23 @@ typedef enum {
     HPO_EDEVICE = -5  /* the current device is not the set's device */
 } hpo_status;
 
-/* dtype of the model params a set writes back to.
+/* dtype of the model params a set writes back to ([OPT-INFRA] §9.2: the
+ * wrapper keeps an fp32 master for fp16 and bf16 params).
  * HPO_PARAM_BF16: bf16 params, each with its own fp32 master.
  * HPO_PARAM_FP32: fp32 params are their own master ([FP32-RFC] §7.2, native
  *                 fp32 params): param must be NULL or equal to main_param, and
  *                 no write-back happens.
- * Any other value (fp16 included) is rejected with HPO_EDTYPE. */
-typedef enum { HPO_PARAM_BF16 = 0, HPO_PARAM_FP32 = 1 } hpo_param_dtype;
+ * HPO_PARAM_FP16: fp16 params (IEEE round-to-nearest-even write-back, fp16
+ *                 subnormals kept, overflow to infinity); fp16 training is
+ *                 what the dynamic loss scaler below is for.
+ * Optionally OR-ed with HPO_STATE_BF16: exp_avg and exp_avg_sq are then bf16
+ * arrays (the exp_avg / exp_avg_sq pointers point at 2-byte elements), read
+ * exactly and written back rounded to nearest even ([OPT-INFRA] §16, the
+ * precision-aware optimizer's lower-precision moments); the update itself
+ * still runs in fp32.  Any other value is rejected with HPO_EDTYPE, never
+ * silently cast ([FP32-RFC] §7.2). */
+typedef enum { HPO_PARAM_BF16 = 0, HPO_PARAM_FP32 = 1, HPO_PARAM_FP16 = 2 } hpo_param_dtype;
+#define HPO_STATE_BF16 0x100
 
 /* Weight-decay form ([OPT-INFRA] §3): decoupled (AdamW, the default there) or
  * an L2 term added to the gradient before the moments (Adam + L2). */

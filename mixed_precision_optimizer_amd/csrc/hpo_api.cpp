@@ -111,21 +111,48 @@ hpo_status check_sizes(int32_t n_tensors, const int64_t* numel)
     return HPO_OK;
 }
 
+/* What a set stores: the model-param dtype and the moments' width. */
+struct Layout {
+    int32_t pdt;        /* HPO_PARAM_BF16 / FP32 / FP16 */
+    int32_t state_bf16; /* exp_avg / exp_avg_sq are bf16 */
+    int64_t mom_bytes() const { return state_bf16 ? 2 : 4; }
+};
+
+hpo_status decode_dtype(int32_t param_dtype, Layout& lay)
+{
+    lay.pdt = param_dtype & 0xFF;
+    lay.state_bf16 = (param_dtype & HPO_STATE_BF16) ? 1 : 0;
+    const bool pdt_ok = lay.pdt == HPO_PARAM_BF16 || lay.pdt == HPO_PARAM_FP32 || lay.pdt == HPO_PARAM_FP16;
+    if (!pdt_ok || (param_dtype & ~(0xFF | HPO_STATE_BF16)) != 0)
+        return fail(HPO_EDTYPE,
+                    "param dtype %d is not supported (bf16 = 0, fp32 = 1, fp16 = 2, optionally | HPO_STATE_BF16)",
+                    param_dtype);
+    return HPO_OK;
+}
+
+void* advance(void* p, int64_t elems, int64_t bytes)
+{
+    return p ? static_cast<void*>(static_cast<char*>(p) + elems * bytes) : nullptr;
+}
+
 /* Pointer rules for one tensor (see hpo.h). */
-hpo_status check_tensor(int32_t i, int32_t pdt, void* param, float* master, float* grad, float* m,
-                        float* v, int64_t numel)
+hpo_status check_tensor(int32_t i, const Layout& lay, void* param, float* master, float* grad, void* m, void* v,
+                        int64_t numel)
 {
     if (numel == 0)
         return HPO_OK;
     if (!master || !grad || !m || !v)
         return fail(HPO_EINVAL, "tensor %d: main_param, main_grad, exp_avg and exp_avg_sq must be non-NULL", i);
-    if (!aligned(master, 4) || !aligned(grad, 4) || !aligned(m, 4) || !aligned(v, 4))
+    if (!aligned(master, 4) || !aligned(grad, 4))
         return fail(HPO_EINVAL, "tensor %d: fp32 pointers must be 4-byte aligned", i);
-    if (pdt == HPO_PARAM_BF16) {
+    if (!aligned(m, static_cast<uintptr_t>(lay.mom_bytes())) || !aligned(v, static_cast<uintptr_t>(lay.mom_bytes())))
+        return fail(HPO_EINVAL, "tensor %d: exp_avg / exp_avg_sq must be %lld-byte aligned", i,
+                    (long long)lay.mom_bytes());
+    if (lay.pdt != HPO_PARAM_FP32) {
         if (!param)
-            return fail(HPO_EINVAL, "tensor %d: bf16 param pointer is NULL", i);
+            return fail(HPO_EINVAL, "tensor %d: 16-bit param pointer is NULL", i);
         if (!aligned(param, 2))
-            return fail(HPO_EINVAL, "tensor %d: bf16 param pointer must be 2-byte aligned", i);
+            return fail(HPO_EINVAL, "tensor %d: 16-bit param pointer must be 2-byte aligned", i);
     } else if (param != nullptr && param != static_cast<void*>(master)) {
         return fail(HPO_EINVAL,
                     "tensor %d: an fp32 param is its own master, so param must be NULL or equal main_param", i);
@@ -133,58 +160,61 @@ hpo_status check_tensor(int32_t i, int32_t pdt, void* param, float* master, floa
     return HPO_OK;
 }
 
-hpo::TensorDesc make_desc(int32_t pdt, void* param, float* master, float* grad, float* m, float* v,
+hpo::TensorDesc make_desc(const Layout& lay, void* param, float* master, float* grad, void* m, void* v,
                           int64_t numel, int32_t group)
 {
     hpo::TensorDesc d{};
-    d.param = (pdt == HPO_PARAM_FP32) ? static_cast<void*>(master) : param;
+    d.param = (lay.pdt == HPO_PARAM_FP32) ? static_cast<void*>(master) : param;
     d.master = master;
     d.grad = grad;
     d.exp_avg = m;
     d.exp_avg_sq = v;
     d.numel = numel;
     d.group = group;
-    const bool p_ok = (pdt == HPO_PARAM_FP32) || aligned(d.param, 8);
-    d.vec_ok = (aligned(master, 16) && aligned(grad, 16) && aligned(m, 16) && aligned(v, 16) && p_ok) ? 1 : 0;
+    const bool p_ok = (lay.pdt == HPO_PARAM_FP32) || aligned(d.param, 8);
+    const uintptr_t mv = static_cast<uintptr_t>(4 * lay.mom_bytes());  /* 4 elements */
+    d.vec_ok = (aligned(master, 16) && aligned(grad, 16) && aligned(m, mv) && aligned(v, mv) && p_ok) ? 1 : 0;
     return d;
 }
 
-/* Position of an fp32 (bf16) pointer inside its 16-byte (8-byte) line, in
- * elements: 0..3. */
+/* Position of a pointer inside the line that holds 4 of its elements, in
+ * elements: 0..3 (16-byte lines for fp32, 8-byte lines for 16-bit data). */
 int32_t phase32(const void* p) { return static_cast<int32_t>((reinterpret_cast<uintptr_t>(p) / 4) % 4); }
 int32_t phase16(const void* p) { return static_cast<int32_t>((reinterpret_cast<uintptr_t>(p) / 2) % 4); }
 
-/* Appends the descriptor piece(s) of one tensor.  A tensor whose five
- * pointers sit at the same element phase of a 16-byte line (views that start
+/* Appends the descriptor piece(s) of one tensor.  A tensor whose pointers all
+ * sit at the same element phase of their 4-element lines (views that start
  * a few elements into a flat buffer, shard ranges) is split into a head of
  * fewer than 4 elements on the element-at-a-time path and a body whose
- * pointers are all 16-byte (bf16: 8-byte) aligned.  Returns whether the
- * tensor's body takes the vector path. */
-bool add_pieces(std::vector<hpo::TensorDesc>& out, int32_t pdt, void* param, float* master, float* grad,
-                float* m, float* v, int64_t numel, int32_t group)
+ * pointers all allow vector access.  Returns whether the tensor's body takes
+ * the vector path. */
+bool add_pieces(std::vector<hpo::TensorDesc>& out, const Layout& lay, void* param, float* master, float* grad,
+                void* m, void* v, int64_t numel, int32_t group)
 {
     if (numel == 0) {
-        out.push_back(make_desc(pdt, param, master, grad, m, v, 0, group));
+        out.push_back(make_desc(lay, param, master, grad, m, v, 0, group));
         return false;
     }
-    hpo::TensorDesc d = make_desc(pdt, param, master, grad, m, v, numel, group);
+    hpo::TensorDesc d = make_desc(lay, param, master, grad, m, v, numel, group);
     if (d.vec_ok) {
         out.push_back(d);
         return true;
     }
     const int32_t ph = phase32(master);
-    const bool same = phase32(grad) == ph && phase32(m) == ph && phase32(v) == ph &&
-                      (pdt == HPO_PARAM_FP32 || phase16(param) == ph);
+    auto mphase = [&](const void* q) { return lay.state_bf16 ? phase16(q) : phase32(q); };
+    const bool same = phase32(grad) == ph && mphase(m) == ph && mphase(v) == ph &&
+                      (lay.pdt == HPO_PARAM_FP32 || phase16(param) == ph);
     if (!same) {
         out.push_back(d);
         return false;
     }
     const int64_t head = std::min<int64_t>((4 - ph) % 4, numel);
-    out.push_back(make_desc(pdt, param, master, grad, m, v, head, group));
+    out.push_back(make_desc(lay, param, master, grad, m, v, head, group));
     if (numel == head)
         return false;
-    void* p2 = (pdt == HPO_PARAM_FP32) ? nullptr : static_cast<void*>(static_cast<uint16_t*>(param) + head);
-    hpo::TensorDesc body = make_desc(pdt, p2, master + head, grad + head, m + head, v + head, numel - head, group);
+    void* p2 = (lay.pdt == HPO_PARAM_FP32) ? nullptr : advance(param, head, 2);
+    hpo::TensorDesc body = make_desc(lay, p2, master + head, grad + head, advance(m, head, lay.mom_bytes()),
+                                     advance(v, head, lay.mom_bytes()), numel - head, group);
     out.push_back(body);
     return body.vec_ok != 0;
 }
@@ -319,8 +349,9 @@ hpo_status hpo_plan_chunks(int32_t n_tensors, const int64_t* numel, int64_t n_ch
 namespace {
 
 /* Builds a table-driven set from descriptor pieces (see add_pieces). */
-hpo_status create_from_pieces(hpo_set* out, int32_t param_dtype, std::vector<hpo::TensorDesc>& descs,
-                              int32_t n_tensors, int32_t n_vector, int32_t max_group, void* stream)
+hpo_status create_from_pieces(hpo_set* out, int32_t param_dtype, const Layout& lay,
+                              std::vector<hpo::TensorDesc>& descs, int32_t n_tensors, int32_t n_vector,
+                              int32_t max_group, void* stream)
 {
     if (descs.size() > 0x7FFFFFFFu)
         return fail(HPO_EINVAL, "too many tensor pieces");
@@ -381,16 +412,10 @@ hpo_status create_from_pieces(hpo_set* out, int32_t param_dtype, std::vector<hpo
     s->view.tensors = s->d_tensors;
     s->view.chunks = s->d_chunks;
     s->view.is_flat = 0;
-    s->view.param_dtype = param_dtype;
+    s->view.param_dtype = lay.pdt;
+    s->view.state_bf16 = lay.state_bf16;
     *out = s;
     return ok();
-}
-
-hpo_status check_dtype(int32_t param_dtype)
-{
-    if (param_dtype != HPO_PARAM_BF16 && param_dtype != HPO_PARAM_FP32)
-        return fail(HPO_EDTYPE, "param dtype %d is not supported (bf16 = 0 with an fp32 master, or fp32 = 1)", param_dtype);
-    return HPO_OK;
 }
 
 }  // namespace
@@ -406,7 +431,8 @@ hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dt
     if (!out)
         return fail(HPO_EINVAL, "out is NULL");
     *out = nullptr;
-    hpo_status st = check_dtype(param_dtype);
+    Layout lay{};
+    hpo_status st = decode_dtype(param_dtype, lay);
     if (st != HPO_OK)
         return st;
     st = check_sizes(n_tensors, numel);
@@ -414,12 +440,12 @@ hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dt
         return st;
     if (n_tensors > 0 && (!main_param || !main_grad || !exp_avg || !exp_avg_sq))
         return fail(HPO_EINVAL, "pointer arrays must be non-NULL");
-    if (n_tensors > 0 && param_dtype == HPO_PARAM_BF16 && !param)
-        return fail(HPO_EINVAL, "param array is NULL for a bf16 set");
+    if (n_tensors > 0 && lay.pdt != HPO_PARAM_FP32 && !param)
+        return fail(HPO_EINVAL, "param array is NULL for a 16-bit-param set");
     int32_t max_group = 0;
     for (int32_t i = 0; i < n_tensors; ++i) {
         void* p = param ? param[i] : nullptr;
-        st = check_tensor(i, param_dtype, p, main_param[i], main_grad[i], exp_avg[i], exp_avg_sq[i], numel[i]);
+        st = check_tensor(i, lay, p, main_param[i], main_grad[i], exp_avg[i], exp_avg_sq[i], numel[i]);
         if (st != HPO_OK)
             return st;
         const int32_t g = group_index ? group_index[i] : 0;
@@ -432,9 +458,9 @@ hpo_status hpo_set_create_list(hpo_set* out, int32_t n_tensors, int32_t param_dt
     descs.reserve(static_cast<size_t>(n_tensors));
     int32_t n_vector = 0;
     for (int32_t i = 0; i < n_tensors; ++i)
-        n_vector += add_pieces(descs, param_dtype, param ? param[i] : nullptr, main_param[i], main_grad[i],
+        n_vector += add_pieces(descs, lay, param ? param[i] : nullptr, main_param[i], main_grad[i],
                                exp_avg[i], exp_avg_sq[i], numel[i], group_index ? group_index[i] : 0);
-    return create_from_pieces(out, param_dtype, descs, n_tensors, n_vector, max_group, stream);
+    return create_from_pieces(out, param_dtype, lay, descs, n_tensors, n_vector, max_group, stream);
 }
 
 hpo_status hpo_set_create_flat_ranges(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
@@ -445,13 +471,14 @@ hpo_status hpo_set_create_flat_ranges(hpo_set* out, int64_t numel, int32_t param
     if (!out)
         return fail(HPO_EINVAL, "out is NULL");
     *out = nullptr;
-    hpo_status st = check_dtype(param_dtype);
+    Layout lay{};
+    hpo_status st = decode_dtype(param_dtype, lay);
     if (st != HPO_OK)
         return st;
     st = check_sizes(1, &numel);
     if (st != HPO_OK)
         return st;
-    st = check_tensor(0, param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel);
+    st = check_tensor(0, lay, param, main_param, main_grad, exp_avg, exp_avg_sq, numel);
     if (st != HPO_OK)
         return st;
     if (n_ranges < 1 || !range_start || !range_group)
@@ -474,12 +501,11 @@ hpo_status hpo_set_create_flat_ranges(hpo_set* out, int64_t numel, int32_t param
     for (int32_t k = 0; k < n_ranges; ++k) {
         const int64_t a = range_start[k];
         const int64_t len = (k + 1 < n_ranges ? range_start[k + 1] : numel) - a;
-        void* p = (param_dtype == HPO_PARAM_FP32 || !param) ? param
-                                                             : static_cast<void*>(static_cast<uint16_t*>(param) + a);
-        n_vector += add_pieces(descs, param_dtype, p, main_param + a, main_grad + a, exp_avg + a, exp_avg_sq + a,
-                               len, range_group[k]);
+        void* p = (lay.pdt == HPO_PARAM_FP32) ? param : advance(param, a, 2);
+        n_vector += add_pieces(descs, lay, p, main_param + a, main_grad + a, advance(exp_avg, a, lay.mom_bytes()),
+                               advance(exp_avg_sq, a, lay.mom_bytes()), len, range_group[k]);
     }
-    return create_from_pieces(out, param_dtype, descs, n_ranges, n_vector, max_group, stream);
+    return create_from_pieces(out, param_dtype, lay, descs, n_ranges, n_vector, max_group, stream);
 }
 
 hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
@@ -489,21 +515,22 @@ hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype,
     if (!out)
         return fail(HPO_EINVAL, "out is NULL");
     *out = nullptr;
-    hpo_status st = check_dtype(param_dtype);
+    Layout lay{};
+    hpo_status st = decode_dtype(param_dtype, lay);
     if (st != HPO_OK)
         return st;
     st = check_sizes(1, &numel);
     if (st != HPO_OK)
         return st;
-    st = check_tensor(0, param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel);
+    st = check_tensor(0, lay, param, main_param, main_grad, exp_avg, exp_avg_sq, numel);
     if (st != HPO_OK)
         return st;
-    if (numel > 0 && !make_desc(param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0).vec_ok) {
-        /* a flat range that does not start on a 16-byte line: table-driven,
+    if (numel > 0 && !make_desc(lay, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0).vec_ok) {
+        /* a flat range that does not start on a vector line: table-driven,
          * with the head peeled off (same results, vector body) */
         std::vector<hpo::TensorDesc> descs;
-        const int32_t nv = add_pieces(descs, param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0);
-        st = create_from_pieces(out, param_dtype, descs, 1, nv, 0, stream);
+        const int32_t nv = add_pieces(descs, lay, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0);
+        st = create_from_pieces(out, param_dtype, lay, descs, 1, nv, 0, stream);
         if (st == HPO_OK)
             (*out)->is_flat = 1;
         return st;
@@ -526,11 +553,12 @@ hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype,
     s->is_flat = 1;
     s->numel = numel;
     s->n_chunks = nc;
-    s->view.flat = make_desc(param_dtype, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0);
+    s->view.flat = make_desc(lay, param, main_param, main_grad, exp_avg, exp_avg_sq, numel, 0);
     s->n_vector = s->view.flat.vec_ok;
     s->view.chunk_elems = ch;
     s->view.is_flat = 1;
-    s->view.param_dtype = param_dtype;
+    s->view.param_dtype = lay.pdt;
+    s->view.state_bf16 = lay.state_bf16;
     st = alloc_partials(s);
     if (st != HPO_OK) { free_set(s); return st; }
     *out = s;
@@ -771,7 +799,7 @@ hpo_status hpo_copy_main_to_model(hpo_set s, void* stream)
     hpo_status st = check_set(s);
     if (st != HPO_OK)
         return st;
-    if (s->param_dtype == HPO_PARAM_FP32)
+    if (s->view.param_dtype == HPO_PARAM_FP32)
         return ok();
     hipError_t e = hpo::launch_copy_main_to_model(s->view, s->n_chunks, as_stream(stream));
     if (e != hipSuccess)

@@ -50,14 +50,14 @@ inline int64_t stage_parts(int64_t n) { return n > kFinalSpan ? (n + kFinalSpan 
 
 /* One tensor of a set, as the kernels see it (64 bytes). */
 struct TensorDesc {
-    void* param;       /* bf16 model param; == master for fp32 sets */
+    void* param;       /* 16-bit model param; == master for fp32 sets */
     float* master;
     float* grad;
-    float* exp_avg;
-    float* exp_avg_sq;
+    void* exp_avg;     /* fp32 or bf16 elements, per the set's state dtype */
+    void* exp_avg_sq;
     int64_t numel;
     int32_t group;
-    int32_t vec_ok;    /* all five pointers allow 16-byte (bf16: 8-byte) access */
+    int32_t vec_ok;    /* every array allows a 4-element vector access (16 B fp32, 8 B 16-bit) */
     int64_t reserved;  /* pads the descriptor to 64 bytes */
 };
 static_assert(sizeof(TensorDesc) == 64, "TensorDesc layout");
@@ -79,7 +79,9 @@ struct SetView {
     const Chunk* chunks;        /* list sets only */
     int64_t chunk_elems;
     int32_t is_flat;
-    int32_t param_dtype;
+    int32_t param_dtype;  /* HPO_PARAM_BF16 / FP32 / FP16 */
+    int32_t state_bf16;   /* exp_avg / exp_avg_sq held as bf16 */
+    int32_t reserved;
 };
 
 /* Per-step scalars of the update, all formed on the host in binary64 and

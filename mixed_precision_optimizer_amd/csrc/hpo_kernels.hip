@@ -82,6 +82,16 @@ __device__ __forceinline__ float4 ld_stream(const float4* p)
 #endif
 }
 
+__device__ __forceinline__ uint2 ld_stream(const uint2* p)
+{
+#if HPO_NT_LOADS
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+#else
+    return *p;
+#endif
+}
+
 __device__ __forceinline__ void st_stream(float4* p, float4 v)
 {
 #if HPO_NT_STORES
@@ -160,6 +170,74 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+}
+
+/* fp32 -> fp16 bits for fp16 model params ([OPT-INFRA] §9.2 write-back):
+ * the hardware conversion, which rounds to nearest even under the default
+ * mode and keeps fp16 subnormals. */
+__device__ __forceinline__ uint32_t fp16_rne_bits(float x)
+{
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+}
+
+/* 16-bit model param bits of a master value, by param dtype. */
+template <int PDT>
+__device__ __forceinline__ uint32_t param_bits(float x)
+{
+    if constexpr (PDT == HPO_PARAM_FP16)
+        return fp16_rne_bits(x);
+    else
+        return bf16_rne_bits(x);
+}
+
+template <int PDT>
+__device__ __forceinline__ uint2 pack_param4(float4 t)
+{
+    return make_uint2(param_bits<PDT>(t.x) | (param_bits<PDT>(t.y) << 16),
+                      param_bits<PDT>(t.z) | (param_bits<PDT>(t.w) << 16));
+}
+
+/* Moments: fp32, or bf16 widened exactly on load and rounded to nearest even
+ * on store ([OPT-INFRA] §16, lower-precision exp_avg / exp_avg_sq). */
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+template <int SDT>
+__device__ __forceinline__ float4 ld_moment4(const void* base, int64_t i)
+{
+    if constexpr (SDT == 1) {
+        const uint2 w = ld_stream(static_cast<const uint2*>(base) + i);
+        return make_float4(bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
+                           bf16_to_f32(w.y >> 16));
+    } else {
+        return ld_stream(static_cast<const float4*>(base) + i);
+    }
+}
+
+template <int SDT>
+__device__ __forceinline__ void st_moment4(void* base, int64_t i, float4 x)
+{
+    if constexpr (SDT == 1)
+        st_stream(static_cast<uint2*>(base) + i, make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)));
+    else
+        st_stream(static_cast<float4*>(base) + i, x);
+}
+
+template <int SDT>
+__device__ __forceinline__ float ld_moment1(const void* base, int64_t e)
+{
+    if constexpr (SDT == 1)
+        return bf16_to_f32(static_cast<const uint16_t*>(base)[e]);
+    else
+        return static_cast<const float*>(base)[e];
+}
+
+template <int SDT>
+__device__ __forceinline__ void st_moment1(void* base, int64_t e, float x)
+{
+    if constexpr (SDT == 1)
+        static_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(bf16_rne_bits(x));
+    else
+        static_cast<float*>(base)[e] = x;
 }
 
 /* Binary64 sum over a workgroup of NT lanes: shuffle tree inside each
@@ -386,7 +464,7 @@ __device__ __forceinline__ void adam_elem(float G, float& th, float& m, float& v
 #define HPO_ADAM_BOUNDS __launch_bounds__(kBlock)
 #endif
 
-template <bool FLAT, int PDT, int MODE, bool DEV>
+template <bool FLAT, int PDT, int MODE, bool DEV, int SDT>
 __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chunks)
 {
     StepVals k;
@@ -425,10 +503,11 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
     const Range r = chunk_range<FLAT>(sv, update_chunk(n_chunks));
     const float lr = sc.lr[r.d.group];
     const float wd = sc.wd[r.d.group];
+    constexpr int64_t kMomBytes = SDT == 1 ? 2 : 4;
     const float* __restrict__ G = r.d.grad + r.start;
     float* __restrict__ T = r.d.master + r.start;
-    float* __restrict__ M = r.d.exp_avg + r.start;
-    float* __restrict__ V = r.d.exp_avg_sq + r.start;
+    void* __restrict__ M = static_cast<char*>(r.d.exp_avg) + r.start * kMomBytes;
+    void* __restrict__ V = static_cast<char*>(r.d.exp_avg_sq) + r.start * kMomBytes;
     uint16_t* __restrict__ P = static_cast<uint16_t*>(r.d.param) + r.start;
     const int tid = threadIdx.x;
     int64_t done = 0;
@@ -436,8 +515,6 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
         const int64_t nv = r.len / kVec;
         const float4* __restrict__ G4 = reinterpret_cast<const float4*>(G);
         float4* __restrict__ T4 = reinterpret_cast<float4*>(T);
-        float4* __restrict__ M4 = reinterpret_cast<float4*>(M);
-        float4* __restrict__ V4 = reinterpret_cast<float4*>(V);
         uint2* __restrict__ P4 = reinterpret_cast<uint2*>(P);
         constexpr int U = HPO_ADAM_UNROLL;
         for (int64_t base = tid; base < nv; base += kBlock * U) {
@@ -448,8 +525,8 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
                 if (i < nv) {
                     g[u] = ld_stream(G4 + i);
                     th[u] = ld_stream(T4 + i);
-                    m[u] = ld_stream(M4 + i);
-                    v[u] = ld_stream(V4 + i);
+                    m[u] = ld_moment4<SDT>(M, i);
+                    v[u] = ld_moment4<SDT>(V, i);
                 }
             }
 #pragma unroll
@@ -461,30 +538,30 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
                     adam_elem<MODE>(g[u].z, th[u].z, m[u].z, v[u].z, sc, k, lr, wd);
                     adam_elem<MODE>(g[u].w, th[u].w, m[u].w, v[u].w, sc, k, lr, wd);
                     st_stream(T4 + i, th[u]);
-                    st_stream(M4 + i, m[u]);
-                    st_stream(V4 + i, v[u]);
-                    if constexpr (PDT == HPO_PARAM_BF16)
-                        st_stream(P4 + i, make_uint2(pack_bf16x2(th[u].x, th[u].y), pack_bf16x2(th[u].z, th[u].w)));
+                    st_moment4<SDT>(M, i, m[u]);
+                    st_moment4<SDT>(V, i, v[u]);
+                    if constexpr (PDT != HPO_PARAM_FP32)
+                        st_stream(P4 + i, pack_param4<PDT>(th[u]));
                 }
             }
         }
         done = nv * kVec;
     }
     for (int64_t i = done + tid; i < r.len; i += kBlock) {
-        float th = T[i], m = M[i], v = V[i];
+        float th = T[i], m = ld_moment1<SDT>(M, i), v = ld_moment1<SDT>(V, i);
         adam_elem<MODE>(G[i], th, m, v, sc, k, lr, wd);
         T[i] = th;
-        M[i] = m;
-        V[i] = v;
-        if constexpr (PDT == HPO_PARAM_BF16)
-            P[i] = static_cast<uint16_t>(bf16_rne_bits(th));
+        st_moment1<SDT>(M, i, m);
+        st_moment1<SDT>(V, i, v);
+        if constexpr (PDT != HPO_PARAM_FP32)
+            P[i] = static_cast<uint16_t>(param_bits<PDT>(th));
     }
 }
 
 /* ---------------------------------------------------------------------- */
 /* master -> model copy                                                   */
 /* ---------------------------------------------------------------------- */
-template <bool FLAT>
+template <bool FLAT, int PDT>
 __global__ __launch_bounds__(kBlock) void k_copy_main_to_model(SetView sv)
 {
     const Range r = chunk_range<FLAT>(sv, blockIdx.x);
@@ -496,14 +573,12 @@ __global__ __launch_bounds__(kBlock) void k_copy_main_to_model(SetView sv)
         const int64_t nv = r.len / kVec;
         const float4* __restrict__ T4 = reinterpret_cast<const float4*>(T);
         uint2* __restrict__ P4 = reinterpret_cast<uint2*>(P);
-        for (int64_t i = tid; i < nv; i += kBlock) {
-            const float4 th = T4[i];
-            P4[i] = make_uint2(pack_bf16x2(th.x, th.y), pack_bf16x2(th.z, th.w));
-        }
+        for (int64_t i = tid; i < nv; i += kBlock)
+            P4[i] = pack_param4<PDT>(T4[i]);
         done = nv * kVec;
     }
     for (int64_t i = done + tid; i < r.len; i += kBlock)
-        P[i] = static_cast<uint16_t>(bf16_rne_bits(T[i]));
+        P[i] = static_cast<uint16_t>(param_bits<PDT>(T[i]));
 }
 
 /* ---------------------------------------------------------------------- */
@@ -610,23 +685,35 @@ hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int
     return launch(k_finalize, 1, kFinalBlock, stream, ps, part_flag, n_parts, d_norm, d_found);
 }
 
+template <bool DEV, int SDT, int PDT>
+hipError_t launch_adam_p(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+                         hipStream_t stream)
+{
+    const bool flat = sv.is_flat != 0;
+    if (mode == HPO_ADAMW)
+        return flat ? launch(k_adam<true, PDT, HPO_ADAMW, DEV, SDT>, n_chunks, kBlock, stream, sv, sc, n_chunks)
+                    : launch(k_adam<false, PDT, HPO_ADAMW, DEV, SDT>, n_chunks, kBlock, stream, sv, sc, n_chunks);
+    return flat ? launch(k_adam<true, PDT, HPO_ADAM_L2, DEV, SDT>, n_chunks, kBlock, stream, sv, sc, n_chunks)
+                : launch(k_adam<false, PDT, HPO_ADAM_L2, DEV, SDT>, n_chunks, kBlock, stream, sv, sc, n_chunks);
+}
+
+template <bool DEV, int SDT>
+hipError_t launch_adam_s(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+                         hipStream_t stream)
+{
+    switch (sv.param_dtype) {
+    case HPO_PARAM_BF16: return launch_adam_p<DEV, SDT, HPO_PARAM_BF16>(sv, n_chunks, mode, sc, stream);
+    case HPO_PARAM_FP16: return launch_adam_p<DEV, SDT, HPO_PARAM_FP16>(sv, n_chunks, mode, sc, stream);
+    default: return launch_adam_p<DEV, SDT, HPO_PARAM_FP32>(sv, n_chunks, mode, sc, stream);
+    }
+}
+
 template <bool DEV>
 hipError_t launch_adam_t(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                          hipStream_t stream)
 {
-    const bool flat = sv.is_flat != 0;
-    const bool bf16 = sv.param_dtype == HPO_PARAM_BF16;
-    const bool adamw = mode == HPO_ADAMW;
-#define HPO_ADAM_LAUNCH(F, P, M) launch(k_adam<F, P, M, DEV>, n_chunks, kBlock, stream, sv, sc, n_chunks)
-    if (flat) {
-        if (bf16)
-            return adamw ? HPO_ADAM_LAUNCH(true, HPO_PARAM_BF16, HPO_ADAMW) : HPO_ADAM_LAUNCH(true, HPO_PARAM_BF16, HPO_ADAM_L2);
-        return adamw ? HPO_ADAM_LAUNCH(true, HPO_PARAM_FP32, HPO_ADAMW) : HPO_ADAM_LAUNCH(true, HPO_PARAM_FP32, HPO_ADAM_L2);
-    }
-    if (bf16)
-        return adamw ? HPO_ADAM_LAUNCH(false, HPO_PARAM_BF16, HPO_ADAMW) : HPO_ADAM_LAUNCH(false, HPO_PARAM_BF16, HPO_ADAM_L2);
-    return adamw ? HPO_ADAM_LAUNCH(false, HPO_PARAM_FP32, HPO_ADAMW) : HPO_ADAM_LAUNCH(false, HPO_PARAM_FP32, HPO_ADAM_L2);
-#undef HPO_ADAM_LAUNCH
+    return sv.state_bf16 ? launch_adam_s<DEV, 1>(sv, n_chunks, mode, sc, stream)
+                         : launch_adam_s<DEV, 0>(sv, n_chunks, mode, sc, stream);
 }
 
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
@@ -670,10 +757,13 @@ hipError_t launch_step_end(hpo_scaler_state* st, ScalerRule rule, int64_t t_firs
 
 hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream)
 {
-    if (n_chunks == 0)
+    if (n_chunks == 0 || sv.param_dtype == HPO_PARAM_FP32)
         return hipSuccess;
-    return sv.is_flat ? launch(k_copy_main_to_model<true>, n_chunks, kBlock, stream, sv)
-                      : launch(k_copy_main_to_model<false>, n_chunks, kBlock, stream, sv);
+    if (sv.param_dtype == HPO_PARAM_FP16)
+        return sv.is_flat ? launch(k_copy_main_to_model<true, HPO_PARAM_FP16>, n_chunks, kBlock, stream, sv)
+                          : launch(k_copy_main_to_model<false, HPO_PARAM_FP16>, n_chunks, kBlock, stream, sv);
+    return sv.is_flat ? launch(k_copy_main_to_model<true, HPO_PARAM_BF16>, n_chunks, kBlock, stream, sv)
+                      : launch(k_copy_main_to_model<false, HPO_PARAM_BF16>, n_chunks, kBlock, stream, sv);
 }
 
 }  // namespace hpo

@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhpo.so")
 
 HPO_OK, HPO_EINVAL, HPO_EDTYPE, HPO_ENOMEM, HPO_EHIP, HPO_EDEVICE = 0, -1, -2, -3, -4, -5
-HPO_PARAM_BF16, HPO_PARAM_FP32 = 0, 1
+HPO_PARAM_BF16, HPO_PARAM_FP32, HPO_PARAM_FP16 = 0, 1, 2
+HPO_STATE_BF16 = 0x100
 HPO_ADAMW, HPO_ADAM_L2 = 0, 1
 HPO_MAX_GROUPS = 16
 
@@ -147,13 +148,26 @@ def _require(t: torch.Tensor, dtype, what: str, i: int) -> None:
 
 
 def param_dtype_code(dtype) -> int:
-    """bf16 -> HPO_PARAM_BF16, fp32 -> HPO_PARAM_FP32; other dtypes (fp16
-    included) go to the library as an unsupported code, which it rejects."""
+    """bf16 / fp32 / fp16 -> the library's code; any other dtype goes to the
+    library as an unsupported code, which it rejects."""
     if dtype == torch.bfloat16:
         return HPO_PARAM_BF16
     if dtype == torch.float32:
         return HPO_PARAM_FP32
-    return 100 + {torch.float16: 0, torch.float64: 1}.get(dtype, 9)
+    if dtype == torch.float16:
+        return HPO_PARAM_FP16
+    return 100 + {torch.float64: 1}.get(dtype, 9)
+
+
+def _moments_flag(exp_avgs, exp_avg_sqs) -> int:
+    """HPO_STATE_BF16 when the moments are bf16 tensors, 0 for fp32; both
+    moments of every tensor must share one of these dtypes."""
+    dts = {t.dtype for t in list(exp_avgs) + list(exp_avg_sqs)}
+    if not dts or dts == {torch.float32}:
+        return 0
+    if dts == {torch.bfloat16}:
+        return HPO_STATE_BF16
+    raise TypeError(f"exp_avg / exp_avg_sq must all be float32 or all bfloat16, got {sorted(map(str, dts))}")
 
 
 # --------------------------------------------------------------------------
@@ -196,11 +210,13 @@ def hpo_set_create_list(params: Sequence[Optional[torch.Tensor]], main_params: S
     if param_dtype is None:
         first = next((p for p in params if p is not None), None)
         param_dtype = HPO_PARAM_FP32 if first is None else param_dtype_code(first.dtype)
+    mflag = _moments_flag(exp_avgs, exp_avg_sqs)
+    mdt = torch.bfloat16 if mflag else torch.float32
     numel = []
     for i in range(n):
-        for what, lst in (("main_params", main_params), ("main_grads", main_grads),
-                          ("exp_avgs", exp_avgs), ("exp_avg_sqs", exp_avg_sqs)):
-            _require(lst[i], torch.float32, what, i)
+        for what, lst, dt in (("main_params", main_params, torch.float32), ("main_grads", main_grads, torch.float32),
+                              ("exp_avgs", exp_avgs, mdt), ("exp_avg_sqs", exp_avg_sqs, mdt)):
+            _require(lst[i], dt, what, i)
             if lst[i].numel() != main_params[i].numel():
                 raise ValueError(f"{what}[{i}] has {lst[i].numel()} elements, main_params[{i}] has "
                                  f"{main_params[i].numel()}")
@@ -216,7 +232,7 @@ def hpo_set_create_list(params: Sequence[Optional[torch.Tensor]], main_params: S
             raise ValueError("group_index has the wrong length")
         c_groups = (ctypes.c_int32 * max(n, 1))(*group_index)
     out = ctypes.c_void_p()
-    st = load().hpo_set_create_list(ctypes.byref(out), n, param_dtype, arr(params), arr(main_params),
+    st = load().hpo_set_create_list(ctypes.byref(out), n, param_dtype | mflag, arr(params), arr(main_params),
                                     arr(main_grads), arr(exp_avgs), arr(exp_avg_sqs), c_numel, c_groups,
                                     _stream(stream))
     _check(st, "hpo_set_create_list")
@@ -226,9 +242,11 @@ def hpo_set_create_list(params: Sequence[Optional[torch.Tensor]], main_params: S
 def hpo_set_create_flat(param: Optional[torch.Tensor], main_param: torch.Tensor, main_grad: torch.Tensor,
                         exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, param_dtype: Optional[int] = None,
                         stream=None) -> HpoSet:
-    for what, t in (("main_param", main_param), ("main_grad", main_grad), ("exp_avg", exp_avg),
-                    ("exp_avg_sq", exp_avg_sq)):
-        _require(t, torch.float32, what, 0)
+    mflag = _moments_flag([exp_avg], [exp_avg_sq])
+    mdt = torch.bfloat16 if mflag else torch.float32
+    for what, t, dt in (("main_param", main_param, torch.float32), ("main_grad", main_grad, torch.float32),
+                        ("exp_avg", exp_avg, mdt), ("exp_avg_sq", exp_avg_sq, mdt)):
+        _require(t, dt, what, 0)
         if t.numel() != main_param.numel():
             raise ValueError(f"{what} has the wrong number of elements")
     if param_dtype is None:
@@ -236,7 +254,7 @@ def hpo_set_create_flat(param: Optional[torch.Tensor], main_param: torch.Tensor,
     if param is not None and (not param.is_contiguous() or param.numel() != main_param.numel()):
         raise ValueError("param must be contiguous with main_param's size")
     out = ctypes.c_void_p()
-    st = load().hpo_set_create_flat(ctypes.byref(out), main_param.numel(), param_dtype, _ptr(param),
+    st = load().hpo_set_create_flat(ctypes.byref(out), main_param.numel(), param_dtype | mflag, _ptr(param),
                                     _ptr(main_param), _ptr(main_grad), _ptr(exp_avg), _ptr(exp_avg_sq),
                                     _stream(stream))
     _check(st, "hpo_set_create_flat")
@@ -246,9 +264,11 @@ def hpo_set_create_flat(param: Optional[torch.Tensor], main_param: torch.Tensor,
 def hpo_set_create_flat_ranges(param: Optional[torch.Tensor], main_param: torch.Tensor, main_grad: torch.Tensor,
                                exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, range_start: Sequence[int],
                                range_group: Sequence[int], param_dtype: Optional[int] = None, stream=None) -> HpoSet:
-    for what, t in (("main_param", main_param), ("main_grad", main_grad), ("exp_avg", exp_avg),
-                    ("exp_avg_sq", exp_avg_sq)):
-        _require(t, torch.float32, what, 0)
+    mflag = _moments_flag([exp_avg], [exp_avg_sq])
+    mdt = torch.bfloat16 if mflag else torch.float32
+    for what, t, dt in (("main_param", main_param, torch.float32), ("main_grad", main_grad, torch.float32),
+                        ("exp_avg", exp_avg, mdt), ("exp_avg_sq", exp_avg_sq, mdt)):
+        _require(t, dt, what, 0)
         if t.numel() != main_param.numel():
             raise ValueError(f"{what} has the wrong number of elements")
     if param_dtype is None:
@@ -261,7 +281,7 @@ def hpo_set_create_flat_ranges(param: Optional[torch.Tensor], main_param: torch.
     c_start = (ctypes.c_int64 * max(k, 1))(*range_start)
     c_group = (ctypes.c_int32 * max(k, 1))(*range_group)
     out = ctypes.c_void_p()
-    st = load().hpo_set_create_flat_ranges(ctypes.byref(out), main_param.numel(), param_dtype, _ptr(param),
+    st = load().hpo_set_create_flat_ranges(ctypes.byref(out), main_param.numel(), param_dtype | mflag, _ptr(param),
                                            _ptr(main_param), _ptr(main_grad), _ptr(exp_avg), _ptr(exp_avg_sq),
                                            k, c_start, c_group, _stream(stream))
     _check(st, "hpo_set_create_flat_ranges")

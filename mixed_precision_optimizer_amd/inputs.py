@@ -35,7 +35,8 @@ class Workload:
     name: str
     numels: List[int]
     ndims: List[int]
-    param_dtype: str = "bf16"          # "bf16" or "fp32" (fp32 params are their own master)
+    param_dtype: str = "bf16"          # "bf16", "fp16" or "fp32" (fp32 params are their own master)
+    state_dtype: str = "fp32"          # exp_avg / exp_avg_sq storage: "fp32" or "bf16"
     lr: float = 1e-3
     weight_decay: float = 0.1
     beta1: float = 0.9
@@ -121,10 +122,12 @@ def ragged(n: int = 20000, max_elems: int = 4 * 2 ** 20, steps: int = 8, inf_ste
                     loss_scale=65536.0, steps=steps, grad_std=[1e-3] * n, inf_step=inf_step)
 
 
-def zero_shard(numel: int = 8_750_000_000) -> Workload:
+def zero_shard(numel: int = 8_750_000_000, state_dtype: str = "fp32", param_dtype: str = "bf16") -> Workload:
     # a flat shard mixes every kind of param; it is stepped as one decaying group
-    return Workload("zero1_shard_70b_over_8", [numel], [1], lr=1e-3, weight_decay=0.1, max_norm=1.0,
-                    steps=3, grad_std=[1e-4], flat=True, no_decay_1d=False)
+    tag = "" if (state_dtype, param_dtype) == ("fp32", "bf16") else f"_{param_dtype}_params_{state_dtype}_moments"
+    return Workload(f"zero1_shard_70b_over_8{tag}", [numel], [1], lr=1e-3, weight_decay=0.1, max_norm=1.0,
+                    steps=3, grad_std=[1e-4], flat=True, no_decay_1d=False, state_dtype=state_dtype,
+                    param_dtype=param_dtype)
 
 
 def llama70b_shapes():
@@ -212,7 +215,7 @@ class Buffers:
     grad: torch.Tensor
     exp_avg: torch.Tensor
     exp_avg_sq: torch.Tensor
-    param: torch.Tensor        # bf16 buffer, or the master itself for fp32 params
+    param: torch.Tensor        # 16-bit buffer, or the master itself for fp32 params
 
     def view(self, buf: torch.Tensor, i: int) -> torch.Tensor:
         o = self.offs[i]
@@ -249,12 +252,14 @@ def allocate(w: Workload, device) -> Buffers:
     else:
         fill_normal_(master, w.master_seed)
     grad = torch.zeros(total, **f32)
-    exp_avg = torch.zeros(total, **f32)
-    exp_avg_sq = torch.zeros(total, **f32)
+    sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
+    exp_avg = torch.zeros(total, dtype=sdt, device=device)
+    exp_avg_sq = torch.zeros(total, dtype=sdt, device=device)
     if w.param_dtype == "fp32":
         param = master
     else:
-        param = torch.empty(total, dtype=torch.bfloat16, device=device)
+        pdt = torch.float16 if w.param_dtype == "fp16" else torch.bfloat16
+        param = torch.empty(total, dtype=pdt, device=device)
         for a in range(0, total, FILL_CHUNK):
             b = min(total, a + FILL_CHUNK)
             param[a:b].copy_(master[a:b])

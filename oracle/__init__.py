@@ -69,6 +69,8 @@ class _UpdateArgs(ctypes.Structure):
         ("inv_scale", ctypes.c_float),
         ("clip_C", ctypes.c_float),
         ("clip_c64", ctypes.c_double),
+        ("state_bf16", ctypes.c_int32),
+        ("param_fp16", ctypes.c_int32),
     ]
 
 
@@ -89,6 +91,10 @@ def lib():
         L.orc_bf16_rne.restype = ctypes.c_uint16
         L.orc_bf16_rne_array.argtypes = [P, P, I64]
         L.orc_bf16_rne_patterns.argtypes = [ctypes.c_uint32, I64, P]
+        L.orc_fp16_rne.argtypes = [ctypes.c_float]
+        L.orc_fp16_rne.restype = ctypes.c_uint16
+        L.orc_fp16_rne_patterns.argtypes = [ctypes.c_uint32, I64, P]
+        L.orc_fp16_rne_array.argtypes = [P, P, I64]
         L.orc_any_nonfinite.argtypes = [P, I64]
         L.orc_any_nonfinite.restype = ctypes.c_int32
         L.orc_unscale_inplace.argtypes = [P, I64, ctypes.c_float]
@@ -132,6 +138,20 @@ def bf16_rne(x: np.ndarray) -> np.ndarray:
 def bf16_rne_patterns(first: int, count: int) -> np.ndarray:
     out = np.empty(count, dtype=np.uint16)
     lib().orc_bf16_rne_patterns(ctypes.c_uint32(first), count, _ptr(out))
+    return out
+
+
+def fp16_rne_patterns(first: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.uint16)
+    lib().orc_fp16_rne_patterns(ctypes.c_uint32(first), count, _ptr(out))
+    return out
+
+
+def fp16_rne(x: np.ndarray) -> np.ndarray:
+    """fp32 -> fp16 bit patterns (uint16), IEEE RNE (oracle definition)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_fp16_rne_array(_ptr(x), _ptr(out), x.size)
     return out
 
 
@@ -182,20 +202,30 @@ class Hyper:
 class OTensor:
     """One parameter's optimizer-side state, all host numpy arrays."""
     theta: np.ndarray                 # fp32 master (is the param for fp32 params)
-    m: np.ndarray                     # fp32 exp_avg
-    v: np.ndarray                     # fp32 exp_avg_sq
-    p: Optional[np.ndarray] = None    # uint16 bf16 bits of the model param, or None (fp32 param)
+    m: np.ndarray                     # exp_avg: fp32, or uint16 bf16 bits (bf16 state)
+    v: np.ndarray                     # exp_avg_sq: same dtype as m
+    p: Optional[np.ndarray] = None    # uint16 bits of the 16-bit model param, or None (fp32 param)
     group: int = 0
+    param_fp16: bool = False          # p holds fp16 bits instead of bf16
+
+    @property
+    def state_bf16(self) -> bool:
+        return self.m.dtype == np.uint16
 
     @staticmethod
-    def fresh(theta: np.ndarray, bf16_param: bool = True, group: int = 0) -> "OTensor":
+    def fresh(theta: np.ndarray, bf16_param: bool = True, group: int = 0, fp16_param: bool = False,
+              state_bf16: bool = False) -> "OTensor":
         theta = np.ascontiguousarray(theta, dtype=np.float32).copy()
-        p = bf16_rne(theta) if bf16_param else None
-        return OTensor(theta, np.zeros_like(theta), np.zeros_like(theta), p, group)
+        if fp16_param:
+            p = fp16_rne(theta)
+        else:
+            p = bf16_rne(theta) if bf16_param else None
+        sdt = np.uint16 if state_bf16 else np.float32
+        return OTensor(theta, np.zeros(theta.shape, sdt), np.zeros(theta.shape, sdt), p, group, fp16_param)
 
     def copy(self) -> "OTensor":
         return OTensor(self.theta.copy(), self.m.copy(), self.v.copy(),
-                       None if self.p is None else self.p.copy(), self.group)
+                       None if self.p is None else self.p.copy(), self.group, self.param_fp16)
 
 
 @dataclass
@@ -255,8 +285,15 @@ def apply_update(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper:
         lr, wd = groups[T.group]
         args = _UpdateArgs(lr=lr, wd=wd, beta1=hyper.beta1, beta2=hyper.beta2,
                            eps=hyper.eps, t=t, mode=hyper.mode, do_clip=int(do_clip),
-                           inv_scale=float(np.float32(inv_scale)), clip_C=C, clip_c64=c64)
-        fn(T.theta.size, _ptr(_f32(T.theta)), _ptr(_f32(T.m)), _ptr(_f32(T.v)),
+                           inv_scale=float(np.float32(inv_scale)), clip_C=C, clip_c64=c64,
+                           state_bf16=int(T.state_bf16), param_fp16=int(T.param_fp16))
+        if T.state_bf16:
+            assert variant == "f32", "bf16 moments are defined for the fp32-literal reading only"
+            assert T.m.flags["C_CONTIGUOUS"] and T.v.flags["C_CONTIGUOUS"]
+            mp, vp = _ptr(T.m), _ptr(T.v)
+        else:
+            mp, vp = _ptr(_f32(T.m)), _ptr(_f32(T.v))
+        fn(T.theta.size, _ptr(_f32(T.theta)), mp, vp,
            _ptr(_f32(np.ascontiguousarray(G))), _ptr(T.p), ctypes.byref(args))
 
 

@@ -86,6 +86,77 @@ void orc_bf16_rne_patterns(uint32_t first, int64_t count, uint16_t* out)
 }
 
 /* ------------------------------------------------------------------------ */
+/* fp32 -> fp16 write-back for fp16 model params ([OPT-INFRA] §9.2: the     */
+/* master is cast to the 16-bit model dtype, fp16 or bf16).  Reading: IEEE  */
+/* binary32 -> binary16 round to nearest, ties to even, with binary16       */
+/* subnormals, overflow to infinity, NaN -> quiet NaN 0x7E00 with the sign. */
+/* Written from the definition: the value is sig * 2^(e - 23) with a 24-bit */
+/* significand; the binary16 quantum is 2^(e - 10) for normal results and   */
+/* 2^-24 below 2^-14; the significand is divided by the quantum with the    */
+/* dropped bits deciding the rounding, and the encoding is built by adding  */
+/* the kept significand to the biased exponent field, so a carry moves into */
+/* the exponent (up to infinity).                                           */
+/* ------------------------------------------------------------------------ */
+uint16_t orc_fp16_rne(float x)
+{
+    uint32_t bits;
+    memcpy(&bits, &x, sizeof bits);
+    const uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u)
+        return (uint16_t)(sign | 0x7E00u);
+    if (mag == 0x7F800000u)
+        return (uint16_t)(sign | 0x7C00u);
+    const int biased = (int)(mag >> 23);
+    if (biased == 0) /* fp32 zero or subnormal: far below 2^-25, rounds to zero */
+        return sign;
+    const uint32_t sig = (mag & 0x7FFFFFu) | 0x800000u;
+    const int e = biased - 127;                /* value = sig * 2^(e - 23) */
+    const int q = e >= -14 ? e - 10 : -24;     /* log2 of the binary16 quantum */
+    const int shift = q - (e - 23);            /* significand bits dropped, >= 13 */
+    if (shift > 24)
+        return sign;                           /* below half the smallest subnormal */
+    uint32_t kept = sig >> shift;
+    const uint32_t rem = sig & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (kept & 1u)))
+        kept += 1u;
+    uint32_t enc;
+    if (q == -24)
+        enc = kept;                            /* subnormal; kept == 1024 is the smallest normal */
+    else
+        enc = ((uint32_t)(e + 15) << 10) + (kept - 1024u);
+    if (enc >= 0x7C00u)
+        enc = 0x7C00u;                         /* overflow */
+    return (uint16_t)(sign | enc);
+}
+
+void orc_fp16_rne_array(const float* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_fp16_rne(x[i]);
+}
+
+void orc_fp16_rne_patterns(uint32_t first, int64_t count, uint16_t* out)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        uint32_t b = first + (uint32_t)i;
+        float x;
+        memcpy(&x, &b, sizeof x);
+        out[i] = orc_fp16_rne(x);
+    }
+}
+
+/* bf16 bits -> fp32 value (exact: bf16 is the top half of binary32). */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float x;
+    memcpy(&x, &u, sizeof x);
+    return x;
+}
+
+/* ------------------------------------------------------------------------ */
 /* a1: non-finite check over the stored (still scaled) gradients.           */
 /* [OPT-INFRA] §9.2 table (unscale row) and §10.2: one pass sets found_inf  */
 /* when any main grad is inf or NaN; the values checked are the stored ones.*/
@@ -177,10 +248,17 @@ typedef struct {
     float inv_scale;   /* unscale multiplier (fp32, as the caller holds it) */
     float clip_C;      /* fp32 clip coefficient (O32) */
     double clip_c64;   /* binary64 clip coefficient (O64) */
+    int32_t state_bf16;  /* O32 only: exp_avg / exp_avg_sq held as bf16 (uint16 arrays) */
+    int32_t param_fp16;  /* the 16-bit model param is fp16 instead of bf16 */
 } orc_update_args;
 
-void orc_update_f32(int64_t n, float* theta, float* m, float* v, const float* G,
-                    uint16_t* p_bf16, const orc_update_args* a)
+/* m and v point at fp32 arrays, or at bf16 (uint16) arrays when
+ * a->state_bf16 is set ([OPT-INFRA] §16: the precision-aware optimizer may
+ * keep exp_avg / exp_avg_sq in a lower precision).  Reading for bf16 moments:
+ * they are widened exactly to fp32, the update runs in fp32 as above, and the
+ * new moments are stored with the bf16 write-back rounding. */
+void orc_update_f32(int64_t n, float* theta, void* m_ptr, void* v_ptr, const float* G,
+                    uint16_t* p16, const orc_update_args* a)
 {
     /* scalars: binary64 once, rounded to binary32 once */
     const float B1 = (float)a->beta1;
@@ -194,6 +272,10 @@ void orc_update_f32(int64_t n, float* theta, float* m, float* v, const float* G,
     const float WD = (float)a->wd;
     const float INV = a->inv_scale;
     const float C = a->clip_C;
+    float* m32 = (float*)m_ptr;
+    float* v32 = (float*)v_ptr;
+    uint16_t* m16 = (uint16_t*)m_ptr;
+    uint16_t* v16 = (uint16_t*)v_ptr;
 
     for (int64_t i = 0; i < n; ++i) {
         float g = G[i] * INV;
@@ -202,8 +284,10 @@ void orc_update_f32(int64_t n, float* theta, float* m, float* v, const float* G,
         float th = theta[i];
         if (a->mode == ORC_ADAM_L2)
             g = g + WD * th;
-        float mi = B1 * m[i] + C1 * g;
-        float vi = B2 * v[i] + C2 * (g * g);
+        const float m_old = a->state_bf16 ? bf16_to_f32(m16[i]) : m32[i];
+        const float v_old = a->state_bf16 ? bf16_to_f32(v16[i]) : v32[i];
+        float mi = B1 * m_old + C1 * g;
+        float vi = B2 * v_old + C2 * (g * g);
         float mh = mi / BC1;
         float vh = vi / BC2;
         float denom = sqrtf(vh) + EPS;
@@ -212,11 +296,16 @@ void orc_update_f32(int64_t n, float* theta, float* m, float* v, const float* G,
             th = th - LR * (u + WD * th);
         else
             th = th - LR * u;
-        m[i] = mi;
-        v[i] = vi;
+        if (a->state_bf16) {
+            m16[i] = orc_bf16_rne(mi);
+            v16[i] = orc_bf16_rne(vi);
+        } else {
+            m32[i] = mi;
+            v32[i] = vi;
+        }
         theta[i] = th;
-        if (p_bf16)
-            p_bf16[i] = orc_bf16_rne(th);
+        if (p16)
+            p16[i] = a->param_fp16 ? orc_fp16_rne(th) : orc_bf16_rne(th);
     }
 }
 
@@ -244,6 +333,6 @@ void orc_update_f64(int64_t n, float* theta, float* m, float* v, const float* G,
         v[i] = (float)vi;
         theta[i] = (float)th;
         if (p_bf16)
-            p_bf16[i] = orc_bf16_rne(theta[i]);
+            p_bf16[i] = a->param_fp16 ? orc_fp16_rne(theta[i]) : orc_bf16_rne(theta[i]);
     }
 }

@@ -29,8 +29,9 @@ def banner(msg: str) -> None:
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:
+    """Host copy; 16-bit float tensors come back as their uint16 bit patterns."""
     t = t.detach()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).cpu().numpy().view(np.uint16).copy()
     return t.cpu().numpy().copy()
 
@@ -40,10 +41,19 @@ def bf16_of(theta: np.ndarray) -> np.ndarray:
     return torch.from_numpy(theta).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def fp16_of(theta: np.ndarray) -> np.ndarray:
+    """torch's CPU fp32 -> fp16 cast (a library routine, not the oracle)."""
+    return torch.from_numpy(theta).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
 def make_set(bufs, stream=None):
     from mixed_precision_optimizer_amd import hpo
     w = bufs.workload
-    pdt = hpo.HPO_PARAM_FP32 if w.param_dtype == "fp32" else hpo.HPO_PARAM_BF16
+    pdt = {"fp32": hpo.HPO_PARAM_FP32, "bf16": hpo.HPO_PARAM_BF16, "fp16": hpo.HPO_PARAM_FP16}[w.param_dtype]
     if w.flat and w.n_tensors > 1:
         return hpo.hpo_set_create_flat_ranges(None if w.param_dtype == "fp32" else bufs.param, bufs.master, bufs.grad,
                                               bufs.exp_avg, bufs.exp_avg_sq, bufs.offs,
@@ -51,14 +61,12 @@ def make_set(bufs, stream=None):
                                               stream=stream)
     if w.flat:
         return hpo.hpo_set_create_flat(None if w.param_dtype == "fp32" else bufs.param, bufs.master, bufs.grad,
-                                       bufs.exp_avg, bufs.exp_avg_sq, stream=stream,
-                                       param_dtype=hpo.HPO_PARAM_FP32 if w.param_dtype == "fp32" else hpo.HPO_PARAM_BF16)
+                                       bufs.exp_avg, bufs.exp_avg_sq, stream=stream, param_dtype=pdt)
     ps, ms, gs, m1, m2 = bufs.lists()
     if w.param_dtype == "fp32":
         ps = None
     return hpo.hpo_set_create_list(ps, ms, gs, m1, m2, [w.group_of(i) for i in range(w.n_tensors)],
-                                   param_dtype=hpo.HPO_PARAM_FP32 if w.param_dtype == "fp32" else hpo.HPO_PARAM_BF16,
-                                   stream=stream)
+                                   param_dtype=pdt, stream=stream)
 
 
 def make_opt(hset, w, device=None):
@@ -67,26 +75,40 @@ def make_opt(hset, w, device=None):
                                max_norm=w.max_norm, loss_scale=w.loss_scale, device=device)
 
 
-def compare_tensor(tag, gpu, orc_new, orc_prev, G, *, inv, clip, C, c64, lr, wd, t, mode, bf16, stats):
-    """gpu: dict theta/m/v[/p] numpy; orc_new / orc_prev: oracle OTensor after / before the step."""
-    E_m, E_v, E_th = step_error_bounds(orc_prev.theta, orc_prev.m, orc_prev.v, G, inv=inv, C=c64, do_clip=clip,
+def compare_tensor(tag, gpu, orc_new, orc_prev, G, *, inv, clip, C, c64, lr, wd, t, mode, bf16, stats,
+                   fp16=False):
+    """gpu: dict theta/m/v[/p] numpy; orc_new / orc_prev: oracle OTensor after / before the step.
+    fp32 moments: the rel-1e-6 propagated bound; bf16 moments: within one bf16
+    ulp (the master's bound then uses the widened moments)."""
+    sbf16 = orc_new.m.dtype == np.uint16
+    m_prev = widen_bf16(orc_prev.m) if sbf16 else orc_prev.m
+    v_prev = widen_bf16(orc_prev.v) if sbf16 else orc_prev.v
+    E_m, E_v, E_th = step_error_bounds(orc_prev.theta, m_prev, v_prev, G, inv=inv, C=c64, do_clip=clip,
                                        lr=lr, wd=wd, t=t, mode=mode)
-    check_within(f"{tag} m", gpu["m"], orc_new.m, E_m)
-    check_within(f"{tag} v", gpu["v"], orc_new.v, E_v)
+    if sbf16:
+        for key in ("m", "v"):
+            d = np.abs(gpu[key].astype(np.int32) - getattr(orc_new, key).astype(np.int32))
+            assert np.all(d <= 1), f"{tag} {key}: bf16 moment more than 1 ulp from the oracle"
+        eq_mv = int(np.sum(gpu["m"] == orc_new.m)) + int(np.sum(gpu["v"] == orc_new.v))
+    else:
+        check_within(f"{tag} m", gpu["m"], orc_new.m, E_m)
+        check_within(f"{tag} v", gpu["v"], orc_new.v, E_v)
+        eq_mv = int(np.sum(gpu["m"].view(np.uint32) == orc_new.m.view(np.uint32)))
+        eq_mv += int(np.sum(gpu["v"].view(np.uint32) == orc_new.v.view(np.uint32)))
     check_within(f"{tag} theta", gpu["theta"], orc_new.theta, E_th)
     n = gpu["theta"].size
-    eq = int(np.sum(gpu["theta"].view(np.uint32) == orc_new.theta.view(np.uint32)))
-    eq += int(np.sum(gpu["m"].view(np.uint32) == orc_new.m.view(np.uint32)))
-    eq += int(np.sum(gpu["v"].view(np.uint32) == orc_new.v.view(np.uint32)))
+    eq = int(np.sum(gpu["theta"].view(np.uint32) == orc_new.theta.view(np.uint32))) + eq_mv
     stats["bit_equal"] = stats.get("bit_equal", 0) + eq
     stats["compared"] = stats.get("compared", 0) + 3 * n
-    if bf16:
+    if bf16 or fp16:
         p = gpu["p"]
         # the write-back of the GPU's own master is bit-exact (the pages' invariant)
-        assert np.array_equal(p, bf16_of(gpu["theta"])), f"{tag}: param != bf16(master)"
-        # and within one bf16 ulp of the oracle's param
+        want = fp16_of(gpu["theta"]) if fp16 else bf16_of(gpu["theta"])
+        isnan = np.isnan(gpu["theta"])
+        assert np.array_equal(p[~isnan], want[~isnan]), f"{tag}: param != 16-bit(master)"
+        # and within one ulp of the oracle's param
         d = np.abs(p.astype(np.int32) - orc_new.p.astype(np.int32))
-        assert np.all(d <= 1), f"{tag}: bf16 param more than 1 ulp from the oracle"
+        assert np.all(d <= 1), f"{tag}: 16-bit param more than 1 ulp from the oracle"
 
 
 def read_state(bufs, i=None, lo=0, hi=None):
@@ -98,7 +120,7 @@ def read_state(bufs, i=None, lo=0, hi=None):
     hi = n if hi is None else hi
     a, b = off + lo, off + hi
     out = {"theta": to_np(bufs.master[a:b]), "m": to_np(bufs.exp_avg[a:b]), "v": to_np(bufs.exp_avg_sq[a:b])}
-    if w.param_dtype == "bf16":
+    if w.param_dtype in ("bf16", "fp16"):
         out["p"] = to_np(bufs.param[a:b])
     return out
 

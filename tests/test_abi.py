@@ -77,9 +77,13 @@ def test_validation_happens_before_any_device_call(H):
     assert st == H.HPO_EINVAL and "non-NULL" in msg
     st, msg = _flat(H, -1, 0, [0] * 5)
     assert st == H.HPO_EINVAL and "negative" in msg
-    # unsupported dtype (fp16 and anything else): an error, never a silent cast
-    st, msg = _flat(H, 16, 2, [0x1000] * 5)
-    assert st == H.HPO_EDTYPE and "not supported" in msg
+    # unsupported dtypes: an error, never a silent cast
+    for code in (3, 0x200, 0x101 | 0x1000, -1):
+        st, msg = _flat(H, 16, code, [0x1000] * 5)
+        assert st == H.HPO_EDTYPE and "not supported" in msg, code
+    # bf16 moments need only 2-byte alignment; fp32 moments 4-byte
+    st, msg = _flat(H, 16, 0, [0x1000, 0x2000, 0x3000, 0x4002, 0x5000])
+    assert st == H.HPO_EINVAL and "exp_avg" in msg
     # fp32 sets: the param is its own master
     st, msg = _flat(H, 16, 1, [0x9000, 0x1000, 0x2000, 0x3000, 0x4000])
     assert st == H.HPO_EINVAL and "own master" in msg

@@ -41,14 +41,15 @@ def _true_grads(k, rng_seed=500):
     return gs
 
 
-@pytest.mark.parametrize("mode", [0, 1])
-def test_device_step_sequence_matches_oracle(H, orc, mode):
-    banner(f"device-resident step sequence, mode {mode}")
+@pytest.mark.parametrize("mode,pdt", [(0, "bf16"), (1, "bf16"), (0, "fp16")])
+def test_device_step_sequence_matches_oracle(H, orc, mode, pdt):
+    banner(f"device-resident step sequence, mode {mode}, {pdt} params")
     from mixed_precision_optimizer_amd import DeviceAdamW
     rng = np.random.default_rng(400)
     th0 = [rng.standard_normal(n).astype(np.float32) for n in SIZES]
     ths = [torch.from_numpy(a.copy()).to(DEV) for a in th0]
-    ps = [t.to(torch.bfloat16) for t in ths]
+    tdt = torch.float16 if pdt == "fp16" else torch.bfloat16
+    ps = [t.to(tdt) for t in ths]
     gs = [torch.zeros(n, device=DEV) for n in SIZES]
     ms = [torch.zeros(n, device=DEV) for n in SIZES]
     vs = [torch.zeros(n, device=DEV) for n in SIZES]
@@ -57,8 +58,8 @@ def test_device_step_sequence_matches_oracle(H, orc, mode):
     kw = dict(loss_scale=2.0 ** 16, dynamic=True, growth_interval=5, hysteresis=2, min_scale=1.0,
               grad_norm_skip_threshold=50.0)
     opt = DeviceAdamW(hset, groups, mode=mode, max_norm=1.0, **kw)
-    T = [orc.OTensor(a.copy(), np.zeros_like(a), np.zeros_like(a), p.view(torch.int16).cpu().numpy().view(np.uint16).copy(), g)
-         for a, p, g in zip(th0, ps, GROUPS)]
+    T = [orc.OTensor(a.copy(), np.zeros_like(a), np.zeros_like(a), p.view(torch.int16).cpu().numpy().view(np.uint16).copy(), g,
+                     pdt == "fp16") for a, p, g in zip(th0, ps, GROUPS)]
     O = orc.OracleOptimizer(T, orc.Hyper(mode=mode), groups, max_norm=1.0)
     sc = orc.LossScaler(scale=2.0 ** 16, dynamic=True, growth_interval=5, hysteresis=2, min_scale=1.0)
     applied = skipped = 0

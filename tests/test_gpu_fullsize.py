@@ -91,7 +91,7 @@ class Sample:
     def state(self):
         b = self.bufs
         out = {"theta": self.gather(b.master), "m": self.gather(b.exp_avg), "v": self.gather(b.exp_avg_sq)}
-        if b.workload.param_dtype == "bf16":
+        if b.workload.param_dtype in ("bf16", "fp16"):
             out["p"] = self.gather(b.param)
         return out
 
@@ -113,13 +113,15 @@ def _run_fullsize(H, orc, w, picks_kw, steps=None):
     # the oracle's sampled state: one array per field, one view per segment
     big = S.state()
     bf16 = w.param_dtype == "bf16"
+    fp16 = w.param_dtype == "fp16"
+    has_p = bf16 or fp16
     Ts = []
     lr_e = np.empty(S.n)
     wd_e = np.empty(S.n)
     for i, pos, n in S.seg:
         sl = slice(pos, pos + n)
         g = w.group_of(i)
-        Ts.append(orc.OTensor(big["theta"][sl], big["m"][sl], big["v"][sl], big["p"][sl] if bf16 else None, g))
+        Ts.append(orc.OTensor(big["theta"][sl], big["m"][sl], big["v"][sl], big["p"][sl] if has_p else None, g, fp16))
         lr_e[sl], wd_e[sl] = w.groups()[g]
     hset = make_set(bufs)
     opt = make_opt(hset, w)
@@ -142,8 +144,8 @@ def _run_fullsize(H, orc, w, picks_kw, steps=None):
         st = S.state()
         if found:
             for key in ("theta", "m", "v"):
-                assert np.array_equal(st[key].view(np.uint32), big[key].view(np.uint32))
-            if bf16:
+                assert np.array_equal(st[key].view(np.uint8), big[key].view(np.uint8))
+            if has_p:
                 assert np.array_equal(st["p"], big["p"])
             stats.setdefault("skipped", []).append(k)
             continue
@@ -152,13 +154,13 @@ def _run_fullsize(H, orc, w, picks_kw, steps=None):
         assert abs(norm - norm64) <= 1e-5 * norm64
         do_clip, C, c64 = orc.clip_coeff(w.max_norm, norm32)
         prev = orc.OTensor(big["theta"].copy(), big["m"].copy(), big["v"].copy(),
-                           big["p"].copy() if bf16 else None)
+                           big["p"].copy() if has_p else None, 0, fp16)
         orc.apply_update(Ts, [Gs[pos:pos + n] for _, pos, n in S.seg], hyper, w.groups(), t_orc, inv,
                          do_clip, C, c64)
         assert opt.t == t_orc
-        now = orc.OTensor(big["theta"], big["m"], big["v"], big["p"] if bf16 else None)
+        now = orc.OTensor(big["theta"], big["m"], big["v"], big["p"] if has_p else None, 0, fp16)
         compare_tensor(f"{w.name} step {k}", st, now, prev, Gs, inv=inv, clip=do_clip, C=C, c64=c64,
-                       lr=lr_e, wd=wd_e, t=t_orc, mode=w.mode, bf16=bf16, stats=stats)
+                       lr=lr_e, wd=wd_e, t=t_orc, mode=w.mode, bf16=bf16, fp16=fp16, stats=stats)
     banner(f"bit-equal {stats.get('bit_equal', 0)}/{stats.get('compared', 0)}; skipped {stats.get('skipped', [])}")
     hset.close()
     del bufs
@@ -204,4 +206,14 @@ def test_zero_shard_with_param_ranges_llama70b(H, orc):
     from mixed_precision_optimizer_amd import inputs
     w = inputs.zero_shard_ranges()
     stats = _run_fullsize(H, orc, w, dict(head=2048, windows_big=2, window=16384, whole_below=8192))
+    assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.timeout(900)
+def test_zero_shard_bf16_moments(H, orc):
+    """The 70B/8 flat shard with exp_avg / exp_avg_sq held in bf16 (22 bytes per
+    element per update instead of 30), 3 steps."""
+    from mixed_precision_optimizer_amd import inputs
+    w = inputs.zero_shard(state_dtype="bf16")
+    stats = _run_fullsize(H, orc, w, dict(head=4096, windows_big=64, window=65536))
     assert stats["bit_equal"] == stats["compared"]

@@ -37,7 +37,7 @@ def _oracle_tensors(orc, bufs):
     out = []
     for i in range(w.n_tensors):
         st = read_state(bufs, i)
-        T = orc.OTensor(st["theta"], st["m"], st["v"], st.get("p"), w.group_of(i))
+        T = orc.OTensor(st["theta"], st["m"], st["v"], st.get("p"), w.group_of(i), w.param_dtype == "fp16")
         out.append(T)
     return out
 
@@ -69,7 +69,7 @@ def _run_parity(H, orc, w, steps=None, stats=None, inplace=False):
             for i, T in enumerate(Ts):
                 st = read_state(bufs, i)
                 for key in ("theta", "m", "v"):
-                    assert np.array_equal(st[key].view(np.uint32), getattr(T, key).view(np.uint32))
+                    assert np.array_equal(st[key].view(np.uint8), getattr(T, key).view(np.uint8))
                 if T.p is not None:
                     assert np.array_equal(st["p"], T.p)
             stats.setdefault("skipped", []).append(k)
@@ -82,7 +82,7 @@ def _run_parity(H, orc, w, steps=None, stats=None, inplace=False):
             lr, wd = w.groups()[T.group]
             compare_tensor(f"{w.name} step {k} tensor {i}", st, T, prev[i], G[i], inv=w.inv_scale(),
                            clip=r.clip_applied, C=r.clip_C, c64=c64, lr=lr, wd=wd, t=O.t, mode=w.mode,
-                           bf16=w.param_dtype == "bf16", stats=stats)
+                           bf16=w.param_dtype == "bf16", fp16=w.param_dtype == "fp16", stats=stats)
     hset.close()
     return stats, Ts, bufs
 
@@ -114,13 +114,14 @@ def test_two_matrices_ten_steps(H, orc):
     assert stats["bit_equal"] >= 0.999999 * stats["compared"]
 
 
-def _edge_workload(mode, loss_scale, inf_step=None, max_norm=1.0, steps=4):
+def _edge_workload(mode, loss_scale, inf_step=None, max_norm=1.0, steps=4, param_dtype="bf16",
+                   state_dtype="fp32"):
     from mixed_precision_optimizer_amd.inputs import Workload
     sizes = [1, 3, 4, 5, 63, 64, 65, 255, 1023, 4095, 4096, 4097, 0, 12345, 70001, 131072, 300000, 2]
     ndims = [1 if n in (4095, 5, 63) else 2 for n in sizes]
     return Workload(f"edge_mode{mode}", sizes, ndims, lr=1e-3, weight_decay=0.1, mode=mode, max_norm=max_norm,
                     loss_scale=loss_scale, steps=steps, grad_std=[1e-3 * (1 + (i % 5)) for i in range(len(sizes))],
-                    inf_step=inf_step)
+                    inf_step=inf_step, param_dtype=param_dtype, state_dtype=state_dtype)
 
 
 @pytest.mark.parametrize("mode", [0, 1])
@@ -134,6 +135,44 @@ def test_ragged_tails_groups_scale_and_skip(H, orc, mode, inplace):
     stats, Ts, bufs = _run_parity(H, orc, w, inplace=inplace)
     assert stats["skipped"] == [2]
     assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("pdt,sdt", [("fp16", "fp32"), ("bf16", "bf16"), ("fp16", "bf16"), ("fp32", "bf16")])
+def test_reduced_precision_variants(H, orc, mode, pdt, sdt):
+    """fp16 model params (fp16 RNE write-back) and bf16 moments, on the ragged
+    edge sets with loss scale 1024, clipping, a no-decay group and a skipped
+    step, against the oracle's own trajectory."""
+    banner(f"reduced precision: params {pdt}, moments {sdt}, mode {mode}")
+    w = _edge_workload(mode, 1024.0, inf_step=3, steps=6, param_dtype=pdt, state_dtype=sdt)
+    stats, Ts, bufs = _run_parity(H, orc, w)
+    assert stats["skipped"] == [3]
+    assert stats["bit_equal"] == stats["compared"]
+
+
+def test_fp16_writeback_exhaustive(H, orc):
+    """hpo_copy_main_to_model on an fp16 set over all 2^32 fp32 patterns against
+    the oracle's fp16 RNE: bit-equal for every non-NaN input, NaN stays NaN."""
+    banner("exhaustive fp16 write-back")
+    step = 1 << 30
+    master = torch.empty(step, dtype=torch.float32, device=DEV)
+    extra = [torch.zeros(step, dtype=torch.float32, device=DEV) for _ in range(3)]
+    param = torch.empty(step, dtype=torch.float16, device=DEV)
+    hset = H.hpo_set_create_flat(param, master, *extra)
+    base = torch.arange(step, dtype=torch.int64, device=DEV)
+    for first in range(0, 1 << 32, step):
+        bits = base + first
+        master.view(torch.int32).copy_(torch.where(bits >= 2 ** 31, bits - 2 ** 32, bits).to(torch.int32))
+        H.hpo_copy_main_to_model(hset)
+        torch.cuda.synchronize()
+        got = to_np(param)
+        want = orc.fp16_rne_patterns(first, step)
+        u = np.arange(step, dtype=np.uint32) + np.uint32(first)
+        nan = (u & 0x7FFFFFFF) > 0x7F800000
+        assert np.array_equal(got[~nan], want[~nan]), hex(first)
+        assert np.all((got[nan] & 0x7FFF) > 0x7C00)
+        print(f"  patterns {first:#x}.. ok", flush=True)
+    hset.close()
 
 
 @pytest.mark.parametrize("bad", [float("inf"), float("-inf"), float("nan")])
@@ -410,12 +449,14 @@ def test_fp32_param_set_has_no_writeback(H, orc):
     hset.close()
 
 
-def test_fp16_params_are_rejected(H):
+def test_unsupported_param_dtype_is_rejected(H):
     n = 64
     th = torch.zeros(n, device=DEV)
     with pytest.raises(H.HpoError) as e:
-        H.hpo_set_create_flat(th.half(), th, th.clone(), th.clone(), th.clone())
+        H.hpo_set_create_flat(th.double(), th, th.clone(), th.clone(), th.clone())
     assert e.value.status == H.HPO_EDTYPE
+    with pytest.raises(TypeError):  # mixed moment dtypes are refused before the call
+        H.hpo_set_create_flat(th.to(torch.bfloat16), th, th.clone(), th.to(torch.bfloat16), th.clone())
 
 
 def test_bf16_writeback_exhaustive(H, orc):

@@ -498,3 +498,69 @@ def test_scaled_step_skips_and_counts(orc):
     assert not r.applied and not r.found_inf and O.t == 1 and r.extra["threshold_skip"]
     r = O.step_scaled([g * np.float32(512.0)], sc, skip_threshold=1.0)
     assert r.applied and O.t == 2 and float(sc.scale) == 1024.0  # two clean steps: grown
+
+
+# ---------------------------------------------------------------------------
+# reduced-precision variants ("02 · Optimizer：算法与 infra" §9.2 fp16/bf16 model
+# params, §16 lower-precision exp_avg / exp_avg_sq)
+# ---------------------------------------------------------------------------
+def test_fp16_rne_exhaustive_against_torch_cast(orc):
+    """All 2^32 fp32 patterns against torch's CPU float32 -> float16 cast (a
+    library routine, IEEE round to nearest even with subnormals).  NaNs by
+    class."""
+    step = 1 << 28
+    base = np.arange(step, dtype=np.uint32)
+    for first in range(0, 1 << 32, step):
+        bits = base + np.uint32(first)
+        ours = orc.fp16_rne_patterns(first, step)
+        ref = torch.from_numpy(bits.view(np.float32)).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+        isnan = (bits & 0x7FFFFFFF) > 0x7F800000
+        assert np.array_equal(ours[~isnan], ref[~isnan]), hex(first)
+        assert np.all((ours[isnan] & 0x7FFF) > 0x7C00)
+
+
+def test_fp16_rne_against_numpy_cast_stratified(orc):
+    """A second library (numpy's float32 -> float16) on every exponent and sign
+    with random mantissas plus every tie pattern of the dropped bits."""
+    rng = np.random.default_rng(61)
+    se = np.repeat(np.arange(512, dtype=np.uint32) << 23, 16384)
+    mant = rng.integers(0, 1 << 23, size=se.size, dtype=np.uint32)
+    ties = []
+    for drop in range(13, 24):  # a dropped-bits field of width `drop` exactly at half, +-1
+        for d in (-1, 0, 1):
+            ties.append(((1 << (drop - 1)) + d) & 0x7FFFFF)
+    tie_bits = (np.arange(512, dtype=np.uint32)[:, None] << 23 | np.array(ties, np.uint32)[None, :]).ravel()
+    odd = (tie_bits | (1 << 13)) & 0xFFFFFFFF  # same, with an odd kept bit
+    bits = np.concatenate([se | mant, tie_bits, odd.astype(np.uint32)])
+    x = bits.view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    ours = orc.fp16_rne(x)
+    isnan = (bits & 0x7FFFFFFF) > 0x7F800000
+    assert np.array_equal(ours[~isnan], ref[~isnan])
+
+
+@pytest.mark.parametrize("mode", [ADAMW, ADAM_L2])
+def test_bf16_moments_are_the_fp32_update_rounded(orc, mode):
+    """With moments held in bf16, one step equals the fp32-moment step run from
+    the same (bf16-representable) moments, followed by the bf16 rounding of the
+    new moments (torch's CPU cast), with the master untouched by that
+    rounding; the fp16 param is the fp16 rounding of the master (numpy cast)."""
+    th, m, v, G = _rand_state(100_003, 60)
+    m16 = torch.from_numpy(m).to(torch.bfloat16)
+    v16 = torch.from_numpy(v).to(torch.bfloat16)
+    m_b = m16.view(torch.int16).numpy().view(np.uint16).copy()
+    v_b = v16.view(torch.int16).numpy().view(np.uint16).copy()
+    m_f = m16.float().numpy().copy()
+    v_f = v16.float().numpy().copy()
+    import ctypes
+    for t in (1, 7):
+        a = orc.OTensor(th.copy(), m_b.copy(), v_b.copy(), np.zeros(th.size, np.uint16), 0, param_fp16=True)
+        b = orc.OTensor(th.copy(), m_f.copy(), v_f.copy(), np.zeros(th.size, np.uint16), 0, param_fp16=False)
+        for T in (a, b):
+            orc.apply_update([T], [G], orc.Hyper(mode=mode), [(1e-3, 0.1)], t, 1.0, True, 0.5, 0.5)
+        assert np.array_equal(a.theta.view(np.uint32), b.theta.view(np.uint32))
+        assert np.array_equal(a.m, torch.from_numpy(b.m).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+        assert np.array_equal(a.v, torch.from_numpy(b.v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+        with np.errstate(over="ignore"):
+            assert np.array_equal(a.p, a.theta.astype(np.float16).view(np.uint16))
