@@ -18,6 +18,9 @@ orders the steps of one optimizer step the way the pages order them:
     §9.2   the master is then written back to the 16-bit model params.
   [FP32-RFC] "支持FP32优化器" §7.2: fp32 params are their own master.
 
+``muon.py`` adds the Muon step (momentum, Newton-Schulz, scaled update)
+and the AdamW + Muon chain in numpy, with its own pins.
+
 Parity pinning: every function here is checked in ``tests/test_oracle_pins.py``
 against values the pages print, closed forms, ``math.fsum``, torch's CPU cast
 and torch's CPU Adam/AdamW (a different op order).  NaN bit patterns of the
