@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define HPO_ABI_VERSION 1
+#define HPO_ABI_VERSION 2
 /* Most parameter groups one step can take (per-group lr / weight decay). */
 #define HPO_MAX_GROUPS 16
 
@@ -116,9 +116,13 @@ typedef struct {
     int32_t device;        /* HIP device ordinal of the set */
     int32_t n_vector;      /* tensors (ranges) whose body takes the 16-byte vector path */
     int32_t grad_group;    /* consecutive chunks per grad-pass workgroup */
-    int32_t reserved;
+    int32_t kind;          /* HPO_SET_ADAM or HPO_SET_MUON */
     int64_t n_grad_parts;  /* grad-pass workgroups = binary64 partials per norm */
 } hpo_set_info_t;
+
+/* What a set is stepped with: AdamW (the list and flat sets) or Muon (the
+ * matrix sets of hpo_muon_set_create). */
+typedef enum { HPO_SET_ADAM = 0, HPO_SET_MUON = 1 } hpo_set_kind;
 
 /* ---------------------------------------------------------------------- */
 /* Sets                                                                    */
@@ -298,6 +302,113 @@ hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* 
  * of a bf16 set ([OPT-INFRA] §9.2, the write-back row; the same conversion the
  * step fuses).  A no-op for fp32 sets. */
 hpo_status hpo_copy_main_to_model(hpo_set s, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Muon, chained with AdamW                                                */
+/* ---------------------------------------------------------------------- */
+/* Muon ([HANDBOOK] "优化器：AdamW、Muon 与分布式优化器", Muon section;
+ * [OPT-INFRA] §5) steps the hidden 2-D weight matrices; embeddings, the
+ * output head and every 1-D parameter stay on AdamW ([OPT-INFRA] §5.5,
+ * §14.2).  Per matrix W (rows x cols) with fp32 master, fp32 main grad G and
+ * fp32 momentum M, each applied step computes, with g = G * inv_scale
+ * (times the clip coefficient C when clipping, the same global norm and rule
+ * as the AdamW step):
+ *   momentum   HPO_MUON_MOMENTUM_SUM ([HANDBOOK]):  M = mu M + g,          g~ = g + mu M
+ *              HPO_MUON_MOMENTUM_EMA ([OPT-INFRA] §1): M = mu M + (1-mu) g, g~ = (1-mu) g + mu M
+ *              (without Nesterov g~ = M); fp32, one rounding per operation;
+ *   NS         X = g~ / (||g~||_F + eps) (the sum of squares in binary64, the
+ *              norm and the guard in fp32), transposed when rows > cols; then
+ *              ns_steps times: A = X X^T, B = b A + c A A, X = a X + B X, with
+ *              (a, b, c) of each step; O = X, transposed back.  The matmuls
+ *              run on the bf16 matrix cores ([OPT-INFRA] §5.2, §5.4): X, A
+ *              and B are rounded to bf16 (nearest even) as operands, products
+ *              accumulate in fp32, the last X stays fp32;
+ *   update     W = fp32(W * fp32(1 - lr*wd)); W = fp32(W - fp32(lr*scale) * O)
+ *              (decay first, as the handbook listing does), scale =
+ *              base * extra_scale with base sqrt(max(rows, cols)) (spectral;
+ *              extra 0.2 is Moonlight's RMS match, [OPT-INFRA] §5.4),
+ *              sqrt(max(1, rows/cols)) (shape) or sqrt(rows/cols) (unit RMS)
+ *              ([OPT-INFRA] §14.6); then param = bf16_rne(W).
+ * The momentum and the param / master of skipped steps are bit-unchanged. */
+typedef enum { HPO_MUON_MOMENTUM_SUM = 0, HPO_MUON_MOMENTUM_EMA = 1 } hpo_muon_momentum;
+typedef enum { HPO_MUON_SCALE_SPECTRAL = 0, HPO_MUON_SCALE_SHAPE = 1, HPO_MUON_SCALE_UNIT_RMS = 2 } hpo_muon_scale;
+#define HPO_NS_MAX_STEPS 16
+
+/* Muon hyperparameters.  Defaults (the handbook's Muon): momentum 0.95,
+ * nesterov 1, HPO_MUON_MOMENTUM_SUM, 5 NS steps with (a, b, c) =
+ * (3.4445, -4.7750, 2.0315), eps 1e-7, spectral scale with extra 0.2. */
+typedef struct {
+    double momentum;          /* mu, in [0, 1) */
+    int32_t nesterov;         /* 0 or 1 */
+    int32_t momentum_form;    /* hpo_muon_momentum */
+    int32_t ns_steps;         /* 1 .. HPO_NS_MAX_STEPS */
+    int32_t scale_mode;       /* hpo_muon_scale */
+    double extra_scale;       /* finite, >= 0 */
+    double ns_eps;            /* finite, >= 0 */
+    const double* ns_coeffs;  /* host array of 3 * ns_steps (a, b, c per step, rounded to fp32),
+                                 or NULL for the original set at every step */
+} hpo_muon_cfg;
+
+/* Default workspace cap of a Muon set (see hpo_muon_set_create). */
+#define HPO_MUON_DEFAULT_WORKSPACE (((int64_t)4) << 30)
+
+/* A Muon set over n_matrices row-major matrices: matrix i has rows[i] x
+ * cols[i] elements at param[i] (bf16 model param, or NULL / main_param[i]
+ * for HPO_PARAM_FP32), main_param[i] (fp32 master), main_grad[i] (fp32 main
+ * grad, as stored) and momentum[i] (fp32).  Every pointer must be 16-byte
+ * aligned.  param_dtype: HPO_PARAM_BF16 or HPO_PARAM_FP32; fp16 params with
+ * Muon are an error ([OPT-INFRA] §14.3), as is HPO_STATE_BF16 (HPO_EDTYPE).
+ * group_index[i] selects the matrix's hpo_group in hpo_muon_step (NULL:
+ * group 0).  Matrices with rows or cols 0 are allowed and never touched.
+ * The set plans batches of same-shape matrices and allocates one device
+ * workspace for the largest batch: per matrix 4 B per element (the Nesterov
+ * gradient) plus bf16 X, two X^T and the two Gram-sized matrices of NS, with
+ * both dimensions padded to multiples of 256.  workspace_bytes caps the
+ * batch size (0: HPO_MUON_DEFAULT_WORKSPACE); a matrix that alone needs more
+ * gets a batch of its own.  hpo_set_info reports the total in device_bytes.
+ * hpo_unscale_check_inf, hpo_grad_global_norm, hpo_grad_global_norm_sets and
+ * hpo_copy_main_to_model accept Muon sets; hpo_adamw_step and
+ * hpo_step_device do not (HPO_EINVAL). */
+hpo_status hpo_muon_set_create(hpo_set* out, int32_t n_matrices, int32_t param_dtype, void* const* param,
+                               float* const* main_param, float* const* main_grad, float* const* momentum,
+                               const int64_t* rows, const int64_t* cols, const int32_t* group_index,
+                               int64_t workspace_bytes, void* stream);
+
+/* One Muon update of every matrix of the set, host-driven like
+ * hpo_adamw_step: inv_scale, the clip from max_norm and *d_norm (device fp32,
+ * read when max_norm > 0), and the device-side skip on *d_found_inf (nullable).
+ * groups[k] = lr / weight decay of group k. */
+hpo_status hpo_muon_step(hpo_set s, const hpo_muon_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                         float inv_scale, double max_norm, const float* d_norm, const int32_t* d_found_inf,
+                         void* stream);
+
+/* The global norm over several sets at once ([OPT-INFRA] §11.4: a chain of
+ * optimizers takes one norm over all of its grads): *d_norm receives
+ * fp32(sqrt(sum over every element of every set of (G * inv_scale)^2)), the
+ * sum in binary64, the sets' partial sums added in array order; d_found_inf
+ * as in hpo_grad_global_norm.  1 <= n_sets <= 4, all on one device. */
+hpo_status hpo_grad_global_norm_sets(const hpo_set* sets, int32_t n_sets, float inv_scale, float* d_norm,
+                                     int32_t* d_found_inf, void* stream);
+
+/* hpo_step_device for an AdamW set and a Muon set stepped as one chain
+ * ([OPT-INFRA] §11.4): one grad pass over both, one norm (AdamW grads
+ * first), one found_inf and one skip decision; then the AdamW update, the
+ * Muon update and the counters / scaler.  Either set may be NULL (not both). */
+hpo_status hpo_step_device_chain(hpo_set adam_set, const hpo_adam_cfg* cfg, const hpo_group* groups,
+                                 int32_t n_groups, hpo_set muon_set, const hpo_muon_cfg* mcfg,
+                                 const hpo_group* muon_groups, int32_t n_muon_groups, double max_norm,
+                                 const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state, int64_t t_first,
+                                 int32_t window, void* stream);
+
+/* Newton-Schulz alone ([HANDBOOK] Muon listing, the NS function): O (fp32,
+ * rows x cols, row-major, device) from G (fp32, same shape, device), with
+ * cfg's ns_steps, ns_coeffs and ns_eps (the momentum and scale fields are not
+ * read) and the same bf16 matrix-core arithmetic as hpo_muon_step.  The
+ * caller provides a device workspace of at least
+ * hpo_newton_schulz_workspace(rows, cols) bytes, 256-byte aligned. */
+hpo_status hpo_newton_schulz(const float* d_G, int64_t rows, int64_t cols, const hpo_muon_cfg* cfg, float* d_out,
+                             void* d_workspace, int64_t workspace_bytes, void* stream);
+hpo_status hpo_newton_schulz_workspace(int64_t rows, int64_t cols, int64_t* out_bytes);
 
 /* ---------------------------------------------------------------------- */
 /* Host-only queries (no device needed)                                   */

@@ -23,6 +23,11 @@ LIB_PATH = os.path.join(PKG, "libhpo.so")
 ARCH = "gfx950"
 
 
+# gfx950 kernel files and host files of libhpo
+DEVICE_SOURCES = ("hpo_kernels.hip", "hpo_muon.hip")
+HOST_SOURCES = ("hpo_api.cpp", "hpo_muon_api.cpp")
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -54,13 +59,18 @@ def build(verbose: bool = False) -> str:
     """Compile the kernels and the host API, link libhpo.so (always rebuilds)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    k_obj = os.path.join(BUILD_DIR, "hpo_kernels.o")
-    a_obj = os.path.join(BUILD_DIR, "hpo_api.o")
     inc = ["-I", INCLUDE, "-I", CSRC]
-    _run([cc, *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, "hpo_kernels.hip"), "-o", k_obj], verbose)
-    _run([cc, *HOST_FLAGS, *inc, "-I", rocm_include(), "-c", os.path.join(CSRC, "hpo_api.cpp"), "-o", a_obj], verbose)
+    objs = []
+    for src in DEVICE_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        _run([cc, *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        _run([cc, *HOST_FLAGS, *inc, "-I", rocm_include(), "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     tmp = LIB_PATH + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, a_obj, "-o", tmp], verbose)
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

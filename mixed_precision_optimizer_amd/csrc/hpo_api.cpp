@@ -16,28 +16,9 @@
 #include <string>
 #include <vector>
 
-#include "hpo_impl.h"
+#include "hpo_set.h"
 
-struct hpo_set_ {
-    hpo::SetView view{};
-    int32_t n_tensors = 0;
-    int32_t param_dtype = 0;
-    int32_t is_flat = 0;
-    int32_t device = 0;
-    int32_t max_group = 0;   /* largest group index in the set */
-    int32_t n_vector = 0;
-    int64_t numel = 0;
-    int64_t n_chunks = 0;
-    int32_t grad_group = 1;  /* chunks per grad-pass workgroup */
-    int64_t n_parts = 0;     /* grad-pass workgroups = reduction partials */
-    int64_t device_bytes = 0;
-    hpo::TensorDesc* d_tensors = nullptr;
-    hpo::Chunk* d_chunks = nullptr;
-    double* d_part_sum = nullptr;
-    int32_t* d_part_flag = nullptr;
-};
-
-namespace {
+namespace hpo_host {
 
 thread_local std::string g_last_error;
 
@@ -246,6 +227,7 @@ void free_set(hpo_set s)
     if (s->d_chunks) (void)hipFree(s->d_chunks);
     if (s->d_part_sum) (void)hipFree(s->d_part_sum);
     if (s->d_part_flag) (void)hipFree(s->d_part_flag);
+    free_muon(s->muon);
     delete s;
 }
 
@@ -285,7 +267,14 @@ int32_t* stage_flag(hpo_set s) { return s->d_part_flag + (s->n_parts > 0 ? s->n_
 
 bool is_finite(double x) { return std::isfinite(x); }
 
-}  // namespace
+hpo::Partials partials_of(hpo_set s)
+{
+    return hpo::Partials{s->d_part_sum, s->d_part_flag, s->n_parts, stage_sum(s), stage_flag(s)};
+}
+
+}  // namespace hpo_host
+
+using namespace hpo_host;
 
 extern "C" {
 
@@ -590,6 +579,7 @@ hpo_status hpo_set_info(hpo_set s, hpo_set_info_t* out)
     out->device = s->device;
     out->n_vector = s->n_vector;
     out->grad_group = s->grad_group;
+    out->kind = s->kind;
     out->n_grad_parts = s->n_parts;
     return ok();
 }
@@ -650,6 +640,8 @@ hpo_status check_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* group
     hpo_status st = check_set(s);
     if (st != HPO_OK)
         return st;
+    if (s->kind != HPO_SET_ADAM)
+        return fail(HPO_EINVAL, "a Muon set takes hpo_muon_step / hpo_step_device_chain, not the AdamW step");
     if (!cfg)
         return fail(HPO_EINVAL, "cfg is NULL");
     if (cfg->mode != HPO_ADAMW && cfg->mode != HPO_ADAM_L2)
@@ -736,13 +728,13 @@ hpo_status hpo_scaler_state_init(hpo_scaler_state* d_state, float loss_scale, in
     return ok();
 }
 
-hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
-                           double max_norm, const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state,
-                           int64_t t_first, int32_t window, void* stream)
+}  // extern "C"
+
+namespace {
+
+hpo_status check_scaler_args(const hpo_scaler_cfg* scfg, const hpo_scaler_state* d_state, int64_t t_first,
+                             int32_t window)
 {
-    hpo_status st = check_step(s, cfg, groups, n_groups, max_norm);
-    if (st != HPO_OK)
-        return st;
     if (!scfg)
         return fail(HPO_EINVAL, "scfg is NULL");
     if (!d_state || !aligned(d_state, 8))
@@ -761,6 +753,12 @@ hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* 
             !std::isfinite(scfg->min_scale))
             return fail(HPO_EINVAL, "growth_factor, backoff_factor and min_scale must be finite and > 0");
     }
+    return HPO_OK;
+}
+
+hpo::AdamScalars device_scalars(const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                                double max_norm, hpo_scaler_state* d_state, int64_t t_first, int32_t window)
+{
     hpo::AdamScalars sc = base_scalars(cfg, groups, n_groups, max_norm);
     sc.d_state = d_state;
     sc.t_first = t_first;
@@ -769,6 +767,11 @@ hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* 
         sc.bc1_tab[j] = bias_correction(cfg->beta1, t_first + j);
         sc.bc2_tab[j] = bias_correction(cfg->beta2, t_first + j);
     }
+    return sc;
+}
+
+hpo::ScalerRule rule_of(const hpo_scaler_cfg* scfg)
+{
     hpo::ScalerRule rule{};
     rule.dynamic = scfg->dynamic ? 1 : 0;
     rule.growth_interval = scfg->growth_interval;
@@ -776,6 +779,25 @@ hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* 
     rule.growth_factor = scfg->growth_factor;
     rule.backoff_factor = scfg->backoff_factor;
     rule.min_scale = scfg->min_scale;
+    return rule;
+}
+
+}  // namespace
+
+extern "C" {
+
+hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                           double max_norm, const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state,
+                           int64_t t_first, int32_t window, void* stream)
+{
+    hpo_status st = check_step(s, cfg, groups, n_groups, max_norm);
+    if (st != HPO_OK)
+        return st;
+    st = check_scaler_args(scfg, d_state, t_first, window);
+    if (st != HPO_OK)
+        return st;
+    const hpo::AdamScalars sc = device_scalars(cfg, groups, n_groups, max_norm, d_state, t_first, window);
+    const hpo::ScalerRule rule = rule_of(scfg);
     hipStream_t strm = as_stream(stream);
     hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, 1.0f,
                                          &d_state->inv_scale, s->d_part_sum, s->d_part_flag, strm);
@@ -804,6 +826,101 @@ hpo_status hpo_copy_main_to_model(hpo_set s, void* stream)
     hipError_t e = hpo::launch_copy_main_to_model(s->view, s->n_chunks, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch master->model copy");
+    return ok();
+}
+
+hpo_status hpo_grad_global_norm_sets(const hpo_set* sets, int32_t n_sets, float inv_scale, float* d_norm,
+                                     int32_t* d_found_inf, void* stream)
+{
+    if (!sets || n_sets < 1 || n_sets > hpo::kMaxFoldSets)
+        return fail(HPO_EINVAL, "sets must be an array of 1..%d sets (got %d)", hpo::kMaxFoldSets, n_sets);
+    if (!d_norm)
+        return fail(HPO_EINVAL, "d_norm is NULL");
+    if (!std::isfinite(inv_scale))
+        return fail(HPO_EINVAL, "inv_scale must be finite");
+    hpo::Partials p[hpo::kMaxFoldSets];
+    for (int32_t k = 0; k < n_sets; ++k) {
+        hpo_status st = check_set(sets[k]);
+        if (st != HPO_OK)
+            return st;
+        for (int32_t j = 0; j < k; ++j)
+            if (sets[j] == sets[k])
+                return fail(HPO_EINVAL, "set %d appears twice", k);
+        p[k] = partials_of(sets[k]);
+    }
+    hipStream_t strm = as_stream(stream);
+    for (int32_t k = 0; k < n_sets; ++k) {
+        hpo_set s = sets[k];
+        hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, inv_scale,
+                                             nullptr, s->d_part_sum, s->d_part_flag, strm);
+        if (e != hipSuccess)
+            return hip_fail(e, "launch norm pass");
+    }
+    hipError_t e = hpo::launch_finalize_sets(p, n_sets, d_norm, d_found_inf, strm);
+    if (e != hipSuccess)
+        return hip_fail(e, "launch norm finalize");
+    return ok();
+}
+
+hpo_status hpo_step_device_chain(hpo_set adam_set, const hpo_adam_cfg* cfg, const hpo_group* groups,
+                                 int32_t n_groups, hpo_set muon_set, const hpo_muon_cfg* mcfg,
+                                 const hpo_group* muon_groups, int32_t n_muon_groups, double max_norm,
+                                 const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state, int64_t t_first,
+                                 int32_t window, void* stream)
+{
+    if (!adam_set && !muon_set)
+        return fail(HPO_EINVAL, "the chain needs at least one set");
+    hpo_status st = HPO_OK;
+    if (adam_set) {
+        st = check_step(adam_set, cfg, groups, n_groups, max_norm);
+        if (st != HPO_OK)
+            return st;
+    }
+    if (muon_set) {
+        st = check_muon_step(muon_set, mcfg, muon_groups, n_muon_groups, max_norm);
+        if (st != HPO_OK)
+            return st;
+    }
+    if (adam_set && muon_set && adam_set->device != muon_set->device)
+        return fail(HPO_EDEVICE, "the two sets live on different devices");
+    st = check_scaler_args(scfg, d_state, t_first, window);
+    if (st != HPO_OK)
+        return st;
+    const hpo::ScalerRule rule = rule_of(scfg);
+    hipStream_t strm = as_stream(stream);
+    hpo::Partials p[2];
+    int n_sets = 0;
+    for (hpo_set s : {adam_set, muon_set}) {
+        if (!s)
+            continue;
+        hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, 1.0f,
+                                             &d_state->inv_scale, s->d_part_sum, s->d_part_flag, strm);
+        if (e != hipSuccess)
+            return hip_fail(e, "launch norm pass");
+        p[n_sets++] = partials_of(s);
+    }
+    hipError_t e = hpo::launch_finalize_state_sets(p, n_sets, d_state, scfg->grad_norm_skip_threshold, strm);
+    if (e != hipSuccess)
+        return hip_fail(e, "launch norm finalize");
+    if (adam_set) {
+        const hpo::AdamScalars sc = device_scalars(cfg, groups, n_groups, max_norm, d_state, t_first, window);
+        e = hpo::launch_adam(adam_set->view, adam_set->n_chunks, cfg->mode, sc, strm);
+        if (e != hipSuccess)
+            return hip_fail(e, "launch adam update");
+    }
+    if (muon_set) {
+        hpo::MuonGate gate{};
+        gate.st = d_state;
+        gate.t_first = t_first;
+        gate.window = window;
+        gate.dev = 1;
+        st = muon_enqueue(muon_set, mcfg, muon_groups, n_muon_groups, gate, 1.0f, max_norm, nullptr, strm);
+        if (st != HPO_OK)
+            return st;
+    }
+    e = hpo::launch_step_end(d_state, rule, t_first, window, strm);
+    if (e != hipSuccess)
+        return hip_fail(e, "launch step end");
     return ok();
 }
 

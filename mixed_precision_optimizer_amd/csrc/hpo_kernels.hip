@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include "hpo_impl.h"
+#include "hpo_device.h"
 
 /* Tuning knobs (compile time), defaults chosen by measurement on MI355X at
  * 8.75e9 elements.  UNROLL: 16-byte vectors per lane per array in flight in
@@ -152,21 +153,6 @@ __device__ __forceinline__ Range chunk_range(const SetView& sv, int64_t chunk)
     return r;
 }
 
-/* fp32 -> bf16 bits, IEEE round to nearest, ties to even ([OPT-INFRA] §9.2
- * write-back; [FP32-RFC] case 1: the model param equals the bf16 image of the
- * master after every step).  Adding 0x7FFF plus the kept part's lowest bit to
- * the fp32 bits and dropping the low half rounds up exactly when the dropped
- * half exceeds 0x8000, or equals it with an odd kept part; a carry ripples
- * into the exponent (up to infinity).  NaN becomes the quiet NaN 0x7FC0 with
- * the input's sign. */
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return ((u >> 16) & 0x8000u) | 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
@@ -199,7 +185,6 @@ __device__ __forceinline__ uint2 pack_param4(float4 t)
 
 /* Moments: fp32, or bf16 widened exactly on load and rounded to nearest even
  * on store ([OPT-INFRA] §16, lower-precision exp_avg / exp_avg_sq). */
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 template <int SDT>
 __device__ __forceinline__ float4 ld_moment4(const void* base, int64_t i)
@@ -243,27 +228,7 @@ __device__ __forceinline__ void st_moment1(void* base, int64_t e, float x)
 /* Binary64 sum over a workgroup of NT lanes: shuffle tree inside each
  * wavefront, then wavefront 0 adds the per-wavefront sums in index order.
  * The order is fixed by the lane layout alone, so results are reproducible. */
-template <int NT>
-__device__ __forceinline__ double block_sum(double x)
-{
-    constexpr int kWaves = NT / 64;
-    __shared__ double wsum[kWaves];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        x += __shfl_down(x, off, 64);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    if (lane == 0)
-        wsum[wave] = x;
-    __syncthreads();
-    double tot = 0.0;
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            tot += wsum[w];
-    }
-    return tot; /* valid in thread 0 */
-}
+
 
 /* ---------------------------------------------------------------------- */
 /* grad pass: non-finite flag + sum of squares, or in-place unscale        */
@@ -393,15 +358,34 @@ __global__ __launch_bounds__(kFinalBlock) void k_reduce_stage(const double* part
     }
 }
 
+/* The last-stage inputs of up to kMaxFoldSets sets, folded in order. */
+struct Fold {
+    const double* sum[kMaxFoldSets];
+    const int32_t* flag[kMaxFoldSets];
+    int64_t n[kMaxFoldSets];
+    int32_t count;
+};
+
+__device__ __forceinline__ double fold_sets(const Fold& f, bool want_sum, int& any_bad)
+{
+    double tot = 0.0;
+    any_bad = 0;
+    for (int k = 0; k < f.count; ++k) {
+        int bad = 0;
+        const double s = reduce_partials(f.sum[k], f.flag[k], 0, f.n[k], want_sum, bad);
+        tot = k == 0 ? s : tot + s;
+        any_bad |= bad;
+    }
+    return tot;
+}
+
 /* Last stage: one workgroup over all remaining partials, then sqrt and the
- * flag.  d_norm == nullptr: flag only (part_sum is not read). */
-__global__ __launch_bounds__(kFinalBlock) void k_finalize(const double* part_sum,
-                                                          const int32_t* part_flag, int64_t n,
-                                                          float* d_norm, int32_t* d_found)
+ * flag.  d_norm == nullptr: flag only (the sums are not read). */
+__global__ __launch_bounds__(kFinalBlock) void k_finalize(Fold f, float* d_norm, int32_t* d_found)
 {
     const bool want_norm = d_norm != nullptr;
     int any_bad = 0;
-    const double tot = reduce_partials(part_sum, part_flag, 0, n, want_norm, any_bad);
+    const double tot = fold_sets(f, want_norm, any_bad);
     if (threadIdx.x == 0) {
         if (want_norm)
             *d_norm = static_cast<float>(sqrt(tot));
@@ -412,11 +396,10 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(const double* part_sum
 
 /* Last stage of the device-resident step: norm, found_inf and whether the
  * step will be applied (finite grads, norm not above the skip threshold). */
-__global__ __launch_bounds__(kFinalBlock) void k_finalize_state(const double* part_sum, const int32_t* part_flag,
-                                                                int64_t n, hpo_scaler_state* st, double threshold)
+__global__ __launch_bounds__(kFinalBlock) void k_finalize_state(Fold f, hpo_scaler_state* st, double threshold)
 {
     int any_bad = 0;
-    const double tot = reduce_partials(part_sum, part_flag, 0, n, true, any_bad);
+    const double tot = fold_sets(f, true, any_bad);
     if (threadIdx.x == 0) {
         const float norm = static_cast<float>(sqrt(tot));
         st->grad_norm = norm;
@@ -667,24 +650,6 @@ hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_gr
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
-                           double* stage_sum, int32_t* stage_flag, float* d_norm, int32_t* d_found,
-                           hipStream_t stream)
-{
-    const double* ps = d_norm != nullptr ? part_sum : nullptr;
-    if (n_parts > kFinalSpan) {
-        const int64_t n_stage = (n_parts + kFinalSpan - 1) / kFinalSpan;
-        hipError_t e = launch(k_reduce_stage, n_stage, kFinalBlock, stream, ps, part_flag, n_parts,
-                              stage_sum, stage_flag);
-        if (e != hipSuccess)
-            return e;
-        ps = d_norm != nullptr ? static_cast<const double*>(stage_sum) : nullptr;
-        part_flag = stage_flag;
-        n_parts = n_stage;
-    }
-    return launch(k_finalize, 1, kFinalBlock, stream, ps, part_flag, n_parts, d_norm, d_found);
-}
-
 template <bool DEV, int SDT, int PDT>
 hipError_t launch_adam_p(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                          hipStream_t stream)
@@ -725,22 +690,71 @@ hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const 
                                  : launch_adam_t<false>(sv, n_chunks, mode, sc, stream);
 }
 
+
+namespace {
+
+/* First stage for the sets with many partials, then the last-stage inputs. */
+hipError_t fold_inputs(const Partials* p, int n_sets, bool want_sum, Fold& f, hipStream_t stream)
+{
+    if (n_sets < 1 || n_sets > kMaxFoldSets)
+        return hipErrorInvalidValue;
+    f.count = n_sets;
+    for (int k = 0; k < n_sets; ++k) {
+        const double* ps = want_sum ? p[k].sum : nullptr;
+        const int32_t* pf = p[k].flag;
+        int64_t n = p[k].n;
+        if (n > kFinalSpan) {
+            const int64_t n_stage = (n + kFinalSpan - 1) / kFinalSpan;
+            hipError_t e = launch(k_reduce_stage, n_stage, kFinalBlock, stream, ps, pf, n, p[k].stage_sum,
+                                  p[k].stage_flag);
+            if (e != hipSuccess)
+                return e;
+            ps = want_sum ? static_cast<const double*>(p[k].stage_sum) : nullptr;
+            pf = p[k].stage_flag;
+            n = n_stage;
+        }
+        f.sum[k] = ps;
+        f.flag[k] = pf;
+        f.n[k] = n;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_finalize_sets(const Partials* p, int n_sets, float* d_norm, int32_t* d_found, hipStream_t stream)
+{
+    Fold f{};
+    hipError_t e = fold_inputs(p, n_sets, d_norm != nullptr, f, stream);
+    if (e != hipSuccess)
+        return e;
+    return launch(k_finalize, 1, kFinalBlock, stream, f, d_norm, d_found);
+}
+
+hipError_t launch_finalize_state_sets(const Partials* p, int n_sets, hpo_scaler_state* st, double threshold,
+                                      hipStream_t stream)
+{
+    Fold f{};
+    hipError_t e = fold_inputs(p, n_sets, true, f, stream);
+    if (e != hipSuccess)
+        return e;
+    return launch(k_finalize_state, 1, kFinalBlock, stream, f, st, threshold);
+}
+
+hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
+                           double* stage_sum, int32_t* stage_flag, float* d_norm, int32_t* d_found,
+                           hipStream_t stream)
+{
+    const Partials p{part_sum, part_flag, n_parts, stage_sum, stage_flag};
+    return launch_finalize_sets(&p, 1, d_norm, d_found, stream);
+}
+
 hipError_t launch_finalize_state(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
                                  double* stage_sum, int32_t* stage_flag, hpo_scaler_state* st,
                                  double threshold, hipStream_t stream)
 {
-    const double* ps = part_sum;
-    if (n_parts > kFinalSpan) {
-        const int64_t n_stage = (n_parts + kFinalSpan - 1) / kFinalSpan;
-        hipError_t e = launch(k_reduce_stage, n_stage, kFinalBlock, stream, ps, part_flag, n_parts,
-                              stage_sum, stage_flag);
-        if (e != hipSuccess)
-            return e;
-        ps = stage_sum;
-        part_flag = stage_flag;
-        n_parts = n_stage;
-    }
-    return launch(k_finalize_state, 1, kFinalBlock, stream, ps, part_flag, n_parts, st, threshold);
+    const Partials p{part_sum, part_flag, n_parts, stage_sum, stage_flag};
+    return launch_finalize_state_sets(&p, 1, st, threshold, stream);
 }
 
 hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hysteresis, int64_t applied,

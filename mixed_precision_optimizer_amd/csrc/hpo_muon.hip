@@ -1,0 +1,630 @@
+/*
+ * hpo_muon.hip -- gfx950 kernels of the Muon step: momentum and Nesterov
+ * gradient, Newton-Schulz orthogonalization on the bf16 matrix cores, and
+ * the decayed, scaled master update with the 16-bit write-back.
+ *
+ * Sources (web pages):
+ *   [HANDBOOK]   "优化器：AdamW、Muon 与分布式优化器" (ai-infra-handbooks,
+ *                train/algo/optimizer), section on Muon: the momentum, the
+ *                Nesterov gradient fed to NS, the NS iteration and its
+ *                coefficients, and the update W(1 - lr*wd) - lr*0.2*sqrt(max(A, B))*O
+ *   [OPT-INFRA]  "02 · Optimizer：算法与 infra" (llm-infra-atlas, train/02_optimizer),
+ *                §1 (EMA momentum), §5.2 (NS, run in bf16), §5.4 (Moonlight
+ *                scale and decay), §14.6 (other scales)
+ *
+ * One batch is a run of same-shape matrices.  Per batch:
+ *   momentum   one pass over grad and momentum (chunk table): g = G*inv (*C),
+ *              M <- mu M + g (or the EMA form), g~ (Nesterov) to the
+ *              workspace, binary64 sum of g~^2 per chunk;     16 B/elem
+ *   norm       one workgroup per matrix: fixed-order sum of its chunks
+ *   input      X0 = bf16(g~ / (norm + eps)) in the wide orientation (m <= n),
+ *              and its transpose, both zero-padded to multiples of 256,
+ *              through 64 x 64 LDS tiles;                       8 B/elem
+ *   NS step    three bf16 GEMMs on MFMA (v_mfma_f32_32x32x16_bf16, fp32
+ *              accumulation), each C = P Q^T with both operands read along
+ *              their rows (the matrix cores' natural operand order):
+ *                A  = X X^T                  (P = Q = X)
+ *                B  = b A + c A A^T          (P = Q = A; A is symmetric)
+ *                X' = a X + B X              (P = B, Q = X^T)
+ *              the epilogues round A, B and X' to bf16 and write X' both
+ *              ways round (X for the next A, X^T for the next B X).
+ *   last step  the epilogue keeps O = a X + B X in fp32 and applies
+ *              W <- fp32(W * fp32(1 - lr*wd)); W <- fp32(W - fp32(lr*scale) * O)
+ *              and the bf16 write-back in place of storing O.
+ * Zero padding is a fixed point of the iteration (zero rows and columns of
+ * X give zero rows and columns of A, B and X'), so the GEMMs run on whole
+ * tiles with no bounds checks.
+ *
+ * GEMM tiling: a 256-lane workgroup (2 x 2 wavefronts) computes a
+ * 128 x 128 tile of C; each wavefront a 64 x 64 block as 2 x 2 MFMA tiles of
+ * 32 x 32, k in slices of 16.  Operands stream through LDS in k-stages of 64
+ * (128 B per row), double-buffered (64 KB), rows stored with their eight
+ * 16-byte pieces permuted by an XOR of the row index so that the MFMA
+ * fragment reads (32 rows x 16 B per half-wavefront) hit distinct banks.
+ *
+ * Floating point: built with -ffp-contract=off; every elementwise operation
+ * rounds on its own, in the order written.
+ */
+#include <hip/hip_runtime.h>
+
+#include "hpo_impl.h"
+#include "hpo_device.h"
+
+namespace hpo {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kNsThreads = 256;        /* 4 wavefronts, 2 x 2 over the C tile */
+constexpr int kWaveTiles = 2;          /* 32 x 32 MFMA tiles per wavefront, each way */
+constexpr int kBM = 2 * 32 * kWaveTiles;
+constexpr int kBN = 2 * 32 * kWaveTiles;
+constexpr int kBK = 64;                /* k per LDS stage */
+constexpr int kRowBytes = kBK * 2;     /* 128 B: eight 16-byte pieces */
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;
+static_assert(kNsPad % kBM == 0 && kNsPad % kBN == 0 && kNsPad % kBK == 0, "padding covers the tiles");
+constexpr int kTile = 64;              /* transpose tile of the input kernel */
+
+/* ---------------------------------------------------------------------- */
+/* gates and per-step values                                              */
+/* ---------------------------------------------------------------------- */
+__device__ __forceinline__ bool gate_open(const MuonGate& g)
+{
+    if (g.dev) {
+        if (!g.st->applied)
+            return false;
+        const int64_t j = g.st->applied_steps + 1 - g.t_first;
+        return j >= 0 && j < g.window;  /* outside the window the end kernel records the error */
+    }
+    return !(g.d_found != nullptr && *g.d_found != 0);
+}
+
+struct GradVals {
+    float inv_scale;
+    float C;
+    bool clip;
+};
+
+/* Unscale factor and clip coefficient ([OPT-INFRA] §11.1): the same global
+ * norm and rule as the AdamW update of the same step. */
+__device__ __forceinline__ GradVals grad_vals(const MuonScalars& sc)
+{
+    GradVals v;
+    float norm = 0.0f;
+    if (sc.gate.dev) {
+        v.inv_scale = sc.gate.st->inv_scale;
+        norm = sc.gate.st->grad_norm;
+    } else {
+        v.inv_scale = sc.inv_scale;
+        if (sc.max_norm > 0.0)
+            norm = *sc.d_norm;
+    }
+    v.clip = false;
+    v.C = 1.0f;
+    if (sc.max_norm > 0.0) {
+        const double c = sc.max_norm / (static_cast<double>(norm) + 1e-6);
+        if (c < 1.0) {
+            v.clip = true;
+            v.C = static_cast<float>(c);
+        }
+    }
+    return v;
+}
+
+/* ---------------------------------------------------------------------- */
+/* momentum + Nesterov gradient                                           */
+/* ---------------------------------------------------------------------- */
+template <int FORM, bool NEST>
+__device__ __forceinline__ float momentum_elem(float G, float& M, const GradVals& k, float mu, float omu, double& acc)
+{
+    float g = G * k.inv_scale;
+    if (k.clip)
+        g = g * k.C;
+    float gt;
+    if constexpr (FORM == HPO_MUON_MOMENTUM_SUM) {
+        M = mu * M + g;                 /* [HANDBOOK]: M <- mu M + g */
+        gt = NEST ? g + mu * M : M;     /* Nesterov: g + mu M */
+    } else {
+        M = mu * M + omu * g;           /* [OPT-INFRA] §1: lerp(M, g, 1 - mu) */
+        gt = NEST ? omu * g + mu * M : M;
+    }
+    acc += static_cast<double>(gt) * static_cast<double>(gt);
+    return gt;
+}
+
+template <int FORM, bool NEST>
+__global__ __launch_bounds__(kBlock) void k_muon_momentum(SetView sv, MuonScalars sc, MuonBatch b, float* gt,
+                                                         int64_t gt_stride, double* part)
+{
+    if (!gate_open(sc.gate))
+        return;
+    const GradVals k = grad_vals(sc);
+    const int64_t chunk = b.c0 + blockIdx.x;
+    const Chunk c = sv.chunks[chunk];
+    const TensorDesc d = sv.tensors[c.tensor];
+    const int64_t slot = c.tensor - b.first;
+    const float* __restrict__ G = d.grad + c.start;
+    float* __restrict__ M = static_cast<float*>(d.exp_avg) + c.start;
+    float* __restrict__ O = gt + slot * gt_stride + c.start;
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    const int64_t nv = c.len / kVec;  /* Muon tensors are 16-byte aligned */
+    for (int64_t i = tid; i < nv; i += kBlock) {
+        const float4 g4 = reinterpret_cast<const float4*>(G)[i];
+        float4 m4 = reinterpret_cast<float4*>(M)[i];
+        float4 o4;
+        o4.x = momentum_elem<FORM, NEST>(g4.x, m4.x, k, sc.mu, sc.omu, acc);
+        o4.y = momentum_elem<FORM, NEST>(g4.y, m4.y, k, sc.mu, sc.omu, acc);
+        o4.z = momentum_elem<FORM, NEST>(g4.z, m4.z, k, sc.mu, sc.omu, acc);
+        o4.w = momentum_elem<FORM, NEST>(g4.w, m4.w, k, sc.mu, sc.omu, acc);
+        reinterpret_cast<float4*>(M)[i] = m4;
+        reinterpret_cast<float4*>(O)[i] = o4;
+    }
+    for (int64_t e = nv * kVec + tid; e < c.len; e += kBlock) {
+        float m = M[e];
+        O[e] = momentum_elem<FORM, NEST>(G[e], m, k, sc.mu, sc.omu, acc);
+        M[e] = m;
+    }
+    const double tot = block_sum<kBlock>(acc);
+    if (tid == 0)
+        part[chunk] = tot;
+}
+
+/* Per-matrix fold of the chunk sums: dnorm = fp32(fp32(sqrt(sum)) + eps). */
+__global__ __launch_bounds__(kBlock) void k_muon_norm(const MuonInfo* info, MuonGate gate, int32_t first,
+                                                     const double* part, float eps, float* dnorm)
+{
+    if (!gate_open(gate))
+        return;
+    const int32_t mat = first + static_cast<int32_t>(blockIdx.x);
+    const MuonInfo in = info[mat];
+    double acc = 0.0;
+    for (int32_t i = threadIdx.x; i < in.n_chunks; i += kBlock)
+        acc += part[in.first_chunk + i];
+    const double tot = block_sum<kBlock>(acc);
+    if (threadIdx.x == 0)
+        dnorm[mat] = static_cast<float>(sqrt(tot)) + eps;
+}
+
+/* Sum of squares of a plain fp32 matrix (the standalone NS entry). */
+__global__ __launch_bounds__(kBlock) void k_sumsq_rows(const float* G, int64_t n, int64_t per_block, double* part)
+{
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * per_block;
+    const int64_t hi = lo + per_block < n ? lo + per_block : n;
+    double acc = 0.0;
+    for (int64_t e = lo + threadIdx.x; e < hi; e += kBlock) {
+        const double x = G[e];
+        acc += x * x;
+    }
+    const double tot = block_sum<kBlock>(acc);
+    if (threadIdx.x == 0)
+        part[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kBlock) void k_sumsq_fold(const double* part, int32_t n, float eps, float* dnorm)
+{
+    double acc = 0.0;
+    for (int32_t i = threadIdx.x; i < n; i += kBlock)
+        acc += part[i];
+    const double tot = block_sum<kBlock>(acc);
+    if (threadIdx.x == 0)
+        dnorm[0] = static_cast<float>(sqrt(tot)) + eps;
+}
+
+/* ---------------------------------------------------------------------- */
+/* NS input: X0 = bf16(g~ / d) both ways round                            */
+/* ---------------------------------------------------------------------- */
+/* grid (Cp / 64, Rp / 64, count) over the padded natural shape.  Natural
+ * row-major g~ (R x C) is read along its rows; the bf16 tile goes out once
+ * in the natural orientation ("copy") and once transposed.  In the wide
+ * orientation the copy is X (not transposed) or X^T (transposed matrix). */
+__global__ __launch_bounds__(kBlock) void k_muon_ns_input(const float* src, int64_t src_stride, const float* dnorm,
+                                                         int32_t dnorm_first, int64_t R, int64_t C,
+                                                         uint16_t* copy, int64_t ld_copy, int64_t s_copy,
+                                                         uint16_t* trans, int64_t ld_trans, int64_t s_trans,
+                                                         MuonGate gate)
+{
+    if (!gate_open(gate))
+        return;
+    __shared__ uint16_t tile[kTile][kTile + 2];
+    const int64_t z = blockIdx.z;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kTile;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTile;
+    const float d = dnorm[dnorm_first + z];
+    const float* __restrict__ S = src + z * src_stride;
+    const int tid = threadIdx.x;
+#pragma unroll 4
+    for (int k = 0; k < kTile * kTile / kBlock; ++k) {
+        const int e = tid + k * kBlock;
+        const int r = e / kTile, c = e % kTile;
+        const int64_t gr = r0 + r, gc = c0 + c;
+        float x = 0.0f;
+        if (gr < R && gc < C)
+            x = S[gr * C + gc] / d;
+        tile[r][c] = static_cast<uint16_t>(bf16_rne_bits(x));
+    }
+    __syncthreads();
+    uint16_t* __restrict__ Cp = copy + z * s_copy;
+    uint16_t* __restrict__ Tp = trans + z * s_trans;
+    /* 64 rows x 8 pieces of 8 bf16 (16 B) each way */
+#pragma unroll
+    for (int q = 0; q < kTile * kTile / 8 / kBlock; ++q) {
+        const int e = tid + q * kBlock;
+        const int r = e / 8, p = (e % 8) * 8;
+        u32x4_t v;
+        v.x = tile[r][p + 0] | (static_cast<uint32_t>(tile[r][p + 1]) << 16);
+        v.y = tile[r][p + 2] | (static_cast<uint32_t>(tile[r][p + 3]) << 16);
+        v.z = tile[r][p + 4] | (static_cast<uint32_t>(tile[r][p + 5]) << 16);
+        v.w = tile[r][p + 6] | (static_cast<uint32_t>(tile[r][p + 7]) << 16);
+        *reinterpret_cast<u32x4_t*>(Cp + (r0 + r) * ld_copy + c0 + p) = v;
+        u32x4_t t;
+        t.x = tile[p + 0][r] | (static_cast<uint32_t>(tile[p + 1][r]) << 16);
+        t.y = tile[p + 2][r] | (static_cast<uint32_t>(tile[p + 3][r]) << 16);
+        t.z = tile[p + 4][r] | (static_cast<uint32_t>(tile[p + 5][r]) << 16);
+        t.w = tile[p + 6][r] | (static_cast<uint32_t>(tile[p + 7][r]) << 16);
+        *reinterpret_cast<u32x4_t*>(Tp + (c0 + r) * ld_trans + r0 + p) = t;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* NS GEMM: C = P Q^T on bf16 MFMA with fused epilogues                   */
+/* ---------------------------------------------------------------------- */
+enum Epi : int {
+    kEpiGram = 0,    /* C = bf16(acc)                              A = X X^T      */
+    kEpiPoly = 1,    /* C = bf16(b * P[i][j] + c * acc)           B = b A + c A A */
+    kEpiStep = 2,    /* X = bf16(a * X + acc) in place, and X^T    X' = a X + B X */
+    kEpiUpdate = 3,  /* O = a * X + acc (fp32) -> master / param update */
+    kEpiOut = 4,     /* O = a * X + acc (fp32) -> out, natural layout */
+};
+
+struct GemmArgs {
+    const uint16_t* P;
+    const uint16_t* Q;
+    int64_t ldp, sp, ldq, sq;
+    int32_t K;
+    int32_t first;       /* matrix index of slot 0 (update epilogue) */
+    uint16_t* C;         /* gram / poly output */
+    int64_t ldc, sc;
+    uint16_t* X;         /* step / update / out: X (wide, bf16) */
+    int64_t ldx, sx;
+    uint16_t* XT;        /* step: next X^T */
+    int64_t ldxt, sxt;
+    float a, b, c;
+    int32_t transposed;  /* update / out: matrices of this batch are transposed */
+    int64_t R, Cn;       /* update / out: natural shape */
+    float* out;          /* out epilogue */
+    const TensorDesc* desc;
+    const MuonInfo* info;
+    MuonGate gate;
+};
+
+/* Position of 16-byte piece p of LDS row r: the XOR keeps the 16 (or 8)
+ * rows one fragment read touches per cycle on distinct banks. */
+__device__ __forceinline__ int lds_off(int r, int p)
+{
+    const int swz = (r & 7) ^ ((r >> 3) & 1);
+    return r * kRowBytes + ((p ^ swz) << 4);
+}
+
+__device__ __forceinline__ float bf16v(uint16_t b) { return bf16_to_f32(b); }
+
+/* Scale of the orthogonalized update, binary64 ([OPT-INFRA] §5.4 Moonlight:
+ * 0.2 * sqrt(max(A, B)); §14.6: the spectral, shape and unit-RMS bases times
+ * an extra factor, with fan_out = rows and fan_in = cols). */
+__device__ __forceinline__ double update_scale(int64_t rows, int64_t cols, const MuonUpdate& up)
+{
+    const double r = static_cast<double>(rows), c = static_cast<double>(cols);
+    double base;
+    if (up.scale_mode == HPO_MUON_SCALE_SHAPE)
+        base = sqrt(r / c > 1.0 ? r / c : 1.0);
+    else if (up.scale_mode == HPO_MUON_SCALE_UNIT_RMS)
+        base = sqrt(r / c);
+    else
+        base = sqrt(r > c ? r : c);
+    return base * up.extra_scale;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate up)
+{
+    if (!gate_open(g.gate))
+        return;
+    __shared__ __attribute__((aligned(16))) char lds[2][kStageBytes];
+    const int64_t z = blockIdx.z;
+    const int64_t row0 = static_cast<int64_t>(blockIdx.y) * kBM;
+    const int64_t col0 = static_cast<int64_t>(blockIdx.x) * kBN;
+    const uint16_t* __restrict__ P = g.P + z * g.sp + row0 * g.ldp;
+    const uint16_t* __restrict__ Q = g.Q + z * g.sq + col0 * g.ldq;
+    const int tid = threadIdx.x;
+    const int ld_piece = tid & 7, ld_row = tid >> 3;   /* loader: row ld_row + 32 k, piece ld_piece */
+    constexpr int kLoads = kBM / 32;                   /* 16-byte loads per operand per lane */
+    u32x4_t rp[kLoads], rq[kLoads];
+    auto gload = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            rp[i] = *reinterpret_cast<const u32x4_t*>(P + (ld_row + 32 * i) * g.ldp + k0 + ld_piece * 8);
+            rq[i] = *reinterpret_cast<const u32x4_t*>(Q + (ld_row + 32 * i) * g.ldq + k0 + ld_piece * 8);
+        }
+    };
+    auto lstore = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            *reinterpret_cast<u32x4_t*>(&lds[s][lds_off(ld_row + 32 * i, ld_piece)]) = rp[i];
+            *reinterpret_cast<u32x4_t*>(&lds[s][kBM * kRowBytes + lds_off(ld_row + 32 * i, ld_piece)]) = rq[i];
+        }
+    };
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = (wave >> 1) * 32 * kWaveTiles, wn = (wave & 1) * 32 * kWaveTiles;
+    const int frow = lane & 31, fhalf = lane >> 5;
+    f32x16_t acc[kWaveTiles][kWaveTiles];
+#pragma unroll
+    for (int i = 0; i < kWaveTiles; ++i)
+#pragma unroll
+        for (int j = 0; j < kWaveTiles; ++j)
+            acc[i][j] = f32x16_t{};
+    const int nk = g.K / kBK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s = kt & 1;
+        if (kt + 1 < nk)
+            gload(static_cast<int64_t>(kt + 1) * kBK);
+        const char* Ps = lds[s];
+        const char* Qs = lds[s] + kBM * kRowBytes;
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int piece = kk * 2 + fhalf;  /* lanes 0-31: k 0..7 of the slice, 32-63: k 8..15 */
+            bf16x8_t fa[kWaveTiles], fb[kWaveTiles];
+#pragma unroll
+            for (int i = 0; i < kWaveTiles; ++i)
+                fa[i] = __builtin_bit_cast(bf16x8_t,
+                                           *reinterpret_cast<const u32x4_t*>(Ps + lds_off(wm + 32 * i + frow, piece)));
+#pragma unroll
+            for (int j = 0; j < kWaveTiles; ++j)
+                fb[j] = __builtin_bit_cast(bf16x8_t,
+                                           *reinterpret_cast<const u32x4_t*>(Qs + lds_off(wn + 32 * j + frow, piece)));
+#pragma unroll
+            for (int i = 0; i < kWaveTiles; ++i)
+#pragma unroll
+                for (int j = 0; j < kWaveTiles; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk)
+            lstore(s ^ 1);
+        __syncthreads();
+    }
+
+    /* Epilogue.  acc[i][j][r] holds C[row][col] with
+     * row = wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, col = wn + 32 j + lane % 32. */
+    const int64_t lcol = lane & 31;
+    const int64_t lrow4 = 4 * (lane >> 5);
+    float k1 = 0.0f, k2 = 0.0f;
+    float* __restrict__ W = nullptr;
+    uint16_t* __restrict__ Pm = nullptr;
+    if constexpr (EPI == kEpiUpdate) {
+        const int32_t mat = g.first + static_cast<int32_t>(z);
+        const MuonInfo in = g.info[mat];
+        const double lr = up.lr[in.group], wd = up.wd[in.group];
+        k1 = static_cast<float>(1.0 - lr * wd);
+        k2 = static_cast<float>(lr * update_scale(in.rows, in.cols, up));
+        W = g.desc[mat].master;
+        Pm = up.param_dtype == HPO_PARAM_FP32 ? nullptr : static_cast<uint16_t*>(g.desc[mat].param);
+    }
+#pragma unroll
+    for (int i = 0; i < kWaveTiles; ++i) {
+#pragma unroll
+        for (int j = 0; j < kWaveTiles; ++j) {
+            const int64_t col = col0 + wn + 32 * j + lcol;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t rbase = row0 + wm + 32 * i + 8 * q + lrow4;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = acc[i][j][4 * q + e];
+                if constexpr (EPI == kEpiGram) {
+                    uint16_t* __restrict__ Cz = g.C + z * g.sc;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        Cz[(rbase + e) * g.ldc + col] = static_cast<uint16_t>(bf16_rne_bits(v[e]));
+                } else if constexpr (EPI == kEpiPoly) {
+                    uint16_t* __restrict__ Cz = g.C + z * g.sc;
+                    const uint16_t* __restrict__ Az = g.P + z * g.sp;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float a = bf16v(Az[(rbase + e) * g.ldp + col]);
+                        const float bv = g.b * a;
+                        const float cv = g.c * v[e];
+                        Cz[(rbase + e) * g.ldc + col] = static_cast<uint16_t>(bf16_rne_bits(bv + cv));
+                    }
+                } else if constexpr (EPI == kEpiStep) {
+                    uint16_t* __restrict__ Xz = g.X + z * g.sx;
+                    uint32_t bits[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint16_t* px = Xz + (rbase + e) * g.ldx + col;
+                        const float ax = g.a * bf16v(*px);
+                        bits[e] = bf16_rne_bits(ax + v[e]);
+                        *px = static_cast<uint16_t>(bits[e]);
+                    }
+                    u32x2_t t;
+                    t.x = bits[0] | (bits[1] << 16);
+                    t.y = bits[2] | (bits[3] << 16);
+                    *reinterpret_cast<u32x2_t*>(g.XT + z * g.sxt + col * g.ldxt + rbase) = t;
+                } else {
+                    const uint16_t* __restrict__ Xz = g.X + z * g.sx;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t row = rbase + e;
+                        const float ax = g.a * bf16v(Xz[row * g.ldx + col]);
+                        const float o = ax + v[e];
+                        const int64_t nr = g.transposed ? col : row;
+                        const int64_t nc = g.transposed ? row : col;
+                        if (nr < g.R && nc < g.Cn) {
+                            const int64_t idx = nr * g.Cn + nc;
+                            if constexpr (EPI == kEpiUpdate) {
+                                float w = W[idx];
+                                w = w * k1;             /* decoupled decay first ([HANDBOOK] listing) */
+                                const float u = k2 * o;
+                                w = w - u;
+                                W[idx] = w;
+                                if (Pm != nullptr)
+                                    Pm[idx] = static_cast<uint16_t>(bf16_rne_bits(w));
+                            } else {
+                                g.out[idx] = o;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <typename... Args>
+hipError_t launch3(void (*kernel)(Args...), dim3 grid, int block, hipStream_t stream, Args... args)
+{
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(block), argv, 0, stream);
+}
+
+struct Dims {
+    int64_t mp, np;
+};
+
+/* One NS step's three GEMMs on a batch. */
+hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonBatch& b, const MuonWork& w,
+                   const MuonGate& gate, float a, float bc, float cc, int cur, bool last, const MuonUpdate& up,
+                   float* out, hipStream_t stream)
+{
+    const int64_t mp = b.mp, np = b.np;
+    const uint32_t cnt = static_cast<uint32_t>(b.count);
+    GemmArgs g{};
+    g.gate = gate;
+    g.first = b.first;
+    g.desc = d_desc;
+    g.info = d_info;
+    /* A = X X^T */
+    g.P = w.X; g.ldp = np; g.sp = mp * np;
+    g.Q = w.X; g.ldq = np; g.sq = mp * np;
+    g.K = static_cast<int32_t>(np);
+    g.C = w.A; g.ldc = mp; g.sc = mp * mp;
+    hipError_t e = launch3(k_ns_gemm<kEpiGram>, dim3(mp / kBN, mp / kBM, cnt), kNsThreads, stream, g, up);
+    if (e != hipSuccess)
+        return e;
+    /* B = b A + c A A^T */
+    g.P = w.A; g.ldp = mp; g.sp = mp * mp;
+    g.Q = w.A; g.ldq = mp; g.sq = mp * mp;
+    g.K = static_cast<int32_t>(mp);
+    g.C = w.B; g.ldc = mp; g.sc = mp * mp;
+    g.b = bc; g.c = cc;
+    e = launch3(k_ns_gemm<kEpiPoly>, dim3(mp / kBN, mp / kBM, cnt), kNsThreads, stream, g, up);
+    if (e != hipSuccess)
+        return e;
+    /* X' = a X + B X  (Q = X^T, rows of X^T are columns of X) */
+    g.P = w.B; g.ldp = mp; g.sp = mp * mp;
+    g.Q = w.XT[cur]; g.ldq = mp; g.sq = np * mp;
+    g.K = static_cast<int32_t>(mp);
+    g.X = w.X; g.ldx = np; g.sx = mp * np;
+    g.XT = w.XT[cur ^ 1]; g.ldxt = mp; g.sxt = np * mp;
+    g.a = a;
+    const dim3 grid(static_cast<uint32_t>(np / kBN), static_cast<uint32_t>(mp / kBM), cnt);
+    if (!last)
+        return launch3(k_ns_gemm<kEpiStep>, grid, kNsThreads, stream, g, up);
+    g.transposed = 0;
+    g.R = b.m;
+    g.Cn = b.n;
+    if (b.transposed) {
+        g.transposed = 1;
+        g.R = b.n;
+        g.Cn = b.m;
+    }
+    if (out != nullptr) {
+        g.out = out;
+        return launch3(k_ns_gemm<kEpiOut>, grid, kNsThreads, stream, g, up);
+    }
+    return launch3(k_ns_gemm<kEpiUpdate>, grid, kNsThreads, stream, g, up);
+}
+
+}  // namespace
+
+hipError_t launch_muon_momentum(const SetView& sv, const MuonInfo* d_info, const MuonBatch& b, const MuonScalars& sc,
+                                const MuonWork& w, hipStream_t stream)
+{
+    const int64_t n = b.c1 - b.c0;
+    if (n > 0) {
+        hipError_t e;
+        const int64_t stride = b.gt_stride;
+        if (sc.form == HPO_MUON_MOMENTUM_SUM)
+            e = sc.nesterov ? launch3(k_muon_momentum<HPO_MUON_MOMENTUM_SUM, true>, dim3(n), kBlock, stream, sv, sc, b,
+                                      w.gt, stride, w.part)
+                            : launch3(k_muon_momentum<HPO_MUON_MOMENTUM_SUM, false>, dim3(n), kBlock, stream, sv, sc,
+                                      b, w.gt, stride, w.part);
+        else
+            e = sc.nesterov ? launch3(k_muon_momentum<HPO_MUON_MOMENTUM_EMA, true>, dim3(n), kBlock, stream, sv, sc, b,
+                                      w.gt, stride, w.part)
+                            : launch3(k_muon_momentum<HPO_MUON_MOMENTUM_EMA, false>, dim3(n), kBlock, stream, sv, sc,
+                                      b, w.gt, stride, w.part);
+        if (e != hipSuccess)
+            return e;
+    }
+    return launch3(k_muon_norm, dim3(static_cast<uint32_t>(b.count)), kBlock, stream, d_info, sc.gate, b.first,
+                   static_cast<const double*>(w.part), sc.eps, w.dnorm);
+}
+
+hipError_t launch_muon_ns_input(const MuonBatch& b, const MuonWork& w, const MuonGate& gate, hipStream_t stream)
+{
+    const int64_t R = b.transposed ? b.n : b.m;
+    const int64_t C = b.transposed ? b.m : b.n;
+    const int64_t Rp = b.transposed ? b.np : b.mp;
+    const int64_t Cp = b.transposed ? b.mp : b.np;
+    uint16_t* copy = b.transposed ? w.XT[0] : w.X;
+    uint16_t* trans = b.transposed ? w.X : w.XT[0];
+    const int64_t ld_copy = b.transposed ? b.mp : b.np;
+    const int64_t ld_trans = b.transposed ? b.np : b.mp;
+    const int64_t s = b.mp * b.np;
+    const dim3 grid(static_cast<uint32_t>(Cp / kTile), static_cast<uint32_t>(Rp / kTile),
+                    static_cast<uint32_t>(b.count));
+    return launch3(k_muon_ns_input, grid, kBlock, stream, static_cast<const float*>(w.gt), b.gt_stride,
+                   static_cast<const float*>(w.dnorm), b.first, R, C, copy, ld_copy, s, trans, ld_trans, s, gate);
+}
+
+hipError_t launch_ns_input_from(const float* G, float eps, const MuonBatch& b, const MuonWork& w, hipStream_t stream)
+{
+    const int64_t n = b.m * b.n;
+    constexpr int64_t kPer = 1 << 16;
+    const int64_t blocks = n > 0 ? (n + kPer - 1) / kPer : 1;
+    hipError_t e = launch3(k_sumsq_rows, dim3(static_cast<uint32_t>(blocks)), kBlock, stream, G, n, kPer, w.part);
+    if (e != hipSuccess)
+        return e;
+    e = launch3(k_sumsq_fold, dim3(1), kBlock, stream, static_cast<const double*>(w.part),
+                static_cast<int32_t>(blocks), eps, w.dnorm);
+    if (e != hipSuccess)
+        return e;
+    MuonWork w2 = w;
+    w2.gt = const_cast<float*>(G);
+    MuonGate open{};
+    return launch_muon_ns_input(b, w2, open, stream);
+}
+
+hipError_t launch_muon_ns(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonBatch& b, const MuonWork& w,
+                          const MuonGate& gate, int32_t steps, const float* coeffs, const MuonUpdate& up, float* out,
+                          hipStream_t stream)
+{
+    int cur = 0;
+    for (int32_t s = 0; s < steps; ++s) {
+        const bool last = s + 1 == steps;
+        hipError_t e = ns_step(d_desc, d_info, b, w, gate, coeffs[3 * s], coeffs[3 * s + 1], coeffs[3 * s + 2], cur,
+                               last, up, out, stream);
+        if (e != hipSuccess)
+            return e;
+        cur ^= 1;
+    }
+    return hipSuccess;
+}
+
+}  // namespace hpo

@@ -1,0 +1,77 @@
+/*
+ * hpo_set.h -- the set object and the host helpers shared by libhpo's two
+ * host files (hpo_api.cpp: sets and the AdamW step; hpo_muon_api.cpp: Muon
+ * sets, NS and the chained step).  Not part of the public ABI.
+ */
+#ifndef HPO_SET_H
+#define HPO_SET_H
+
+#include <string>
+#include <vector>
+
+#include "hpo_impl.h"
+
+/* Muon-only part of a set: per-matrix facts, the batch plan and the
+ * workspace (one device allocation sized for the largest batch). */
+struct hpo_muon_part {
+    std::vector<hpo::MuonInfo> info;       /* internal (batched) order */
+    std::vector<hpo::MuonBatch> batches;
+    hpo::MuonInfo* d_info = nullptr;
+    char* d_ws = nullptr;                  /* batch buffers, see muon_work() */
+    int64_t ws_bytes = 0;
+    float* d_dnorm = nullptr;              /* one per matrix */
+    double* d_part = nullptr;              /* one per chunk */
+};
+
+struct hpo_set_ {
+    hpo::SetView view{};
+    int32_t kind = HPO_SET_ADAM;
+    int32_t n_tensors = 0;
+    int32_t param_dtype = 0;
+    int32_t is_flat = 0;
+    int32_t device = 0;
+    int32_t max_group = 0;   /* largest group index in the set */
+    int32_t n_vector = 0;
+    int64_t numel = 0;
+    int64_t n_chunks = 0;
+    int32_t grad_group = 1;  /* chunks per grad-pass workgroup */
+    int64_t n_parts = 0;     /* grad-pass workgroups = reduction partials */
+    int64_t device_bytes = 0;
+    hpo::TensorDesc* d_tensors = nullptr;
+    hpo::Chunk* d_chunks = nullptr;
+    double* d_part_sum = nullptr;
+    int32_t* d_part_flag = nullptr;
+    hpo_muon_part* muon = nullptr;
+};
+
+namespace hpo_host {
+
+hpo_status fail(hpo_status st, const char* fmt, ...);
+hpo_status hip_fail(hipError_t e, const char* what);
+hpo_status ok();
+bool aligned(const void* p, uintptr_t a);
+bool is_finite(double x);
+int64_t count_chunks(const int64_t* numel, int32_t n, int64_t ch);
+int32_t choose_chunk(const int64_t* numel, int32_t n);
+void build_chunks(const int64_t* numel, int32_t n, int64_t ch, std::vector<hpo::Chunk>& out);
+hpo_status alloc_partials(hpo_set s);
+void free_set(hpo_set s);
+hpo_status check_set(hpo_set s);
+hipStream_t as_stream(void* stream);
+double* stage_sum(hpo_set s);
+int32_t* stage_flag(hpo_set s);
+hpo::Partials partials_of(hpo_set s);
+
+/* hpo_muon_api.cpp */
+void free_muon(hpo_muon_part* m);
+/* Validates a Muon configuration and the groups against a Muon set. */
+hpo_status check_muon_step(hpo_set s, const hpo_muon_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                           double max_norm);
+/* Enqueues the Muon update of every batch of s behind `gate`. */
+hpo_status muon_enqueue(hpo_set s, const hpo_muon_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                        const hpo::MuonGate& gate, float inv_scale, double max_norm, const float* d_norm,
+                        hipStream_t stream);
+
+}  // namespace hpo_host
+
+#endif /* HPO_SET_H */

@@ -45,7 +45,24 @@ class hpo_set_info_t(ctypes.Structure):
                 ("numel", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("device_bytes", ctypes.c_int64), ("device", ctypes.c_int32),
                 ("n_vector", ctypes.c_int32), ("grad_group", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("n_grad_parts", ctypes.c_int64)]
+                ("kind", ctypes.c_int32), ("n_grad_parts", ctypes.c_int64)]
+
+
+HPO_SET_ADAM = 0
+HPO_SET_MUON = 1
+HPO_MUON_MOMENTUM_SUM = 0
+HPO_MUON_MOMENTUM_EMA = 1
+HPO_MUON_SCALE_SPECTRAL = 0
+HPO_MUON_SCALE_SHAPE = 1
+HPO_MUON_SCALE_UNIT_RMS = 2
+HPO_NS_MAX_STEPS = 16
+HPO_MUON_DEFAULT_WORKSPACE = 4 << 30
+
+
+class hpo_muon_cfg(ctypes.Structure):
+    _fields_ = [("momentum", ctypes.c_double), ("nesterov", ctypes.c_int32), ("momentum_form", ctypes.c_int32),
+                ("ns_steps", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("extra_scale", ctypes.c_double),
+                ("ns_eps", ctypes.c_double), ("ns_coeffs", ctypes.POINTER(ctypes.c_double))]
 
 
 class hpo_scaler_state(ctypes.Structure):
@@ -88,6 +105,16 @@ SIGNATURES = {
     "hpo_scaler_state_init": (_I32, [_P, ctypes.c_float, _I32, _I64, _P]),
     "hpo_step_device": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32, ctypes.c_double,
                                ctypes.POINTER(hpo_scaler_cfg), _P, _I64, _I32, _P]),
+    "hpo_muon_set_create": (_I32, [ctypes.POINTER(_P), _I32, _I32, _PP, _PP, _PP, _PP, ctypes.POINTER(_I64),
+                                   ctypes.POINTER(_I64), ctypes.POINTER(_I32), _I64, _P]),
+    "hpo_muon_step": (_I32, [_P, ctypes.POINTER(hpo_muon_cfg), ctypes.POINTER(hpo_group), _I32, ctypes.c_float,
+                             ctypes.c_double, _P, _P, _P]),
+    "hpo_grad_global_norm_sets": (_I32, [ctypes.POINTER(_P), _I32, ctypes.c_float, _P, _P, _P]),
+    "hpo_step_device_chain": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32, _P,
+                                     ctypes.POINTER(hpo_muon_cfg), ctypes.POINTER(hpo_group), _I32, ctypes.c_double,
+                                     ctypes.POINTER(hpo_scaler_cfg), _P, _I64, _I32, _P]),
+    "hpo_newton_schulz": (_I32, [_P, _I64, _I64, ctypes.POINTER(hpo_muon_cfg), _P, _P, _I64, _P]),
+    "hpo_newton_schulz_workspace": (_I32, [_I64, _I64, ctypes.POINTER(_I64)]),
     "hpo_plan": (_I32, [_I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32), ctypes.POINTER(_I64),
                         ctypes.POINTER(_I64)]),
     "hpo_plan_chunks": (_I32, [_I32, ctypes.POINTER(_I64), _I64, ctypes.POINTER(_I32),
@@ -362,6 +389,116 @@ def hpo_step_device(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int
 
 def hpo_copy_main_to_model(s: HpoSet, stream=None) -> None:
     _check(load().hpo_copy_main_to_model(s.handle, _stream(stream)), "hpo_copy_main_to_model")
+
+
+# ---------------------------------------------------------------------------
+# Muon
+# ---------------------------------------------------------------------------
+def make_muon_cfg(momentum=0.95, nesterov=True, momentum_form=HPO_MUON_MOMENTUM_SUM, ns_steps=5,
+                  scale_mode=HPO_MUON_SCALE_SPECTRAL, extra_scale=0.2, ns_eps=1e-7, ns_coeffs=None) -> hpo_muon_cfg:
+    """Defaults: the handbook's Muon (Nesterov, sum form, 5 steps of the
+    original quintic) with Moonlight's 0.2 * sqrt(max(A, B)) update scale."""
+    cfg = hpo_muon_cfg(momentum=momentum, nesterov=int(bool(nesterov)), momentum_form=momentum_form,
+                       ns_steps=ns_steps, scale_mode=scale_mode, extra_scale=extra_scale, ns_eps=ns_eps)
+    if ns_coeffs is not None:
+        flat = [float(x) for c in ns_coeffs for x in c]
+        if len(flat) != 3 * ns_steps:
+            raise ValueError("ns_coeffs needs one (a, b, c) per step")
+        cfg._coeffs = (ctypes.c_double * len(flat))(*flat)  # kept alive with the struct
+        cfg.ns_coeffs = ctypes.cast(cfg._coeffs, ctypes.POINTER(ctypes.c_double))
+    return cfg
+
+
+def hpo_muon_set_create(params: Sequence[Optional[torch.Tensor]], main_params: Sequence[torch.Tensor],
+                        main_grads: Sequence[torch.Tensor], momenta: Sequence[torch.Tensor],
+                        group_index: Optional[Sequence[int]] = None, workspace_bytes: int = 0,
+                        stream=None) -> HpoSet:
+    """A Muon set over 2-D matrices (each tensor's shape gives rows x cols)."""
+    n = len(main_params)
+    if not (len(main_grads) == len(momenta) == n):
+        raise ValueError("all per-matrix lists must have the same length")
+    if params is None:
+        params = [None] * n
+    if len(params) != n:
+        raise ValueError("params has the wrong length")
+    first = next((p for p in params if p is not None), None)
+    param_dtype = HPO_PARAM_FP32 if first is None else param_dtype_code(first.dtype)
+    rows, cols = [], []
+    for i in range(n):
+        if main_params[i].dim() != 2:
+            raise ValueError(f"main_params[{i}] is not a matrix")
+        for what, lst in (("main_params", main_params), ("main_grads", main_grads), ("momenta", momenta)):
+            _require(lst[i], torch.float32, what, i)
+            if tuple(lst[i].shape) != tuple(main_params[i].shape):
+                raise ValueError(f"{what}[{i}] has shape {tuple(lst[i].shape)}, main_params[{i}] "
+                                 f"{tuple(main_params[i].shape)}")
+        if params[i] is not None and (not params[i].is_contiguous()
+                                      or tuple(params[i].shape) != tuple(main_params[i].shape)):
+            raise ValueError(f"params[{i}] must be contiguous with main_params[{i}]'s shape")
+        rows.append(main_params[i].shape[0])
+        cols.append(main_params[i].shape[1])
+    arr = lambda ts: (ctypes.c_void_p * max(n, 1))(*[(t.data_ptr() if t is not None else 0) for t in ts])
+    c_rows = (ctypes.c_int64 * max(n, 1))(*rows)
+    c_cols = (ctypes.c_int64 * max(n, 1))(*cols)
+    c_groups = None
+    if group_index is not None:
+        if len(group_index) != n:
+            raise ValueError("group_index has the wrong length")
+        c_groups = (ctypes.c_int32 * max(n, 1))(*group_index)
+    out = ctypes.c_void_p()
+    st = load().hpo_muon_set_create(ctypes.byref(out), n, param_dtype, arr(params), arr(main_params),
+                                    arr(main_grads), arr(momenta), c_rows, c_cols, c_groups, workspace_bytes,
+                                    _stream(stream))
+    _check(st, "hpo_muon_set_create")
+    return HpoSet(out, (list(params), list(main_params), list(main_grads), list(momenta)))
+
+
+def hpo_muon_step(s: HpoSet, cfg: hpo_muon_cfg, groups, n_groups: Optional[int], inv_scale: float = 1.0,
+                  max_norm: float = 0.0, d_norm=None, d_found_inf=None, stream=None) -> None:
+    if not isinstance(groups, ctypes.Array):
+        groups, n_groups = make_groups(groups)
+    _check(load().hpo_muon_step(s.handle, ctypes.byref(cfg), groups, n_groups, inv_scale, max_norm, _ptr(d_norm),
+                                _ptr(d_found_inf), _stream(stream)), "hpo_muon_step")
+
+
+def hpo_grad_global_norm_sets(sets: Sequence[HpoSet], inv_scale: float, d_norm, d_found_inf=None,
+                              stream=None) -> None:
+    handles = (ctypes.c_void_p * max(len(sets), 1))(*[x.handle for x in sets])
+    _check(load().hpo_grad_global_norm_sets(handles, len(sets), inv_scale, _ptr(d_norm), _ptr(d_found_inf),
+                                            _stream(stream)), "hpo_grad_global_norm_sets")
+
+
+def hpo_step_device_chain(adam_set: Optional[HpoSet], cfg: Optional[hpo_adam_cfg], groups,
+                          muon_set: Optional[HpoSet], mcfg: Optional[hpo_muon_cfg], muon_groups, max_norm: float,
+                          scfg: hpo_scaler_cfg, d_state, t_first: int, window: int, stream=None) -> None:
+    g, ng = make_groups(groups) if groups else (None, 0)
+    mg, nmg = make_groups(muon_groups) if muon_groups else (None, 0)
+    _check(load().hpo_step_device_chain(adam_set.handle if adam_set else None,
+                                        ctypes.byref(cfg) if cfg is not None else None, g, ng,
+                                        muon_set.handle if muon_set else None,
+                                        ctypes.byref(mcfg) if mcfg is not None else None, mg, nmg, max_norm,
+                                        ctypes.byref(scfg), _ptr(d_state), t_first, window, _stream(stream)),
+           "hpo_step_device_chain")
+
+
+def hpo_newton_schulz_workspace(rows: int, cols: int) -> int:
+    out = ctypes.c_int64()
+    _check(load().hpo_newton_schulz_workspace(rows, cols, ctypes.byref(out)), "hpo_newton_schulz_workspace")
+    return out.value
+
+
+def hpo_newton_schulz(G: torch.Tensor, out: torch.Tensor, cfg: hpo_muon_cfg, workspace: torch.Tensor,
+                      stream=None) -> None:
+    """O = NS(G) on the device: G and out fp32 (rows, cols) contiguous; the
+    workspace a uint8 device tensor of at least hpo_newton_schulz_workspace bytes."""
+    for what, t in (("G", G), ("out", out)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{what} must be a contiguous fp32 matrix")
+    if tuple(out.shape) != tuple(G.shape):
+        raise ValueError("out must have G's shape")
+    _check(load().hpo_newton_schulz(_ptr(G), G.shape[0], G.shape[1], ctypes.byref(cfg), _ptr(out),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "hpo_newton_schulz")
 
 
 def hpo_plan(numel: Sequence[int]):

@@ -304,3 +304,51 @@ def fill_grads_(bufs: Buffers, k: int) -> None:
     if w.inf_step is not None and k == w.inf_step:
         ti, e = inf_position(w)
         bufs.grad[bufs.offs[ti] + e] = float("inf")
+
+
+# ---------------------------------------------------------------------------
+# Muon workloads
+# ---------------------------------------------------------------------------
+# Shapes of the small Muon parity set: tall and wide matrices (transposed and
+# not), square, a shape class of two (one batch of two), vectors as 1 x n and
+# n x 1 matrices, an empty matrix, sizes that are not multiples of the 256
+# padding, and one wider than a single GEMM tile in both directions.
+MUON_PARITY_SHAPES = [(128, 384), (384, 128), (200, 200), (1, 64), (64, 1), (0, 5), (300, 700), (300, 700),
+                      (37, 129), (520, 260)]
+
+
+def seeded_matrix(shape, seed: int, std: float = 1.0) -> np.ndarray:
+    """fp32 N(0, std) matrix from torch's CPU generator seeded with seed."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(int(np.prod(shape)) if len(shape) else 1, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.numpy().reshape(shape)
+
+
+def handbook_ns_matrix(seed: int = 2024) -> np.ndarray:
+    """256 x 1024 fp32 G = U diag(S) V^T with orthonormal U, V (QR of seeded
+    Gaussians) and S = 256 values log-spaced from 1 to 0.01: the input of the
+    Newton-Schulz demonstration on "优化器：AdamW、Muon 与分布式优化器" (Muon
+    section).  Returns (G, V) -- V's first columns are the largest directions."""
+    rng = np.random.default_rng(seed)
+    U, R = np.linalg.qr(rng.standard_normal((256, 256)))
+    U = U * np.sign(np.diag(R))
+    V, R = np.linalg.qr(rng.standard_normal((1024, 256)))
+    V = V * np.sign(np.diag(R))
+    S = np.logspace(0, -2, 256)
+    return ((U * S) @ V.T).astype(np.float32), V
+
+
+def llama8b_muon_split():
+    """Route the Llama-8B-shaped parameters the way the pages do
+    ("02 · Optimizer：算法与 infra" §5.5, §14.2): hidden 2-D matrices to
+    Muon; embedding, output head and every 1-D parameter to AdamW.
+    Returns (adam [(name, shape)], muon [(name, shape)])."""
+    adam, muon = [], []
+    for name, shape in llama8b_shapes():
+        if len(shape) == 2 and name not in ("embed", "lm_head"):
+            muon.append((name, shape))
+        else:
+            adam.append((name, shape))
+    return adam, muon

@@ -119,6 +119,13 @@ def _exact_matmul_f32(P: np.ndarray, Q: np.ndarray) -> np.ndarray:
     return (P.astype(np.float64) @ Q.astype(np.float64)).astype(F32)
 
 
+def _f32_matmul(P: np.ndarray, Q: np.ndarray) -> np.ndarray:
+    """The same product with fp32 accumulation in the BLAS's own order: a
+    second valid evaluation of the bf16 reading, for sizing how much the
+    accumulation order alone moves the result."""
+    return np.asarray(P, dtype=F32) @ np.asarray(Q, dtype=F32)
+
+
 def frobenius_norm32(x32: np.ndarray) -> float:
     """fp32(sqrt(sum of squares in binary64)), the squares exact."""
     x = np.asarray(x32, dtype=np.float64).ravel()
@@ -136,19 +143,22 @@ def ns_input_bf16(Gt32: np.ndarray, eps: float = NS_EPS) -> np.ndarray:
     return _bf16_values(np.ascontiguousarray(X))
 
 
-def newton_schulz_bf16(Gt32: np.ndarray, steps: int = 5, coeffs=None, eps: float = NS_EPS) -> np.ndarray:
+def newton_schulz_bf16(Gt32: np.ndarray, steps: int = 5, coeffs=None, eps: float = NS_EPS,
+                       acc: str = "exact") -> np.ndarray:
     """The pages' bf16 NS (module docstring); returns fp32 O in the input's
-    orientation."""
+    orientation.  acc="exact": each product sum formed exactly and rounded
+    once (the reference); acc="f32": summed in fp32 by the BLAS instead."""
     Gt32 = np.asarray(Gt32, dtype=F32)
     transposed = Gt32.shape[0] > Gt32.shape[1]
     X = ns_input_bf16(Gt32, eps)
     cs = _coeffs(steps, coeffs)
+    mm = _exact_matmul_f32 if acc == "exact" else _f32_matmul
     for k, (a, b, c) in enumerate(cs):
         a32, b32, c32 = F32(a), F32(b), F32(c)
-        A = _bf16_values(_exact_matmul_f32(X, X.T))
-        AA = _exact_matmul_f32(A, A)
+        A = _bf16_values(mm(X, X.T))
+        AA = mm(A, A)
         B = _bf16_values((b32 * A).astype(F32) + (c32 * AA).astype(F32))
-        BX = _exact_matmul_f32(B, X)
+        BX = mm(B, X)
         Xn = ((a32 * X).astype(F32) + BX).astype(F32)
         X = Xn if k == len(cs) - 1 else _bf16_values(Xn)
     if steps == 0:

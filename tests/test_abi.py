@@ -30,13 +30,13 @@ def _declared():
 
 def test_exports_every_declared_symbol(H):
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 22
     lib = H.load()
     for n in names:
         assert hasattr(lib, n), n
         assert n in H.SIGNATURES, f"binding lacks {n}"
     assert set(H.SIGNATURES) == set(names)
-    assert H.hpo_abi_version() == 1
+    assert H.hpo_abi_version() == 2
 
 
 def test_struct_layouts(H):
@@ -45,6 +45,7 @@ def test_struct_layouts(H):
     assert ctypes.sizeof(H.hpo_set_info_t) == 64
     assert ctypes.sizeof(H.hpo_adam_cfg) == 32 and ctypes.sizeof(H.hpo_group) == 16
     assert ctypes.sizeof(H.hpo_scaler_cfg) == 32
+    assert ctypes.sizeof(H.hpo_muon_cfg) == 48
 
 
 def test_device_step_validation(H):
@@ -200,3 +201,73 @@ def test_llama_and_ragged_plans(H):
     small = sum(1 for n in r.numels if n < 100) / r.n_tensors
     assert 0.25 < small < 0.35  # log-uniform sizes: about 30% below 100 elements
     assert 4.5e9 < r.numel < 6.5e9
+
+
+def _muon(H, shapes, pdt=0, ptrs=None, groups=None, ws=0):
+    L = H.load()
+    n = len(shapes)
+    base = ptrs or [0x100000 * (k + 1) for k in range(4)]
+    P = ctypes.c_void_p * max(n, 1)
+    arrs = [P(*[b + 0x10000 * i for i in range(n)]) for b in base]
+    rows = (ctypes.c_int64 * max(n, 1))(*[r for r, _ in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[c for _, c in shapes])
+    g = (ctypes.c_int32 * max(n, 1))(*groups) if groups else None
+    out = ctypes.c_void_p()
+    st = L.hpo_muon_set_create(ctypes.byref(out), n, pdt, *arrs, rows, cols, g, ws, None)
+    return st, H.hpo_last_error()
+
+
+def test_muon_set_validation(H):
+    """Muon sets: fp16 params are refused ([OPT-INFRA] §14.3), so are bf16
+    moments flags, bad shapes, groups and unaligned pointers -- all before
+    any device call."""
+    st, msg = _muon(H, [(4, 8)], pdt=2)
+    assert st == H.HPO_EDTYPE and "fp16" in msg
+    st, msg = _muon(H, [(4, 8)], pdt=0x100)
+    assert st == H.HPO_EDTYPE
+    st, msg = _muon(H, [(4, -8)])
+    assert st == H.HPO_EINVAL and "negative" in msg
+    st, msg = _muon(H, [(4, 8)], groups=[16])
+    assert st == H.HPO_EINVAL and "group_index[0]" in msg
+    st, msg = _muon(H, [(4, 8)], ptrs=[0x100000, 0x200008, 0x300000, 0x400000])
+    assert st == H.HPO_EINVAL and "16-byte" in msg
+    st, msg = _muon(H, [(4, 8)], pdt=1, ptrs=[0x900000, 0x200000, 0x300000, 0x400000])
+    assert st == H.HPO_EINVAL and "own master" in msg
+    st, msg = _muon(H, [(1 << 21, 1 << 21)])
+    assert st == H.HPO_EINVAL and "too large" in msg
+    assert H.load().hpo_muon_set_create(None, 0, 0, None, None, None, None, None, None, None, 0, None) == H.HPO_EINVAL
+    if not torch.cuda.is_available():
+        st, msg = _muon(H, [(4, 8), (0, 3)])
+        assert st == H.HPO_EHIP and "hipGetDevice" in msg
+
+
+def test_muon_step_and_ns_validation(H):
+    L = H.load()
+    cfg = H.make_muon_cfg()
+    groups, n = H.make_groups([(1e-3, 0.1)])
+    assert L.hpo_muon_step(None, ctypes.byref(cfg), groups, n, 1.0, 0.0, None, None, None) == H.HPO_EINVAL
+    ws = ctypes.c_int64()
+    assert L.hpo_newton_schulz_workspace(-1, 4, ctypes.byref(ws)) == H.HPO_EINVAL
+    assert L.hpo_newton_schulz_workspace(0, 4, ctypes.byref(ws)) == H.HPO_OK and ws.value == 0
+    # one 300 x 1000 matrix: partials + norm + bf16 X, two X^T (256-padded) and two Gram matrices
+    assert L.hpo_newton_schulz_workspace(300, 1000, ctypes.byref(ws)) == H.HPO_OK
+    mp, np_ = 512, 1024
+    assert ws.value == 256 + 256 + 2 * (3 * mp * np_ + 2 * mp * mp)
+    assert L.hpo_newton_schulz_workspace(1000, 300, ctypes.byref(ws)) == H.HPO_OK
+    assert ws.value == 256 + 256 + 2 * (3 * mp * np_ + 2 * mp * mp)
+    bad = H.make_muon_cfg(ns_steps=0)
+    assert L.hpo_newton_schulz(ctypes.c_void_p(0x1000), 4, 4, ctypes.byref(bad), ctypes.c_void_p(0x2000),
+                               ctypes.c_void_p(0x3000), 1 << 20, None) == H.HPO_EINVAL
+    ok = H.make_muon_cfg()
+    assert L.hpo_newton_schulz(ctypes.c_void_p(0x1000), 4, 4, ctypes.byref(ok), ctypes.c_void_p(0x2000),
+                               ctypes.c_void_p(0x3000), 16, None) == H.HPO_EINVAL
+    assert "workspace" in H.hpo_last_error()
+    assert L.hpo_newton_schulz(ctypes.c_void_p(0x1000), 4, 4, ctypes.byref(ok), ctypes.c_void_p(0x2000),
+                               ctypes.c_void_p(0x3010), 1 << 24, None) == H.HPO_EINVAL
+    assert "256-byte" in H.hpo_last_error()
+    with pytest.raises(ValueError):
+        H.make_muon_cfg(ns_steps=2, ns_coeffs=[(1, 2, 3)])
+    scfg = H.make_scaler_cfg()
+    assert L.hpo_step_device_chain(None, None, None, 0, None, None, None, 0, 1.0, ctypes.byref(scfg),
+                                   ctypes.c_void_p(0x1000), 1, 1, None) == H.HPO_EINVAL
+    assert L.hpo_grad_global_norm_sets(None, 1, 1.0, ctypes.c_void_p(0x1000), None, None) == H.HPO_EINVAL
