@@ -87,7 +87,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zero_shard",
-                    choices=["zero_shard", "zero_shard_ranges", "llama8b", "ragged", "two_matrices"])
+                    choices=["zero_shard", "zero_shard_ranges", "llama8b", "ragged", "two_matrices",
+                             "llama8b_muon"])
+    ap.add_argument("--muon-workspace", type=int, default=0,
+                    help="Muon set workspace cap in bytes (0: the library default)")
     ap.add_argument("--numel", type=int, default=None, help="override the flat shard's size")
     ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"],
                     help="exp_avg / exp_avg_sq storage of the flat shard")
@@ -197,6 +200,9 @@ def main():
         return
     dev = torch.device("cuda", 0)
     hpo.load()
+    if args.workload == "llama8b_muon":
+        main_muon(args, dev)
+        return
     w = workload(args)
     N = w.numel
     log(f"workload {w.name}: {N} elements, {w.n_tensors} tensors; allocating {N * 18 / 1e9:.1f} GB")
@@ -308,6 +314,150 @@ def main():
     if sample is not None:
         log(f"cpu baseline on {sample[0].size} elements")
         out["cpu_baseline"] = cpu_baseline(sample, w, args.cpu_steps)
+    print(json.dumps(out), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MUON_METRIC = "G params/s per full chained AdamW + Muon step (bf16 MFMA Newton-Schulz)"
+
+
+def muon_cpu_baseline(matrices, steps=1):
+    """The Muon oracle (numpy, bf16 reading with exact sums; BLAS-threaded)
+    on one matrix of the workload: its momentum, NS and update."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import oracle.muon as mu
+    from mixed_precision_optimizer_amd import inputs
+    oracle.lib()
+    name, (r, c), std = next(m for m in matrices if m[0].endswith(".k"))
+    W = inputs.seeded_matrix((r, c), 5, 1.0)
+    G = inputs.seeded_matrix((r, c), 6, std)
+    T = mu.OMatrix.fresh(W)
+    times = []
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        mu.muon_matrix_step(T, G, mu.MuonCfg(), 1e-3, 0.1, 1.0, False, 1.0, "bf16")
+        times.append(time.perf_counter() - t0)
+    ms = 1e3 * statistics.median(times)
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": round(r * c / (ms * 1e-3) / 1e9, 5), "unit": "G params/s", "cores": threads, "kind": "oracle",
+            "sample": f"one {r}x{c} Muon matrix ({name}) of the same workload: momentum, 5-step bf16-reading NS "
+                      f"(numpy binary64 matmuls over bf16 values, {threads} BLAS threads), decayed scaled update, "
+                      f"bf16 write-back; median of {steps}", "ms_per_step": round(ms, 2)}
+
+
+def main_muon(args, dev):
+    """Llama-8B-shaped chained step: AdamW on the embedding, output head and
+    1-D gains (1.05e9 params), Muon on the 224 hidden matrices (6.98e9),
+    device-resident (hpo_step_device_chain), constant loss scale 1, clip 1.0."""
+    import torch
+
+    from mixed_precision_optimizer_amd import hpo, inputs
+    wa, mats = inputs.llama8b_chain()
+    n_adam = wa.numel
+    n_muon = sum(r * c for _, (r, c), _ in mats)
+    N = n_adam + n_muon
+    log(f"chain: AdamW {n_adam} params in {wa.n_tensors} tensors, Muon {n_muon} in {len(mats)} matrices; "
+        f"allocating {(18 * n_adam + 14 * n_muon) / 1e9:.1f} GB")
+    bufs = inputs.allocate(wa, dev)
+    inputs.fill_grads_(bufs, 1)
+    aset = make_set(bufs)
+    mb = inputs.allocate_muon(mats, dev)
+    mset = hpo.hpo_muon_set_create(mb.views(mb.param), mb.views(mb.master), mb.views(mb.grad),
+                                   mb.views(mb.momentum), workspace_bytes=args.muon_workspace)
+    torch.cuda.synchronize()
+    log(f"Muon set: {mset.info().device_bytes / 1e9:.2f} GB of tables and NS workspace")
+    acfg = hpo.make_cfg(wa.beta1, wa.beta2, wa.eps, wa.mode)
+    mcfg = hpo.make_muon_cfg()
+    groups = wa.groups()
+    mgroups = [(wa.lr, wa.weight_decay)]
+    scfg = hpo.make_scaler_cfg(dynamic=False)
+    stream = torch.cuda.current_stream()
+    d_state = hpo.new_scaler_state(dev)
+    hpo.hpo_scaler_state_init(d_state, 1.0, 1, 0, stream)
+    st = {"t_first": 1, "window": 0}
+
+    def step():
+        if st["window"] == hpo.HPO_MAX_WINDOW:
+            s = hpo.read_scaler_state(d_state)
+            if s.error:
+                raise RuntimeError("device step window overrun")
+            st["t_first"], st["window"] = s.applied_steps + 1, 0
+        st["window"] += 1
+        hpo.hpo_step_device_chain(aset, acfg, groups, mset, mcfg, mgroups, wa.max_norm, scfg, d_state,
+                                  st["t_first"], st["window"], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    s = hpo.read_scaler_state(d_state)
+    if s.error or s.applied_steps != args.warmup + args.steps:
+        raise RuntimeError(f"unexpected device state: applied {s.applied_steps}, error {s.error}")
+    log(f"chained step {wall_ms:.2f} ms (events {ev_ms:.2f} ms), norm {s.grad_norm:.5g}, applied {s.applied_steps}")
+    # live per-launch timing of the Muon kernels over a few more steps
+    hpo.hpo_muon_profile_enable(mset, True)
+    n_prof = max(2, min(5, args.steps))
+    torch.cuda.synchronize()
+    for _ in range(n_prof):
+        step()
+    prof = hpo.hpo_muon_profile_read(mset)
+    hpo.hpo_muon_profile_enable(mset, False)
+    kernels = {}
+    for k, v in prof.items():
+        ms = v["ms"] / n_prof
+        ent = {"ms_per_step": round(ms, 4), "launches_per_step": v["launches"] // n_prof}
+        if v["flops"]:
+            ent["TFLOPs"] = round(v["flops"] / n_prof / (ms * 1e-3) / 1e12, 1)
+        if v["bytes"]:
+            ent["GBps"] = round(v["bytes"] / n_prof / (ms * 1e-3) / 1e9, 1)
+        kernels[k] = ent
+    gemm_ms = sum(prof[k]["ms"] for k in ("gram", "poly", "step", "update")) / n_prof
+    gemm_fl = sum(prof[k]["flops"] for k in ("gram", "poly", "step", "update")) / n_prof
+    dom = max(("gram", "poly", "step", "update"), key=lambda k: prof[k]["ms"])
+    dom_ms = prof[dom]["ms"] / max(1, prof[dom]["launches"])
+    dom_fl = prof[dom]["flops"] / max(1, prof[dom]["launches"])
+    achieved = dom_fl / (dom_ms * 1e-3) / 1e12
+    log(f"NS GEMMs {gemm_ms:.2f} ms per step = {gemm_fl / (gemm_ms * 1e-3) / 1e12:.1f} TFLOP/s; "
+        f"dominant {dom}: {dom_ms:.3f} ms per launch, {achieved:.1f} TFLOP/s")
+    out = {
+        "metric": MUON_METRIC,
+        "value": round(N / (wall_ms * 1e-3) / 1e9, 3),
+        "unit": "G params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 (NS matmuls), f32 (momentum, masters, AdamW)",
+        "data": "synthetic",
+        "config": {"workload": "llama8b_chain_adamw_muon", "params": N, "adamw_params": n_adam,
+                   "muon_params": n_muon, "muon_matrices": len(mats), "ns_steps": 5, "max_norm": wa.max_norm,
+                   "lr": wa.lr, "weight_decay": wa.weight_decay, "loss_scale": 1.0,
+                   "parallelism": "one GPU (whole model, no data-parallel sharding)"},
+        "kernels": kernels,
+        "ns_gemms": {"ms_per_step": round(gemm_ms, 3), "TFLOPs": round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1),
+                     "flops_per_step": gemm_fl},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": f"k_ns_gemm ({dom}), algorithmic flops per launch {dom_fl:.4g}"},
+    }
+    aset.close()
+    mset.close()
+    if args.cpu_sample > 0:
+        out["cpu_baseline"] = muon_cpu_baseline(mats, args.cpu_steps)
     print(json.dumps(out), flush=True)
 
 

@@ -410,6 +410,36 @@ hpo_status hpo_newton_schulz(const float* d_G, int64_t rows, int64_t cols, const
                              void* d_workspace, int64_t workspace_bytes, void* stream);
 hpo_status hpo_newton_schulz_workspace(int64_t rows, int64_t cols, int64_t* out_bytes);
 
+/* Opt-in timing of a Muon set's launches (for measurement, not for the
+ * hot loop): while enabled, every Muon update of the set (hpo_muon_step,
+ * hpo_step_device_chain) records HIP events on its stream around each launch
+ * and notes the launch's algorithmic work.  hpo_muon_profile_read waits for
+ * the recorded events, returns the totals since the last read (or since
+ * enabling) and clears them.  Categories: */
+typedef enum {
+    HPO_MUON_PROF_MOMENTUM = 0,  /* momentum + Nesterov gradient pass and the per-matrix norms */
+    HPO_MUON_PROF_INPUT = 1,     /* X0 = bf16(g~ / (norm + eps)) and its transpose */
+    HPO_MUON_PROF_GRAM = 2,      /* A = X X^T (symmetric: upper-triangle tiles, mirrored) */
+    HPO_MUON_PROF_POLY = 3,      /* B = b A + c A A^T (symmetric) */
+    HPO_MUON_PROF_STEP = 4,      /* X' = a X + B X, steps before the last */
+    HPO_MUON_PROF_UPDATE = 5,    /* the last step's X' = a X + B X fused with the master update */
+    HPO_MUON_PROF_N = 6
+} hpo_muon_prof_kind;
+
+typedef struct {
+    double ms[HPO_MUON_PROF_N];        /* summed launch time (event to event) */
+    int64_t launches[HPO_MUON_PROF_N];
+    double flops[HPO_MUON_PROF_N];     /* algorithmic: m(m+1)n for a Gram matrix of an m x n X (one
+                                          triangle), m^2(m+1) for A A^T, 2 m^2 n for B X; 0 for the
+                                          elementwise passes */
+    double bytes[HPO_MUON_PROF_N];     /* algorithmic HBM bytes of the elementwise passes: momentum
+                                          16 per element (read G, M; write M, g~), input 12 (read g~,
+                                          write X and X^T in bf16) */
+} hpo_muon_profile;
+
+hpo_status hpo_muon_profile_enable(hpo_set s, int32_t enable);
+hpo_status hpo_muon_profile_read(hpo_set s, hpo_muon_profile* out);
+
 /* ---------------------------------------------------------------------- */
 /* Host-only queries (no device needed)                                   */
 /* ---------------------------------------------------------------------- */

@@ -249,9 +249,16 @@ hipError_t launch_muon_ns_input(const MuonBatch& b, const MuonWork& w, const Muo
 /* steps Newton-Schulz iterations on the batch; the last one either updates
  * the masters / params (out == nullptr) or writes O (fp32, natural layout,
  * one matrix: batch count 1) to out.  coeffs: host array of 3 * steps. */
+/* Optional callback around each NS launch (timing): kind is a
+ * hpo_muon_prof_kind, after = 0 before the launch and 1 after it, flops the
+ * launch's algorithmic work. */
+struct NsHook {
+    void (*fn)(void* ctx, int kind, int after, double flops);
+    void* ctx;
+};
 hipError_t launch_muon_ns(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonBatch& b, const MuonWork& w,
                           const MuonGate& gate, int32_t steps, const float* coeffs, const MuonUpdate& up, float* out,
-                          hipStream_t stream);
+                          hipStream_t stream, const NsHook* hook = nullptr);
 /* Standalone NS input: fp32 G (natural layout, batch count 1) -> its norm
  * into w.dnorm[0], then X0 / XT0. */
 hipError_t launch_ns_input_from(const float* G, float eps, const MuonBatch& b, const MuonWork& w, hipStream_t stream);

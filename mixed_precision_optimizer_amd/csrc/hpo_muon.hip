@@ -58,14 +58,58 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kNsThreads = 256;        /* 4 wavefronts, 2 x 2 over the C tile */
-constexpr int kWaveTiles = 2;          /* 32 x 32 MFMA tiles per wavefront, each way */
-constexpr int kBM = 2 * 32 * kWaveTiles;
-constexpr int kBN = 2 * 32 * kWaveTiles;
-constexpr int kBK = 64;                /* k per LDS stage */
-constexpr int kRowBytes = kBK * 2;     /* 128 B: eight 16-byte pieces */
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;
-static_assert(kNsPad % kBM == 0 && kNsPad % kBN == 0 && kNsPad % kBK == 0, "padding covers the tiles");
+/* NS GEMM tiling (compile-time knobs): a workgroup of WAVES_M x WAVES_N
+ * wavefronts, each computing TILES_M x TILES_N MFMA tiles of 32 x 32; the k
+ * depth of one LDS stage. */
+#ifndef HPO_NS_WAVES_M
+#define HPO_NS_WAVES_M 4
+#endif
+#ifndef HPO_NS_WAVES_N
+#define HPO_NS_WAVES_N 4
+#endif
+#ifndef HPO_NS_TILES_M
+#define HPO_NS_TILES_M 2
+#endif
+#ifndef HPO_NS_TILES_N
+#define HPO_NS_TILES_N 2
+#endif
+#ifndef HPO_NS_BK
+#define HPO_NS_BK 64
+#endif
+/* Stage operands with direct global -> LDS loads (no register staging, no
+ * LDS store instructions); rows are then XOR-swizzled instead of padded. */
+#ifndef HPO_NS_DIRECT
+#define HPO_NS_DIRECT 1
+#endif
+/* Pin the interleave of fragment reads and MFMAs with scheduling barriers. */
+#ifndef HPO_NS_SCHED
+#define HPO_NS_SCHED 1
+#endif
+/* Tile order: each XCD takes a contiguous run of tiles, rows grouped by this
+ * many (0: hardware order). */
+#ifndef HPO_NS_GROUP
+#define HPO_NS_GROUP 8
+#endif
+constexpr int kWavesM = HPO_NS_WAVES_M, kWavesN = HPO_NS_WAVES_N;
+constexpr int kTM = HPO_NS_TILES_M, kTN = HPO_NS_TILES_N;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kNsThreads = 64 * kWaves;
+constexpr int kBM = kWavesM * kTM * 32;          /* C tile is kBM x kBM */
+static_assert(kBM == kWavesN * kTN * 32, "square C tiles (symmetric outputs mirror them)");
+constexpr int kBK = HPO_NS_BK;
+constexpr int kPieces = kBK / 8;                 /* 16-byte pieces per operand row and stage */
+#if HPO_NS_DIRECT
+constexpr int kRowStride = kBK * 2;              /* pieces XOR-swizzled by row (see piece_at) */
+static_assert(kBK == 64, "direct staging fills 8 rows of 128 B per wavefront load");
+static_assert((2 * kBM / 8) % kWaves == 0, "stage chunks split evenly over the wavefronts");
+#else
+constexpr int kRowStride = kBK * 2 + 16;         /* one piece of padding: conflict-free fragment reads */
+#endif
+constexpr int kStageBytes = 2 * kBM * kRowStride;
+constexpr int kRowsPerPass = kNsThreads / kPieces;
+constexpr int kLoads = kBM / kRowsPerPass;       /* 16-byte global loads per operand per lane and stage */
+static_assert(kNsPad % kBM == 0 && kNsPad % kBK == 0, "padding covers the tiles");
+static_assert(kBK % 16 == 0 && kBM % kRowsPerPass == 0, "tiling");
 constexpr int kTile = 64;              /* transpose tile of the input kernel */
 
 /* ---------------------------------------------------------------------- */
@@ -285,6 +329,8 @@ struct GemmArgs {
     const uint16_t* Q;
     int64_t ldp, sp, ldq, sq;
     int32_t K;
+    int32_t nt;          /* symmetric outputs: tiles per side */
+    int32_t nx, ny;      /* general outputs: tiles per row, per column */
     int32_t first;       /* matrix index of slot 0 (update epilogue) */
     uint16_t* C;         /* gram / poly output */
     int64_t ldc, sc;
@@ -293,21 +339,12 @@ struct GemmArgs {
     uint16_t* XT;        /* step: next X^T */
     int64_t ldxt, sxt;
     float a, b, c;
-    int32_t transposed;  /* update / out: matrices of this batch are transposed */
-    int64_t R, Cn;       /* update / out: natural shape */
+    int64_t R, Cn;       /* update / out: natural shape; the C tile is in natural orientation */
     float* out;          /* out epilogue */
     const TensorDesc* desc;
     const MuonInfo* info;
     MuonGate gate;
 };
-
-/* Position of 16-byte piece p of LDS row r: the XOR keeps the 16 (or 8)
- * rows one fragment read touches per cycle on distinct banks. */
-__device__ __forceinline__ int lds_off(int r, int p)
-{
-    const int swz = (r & 7) ^ ((r >> 3) & 1);
-    return r * kRowBytes + ((p ^ swz) << 4);
-}
 
 __device__ __forceinline__ float bf16v(uint16_t b) { return bf16_to_f32(b); }
 
@@ -327,81 +364,214 @@ __device__ __forceinline__ double update_scale(int64_t rows, int64_t cols, const
     return base * up.extra_scale;
 }
 
-template <int EPI>
+/* Byte offset of 16-byte piece p of LDS row r.  Direct staging stores row r's
+ * pieces permuted by an XOR with (r & 7) ^ ((r >> 3) & 1): the 16 (or 8) rows
+ * that one fragment read serves per LDS cycle then land on distinct banks
+ * whether the LDS has 64 or 32 four-byte banks.  Padded rows need no
+ * permutation. */
+__device__ __forceinline__ int piece_at(int r, int p)
+{
+#if HPO_NS_DIRECT
+    return r * kRowStride + ((p ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
+#else
+    return r * kRowStride + (p << 4);
+#endif
+}
+
+/* Tile of the t-th workgroup in dispatch order.  Workgroups go to the 8
+ * XCDs round-robin; the remap gives XCD x one contiguous run of tile numbers
+ * (so the tiles running on one XCD share operand panels in its L2).  Tile
+ * numbers then walk groups of HPO_NS_GROUP tile rows column by column
+ * (general outputs), or the upper triangle row by row (symmetric outputs,
+ * tiles with ty <= tx only). */
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t n)
+{
+#if HPO_NS_GROUP
+    constexpr int64_t kXcd = 8;
+    const int64_t x = b % kXcd, k = b / kXcd;
+    const int64_t q = n / kXcd, r = n % kXcd;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+#else
+    (void)n;
+    return b;
+#endif
+}
+
+template <bool SYM>
+__device__ __forceinline__ void tile_of(const GemmArgs& g, int64_t& ty, int64_t& tx)
+{
+    if constexpr (SYM) {
+        const int32_t nt = g.nt;
+        int64_t t = xcd_contiguous(blockIdx.x, static_cast<int64_t>(nt) * (nt + 1) / 2);
+        int64_t y = 0, row = nt;
+        while (t >= row) {
+            t -= row;
+            ++y;
+            --row;
+        }
+        ty = y;
+        tx = y + t;
+    } else {
+        const int64_t nx = g.nx, ny = g.ny;
+        const int64_t t = xcd_contiguous(blockIdx.x, nx * ny);
+#if HPO_NS_GROUP
+        const int64_t G = HPO_NS_GROUP;
+        const int64_t group = t / (G * nx);
+        const int64_t first = group * G;
+        const int64_t rows = ny - first < G ? ny - first : G;
+        const int64_t within = t - group * G * nx;
+        ty = first + within % rows;
+        tx = within / rows;
+#else
+        ty = t / nx;
+        tx = t % nx;
+#endif
+    }
+}
+
+template <int EPI, bool SYM>
 __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate up)
 {
     if (!gate_open(g.gate))
         return;
     __shared__ __attribute__((aligned(16))) char lds[2][kStageBytes];
     const int64_t z = blockIdx.z;
-    const int64_t row0 = static_cast<int64_t>(blockIdx.y) * kBM;
-    const int64_t col0 = static_cast<int64_t>(blockIdx.x) * kBN;
+    int64_t ty, tx;
+    tile_of<SYM>(g, ty, tx);
+    const int64_t row0 = ty * kBM;
+    const int64_t col0 = tx * kBM;
     const uint16_t* __restrict__ P = g.P + z * g.sp + row0 * g.ldp;
     const uint16_t* __restrict__ Q = g.Q + z * g.sq + col0 * g.ldq;
     const int tid = threadIdx.x;
-    const int ld_piece = tid & 7, ld_row = tid >> 3;   /* loader: row ld_row + 32 k, piece ld_piece */
-    constexpr int kLoads = kBM / 32;                   /* 16-byte loads per operand per lane */
+    const int wave = tid >> 6, lane = tid & 63;
+#if HPO_NS_DIRECT
+    /* one wavefront load fills 1 KB = 8 rows of one stage, lane l landing in
+     * row l / 8, physical piece l % 8; the lane fetches the logical piece
+     * that the swizzle puts there */
+    constexpr int kChunks = 2 * kBM / 8;         /* 8-row chunks per stage (P rows, then Q rows) */
+    constexpr int kChunksPerWave = kChunks / kWaves;
+    auto gload = [&](int s, int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < kChunksPerWave; ++i) {
+            const int c = wave * kChunksPerWave + i;
+            const int r = c * 8 + (lane >> 3);
+            const int p = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
+            const uint16_t* src = r < kBM ? P + r * g.ldp : Q + (r - kBM) * g.ldq;
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + k0 + p * 8),
+                                             (__attribute__((address_space(3))) void*)(&lds[s][c * 8 * kRowStride]),
+                                             16, 0, 0);
+        }
+    };
+#else
+    const int ld_piece = tid % kPieces, ld_row = tid / kPieces;
     u32x4_t rp[kLoads], rq[kLoads];
     auto gload = [&](int64_t k0) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            rp[i] = *reinterpret_cast<const u32x4_t*>(P + (ld_row + 32 * i) * g.ldp + k0 + ld_piece * 8);
-            rq[i] = *reinterpret_cast<const u32x4_t*>(Q + (ld_row + 32 * i) * g.ldq + k0 + ld_piece * 8);
+            rp[i] = *reinterpret_cast<const u32x4_t*>(P + (ld_row + kRowsPerPass * i) * g.ldp + k0 + ld_piece * 8);
+            rq[i] = *reinterpret_cast<const u32x4_t*>(Q + (ld_row + kRowsPerPass * i) * g.ldq + k0 + ld_piece * 8);
         }
     };
     auto lstore = [&](int s) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            *reinterpret_cast<u32x4_t*>(&lds[s][lds_off(ld_row + 32 * i, ld_piece)]) = rp[i];
-            *reinterpret_cast<u32x4_t*>(&lds[s][kBM * kRowBytes + lds_off(ld_row + 32 * i, ld_piece)]) = rq[i];
+            const int off = (ld_row + kRowsPerPass * i) * kRowStride + ld_piece * 16;
+            *reinterpret_cast<u32x4_t*>(&lds[s][off]) = rp[i];
+            *reinterpret_cast<u32x4_t*>(&lds[s][kBM * kRowStride + off]) = rq[i];
         }
     };
-    const int wave = tid >> 6, lane = tid & 63;
-    const int wm = (wave >> 1) * 32 * kWaveTiles, wn = (wave & 1) * 32 * kWaveTiles;
+#endif
+    const int wm = (wave / kWavesN) * 32 * kTM, wn = (wave % kWavesN) * 32 * kTN;
     const int frow = lane & 31, fhalf = lane >> 5;
-    f32x16_t acc[kWaveTiles][kWaveTiles];
+    f32x16_t acc[kTM][kTN];
 #pragma unroll
-    for (int i = 0; i < kWaveTiles; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kWaveTiles; ++j)
+        for (int j = 0; j < kTN; ++j)
             acc[i][j] = f32x16_t{};
+    /* One k-stage from LDS buffer s: fragments of slice kk + 1 are read
+     * while the MFMAs of slice kk run; the scheduling barriers keep the
+     * compiler from sinking the reads next to their uses. */
+    auto compute = [&](int s) {
+        const char* Ps = lds[s];
+        const char* Qs = lds[s] + kBM * kRowStride;
+        bf16x8_t fa[2][kTM], fb[2][kTN];
+        auto fload = [&](int kk, int buf) {
+            const int piece = kk * 2 + fhalf;  /* lanes 0-31: k 0..7 of the slice, 32-63: k 8..15 */
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+                fa[buf][i] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Ps + piece_at(wm + 32 * i + frow, piece)));
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+                fb[buf][j] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Qs + piece_at(wn + 32 * j + frow, piece)));
+        };
+        fload(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < kBK / 16)
+                fload(kk + 1, cur ^ 1);
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+#if HPO_NS_SCHED
+            if (kk + 1 < kBK / 16) {
+                /* the next slice's kTM + kTN reads spread over this slice's kTM * kTN MFMAs */
+                constexpr int kReads = kTM + kTN, kPer = kTM * kTN / kReads, kRest = kTM * kTN - kPer * kReads;
+#pragma unroll
+                for (int q = 0; q < kReads; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      /* one DS read */
+                    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);   /* MFMAs */
+                }
+                if (kRest > 0)
+                    __builtin_amdgcn_sched_group_barrier(0x008, kRest, 0);
+            }
+#endif
+        }
+    };
     const int nk = g.K / kBK;
+#if HPO_NS_DIRECT
+    gload(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        const int s = kt & 1;
+        gload(s ^ 1, static_cast<int64_t>(kt + 1) * kBK);  /* buffer s ^ 1 was released by the last barrier */
+#if HPO_NS_SCHED
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+        compute(s);
+        __builtin_amdgcn_s_waitcnt(0);  /* this wavefront's loads of stage kt + 1 are in LDS */
+        __syncthreads();                 /* ... and everyone's; buffer s is free again */
+    }
+#else
     gload(0);
     lstore(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt + 1 < nk; ++kt) {
         const int s = kt & 1;
-        if (kt + 1 < nk)
-            gload(static_cast<int64_t>(kt + 1) * kBK);
-        const char* Ps = lds[s];
-        const char* Qs = lds[s] + kBM * kRowBytes;
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int piece = kk * 2 + fhalf;  /* lanes 0-31: k 0..7 of the slice, 32-63: k 8..15 */
-            bf16x8_t fa[kWaveTiles], fb[kWaveTiles];
-#pragma unroll
-            for (int i = 0; i < kWaveTiles; ++i)
-                fa[i] = __builtin_bit_cast(bf16x8_t,
-                                           *reinterpret_cast<const u32x4_t*>(Ps + lds_off(wm + 32 * i + frow, piece)));
-#pragma unroll
-            for (int j = 0; j < kWaveTiles; ++j)
-                fb[j] = __builtin_bit_cast(bf16x8_t,
-                                           *reinterpret_cast<const u32x4_t*>(Qs + lds_off(wn + 32 * j + frow, piece)));
-#pragma unroll
-            for (int i = 0; i < kWaveTiles; ++i)
-#pragma unroll
-                for (int j = 0; j < kWaveTiles; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk)
-            lstore(s ^ 1);
+        gload(static_cast<int64_t>(kt + 1) * kBK);
+#if HPO_NS_SCHED
+        __builtin_amdgcn_sched_barrier(0);  /* the next stage's loads go out before this stage's math */
+#endif
+        compute(s);
+        lstore(s ^ 1);
         __syncthreads();
     }
+#endif
+    compute((nk - 1) & 1);
 
     /* Epilogue.  acc[i][j][r] holds C[row][col] with
-     * row = wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, col = wn + 32 j + lane % 32. */
+     * row = wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, col = wn + 32 j + lane % 32.
+     * Symmetric outputs: a diagonal tile stores its upper triangle and
+     * mirrors it; an off-diagonal tile stores itself and its mirror image. */
     const int64_t lcol = lane & 31;
     const int64_t lrow4 = 4 * (lane >> 5);
+    const bool diag = SYM && ty == tx;
     float k1 = 0.0f, k2 = 0.0f;
     float* __restrict__ W = nullptr;
     uint16_t* __restrict__ Pm = nullptr;
@@ -414,37 +584,56 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
         W = g.desc[mat].master;
         Pm = up.param_dtype == HPO_PARAM_FP32 ? nullptr : static_cast<uint16_t*>(g.desc[mat].param);
     }
-#pragma unroll
-    for (int i = 0; i < kWaveTiles; ++i) {
-#pragma unroll
-        for (int j = 0; j < kWaveTiles; ++j) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < kTM; ++i) {
+#pragma clang loop unroll(full)
+        for (int j = 0; j < kTN; ++j) {
             const int64_t col = col0 + wn + 32 * j + lcol;
-#pragma unroll
+#pragma clang loop unroll(full)
             for (int q = 0; q < 4; ++q) {
                 const int64_t rbase = row0 + wm + 32 * i + 8 * q + lrow4;
                 float v[4];
-#pragma unroll
+#pragma clang loop unroll(full)
                 for (int e = 0; e < 4; ++e)
                     v[e] = acc[i][j][4 * q + e];
-                if constexpr (EPI == kEpiGram) {
+                if constexpr (EPI == kEpiGram || EPI == kEpiPoly) {
                     uint16_t* __restrict__ Cz = g.C + z * g.sc;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        Cz[(rbase + e) * g.ldc + col] = static_cast<uint16_t>(bf16_rne_bits(v[e]));
-                } else if constexpr (EPI == kEpiPoly) {
-                    uint16_t* __restrict__ Cz = g.C + z * g.sc;
-                    const uint16_t* __restrict__ Az = g.P + z * g.sp;
-#pragma unroll
+                    uint32_t bits[4];
+#pragma clang loop unroll(full)
                     for (int e = 0; e < 4; ++e) {
-                        const float a = bf16v(Az[(rbase + e) * g.ldp + col]);
-                        const float bv = g.b * a;
-                        const float cv = g.c * v[e];
-                        Cz[(rbase + e) * g.ldc + col] = static_cast<uint16_t>(bf16_rne_bits(bv + cv));
+                        float x = v[e];
+                        if constexpr (EPI == kEpiPoly) {
+                            const float a = bf16v(g.P[z * g.sp + (rbase + e) * g.ldp + col]);
+                            const float bv = g.b * a;
+                            const float cv = g.c * x;
+                            x = bv + cv;
+                        }
+                        bits[e] = bf16_rne_bits(x);
+                    }
+                    if (!diag) {
+#pragma clang loop unroll(full)
+                        for (int e = 0; e < 4; ++e)
+                            Cz[(rbase + e) * g.ldc + col] = static_cast<uint16_t>(bits[e]);
+                        if constexpr (SYM) {
+                            u32x2_t t;
+                            t.x = bits[0] | (bits[1] << 16);
+                            t.y = bits[2] | (bits[3] << 16);
+                            *reinterpret_cast<u32x2_t*>(Cz + col * g.ldc + rbase) = t;
+                        }
+                    } else {
+#pragma clang loop unroll(full)
+                        for (int e = 0; e < 4; ++e) {
+                            const int64_t row = rbase + e;
+                            if (row <= col)
+                                Cz[row * g.ldc + col] = static_cast<uint16_t>(bits[e]);
+                            if (row < col)
+                                Cz[col * g.ldc + row] = static_cast<uint16_t>(bits[e]);
+                        }
                     }
                 } else if constexpr (EPI == kEpiStep) {
                     uint16_t* __restrict__ Xz = g.X + z * g.sx;
                     uint32_t bits[4];
-#pragma unroll
+#pragma clang loop unroll(full)
                     for (int e = 0; e < 4; ++e) {
                         uint16_t* px = Xz + (rbase + e) * g.ldx + col;
                         const float ax = g.a * bf16v(*px);
@@ -457,15 +646,13 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
                     *reinterpret_cast<u32x2_t*>(g.XT + z * g.sxt + col * g.ldxt + rbase) = t;
                 } else {
                     const uint16_t* __restrict__ Xz = g.X + z * g.sx;
-#pragma unroll
+#pragma clang loop unroll(full)
                     for (int e = 0; e < 4; ++e) {
                         const int64_t row = rbase + e;
                         const float ax = g.a * bf16v(Xz[row * g.ldx + col]);
                         const float o = ax + v[e];
-                        const int64_t nr = g.transposed ? col : row;
-                        const int64_t nc = g.transposed ? row : col;
-                        if (nr < g.R && nc < g.Cn) {
-                            const int64_t idx = nr * g.Cn + nc;
+                        if (row < g.R && col < g.Cn) {
+                            const int64_t idx = row * g.Cn + col;
                             if constexpr (EPI == kEpiUpdate) {
                                 float w = W[idx];
                                 w = w * k1;             /* decoupled decay first ([HANDBOOK] listing) */
@@ -497,10 +684,26 @@ struct Dims {
 };
 
 /* One NS step's three GEMMs on a batch. */
+/* Runs one launch between the hook's before / after calls. */
+template <typename F>
+hipError_t hooked(const NsHook* hook, int kind, double flops, F&& launch_fn)
+{
+    if (hook)
+        hook->fn(hook->ctx, kind, 0, flops);
+    hipError_t e = launch_fn();
+    if (hook && e == hipSuccess)
+        hook->fn(hook->ctx, kind, 1, flops);
+    return e;
+}
+
 hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonBatch& b, const MuonWork& w,
                    const MuonGate& gate, float a, float bc, float cc, int cur, bool last, const MuonUpdate& up,
-                   float* out, hipStream_t stream)
+                   float* out, hipStream_t stream, const NsHook* hook)
 {
+    const double cntd = static_cast<double>(b.count), md = static_cast<double>(b.m), nd = static_cast<double>(b.n);
+    const double f_gram = cntd * md * (md + 1.0) * nd;
+    const double f_poly = cntd * md * md * (md + 1.0);
+    const double f_step = cntd * 2.0 * md * md * nd;
     const int64_t mp = b.mp, np = b.np;
     const uint32_t cnt = static_cast<uint32_t>(b.count);
     GemmArgs g{};
@@ -513,7 +716,11 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
     g.Q = w.X; g.ldq = np; g.sq = mp * np;
     g.K = static_cast<int32_t>(np);
     g.C = w.A; g.ldc = mp; g.sc = mp * mp;
-    hipError_t e = launch3(k_ns_gemm<kEpiGram>, dim3(mp / kBN, mp / kBM, cnt), kNsThreads, stream, g, up);
+    const int32_t nt = static_cast<int32_t>(mp / kBM);
+    const dim3 tri(static_cast<uint32_t>(nt * (nt + 1) / 2), 1, cnt);
+    g.nt = nt;
+    hipError_t e = hooked(hook, HPO_MUON_PROF_GRAM, f_gram,
+                          [&] { return launch3(k_ns_gemm<kEpiGram, true>, tri, kNsThreads, stream, g, up); });
     if (e != hipSuccess)
         return e;
     /* B = b A + c A A^T */
@@ -522,7 +729,8 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
     g.K = static_cast<int32_t>(mp);
     g.C = w.B; g.ldc = mp; g.sc = mp * mp;
     g.b = bc; g.c = cc;
-    e = launch3(k_ns_gemm<kEpiPoly>, dim3(mp / kBN, mp / kBM, cnt), kNsThreads, stream, g, up);
+    e = hooked(hook, HPO_MUON_PROF_POLY, f_poly,
+               [&] { return launch3(k_ns_gemm<kEpiPoly, true>, tri, kNsThreads, stream, g, up); });
     if (e != hipSuccess)
         return e;
     /* X' = a X + B X  (Q = X^T, rows of X^T are columns of X) */
@@ -532,22 +740,34 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
     g.X = w.X; g.ldx = np; g.sx = mp * np;
     g.XT = w.XT[cur ^ 1]; g.ldxt = mp; g.sxt = np * mp;
     g.a = a;
-    const dim3 grid(static_cast<uint32_t>(np / kBN), static_cast<uint32_t>(mp / kBM), cnt);
+    g.nx = static_cast<int32_t>(np / kBM);
+    g.ny = static_cast<int32_t>(mp / kBM);
+    const dim3 grid(static_cast<uint32_t>(g.nx * g.ny), 1, cnt);
     if (!last)
-        return launch3(k_ns_gemm<kEpiStep>, grid, kNsThreads, stream, g, up);
-    g.transposed = 0;
+        return hooked(hook, HPO_MUON_PROF_STEP, f_step,
+                      [&] { return launch3(k_ns_gemm<kEpiStep, false>, grid, kNsThreads, stream, g, up); });
     g.R = b.m;
     g.Cn = b.n;
     if (b.transposed) {
-        g.transposed = 1;
+        /* The natural orientation is the transpose: compute O^T = a X^T + X^T B
+         * (B is symmetric) as C = X^T B^T, so the output tile comes out in
+         * the master's own row-major order and the update's reads and writes
+         * of W run along its rows. */
+        g.P = w.XT[cur]; g.ldp = mp; g.sp = np * mp;
+        g.Q = w.B; g.ldq = mp; g.sq = mp * mp;
+        g.X = w.XT[cur]; g.ldx = mp; g.sx = np * mp;
+        g.nx = static_cast<int32_t>(mp / kBM);
+        g.ny = static_cast<int32_t>(np / kBM);
         g.R = b.n;
         g.Cn = b.m;
     }
     if (out != nullptr) {
         g.out = out;
-        return launch3(k_ns_gemm<kEpiOut>, grid, kNsThreads, stream, g, up);
+        return hooked(hook, HPO_MUON_PROF_UPDATE, f_step,
+                      [&] { return launch3(k_ns_gemm<kEpiOut, false>, grid, kNsThreads, stream, g, up); });
     }
-    return launch3(k_ns_gemm<kEpiUpdate>, grid, kNsThreads, stream, g, up);
+    return hooked(hook, HPO_MUON_PROF_UPDATE, f_step,
+                  [&] { return launch3(k_ns_gemm<kEpiUpdate, false>, grid, kNsThreads, stream, g, up); });
 }
 
 }  // namespace
@@ -613,13 +833,13 @@ hipError_t launch_ns_input_from(const float* G, float eps, const MuonBatch& b, c
 
 hipError_t launch_muon_ns(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonBatch& b, const MuonWork& w,
                           const MuonGate& gate, int32_t steps, const float* coeffs, const MuonUpdate& up, float* out,
-                          hipStream_t stream)
+                          hipStream_t stream, const NsHook* hook)
 {
     int cur = 0;
     for (int32_t s = 0; s < steps; ++s) {
         const bool last = s + 1 == steps;
         hipError_t e = ns_step(d_desc, d_info, b, w, gate, coeffs[3 * s], coeffs[3 * s + 1], coeffs[3 * s + 2], cur,
-                               last, up, out, stream);
+                               last, up, out, stream, hook);
         if (e != hipSuccess)
             return e;
         cur ^= 1;

@@ -12,6 +12,7 @@
  *                §14.3 (no fp16 with Muon), §14.6 (update scales)
  */
 #include <cmath>
+#include <cstdint>
 #include <map>
 #include <new>
 #include <utility>
@@ -107,6 +108,48 @@ hpo_status check_muon_cfg(const hpo_muon_cfg* cfg, bool ns_only)
     return HPO_OK;
 }
 
+/* Records one event of the profile pool on `stream`; returns its index. */
+size_t prof_mark(hpo_muon_prof& p, hipStream_t stream)
+{
+    if (p.used == p.pool.size()) {
+        hipEvent_t ev = nullptr;
+        if (hipEventCreate(&ev) != hipSuccess)
+            return SIZE_MAX;
+        p.pool.push_back(ev);
+    }
+    const size_t k = p.used++;
+    if (hipEventRecord(p.pool[k], stream) != hipSuccess)
+        return SIZE_MAX;
+    return k;
+}
+
+struct ProfCtx {
+    hpo_muon_prof* p;
+    hipStream_t stream;
+    size_t ev0;
+};
+
+void prof_hook(void* ctx, int kind, int after, double flops)
+{
+    ProfCtx* c = static_cast<ProfCtx*>(ctx);
+    if (!after) {
+        c->ev0 = prof_mark(*c->p, c->stream);
+        return;
+    }
+    const size_t ev1 = prof_mark(*c->p, c->stream);
+    if (c->ev0 != SIZE_MAX && ev1 != SIZE_MAX)
+        c->p->recs.push_back({kind, c->ev0, ev1, flops, 0.0});
+}
+
+void free_prof(hpo_muon_prof* p)
+{
+    if (!p)
+        return;
+    for (hipEvent_t ev : p->pool)
+        (void)hipEventDestroy(ev);
+    delete p;
+}
+
 }  // namespace
 
 namespace hpo_host {
@@ -115,6 +158,7 @@ void free_muon(hpo_muon_part* m)
 {
     if (!m)
         return;
+    free_prof(m->prof);
     if (m->d_info) (void)hipFree(m->d_info);
     if (m->d_ws) (void)hipFree(m->d_ws);
     if (m->d_dnorm) (void)hipFree(m->d_dnorm);
@@ -172,15 +216,31 @@ hpo_status muon_enqueue(hpo_set s, const hpo_muon_cfg* cfg, const hpo_group* gro
     float coeffs[3 * HPO_NS_MAX_STEPS];
     ns_coeffs(cfg, coeffs);
     const hpo_muon_part& m = *s->muon;
+    ProfCtx pc{m.prof, stream, SIZE_MAX};
+    const hpo::NsHook hook{prof_hook, &pc};
+    const hpo::NsHook* hk = m.prof ? &hook : nullptr;
     for (const hpo::MuonBatch& b : m.batches) {
         const hpo::MuonWork w = muon_work(m, b);
+        const double elems = static_cast<double>(b.count) * static_cast<double>(b.m * b.n);
+        size_t ev0 = m.prof ? prof_mark(*m.prof, stream) : 0;
         hipError_t e = hpo::launch_muon_momentum(s->view, m.d_info, b, sc, w, stream);
         if (e != hipSuccess)
             return hip_fail(e, "launch Muon momentum");
+        if (m.prof) {
+            const size_t ev1 = prof_mark(*m.prof, stream);
+            if (ev0 != SIZE_MAX && ev1 != SIZE_MAX)
+                m.prof->recs.push_back({HPO_MUON_PROF_MOMENTUM, ev0, ev1, 0.0, 16.0 * elems});
+            ev0 = ev1;
+        }
         e = hpo::launch_muon_ns_input(b, w, gate, stream);
         if (e != hipSuccess)
             return hip_fail(e, "launch Newton-Schulz input");
-        e = hpo::launch_muon_ns(s->d_tensors, m.d_info, b, w, gate, cfg->ns_steps, coeffs, up, nullptr, stream);
+        if (m.prof) {
+            const size_t ev1 = prof_mark(*m.prof, stream);
+            if (ev0 != SIZE_MAX && ev1 != SIZE_MAX)
+                m.prof->recs.push_back({HPO_MUON_PROF_INPUT, ev0, ev1, 0.0, 12.0 * elems});
+        }
+        e = hpo::launch_muon_ns(s->d_tensors, m.d_info, b, w, gate, cfg->ns_steps, coeffs, up, nullptr, stream, hk);
         if (e != hipSuccess)
             return hip_fail(e, "launch Newton-Schulz");
     }
@@ -480,6 +540,56 @@ hpo_status hpo_newton_schulz(const float* d_G, int64_t rows, int64_t cols, const
     e = hpo::launch_muon_ns(nullptr, nullptr, b, w, open, cfg->ns_steps, coeffs, up, d_out, strm);
     if (e != hipSuccess)
         return hip_fail(e, "launch Newton-Schulz");
+    return ok();
+}
+
+hpo_status hpo_muon_profile_enable(hpo_set s, int32_t enable)
+{
+    hpo_status st = check_set(s);
+    if (st != HPO_OK)
+        return st;
+    if (s->kind != HPO_SET_MUON || !s->muon)
+        return fail(HPO_EINVAL, "not a Muon set");
+    if (enable && !s->muon->prof) {
+        s->muon->prof = new (std::nothrow) hpo_muon_prof;
+        if (!s->muon->prof)
+            return fail(HPO_ENOMEM, "host allocation failed");
+    } else if (!enable && s->muon->prof) {
+        hipError_t e = hipDeviceSynchronize();
+        free_prof(s->muon->prof);
+        s->muon->prof = nullptr;
+        if (e != hipSuccess)
+            return hip_fail(e, "hipDeviceSynchronize before dropping the profile events");
+    }
+    return ok();
+}
+
+hpo_status hpo_muon_profile_read(hpo_set s, hpo_muon_profile* out)
+{
+    hpo_status st = check_set(s);
+    if (st != HPO_OK)
+        return st;
+    if (!out)
+        return fail(HPO_EINVAL, "out is NULL");
+    if (s->kind != HPO_SET_MUON || !s->muon || !s->muon->prof)
+        return fail(HPO_EINVAL, "timing is not enabled on this set (hpo_muon_profile_enable)");
+    hpo_muon_prof& p = *s->muon->prof;
+    *out = hpo_muon_profile{};
+    for (const auto& r : p.recs) {
+        hipError_t e = hipEventSynchronize(p.pool[r.ev1]);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipEventSynchronize");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, p.pool[r.ev0], p.pool[r.ev1]);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipEventElapsedTime");
+        out->ms[r.kind] += ms;
+        out->launches[r.kind] += 1;
+        out->flops[r.kind] += r.flops;
+        out->bytes[r.kind] += r.bytes;
+    }
+    p.recs.clear();
+    p.used = 0;
     return ok();
 }
 

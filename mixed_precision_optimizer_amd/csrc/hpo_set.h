@@ -11,9 +11,18 @@
 
 #include "hpo_impl.h"
 
+/* Event-pair timing of Muon launches (hpo_muon_profile_enable). */
+struct hpo_muon_prof {
+    std::vector<hipEvent_t> pool;  /* created on demand, reused after each read */
+    size_t used = 0;               /* events recorded since the last read */
+    struct Rec { int kind; size_t ev0, ev1; double flops, bytes; };
+    std::vector<Rec> recs;
+};
+
 /* Muon-only part of a set: per-matrix facts, the batch plan and the
  * workspace (one device allocation sized for the largest batch). */
 struct hpo_muon_part {
+    hpo_muon_prof* prof = nullptr;     /* non-NULL while timing is enabled */
     std::vector<hpo::MuonInfo> info;       /* internal (batched) order */
     std::vector<hpo::MuonBatch> batches;
     hpo::MuonInfo* d_info = nullptr;

@@ -59,6 +59,15 @@ HPO_NS_MAX_STEPS = 16
 HPO_MUON_DEFAULT_WORKSPACE = 4 << 30
 
 
+HPO_MUON_PROF_N = 6
+MUON_PROF_KINDS = ("momentum", "input", "gram", "poly", "step", "update")
+
+
+class hpo_muon_profile(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * HPO_MUON_PROF_N), ("launches", ctypes.c_int64 * HPO_MUON_PROF_N),
+                ("flops", ctypes.c_double * HPO_MUON_PROF_N), ("bytes", ctypes.c_double * HPO_MUON_PROF_N)]
+
+
 class hpo_muon_cfg(ctypes.Structure):
     _fields_ = [("momentum", ctypes.c_double), ("nesterov", ctypes.c_int32), ("momentum_form", ctypes.c_int32),
                 ("ns_steps", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("extra_scale", ctypes.c_double),
@@ -115,6 +124,8 @@ SIGNATURES = {
                                      ctypes.POINTER(hpo_scaler_cfg), _P, _I64, _I32, _P]),
     "hpo_newton_schulz": (_I32, [_P, _I64, _I64, ctypes.POINTER(hpo_muon_cfg), _P, _P, _I64, _P]),
     "hpo_newton_schulz_workspace": (_I32, [_I64, _I64, ctypes.POINTER(_I64)]),
+    "hpo_muon_profile_enable": (_I32, [_P, _I32]),
+    "hpo_muon_profile_read": (_I32, [_P, ctypes.POINTER(hpo_muon_profile)]),
     "hpo_plan": (_I32, [_I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32), ctypes.POINTER(_I64),
                         ctypes.POINTER(_I64)]),
     "hpo_plan_chunks": (_I32, [_I32, ctypes.POINTER(_I64), _I64, ctypes.POINTER(_I32),
@@ -499,6 +510,18 @@ def hpo_newton_schulz(G: torch.Tensor, out: torch.Tensor, cfg: hpo_muon_cfg, wor
     _check(load().hpo_newton_schulz(_ptr(G), G.shape[0], G.shape[1], ctypes.byref(cfg), _ptr(out),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "hpo_newton_schulz")
+
+
+def hpo_muon_profile_enable(s: HpoSet, enable: bool = True) -> None:
+    _check(load().hpo_muon_profile_enable(s.handle, int(bool(enable))), "hpo_muon_profile_enable")
+
+
+def hpo_muon_profile_read(s: HpoSet) -> dict:
+    """{kind: {"ms", "launches", "flops", "bytes"}} since the last read."""
+    out = hpo_muon_profile()
+    _check(load().hpo_muon_profile_read(s.handle, ctypes.byref(out)), "hpo_muon_profile_read")
+    return {k: {"ms": out.ms[i], "launches": out.launches[i], "flops": out.flops[i], "bytes": out.bytes[i]}
+            for i, k in enumerate(MUON_PROF_KINDS)}
 
 
 def hpo_plan(numel: Sequence[int]):

@@ -352,3 +352,52 @@ def llama8b_muon_split():
         else:
             adam.append((name, shape))
     return adam, muon
+
+
+def llama8b_chain():
+    """The Llama-8B-shaped parameters split between the two optimizers of a
+    chain: (AdamW Workload over the embedding, output head and 1-D gains, and
+    the Muon matrices as (name, (rows, cols), grad std)).  Grad stds are the
+    per-tensor ones of llama8b()."""
+    full = llama8b_shapes()
+    stds = dict(zip([n for n, _ in full], llama8b().grad_std))
+    adam, muon = llama8b_muon_split()
+    w = Workload("llama8b_chain_adamw_part", [int(np.prod(s)) for _, s in adam], [len(s) for _, s in adam],
+                 lr=1e-3, weight_decay=0.1, max_norm=1.0, steps=5, grad_std=[stds[n] for n, _ in adam])
+    return w, [(n, s, stds[n]) for n, s in muon]
+
+
+@dataclass
+class MuonBuffers:
+    """Flat buffers of a Muon matrix list (64-element aligned starts) and the
+    per-matrix 2-D views."""
+    shapes: list
+    offs: list
+    master: torch.Tensor
+    grad: torch.Tensor
+    momentum: torch.Tensor
+    param: torch.Tensor
+
+    def views(self, buf):
+        return [buf[o:o + r * c].view(r, c) for o, (r, c) in zip(self.offs, self.shapes)]
+
+
+def allocate_muon(matrices, device, master_seed: int = 7, grad_seed: int = 2001) -> MuonBuffers:
+    """fp32 master N(0, 1), fp32 momentum 0, bf16 param = cast of the master,
+    fp32 grads N(0, std_i) for matrix i (one seeded fill, then per-matrix
+    scaling)."""
+    shapes = [tuple(s) for _, s, _ in matrices]
+    offs, total = offsets([r * c for r, c in shapes])
+    f32 = dict(dtype=torch.float32, device=device)
+    master = torch.empty(total, **f32)
+    fill_normal_(master, master_seed)
+    grad = torch.empty(total, **f32)
+    fill_normal_(grad, grad_seed)
+    for (_, (r, c), std), o in zip(matrices, offs):
+        grad[o:o + r * c].mul_(std)
+    momentum = torch.zeros(total, **f32)
+    param = torch.empty(total, dtype=torch.bfloat16, device=device)
+    for a in range(0, total, FILL_CHUNK):
+        b = min(total, a + FILL_CHUNK)
+        param[a:b].copy_(master[a:b])
+    return MuonBuffers(shapes, offs, master, grad, momentum, param)

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(H):
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 24
     lib = H.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -46,6 +46,7 @@ def test_struct_layouts(H):
     assert ctypes.sizeof(H.hpo_adam_cfg) == 32 and ctypes.sizeof(H.hpo_group) == 16
     assert ctypes.sizeof(H.hpo_scaler_cfg) == 32
     assert ctypes.sizeof(H.hpo_muon_cfg) == 48
+    assert ctypes.sizeof(H.hpo_muon_profile) == 4 * 8 * 6
 
 
 def test_device_step_validation(H):

@@ -327,3 +327,27 @@ def test_chained_device_step(H, mu, I):
             assert np.array_equal(to_np(a2[i]).view(np.uint32), T.v.view(np.uint32))
             assert np.array_equal(to_np(ap[i]), T.p)
         _compare_case(case, mu, cfg_o, chain.last, mgroups, f"chain step {k}")
+
+
+def test_muon_profile_counts(H, mu, I):
+    """The opt-in timing records one momentum and one input launch per batch,
+    ns_steps Gram / polynomial launches per batch, ns_steps - 1 plain steps
+    and one fused update; flops follow m(m+1)n, m^2(m+1) and 2 m^2 n."""
+    banner("Muon profile")
+    shapes = [(300, 700), (300, 700), (128, 384)]
+    case = MuonCase(H, mu, I, shapes, seed=3)
+    H.hpo_muon_profile_enable(case.set, True)
+    H.hpo_muon_step(case.set, H.make_muon_cfg(), [(0.02, 0.1), (0.01, 0.0)], None)
+    p = H.hpo_muon_profile_read(case.set)
+    H.hpo_muon_profile_enable(case.set, False)
+    n_batches = 2
+    assert p["momentum"]["launches"] == n_batches and p["input"]["launches"] == n_batches
+    assert p["gram"]["launches"] == 5 * n_batches and p["poly"]["launches"] == 5 * n_batches
+    assert p["step"]["launches"] == 4 * n_batches and p["update"]["launches"] == n_batches
+    want_gram = 5 * (2 * 300 * 301 * 700 + 128 * 129 * 384)
+    want_step = 4 * (2 * 2 * 300 ** 2 * 700 + 2 * 128 ** 2 * 384)
+    assert p["gram"]["flops"] == want_gram and p["step"]["flops"] == want_step
+    assert p["momentum"]["bytes"] == 16 * (2 * 300 * 700 + 128 * 384)
+    assert all(v["ms"] > 0 for v in p.values())
+    with pytest.raises(H.HpoError):
+        H.hpo_muon_profile_read(case.set)
