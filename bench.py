@@ -47,7 +47,9 @@ def update_bytes(w) -> int:
 
 
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_hbm_traffic_zero_shard_70b_over_8.txt")
-KERNEL_SOURCES = ("mixed_precision_optimizer_amd/csrc/hpo_kernels.hip", "mixed_precision_optimizer_amd/csrc/hpo_impl.h")
+# the sources of the AdamW-path kernels (the counters in profiles/ name this digest)
+KERNEL_SOURCES = ("mixed_precision_optimizer_amd/csrc/hpo_kernels.hip", "mixed_precision_optimizer_amd/csrc/hpo_impl.h",
+                  "mixed_precision_optimizer_amd/csrc/hpo_device.h")
 
 
 def kernel_digest():

@@ -47,7 +47,7 @@
  */
 #include <hip/hip_runtime.h>
 
-#include "hpo_impl.h"
+#include "hpo_muon_impl.h"
 #include "hpo_device.h"
 
 namespace hpo {

@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "hpo_impl.h"
+#include "hpo_muon_impl.h"
 
 /* Event-pair timing of Muon launches (hpo_muon_profile_enable). */
 struct hpo_muon_prof {
