@@ -76,6 +76,10 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #ifndef HPO_NS_BK
 #define HPO_NS_BK 64
 #endif
+/* LDS stages in flight (direct staging): loads run STAGES - 1 stages ahead. */
+#ifndef HPO_NS_STAGES
+#define HPO_NS_STAGES 2
+#endif
 /* Stage operands with direct global -> LDS loads (no register staging, no
  * LDS store instructions); rows are then XOR-swizzled instead of padded. */
 #ifndef HPO_NS_DIRECT
@@ -84,6 +88,10 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 /* Pin the interleave of fragment reads and MFMAs with scheduling barriers. */
 #ifndef HPO_NS_SCHED
 #define HPO_NS_SCHED 1
+#endif
+/* Raise the wavefront's issue priority while it runs its MFMAs. */
+#ifndef HPO_NS_PRIO
+#define HPO_NS_PRIO 1
 #endif
 /* Tile order: each XCD takes a contiguous run of tiles, rows grouped by this
  * many (0: hardware order). */
@@ -100,9 +108,13 @@ constexpr int kBK = HPO_NS_BK;
 constexpr int kPieces = kBK / 8;                 /* 16-byte pieces per operand row and stage */
 #if HPO_NS_DIRECT
 constexpr int kRowStride = kBK * 2;              /* pieces XOR-swizzled by row (see piece_at) */
-static_assert(kBK == 64, "direct staging fills 8 rows of 128 B per wavefront load");
-static_assert((2 * kBM / 8) % kWaves == 0, "stage chunks split evenly over the wavefronts");
+constexpr int kStages = HPO_NS_STAGES;
+constexpr int kRowsPerChunk = 1024 / kRowStride; /* rows one wavefront load (64 x 16 B) fills */
+static_assert(kBK == 64 || kBK == 32, "direct staging: rows of 128 or 64 B");
+static_assert((2 * kBM / kRowsPerChunk) % kWaves == 0, "stage chunks split evenly over the wavefronts");
+static_assert(kStages >= 2, "at least double buffering");
 #else
+constexpr int kStages = 2;
 constexpr int kRowStride = kBK * 2 + 16;         /* one piece of padding: conflict-free fragment reads */
 #endif
 constexpr int kStageBytes = 2 * kBM * kRowStride;
@@ -369,10 +381,18 @@ __device__ __forceinline__ double update_scale(int64_t rows, int64_t cols, const
  * that one fragment read serves per LDS cycle then land on distinct banks
  * whether the LDS has 64 or 32 four-byte banks.  Padded rows need no
  * permutation. */
+__device__ __forceinline__ int swizzle(int r)
+{
+    if constexpr (kBK == 64)
+        return (r & 7) ^ ((r >> 3) & 1);   /* 8 pieces per row */
+    else
+        return (r ^ (r >> 2)) & 3;         /* 4 pieces per row */
+}
+
 __device__ __forceinline__ int piece_at(int r, int p)
 {
 #if HPO_NS_DIRECT
-    return r * kRowStride + ((p ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
+    return r * kRowStride + ((p ^ swizzle(r)) << 4);
 #else
     return r * kRowStride + (p << 4);
 #endif
@@ -434,7 +454,7 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
 {
     if (!gate_open(g.gate))
         return;
-    __shared__ __attribute__((aligned(16))) char lds[2][kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds[kStages][kStageBytes];
     const int64_t z = blockIdx.z;
     int64_t ty, tx;
     tile_of<SYM>(g, ty, tx);
@@ -445,20 +465,20 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
 #if HPO_NS_DIRECT
-    /* one wavefront load fills 1 KB = 8 rows of one stage, lane l landing in
-     * row l / 8, physical piece l % 8; the lane fetches the logical piece
-     * that the swizzle puts there */
-    constexpr int kChunks = 2 * kBM / 8;         /* 8-row chunks per stage (P rows, then Q rows) */
+    /* one wavefront load fills 1 KB = kRowsPerChunk rows of one stage, lane
+     * l landing in row l / kPieces, physical piece l % kPieces; the lane
+     * fetches the logical piece that the swizzle puts there */
+    constexpr int kChunks = 2 * kBM / kRowsPerChunk;   /* chunks per stage (P rows, then Q rows) */
     constexpr int kChunksPerWave = kChunks / kWaves;
     auto gload = [&](int s, int64_t k0) {
 #pragma unroll
         for (int i = 0; i < kChunksPerWave; ++i) {
             const int c = wave * kChunksPerWave + i;
-            const int r = c * 8 + (lane >> 3);
-            const int p = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
+            const int r = c * kRowsPerChunk + lane / kPieces;
+            const int p = (lane % kPieces) ^ swizzle(r);
             const uint16_t* src = r < kBM ? P + r * g.ldp : Q + (r - kBM) * g.ldq;
             __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + k0 + p * 8),
-                                             (__attribute__((address_space(3))) void*)(&lds[s][c * 8 * kRowStride]),
+                                             (__attribute__((address_space(3))) void*)(&lds[s][c * 1024]),
                                              16, 0, 0);
         }
     };
@@ -508,6 +528,9 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
                     bf16x8_t, *reinterpret_cast<const u32x4_t*>(Qs + piece_at(wn + 32 * j + frow, piece)));
         };
         fload(0, 0);
+#if HPO_NS_PRIO
+        __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
             const int cur = kk & 1;
@@ -532,21 +555,43 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
             }
 #endif
         }
+#if HPO_NS_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
     };
     const int nk = g.K / kBK;
 #if HPO_NS_DIRECT
-    gload(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-        const int s = kt & 1;
-        gload(s ^ 1, static_cast<int64_t>(kt + 1) * kBK);  /* buffer s ^ 1 was released by the last barrier */
+    /* Stages kt .. kt + kStages - 2 are in flight while stage kt is
+     * computed.  At the top of iteration kt a wavefront waits until its own
+     * loads of stage kt have landed (vmcnt counts its outstanding loads, in
+     * issue order, kChunksPerWave per stage), the barrier makes that true
+     * for every wavefront and retires buffer (kt - 1) % kStages, which then
+     * receives stage kt + kStages - 1. */
+    for (int st = 0; st < kStages - 1 && st < nk; ++st)
+        gload(st, static_cast<int64_t>(st) * kBK);
+    for (int kt = 0; kt < nk; ++kt) {
+        /* gfx9 s_waitcnt encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
+         * lgkmcnt [11:8].  lgkmcnt(0): this wavefront's LDS reads of the
+         * buffer about to be refilled have completed.  The barrier is the
+         * bare instruction: __syncthreads()'s release fence would also wait
+         * for every outstanding load (vmcnt(0)) and drain the pipeline. */
+        constexpr int kAhead = (kStages - 2) * kChunksPerWave;
+        constexpr int kWaitAhead = 0x0070 | (kAhead & 15) | ((kAhead >> 4) << 14);
+        static_assert(kAhead < 64, "vmcnt range");
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + kStages - 2 < nk)
+            __builtin_amdgcn_s_waitcnt(kWaitAhead);
+        else
+            __builtin_amdgcn_s_waitcnt(0x0070);   /* the tail: nothing later was issued */
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const int nxt = kt + kStages - 1;
+        if (nxt < nk)
+            gload(nxt % kStages, static_cast<int64_t>(nxt) * kBK);
 #if HPO_NS_SCHED
         __builtin_amdgcn_sched_barrier(0);
 #endif
-        compute(s);
-        __builtin_amdgcn_s_waitcnt(0);  /* this wavefront's loads of stage kt + 1 are in LDS */
-        __syncthreads();                 /* ... and everyone's; buffer s is free again */
+        compute(kt % kStages);
     }
 #else
     gload(0);
@@ -562,8 +607,8 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
         lstore(s ^ 1);
         __syncthreads();
     }
-#endif
     compute((nk - 1) & 1);
+#endif
 
     /* Epilogue.  acc[i][j][r] holds C[row][col] with
      * row = wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, col = wn + 32 j + lane % 32.
