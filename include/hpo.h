@@ -350,7 +350,7 @@ typedef struct {
 } hpo_muon_cfg;
 
 /* Default workspace cap of a Muon set (see hpo_muon_set_create). */
-#define HPO_MUON_DEFAULT_WORKSPACE (((int64_t)4) << 30)
+#define HPO_MUON_DEFAULT_WORKSPACE (((int64_t)16) << 30)
 
 /* A Muon set over n_matrices row-major matrices: matrix i has rows[i] x
  * cols[i] elements at param[i] (bf16 model param, or NULL / main_param[i]
@@ -364,8 +364,10 @@ typedef struct {
  * workspace for the largest batch: per matrix 4 B per element (the Nesterov
  * gradient) plus bf16 X, two X^T and the two Gram-sized matrices of NS, with
  * both dimensions padded to multiples of 256.  workspace_bytes caps the
- * batch size (0: HPO_MUON_DEFAULT_WORKSPACE); a matrix that alone needs more
- * gets a batch of its own.  hpo_set_info reports the total in device_bytes.
+ * batch size (0: HPO_MUON_DEFAULT_WORKSPACE); a shape class is split into
+ * equal batches under the cap, and a matrix that alone needs more gets a
+ * batch of its own.  Larger batches keep more of the GPU busy in the NS
+ * launches (16 GiB holds 24 of Llama-8B's 4096 x 14336 matrices).  hpo_set_info reports the total in device_bytes.
  * hpo_unscale_check_inf, hpo_grad_global_norm, hpo_grad_global_norm_sets and
  * hpo_copy_main_to_model accept Muon sets; hpo_adamw_step and
  * hpo_step_device do not (HPO_EINVAL). */

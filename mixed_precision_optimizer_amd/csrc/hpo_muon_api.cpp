@@ -365,7 +365,11 @@ hpo_status hpo_muon_set_create(hpo_set* out, int32_t n_matrices, int32_t param_d
         const int32_t cnt = static_cast<int32_t>(members[key].size());
         hpo::MuonBatch proto = shape_batch(key.first, key.second);
         const int64_t per = slot_bytes(proto);
-        const int32_t fit = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(cnt, cap / per)));
+        /* as many matrices per batch as the cap allows, then the class
+         * split into equal batches (no small remainder batch) */
+        const int32_t most = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(cnt, cap / per)));
+        const int32_t n_batches = (cnt + most - 1) / most;
+        const int32_t fit = (cnt + n_batches - 1) / n_batches;
         for (int32_t a = 0; a < cnt; a += fit) {
             hpo::MuonBatch b = proto;
             b.first = k0 + a;
