@@ -85,6 +85,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #ifndef HPO_NS_DIRECT
 #define HPO_NS_DIRECT 1
 #endif
+/* Direct staging through buffer loads (a resource descriptor per operand
+ * panel; per-lane offsets fixed, the k offset in a scalar) instead of
+ * global loads with per-load address arithmetic. */
+#ifndef HPO_NS_BUFFER
+#define HPO_NS_BUFFER 1
+#endif
 /* Pin the interleave of fragment reads and MFMAs with scheduling barriers. */
 #ifndef HPO_NS_SCHED
 #define HPO_NS_SCHED 1
@@ -463,13 +469,43 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
     const uint16_t* __restrict__ P = g.P + z * g.sp + row0 * g.ldp;
     const uint16_t* __restrict__ Q = g.Q + z * g.sq + col0 * g.ldq;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    /* the wavefront index is uniform: keep it scalar so chunk choices, descriptors and the LDS
+     * destination of each load stay in SGPRs */
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 #if HPO_NS_DIRECT
     /* one wavefront load fills 1 KB = kRowsPerChunk rows of one stage, lane
      * l landing in row l / kPieces, physical piece l % kPieces; the lane
      * fetches the logical piece that the swizzle puts there */
     constexpr int kChunks = 2 * kBM / kRowsPerChunk;   /* chunks per stage (P rows, then Q rows) */
     constexpr int kChunksPerWave = kChunks / kWaves;
+#if HPO_NS_BUFFER
+    /* gfx9 buffer descriptor, last dword: 32-bit data format, raw (untyped,
+     * unswizzled) addressing.  Each operand panel is kBM rows from the
+     * tile's first row, so every offset fits 32 bits. */
+    constexpr int kRawBuffer = 0x00020000;
+    const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(P), 0, static_cast<int>(kBM * g.ldp * 2), kRawBuffer);
+    const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Q), 0, static_cast<int>(kBM * g.ldq * 2), kRawBuffer);
+    int voff[kChunksPerWave];
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) {
+        const int c = wave * kChunksPerWave + i;
+        const int r = c * kRowsPerChunk + lane / kPieces;
+        const int p = (lane % kPieces) ^ swizzle(r);
+        voff[i] = r < kBM ? (r * static_cast<int>(g.ldp) + p * 8) * 2 : ((r - kBM) * static_cast<int>(g.ldq) + p * 8) * 2;
+    }
+    auto gload = [&](int s, int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < kChunksPerWave; ++i) {
+            const int c = wave * kChunksPerWave + i;
+            const bool is_p = c * kRowsPerChunk < kBM;   /* uniform per chunk */
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_p ? rsP : rsQ,
+                                                     (__attribute__((address_space(3))) void*)(&lds[s][c * 1024]),
+                                                     16, voff[i], static_cast<int>(k0 * 2), 0, 0);
+        }
+    };
+#else
     auto gload = [&](int s, int64_t k0) {
 #pragma unroll
         for (int i = 0; i < kChunksPerWave; ++i) {
@@ -482,6 +518,7 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
                                              16, 0, 0);
         }
     };
+#endif
 #else
     const int ld_piece = tid % kPieces, ld_row = tid / kPieces;
     u32x4_t rp[kLoads], rq[kLoads];
