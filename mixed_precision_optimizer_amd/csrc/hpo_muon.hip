@@ -57,6 +57,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 /* NS GEMM tiling (compile-time knobs): a workgroup of WAVES_M x WAVES_N
  * wavefronts, each computing TILES_M x TILES_N MFMA tiles of 32 x 32; the k
@@ -356,6 +357,8 @@ struct GemmArgs {
     int64_t ldx, sx;
     uint16_t* XT;        /* step: next X^T */
     int64_t ldxt, sxt;
+    const uint16_t* XS;  /* step / update / out: X^T (rows are columns of X), read by the epilogue */
+    int64_t ldxs, sxs;
     float a, b, c;
     int64_t R, Cn;       /* update / out: natural shape; the C tile is in natural orientation */
     float* out;          /* out epilogue */
@@ -647,104 +650,267 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
     compute((nk - 1) & 1);
 #endif
 
-    /* Epilogue.  acc[i][j][r] holds C[row][col] with
-     * row = wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, col = wn + 32 j + lane % 32.
-     * Symmetric outputs: a diagonal tile stores its upper triangle and
-     * mirrors it; an off-diagonal tile stores itself and its mirror image. */
-    const int64_t lcol = lane & 31;
-    const int64_t lrow4 = 4 * (lane >> 5);
-    const bool diag = SYM && ty == tx;
-    float k1 = 0.0f, k2 = 0.0f;
-    float* __restrict__ W = nullptr;
-    uint16_t* __restrict__ Pm = nullptr;
-    if constexpr (EPI == kEpiUpdate) {
-        const int32_t mat = g.first + static_cast<int32_t>(z);
-        const MuonInfo in = g.info[mat];
-        const double lr = up.lr[in.group], wd = up.wd[in.group];
-        k1 = static_cast<float>(1.0 - lr * wd);
-        k2 = static_cast<float>(lr * update_scale(in.rows, in.cols, up));
-        W = g.desc[mat].master;
-        Pm = up.param_dtype == HPO_PARAM_FP32 ? nullptr : static_cast<uint16_t*>(g.desc[mat].param);
-    }
+    /* Staged epilogue.  acc[ti][tj][r] holds C[i][j] (tile coordinates) with
+     * i = wm + 32 ti + 8 (r / 4) + 4 (lane / 32) + r % 4 and
+     * j = wn + 32 tj + lane % 32: four consecutive rows of one column per
+     * group of four registers.  The stage buffers are free once every
+     * wavefront has left the k-loop; they then hold the bf16 tile
+     * column-major (Tt[j][i] = C[i][j]), so such a group is one 8-byte LDS
+     * access, the transposed copy of the tile leaves with 16-byte LDS reads
+     * and the row-major copy gathers 8 x 4 blocks with 8-byte reads.  The
+     * 16-byte chunks of column j are XOR-permuted by f(j) = (j ^ j / 8) % 16:
+     * each of the three access patterns then spreads over all banks.  For the
+     * master update the fp32 output goes through LDS half a tile at a time
+     * (row-major, a 32-float XOR that separates the two row halves of a
+     * wavefront's access).  Global traffic is whole 16-byte pieces, eight
+     * lanes per 128-byte line. */
+    {
+        static_assert(kBM == 256 && kNsThreads == 1024, "the staged epilogue's thread maps assume 256 x 256 tiles and 1024 threads");
+        static_assert(kStages * kStageBytes >= kBM * kBM * 2, "LDS holds a bf16 C tile");
+        static_assert(kStages * kStageBytes >= (kBM / 2) * kBM * 4, "LDS holds half an fp32 C tile");
+        constexpr int kCPR = kBM / 8;                        /* 16-byte chunks per tile column */
+        constexpr int kPieces = kBM * kCPR / kNsThreads;     /* 16-byte pieces per thread */
+        uint16_t* Tt = reinterpret_cast<uint16_t*>(&lds[0][0]);
+        float* T32 = reinterpret_cast<float*>(&lds[0][0]);
+        /* element offset of C[i][j] */
+        auto tt = [](int j, int i) {
+            return j * kBM + ((((i >> 3) ^ ((j ^ (j >> 3)) & 15)) & (kCPR - 1)) << 3) + (i & 7);
+        };
+        /* Tt[j][.] = src[j][.] : src holds C^T row-major (row j = column j of C) */
+        auto stage_in = [&](const uint16_t* src, int64_t ld) {
+            u32x4_t v[kPieces];   /* all loads in flight before the first LDS write */
 #pragma clang loop unroll(full)
-    for (int i = 0; i < kTM; ++i) {
+            for (int k = 0; k < kPieces; ++k) {
+                const int idx = tid + k * kNsThreads, j = idx / kCPR, i = (idx % kCPR) * 8;
+                v[k] = *reinterpret_cast<const u32x4_t*>(src + j * ld + i);
+            }
 #pragma clang loop unroll(full)
-        for (int j = 0; j < kTN; ++j) {
-            const int64_t col = col0 + wn + 32 * j + lcol;
+            for (int k = 0; k < kPieces; ++k) {
+                const int idx = tid + k * kNsThreads, j = idx / kCPR, i = (idx % kCPR) * 8;
+                *reinterpret_cast<u32x4_t*>(Tt + tt(j, i)) = v[k];
+            }
+        };
+        /* dst[j][i] = C[i][j] */
+        auto store_t = [&](uint16_t* dst, int64_t ld) {
 #pragma clang loop unroll(full)
-            for (int q = 0; q < 4; ++q) {
-                const int64_t rbase = row0 + wm + 32 * i + 8 * q + lrow4;
-                float v[4];
+            for (int k = 0; k < kPieces; ++k) {
+                const int idx = tid + k * kNsThreads, j = idx / kCPR, i = (idx % kCPR) * 8;
+                *reinterpret_cast<u32x4_t*>(dst + j * ld + i) = *reinterpret_cast<const u32x4_t*>(Tt + tt(j, i));
+            }
+        };
+        /* dst[i][j] = C[i][j]: a thread moves 4 rows x 8 columns per block;
+         * of 32 consecutive blocks, 16 run along a row pair (jb) and the
+         * lowest bit picks the row quad (par) */
+        auto store_n = [&](uint16_t* dst, int64_t ld) {
 #pragma clang loop unroll(full)
-                for (int e = 0; e < 4; ++e)
-                    v[e] = acc[i][j][4 * q + e];
-                if constexpr (EPI == kEpiGram || EPI == kEpiPoly) {
-                    uint16_t* __restrict__ Cz = g.C + z * g.sc;
-                    uint32_t bits[4];
+            for (int k = 0; k < 2; ++k) {
+                const int bidx = tid + k * kNsThreads;
+                const int par = bidx & 1, jb = ((bidx >> 1) & 15) | (((bidx >> 5) & 1) << 4), ic = bidx >> 6;
+                const int i0 = 8 * ic + 4 * par, j0 = 8 * jb;
+                u32x2_t v[8];
 #pragma clang loop unroll(full)
-                    for (int e = 0; e < 4; ++e) {
-                        float x = v[e];
-                        if constexpr (EPI == kEpiPoly) {
-                            const float a = bf16v(g.P[z * g.sp + (rbase + e) * g.ldp + col]);
-                            const float bv = g.b * a;
-                            const float cv = g.c * x;
-                            x = bv + cv;
-                        }
-                        bits[e] = bf16_rne_bits(x);
-                    }
-                    if (!diag) {
+                for (int e = 0; e < 8; ++e)
+                    v[e] = *reinterpret_cast<const u32x2_t*>(Tt + tt(j0 + e, i0));
+#pragma clang loop unroll(full)
+                for (int r = 0; r < 4; ++r) {
+                    const int sh = 16 * (r & 1);
+                    auto el = [&](int e) { return ((r < 2 ? v[e].x : v[e].y) >> sh) & 0xffffu; };
+                    u32x4_t o;
+                    o.x = el(0) | (el(1) << 16);
+                    o.y = el(2) | (el(3) << 16);
+                    o.z = el(4) | (el(5) << 16);
+                    o.w = el(6) | (el(7) << 16);
+                    *reinterpret_cast<u32x4_t*>(dst + (i0 + r) * ld + j0) = o;
+                }
+            }
+        };
+        const int lcol = lane & 31, lrow4 = 4 * (lane >> 5);
+        auto pack4 = [](float a0, float a1, float a2, float a3) {
+            u32x2_t t;
+            t.x = bf16_rne_bits(a0) | (bf16_rne_bits(a1) << 16);
+            t.y = bf16_rne_bits(a2) | (bf16_rne_bits(a3) << 16);
+            return t;
+        };
+        auto unpack = [](u32x2_t t, int e) {
+            const uint32_t w = e < 2 ? t.x : t.y;
+            return bf16v(static_cast<uint16_t>(e & 1 ? w >> 16 : w & 0xffffu));
+        };
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();   /* every wavefront is past its last fragment read */
+        if constexpr (EPI == kEpiGram || EPI == kEpiPoly) {
+            const bool diag = SYM && ty == tx;
+            if constexpr (EPI == kEpiPoly) {
+                /* A is symmetric and stored whole: column j of the tile is row col0 + j */
+                stage_in(g.P + z * g.sp + col0 * g.ldp + row0, g.ldp);
+                __syncthreads();
+            }
+#pragma clang loop unroll(full)
+            for (int ti = 0; ti < kTM; ++ti)
+#pragma clang loop unroll(full)
+                for (int tj = 0; tj < kTN; ++tj) {
+#pragma clang loop unroll(full)
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = wm + 32 * ti + 8 * q + lrow4, j = wn + 32 * tj + lcol;
+                        u32x2_t* pt = reinterpret_cast<u32x2_t*>(Tt + tt(j, i));
+                        float x[4];
 #pragma clang loop unroll(full)
                         for (int e = 0; e < 4; ++e)
-                            Cz[(rbase + e) * g.ldc + col] = static_cast<uint16_t>(bits[e]);
-                        if constexpr (SYM) {
-                            u32x2_t t;
-                            t.x = bits[0] | (bits[1] << 16);
-                            t.y = bits[2] | (bits[3] << 16);
-                            *reinterpret_cast<u32x2_t*>(Cz + col * g.ldc + rbase) = t;
+                            x[e] = acc[ti][tj][4 * q + e];
+                        if constexpr (EPI == kEpiPoly) {
+                            const u32x2_t av = *pt;
+#pragma clang loop unroll(full)
+                            for (int e = 0; e < 4; ++e) {
+                                const float bv = g.b * unpack(av, e);
+                                const float cv = g.c * x[e];
+                                x[e] = bv + cv;
+                            }
                         }
-                    } else {
+                        *pt = pack4(x[0], x[1], x[2], x[3]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   /* one 32 x 32 block at a time */
+                }
+            __syncthreads();
+            if (diag) {
+                /* the lower triangle of a diagonal tile is the mirror of its upper one */
+#pragma clang loop unroll(full)
+                for (int k = 0; k < kBM * kBM / kNsThreads; ++k) {
+                    const int idx = tid + k * kNsThreads, j = idx / kBM, i = idx % kBM;
+                    if (i > j)
+                        Tt[tt(j, i)] = Tt[tt(i, j)];
+                }
+                __syncthreads();
+            }
+            uint16_t* Cz = g.C + z * g.sc;
+            store_n(Cz + row0 * g.ldc + col0, g.ldc);
+            if (SYM && !diag)
+                store_t(Cz + col0 * g.ldc + row0, g.ldc);   /* the mirror tile */
+        } else if constexpr (EPI == kEpiStep) {
+            stage_in(g.XS + z * g.sxs + col0 * g.ldxs + row0, g.ldxs);
+            __syncthreads();
+#pragma clang loop unroll(full)
+            for (int ti = 0; ti < kTM; ++ti)
+#pragma clang loop unroll(full)
+                for (int tj = 0; tj < kTN; ++tj) {
+#pragma clang loop unroll(full)
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = wm + 32 * ti + 8 * q + lrow4, j = wn + 32 * tj + lcol;
+                        u32x2_t* pt = reinterpret_cast<u32x2_t*>(Tt + tt(j, i));
+                        const u32x2_t xv = *pt;
+                        float x[4];
 #pragma clang loop unroll(full)
                         for (int e = 0; e < 4; ++e) {
-                            const int64_t row = rbase + e;
-                            if (row <= col)
-                                Cz[row * g.ldc + col] = static_cast<uint16_t>(bits[e]);
-                            if (row < col)
-                                Cz[col * g.ldc + row] = static_cast<uint16_t>(bits[e]);
+                            const float ax = g.a * unpack(xv, e);
+                            x[e] = ax + acc[ti][tj][4 * q + e];
+                        }
+                        *pt = pack4(x[0], x[1], x[2], x[3]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            __syncthreads();
+            store_n(g.X + z * g.sx + row0 * g.ldx + col0, g.ldx);
+            store_t(g.XT + z * g.sxt + col0 * g.ldxt + row0, g.ldxt);
+        } else {
+            /* last step: O = a X + acc in fp32 (registers), then the master
+             * update (or O itself) streamed by rows, half a tile at a time.
+             * The per-matrix factors are wave-uniform: kept in scalar
+             * registers, computed before the tile work. */
+            float k1 = 0.0f, k2 = 0.0f;
+            float* __restrict__ W = nullptr;
+            uint16_t* __restrict__ Pm = nullptr;
+            if constexpr (EPI == kEpiUpdate) {
+                const int32_t mat = g.first + static_cast<int32_t>(z);
+                const MuonInfo in = g.info[mat];
+                const double lr = up.lr[in.group], wd = up.wd[in.group];
+                k1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                         __builtin_bit_cast(int, static_cast<float>(1.0 - lr * wd))));
+                k2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                         __builtin_bit_cast(int, static_cast<float>(lr * update_scale(in.rows, in.cols, up)))));
+                W = g.desc[mat].master;
+                Pm = up.param_dtype == HPO_PARAM_FP32 ? nullptr : static_cast<uint16_t*>(g.desc[mat].param);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            stage_in(g.XS + z * g.sxs + col0 * g.ldxs + row0, g.ldxs);
+            __syncthreads();
+#pragma clang loop unroll(full)
+            for (int ti = 0; ti < kTM; ++ti)
+#pragma clang loop unroll(full)
+                for (int tj = 0; tj < kTN; ++tj) {
+#pragma clang loop unroll(full)
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = wm + 32 * ti + 8 * q + lrow4, j = wn + 32 * tj + lcol;
+                        const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(Tt + tt(j, i));
+#pragma clang loop unroll(full)
+                        for (int e = 0; e < 4; ++e) {
+                            const float ax = g.a * unpack(xv, e);
+                            acc[ti][tj][4 * q + e] = ax + acc[ti][tj][4 * q + e];
                         }
                     }
-                } else if constexpr (EPI == kEpiStep) {
-                    uint16_t* __restrict__ Xz = g.X + z * g.sx;
-                    uint32_t bits[4];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            /* whole float4 pieces when every row starts 16-byte aligned (W always is) */
+            const bool vec = (g.Cn & 3) == 0 &&
+                             (EPI == kEpiUpdate || (reinterpret_cast<uintptr_t>(g.out) & 15) == 0);
+            constexpr int kHalf = kBM / 2;
+            /* row-major half tile; column bit 5 flipped on rows with bit 2 set */
+            auto t32 = [](int i, int j) { return i * kBM + (j ^ (((i >> 2) & 1) << 5)); };
+            static_assert(kHalf % (32 * kTM) == 0, "a wavefront's rows lie in one half");
 #pragma clang loop unroll(full)
-                    for (int e = 0; e < 4; ++e) {
-                        uint16_t* px = Xz + (rbase + e) * g.ldx + col;
-                        const float ax = g.a * bf16v(*px);
-                        bits[e] = bf16_rne_bits(ax + v[e]);
-                        *px = static_cast<uint16_t>(bits[e]);
-                    }
-                    u32x2_t t;
-                    t.x = bits[0] | (bits[1] << 16);
-                    t.y = bits[2] | (bits[3] << 16);
-                    *reinterpret_cast<u32x2_t*>(g.XT + z * g.sxt + col * g.ldxt + rbase) = t;
-                } else {
-                    const uint16_t* __restrict__ Xz = g.X + z * g.sx;
+            for (int h = 0; h < 2; ++h) {
+                __syncthreads();   /* Tt / the previous half is no longer read */
+                if (wm / kHalf == h) {
 #pragma clang loop unroll(full)
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t row = rbase + e;
-                        const float ax = g.a * bf16v(Xz[row * g.ldx + col]);
-                        const float o = ax + v[e];
-                        if (row < g.R && col < g.Cn) {
-                            const int64_t idx = row * g.Cn + col;
+                    for (int ti = 0; ti < kTM; ++ti)
+#pragma clang loop unroll(full)
+                        for (int tj = 0; tj < kTN; ++tj)
+#pragma clang loop unroll(full)
+                            for (int r = 0; r < 16; ++r) {
+                                const int i = wm - h * kHalf + 32 * ti + 8 * (r >> 2) + lrow4 + (r & 3);
+                                const int j = wn + 32 * tj + lcol;
+                                T32[t32(i, j)] = acc[ti][tj][r];
+                            }
+                }
+                __syncthreads();
+#pragma clang loop unroll(disable)
+                for (int idx = tid; idx < kHalf * (kBM / 4); idx += kNsThreads) {
+                    const int rr = idx / (kBM / 4), c = (idx % (kBM / 4)) * 4;
+                    const int64_t nr = row0 + h * kHalf + rr, nc = col0 + c;
+                    if (nr >= g.R || nc >= g.Cn)
+                        continue;
+                    const f32x4_t o = *reinterpret_cast<const f32x4_t*>(T32 + t32(rr, c));
+                    const int64_t base = nr * g.Cn + nc;
+                    if (vec) {   /* nc + 3 < Cn: Cn and nc are multiples of 4 */
+                        if constexpr (EPI == kEpiUpdate) {
+                            f32x4_t w = *reinterpret_cast<const f32x4_t*>(W + base);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float x = w[e] * k1;   /* decoupled decay first ([HANDBOOK] listing) */
+                                const float u = k2 * o[e];
+                                w[e] = x - u;
+                            }
+                            *reinterpret_cast<f32x4_t*>(W + base) = w;
+                            if (Pm != nullptr) {
+                                u32x2_t pb;
+                                pb.x = bf16_rne_bits(w[0]) | (bf16_rne_bits(w[1]) << 16);
+                                pb.y = bf16_rne_bits(w[2]) | (bf16_rne_bits(w[3]) << 16);
+                                *reinterpret_cast<u32x2_t*>(Pm + base) = pb;
+                            }
+                        } else {
+                            *reinterpret_cast<f32x4_t*>(g.out + base) = o;
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (nc + e >= g.Cn)
+                                break;
                             if constexpr (EPI == kEpiUpdate) {
-                                float w = W[idx];
-                                w = w * k1;             /* decoupled decay first ([HANDBOOK] listing) */
-                                const float u = k2 * o;
+                                float w = W[base + e] * k1;
+                                const float u = k2 * o[e];
                                 w = w - u;
-                                W[idx] = w;
+                                W[base + e] = w;
                                 if (Pm != nullptr)
-                                    Pm[idx] = static_cast<uint16_t>(bf16_rne_bits(w));
+                                    Pm[base + e] = static_cast<uint16_t>(bf16_rne_bits(w));
                             } else {
-                                g.out[idx] = o;
+                                g.out[base + e] = o[e];
                             }
                         }
                     }
@@ -821,6 +987,7 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
     g.K = static_cast<int32_t>(mp);
     g.X = w.X; g.ldx = np; g.sx = mp * np;
     g.XT = w.XT[cur ^ 1]; g.ldxt = mp; g.sxt = np * mp;
+    g.XS = w.XT[cur]; g.ldxs = mp; g.sxs = np * mp;
     g.a = a;
     g.nx = static_cast<int32_t>(np / kBM);
     g.ny = static_cast<int32_t>(mp / kBM);
@@ -838,6 +1005,7 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
         g.P = w.XT[cur]; g.ldp = mp; g.sp = np * mp;
         g.Q = w.B; g.ldq = mp; g.sq = mp * mp;
         g.X = w.XT[cur]; g.ldx = mp; g.sx = np * mp;
+        g.XS = w.X; g.ldxs = np; g.sxs = mp * np;
         g.nx = static_cast<int32_t>(mp / kBM);
         g.ny = static_cast<int32_t>(np / kBM);
         g.R = b.n;
