@@ -59,39 +59,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-/* NS GEMM tiling (compile-time knobs): a workgroup of WAVES_M x WAVES_N
- * wavefronts, each computing TILES_M x TILES_N MFMA tiles of 32 x 32; the k
- * depth of one LDS stage. */
-#ifndef HPO_NS_WAVES_M
-#define HPO_NS_WAVES_M 4
-#endif
-#ifndef HPO_NS_WAVES_N
-#define HPO_NS_WAVES_N 4
-#endif
-#ifndef HPO_NS_TILES_M
-#define HPO_NS_TILES_M 2
-#endif
-#ifndef HPO_NS_TILES_N
-#define HPO_NS_TILES_N 2
-#endif
-#ifndef HPO_NS_BK
-#define HPO_NS_BK 64
-#endif
-/* LDS stages in flight (direct staging): loads run STAGES - 1 stages ahead. */
-#ifndef HPO_NS_STAGES
-#define HPO_NS_STAGES 2
-#endif
-/* Stage operands with direct global -> LDS loads (no register staging, no
- * LDS store instructions); rows are then XOR-swizzled instead of padded. */
-#ifndef HPO_NS_DIRECT
-#define HPO_NS_DIRECT 1
-#endif
-/* Direct staging through buffer loads (a resource descriptor per operand
- * panel; per-lane offsets fixed, the k offset in a scalar) instead of
- * global loads with per-load address arithmetic. */
-#ifndef HPO_NS_BUFFER
-#define HPO_NS_BUFFER 1
-#endif
 /* Pin the interleave of fragment reads and MFMAs with scheduling barriers. */
 #ifndef HPO_NS_SCHED
 #define HPO_NS_SCHED 1
@@ -105,30 +72,57 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #ifndef HPO_NS_GROUP
 #define HPO_NS_GROUP 8
 #endif
-constexpr int kWavesM = HPO_NS_WAVES_M, kWavesN = HPO_NS_WAVES_N;
-constexpr int kTM = HPO_NS_TILES_M, kTN = HPO_NS_TILES_N;
-constexpr int kWaves = kWavesM * kWavesN;
-constexpr int kNsThreads = 64 * kWaves;
-constexpr int kBM = kWavesM * kTM * 32;          /* C tile is kBM x kBM */
-static_assert(kBM == kWavesN * kTN * 32, "square C tiles (symmetric outputs mirror them)");
-constexpr int kBK = HPO_NS_BK;
-constexpr int kPieces = kBK / 8;                 /* 16-byte pieces per operand row and stage */
-#if HPO_NS_DIRECT
-constexpr int kRowStride = kBK * 2;              /* pieces XOR-swizzled by row (see piece_at) */
-constexpr int kStages = HPO_NS_STAGES;
-constexpr int kRowsPerChunk = 1024 / kRowStride; /* rows one wavefront load (64 x 16 B) fills */
-static_assert(kBK == 64 || kBK == 32, "direct staging: rows of 128 or 64 B");
-static_assert((2 * kBM / kRowsPerChunk) % kWaves == 0, "stage chunks split evenly over the wavefronts");
-static_assert(kStages >= 2, "at least double buffering");
-#else
-constexpr int kStages = 2;
-constexpr int kRowStride = kBK * 2 + 16;         /* one piece of padding: conflict-free fragment reads */
+/* NS GEMM tile configurations.  A workgroup of WM x WN wavefronts computes
+ * a (WM * TM * 32) x (WN * TN * 32) tile of C, each wavefront TM x TN MFMA
+ * tiles of 32 x 32; operands go through LDS in k-stages of BK (STAGES
+ * buffers, loads running STAGES - 1 stages ahead); WG is the number of
+ * workgroups meant to share a CU (it caps the registers so they fit). */
+template <int WM, int WN, int TM, int TN, int BK, int STAGES, int WG>
+struct NsTile {
+    static constexpr int kWavesM = WM, kWavesN = WN, kTM = TM, kTN = TN, kBK = BK, kStages = STAGES;
+    static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+    static constexpr int kBM = WM * TM * 32, kBN = WN * TN * 32;   /* C tile: kBM rows x kBN columns */
+    static constexpr int kWavesPerSimd = WG * kWaves / 4;
+    static constexpr int kPieces = BK / 8;                /* 16-byte pieces per operand row and stage */
+    static constexpr int kRowStride = BK * 2;             /* pieces XOR-swizzled by row (see piece_at) */
+    static constexpr int kRowsPerChunk = 1024 / kRowStride;   /* rows one wavefront load (64 x 16 B) fills */
+    static constexpr int kStageBytes = (kBM + kBN) * kRowStride;
+    static constexpr int kChunks = (kBM + kBN) / kRowsPerChunk;   /* chunks per stage (P rows, then Q rows) */
+    static constexpr int kChunksPerWave = kChunks / kWaves;
+    /* the epilogue reuses the stages: a bf16 C tile, or half of it in fp32 */
+    static constexpr int kEpiBytes = kBM * kBN * 2 > kBM / 2 * kBN * 4 ? kBM * kBN * 2 : kBM / 2 * kBN * 4;
+    static constexpr int kLdsBytes = STAGES * kStageBytes > kEpiBytes ? STAGES * kStageBytes : kEpiBytes;
+    static_assert(BK == 64 || BK == 32, "direct staging: rows of 128 or 64 B");
+    static_assert(kChunks % kWaves == 0, "stage chunks split evenly over the wavefronts");
+    static_assert(STAGES >= 2, "at least double buffering");
+    static_assert(kNsPad % kBM == 0 && kNsPad % kBN == 0 && kNsPad % BK == 0, "padding covers the tiles");
+    static_assert(kBM == 256 && (kBN == 256 || kBN == 128), "the epilogue's thread maps");
+    static_assert(kLdsBytes * WG <= 160 * 1024, "the workgroups of a CU fit its LDS");
+};
+/* Symmetric outputs (A = XX^T, B = bA + cAA^T) mirror whole tiles: square,
+ * 1024 lanes, one workgroup per CU. */
+using SymTile = NsTile<4, 4, 2, 2, 64, 2, 1>;
+/* General outputs (X' = aX + BX and the last step) take SymTile.
+ * HPO_NS_GEN_HALF = 1 selects 256 x 128 tiles of 512 lanes instead, two
+ * workgroups per CU (k-stages of HPO_NS_GEN_BK in HPO_NS_GEN_STAGES
+ * buffers), so that one workgroup's barriers and stores could overlap the
+ * other's MFMAs.  Measured on the MLP batch it is slower (X' = aX + BX at
+ * 920-940 TFLOP/s against 1135): the k-stages of 32 double the barriers and
+ * the narrower tile reads 1.5x the operand bytes per flop. */
+#ifndef HPO_NS_GEN_HALF
+#define HPO_NS_GEN_HALF 0
 #endif
-constexpr int kStageBytes = 2 * kBM * kRowStride;
-constexpr int kRowsPerPass = kNsThreads / kPieces;
-constexpr int kLoads = kBM / kRowsPerPass;       /* 16-byte global loads per operand per lane and stage */
-static_assert(kNsPad % kBM == 0 && kNsPad % kBK == 0, "padding covers the tiles");
-static_assert(kBK % 16 == 0 && kBM % kRowsPerPass == 0, "tiling");
+#ifndef HPO_NS_GEN_BK
+#define HPO_NS_GEN_BK 32
+#endif
+#ifndef HPO_NS_GEN_STAGES
+#define HPO_NS_GEN_STAGES 2
+#endif
+#if HPO_NS_GEN_HALF
+using GenTile = NsTile<4, 2, 2, 2, HPO_NS_GEN_BK, HPO_NS_GEN_STAGES, 2>;
+#else
+using GenTile = SymTile;
+#endif
 constexpr int kTile = 64;              /* transpose tile of the input kernel */
 
 /* ---------------------------------------------------------------------- */
@@ -388,23 +382,28 @@ __device__ __forceinline__ double update_scale(int64_t rows, int64_t cols, const
 /* Byte offset of 16-byte piece p of LDS row r.  Direct staging stores row r's
  * pieces permuted by an XOR with (r & 7) ^ ((r >> 3) & 1): the 16 (or 8) rows
  * that one fragment read serves per LDS cycle then land on distinct banks
- * whether the LDS has 64 or 32 four-byte banks.  Padded rows need no
- * permutation. */
+ * whether the LDS has 64 or 32 four-byte banks. */
+template <int BK>
 __device__ __forceinline__ int swizzle(int r)
 {
-    if constexpr (kBK == 64)
+    if constexpr (BK == 64)
         return (r & 7) ^ ((r >> 3) & 1);   /* 8 pieces per row */
     else
         return (r ^ (r >> 2)) & 3;         /* 4 pieces per row */
 }
 
+template <int BK>
 __device__ __forceinline__ int piece_at(int r, int p)
 {
-#if HPO_NS_DIRECT
-    return r * kRowStride + ((p ^ swizzle(r)) << 4);
-#else
-    return r * kRowStride + (p << 4);
-#endif
+    return r * (BK * 2) + ((p ^ swizzle<BK>(r)) << 4);
+}
+
+/* One wavefront load of 64 x 16 bytes from a buffer straight into LDS: lane
+ * l's piece lands at dst + 16 l.  (A plain device function: the host pass
+ * of a kernel template does not take this builtin in a dependent context.) */
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst, int voff, int soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
 /* Tile of the t-th workgroup in dispatch order.  Workgroups go to the 8
@@ -458,44 +457,46 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, int64_t& ty, int64_t&
     }
 }
 
-template <int EPI, bool SYM>
-__global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate up)
+template <int EPI, bool SYM, class T>
+__global__ __launch_bounds__(T::kThreads, T::kWavesPerSimd) void k_ns_gemm(GemmArgs g, MuonUpdate up)
 {
+    constexpr int kWavesN = T::kWavesN, kTM = T::kTM, kTN = T::kTN, kBK = T::kBK, kStages = T::kStages;
+    constexpr int kBM = T::kBM, kBN = T::kBN, kNsThreads = T::kThreads;
+    constexpr int kRowStride = T::kRowStride, kPieces = T::kPieces, kRowsPerChunk = T::kRowsPerChunk;
+    constexpr int kStageBytes = T::kStageBytes, kChunksPerWave = T::kChunksPerWave;
+    static_assert(!SYM || kBM == kBN, "symmetric outputs mirror square tiles");
     if (!gate_open(g.gate))
         return;
-    __shared__ __attribute__((aligned(16))) char lds[kStages][kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes];
     const int64_t z = blockIdx.z;
     int64_t ty, tx;
     tile_of<SYM>(g, ty, tx);
     const int64_t row0 = ty * kBM;
-    const int64_t col0 = tx * kBM;
+    const int64_t col0 = tx * kBN;
     const uint16_t* __restrict__ P = g.P + z * g.sp + row0 * g.ldp;
     const uint16_t* __restrict__ Q = g.Q + z * g.sq + col0 * g.ldq;
     const int tid = threadIdx.x;
     /* the wavefront index is uniform: keep it scalar so chunk choices, descriptors and the LDS
      * destination of each load stay in SGPRs */
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-#if HPO_NS_DIRECT
-    /* one wavefront load fills 1 KB = kRowsPerChunk rows of one stage, lane
-     * l landing in row l / kPieces, physical piece l % kPieces; the lane
-     * fetches the logical piece that the swizzle puts there */
-    constexpr int kChunks = 2 * kBM / kRowsPerChunk;   /* chunks per stage (P rows, then Q rows) */
-    constexpr int kChunksPerWave = kChunks / kWaves;
-#if HPO_NS_BUFFER
-    /* gfx9 buffer descriptor, last dword: 32-bit data format, raw (untyped,
-     * unswizzled) addressing.  Each operand panel is kBM rows from the
-     * tile's first row, so every offset fits 32 bits. */
+    /* Operands go straight from global memory into LDS.  One wavefront load
+     * fills 1 KB = kRowsPerChunk rows of one stage, lane l landing in row
+     * l / kPieces, physical piece l % kPieces; the lane fetches the logical
+     * piece that the swizzle puts there.  gfx9 buffer descriptor, last dword:
+     * 32-bit data format, raw (untyped, unswizzled) addressing.  Each operand
+     * panel is the tile's rows (P) or columns (Q) from its first one, so every
+     * offset fits 32 bits. */
     constexpr int kRawBuffer = 0x00020000;
     const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(P), 0, static_cast<int>(kBM * g.ldp * 2), kRawBuffer);
     const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(Q), 0, static_cast<int>(kBM * g.ldq * 2), kRawBuffer);
+        const_cast<uint16_t*>(Q), 0, static_cast<int>(kBN * g.ldq * 2), kRawBuffer);
     int voff[kChunksPerWave];
 #pragma unroll
     for (int i = 0; i < kChunksPerWave; ++i) {
         const int c = wave * kChunksPerWave + i;
         const int r = c * kRowsPerChunk + lane / kPieces;
-        const int p = (lane % kPieces) ^ swizzle(r);
+        const int p = (lane % kPieces) ^ swizzle<kBK>(r);
         voff[i] = r < kBM ? (r * static_cast<int>(g.ldp) + p * 8) * 2 : ((r - kBM) * static_cast<int>(g.ldq) + p * 8) * 2;
     }
     auto gload = [&](int s, int64_t k0) {
@@ -503,44 +504,9 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
         for (int i = 0; i < kChunksPerWave; ++i) {
             const int c = wave * kChunksPerWave + i;
             const bool is_p = c * kRowsPerChunk < kBM;   /* uniform per chunk */
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_p ? rsP : rsQ,
-                                                     (__attribute__((address_space(3))) void*)(&lds[s][c * 1024]),
-                                                     16, voff[i], static_cast<int>(k0 * 2), 0, 0);
+            buffer_load_lds16(is_p ? rsP : rsQ, &lds[s * kStageBytes + c * 1024], voff[i], static_cast<int>(k0 * 2));
         }
     };
-#else
-    auto gload = [&](int s, int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < kChunksPerWave; ++i) {
-            const int c = wave * kChunksPerWave + i;
-            const int r = c * kRowsPerChunk + lane / kPieces;
-            const int p = (lane % kPieces) ^ swizzle(r);
-            const uint16_t* src = r < kBM ? P + r * g.ldp : Q + (r - kBM) * g.ldq;
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + k0 + p * 8),
-                                             (__attribute__((address_space(3))) void*)(&lds[s][c * 1024]),
-                                             16, 0, 0);
-        }
-    };
-#endif
-#else
-    const int ld_piece = tid % kPieces, ld_row = tid / kPieces;
-    u32x4_t rp[kLoads], rq[kLoads];
-    auto gload = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            rp[i] = *reinterpret_cast<const u32x4_t*>(P + (ld_row + kRowsPerPass * i) * g.ldp + k0 + ld_piece * 8);
-            rq[i] = *reinterpret_cast<const u32x4_t*>(Q + (ld_row + kRowsPerPass * i) * g.ldq + k0 + ld_piece * 8);
-        }
-    };
-    auto lstore = [&](int s) {
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int off = (ld_row + kRowsPerPass * i) * kRowStride + ld_piece * 16;
-            *reinterpret_cast<u32x4_t*>(&lds[s][off]) = rp[i];
-            *reinterpret_cast<u32x4_t*>(&lds[s][kBM * kRowStride + off]) = rq[i];
-        }
-    };
-#endif
     const int wm = (wave / kWavesN) * 32 * kTM, wn = (wave % kWavesN) * 32 * kTN;
     const int frow = lane & 31, fhalf = lane >> 5;
     f32x16_t acc[kTM][kTN];
@@ -553,19 +519,19 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
      * while the MFMAs of slice kk run; the scheduling barriers keep the
      * compiler from sinking the reads next to their uses. */
     auto compute = [&](int s) {
-        const char* Ps = lds[s];
-        const char* Qs = lds[s] + kBM * kRowStride;
+        const char* Ps = lds + s * kStageBytes;
+        const char* Qs = Ps + kBM * kRowStride;
         bf16x8_t fa[2][kTM], fb[2][kTN];
         auto fload = [&](int kk, int buf) {
             const int piece = kk * 2 + fhalf;  /* lanes 0-31: k 0..7 of the slice, 32-63: k 8..15 */
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
                 fa[buf][i] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Ps + piece_at(wm + 32 * i + frow, piece)));
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Ps + piece_at<kBK>(wm + 32 * i + frow, piece)));
 #pragma unroll
             for (int j = 0; j < kTN; ++j)
                 fb[buf][j] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Qs + piece_at(wn + 32 * j + frow, piece)));
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Qs + piece_at<kBK>(wn + 32 * j + frow, piece)));
         };
         fload(0, 0);
 #if HPO_NS_PRIO
@@ -600,7 +566,6 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
 #endif
     };
     const int nk = g.K / kBK;
-#if HPO_NS_DIRECT
     /* Stages kt .. kt + kStages - 2 are in flight while stage kt is
      * computed.  At the top of iteration kt a wavefront waits until its own
      * loads of stage kt have landed (vmcnt counts its outstanding loads, in
@@ -633,22 +598,6 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
 #endif
         compute(kt % kStages);
     }
-#else
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-        const int s = kt & 1;
-        gload(static_cast<int64_t>(kt + 1) * kBK);
-#if HPO_NS_SCHED
-        __builtin_amdgcn_sched_barrier(0);  /* the next stage's loads go out before this stage's math */
-#endif
-        compute(s);
-        lstore(s ^ 1);
-        __syncthreads();
-    }
-    compute((nk - 1) & 1);
-#endif
 
     /* Staged epilogue.  acc[ti][tj][r] holds C[i][j] (tile coordinates) with
      * i = wm + 32 ti + 8 (r / 4) + 4 (lane / 32) + r % 4 and
@@ -665,27 +614,28 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
      * wavefront's access).  Global traffic is whole 16-byte pieces, eight
      * lanes per 128-byte line. */
     {
-        static_assert(kBM == 256 && kNsThreads == 1024, "the staged epilogue's thread maps assume 256 x 256 tiles and 1024 threads");
-        static_assert(kStages * kStageBytes >= kBM * kBM * 2, "LDS holds a bf16 C tile");
-        static_assert(kStages * kStageBytes >= (kBM / 2) * kBM * 4, "LDS holds half an fp32 C tile");
         constexpr int kCPR = kBM / 8;                        /* 16-byte chunks per tile column */
-        constexpr int kPieces = kBM * kCPR / kNsThreads;     /* 16-byte pieces per thread */
-        uint16_t* Tt = reinterpret_cast<uint16_t*>(&lds[0][0]);
-        float* T32 = reinterpret_cast<float*>(&lds[0][0]);
+        constexpr int kEpiPieces = kBN * kCPR / kNsThreads;  /* 16-byte pieces per thread */
+        constexpr int kJB = kBN / 8;                         /* 8-column blocks per tile row */
+        constexpr int kBlocks = (kBM / 4) * kJB / kNsThreads;   /* 4 x 8 blocks per thread */
+        static_assert(kEpiPieces * kNsThreads == kBN * kCPR && kBlocks * kNsThreads == (kBM / 4) * kJB, "whole pieces");
+        static_assert(kCPR >= 16 && (kJB == 16 || kJB == 32), "bank maps");
+        uint16_t* Tt = reinterpret_cast<uint16_t*>(lds);
+        float* T32 = reinterpret_cast<float*>(lds);
         /* element offset of C[i][j] */
         auto tt = [](int j, int i) {
             return j * kBM + ((((i >> 3) ^ ((j ^ (j >> 3)) & 15)) & (kCPR - 1)) << 3) + (i & 7);
         };
         /* Tt[j][.] = src[j][.] : src holds C^T row-major (row j = column j of C) */
         auto stage_in = [&](const uint16_t* src, int64_t ld) {
-            u32x4_t v[kPieces];   /* all loads in flight before the first LDS write */
+            u32x4_t v[kEpiPieces];   /* all loads in flight before the first LDS write */
 #pragma clang loop unroll(full)
-            for (int k = 0; k < kPieces; ++k) {
+            for (int k = 0; k < kEpiPieces; ++k) {
                 const int idx = tid + k * kNsThreads, j = idx / kCPR, i = (idx % kCPR) * 8;
                 v[k] = *reinterpret_cast<const u32x4_t*>(src + j * ld + i);
             }
 #pragma clang loop unroll(full)
-            for (int k = 0; k < kPieces; ++k) {
+            for (int k = 0; k < kEpiPieces; ++k) {
                 const int idx = tid + k * kNsThreads, j = idx / kCPR, i = (idx % kCPR) * 8;
                 *reinterpret_cast<u32x4_t*>(Tt + tt(j, i)) = v[k];
             }
@@ -693,19 +643,20 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
         /* dst[j][i] = C[i][j] */
         auto store_t = [&](uint16_t* dst, int64_t ld) {
 #pragma clang loop unroll(full)
-            for (int k = 0; k < kPieces; ++k) {
+            for (int k = 0; k < kEpiPieces; ++k) {
                 const int idx = tid + k * kNsThreads, j = idx / kCPR, i = (idx % kCPR) * 8;
                 *reinterpret_cast<u32x4_t*>(dst + j * ld + i) = *reinterpret_cast<const u32x4_t*>(Tt + tt(j, i));
             }
         };
         /* dst[i][j] = C[i][j]: a thread moves 4 rows x 8 columns per block;
-         * of 32 consecutive blocks, 16 run along a row pair (jb) and the
-         * lowest bit picks the row quad (par) */
+         * of 32 consecutive blocks, the lowest bit picks the row quad (par)
+         * and the next four 16 of the column blocks (jb) */
         auto store_n = [&](uint16_t* dst, int64_t ld) {
 #pragma clang loop unroll(full)
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < kBlocks; ++k) {
                 const int bidx = tid + k * kNsThreads;
-                const int par = bidx & 1, jb = ((bidx >> 1) & 15) | (((bidx >> 5) & 1) << 4), ic = bidx >> 6;
+                const int rest = bidx >> 5;
+                const int par = bidx & 1, jb = ((bidx >> 1) & 15) | ((rest % (kJB / 16)) << 4), ic = rest / (kJB / 16);
                 const int i0 = 8 * ic + 4 * par, j0 = 8 * jb;
                 u32x2_t v[8];
 #pragma clang loop unroll(full)
@@ -773,7 +724,7 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
             if (diag) {
                 /* the lower triangle of a diagonal tile is the mirror of its upper one */
 #pragma clang loop unroll(full)
-                for (int k = 0; k < kBM * kBM / kNsThreads; ++k) {
+                for (int k = 0; k < kBM * kBN / kNsThreads; ++k) {
                     const int idx = tid + k * kNsThreads, j = idx / kBM, i = idx % kBM;
                     if (i > j)
                         Tt[tt(j, i)] = Tt[tt(i, j)];
@@ -852,7 +803,7 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
                              (EPI == kEpiUpdate || (reinterpret_cast<uintptr_t>(g.out) & 15) == 0);
             constexpr int kHalf = kBM / 2;
             /* row-major half tile; column bit 5 flipped on rows with bit 2 set */
-            auto t32 = [](int i, int j) { return i * kBM + (j ^ (((i >> 2) & 1) << 5)); };
+            auto t32 = [](int i, int j) { return i * kBN + (j ^ (((i >> 2) & 1) << 5)); };
             static_assert(kHalf % (32 * kTM) == 0, "a wavefront's rows lie in one half");
 #pragma clang loop unroll(full)
             for (int h = 0; h < 2; ++h) {
@@ -871,8 +822,8 @@ __global__ __launch_bounds__(kNsThreads) void k_ns_gemm(GemmArgs g, MuonUpdate u
                 }
                 __syncthreads();
 #pragma clang loop unroll(disable)
-                for (int idx = tid; idx < kHalf * (kBM / 4); idx += kNsThreads) {
-                    const int rr = idx / (kBM / 4), c = (idx % (kBM / 4)) * 4;
+                for (int idx = tid; idx < kHalf * (kBN / 4); idx += kNsThreads) {
+                    const int rr = idx / (kBN / 4), c = (idx % (kBN / 4)) * 4;
                     const int64_t nr = row0 + h * kHalf + rr, nc = col0 + c;
                     if (nr >= g.R || nc >= g.Cn)
                         continue;
@@ -964,11 +915,11 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
     g.Q = w.X; g.ldq = np; g.sq = mp * np;
     g.K = static_cast<int32_t>(np);
     g.C = w.A; g.ldc = mp; g.sc = mp * mp;
-    const int32_t nt = static_cast<int32_t>(mp / kBM);
+    const int32_t nt = static_cast<int32_t>(mp / SymTile::kBM);
     const dim3 tri(static_cast<uint32_t>(nt * (nt + 1) / 2), 1, cnt);
     g.nt = nt;
     hipError_t e = hooked(hook, HPO_MUON_PROF_GRAM, f_gram,
-                          [&] { return launch3(k_ns_gemm<kEpiGram, true>, tri, kNsThreads, stream, g, up); });
+                          [&] { return launch3(k_ns_gemm<kEpiGram, true, SymTile>, tri, SymTile::kThreads, stream, g, up); });
     if (e != hipSuccess)
         return e;
     /* B = b A + c A A^T */
@@ -978,7 +929,7 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
     g.C = w.B; g.ldc = mp; g.sc = mp * mp;
     g.b = bc; g.c = cc;
     e = hooked(hook, HPO_MUON_PROF_POLY, f_poly,
-               [&] { return launch3(k_ns_gemm<kEpiPoly, true>, tri, kNsThreads, stream, g, up); });
+               [&] { return launch3(k_ns_gemm<kEpiPoly, true, SymTile>, tri, SymTile::kThreads, stream, g, up); });
     if (e != hipSuccess)
         return e;
     /* X' = a X + B X  (Q = X^T, rows of X^T are columns of X) */
@@ -989,12 +940,12 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
     g.XT = w.XT[cur ^ 1]; g.ldxt = mp; g.sxt = np * mp;
     g.XS = w.XT[cur]; g.ldxs = mp; g.sxs = np * mp;
     g.a = a;
-    g.nx = static_cast<int32_t>(np / kBM);
-    g.ny = static_cast<int32_t>(mp / kBM);
-    const dim3 grid(static_cast<uint32_t>(g.nx * g.ny), 1, cnt);
+    g.nx = static_cast<int32_t>(np / GenTile::kBN);
+    g.ny = static_cast<int32_t>(mp / GenTile::kBM);
+    dim3 grid(static_cast<uint32_t>(g.nx * g.ny), 1, cnt);
     if (!last)
         return hooked(hook, HPO_MUON_PROF_STEP, f_step,
-                      [&] { return launch3(k_ns_gemm<kEpiStep, false>, grid, kNsThreads, stream, g, up); });
+                      [&] { return launch3(k_ns_gemm<kEpiStep, false, GenTile>, grid, GenTile::kThreads, stream, g, up); });
     g.R = b.m;
     g.Cn = b.n;
     if (b.transposed) {
@@ -1006,18 +957,19 @@ hipError_t ns_step(const TensorDesc* d_desc, const MuonInfo* d_info, const MuonB
         g.Q = w.B; g.ldq = mp; g.sq = mp * mp;
         g.X = w.XT[cur]; g.ldx = mp; g.sx = np * mp;
         g.XS = w.X; g.ldxs = np; g.sxs = mp * np;
-        g.nx = static_cast<int32_t>(mp / kBM);
-        g.ny = static_cast<int32_t>(np / kBM);
+        g.nx = static_cast<int32_t>(mp / GenTile::kBN);
+        g.ny = static_cast<int32_t>(np / GenTile::kBM);
+        grid.x = static_cast<uint32_t>(g.nx * g.ny);   /* tiles need not be square */
         g.R = b.n;
         g.Cn = b.m;
     }
     if (out != nullptr) {
         g.out = out;
         return hooked(hook, HPO_MUON_PROF_UPDATE, f_step,
-                      [&] { return launch3(k_ns_gemm<kEpiOut, false>, grid, kNsThreads, stream, g, up); });
+                      [&] { return launch3(k_ns_gemm<kEpiOut, false, GenTile>, grid, GenTile::kThreads, stream, g, up); });
     }
     return hooked(hook, HPO_MUON_PROF_UPDATE, f_step,
-                  [&] { return launch3(k_ns_gemm<kEpiUpdate, false>, grid, kNsThreads, stream, g, up); });
+                  [&] { return launch3(k_ns_gemm<kEpiUpdate, false, GenTile>, grid, GenTile::kThreads, stream, g, up); });
 }
 
 }  // namespace
