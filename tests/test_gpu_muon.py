@@ -91,6 +91,32 @@ def test_newton_schulz_degenerate_inputs(H, mu, I):
     check_ns("tiny (below the guard)", gpu_ns(H, tiny, H.make_muon_cfg()), O, spread, rel)
 
 
+@pytest.mark.parametrize("shape", [(96, 200), (200, 96)])
+def test_newton_schulz_unaligned_buffers(H, mu, I, shape):
+    """G and out one float past a 16-byte boundary (the boundary asks for
+    4-byte alignment only): the output leaves through the element-wise path
+    and must equal, bit for bit, the aligned call's float4 stores."""
+    banner(f"NS unaligned {shape}")
+    dev = torch.device("cuda")
+    G = I.seeded_matrix(shape, seed=77 + shape[0])
+    n = G.size
+    gbuf = torch.zeros(n + 4, dtype=torch.float32, device=dev)
+    obuf = torch.full((n + 4,), float("nan"), dtype=torch.float32, device=dev)
+    g = gbuf[1:n + 1].view(shape)
+    out = obuf[1:n + 1].view(shape)
+    assert g.data_ptr() % 16 == 4 and out.data_ptr() % 16 == 4
+    g.copy_(torch.from_numpy(G))
+    ws = torch.empty(H.hpo_newton_schulz_workspace(*shape), dtype=torch.uint8, device=dev)
+    H.hpo_newton_schulz(g, out, H.make_muon_cfg(), ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert torch.isnan(obuf[0]) and torch.all(torch.isnan(obuf[n + 1:])), "wrote outside the output view"
+    aligned = gpu_ns(H, G, H.make_muon_cfg())
+    assert np.array_equal(got.view(np.uint32), aligned.view(np.uint32))
+    O, spread, rel = ns_reference(mu, G)
+    check_ns(f"unaligned {shape}", got, O, spread, rel)
+
+
 def test_newton_schulz_handbook_printout(H, I):
     """The GPU's NS output reproduces the figures the handbook prints for its
     256 x 1024 demonstration, within one unit of each printed last digit."""
