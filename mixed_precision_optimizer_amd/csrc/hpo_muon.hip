@@ -35,12 +35,16 @@
  * X give zero rows and columns of A, B and X'), so the GEMMs run on whole
  * tiles with no bounds checks.
  *
- * GEMM tiling: a 256-lane workgroup (2 x 2 wavefronts) computes a
- * 128 x 128 tile of C; each wavefront a 64 x 64 block as 2 x 2 MFMA tiles of
- * 32 x 32, k in slices of 16.  Operands stream through LDS in k-stages of 64
- * (128 B per row), double-buffered (64 KB), rows stored with their eight
+ * GEMM tiling: a 1024-lane workgroup (4 x 4 wavefronts, one per CU)
+ * computes a 256 x 256 tile of C; each wavefront a 64 x 64 block as 2 x 2
+ * MFMA tiles of 32 x 32, k in slices of 16.  Operands go straight from
+ * global memory into LDS (buffer loads with an LDS destination) in k-stages
+ * of 64 (128 B per row), two 64 KB buffers, rows stored with their eight
  * 16-byte pieces permuted by an XOR of the row index so that the MFMA
  * fragment reads (32 rows x 16 B per half-wavefront) hit distinct banks.
+ * Tiles are handed out XCD by XCD in groups of 8 tile rows.  The epilogues
+ * reuse the 128 KB: the bf16 C tile is combined there with its input tile
+ * and leaves in whole 128-byte lines, row-major and transposed.
  *
  * Floating point: built with -ffp-contract=off; every elementwise operation
  * rounds on its own, in the order written.
@@ -286,22 +290,48 @@ __global__ __launch_bounds__(kBlock) void k_muon_ns_input(const float* src, int6
 {
     if (!gate_open(gate))
         return;
-    __shared__ uint16_t tile[kTile][kTile + 2];
+    __shared__ __attribute__((aligned(4))) uint16_t tile[kTile][kTile + 2];
     const int64_t z = blockIdx.z;
     const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kTile;
     const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTile;
     const float d = dnorm[dnorm_first + z];
     const float* __restrict__ S = src + z * src_stride;
     const int tid = threadIdx.x;
-#pragma unroll 4
-    for (int k = 0; k < kTile * kTile / kBlock; ++k) {
+    /* a thread takes column pairs (one 4-byte LDS write each); all of its
+     * loads are issued before the first use */
+    constexpr int kPairs = kTile * kTile / 2 / kBlock;
+    float x0[kPairs], x1[kPairs];
+    /* even rows on an 8-byte aligned base: each pair is one 8-byte load
+     * (gc is even, so gc < C means gc + 1 < C) */
+    const bool pairs = (C & 1) == 0 && (reinterpret_cast<uintptr_t>(S) & 7) == 0;
+    if (pairs) {
+#pragma unroll
+        for (int k = 0; k < kPairs; ++k) {
+            const int e = tid + k * kBlock;
+            const int r = e / (kTile / 2), c = (e % (kTile / 2)) * 2;
+            const int64_t gr = r0 + r, gc = c0 + c;
+            float2 v = make_float2(0.0f, 0.0f);
+            if (gr < R && gc < C)
+                v = *reinterpret_cast<const float2*>(S + gr * C + gc);
+            x0[k] = v.x;
+            x1[k] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPairs; ++k) {
+            const int e = tid + k * kBlock;
+            const int r = e / (kTile / 2), c = (e % (kTile / 2)) * 2;
+            const int64_t gr = r0 + r, gc = c0 + c;
+            x0[k] = gr < R && gc < C ? S[gr * C + gc] : 0.0f;
+            x1[k] = gr < R && gc + 1 < C ? S[gr * C + gc + 1] : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
         const int e = tid + k * kBlock;
-        const int r = e / kTile, c = e % kTile;
-        const int64_t gr = r0 + r, gc = c0 + c;
-        float x = 0.0f;
-        if (gr < R && gc < C)
-            x = S[gr * C + gc] / d;
-        tile[r][c] = static_cast<uint16_t>(bf16_rne_bits(x));
+        const int r = e / (kTile / 2), c = (e % (kTile / 2)) * 2;
+        const uint32_t lo = bf16_rne_bits(x0[k] / d), hi = bf16_rne_bits(x1[k] / d);
+        *reinterpret_cast<uint32_t*>(&tile[r][c]) = lo | (hi << 16);
     }
     __syncthreads();
     uint16_t* __restrict__ Cp = copy + z * s_copy;

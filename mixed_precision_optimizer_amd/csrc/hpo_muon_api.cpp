@@ -238,7 +238,7 @@ hpo_status muon_enqueue(hpo_set s, const hpo_muon_cfg* cfg, const hpo_group* gro
         if (m.prof) {
             const size_t ev1 = prof_mark(*m.prof, stream);
             if (ev0 != SIZE_MAX && ev1 != SIZE_MAX)
-                m.prof->recs.push_back({HPO_MUON_PROF_INPUT, ev0, ev1, 0.0, 12.0 * elems});
+                m.prof->recs.push_back({HPO_MUON_PROF_INPUT, ev0, ev1, 0.0, 8.0 * elems});
         }
         e = hpo::launch_muon_ns(s->d_tensors, m.d_info, b, w, gate, cfg->ns_steps, coeffs, up, nullptr, stream, hk);
         if (e != hipSuccess)
