@@ -352,6 +352,11 @@ typedef struct {
 /* Default workspace cap of a Muon set (see hpo_muon_set_create). */
 #define HPO_MUON_DEFAULT_WORKSPACE (((int64_t)16) << 30)
 
+/* Largest rows or cols of a Muon matrix (and of hpo_newton_schulz): the
+ * matrix-core kernels address one 256-row operand panel with 32-bit byte
+ * offsets. */
+#define HPO_MUON_MAX_DIM (((int64_t)1) << 21)
+
 /* A Muon set over n_matrices row-major matrices: matrix i has rows[i] x
  * cols[i] elements at param[i] (bf16 model param, or NULL / main_param[i]
  * for HPO_PARAM_FP32), main_param[i] (fp32 master), main_grad[i] (fp32 main
@@ -359,7 +364,8 @@ typedef struct {
  * aligned.  param_dtype: HPO_PARAM_BF16 or HPO_PARAM_FP32; fp16 params with
  * Muon are an error ([OPT-INFRA] §14.3), as is HPO_STATE_BF16 (HPO_EDTYPE).
  * group_index[i] selects the matrix's hpo_group in hpo_muon_step (NULL:
- * group 0).  Matrices with rows or cols 0 are allowed and never touched.
+ * group 0).  Matrices with rows or cols 0 are allowed and never touched;
+ * rows or cols above HPO_MUON_MAX_DIM are an error (HPO_EINVAL).
  * The set plans batches of same-shape matrices and allocates one device
  * workspace for the largest batch: per matrix 4 B per element (the Nesterov
  * gradient) plus bf16 X, two X^T and the two Gram-sized matrices of NS, with
@@ -407,7 +413,8 @@ hpo_status hpo_step_device_chain(hpo_set adam_set, const hpo_adam_cfg* cfg, cons
  * cfg's ns_steps, ns_coeffs and ns_eps (the momentum and scale fields are not
  * read) and the same bf16 matrix-core arithmetic as hpo_muon_step.  The
  * caller provides a device workspace of at least
- * hpo_newton_schulz_workspace(rows, cols) bytes, 256-byte aligned. */
+ * hpo_newton_schulz_workspace(rows, cols) bytes, 256-byte aligned.  rows and
+ * cols lie in [0, HPO_MUON_MAX_DIM] (else HPO_EINVAL from both calls). */
 hpo_status hpo_newton_schulz(const float* d_G, int64_t rows, int64_t cols, const hpo_muon_cfg* cfg, float* d_out,
                              void* d_workspace, int64_t workspace_bytes, void* stream);
 hpo_status hpo_newton_schulz_workspace(int64_t rows, int64_t cols, int64_t* out_bytes);

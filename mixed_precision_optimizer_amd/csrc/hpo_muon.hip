@@ -517,6 +517,8 @@ __global__ __launch_bounds__(T::kThreads, T::kWavesPerSimd) void k_ns_gemm(GemmA
      * panel is the tile's rows (P) or columns (Q) from its first one, so every
      * offset fits 32 bits. */
     constexpr int kRawBuffer = 0x00020000;
+    static_assert(int64_t{kBM > kBN ? kBM : kBN} * ns_pad(HPO_MUON_MAX_DIM) * 2 <= INT32_MAX,
+                  "an operand panel of the widest matrix fits 32-bit buffer offsets");
     const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(P), 0, static_cast<int>(kBM * g.ldp * 2), kRawBuffer);
     const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc(

@@ -276,8 +276,10 @@ hpo_status hpo_muon_set_create(hpo_set* out, int32_t n_matrices, int32_t param_d
     for (int32_t i = 0; i < n_matrices; ++i) {
         if (rows[i] < 0 || cols[i] < 0)
             return fail(HPO_EINVAL, "matrix %d: negative shape %lld x %lld", i, (long long)rows[i], (long long)cols[i]);
-        if (rows[i] > 0 && cols[i] > (int64_t(1) << 40) / rows[i])
-            return fail(HPO_EINVAL, "matrix %d: %lld x %lld is too large", i, (long long)rows[i], (long long)cols[i]);
+        if (rows[i] > HPO_MUON_MAX_DIM || cols[i] > HPO_MUON_MAX_DIM ||
+            (rows[i] > 0 && cols[i] > (int64_t(1) << 40) / rows[i]))
+            return fail(HPO_EINVAL, "matrix %d: %lld x %lld is too large (each side at most %lld, 2^40 elements)", i,
+                        (long long)rows[i], (long long)cols[i], (long long)HPO_MUON_MAX_DIM);
         const int32_t g = group_index ? group_index[i] : 0;
         if (g < 0 || g >= HPO_MAX_GROUPS)
             return fail(HPO_EINVAL, "group_index[%d] = %d is outside [0, %d)", i, g, HPO_MAX_GROUPS);
@@ -483,8 +485,10 @@ hpo_status hpo_newton_schulz_workspace(int64_t rows, int64_t cols, int64_t* out_
 {
     if (!out_bytes)
         return fail(HPO_EINVAL, "out_bytes is NULL");
-    if (rows < 0 || cols < 0 || (rows > 0 && cols > (int64_t(1) << 40) / rows))
-        return fail(HPO_EINVAL, "bad shape %lld x %lld", (long long)rows, (long long)cols);
+    if (rows < 0 || cols < 0 || rows > HPO_MUON_MAX_DIM || cols > HPO_MUON_MAX_DIM ||
+        (rows > 0 && cols > (int64_t(1) << 40) / rows))
+        return fail(HPO_EINVAL, "bad shape %lld x %lld (each side in [0, %lld])", (long long)rows, (long long)cols,
+                    (long long)HPO_MUON_MAX_DIM);
     if (rows * cols == 0) {
         *out_bytes = 0;
         return ok();

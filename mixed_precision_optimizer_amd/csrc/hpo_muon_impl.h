@@ -16,7 +16,7 @@ namespace hpo {
  * dimensions (the largest GEMM tile), so the GEMMs need no edge handling:
  * zero rows and columns stay zero through every iteration. */
 constexpr int64_t kNsPad = 256;
-inline int64_t ns_pad(int64_t x) { return (x + kNsPad - 1) / kNsPad * kNsPad; }
+constexpr __host__ __device__ int64_t ns_pad(int64_t x) { return (x + kNsPad - 1) / kNsPad * kNsPad; }
 
 /* Per-matrix facts the Muon kernels need beyond the TensorDesc pointers
  * (param, master, grad, exp_avg = momentum). */

@@ -57,6 +57,7 @@ HPO_MUON_SCALE_SHAPE = 1
 HPO_MUON_SCALE_UNIT_RMS = 2
 HPO_NS_MAX_STEPS = 16
 HPO_MUON_DEFAULT_WORKSPACE = 16 << 30
+HPO_MUON_MAX_DIM = 1 << 21
 
 
 HPO_MUON_PROF_N = 6

@@ -236,6 +236,8 @@ def test_muon_set_validation(H):
     assert st == H.HPO_EINVAL and "own master" in msg
     st, msg = _muon(H, [(1 << 21, 1 << 21)])
     assert st == H.HPO_EINVAL and "too large" in msg
+    st, msg = _muon(H, [(2, H.HPO_MUON_MAX_DIM + 1)])   # few elements, but one side beyond the limit
+    assert st == H.HPO_EINVAL and "too large" in msg
     assert H.load().hpo_muon_set_create(None, 0, 0, None, None, None, None, None, None, None, 0, None) == H.HPO_EINVAL
     if not torch.cuda.is_available():
         st, msg = _muon(H, [(4, 8), (0, 3)])
@@ -250,6 +252,13 @@ def test_muon_step_and_ns_validation(H):
     ws = ctypes.c_int64()
     assert L.hpo_newton_schulz_workspace(-1, 4, ctypes.byref(ws)) == H.HPO_EINVAL
     assert L.hpo_newton_schulz_workspace(0, 4, ctypes.byref(ws)) == H.HPO_OK and ws.value == 0
+    # each side at most HPO_MUON_MAX_DIM (32-bit operand-panel offsets), even when the product is small
+    assert L.hpo_newton_schulz_workspace(1, H.HPO_MUON_MAX_DIM, ctypes.byref(ws)) == H.HPO_OK
+    assert L.hpo_newton_schulz_workspace(1, H.HPO_MUON_MAX_DIM + 1, ctypes.byref(ws)) == H.HPO_EINVAL
+    assert L.hpo_newton_schulz_workspace(H.HPO_MUON_MAX_DIM + 1, 1, ctypes.byref(ws)) == H.HPO_EINVAL
+    assert str(H.HPO_MUON_MAX_DIM) in H.hpo_last_error()
+    assert L.hpo_newton_schulz(ctypes.c_void_p(0x1000), 1, H.HPO_MUON_MAX_DIM + 1, ctypes.byref(H.make_muon_cfg()),
+                               ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 1 << 40, None) == H.HPO_EINVAL
     # one 300 x 1000 matrix: partials + norm + bf16 X, two X^T (256-padded) and two Gram matrices
     assert L.hpo_newton_schulz_workspace(300, 1000, ctypes.byref(ws)) == H.HPO_OK
     mp, np_ = 512, 1024
