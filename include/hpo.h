@@ -442,7 +442,7 @@ typedef struct {
                                           triangle), m^2(m+1) for A A^T, 2 m^2 n for B X; 0 for the
                                           elementwise passes */
     double bytes[HPO_MUON_PROF_N];     /* algorithmic HBM bytes of the elementwise passes: momentum
-                                          16 per element (read G, M; write M, g~), input 12 (read g~,
+                                          16 per element (read G, M; write M, g~), input 8 (read g~,
                                           write X and X^T in bf16) */
 } hpo_muon_profile;
 
