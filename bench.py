@@ -79,6 +79,40 @@ def measured_traffic(workload_name, numel):
     return traffic if digest == kernel_digest() else None
 
 
+MUON_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_hbm_traffic_llama8b_adamw_muon_chain.txt")
+MUON_SOURCES = ("mixed_precision_optimizer_amd/csrc/hpo_muon.hip", "mixed_precision_optimizer_amd/csrc/hpo_muon_impl.h")
+
+
+def muon_kernel_digest():
+    """sha256[:16] over the Muon device sources (named by the Muon counter summaries)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in MUON_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_muon_traffic():
+    """(measured, algorithmic) HBM bytes per launch of the X' = aX + BX GEMM on
+    the Llama-8B chain from the committed rocprofv3 summary, or None when the
+    Muon kernels have changed since it was taken."""
+    if not os.path.exists(MUON_PMC_SUMMARY):
+        return None
+    digest, meas, alg = None, None, None
+    with open(MUON_PMC_SUMMARY) as f:
+        for line in f:
+            if "kernel source digest" in line:
+                digest = line.rsplit(":", 1)[1].strip()
+            if line.startswith("traffic_bytes_per_launch k_ns_gemm_step"):
+                meas = float(line.split()[-1])
+            if line.startswith("algorithmic_bytes_per_launch k_ns_gemm_step"):
+                alg = float(line.split()[-1])
+    if digest != muon_kernel_digest() or meas is None or alg is None:
+        return None
+    return meas, alg
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -499,6 +533,12 @@ def main_muon(args, dev):
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": f"k_ns_gemm ({dom}), algorithmic flops per launch {dom_fl:.4g}"},
     }
+    tr = measured_muon_traffic() if dom == "step" else None
+    if tr is not None:
+        out["roofline"]["traffic"] = round(tr[0] / 1e9, 3)
+        out["roofline"]["traffic_unit"] = (
+            "GB per launch of the step GEMM (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, scales from a device copy "
+            f"of known size); algorithmic {tr[1] / 1e9:.3f} GB: B and X read once, X' and X'^T written")
     aset.close()
     mset.close()
     if args.cpu_sample > 0:
