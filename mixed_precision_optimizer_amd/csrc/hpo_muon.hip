@@ -42,6 +42,10 @@
  * of 64 (128 B per row), two 64 KB buffers, rows stored with their eight
  * 16-byte pieces permuted by an XOR of the row index so that the MFMA
  * fragment reads (32 rows x 16 B per half-wavefront) hit distinct banks.
+ * The k-loop is software-pipelined across the stage barrier: the barrier
+ * comes before each stage's last k-slice, whose fragments are already in
+ * registers, and the next stage's first fragments are read under that
+ * slice's MFMAs.
  * Tiles are handed out XCD by XCD in groups of 8 tile rows.  The epilogues
  * reuse the 128 KB: the bf16 C tile is combined there with its input tile
  * and leaves in whole 128-byte lines, row-major and transposed.
@@ -50,6 +54,8 @@
  * rounds on its own, in the order written.
  */
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "hpo_muon_impl.h"
 #include "hpo_device.h"
@@ -70,6 +76,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 /* Raise the wavefront's issue priority while it runs its MFMAs. */
 #ifndef HPO_NS_PRIO
 #define HPO_NS_PRIO 1
+#endif
+/* Software-pipeline the k-loop across the stage barrier (see the kernel). */
+#ifndef HPO_NS_XBAR
+#define HPO_NS_XBAR 1
 #endif
 /* Tile order: each XCD takes a contiguous run of tiles, rows grouped by this
  * many (0: hardware order). */
@@ -523,6 +533,12 @@ __global__ __launch_bounds__(T::kThreads, T::kWavesPerSimd) void k_ns_gemm(GemmA
         const_cast<uint16_t*>(P), 0, static_cast<int>(kBM * g.ldp * 2), kRawBuffer);
     const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(Q), 0, static_cast<int>(kBN * g.ldq * 2), kRawBuffer);
+    /* LDS: the P panels of all stages, then the Q panels ([P0 P1 .. Q0 Q1 ..]),
+     * so a fragment address of one stage and the same address of the next
+     * differ by kBM * kRowStride (32 KB), within a DS instruction's offset */
+    constexpr int kChunksP = kBM / kRowsPerChunk;   /* chunks holding P rows */
+    auto p_stage = [&](int s) { return lds + s * (kBM * kRowStride); };
+    auto q_stage = [&](int s) { return lds + kStages * (kBM * kRowStride) + s * (kBN * kRowStride); };
     int voff[kChunksPerWave];
 #pragma unroll
     for (int i = 0; i < kChunksPerWave; ++i) {
@@ -536,7 +552,8 @@ __global__ __launch_bounds__(T::kThreads, T::kWavesPerSimd) void k_ns_gemm(GemmA
         for (int i = 0; i < kChunksPerWave; ++i) {
             const int c = wave * kChunksPerWave + i;
             const bool is_p = c * kRowsPerChunk < kBM;   /* uniform per chunk */
-            buffer_load_lds16(is_p ? rsP : rsQ, &lds[s * kStageBytes + c * 1024], voff[i], static_cast<int>(k0 * 2));
+            char* dst = is_p ? p_stage(s) + c * 1024 : q_stage(s) + (c - kChunksP) * 1024;
+            buffer_load_lds16(is_p ? rsP : rsQ, dst, voff[i], static_cast<int>(k0 * 2));
         }
     };
     const int wm = (wave / kWavesN) * 32 * kTM, wn = (wave % kWavesN) * 32 * kTN;
@@ -551,8 +568,8 @@ __global__ __launch_bounds__(T::kThreads, T::kWavesPerSimd) void k_ns_gemm(GemmA
      * while the MFMAs of slice kk run; the scheduling barriers keep the
      * compiler from sinking the reads next to their uses. */
     auto compute = [&](int s) {
-        const char* Ps = lds + s * kStageBytes;
-        const char* Qs = Ps + kBM * kRowStride;
+        const char* Ps = p_stage(s);
+        const char* Qs = q_stage(s);
         bf16x8_t fa[2][kTM], fb[2][kTN];
         auto fload = [&](int kk, int buf) {
             const int piece = kk * 2 + fhalf;  /* lanes 0-31: k 0..7 of the slice, 32-63: k 8..15 */
@@ -598,37 +615,162 @@ __global__ __launch_bounds__(T::kThreads, T::kWavesPerSimd) void k_ns_gemm(GemmA
 #endif
     };
     const int nk = g.K / kBK;
-    /* Stages kt .. kt + kStages - 2 are in flight while stage kt is
-     * computed.  At the top of iteration kt a wavefront waits until its own
-     * loads of stage kt have landed (vmcnt counts its outstanding loads, in
-     * issue order, kChunksPerWave per stage), the barrier makes that true
-     * for every wavefront and retires buffer (kt - 1) % kStages, which then
-     * receives stage kt + kStages - 1. */
-    for (int st = 0; st < kStages - 1 && st < nk; ++st)
-        gload(st, static_cast<int64_t>(st) * kBK);
-    for (int kt = 0; kt < nk; ++kt) {
+    /* the cross-barrier pipeline needs two stages of four k-slices */
+    constexpr bool kXbar = HPO_NS_XBAR && kBK == 64 && kStages == 2;
+    if constexpr (kXbar) {
+        /* Two stages, the barrier moved inside the stream of k-slices.  The
+         * fragments of slice kk + 1 are read while the MFMAs of slice kk run, across
+         * stage boundaries too: before the last slice of stage kt (its fragments
+         * already in registers) a wavefront waits for its own LDS reads of that
+         * buffer and its own loads of stage kt + 1, then the barrier makes both
+         * true for every wavefront.  Stage kt + 2 then goes into the retired
+         * buffer and the first fragments of stage kt + 1 are read while the last
+         * MFMAs of stage kt run, so the matrix pipe is busy across the barrier. */
+        constexpr int kSlices = kBK / 16;
+        bf16x8_t fa[2][kTM], fb[2][kTN];
+        auto fload = [&](int s, int kk, auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+            const char* Ps = p_stage(s);
+            const char* Qs = q_stage(s);
+            const int piece = kk * 2 + fhalf;  /* lanes 0-31: k 0..7 of the slice, 32-63: k 8..15 */
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+                fa[buf][i] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Ps + piece_at<kBK>(wm + 32 * i + frow, piece)));
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+                fb[buf][j] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Qs + piece_at<kBK>(wn + 32 * j + frow, piece)));
+        };
+        auto mfmas = [&](auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        };
+        auto interleave = [&]() {
+            __builtin_amdgcn_sched_barrier(0);   /* one scheduling region per slice */
+#if HPO_NS_SCHED
+            /* the kTM + kTN reads of the next slice spread over this slice's kTM * kTN MFMAs */
+            constexpr int kReads = kTM + kTN, kPer = kTM * kTN / kReads, kRest = kTM * kTN - kPer * kReads;
+#pragma unroll
+            for (int q = 0; q < kReads; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      /* one DS read */
+                __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);   /* MFMAs */
+            }
+            if (kRest > 0)
+                __builtin_amdgcn_sched_group_barrier(0x008, kRest, 0);
+#endif
+            __builtin_amdgcn_sched_barrier(0);
+        };
         /* gfx9 s_waitcnt encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
-         * lgkmcnt [11:8].  lgkmcnt(0): this wavefront's LDS reads of the
-         * buffer about to be refilled have completed.  The barrier is the
-         * bare instruction: __syncthreads()'s release fence would also wait
-         * for every outstanding load (vmcnt(0)) and drain the pipeline. */
-        constexpr int kAhead = (kStages - 2) * kChunksPerWave;
-        constexpr int kWaitAhead = 0x0070 | (kAhead & 15) | ((kAhead >> 4) << 14);
-        static_assert(kAhead < 64, "vmcnt range");
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + kStages - 2 < nk)
-            __builtin_amdgcn_s_waitcnt(kWaitAhead);
+         * lgkmcnt [11:8].  The barriers are the bare instruction:
+         * __syncthreads()'s release fence would also wait for every outstanding
+         * load (vmcnt(0)) and drain the pipeline. */
+        constexpr int kOne = kChunksPerWave;   /* one stage of this wavefront's loads */
+        static_assert(kOne < 64, "vmcnt range");
+        constexpr int kWaitOne = 0x0070 | (kOne & 15) | ((kOne >> 4) << 14);
+        gload(0, 0);
+        if (nk > 1)
+            gload(1, kBK);
+        if (nk > 1)
+            __builtin_amdgcn_s_waitcnt(kWaitOne);   /* stage 0 has landed (stage 1 may still be in flight) */
         else
-            __builtin_amdgcn_s_waitcnt(0x0070);   /* the tail: nothing later was issued */
+            __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        const int nxt = kt + kStages - 1;
-        if (nxt < nk)
-            gload(nxt % kStages, static_cast<int64_t>(nxt) * kBK);
-#if HPO_NS_SCHED
-        __builtin_amdgcn_sched_barrier(0);
+        using F0 = std::integral_constant<int, 0>;
+        using F1 = std::integral_constant<int, 1>;
+        fload(0, 0, F0{});
+        /* nk is even and at least 4 (K is a multiple of 256): two stages per
+         * trip, so that each stage's buffer index is a constant, and the last two
+         * stages peeled, so that no branch inside the loop splits the
+         * accumulators' live range.  kMode: 0 a stage that loads stage kt + 2,
+         * 1 the last but one (no later stage to load), 2 the last (no barrier). */
+        auto stage = [&](int kt, auto sbuf, auto mode) {
+            constexpr int s = decltype(sbuf)::value;
+            constexpr int kMode = decltype(mode)::value;
+#if HPO_NS_PRIO
+            __builtin_amdgcn_s_setprio(1);
 #endif
-        compute(kt % kStages);
+            static_assert(kSlices == 4, "four k-slices per stage");
+            fload(s, 1, F1{});
+            mfmas(F0{});
+            interleave();
+            fload(s, 2, F0{});
+            mfmas(F1{});
+            interleave();
+            fload(s, 3, F1{});
+            mfmas(F0{});
+            interleave();
+            if constexpr (kMode < 2) {
+#if HPO_NS_PRIO
+                __builtin_amdgcn_s_setprio(0);
+#endif
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0x0070);   /* own reads of buffer s, own loads of stage kt + 1 */
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (kMode == 0)
+                    gload(s, static_cast<int64_t>(kt + 2) * kBK);
+                __builtin_amdgcn_sched_barrier(0);
+#if HPO_NS_PRIO
+                __builtin_amdgcn_s_setprio(1);
+#endif
+                fload(s ^ 1, 0, F0{});   /* the next stage's first slice, under this stage's last MFMAs */
+                mfmas(F1{});
+                interleave();
+            } else {
+                mfmas(F1{});
+            }
+#if HPO_NS_PRIO
+            __builtin_amdgcn_s_setprio(0);
+#endif
+        };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        int kt = 0;
+        for (; kt + 2 < nk; kt += 2) {
+            stage(kt, S0{}, std::integral_constant<int, 0>{});
+            stage(kt + 1, S1{}, std::integral_constant<int, 0>{});
+        }
+        stage(kt, S0{}, std::integral_constant<int, 1>{});
+        stage(kt + 1, S1{}, std::integral_constant<int, 2>{});
+    } else {
+        /* Stages kt .. kt + kStages - 2 are in flight while stage kt is
+         * computed.  At the top of iteration kt a wavefront waits until its own
+         * loads of stage kt have landed (vmcnt counts its outstanding loads, in
+         * issue order, kChunksPerWave per stage), the barrier makes that true
+         * for every wavefront and retires buffer (kt - 1) % kStages, which then
+         * receives stage kt + kStages - 1. */
+        for (int st = 0; st < kStages - 1 && st < nk; ++st)
+            gload(st, static_cast<int64_t>(st) * kBK);
+        for (int kt = 0; kt < nk; ++kt) {
+            /* gfx9 s_waitcnt encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
+             * lgkmcnt [11:8].  lgkmcnt(0): this wavefront's LDS reads of the
+             * buffer about to be refilled have completed.  The barrier is the
+             * bare instruction: __syncthreads()'s release fence would also wait
+             * for every outstanding load (vmcnt(0)) and drain the pipeline. */
+            constexpr int kAhead = (kStages - 2) * kChunksPerWave;
+            constexpr int kWaitAhead = 0x0070 | (kAhead & 15) | ((kAhead >> 4) << 14);
+            static_assert(kAhead < 64, "vmcnt range");
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + kStages - 2 < nk)
+                __builtin_amdgcn_s_waitcnt(kWaitAhead);
+            else
+                __builtin_amdgcn_s_waitcnt(0x0070);   /* the tail: nothing later was issued */
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            const int nxt = kt + kStages - 1;
+            if (nxt < nk)
+                gload(nxt % kStages, static_cast<int64_t>(nxt) * kBK);
+#if HPO_NS_SCHED
+            __builtin_amdgcn_sched_barrier(0);
+#endif
+            compute(kt % kStages);
+        }
     }
 
     /* Staged epilogue.  acc[ti][tj][r] holds C[i][j] (tile coordinates) with
