@@ -199,7 +199,7 @@ def _grow_bounds(case, mu, cfg, groups, rec):
             2 * np.spacing(W.astype(F32)).astype(np.float64)
 
 
-@pytest.mark.parametrize("variant", ["bf16_sum_nesterov", "fp32_ema", "bf16_plain_shape_scale"])
+@pytest.mark.parametrize("variant", ["bf16_sum_nesterov", "fp32_ema", "bf16_plain_shape_scale", "bf16_unit_rms_scale"])
 def test_muon_set_steps(H, mu, I, variant):
     banner(f"Muon set {variant}")
     dev = torch.device("cuda")
@@ -212,6 +212,9 @@ def test_muon_set_steps(H, mu, I, variant):
     elif variant == "bf16_plain_shape_scale":
         cfg_o = mu.MuonCfg(nesterov=False, scale_mode=mu.SCALE_SHAPE, extra_scale=1.0)
         cfg = H.make_muon_cfg(nesterov=False, scale_mode=H.HPO_MUON_SCALE_SHAPE, extra_scale=1.0)
+    elif variant == "bf16_unit_rms_scale":
+        cfg_o = mu.MuonCfg(scale_mode=mu.SCALE_UNIT_RMS, extra_scale=0.5)
+        cfg = H.make_muon_cfg(scale_mode=H.HPO_MUON_SCALE_UNIT_RMS, extra_scale=0.5)
     else:
         cfg_o = mu.MuonCfg()
         cfg = H.make_muon_cfg()
@@ -353,6 +356,81 @@ def test_chained_device_step(H, mu, I):
             assert np.array_equal(to_np(a2[i]).view(np.uint32), T.v.view(np.uint32))
             assert np.array_equal(to_np(ap[i]), T.p)
         _compare_case(case, mu, cfg_o, chain.last, mgroups, f"chain step {k}")
+
+
+def test_chain_with_one_set_matches_the_separate_calls(H, mu, I):
+    """hpo_step_device_chain with only a Muon set, or only an AdamW set, does
+    what the separate calls do: the same bits as hpo_grad_global_norm_sets +
+    hpo_muon_step, and as hpo_step_device, on identical twins of the sets."""
+    banner("chain with one set")
+    dev = torch.device("cuda")
+    shapes = [(128, 384), (384, 128), (37, 129)]
+    mgroups = [(0.02, 0.1), (0.01, 0.0)]
+
+    def muon_twin():
+        W0 = [I.seeded_matrix(s, 40 + i, 0.02) for i, s in enumerate(shapes)]
+        m = [torch.from_numpy(w.copy()).to(dev) for w in W0]
+        g = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+        o = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+        p = [t.to(torch.bfloat16) for t in m]
+        return H.hpo_muon_set_create(p, m, g, o, [0, 1, 0]), m, g, o, p
+
+    a, b = muon_twin(), muon_twin()
+    d_state = H.new_scaler_state(dev)
+    H.hpo_scaler_state_init(d_state, 1.0, 1, 0)
+    d_norm = torch.zeros(1, dtype=torch.float32, device=dev)
+    d_found = torch.zeros(1, dtype=torch.int32, device=dev)
+    scfg = H.make_scaler_cfg(dynamic=False)
+    for k in range(1, 4):
+        grads = [I.seeded_matrix(s, 60 * k + i, 1e-1) for i, s in enumerate(shapes)]
+        for twin in (a, b):
+            for t, g in zip(twin[2], grads):
+                t.copy_(torch.from_numpy(g))
+        H.hpo_step_device_chain(None, None, None, a[0], H.make_muon_cfg(), mgroups, 1.0, scfg, d_state, k, 1)
+        d_found.zero_()
+        H.hpo_grad_global_norm_sets([b[0]], 1.0, d_norm, d_found)
+        H.hpo_muon_step(b[0], H.make_muon_cfg(), mgroups, None, 1.0, 1.0, d_norm, d_found)
+        torch.cuda.synchronize()
+        st = H.read_scaler_state(d_state)
+        assert st.applied_steps == k and st.grad_norm == float(d_norm.item()), k
+        for x, y in zip(a[1] + a[3] + a[4], b[1] + b[3] + b[4]):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y), f"muon-only chain step {k}"
+
+    # AdamW only: the chain against hpo_step_device
+    sizes = [3000, 256, 1000]
+
+    def adam_twin():
+        m = [torch.from_numpy(I.seeded_matrix((n,), 80 + i, 0.02)).to(dev) for i, n in enumerate(sizes)]
+        p = [t.to(torch.bfloat16) for t in m]
+        g = [torch.zeros_like(t) for t in m]
+        m1 = [torch.zeros_like(t) for t in m]
+        m2 = [torch.zeros_like(t) for t in m]
+        return H.hpo_set_create_list(p, m, g, m1, m2, [0, 1, 0]), m, g, m1, m2, p
+
+    a, b = adam_twin(), adam_twin()
+    sa, sb = H.new_scaler_state(dev), H.new_scaler_state(dev)
+    for st_ in (sa, sb):
+        H.hpo_scaler_state_init(st_, 256.0, 2, 0)
+    groups = [(1e-3, 0.1), (1e-3, 0.0)]
+    scfg = H.make_scaler_cfg(dynamic=True, growth_interval=2)
+    for k in range(1, 5):
+        scale = H.read_scaler_state(sa).loss_scale
+        grads = [(I.seeded_matrix((n,), 90 * k + i, 1e-2) * F32(scale)).astype(F32) for i, n in enumerate(sizes)]
+        if k == 2:
+            grads[1][7] = np.nan
+        for twin in (a, b):
+            for t, g in zip(twin[2], grads):
+                t.copy_(torch.from_numpy(g))
+        ta = H.read_scaler_state(sa).applied_steps + 1
+        tb = H.read_scaler_state(sb).applied_steps + 1
+        H.hpo_step_device_chain(a[0], H.make_cfg(), groups, None, None, None, 1.0, scfg, sa, ta, 1)
+        H.hpo_step_device(b[0], H.make_cfg(), groups, None, 1.0, scfg, sb, tb, 1)
+        torch.cuda.synchronize()
+        assert sa.cpu().numpy().tobytes() == sb.cpu().numpy().tobytes(), f"scaler state step {k}"
+        for x, y in zip(a[1] + a[3] + a[4] + a[5], b[1] + b[3] + b[4] + b[5]):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y), f"adam-only chain step {k}"
 
 
 def test_muon_profile_counts(H, mu, I):
