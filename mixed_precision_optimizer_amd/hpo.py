@@ -186,6 +186,21 @@ def _require(t: torch.Tensor, dtype, what: str, i: int) -> None:
         raise ValueError(f"{what}[{i}] must be contiguous")
 
 
+def _check_params(params: Sequence[Optional[torch.Tensor]], tensors: Sequence[torch.Tensor]) -> None:
+    """The 16-bit params of one set share one dtype (the set writes them all
+    in one encoding), and every tensor of the set lives on one device."""
+    given = [p for p in params if p is not None]
+    dts = {p.dtype for p in given}
+    if len(dts) > 1:
+        raise TypeError(f"params mix dtypes {sorted(str(d) for d in dts)}; a set writes one encoding")
+    devs = {t.device for t in list(tensors) + given}
+    if len(devs) > 1:
+        raise ValueError(f"the tensors of a set must share one device, got {sorted(str(d) for d in devs)}")
+    for i, p in enumerate(params):
+        if p is not None and not p.is_cuda:
+            raise ValueError(f"params[{i}] must be a device tensor")
+
+
 def param_dtype_code(dtype) -> int:
     """bf16 / fp32 / fp16 -> the library's code; any other dtype goes to the
     library as an unsupported code, which it rejects."""
@@ -251,6 +266,7 @@ def hpo_set_create_list(params: Sequence[Optional[torch.Tensor]], main_params: S
         param_dtype = HPO_PARAM_FP32 if first is None else param_dtype_code(first.dtype)
     mflag = _moments_flag(exp_avgs, exp_avg_sqs)
     mdt = torch.bfloat16 if mflag else torch.float32
+    _check_params(params, list(main_params) + list(main_grads) + list(exp_avgs) + list(exp_avg_sqs))
     numel = []
     for i in range(n):
         for what, lst, dt in (("main_params", main_params, torch.float32), ("main_grads", main_grads, torch.float32),
@@ -288,6 +304,7 @@ def hpo_set_create_flat(param: Optional[torch.Tensor], main_param: torch.Tensor,
         _require(t, dt, what, 0)
         if t.numel() != main_param.numel():
             raise ValueError(f"{what} has the wrong number of elements")
+    _check_params([param], [main_param, main_grad, exp_avg, exp_avg_sq])
     if param_dtype is None:
         param_dtype = HPO_PARAM_FP32 if param is None else param_dtype_code(param.dtype)
     if param is not None and (not param.is_contiguous() or param.numel() != main_param.numel()):
@@ -310,6 +327,7 @@ def hpo_set_create_flat_ranges(param: Optional[torch.Tensor], main_param: torch.
         _require(t, dt, what, 0)
         if t.numel() != main_param.numel():
             raise ValueError(f"{what} has the wrong number of elements")
+    _check_params([param], [main_param, main_grad, exp_avg, exp_avg_sq])
     if param_dtype is None:
         param_dtype = HPO_PARAM_FP32 if param is None else param_dtype_code(param.dtype)
     if param is not None and (not param.is_contiguous() or param.numel() != main_param.numel()):
@@ -435,6 +453,7 @@ def hpo_muon_set_create(params: Sequence[Optional[torch.Tensor]], main_params: S
         raise ValueError("params has the wrong length")
     first = next((p for p in params if p is not None), None)
     param_dtype = HPO_PARAM_FP32 if first is None else param_dtype_code(first.dtype)
+    _check_params(params, list(main_params) + list(main_grads) + list(momenta))
     rows, cols = [], []
     for i in range(n):
         if main_params[i].dim() != 2:

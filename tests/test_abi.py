@@ -281,3 +281,17 @@ def test_muon_step_and_ns_validation(H):
     assert L.hpo_step_device_chain(None, None, None, 0, None, None, None, 0, 1.0, ctypes.byref(scfg),
                                    ctypes.c_void_p(0x1000), 1, 1, None) == H.HPO_EINVAL
     assert L.hpo_grad_global_norm_sets(None, 1, 1.0, ctypes.c_void_p(0x1000), None, None) == H.HPO_EINVAL
+
+
+def test_binding_rejects_mixed_param_dtypes_and_devices(H):
+    """One set writes one 16-bit encoding and lives on one device: the binding
+    refuses lists that mix either, before any library call."""
+    a = torch.zeros(4, dtype=torch.bfloat16)
+    b = torch.zeros(4, dtype=torch.float16)
+    m = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises(TypeError, match="mix dtypes"):
+        H._check_params([a, b], [m])
+    with pytest.raises(ValueError, match="one device"):
+        H._check_params([None], [m, torch.zeros(4, dtype=torch.float32, device="meta")])
+    with pytest.raises(ValueError, match="device tensor"):
+        H._check_params([a], [a.new_zeros(4, dtype=torch.float32)])
