@@ -369,7 +369,10 @@ hpo_status hpo_muon_set_create(hpo_set* out, int32_t n_matrices, int32_t param_d
         const int64_t per = slot_bytes(proto);
         /* as many matrices per batch as the cap allows, then the class
          * split into equal batches (no small remainder batch) */
-        const int32_t most = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(cnt, cap / per)));
+        /* a batch's matrices are the z dimension of its launches (at most 65535) */
+        constexpr int64_t kMaxBatch = 65535;
+        const int64_t fit_cap = std::min<int64_t>(cap / per, kMaxBatch);
+        const int32_t most = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(cnt, fit_cap)));
         const int32_t n_batches = (cnt + most - 1) / most;
         const int32_t fit = (cnt + n_batches - 1) / n_batches;
         for (int32_t a = 0; a < cnt; a += fit) {
