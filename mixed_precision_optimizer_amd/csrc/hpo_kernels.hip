@@ -225,11 +225,6 @@ __device__ __forceinline__ void st_moment1(void* base, int64_t e, float x)
         static_cast<float*>(base)[e] = x;
 }
 
-/* Binary64 sum over a workgroup of NT lanes: shuffle tree inside each
- * wavefront, then wavefront 0 adds the per-wavefront sums in index order.
- * The order is fixed by the lane layout alone, so results are reproducible. */
-
-
 /* ---------------------------------------------------------------------- */
 /* grad pass: non-finite flag + sum of squares, or in-place unscale        */
 /* ---------------------------------------------------------------------- */

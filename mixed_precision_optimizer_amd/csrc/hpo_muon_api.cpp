@@ -11,6 +11,7 @@
  *                §5 (Muon, NS, Moonlight), §11.4 (one norm for a chain),
  *                §14.3 (no fp16 with Muon), §14.6 (update scales)
  */
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <map>

@@ -177,6 +177,45 @@ def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _on_current_device(t: torch.Tensor, what: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"{what} is on {t.device} but the current device is cuda:{cur}")
+
+
+def _dptr(t, what: str, dtype=None, min_bytes: int = 0) -> ctypes.c_void_p:
+    """Device pointer of a buffer argument the kernels read or write.  None is
+    NULL and an int is taken as a raw device address; a tensor must live on
+    the current device, be contiguous, hold `dtype` and span `min_bytes`, so
+    that a host tensor or a short buffer is refused here rather than reaching
+    a kernel."""
+    if t is None or isinstance(t, int):
+        return _ptr(t)
+    _on_current_device(t, what)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    nbytes = t.numel() * t.element_size()
+    if nbytes < min_bytes:
+        raise ValueError(f"{what} spans {nbytes} bytes, the call needs {min_bytes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _flag_ptr(t, what: str = "d_found_inf") -> ctypes.c_void_p:
+    return _dptr(t, what, torch.int32, 4)
+
+
+def _norm_ptr(t, what: str = "d_norm") -> ctypes.c_void_p:
+    return _dptr(t, what, torch.float32, 4)
+
+
+def _state_ptr(t) -> ctypes.c_void_p:
+    return _dptr(t, "d_state", None, SCALER_STATE_BYTES)
+
+
 def _require(t: torch.Tensor, dtype, what: str, i: int) -> None:
     if t.dtype != dtype:
         raise TypeError(f"{what}[{i}] must be {dtype}, got {t.dtype}")
@@ -188,14 +227,18 @@ def _require(t: torch.Tensor, dtype, what: str, i: int) -> None:
 
 def _check_params(params: Sequence[Optional[torch.Tensor]], tensors: Sequence[torch.Tensor]) -> None:
     """The 16-bit params of one set share one dtype (the set writes them all
-    in one encoding), and every tensor of the set lives on one device."""
+    in one encoding), and every tensor of the set lives on one device: the
+    current one, which the library records as the set's device."""
     given = [p for p in params if p is not None]
     dts = {p.dtype for p in given}
     if len(dts) > 1:
         raise TypeError(f"params mix dtypes {sorted(str(d) for d in dts)}; a set writes one encoding")
-    devs = {t.device for t in list(tensors) + given}
+    everything = list(tensors) + given
+    devs = {t.device for t in everything}
     if len(devs) > 1:
         raise ValueError(f"the tensors of a set must share one device, got {sorted(str(d) for d in devs)}")
+    if everything and everything[0].is_cuda:   # host tensors are refused tensor by tensor
+        _on_current_device(everything[0], "the set's tensors")
     for i, p in enumerate(params):
         if p is not None and not p.is_cuda:
             raise ValueError(f"params[{i}] must be a device tensor")
@@ -356,13 +399,13 @@ def hpo_set_info(s: HpoSet) -> hpo_set_info_t:
 
 
 def hpo_unscale_check_inf(s: HpoSet, inv_scale: float, d_found_inf, stream=None) -> None:
-    _check(load().hpo_unscale_check_inf(s.handle, inv_scale, _ptr(d_found_inf), _stream(stream)),
-           "hpo_unscale_check_inf")
+    flag = _flag_ptr(d_found_inf)
+    _check(load().hpo_unscale_check_inf(s.handle, inv_scale, flag, _stream(stream)), "hpo_unscale_check_inf")
 
 
 def hpo_grad_global_norm(s: HpoSet, inv_scale: float, d_norm, d_found_inf=None, stream=None) -> None:
-    _check(load().hpo_grad_global_norm(s.handle, inv_scale, _ptr(d_norm), _ptr(d_found_inf), _stream(stream)),
-           "hpo_grad_global_norm")
+    norm, flag = _norm_ptr(d_norm), _flag_ptr(d_found_inf)
+    _check(load().hpo_grad_global_norm(s.handle, inv_scale, norm, flag, _stream(stream)), "hpo_grad_global_norm")
 
 
 def make_cfg(beta1=0.9, beta2=0.999, eps=1e-8, mode=HPO_ADAMW) -> hpo_adam_cfg:
@@ -382,8 +425,9 @@ def hpo_adamw_step(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int]
     (lr, weight_decay) tuples (n_groups may then be None)."""
     if not isinstance(groups, ctypes.Array):
         groups, n_groups = make_groups(groups)
+    norm, flag = _norm_ptr(d_norm), _flag_ptr(d_found_inf)
     _check(load().hpo_adamw_step(s.handle, ctypes.byref(cfg), groups, n_groups, t, inv_scale, max_norm,
-                                 _ptr(d_norm), _ptr(d_found_inf), _stream(stream)), "hpo_adamw_step")
+                                 norm, flag, _stream(stream)), "hpo_adamw_step")
 
 
 def new_scaler_state(device=None) -> torch.Tensor:
@@ -405,7 +449,8 @@ def make_scaler_cfg(dynamic=True, growth_interval=1000, hysteresis=2, growth_fac
 
 
 def hpo_scaler_state_init(d_state, loss_scale: float, hysteresis: int, applied_steps: int = 0, stream=None) -> None:
-    _check(load().hpo_scaler_state_init(_ptr(d_state), loss_scale, hysteresis, applied_steps, _stream(stream)),
+    state = _state_ptr(d_state)
+    _check(load().hpo_scaler_state_init(state, loss_scale, hysteresis, applied_steps, _stream(stream)),
            "hpo_scaler_state_init")
 
 
@@ -413,8 +458,9 @@ def hpo_step_device(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int
                     scfg: hpo_scaler_cfg, d_state, t_first: int, window: int, stream=None) -> None:
     if not isinstance(groups, ctypes.Array):
         groups, n_groups = make_groups(groups)
+    state = _state_ptr(d_state)
     _check(load().hpo_step_device(s.handle, ctypes.byref(cfg), groups, n_groups, max_norm, ctypes.byref(scfg),
-                                  _ptr(d_state), t_first, window, _stream(stream)), "hpo_step_device")
+                                  state, t_first, window, _stream(stream)), "hpo_step_device")
 
 
 def hpo_copy_main_to_model(s: HpoSet, stream=None) -> None:
@@ -488,15 +534,17 @@ def hpo_muon_step(s: HpoSet, cfg: hpo_muon_cfg, groups, n_groups: Optional[int],
                   max_norm: float = 0.0, d_norm=None, d_found_inf=None, stream=None) -> None:
     if not isinstance(groups, ctypes.Array):
         groups, n_groups = make_groups(groups)
-    _check(load().hpo_muon_step(s.handle, ctypes.byref(cfg), groups, n_groups, inv_scale, max_norm, _ptr(d_norm),
-                                _ptr(d_found_inf), _stream(stream)), "hpo_muon_step")
+    norm, flag = _norm_ptr(d_norm), _flag_ptr(d_found_inf)
+    _check(load().hpo_muon_step(s.handle, ctypes.byref(cfg), groups, n_groups, inv_scale, max_norm, norm, flag,
+                                _stream(stream)), "hpo_muon_step")
 
 
 def hpo_grad_global_norm_sets(sets: Sequence[HpoSet], inv_scale: float, d_norm, d_found_inf=None,
                               stream=None) -> None:
     handles = (ctypes.c_void_p * max(len(sets), 1))(*[x.handle for x in sets])
-    _check(load().hpo_grad_global_norm_sets(handles, len(sets), inv_scale, _ptr(d_norm), _ptr(d_found_inf),
-                                            _stream(stream)), "hpo_grad_global_norm_sets")
+    norm, flag = _norm_ptr(d_norm), _flag_ptr(d_found_inf)
+    _check(load().hpo_grad_global_norm_sets(handles, len(sets), inv_scale, norm, flag, _stream(stream)),
+           "hpo_grad_global_norm_sets")
 
 
 def hpo_step_device_chain(adam_set: Optional[HpoSet], cfg: Optional[hpo_adam_cfg], groups,
@@ -504,11 +552,12 @@ def hpo_step_device_chain(adam_set: Optional[HpoSet], cfg: Optional[hpo_adam_cfg
                           scfg: hpo_scaler_cfg, d_state, t_first: int, window: int, stream=None) -> None:
     g, ng = make_groups(groups) if groups else (None, 0)
     mg, nmg = make_groups(muon_groups) if muon_groups else (None, 0)
+    state = _state_ptr(d_state)
     _check(load().hpo_step_device_chain(adam_set.handle if adam_set else None,
                                         ctypes.byref(cfg) if cfg is not None else None, g, ng,
                                         muon_set.handle if muon_set else None,
                                         ctypes.byref(mcfg) if mcfg is not None else None, mg, nmg, max_norm,
-                                        ctypes.byref(scfg), _ptr(d_state), t_first, window, _stream(stream)),
+                                        ctypes.byref(scfg), state, t_first, window, _stream(stream)),
            "hpo_step_device_chain")
 
 
@@ -527,9 +576,11 @@ def hpo_newton_schulz(G: torch.Tensor, out: torch.Tensor, cfg: hpo_muon_cfg, wor
             raise ValueError(f"{what} must be a contiguous fp32 matrix")
     if tuple(out.shape) != tuple(G.shape):
         raise ValueError("out must have G's shape")
-    _check(load().hpo_newton_schulz(_ptr(G), G.shape[0], G.shape[1], ctypes.byref(cfg), _ptr(out),
-                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
-           "hpo_newton_schulz")
+    g_ptr, o_ptr = _dptr(G, "G"), _dptr(out, "out")
+    ws_ptr = _dptr(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().hpo_newton_schulz(g_ptr, G.shape[0], G.shape[1], ctypes.byref(cfg), o_ptr, ws_ptr, ws_bytes,
+                                    _stream(stream)), "hpo_newton_schulz")
 
 
 def hpo_muon_profile_enable(s: HpoSet, enable: bool = True) -> None:

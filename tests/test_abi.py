@@ -295,3 +295,29 @@ def test_binding_rejects_mixed_param_dtypes_and_devices(H):
         H._check_params([None], [m, torch.zeros(4, dtype=torch.float32, device="meta")])
     with pytest.raises(ValueError, match="device tensor"):
         H._check_params([a], [a.new_zeros(4, dtype=torch.float32)])
+
+
+def test_binding_refuses_host_tensors_as_device_buffers(H):
+    """Buffers the kernels read or write (norm, flag, step state, the
+    Newton-Schulz operands and workspace) must be device tensors: the binding
+    raises on a host tensor before the library is called, so a host address
+    never reaches a kernel."""
+    class NoSet:
+        handle = None
+    s = NoSet()
+    with pytest.raises(ValueError, match="d_norm must be a device tensor"):
+        H.hpo_grad_global_norm(s, 1.0, torch.zeros(1))
+    with pytest.raises(ValueError, match="d_found_inf must be a device tensor"):
+        H.hpo_unscale_check_inf(s, 1.0, torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="d_norm must be a device tensor"):
+        H.hpo_adamw_step(s, H.make_cfg(), [(1e-3, 0.0)], None, 1, 1.0, 1.0, torch.zeros(1))
+    with pytest.raises(ValueError, match="d_found_inf must be a device tensor"):
+        H.hpo_muon_step(s, H.make_muon_cfg(), [(1e-3, 0.0)], None, d_found_inf=torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="d_state must be a device tensor"):
+        H.hpo_scaler_state_init(torch.zeros(6, dtype=torch.int64), 1.0, 1)
+    with pytest.raises(ValueError, match="d_state must be a device tensor"):
+        H.hpo_step_device(s, H.make_cfg(), [(1e-3, 0.0)], None, 1.0, H.make_scaler_cfg(),
+                          torch.zeros(6, dtype=torch.int64), 1, 1)
+    g = torch.zeros(4, 4)
+    with pytest.raises(ValueError, match="G must be a device tensor"):
+        H.hpo_newton_schulz(g, g.clone(), H.make_muon_cfg(), torch.zeros(1 << 16, dtype=torch.uint8))

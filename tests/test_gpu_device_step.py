@@ -153,3 +153,31 @@ def test_window_error_is_reported_not_applied(H):
     with pytest.raises(H.HpoError):
         H.hpo_step_device(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1.0, scfg, d_state, 1, 33)
     hset.close()
+
+
+def test_binding_refuses_wrong_or_short_device_buffers(H):
+    """Device buffers of the wrong dtype, too short or strided are refused by
+    the binding with a clear error, before any kernel could read or write past
+    them; the well-formed call right after still runs."""
+    banner("binding: device buffer checks")
+    n = 4096
+    t = [torch.zeros(n, device=DEV) for _ in range(4)]
+    hset = H.hpo_set_create_list([x.to(torch.bfloat16) for x in t[:1]], t[:1], t[1:2], t[2:3], t[3:4])
+    with pytest.raises(TypeError, match="d_norm must be torch.float32"):
+        H.hpo_grad_global_norm(hset, 1.0, torch.zeros(1, dtype=torch.float64, device=DEV))
+    with pytest.raises(ValueError, match="d_norm spans 0 bytes"):
+        H.hpo_grad_global_norm(hset, 1.0, torch.zeros(0, device=DEV))
+    with pytest.raises(TypeError, match="d_found_inf must be torch.int32"):
+        H.hpo_unscale_check_inf(hset, 1.0, torch.zeros(1, device=DEV))
+    with pytest.raises(ValueError, match="d_state spans 40 bytes"):
+        H.hpo_scaler_state_init(torch.zeros(5, dtype=torch.int64, device=DEV), 1.0, 1)
+    g = torch.zeros(64, 64, device=DEV)
+    ws = torch.zeros(2 * H.hpo_newton_schulz_workspace(64, 64), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError, match="workspace must be contiguous"):
+        H.hpo_newton_schulz(g, torch.empty_like(g), H.make_muon_cfg(), ws[::2])
+    norm = torch.zeros(1, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.hpo_grad_global_norm(hset, 1.0, norm, flag)
+    torch.cuda.synchronize()
+    assert norm.item() == 0.0 and flag.item() == 0
+    hset.close()
