@@ -113,6 +113,31 @@ def measured_muon_traffic():
     return meas, alg
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), for the CPU baselines."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_info(torch) -> dict:
+    """Name, architecture, CU count and memory of device 0, and the HIP and
+    torch versions the run used."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gb": round(p.total_memory / 1e9, 1), "hip": torch.version.hip, "torch": torch.__version__}
+
+
+def spread(ms) -> dict:
+    """Median, minimum and maximum of per-step kernel times (ms)."""
+    return {"ms_median": round(statistics.median(ms), 4), "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4)}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -218,7 +243,7 @@ def cpu_baseline(sample, w, steps):
                       f"steps, single-threaded C ({os.cpu_count()} host CPUs visible); "
                       f"{(update_bytes(w) + GRADPASS_BYTES) * n / dt / 1e9:.2f} GB/s at "
                       f"{update_bytes(w) + GRADPASS_BYTES} B/elem",
-            "ms_per_step": round(dt * 1e3, 2)}
+            "ms_per_step": round(dt * 1e3, 2), "cpu_model": host_cpu_model()}
 
 
 def cpu_baseline_threads(sample, w, steps, threads):
@@ -258,7 +283,7 @@ def cpu_baseline_threads(sample, w, steps, threads):
     return {"value": round(n / dt / 1e9, 4), "unit": "G params/s", "cores": threads, "kind": "oracle",
             "sample": f"the same {n} elements, the oracle's inf check, binary64 sums and update over {threads} "
                       f"slices in {threads} threads (the oracle's C routines unchanged), median of {steps} steps",
-            "ms_per_step": round(dt * 1e3, 2)}
+            "ms_per_step": round(dt * 1e3, 2), "cpu_model": host_cpu_model()}
 
 
 def main():
@@ -357,14 +382,16 @@ def main():
                    "parallelism": "one GPU (one data-parallel rank's shard)"},
         "hbm_full_step": {"GBps": round(step_gbps, 1), "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
                           "bytes_per_elem": ub + GRADPASS_BYTES},
-        "kernels": {"adam_update": {"ms": round(upd, 4), "GBps": round(upd_gbps, 1), "bytes_per_elem": ub},
+        "kernels": {"adam_update": {"ms": round(upd, 4), "GBps": round(upd_gbps, 1), "bytes_per_elem": ub,
+                                    **spread(update_ms)},
                     "grad_pass+finalize": {"ms": round(gp, 4), "GBps": round(gp_gbps, 1),
-                                           "bytes_per_elem": GRADPASS_BYTES}},
+                                           "bytes_per_elem": GRADPASS_BYTES, **spread(gradpass_ms)}},
         "roofline": {"bound": "hbm", "achieved": round(upd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(upd_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_gb,
                      "traffic_unit": "GB per launch of the update kernel (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, "
                                      "scales from a device copy of known size); algorithmic: "
                                      f"{ub * N / 1e9:.1f} GB"},
+        "device": device_info(torch),
     }
     # the same step with the scaler, skip decision and step counter on the
     # device: no host round trip per step (hpo_step_device); constant scale 1
@@ -424,7 +451,8 @@ def muon_cpu_baseline(matrices, steps=1):
     return {"value": round(r * c / (ms * 1e-3) / 1e9, 5), "unit": "G params/s", "cores": threads, "kind": "oracle",
             "sample": f"one {r}x{c} Muon matrix ({name}) of the same workload: momentum, 5-step bf16-reading NS "
                       f"(numpy binary64 matmuls over bf16 values, {threads} BLAS threads), decayed scaled update, "
-                      f"bf16 write-back; median of {steps}", "ms_per_step": round(ms, 2)}
+                      f"bf16 write-back; median of {steps}", "ms_per_step": round(ms, 2),
+            "cpu_model": host_cpu_model()}
 
 
 def main_muon(args, dev):
@@ -532,6 +560,7 @@ def main_muon(args, dev):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": f"k_ns_gemm ({dom}), algorithmic flops per launch {dom_fl:.4g}"},
+        "device": device_info(torch),
     }
     tr = measured_muon_traffic() if dom == "step" else None
     if tr is not None:
