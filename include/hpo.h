@@ -372,8 +372,10 @@ typedef struct {
  * both dimensions padded to multiples of 256.  workspace_bytes caps the
  * batch size (0: HPO_MUON_DEFAULT_WORKSPACE); a shape class is split into
  * equal batches under the cap (and of at most 65535 matrices, the launch
- * grid's z limit), and a matrix that alone needs more gets a batch of its own.  Larger batches keep more of the GPU busy in the NS
- * launches (16 GiB holds 24 of Llama-8B's 4096 x 14336 matrices).  hpo_set_info reports the total in device_bytes.
+ * grid's z limit), and a matrix that alone needs more gets a batch of its
+ * own.  Larger batches keep more of the GPU busy in the NS launches (16 GiB
+ * holds 24 of Llama-8B's 4096 x 14336 matrices).  hpo_set_info reports the
+ * total in device_bytes.
  * hpo_unscale_check_inf, hpo_grad_global_norm, hpo_grad_global_norm_sets and
  * hpo_copy_main_to_model accept Muon sets; hpo_adamw_step and
  * hpo_step_device do not (HPO_EINVAL). */

@@ -223,6 +223,69 @@ def test_norm_matches_oracle_and_is_deterministic(H, orc):
     hset.close()
 
 
+def test_norm_over_several_sets(H, orc):
+    """hpo_grad_global_norm_sets over four sets of the four kinds (list, flat,
+    flat with param ranges, Muon): one norm over every stored grad of all of
+    them, unscaled ([OPT-INFRA] §11.4), equal to the fp32 rounding of the
+    oracle's binary64 sum; repeated calls give the same bits, the sets in
+    reverse order differ at most by the order of four binary64 partials; a
+    non-finite grad in any one set raises the flag; a set given twice and a
+    fifth set are refused."""
+    banner("norm over several sets")
+    rng = np.random.default_rng(11)
+    inv = float(np.float32(1 / 1024))
+    draw = lambda shape: torch.from_numpy((rng.standard_normal(shape) * 1024 * 1e-2).astype(np.float32)).to(DEV)
+    zeros = lambda t: torch.zeros_like(t)
+    lsizes = [5000, 1, 70_001]
+    lg = [draw(n) for n in lsizes]
+    lt = [torch.zeros(n, device=DEV) for n in lsizes]
+    s_list = H.hpo_set_create_list([t.to(torch.bfloat16) for t in lt], lt, lg, [zeros(t) for t in lt],
+                                   [zeros(t) for t in lt], [0, 1, 0])
+    fg = draw(300_007)
+    ft = zeros(fg)
+    s_flat = H.hpo_set_create_flat(ft.to(torch.bfloat16), ft, fg, zeros(ft), zeros(ft))
+    rg = draw(100_000)
+    rt = zeros(rg)
+    s_rng = H.hpo_set_create_flat_ranges(rt.to(torch.bfloat16), rt, rg, zeros(rt), zeros(rt), [0, 4096, 50_000],
+                                         [0, 1, 0])
+    mshapes = [(64, 300), (300, 64)]
+    mg = [draw(s) for s in mshapes]
+    mm = [torch.zeros(s, device=DEV) for s in mshapes]
+    s_mu = H.hpo_muon_set_create([m.to(torch.bfloat16) for m in mm], mm, mg, [zeros(m) for m in mm])
+    sets = [s_list, s_flat, s_rng, s_mu]
+    grads = lg + [fg, rg] + mg
+    n2 = sum(orc.sumsq(to_np(g).ravel(), inv) for g in grads)
+    norm = torch.zeros(1, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.hpo_grad_global_norm_sets(sets, inv, norm, flag)
+    torch.cuda.synchronize()
+    assert flag.item() == 0
+    first = norm.item()
+    assert first == float(np.float32(math.sqrt(n2))), (first, math.sqrt(n2))
+    for _ in range(3):
+        H.hpo_grad_global_norm_sets(sets, inv, norm, None)
+    torch.cuda.synchronize()
+    assert norm.item() == first
+    H.hpo_grad_global_norm_sets(sets[::-1], inv, norm, None)
+    torch.cuda.synchronize()
+    assert abs(norm.item() - first) <= float(np.spacing(np.float32(first)))
+    for k, g in enumerate([lg[2], fg, rg, mg[1]]):
+        flat = g.view(-1)
+        keep = flat[7].item()
+        flat[7] = float("nan") if k % 2 else float("inf")
+        flag.zero_()
+        H.hpo_grad_global_norm_sets(sets, inv, norm, flag)
+        torch.cuda.synchronize()
+        assert flag.item() == 1, f"set {k}: non-finite grad not flagged"
+        flat[7] = keep
+    with pytest.raises(H.HpoError, match="twice"):
+        H.hpo_grad_global_norm_sets([s_list, s_flat, s_list], inv, norm, None)
+    with pytest.raises(H.HpoError):
+        H.hpo_grad_global_norm_sets(sets + [s_list], inv, norm, None)
+    for s in sets:
+        s.close()
+
+
 def test_empty_set_and_zero_sizes(H):
     banner("empty set")
     hset = H.hpo_set_create_list([], [], [], [], [], param_dtype=H.HPO_PARAM_BF16)
