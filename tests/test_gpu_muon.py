@@ -199,7 +199,8 @@ def _grow_bounds(case, mu, cfg, groups, rec):
             2 * np.spacing(W.astype(F32)).astype(np.float64)
 
 
-@pytest.mark.parametrize("variant", ["bf16_sum_nesterov", "fp32_ema", "bf16_plain_shape_scale", "bf16_unit_rms_scale"])
+@pytest.mark.parametrize("variant", ["bf16_sum_nesterov", "fp32_ema", "bf16_ema_plain", "bf16_plain_shape_scale",
+                                     "bf16_unit_rms_scale"])
 def test_muon_set_steps(H, mu, I, variant):
     banner(f"Muon set {variant}")
     dev = torch.device("cuda")
@@ -209,6 +210,9 @@ def test_muon_set_steps(H, mu, I, variant):
     if variant == "fp32_ema":
         cfg_o = mu.MuonCfg(mu=0.9, form=mu.MOMENTUM_EMA)
         cfg = H.make_muon_cfg(momentum=0.9, momentum_form=H.HPO_MUON_MOMENTUM_EMA)
+    elif variant == "bf16_ema_plain":
+        cfg_o = mu.MuonCfg(mu=0.8, form=mu.MOMENTUM_EMA, nesterov=False)
+        cfg = H.make_muon_cfg(momentum=0.8, momentum_form=H.HPO_MUON_MOMENTUM_EMA, nesterov=False)
     elif variant == "bf16_plain_shape_scale":
         cfg_o = mu.MuonCfg(nesterov=False, scale_mode=mu.SCALE_SHAPE, extra_scale=1.0)
         cfg = H.make_muon_cfg(nesterov=False, scale_mode=H.HPO_MUON_SCALE_SHAPE, extra_scale=1.0)
