@@ -413,6 +413,29 @@ def main():
     out["device_resident_step"] = {"ms_per_step": round(dev_ms, 4), "value": round(N / (dev_ms * 1e-3) / 1e9, 3),
                                    "unit": "G params/s",
                                    "note": "hpo_step_device: no per-step host sync; steps re-read the state every 32"}
+    # the same step captured in a HIP graph and replayed (DeviceAdamW.graph): no launch cost per step;
+    # the graph covers HPO_MAX_WINDOW values of t, so it is captured again (after a read of the state)
+    # every HPO_MAX_WINDOW replays, inside the timed region
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    done = 0
+    while done < args.steps:
+        graph = dopt.graph()
+        k = min(hpo.HPO_MAX_WINDOW, args.steps - done)
+        for _ in range(k):
+            graph.replay()
+        done += k
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    gst = dopt.sync()
+    if gst.error or gst.applied_steps != dst.applied_steps + args.steps:
+        raise RuntimeError(f"graph replays: applied {gst.applied_steps - dst.applied_steps} of {args.steps}, "
+                           f"error {gst.error}")
+    log(f"graph-replayed device step: {graph_ms:.3f} ms")
+    out["graph_step"] = {"ms_per_step": round(graph_ms, 4), "value": round(N / (graph_ms * 1e-3) / 1e9, 3),
+                         "unit": "G params/s",
+                         "note": f"the device-resident step captured once per {hpo.HPO_MAX_WINDOW} steps in a "
+                                 "HIP graph (torch.cuda.CUDAGraph) and replayed; captures and state reads timed"}
     hset.close()
     if sample is not None:
         log(f"cpu baseline on {sample[0].size} elements")

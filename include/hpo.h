@@ -233,8 +233,11 @@ hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* g
 /* device, so steps can be enqueued without a host synchronisation.         */
 /* ---------------------------------------------------------------------- */
 
-/* Most unsynchronised steps one call can account for (see hpo_step_device). */
-#define HPO_MAX_WINDOW 32
+/* Most values of t one device-resident call holds bias corrections for (see
+ * hpo_step_device): the steps that can be enqueued, or replayed from one
+ * captured call (a HIP graph), between two reads of the state.  The fp32
+ * tables travel in the kernel arguments (2 KB at 256). */
+#define HPO_MAX_WINDOW 256
 
 /* Loss-scaler and step state kept in device memory (48 bytes, caller-owned,
  * 8-byte aligned).  The caller multiplies its loss by loss_scale before
@@ -293,7 +296,9 @@ hpo_status hpo_scaler_state_init(hpo_scaler_state* d_state, float loss_scale, in
  * (1..HPO_MAX_WINDOW) counts the steps enqueued since that read, this one
  * included; if the device's t falls outside, the step is not applied and
  * d_state->error is set.  Same arithmetic, bit for bit, as the three calls
- * above with the same scale. */
+ * above with the same scale.  The call enqueues kernels only (no allocation,
+ * no copy, no synchronisation), so it can be captured in a HIP graph; a
+ * replay of the graph is one more step of this window. */
 hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
                            double max_norm, const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state,
                            int64_t t_first, int32_t window, void* stream);

@@ -90,7 +90,7 @@ class hpo_scaler_cfg(ctypes.Structure):
                 ("grad_norm_skip_threshold", ctypes.c_double)]
 
 
-HPO_MAX_WINDOW = 32
+HPO_MAX_WINDOW = 256
 SCALER_STATE_BYTES = ctypes.sizeof(hpo_scaler_state)
 
 _P = ctypes.c_void_p

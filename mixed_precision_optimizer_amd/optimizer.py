@@ -69,8 +69,11 @@ class DeviceAdamW:
     """Steps enqueued with no host synchronisation: the loss scaler, the skip
     decision and the applied-step counter live in device memory
     (hpo_step_device).  The host only tracks which t values the unsynchronised
-    steps can have; it reads the state back when that window is full, or when
-    asked (sync / state)."""
+    steps can have; it reads the state back when that window (EAGER_WINDOW
+    steps) is full, or when asked (sync / state).  graph() captures one step
+    for replay over a window of HPO_MAX_WINDOW steps."""
+
+    EAGER_WINDOW = 32   # steps between state reads in step(); each call forms this many bias corrections
 
     def __init__(self, hset: hpo.HpoSet, groups: Sequence[Tuple[float, float]], *, beta1: float = 0.9,
                  beta2: float = 0.999, eps: float = 1e-8, mode: int = hpo.HPO_ADAMW, max_norm: float = 1.0,
@@ -96,11 +99,26 @@ class DeviceAdamW:
         return self.d_state.view(torch.float32)[0:1]
 
     def step(self) -> None:
-        if self.pending == hpo.HPO_MAX_WINDOW:
+        if self.pending == self.EAGER_WINDOW:
             self.sync()
         self.pending += 1
         hpo.hpo_step_device(self.set, self.cfg, self.groups, self.n_groups, self.max_norm, self.scfg, self.d_state,
                             self.t_first, self.pending, self.stream)
+
+    def graph(self) -> "torch.cuda.CUDAGraph":
+        """One step captured in a HIP graph (torch.cuda.CUDAGraph), to be
+        replayed with g.replay() on this optimizer's stream at no launch cost.
+        Nothing of the step lives on the host except the bias-correction table
+        of the next HPO_MAX_WINDOW values of t, which the graph holds: replay it
+        at most that many times, then call sync() and capture again (a replay
+        past the window is not applied and sets the state's error flag, which
+        sync() reports)."""
+        self.sync()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            hpo.hpo_step_device(self.set, self.cfg, self.groups, self.n_groups, self.max_norm, self.scfg,
+                                self.d_state, self.t_first, hpo.HPO_MAX_WINDOW)
+        return g
 
     def sync(self) -> hpo.hpo_scaler_state:
         self.stream.synchronize()

@@ -151,8 +151,66 @@ def test_window_error_is_reported_not_applied(H):
     assert st.error == 1 and st.applied == 0 and st.applied_steps == 0 and st.skipped_steps == 1
     assert torch.equal(th, th0) and not m.any()
     with pytest.raises(H.HpoError):
-        H.hpo_step_device(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1.0, scfg, d_state, 1, 33)
+        H.hpo_step_device(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1.0, scfg, d_state, 1, H.HPO_MAX_WINDOW + 1)
     hset.close()
+
+
+def test_graph_replays_match_eager_steps(H):
+    """The device-resident step keeps no host state between calls, so one
+    step captured in a HIP graph (DeviceAdamW.graph) replays as the step
+    itself.  Twin sets from one seeded state, a dynamic scaler and an inf at
+    step 5: 12 graph replays against 12 eager steps, with fresh grads copied
+    in, other eager work and a synchronisation before every replay; each
+    replay leaves the same bits (params, masters, moments, scaler state) as its
+    eager twin.  Replays past the graph's window of t values are refused on
+    the device (error flag), not applied."""
+    banner("device-resident step replayed from a HIP graph")
+    from mixed_precision_optimizer_amd import DeviceAdamW
+    sizes = [70_001, 4096, 3]
+    rng = np.random.default_rng(430)
+    th0 = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+
+    def make():
+        ths = [torch.from_numpy(a.copy()).to(DEV) for a in th0]
+        ps = [t.to(torch.bfloat16) for t in ths]
+        gs, ms, vs = ([torch.zeros(n, device=DEV) for n in sizes] for _ in range(3))
+        hset = H.hpo_set_create_list(ps, ths, gs, ms, vs, [0, 1, 0])
+        opt = DeviceAdamW(hset, [(1e-3, 0.1), (1e-3, 0.0)], max_norm=1.0, loss_scale=2.0 ** 10, dynamic=True,
+                          growth_interval=3, hysteresis=1)
+        return hset, opt, (ths, ps, gs, ms, vs)
+
+    set_a, opt_a, bufs_a = make()
+    set_b, opt_b, bufs_b = make()
+    graph = opt_a.graph()
+    other = torch.zeros(1 << 20, device=DEV)
+    for k in range(1, 13):
+        scale = H.read_scaler_state(opt_b.d_state).loss_scale
+        G = [(np.random.default_rng(440 + k).standard_normal(n) * 1e-2 * scale).astype(np.float32) for n in sizes]
+        if k == 5:
+            G[0][123] = np.inf
+        for ga, gb, x in zip(bufs_a[2], bufs_b[2], G):
+            ga.copy_(torch.from_numpy(x))
+            gb.copy_(torch.from_numpy(x))
+        other.add_(1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        opt_b.step()
+        torch.cuda.synchronize()
+        for i in range(len(sizes)):
+            for j in (0, 3, 4):
+                assert torch.equal(bufs_a[j][i].view(torch.int32), bufs_b[j][i].view(torch.int32)), (k, i, j)
+            assert torch.equal(bufs_a[1][i].view(torch.int16), bufs_b[1][i].view(torch.int16)), (k, i)
+        assert torch.equal(opt_a.d_state, opt_b.d_state), f"step {k}: scaler state differs"
+    st = H.read_scaler_state(opt_a.d_state)
+    assert st.applied_steps == 11 and st.skipped_steps == 1 and st.error == 0
+    # the graph holds t = 1 .. HPO_MAX_WINDOW: that many applied steps in all, then refusals
+    for _ in range(H.HPO_MAX_WINDOW - 11 + 4):
+        graph.replay()
+    torch.cuda.synchronize()
+    st = H.read_scaler_state(opt_a.d_state)
+    assert st.applied_steps == H.HPO_MAX_WINDOW and st.skipped_steps == 5 and st.error == 1
+    set_a.close()
+    set_b.close()
 
 
 def test_binding_refuses_wrong_or_short_device_buffers(H):
