@@ -64,10 +64,19 @@ int32_t choose_chunk(const int64_t* numel, int32_t n)
     return hpo::kMinChunk;
 }
 
-/* Chunks per grad-pass workgroup: enough to cover kGradSpan elements. */
-int32_t grad_group_of(int32_t chunk_elems)
+/* A grad pass keeps at least this many workgroups (four per CU of a 256-CU
+ * chip) when the set has the chunks for it, so that small sets are still
+ * read by the whole chip. */
+constexpr int64_t kGradMinParts = 1024;
+
+/* Chunks per grad-pass workgroup: enough to cover kGradSpan elements, fewer
+ * where that would leave under kGradMinParts workgroups. */
+int32_t grad_group_of(int32_t chunk_elems, int64_t n_chunks)
 {
-    const int64_t g = hpo::kGradSpan / chunk_elems;
+    int64_t g = hpo::kGradSpan / chunk_elems;
+    const int64_t cap = n_chunks / kGradMinParts;
+    if (g > cap)
+        g = cap;
     return static_cast<int32_t>(g > 1 ? g : 1);
 }
 
@@ -233,7 +242,7 @@ void free_set(hpo_set s)
 
 hpo_status alloc_partials(hpo_set s)
 {
-    s->grad_group = grad_group_of(static_cast<int32_t>(s->view.chunk_elems));
+    s->grad_group = grad_group_of(static_cast<int32_t>(s->view.chunk_elems), s->n_chunks);
     s->n_parts = parts_of(s->n_chunks, s->grad_group);
     const int64_t n = (s->n_parts > 0 ? s->n_parts : 1) + hpo::stage_parts(s->n_parts);
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->d_part_sum), n * sizeof(double));
@@ -308,7 +317,7 @@ hpo_status hpo_plan(int32_t n_tensors, const int64_t* numel, int32_t* out_chunk_
     if (out_device_bytes)
         *out_device_bytes = static_cast<int64_t>(n_tensors) * sizeof(hpo::TensorDesc) +
                             nc * static_cast<int64_t>(sizeof(hpo::Chunk)) +
-                            partial_bytes(parts_of(nc, grad_group_of(ch)));
+                            partial_bytes(parts_of(nc, grad_group_of(ch, nc)));
     return ok();
 }
 

@@ -174,7 +174,9 @@ def test_chunk_plan_partitions_every_tensor(H, sizes):
     assert covered == list(sizes)
     # the set's own device memory is O(tensors + chunks), never per element:
     # descriptors, chunk table, and one binary64 + int32 partial per grad-pass workgroup
-    group = max(1, 65536 // ch)
+    # (a workgroup covers 64K elements' worth of chunks, fewer when that would leave
+    # under 1024 workgroups)
+    group = max(1, min(65536 // ch, nc // 1024))
     parts = (nc + group - 1) // group
     stage = (parts + 8191) // 8192 if parts > 8192 else 0
     assert nb == 64 * len(sizes) + 16 * nc + 12 * (max(parts, 1) + stage)
