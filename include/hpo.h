@@ -453,6 +453,10 @@ typedef struct {
                                           write X and X^T in bf16) */
 } hpo_muon_profile;
 
+/* enable != 0 starts recording (host memory only); enable == 0 waits for the
+ * device to go idle, then drops the events and any unread totals.  Both
+ * take Muon sets only (HPO_EINVAL otherwise); hpo_muon_profile_read is
+ * HPO_EINVAL while timing is off. */
 hpo_status hpo_muon_profile_enable(hpo_set s, int32_t enable);
 hpo_status hpo_muon_profile_read(hpo_set s, hpo_muon_profile* out);
 
