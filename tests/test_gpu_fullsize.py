@@ -103,7 +103,27 @@ def _ranges(bufs):
     return [(bufs.offs[i], n) for i, n in enumerate(w.numels) if n > 0]
 
 
-def _run_fullsize(H, orc, w, picks_kw, steps=None):
+class _DeviceStep:
+    """The device-resident step (hpo_step_device: scaler state, skip decision and
+    t on the device) behind the host-driven optimizer's interface: each step
+    is enqueued, then the state is read back for the comparison."""
+
+    def __init__(self, hset, w):
+        from mixed_precision_optimizer_amd import DeviceAdamW
+        self.opt = DeviceAdamW(hset, w.groups(), beta1=w.beta1, beta2=w.beta2, eps=w.eps, mode=w.mode,
+                               max_norm=w.max_norm, loss_scale=1.0 if w.loss_scale is None else w.loss_scale,
+                               dynamic=False)
+        self.t = 0
+
+    def step(self):
+        self.opt.step()
+        st = self.opt.sync()
+        assert st.error == 0
+        self.t = st.applied_steps
+        return bool(st.applied), (float(st.grad_norm) if st.applied else None)
+
+
+def _run_fullsize(H, orc, w, picks_kw, steps=None, device_step=False):
     from mixed_precision_optimizer_amd import inputs
     banner(f"{w.name}: {w.numel} elements in {w.n_tensors} tensors, allocating {w.numel * 18 / 1e9:.1f} GB")
     bufs = inputs.allocate(w, DEV)
@@ -124,7 +144,7 @@ def _run_fullsize(H, orc, w, picks_kw, steps=None):
         Ts.append(orc.OTensor(big["theta"][sl], big["m"][sl], big["v"][sl], big["p"][sl] if has_p else None, g, fp16))
         lr_e[sl], wd_e[sl] = w.groups()[g]
     hset = make_set(bufs)
-    opt = make_opt(hset, w)
+    opt = _DeviceStep(hset, w) if device_step else make_opt(hset, w)
     hyper = orc.Hyper(w.beta1, w.beta2, w.eps, w.mode)
     inv = w.inv_scale()
     t_orc = 0
@@ -195,6 +215,20 @@ def test_ragged_20000_tensors_with_skip(H, orc):
     from mixed_precision_optimizer_amd import inputs
     w = inputs.ragged()
     stats = _run_fullsize(H, orc, w, dict(head=256, windows_big=1, window=4096, whole_below=1024))
+    assert stats["skipped"] == [3]
+    assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.timeout(900)
+def test_ragged_20000_tensors_device_resident(H, orc):
+    """The same ragged set through the device-resident step: the loss scale
+    (65536) lives in the device state, the norm and skip decision are written
+    there by the two-stage finalize (83K partials), the update takes t from
+    it.  The +inf at step 3 is skipped on the device; every sampled element
+    matches the oracle bit for bit."""
+    from mixed_precision_optimizer_amd import inputs
+    w = inputs.ragged()
+    stats = _run_fullsize(H, orc, w, dict(head=256, windows_big=1, window=4096, whole_below=1024), device_step=True)
     assert stats["skipped"] == [3]
     assert stats["bit_equal"] == stats["compared"]
 
