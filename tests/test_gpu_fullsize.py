@@ -251,3 +251,14 @@ def test_zero_shard_bf16_moments(H, orc):
     w = inputs.zero_shard(state_dtype="bf16")
     stats = _run_fullsize(H, orc, w, dict(head=4096, windows_big=64, window=65536))
     assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.timeout(900)
+def test_zero_shard_fp16_params_bf16_moments(H, orc):
+    """The 70B/8 flat shard with fp16 model params and bf16 moments (the
+    reduced-precision variants together: 22 bytes per element per update),
+    3 steps; the fp16 write-back of every sampled master is checked."""
+    from mixed_precision_optimizer_amd import inputs
+    w = inputs.zero_shard(state_dtype="bf16", param_dtype="fp16")
+    stats = _run_fullsize(H, orc, w, dict(head=4096, windows_big=64, window=65536))
+    assert stats["bit_equal"] == stats["compared"]
