@@ -503,7 +503,7 @@ __global__ __launch_bounds__(T::kThreads, T::kWavesPerSimd) void k_ns_gemm(GemmA
     constexpr int kWavesN = T::kWavesN, kTM = T::kTM, kTN = T::kTN, kBK = T::kBK, kStages = T::kStages;
     constexpr int kBM = T::kBM, kBN = T::kBN, kNsThreads = T::kThreads;
     constexpr int kRowStride = T::kRowStride, kPieces = T::kPieces, kRowsPerChunk = T::kRowsPerChunk;
-    constexpr int kStageBytes = T::kStageBytes, kChunksPerWave = T::kChunksPerWave;
+    constexpr int kChunksPerWave = T::kChunksPerWave;
     static_assert(!SYM || kBM == kBN, "symmetric outputs mirror square tiles");
     if (!gate_open(g.gate))
         return;
