@@ -353,24 +353,29 @@ def test_flat_and_list_sets_agree_bitwise(H):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
-def test_misaligned_tensors_peel_or_go_scalar(H, orc):
+@pytest.mark.parametrize("moments,param", [("fp32", "bf16"), ("bf16", "bf16"), ("bf16", "fp16")])
+def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param):
     """Views that start 1..3 elements into their buffers: when all five
-    pointers share the offset, the head is peeled and the body vectorized;
-    when they do not, the whole tensor runs element by element.  Every
-    layout must give the same bits (and the oracle's)."""
-    banner("misaligned")
+    pointers share the element offset (for 16-bit moments and params, the
+    offset within their own 4-element lines), the head is peeled and the body
+    vectorized; when they do not, the whole tensor runs element by element.
+    Every layout gives the same bits, and the oracle's, for fp32 or bf16
+    moments and bf16 or fp16 params."""
+    banner(f"misaligned, {moments} moments, {param} params")
     n = 50_001
     rng = np.random.default_rng(6)
     th0 = rng.standard_normal(n).astype(np.float32)
     G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    mdt = torch.bfloat16 if moments == "bf16" else torch.float32
+    pdt = torch.float16 if param == "fp16" else torch.bfloat16
     res = []
     layouts = [(0, 0), (1, 1), (2, 2), (3, 3), (1, 2), (0, 3)]  # (shift of master/m/v/param, shift of grad)
     for shift, gshift in layouts:
-        big = [torch.zeros(n + 4, device=DEV) for _ in range(4)]
-        pb = torch.zeros(n + 4, dtype=torch.bfloat16, device=DEV)
-        th, m, v = (b[shift:shift + n] for b in big[:3])
-        g = big[3][gshift:gshift + n]
-        p = pb[shift:shift + n]
+        tb, gb = (torch.zeros(n + 4, device=DEV) for _ in range(2))
+        mb, vb = (torch.zeros(n + 4, dtype=mdt, device=DEV) for _ in range(2))
+        pb = torch.zeros(n + 4, dtype=pdt, device=DEV)
+        th, m, v, p = (b[shift:shift + n] for b in (tb, mb, vb, pb))
+        g = gb[gshift:gshift + n]
         th.copy_(torch.from_numpy(th0))
         g.copy_(torch.from_numpy(G))
         hset = H.hpo_set_create_list([p], [th], [g], [m], [v])
@@ -384,9 +389,10 @@ def test_misaligned_tensors_peel_or_go_scalar(H, orc):
     for r in res[1:]:
         for a, b in zip(res[0], r):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
-    T = orc.OTensor.fresh(th0)
+    T = orc.OTensor.fresh(th0, fp16_param=param == "fp16", state_bf16=moments == "bf16")
     orc.OracleOptimizer([T], orc.Hyper(mode=1), [(1e-3, 0.1)], max_norm=1.0).step([G])
-    assert np.array_equal(res[0][0].view(np.uint32), T.theta.view(np.uint32))
+    for got, want in zip(res[0], (T.theta, T.m, T.v, T.p)):
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
 
 
 def _mini_model_layout():
