@@ -355,12 +355,12 @@ def test_flat_and_list_sets_agree_bitwise(H):
 
 @pytest.mark.parametrize("moments,param", [("fp32", "bf16"), ("bf16", "bf16"), ("bf16", "fp16")])
 def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param):
-    """Views that start 1..3 elements into their buffers: when all five
-    pointers share the element offset (for 16-bit moments and params, the
-    offset within their own 4-element lines), the head is peeled and the body
-    vectorized; when they do not, the whole tensor runs element by element.
-    Every layout gives the same bits, and the oracle's, for fp32 or bf16
-    moments and bf16 or fp16 params."""
+    """Views that start 1..3 elements into their buffers, as a list set and
+    as a flat set: when all five pointers share the element offset (for
+    16-bit moments and params, the offset within their own 4-element lines),
+    the head is peeled and the body vectorized; when they do not, the whole
+    tensor runs element by element.  Every layout and kind gives the same
+    bits, and the oracle's, for fp32 or bf16 moments and bf16 or fp16 params."""
     banner(f"misaligned, {moments} moments, {param} params")
     n = 50_001
     rng = np.random.default_rng(6)
@@ -370,7 +370,7 @@ def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param):
     pdt = torch.float16 if param == "fp16" else torch.bfloat16
     res = []
     layouts = [(0, 0), (1, 1), (2, 2), (3, 3), (1, 2), (0, 3)]  # (shift of master/m/v/param, shift of grad)
-    for shift, gshift in layouts:
+    for (shift, gshift), kind in [(lay, kind) for lay in layouts for kind in ("list", "flat")]:
         tb, gb = (torch.zeros(n + 4, device=DEV) for _ in range(2))
         mb, vb = (torch.zeros(n + 4, dtype=mdt, device=DEV) for _ in range(2))
         pb = torch.zeros(n + 4, dtype=pdt, device=DEV)
@@ -378,8 +378,12 @@ def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param):
         g = gb[gshift:gshift + n]
         th.copy_(torch.from_numpy(th0))
         g.copy_(torch.from_numpy(G))
-        hset = H.hpo_set_create_list([p], [th], [g], [m], [v])
-        assert hset.info().n_vector == (1 if shift == gshift else 0), (shift, gshift)
+        if kind == "list":
+            hset = H.hpo_set_create_list([p], [th], [g], [m], [v])
+        else:   # a flat range off the vector lines is planned as table pieces, still a flat set
+            hset = H.hpo_set_create_flat(p, th, g, m, v)
+            assert hset.info().is_flat == 1
+        assert hset.info().n_vector == (1 if shift == gshift else 0), (shift, gshift, kind)
         norm = torch.zeros(1, device=DEV)
         H.hpo_grad_global_norm(hset, 1.0, norm, None)
         H.hpo_adamw_step(hset, H.make_cfg(mode=1), [(1e-3, 0.1)], None, 1, 1.0, 1.0, norm, None)
