@@ -213,6 +213,68 @@ def test_graph_replays_match_eager_steps(H):
     set_b.close()
 
 
+def test_long_run_eager_then_graph_replays(H, orc):
+    """2000 device-resident steps on a small set against the oracle's scaled
+    trajectory: steps 1..1000 eager (DeviceAdamW.step, the state read every 32
+    steps), steps 1001..2000 replayed from a captured step (captured again
+    every 256 replays).  A dynamic scaler (growth after 40 clean steps,
+    hysteresis 2), infs in pairs (k = 0, 1 mod 97: the second one backs the
+    scale off) and a spike every 151st step that the norm threshold skips.  At every capture and at the end, the scaler
+    state, the counters and every element equal the oracle's, bit for bit."""
+    banner("device-resident step, 2000 steps, eager then graph replays")
+    from mixed_precision_optimizer_amd import DeviceAdamW
+    sizes, gidx = [20_011, 4096, 7], [0, 1, 0]
+    groups = [(1e-3, 0.1), (1e-3, 0.0)]
+    rng = np.random.default_rng(450)
+    th0 = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    ths = [torch.from_numpy(a.copy()).to(DEV) for a in th0]
+    ps = [t.to(torch.bfloat16) for t in ths]
+    gs, ms, vs = ([torch.zeros(n, device=DEV) for n in sizes] for _ in range(3))
+    hset = H.hpo_set_create_list(ps, ths, gs, ms, vs, gidx)
+    scaler = dict(dynamic=True, growth_interval=40, hysteresis=2, min_scale=1.0)
+    opt = DeviceAdamW(hset, groups, max_norm=1.0, loss_scale=2.0 ** 12, grad_norm_skip_threshold=50.0, **scaler)
+    T = [orc.OTensor.fresh(a, group=g) for a, g in zip(th0, gidx)]
+    O = orc.OracleOptimizer(T, orc.Hyper(), groups, max_norm=1.0)
+    sc = orc.LossScaler(scale=2.0 ** 12, **scaler)
+
+    def check(k):
+        st = opt.sync()
+        assert st.error == 0 and st.applied_steps == O.t, (k, st.applied_steps, O.t)
+        assert st.loss_scale == float(sc.scale) and st.growth_tracker == sc.growth_tracker, k
+        assert st.hysteresis_tracker == sc.hysteresis_tracker, k
+        for i in range(len(sizes)):
+            for got, want in ((ths[i], T[i].theta), (ms[i], T[i].m), (vs[i], T[i].v)):
+                assert np.array_equal(to_np(got).view(np.uint32), want.view(np.uint32)), (k, i)
+            assert np.array_equal(to_np(ps[i]), T[i].p), (k, i)
+
+    graph, replays = None, 0
+    skipped = 0
+    for k in range(1, 2001):
+        if k > 1000 and (graph is None or replays == H.HPO_MAX_WINDOW):
+            check(k - 1)   # both sides have taken steps 1 .. k - 1
+            graph, replays = opt.graph(), 0
+        true = [(np.random.default_rng(460 + k).standard_normal(n) * 1e-3).astype(np.float32) for n in sizes]
+        if k % 151 == 0:
+            true = [(t * np.float32(1e4)).astype(np.float32) for t in true]
+        for g, t in zip(gs, true):
+            g.copy_(torch.from_numpy(t))
+            g.mul_(opt.loss_scale_tensor)   # the caller's backward, scaled on the device, no sync
+        stored = [(t * sc.scale).astype(np.float32) for t in true]
+        if k % 97 in (0, 1):
+            gs[0][5] = float("inf")
+            stored[0][5] = np.inf
+        r = O.step_scaled(stored, sc, skip_threshold=50.0)
+        skipped += int(not r.applied)
+        if k <= 1000:
+            opt.step()
+        else:
+            graph.replay()
+            replays += 1
+    check(2000)
+    assert skipped == sum(1 for k in range(1, 2001) if k % 97 in (0, 1) or k % 151 == 0)
+    hset.close()
+
+
 def test_binding_refuses_wrong_or_short_device_buffers(H):
     """Device buffers of the wrong dtype, too short or strided are refused by
     the binding with a clear error, before any kernel could read or write past
