@@ -17,6 +17,11 @@ orders the steps of one optimizer step the way the pages order them:
     §2,§3  the Adam/AdamW update of the fp32 master, m and v;
     §9.2   the master is then written back to the 16-bit model params.
   [FP32-RFC] "支持FP32优化器" §7.2: fp32 params are their own master.
+  [OPT-INFRA] §16: the precision-aware optimizer may keep exp_avg /
+           exp_avg_sq, the main grads and the master below fp32: bf16
+           moments and bf16 grads are widened exactly on read; an fp16 master
+           under bf16 params is widened, updated in fp32 and stored with the
+           fp16 RNE, and the param is the bf16 RNE of the stored master.
 
 ``muon.py`` adds the Muon step (momentum, Newton-Schulz, scaled update)
 and the AdamW + Muon chain in numpy, with its own pins.
@@ -158,6 +163,30 @@ def fp16_rne(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp32, exact: a bf16 value is the fp32
+    value whose upper 16 bits are the pattern and whose lower 16 are zero."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def widen_fp16(bits: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns (uint16) -> fp32, exact (every binary16 value,
+    subnormals and infinities included, is a binary32 value); numpy's half
+    conversion does the widening."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return b.view(np.float16).astype(np.float32)
+
+
+def grad_f32(G: np.ndarray) -> np.ndarray:
+    """A main grad as the step reads it: fp32 as stored, or bf16 bit patterns
+    (uint16 arrays: the lower-precision main grads of the precision-aware
+    optimizer, [OPT-INFRA] §16) widened exactly."""
+    if G.dtype == np.uint16:
+        return widen_bf16(G)
+    return np.ascontiguousarray(G, dtype=np.float32)
+
+
 def any_nonfinite(G: np.ndarray) -> bool:
     G = _f32(G)
     return bool(lib().orc_any_nonfinite(_ptr(G), G.size))
@@ -166,6 +195,16 @@ def any_nonfinite(G: np.ndarray) -> bool:
 def unscale_inplace(G: np.ndarray, inv_scale: float) -> None:
     G = _f32(G)
     lib().orc_unscale_inplace(_ptr(G), G.size, ctypes.c_float(inv_scale))
+
+
+def unscale_inplace_bf16(G: np.ndarray, inv_scale: float) -> None:
+    """The in-place unscale of bf16 main grads: each element is widened, taken
+    through the fp32 unscale above, and stored back with the bf16 RNE (the
+    rounding a bf16 tensor's in-place multiply stores)."""
+    assert G.dtype == np.uint16 and G.flags["C_CONTIGUOUS"]
+    x = widen_bf16(G).copy()
+    unscale_inplace(x, inv_scale)
+    G[...] = bf16_rne(x)
 
 
 def sumsq(G: np.ndarray, inv_scale: float = 1.0) -> float:
@@ -210,6 +249,7 @@ class OTensor:
     p: Optional[np.ndarray] = None    # uint16 bits of the 16-bit model param, or None (fp32 param)
     group: int = 0
     param_fp16: bool = False          # p holds fp16 bits instead of bf16
+    master_fp16: bool = False         # theta holds fp16 bits (uint16) under bf16 params
 
     @property
     def state_bf16(self) -> bool:
@@ -217,18 +257,25 @@ class OTensor:
 
     @staticmethod
     def fresh(theta: np.ndarray, bf16_param: bool = True, group: int = 0, fp16_param: bool = False,
-              state_bf16: bool = False) -> "OTensor":
+              state_bf16: bool = False, fp16_master: bool = False) -> "OTensor":
         theta = np.ascontiguousarray(theta, dtype=np.float32).copy()
+        sdt = np.uint16 if state_bf16 else np.float32
+        if fp16_master:
+            # the master is the fp16 image of the draw; the bf16 param that of the master
+            assert bf16_param and not fp16_param
+            t16 = fp16_rne(theta)
+            return OTensor(t16, np.zeros(theta.shape, sdt), np.zeros(theta.shape, sdt),
+                           bf16_rne(widen_fp16(t16)), group, False, True)
         if fp16_param:
             p = fp16_rne(theta)
         else:
             p = bf16_rne(theta) if bf16_param else None
-        sdt = np.uint16 if state_bf16 else np.float32
         return OTensor(theta, np.zeros(theta.shape, sdt), np.zeros(theta.shape, sdt), p, group, fp16_param)
 
     def copy(self) -> "OTensor":
         return OTensor(self.theta.copy(), self.m.copy(), self.v.copy(),
-                       None if self.p is None else self.p.copy(), self.group, self.param_fp16)
+                       None if self.p is None else self.p.copy(), self.group, self.param_fp16,
+                       self.master_fp16)
 
 
 @dataclass
@@ -251,8 +298,8 @@ def oracle_step(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper: 
     steps including this one.  Returns the step's flags and norm; a skipped
     step leaves every tensor bit-identical.
     """
-    L = lib()
     assert len(tensors) == len(grads)
+    grads = [grad_f32(G) for G in grads]
     inv32 = float(np.float32(inv_scale))
     # a1: found_inf over the stored grads
     found = False
@@ -279,12 +326,19 @@ def apply_update(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper:
                  c64: float, variant: str = "f32") -> None:
     """The update + write-back of one applied step, with the clip decision
     already taken from the global norm (used directly when only a sample of a
-    very large set is stepped on the host)."""
+    very large set is stepped on the host).
+
+    Lower-precision storage ([OPT-INFRA] §16: main grads and main params may
+    be kept below fp32): bf16 grads are widened exactly; an fp16 master is
+    widened exactly, updated in fp32 like an fp32 master, stored back with the
+    fp16 RNE, and the bf16 param is the bf16 RNE of that stored master (the
+    param is a copy of the master, [OPT-INFRA] §9.2)."""
     L = lib()
     fn = L.orc_update_f32 if variant == "f32" else L.orc_update_f64
     for T, G in zip(tensors, grads):
         if T.theta.size == 0:
             continue
+        G = grad_f32(G)
         lr, wd = groups[T.group]
         args = _UpdateArgs(lr=lr, wd=wd, beta1=hyper.beta1, beta2=hyper.beta2,
                            eps=hyper.eps, t=t, mode=hyper.mode, do_clip=int(do_clip),
@@ -296,6 +350,14 @@ def apply_update(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper:
             mp, vp = _ptr(T.m), _ptr(T.v)
         else:
             mp, vp = _ptr(_f32(T.m)), _ptr(_f32(T.v))
+        if T.master_fp16:
+            assert variant == "f32", "an fp16 master is defined for the fp32-literal reading only"
+            assert T.p is not None and not T.param_fp16 and T.theta.dtype == np.uint16
+            th = widen_fp16(T.theta).copy()
+            fn(th.size, _ptr(th), mp, vp, _ptr(_f32(G)), None, ctypes.byref(args))
+            T.theta[...] = fp16_rne(th)
+            T.p[...] = bf16_rne(widen_fp16(T.theta))
+            continue
         fn(T.theta.size, _ptr(_f32(T.theta)), mp, vp,
            _ptr(_f32(np.ascontiguousarray(G))), _ptr(T.p), ctypes.byref(args))
 
@@ -373,6 +435,7 @@ class OracleOptimizer:
         take the norm, skip when it exceeds grad_norm_skip_threshold, else
         clip and update."""
         inv = scaler.inv_scale()
+        grads = [grad_f32(G) for G in grads]
         found = any(G.size and any_nonfinite(G) for G in grads)
         scaler.update(found)
         if found:

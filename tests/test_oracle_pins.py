@@ -564,3 +564,124 @@ def test_bf16_moments_are_the_fp32_update_rounded(orc, mode):
         assert np.array_equal(a.v, torch.from_numpy(b.v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
         with np.errstate(over="ignore"):
             assert np.array_equal(a.p, a.theta.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# lower-precision main grads and master ([OPT-INFRA] §16: main_grads /
+# main_params may be stored below fp32)
+# ---------------------------------------------------------------------------
+def _torch_bits(t):
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_widening_is_exact_for_every_pattern(orc):
+    """bf16 and fp16 -> fp32 over all 65536 patterns equal torch's CPU casts,
+    and the RNE store of a widened value gives the pattern back (NaN by class)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    tb = torch.from_numpy(bits.view(np.int16))
+    for widen, tdt, rne in ((orc.widen_bf16, torch.bfloat16, orc.bf16_rne),
+                            (orc.widen_fp16, torch.float16, orc.fp16_rne)):
+        ours = widen(bits)
+        ref = tb.view(tdt).float().numpy()
+        isnan = np.isnan(ref)
+        assert np.array_equal(np.isnan(ours), isnan)
+        assert np.array_equal(ours[~isnan].view(np.uint32), ref[~isnan].view(np.uint32))
+        assert np.array_equal(rne(ours)[~isnan], bits[~isnan])
+
+
+# (lr, sign of g) -> (fp16 master bits, bf16 param bits) after one step from
+# a master of 1.0: the first AdamW step with eps = 0 and wd = 0 moves the
+# master by -lr * sign(g) (m_hat = g, v_hat = g^2), so the fp32 result is
+# 1 -+ lr up to a few fp32 ulps, and the stores round that:
+#   1 - 2^-9   is an fp16 value (ulp 2^-11 below 1); in bf16 (ulp 2^-8 below
+#              1) it is the midpoint of 1 - 2^-8 and 1, and the tie goes to
+#              the even pattern, 1.0;
+#   1 - 3*2^-13 is 2^-13 from 1 - 2^-11 and 3*2^-13 from 1: fp16 1 - 2^-11;
+#   1 -+ 2^-13 is below half an fp16 ulp on either side of 1: the update is
+#              lost and the master stays 1.0;
+#   1 + 2^-9   is an fp16 value (ulp 2^-10 above 1); bf16 rounds it to 1.0;
+#   1 + 3*2^-13 is 3*2^-13 from 1 and 5*2^-13 from 1 + 2^-10: fp16 1.0.
+_FP16_MASTER_CASES = [
+    (2.0 ** -9, +1, 1.0 - 2.0 ** -9),
+    (3 * 2.0 ** -13, +1, 1.0 - 2.0 ** -11),
+    (2.0 ** -13, +1, 1.0),
+    (2.0 ** -9, -1, 1.0 + 2.0 ** -9),
+    (3 * 2.0 ** -13, -1, 1.0),
+    (2.0 ** -13, -1, 1.0),
+]
+
+
+@pytest.mark.parametrize("lr,sign,master", _FP16_MASTER_CASES)
+def test_fp16_master_first_step_closed_form(orc, lr, sign, master):
+    g = np.full(257, sign * 3.0e-3, np.float32)
+    T = orc.OTensor.fresh(np.ones(257, np.float32), fp16_master=True)
+    assert np.all(T.theta == 0x3C00) and np.all(T.p == 0x3F80)
+    opt = orc.OracleOptimizer([T], orc.Hyper(eps=0.0), [(lr, 0.0)])
+    assert opt.step([g]).applied
+    # every expected master is an fp16 value, so its cast is exact
+    want = np.float16(master).view(np.uint16)
+    assert float(np.float16(master)) == master
+    assert np.all(T.theta == want), hex(int(T.theta[0]))
+    assert np.all(T.p == 0x3F80)
+
+
+@pytest.mark.parametrize("mode", [ADAMW, ADAM_L2])
+def test_fp16_master_is_the_fp32_update_rounded(orc, mode):
+    """An fp16 master steps exactly as an fp32 master holding the same
+    (widened) value, followed by the fp16 rounding of the new master (torch's
+    CPU cast); the bf16 param is torch's bf16 cast of the stored fp16 master."""
+    th, m, v, G = _rand_state(100_003, 61)
+    th16 = torch.from_numpy(th).to(torch.float16)
+    t_b = _torch_bits(th16).copy()
+    t_f = th16.float().numpy().copy()
+    for t in (1, 9):
+        a = orc.OTensor(t_b.copy(), m.copy(), v.copy(), np.zeros(th.size, np.uint16), 0, master_fp16=True)
+        b = orc.OTensor(t_f.copy(), m.copy(), v.copy(), None, 0)
+        for T in (a, b):
+            orc.apply_update([T], [G], orc.Hyper(mode=mode), [(1e-3, 0.1)], t, 1.0, True, 0.5, 0.5)
+        assert np.array_equal(a.m.view(np.uint32), b.m.view(np.uint32))
+        assert np.array_equal(a.v.view(np.uint32), b.v.view(np.uint32))
+        want16 = torch.from_numpy(b.theta).to(torch.float16)
+        assert np.array_equal(a.theta, _torch_bits(want16))
+        assert np.array_equal(a.p, _torch_bits(want16.to(torch.bfloat16)))
+
+
+def test_bf16_grads_step_as_their_exact_fp32_values(orc):
+    """bf16 main grads (uint16 patterns) give the step of their fp32 values
+    (torch's widening cast): same norm, same state; a bf16 inf or NaN
+    pattern skips the step and leaves every array unchanged."""
+    th, m, v, G = _rand_state(40_000, 62)
+    g16 = torch.from_numpy(G * np.float32(2.0 ** 10)).to(torch.bfloat16)
+    gb = _torch_bits(g16).copy()
+    gf = g16.float().numpy().copy()
+    a = orc.OTensor.fresh(th)
+    b = orc.OTensor.fresh(th)
+    ra = orc.oracle_step([a], [gb], orc.Hyper(), [(1e-3, 0.1)], 1, 2.0 ** -10, max_norm=0.1)
+    rb = orc.oracle_step([b], [gf], orc.Hyper(), [(1e-3, 0.1)], 1, 2.0 ** -10, max_norm=0.1)
+    assert ra.applied and rb.applied and ra.clip_applied
+    assert ra.norm64 == rb.norm64
+    assert math.isclose(ra.norm64, math.sqrt(math.fsum((gf.astype(np.float64) * 2.0 ** -10) ** 2)),
+                        rel_tol=1e-12)
+    for x, y in ((a.theta, b.theta), (a.m, b.m), (a.v, b.v), (a.p, b.p)):
+        assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                              y.view(np.uint32) if y.dtype == np.float32 else y)
+    for bad in (0x7F80, 0xFF80, 0x7FC1):
+        gbad = gb.copy()
+        gbad[12345] = bad
+        c = orc.OTensor.fresh(th)
+        before = c.copy()
+        r = orc.oracle_step([c], [gbad], orc.Hyper(), [(1e-3, 0.1)], 1)
+        assert r.found_inf and not r.applied
+        assert np.array_equal(c.theta, before.theta) and np.array_equal(c.p, before.p)
+
+
+def test_bf16_unscale_inplace_matches_torch(orc):
+    """The in-place unscale of bf16 grads stores what torch's CPU bf16
+    in-place multiply stores."""
+    rng = np.random.default_rng(63)
+    x = torch.from_numpy((rng.standard_normal(70_000) * 1e4).astype(np.float32)).to(torch.bfloat16)
+    for inv in (2.0 ** -13, 1.0 / 3.0, 1.0):
+        bits = _torch_bits(x).copy()
+        orc.unscale_inplace_bf16(bits, float(np.float32(inv)))
+        ref = x.clone().mul_(float(np.float32(inv)))
+        assert np.array_equal(bits, _torch_bits(ref))
