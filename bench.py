@@ -34,16 +34,22 @@ sys.path.insert(0, ROOT)
 
 METRIC = "G params/s and achieved HBM GB/s (% of 8 TB/s) per full AdamW step"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
-GRADPASS_BYTES = 4  # the grad pass reads each stored grad once
+
+
+def gradpass_bytes(w) -> int:
+    """The grad pass reads each stored grad once, at its width."""
+    return 2 if getattr(w, "grad_dtype", "fp32") == "bf16" else 4
 
 
 def update_bytes(w) -> int:
     """Algorithmic bytes per element of the fused update for a workload's
-    storage: grad and master read (8), master written (4), each moment read
-    and written at its width, the 16-bit param written (none for fp32)."""
+    storage: the grad read, the master read and written, each moment read
+    and written, all at their widths, and the 16-bit param written (none for
+    fp32 params)."""
     mom = 2 if w.state_dtype == "bf16" else 4
+    mst = 2 if getattr(w, "master_dtype", "fp32") == "fp16" else 4
     par = 0 if w.param_dtype == "fp32" else 2
-    return 12 + 4 * mom + par
+    return gradpass_bytes(w) + 2 * mst + 4 * mom + par
 
 
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_hbm_traffic_zero_shard_70b_over_8.txt")
@@ -157,6 +163,10 @@ def parse():
                     help="exp_avg / exp_avg_sq storage of the flat shard")
     ap.add_argument("--param-dtype", default="bf16", choices=["bf16", "fp16"],
                     help="model-param dtype of the flat shard")
+    ap.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"],
+                    help="main grad storage of the flat shard")
+    ap.add_argument("--master-dtype", default="fp32", choices=["fp32", "fp16"],
+                    help="master storage of the flat shard (fp16 needs bf16 params)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 28,
                     help="elements of the workload the CPU oracle steps (0: skip)")
     ap.add_argument("--cpu-steps", type=int, default=2)
@@ -186,7 +196,8 @@ def workload(args):
     from mixed_precision_optimizer_amd import inputs
     if args.workload == "zero_shard":
         return inputs.zero_shard(args.numel or 8_750_000_000, state_dtype=args.state_dtype,
-                                 param_dtype=args.param_dtype)
+                                 param_dtype=args.param_dtype, grad_dtype=args.grad_dtype,
+                                 master_dtype=args.master_dtype)
     if args.workload == "zero_shard_ranges":
         return inputs.zero_shard_ranges()
     if args.workload == "llama8b":
@@ -218,8 +229,8 @@ def cpu_sample(bufs, n_sample):
     n = min(n_sample, bufs.total)
     host = lambda t: t[:n].detach().cpu().numpy().copy()
     bits = lambda t: t[:n].view(torch.int16).cpu().numpy().view(np.uint16).copy()
-    mom = bits if bufs.exp_avg.dtype == torch.bfloat16 else host
-    return host(bufs.master), mom(bufs.exp_avg), mom(bufs.exp_avg_sq), bits(bufs.param), host(bufs.grad)
+    get = lambda t: host(t) if t.dtype == torch.float32 else bits(t)
+    return get(bufs.master), get(bufs.exp_avg), get(bufs.exp_avg_sq), bits(bufs.param), get(bufs.grad)
 
 
 def cpu_baseline(sample, w, steps):
@@ -227,7 +238,7 @@ def cpu_baseline(sample, w, steps):
     import oracle
     theta, m, v, p, G = sample
     n = theta.size
-    T = oracle.OTensor(theta, m, v, p, 0, w.param_dtype == "fp16")
+    T = oracle.OTensor(theta, m, v, p, 0, w.param_dtype == "fp16", w.master_dtype == "fp16")
     O = oracle.OracleOptimizer([T], oracle.Hyper(w.beta1, w.beta2, w.eps, w.mode), w.groups(),
                                max_norm=w.max_norm)
     times = []
@@ -238,11 +249,11 @@ def cpu_baseline(sample, w, steps):
     dt = statistics.median(times)
     gps = n / dt / 1e9
     return {"value": round(gps, 4), "unit": "G params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} elements of the same workload (initial fp32 master/m/v, bf16 param, step-1 "
-                      f"grads), full step (inf check, binary64 norm, clip, AdamW, bf16 RNE), median of {steps} "
+            "sample": f"first {n} elements of the same workload (initial master/m/v, param, step-1 grads, "
+                      f"as stored), full step (inf check, binary64 norm, clip, AdamW, RNE stores), median of {steps} "
                       f"steps, single-threaded C ({os.cpu_count()} host CPUs visible); "
-                      f"{(update_bytes(w) + GRADPASS_BYTES) * n / dt / 1e9:.2f} GB/s at "
-                      f"{update_bytes(w) + GRADPASS_BYTES} B/elem",
+                      f"{(update_bytes(w) + gradpass_bytes(w)) * n / dt / 1e9:.2f} GB/s at "
+                      f"{update_bytes(w) + gradpass_bytes(w)} B/elem",
             "ms_per_step": round(dt * 1e3, 2), "cpu_model": host_cpu_model()}
 
 
@@ -260,7 +271,8 @@ def cpu_baseline_threads(sample, w, steps, threads):
     theta, m, v, p, G = sample
     n = theta.size
     cuts = [n * k // threads for k in range(threads + 1)]
-    parts = [(oracle.OTensor(theta[a:b], m[a:b], v[a:b], p[a:b], 0, w.param_dtype == "fp16"), G[a:b])
+    parts = [(oracle.OTensor(theta[a:b], m[a:b], v[a:b], p[a:b], 0, w.param_dtype == "fp16",
+                             w.master_dtype == "fp16"), oracle.grad_f32(G[a:b]))
              for a, b in zip(cuts[:-1], cuts[1:])]
     hyper = oracle.Hyper(w.beta1, w.beta2, w.eps, w.mode)
     inv32 = float(np.float32(w.inv_scale()))
@@ -357,8 +369,8 @@ def main():
     gp = statistics.mean(gradpass_ms)
     ub = update_bytes(w)
     upd_gbps = ub * N / (upd * 1e-3) / 1e9
-    gp_gbps = GRADPASS_BYTES * N / (gp * 1e-3) / 1e9
-    step_gbps = (ub + GRADPASS_BYTES) * N / (ms_step * 1e-3) / 1e9
+    gp_gbps = gradpass_bytes(w) * N / (gp * 1e-3) / 1e9
+    step_gbps = (ub + gradpass_bytes(w)) * N / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(w.name, N)
     traffic_gb = None if traffic is None else round(traffic / 1e9, 3)
     log(f"norm {norm_v:.6g}, applied steps {t_applied}; step {ms_step:.3f} ms, update {upd:.3f} ms "
@@ -377,15 +389,16 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "numel": N, "n_tensors": w.n_tensors, "param_dtype": w.param_dtype,
-                   "state": f"fp32 master, fp32 main_grad, {w.state_dtype} exp_avg/exp_avg_sq", "max_norm": w.max_norm,
+                   "state": f"{w.master_dtype} master, {w.grad_dtype} main_grad, {w.state_dtype} exp_avg/exp_avg_sq",
+                   "max_norm": w.max_norm,
                    "lr": w.lr, "weight_decay": w.weight_decay, "loss_scale": w.loss_scale,
                    "parallelism": "one GPU (one data-parallel rank's shard)"},
         "hbm_full_step": {"GBps": round(step_gbps, 1), "frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
-                          "bytes_per_elem": ub + GRADPASS_BYTES},
+                          "bytes_per_elem": ub + gradpass_bytes(w)},
         "kernels": {"adam_update": {"ms": round(upd, 4), "GBps": round(upd_gbps, 1), "bytes_per_elem": ub,
                                     **spread(update_ms)},
                     "grad_pass+finalize": {"ms": round(gp, 4), "GBps": round(gp_gbps, 1),
-                                           "bytes_per_elem": GRADPASS_BYTES, **spread(gradpass_ms)}},
+                                           "bytes_per_elem": gradpass_bytes(w), **spread(gradpass_ms)}},
         "roofline": {"bound": "hbm", "achieved": round(upd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(upd_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_gb,
                      "traffic_unit": "GB per launch of the update kernel (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, "

@@ -81,6 +81,25 @@ typedef enum {
 typedef enum { HPO_PARAM_BF16 = 0, HPO_PARAM_FP32 = 1, HPO_PARAM_FP16 = 2 } hpo_param_dtype;
 #define HPO_STATE_BF16 0x100
 
+/* The main grads and the master may be stored below fp32 as well ([OPT-INFRA]
+ * §16 lists main_grads and main_params among the precision-aware optimizer's
+ * lower-precision fields).  OR-ed into param_dtype like HPO_STATE_BF16:
+ * HPO_GRAD_BF16: main_grad points at bf16 elements (2 bytes), read exactly;
+ *     the norm, the check and the update see their fp32 values.
+ *     hpo_unscale_check_inf stores bf16(fp32(G * inv_scale)), rounded to
+ *     nearest even.
+ * HPO_MASTER_FP16: main_param points at fp16 elements.  Only with
+ *     HPO_PARAM_BF16 (under fp16 params an fp16 master would be the params
+ *     themselves; fp32 params are their own master).  The update widens the
+ *     master exactly, runs in fp32 as for an fp32 master, stores the master
+ *     rounded to nearest even (fp16 subnormals kept, overflow to infinity), and
+ *     writes the bf16 param as the bf16 rounding of the stored fp16 master, as
+ *     hpo_copy_main_to_model does.  An update below half an fp16 ulp of the
+ *     master is lost: that is the format's.
+ * Both are AdamW-set options: Muon sets reject them (HPO_EDTYPE). */
+#define HPO_GRAD_BF16 0x200
+#define HPO_MASTER_FP16 0x400
+
 /* Weight-decay form ([OPT-INFRA] §3): decoupled (AdamW, the default there) or
  * an L2 term added to the gradient before the moments (Adam + L2). */
 typedef enum { HPO_ADAMW = 0, HPO_ADAM_L2 = 1 } hpo_mode;
@@ -139,11 +158,11 @@ typedef enum { HPO_SET_ADAM = 0, HPO_SET_MUON = 1 } hpo_set_kind;
  * group_index[i] in [0, HPO_MAX_GROUPS) selects the tensor's hpo_group in
  * hpo_adamw_step (NULL: every tensor is in group 0).  numel[i] may be 0;
  * n_tensors may be 0 (then every call is a no-op and the norm is 0).
- * Pointers need 4-byte (fp32) and 2-byte (bf16) alignment.  Tensors whose
- * pointers are 16-byte aligned (8-byte for bf16) take 16-byte vector
- * accesses; a tensor whose five pointers sit at the same element offset
- * inside a 16-byte line (a view a few elements into a flat buffer) has its
- * first 1..3 elements stepped one at a time and the rest vectorized; any
+ * Pointers need 4-byte (fp32) and 2-byte (16-bit) alignment.  Tensors whose
+ * pointers are 16-byte aligned (8-byte for 16-bit arrays) take vector
+ * accesses of 4 elements; a tensor whose five pointers sit at the same
+ * element offset inside their aligned 4-element lines (a view a few elements
+ * into a flat buffer) has its first 1..3 elements stepped one at a time and the rest vectorized; any
  * other tensor is stepped one element at a time.  Results are the same bits
  * on every path.
  * The host arrays are read during the call only.  The device tables are
@@ -169,7 +188,7 @@ hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype,
  * [range_start[k], range_start[k+1]) (the last one ends at numel) and uses
  * group range_group[k] in hpo_adamw_step.  range_start[0] must be 0 and the
  * starts strictly increasing (no empty ranges).  Pointers follow the flat
- * set's rules; a range that does not start on a 16-byte line has its first
+ * set's rules; a range that does not start on a 4-element line has its first
  * 1..3 elements stepped one at a time and the rest vectorized. */
 hpo_status hpo_set_create_flat_ranges(hpo_set* out, int64_t numel, int32_t param_dtype, void* param,
                                       float* main_param, float* main_grad, float* exp_avg,

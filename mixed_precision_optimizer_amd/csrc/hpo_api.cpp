@@ -101,22 +101,33 @@ hpo_status check_sizes(int32_t n_tensors, const int64_t* numel)
     return HPO_OK;
 }
 
-/* What a set stores: the model-param dtype and the moments' width. */
+/* What a set stores: the model-param dtype and the widths of the moments,
+ * the main grads and the master. */
 struct Layout {
-    int32_t pdt;        /* HPO_PARAM_BF16 / FP32 / FP16 */
-    int32_t state_bf16; /* exp_avg / exp_avg_sq are bf16 */
+    int32_t pdt;         /* HPO_PARAM_BF16 / FP32 / FP16 */
+    int32_t state_bf16;  /* exp_avg / exp_avg_sq are bf16 */
+    int32_t grad_bf16;   /* main grads are bf16 */
+    int32_t master_fp16; /* the master is fp16 (bf16 params only) */
     int64_t mom_bytes() const { return state_bf16 ? 2 : 4; }
+    int64_t grad_bytes() const { return grad_bf16 ? 2 : 4; }
+    int64_t master_bytes() const { return master_fp16 ? 2 : 4; }
 };
 
 hpo_status decode_dtype(int32_t param_dtype, Layout& lay)
 {
+    constexpr int32_t kFlags = HPO_STATE_BF16 | HPO_GRAD_BF16 | HPO_MASTER_FP16;
     lay.pdt = param_dtype & 0xFF;
     lay.state_bf16 = (param_dtype & HPO_STATE_BF16) ? 1 : 0;
+    lay.grad_bf16 = (param_dtype & HPO_GRAD_BF16) ? 1 : 0;
+    lay.master_fp16 = (param_dtype & HPO_MASTER_FP16) ? 1 : 0;
     const bool pdt_ok = lay.pdt == HPO_PARAM_BF16 || lay.pdt == HPO_PARAM_FP32 || lay.pdt == HPO_PARAM_FP16;
-    if (!pdt_ok || (param_dtype & ~(0xFF | HPO_STATE_BF16)) != 0)
+    if (!pdt_ok || (param_dtype & ~(0xFF | kFlags)) != 0)
         return fail(HPO_EDTYPE,
-                    "param dtype %d is not supported (bf16 = 0, fp32 = 1, fp16 = 2, optionally | HPO_STATE_BF16)",
+                    "param dtype %d is not supported (bf16 = 0, fp32 = 1, fp16 = 2, optionally | HPO_STATE_BF16 "
+                    "| HPO_GRAD_BF16 | HPO_MASTER_FP16)",
                     param_dtype);
+    if (lay.master_fp16 && lay.pdt != HPO_PARAM_BF16)
+        return fail(HPO_EDTYPE, "HPO_MASTER_FP16 needs bf16 params (param dtype %d)", param_dtype);
     return HPO_OK;
 }
 
@@ -133,8 +144,10 @@ hpo_status check_tensor(int32_t i, const Layout& lay, void* param, float* master
         return HPO_OK;
     if (!master || !grad || !m || !v)
         return fail(HPO_EINVAL, "tensor %d: main_param, main_grad, exp_avg and exp_avg_sq must be non-NULL", i);
-    if (!aligned(master, 4) || !aligned(grad, 4))
-        return fail(HPO_EINVAL, "tensor %d: fp32 pointers must be 4-byte aligned", i);
+    if (!aligned(master, static_cast<uintptr_t>(lay.master_bytes())))
+        return fail(HPO_EINVAL, "tensor %d: main_param must be %lld-byte aligned", i, (long long)lay.master_bytes());
+    if (!aligned(grad, static_cast<uintptr_t>(lay.grad_bytes())))
+        return fail(HPO_EINVAL, "tensor %d: main_grad must be %lld-byte aligned", i, (long long)lay.grad_bytes());
     if (!aligned(m, static_cast<uintptr_t>(lay.mom_bytes())) || !aligned(v, static_cast<uintptr_t>(lay.mom_bytes())))
         return fail(HPO_EINVAL, "tensor %d: exp_avg / exp_avg_sq must be %lld-byte aligned", i,
                     (long long)lay.mom_bytes());
@@ -162,15 +175,23 @@ hpo::TensorDesc make_desc(const Layout& lay, void* param, float* master, float* 
     d.numel = numel;
     d.group = group;
     const bool p_ok = (lay.pdt == HPO_PARAM_FP32) || aligned(d.param, 8);
-    const uintptr_t mv = static_cast<uintptr_t>(4 * lay.mom_bytes());  /* 4 elements */
-    d.vec_ok = (aligned(master, 16) && aligned(grad, 16) && aligned(m, mv) && aligned(v, mv) && p_ok) ? 1 : 0;
+    /* 4 elements of each array */
+    const uintptr_t mv = static_cast<uintptr_t>(4 * lay.mom_bytes());
+    const uintptr_t tv = static_cast<uintptr_t>(4 * lay.master_bytes());
+    const uintptr_t gv = static_cast<uintptr_t>(4 * lay.grad_bytes());
+    d.vec_ok = (aligned(master, tv) && aligned(grad, gv) && aligned(m, mv) && aligned(v, mv) && p_ok) ? 1 : 0;
     return d;
 }
 
-/* Position of a pointer inside the line that holds 4 of its elements, in
- * elements: 0..3 (16-byte lines for fp32, 8-byte lines for 16-bit data). */
-int32_t phase32(const void* p) { return static_cast<int32_t>((reinterpret_cast<uintptr_t>(p) / 4) % 4); }
-int32_t phase16(const void* p) { return static_cast<int32_t>((reinterpret_cast<uintptr_t>(p) / 2) % 4); }
+/* Position of a pointer inside the aligned line that holds 4 of its
+ * elements, in elements: 0..3 (16-byte lines for fp32, 8-byte lines for
+ * 16-bit data). */
+int32_t phase_of(const void* p, int64_t bytes)
+{
+    return static_cast<int32_t>((reinterpret_cast<uintptr_t>(p) / static_cast<uintptr_t>(bytes)) % 4);
+}
+
+float* advance_f(float* p, int64_t elems, int64_t bytes) { return static_cast<float*>(advance(p, elems, bytes)); }
 
 /* Appends the descriptor piece(s) of one tensor.  A tensor whose pointers all
  * sit at the same element phase of their 4-element lines (views that start
@@ -190,10 +211,9 @@ bool add_pieces(std::vector<hpo::TensorDesc>& out, const Layout& lay, void* para
         out.push_back(d);
         return true;
     }
-    const int32_t ph = phase32(master);
-    auto mphase = [&](const void* q) { return lay.state_bf16 ? phase16(q) : phase32(q); };
-    const bool same = phase32(grad) == ph && mphase(m) == ph && mphase(v) == ph &&
-                      (lay.pdt == HPO_PARAM_FP32 || phase16(param) == ph);
+    const int32_t ph = phase_of(master, lay.master_bytes());
+    const bool same = phase_of(grad, lay.grad_bytes()) == ph && phase_of(m, lay.mom_bytes()) == ph &&
+                      phase_of(v, lay.mom_bytes()) == ph && (lay.pdt == HPO_PARAM_FP32 || phase_of(param, 2) == ph);
     if (!same) {
         out.push_back(d);
         return false;
@@ -203,7 +223,8 @@ bool add_pieces(std::vector<hpo::TensorDesc>& out, const Layout& lay, void* para
     if (numel == head)
         return false;
     void* p2 = (lay.pdt == HPO_PARAM_FP32) ? nullptr : advance(param, head, 2);
-    hpo::TensorDesc body = make_desc(lay, p2, master + head, grad + head, advance(m, head, lay.mom_bytes()),
+    hpo::TensorDesc body = make_desc(lay, p2, advance_f(master, head, lay.master_bytes()),
+                                     advance_f(grad, head, lay.grad_bytes()), advance(m, head, lay.mom_bytes()),
                                      advance(v, head, lay.mom_bytes()), numel - head, group);
     out.push_back(body);
     return body.vec_ok != 0;
@@ -412,6 +433,8 @@ hpo_status create_from_pieces(hpo_set* out, int32_t param_dtype, const Layout& l
     s->view.is_flat = 0;
     s->view.param_dtype = lay.pdt;
     s->view.state_bf16 = lay.state_bf16;
+    s->view.grad_bf16 = static_cast<int16_t>(lay.grad_bf16);
+    s->view.master_fp16 = static_cast<int16_t>(lay.master_fp16);
     *out = s;
     return ok();
 }
@@ -500,7 +523,8 @@ hpo_status hpo_set_create_flat_ranges(hpo_set* out, int64_t numel, int32_t param
         const int64_t a = range_start[k];
         const int64_t len = (k + 1 < n_ranges ? range_start[k + 1] : numel) - a;
         void* p = (lay.pdt == HPO_PARAM_FP32) ? param : advance(param, a, 2);
-        n_vector += add_pieces(descs, lay, p, main_param + a, main_grad + a, advance(exp_avg, a, lay.mom_bytes()),
+        n_vector += add_pieces(descs, lay, p, advance_f(main_param, a, lay.master_bytes()),
+                               advance_f(main_grad, a, lay.grad_bytes()), advance(exp_avg, a, lay.mom_bytes()),
                                advance(exp_avg_sq, a, lay.mom_bytes()), len, range_group[k]);
     }
     return create_from_pieces(out, param_dtype, lay, descs, n_ranges, n_vector, max_group, stream);
@@ -557,6 +581,8 @@ hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype,
     s->view.is_flat = 1;
     s->view.param_dtype = lay.pdt;
     s->view.state_bf16 = lay.state_bf16;
+    s->view.grad_bf16 = static_cast<int16_t>(lay.grad_bf16);
+    s->view.master_fp16 = static_cast<int16_t>(lay.master_fp16);
     st = alloc_partials(s);
     if (st != HPO_OK) { free_set(s); return st; }
     *out = s;

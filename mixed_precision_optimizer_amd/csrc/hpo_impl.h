@@ -51,8 +51,8 @@ inline int64_t stage_parts(int64_t n) { return n > kFinalSpan ? (n + kFinalSpan 
 /* One tensor of a set, as the kernels see it (64 bytes). */
 struct TensorDesc {
     void* param;       /* 16-bit model param; == master for fp32 sets */
-    float* master;
-    float* grad;
+    float* master;     /* fp32, or fp16 elements in an HPO_MASTER_FP16 set */
+    float* grad;       /* fp32, or bf16 elements in an HPO_GRAD_BF16 set */
     void* exp_avg;     /* fp32 or bf16 elements, per the set's state dtype */
     void* exp_avg_sq;
     int64_t numel;
@@ -81,7 +81,8 @@ struct SetView {
     int32_t is_flat;
     int32_t param_dtype;  /* HPO_PARAM_BF16 / FP32 / FP16 */
     int32_t state_bf16;   /* exp_avg / exp_avg_sq held as bf16 */
-    int32_t reserved;
+    int16_t grad_bf16;    /* main grads held as bf16 */
+    int16_t master_fp16;  /* master held as fp16 (bf16 params) */
 };
 
 /* Per-step scalars of the update, all formed on the host in binary64 and

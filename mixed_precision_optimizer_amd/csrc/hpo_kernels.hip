@@ -153,11 +153,6 @@ __device__ __forceinline__ Range chunk_range(const SetView& sv, int64_t chunk)
     return r;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
-}
-
 /* fp32 -> fp16 bits for fp16 model params ([OPT-INFRA] §9.2 write-back):
  * the hardware conversion, which rounds to nearest even under the default
  * mode and keeps fp16 subnormals. */
@@ -183,46 +178,90 @@ __device__ __forceinline__ uint2 pack_param4(float4 t)
                       param_bits<PDT>(t.z) | (param_bits<PDT>(t.w) << 16));
 }
 
-/* Moments: fp32, or bf16 widened exactly on load and rounded to nearest even
- * on store ([OPT-INFRA] §16, lower-precision exp_avg / exp_avg_sq). */
+/* Storage of the moments, main grads and master ([OPT-INFRA] §16: the
+ * precision-aware optimizer may keep each below fp32): fp32, or a 16-bit
+ * format widened exactly on load and rounded to nearest even on store.  The
+ * arithmetic is fp32 either way. */
+enum Store : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
-template <int SDT>
-__device__ __forceinline__ float4 ld_moment4(const void* base, int64_t i)
+template <int S>
+constexpr int64_t store_bytes() { return S == kF32 ? 4 : 2; }
+
+template <int S>
+__device__ __forceinline__ float widen16(uint32_t b)
 {
-    if constexpr (SDT == 1) {
-        const uint2 w = ld_stream(static_cast<const uint2*>(base) + i);
-        return make_float4(bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
-                           bf16_to_f32(w.y >> 16));
-    } else {
+    if constexpr (S == kF16)
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+    else
+        return bf16_to_f32(b);
+}
+
+template <int S>
+__device__ __forceinline__ uint32_t narrow16(float x)
+{
+    if constexpr (S == kF16)
+        return fp16_rne_bits(x);
+    else
+        return bf16_rne_bits(x);
+}
+
+/* The value a store of x keeps (x itself for fp32). */
+template <int S>
+__device__ __forceinline__ float stored(float x)
+{
+    if constexpr (S == kF32)
+        return x;
+    else
+        return widen16<S>(narrow16<S>(x));
+}
+
+/* 4 consecutive elements at 4-element index i of base. */
+template <int S>
+__device__ __forceinline__ float4 ld4(const void* base, int64_t i)
+{
+    if constexpr (S == kF32) {
         return ld_stream(static_cast<const float4*>(base) + i);
+    } else {
+        const uint2 w = ld_stream(static_cast<const uint2*>(base) + i);
+        return make_float4(widen16<S>(w.x & 0xFFFFu), widen16<S>(w.x >> 16), widen16<S>(w.y & 0xFFFFu),
+                           widen16<S>(w.y >> 16));
     }
 }
 
-template <int SDT>
-__device__ __forceinline__ void st_moment4(void* base, int64_t i, float4 x)
+template <int S>
+__device__ __forceinline__ void st4(void* base, int64_t i, float4 x)
 {
-    if constexpr (SDT == 1)
-        st_stream(static_cast<uint2*>(base) + i, make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)));
-    else
+    if constexpr (S == kF32)
         st_stream(static_cast<float4*>(base) + i, x);
+    else
+        st_stream(static_cast<uint2*>(base) + i, make_uint2(narrow16<S>(x.x) | (narrow16<S>(x.y) << 16),
+                                                            narrow16<S>(x.z) | (narrow16<S>(x.w) << 16)));
 }
 
-template <int SDT>
-__device__ __forceinline__ float ld_moment1(const void* base, int64_t e)
+/* Element e of base. */
+template <int S>
+__device__ __forceinline__ float ld1(const void* base, int64_t e)
 {
-    if constexpr (SDT == 1)
-        return bf16_to_f32(static_cast<const uint16_t*>(base)[e]);
-    else
+    if constexpr (S == kF32)
         return static_cast<const float*>(base)[e];
+    else
+        return widen16<S>(static_cast<const uint16_t*>(base)[e]);
 }
 
-template <int SDT>
-__device__ __forceinline__ void st_moment1(void* base, int64_t e, float x)
+template <int S>
+__device__ __forceinline__ void st1(void* base, int64_t e, float x)
 {
-    if constexpr (SDT == 1)
-        static_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(bf16_rne_bits(x));
-    else
+    if constexpr (S == kF32)
         static_cast<float*>(base)[e] = x;
+    else
+        static_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(narrow16<S>(x));
+}
+
+/* Element `start` of an array of S elements. */
+template <int S>
+__device__ __forceinline__ void* at(void* base, int64_t start)
+{
+    return static_cast<char*>(base) + start * store_bytes<S>();
 }
 
 /* ---------------------------------------------------------------------- */
@@ -240,23 +279,22 @@ __device__ __forceinline__ void grad_elem(float& G, float inv, double& acc, int&
     }
 }
 
-template <GradPass PASS>
+template <GradPass PASS, int GDT>
 __device__ __forceinline__ void grad_range(const Range& r, float inv, double& acc, int& bad)
 {
-    float* __restrict__ G = r.d.grad + r.start;
+    void* __restrict__ G = at<GDT>(r.d.grad, r.start);
     const int tid = threadIdx.x;
     int64_t done = 0;
     if (r.d.vec_ok) {
         constexpr int U = HPO_GRAD_UNROLL;
         const int64_t nv = r.len / kVec;
-        float4* __restrict__ G4 = reinterpret_cast<float4*>(G);
         for (int64_t base = tid; base < nv; base += kGradBlock * U) {
             float4 x[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t i = base + static_cast<int64_t>(u) * kGradBlock;
                 if (i < nv)
-                    x[u] = ld_stream(G4 + i);
+                    x[u] = ld4<GDT>(G, i);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -267,22 +305,22 @@ __device__ __forceinline__ void grad_range(const Range& r, float inv, double& ac
                     grad_elem<PASS>(x[u].z, inv, acc, bad);
                     grad_elem<PASS>(x[u].w, inv, acc, bad);
                     if constexpr (PASS == GradPass::kUnscale)
-                        st_stream(G4 + i, x[u]);
+                        st4<GDT>(G, i, x[u]);
                 }
             }
         }
         done = nv * kVec;
     }
     for (int64_t i = done + tid; i < r.len; i += kGradBlock) {
-        float x = G[i];
+        float x = ld1<GDT>(G, i);
         grad_elem<PASS>(x, inv, acc, bad);
         if constexpr (PASS == GradPass::kUnscale)
-            G[i] = x;
+            st1<GDT>(G, i, x);
     }
 }
 
 /* One workgroup per group of consecutive chunks; one partial per workgroup. */
-template <bool FLAT, GradPass PASS>
+template <bool FLAT, GradPass PASS, int GDT>
 __global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_chunks, int32_t group,
                                                           float inv_arg, const float* d_inv, double* part_sum,
                                                           int32_t* part_flag)
@@ -293,7 +331,7 @@ __global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_
     const int64_t c0 = static_cast<int64_t>(blockIdx.x) * group;
     const int64_t c1 = c0 + group < n_chunks ? c0 + group : n_chunks;
     for (int64_t c = c0; c < c1; ++c)
-        grad_range<PASS>(chunk_range<FLAT>(sv, c), inv, acc, bad);
+        grad_range<PASS, GDT>(chunk_range<FLAT>(sv, c), inv, acc, bad);
     const int any_bad = __syncthreads_or(bad);
     if constexpr (PASS == GradPass::kNorm) {
         const double tot = block_sum<kGradBlock>(acc);
@@ -442,7 +480,10 @@ __device__ __forceinline__ void adam_elem(float G, float& th, float& m, float& v
 #define HPO_ADAM_BOUNDS __launch_bounds__(kBlock)
 #endif
 
-template <bool FLAT, int PDT, int MODE, bool DEV, int SDT>
+/* SDT, GDT, MST: storage (Store) of the moments, the main grads and the
+ * master.  The param written back is the 16-bit rounding of the master as
+ * stored, so an fp16 master and its bf16 param agree with a later copy. */
+template <bool FLAT, int PDT, int MODE, bool DEV, int SDT, int GDT, int MST>
 __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chunks)
 {
     StepVals k;
@@ -481,18 +522,15 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
     const Range r = chunk_range<FLAT>(sv, update_chunk(n_chunks));
     const float lr = sc.lr[r.d.group];
     const float wd = sc.wd[r.d.group];
-    constexpr int64_t kMomBytes = SDT == 1 ? 2 : 4;
-    const float* __restrict__ G = r.d.grad + r.start;
-    float* __restrict__ T = r.d.master + r.start;
-    void* __restrict__ M = static_cast<char*>(r.d.exp_avg) + r.start * kMomBytes;
-    void* __restrict__ V = static_cast<char*>(r.d.exp_avg_sq) + r.start * kMomBytes;
+    const void* __restrict__ G = at<GDT>(r.d.grad, r.start);
+    void* __restrict__ T = at<MST>(r.d.master, r.start);
+    void* __restrict__ M = at<SDT>(r.d.exp_avg, r.start);
+    void* __restrict__ V = at<SDT>(r.d.exp_avg_sq, r.start);
     uint16_t* __restrict__ P = static_cast<uint16_t*>(r.d.param) + r.start;
     const int tid = threadIdx.x;
     int64_t done = 0;
     if (r.d.vec_ok) {
         const int64_t nv = r.len / kVec;
-        const float4* __restrict__ G4 = reinterpret_cast<const float4*>(G);
-        float4* __restrict__ T4 = reinterpret_cast<float4*>(T);
         uint2* __restrict__ P4 = reinterpret_cast<uint2*>(P);
         constexpr int U = HPO_ADAM_UNROLL;
         for (int64_t base = tid; base < nv; base += kBlock * U) {
@@ -501,10 +539,10 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
             for (int u = 0; u < U; ++u) {
                 const int64_t i = base + static_cast<int64_t>(u) * kBlock;
                 if (i < nv) {
-                    g[u] = ld_stream(G4 + i);
-                    th[u] = ld_stream(T4 + i);
-                    m[u] = ld_moment4<SDT>(M, i);
-                    v[u] = ld_moment4<SDT>(V, i);
+                    g[u] = ld4<GDT>(G, i);
+                    th[u] = ld4<MST>(T, i);
+                    m[u] = ld4<SDT>(M, i);
+                    v[u] = ld4<SDT>(V, i);
                 }
             }
 #pragma unroll
@@ -515,9 +553,11 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
                     adam_elem<MODE>(g[u].y, th[u].y, m[u].y, v[u].y, sc, k, lr, wd);
                     adam_elem<MODE>(g[u].z, th[u].z, m[u].z, v[u].z, sc, k, lr, wd);
                     adam_elem<MODE>(g[u].w, th[u].w, m[u].w, v[u].w, sc, k, lr, wd);
-                    st_stream(T4 + i, th[u]);
-                    st_moment4<SDT>(M, i, m[u]);
-                    st_moment4<SDT>(V, i, v[u]);
+                    th[u] = make_float4(stored<MST>(th[u].x), stored<MST>(th[u].y), stored<MST>(th[u].z),
+                                        stored<MST>(th[u].w));
+                    st4<MST>(T, i, th[u]);
+                    st4<SDT>(M, i, m[u]);
+                    st4<SDT>(V, i, v[u]);
                     if constexpr (PDT != HPO_PARAM_FP32)
                         st_stream(P4 + i, pack_param4<PDT>(th[u]));
                 }
@@ -526,11 +566,12 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
         done = nv * kVec;
     }
     for (int64_t i = done + tid; i < r.len; i += kBlock) {
-        float th = T[i], m = ld_moment1<SDT>(M, i), v = ld_moment1<SDT>(V, i);
-        adam_elem<MODE>(G[i], th, m, v, sc, k, lr, wd);
-        T[i] = th;
-        st_moment1<SDT>(M, i, m);
-        st_moment1<SDT>(V, i, v);
+        float th = ld1<MST>(T, i), m = ld1<SDT>(M, i), v = ld1<SDT>(V, i);
+        adam_elem<MODE>(ld1<GDT>(G, i), th, m, v, sc, k, lr, wd);
+        th = stored<MST>(th);
+        st1<MST>(T, i, th);
+        st1<SDT>(M, i, m);
+        st1<SDT>(V, i, v);
         if constexpr (PDT != HPO_PARAM_FP32)
             P[i] = static_cast<uint16_t>(param_bits<PDT>(th));
     }
@@ -539,24 +580,23 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
 /* ---------------------------------------------------------------------- */
 /* master -> model copy                                                   */
 /* ---------------------------------------------------------------------- */
-template <bool FLAT, int PDT>
+template <bool FLAT, int PDT, int MST>
 __global__ __launch_bounds__(kBlock) void k_copy_main_to_model(SetView sv)
 {
     const Range r = chunk_range<FLAT>(sv, blockIdx.x);
-    const float* __restrict__ T = r.d.master + r.start;
+    const void* __restrict__ T = at<MST>(r.d.master, r.start);
     uint16_t* __restrict__ P = static_cast<uint16_t*>(r.d.param) + r.start;
     const int tid = threadIdx.x;
     int64_t done = 0;
     if (r.d.vec_ok) {
         const int64_t nv = r.len / kVec;
-        const float4* __restrict__ T4 = reinterpret_cast<const float4*>(T);
         uint2* __restrict__ P4 = reinterpret_cast<uint2*>(P);
         for (int64_t i = tid; i < nv; i += kBlock)
-            P4[i] = pack_param4<PDT>(T4[i]);
+            P4[i] = pack_param4<PDT>(ld4<MST>(T, i));
         done = nv * kVec;
     }
     for (int64_t i = done + tid; i < r.len; i += kBlock)
-        P[i] = static_cast<uint16_t>(param_bits<PDT>(T[i]));
+        P[i] = static_cast<uint16_t>(param_bits<PDT>(ld1<MST>(T, i)));
 }
 
 /* ---------------------------------------------------------------------- */
@@ -631,8 +671,10 @@ hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_gr
         return hipSuccess;
     const int64_t grid = (n_chunks + grad_group - 1) / grad_group;
     const bool flat = sv.is_flat != 0;
-#define HPO_GRAD_LAUNCH(F, P) \
-    launch(k_grad_pass<F, P>, grid, kGradBlock, stream, sv, n_chunks, grad_group, inv_scale, d_inv, part_sum, part_flag)
+#define HPO_GRAD_LAUNCH_G(F, P, G) \
+    launch(k_grad_pass<F, P, G>, grid, kGradBlock, stream, sv, n_chunks, grad_group, inv_scale, d_inv, part_sum, \
+           part_flag)
+#define HPO_GRAD_LAUNCH(F, P) (sv.grad_bf16 ? HPO_GRAD_LAUNCH_G(F, P, kBF16) : HPO_GRAD_LAUNCH_G(F, P, kF32))
     switch (pass) {
     case GradPass::kNorm:
         return flat ? HPO_GRAD_LAUNCH(true, GradPass::kNorm) : HPO_GRAD_LAUNCH(false, GradPass::kNorm);
@@ -642,38 +684,53 @@ hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_gr
         return flat ? HPO_GRAD_LAUNCH(true, GradPass::kUnscale) : HPO_GRAD_LAUNCH(false, GradPass::kUnscale);
     }
 #undef HPO_GRAD_LAUNCH
+#undef HPO_GRAD_LAUNCH_G
     return hipErrorInvalidValue;
 }
 
-template <bool DEV, int SDT, int PDT>
+template <bool DEV, int SDT, int GDT, int PDT, int MST>
 hipError_t launch_adam_p(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                          hipStream_t stream)
 {
     const bool flat = sv.is_flat != 0;
     if (mode == HPO_ADAMW)
-        return flat ? launch(k_adam<true, PDT, HPO_ADAMW, DEV, SDT>, n_chunks, kBlock, stream, sv, sc, n_chunks)
-                    : launch(k_adam<false, PDT, HPO_ADAMW, DEV, SDT>, n_chunks, kBlock, stream, sv, sc, n_chunks);
-    return flat ? launch(k_adam<true, PDT, HPO_ADAM_L2, DEV, SDT>, n_chunks, kBlock, stream, sv, sc, n_chunks)
-                : launch(k_adam<false, PDT, HPO_ADAM_L2, DEV, SDT>, n_chunks, kBlock, stream, sv, sc, n_chunks);
+        return flat ? launch(k_adam<true, PDT, HPO_ADAMW, DEV, SDT, GDT, MST>, n_chunks, kBlock, stream, sv, sc,
+                             n_chunks)
+                    : launch(k_adam<false, PDT, HPO_ADAMW, DEV, SDT, GDT, MST>, n_chunks, kBlock, stream, sv, sc,
+                             n_chunks);
+    return flat ? launch(k_adam<true, PDT, HPO_ADAM_L2, DEV, SDT, GDT, MST>, n_chunks, kBlock, stream, sv, sc,
+                         n_chunks)
+                : launch(k_adam<false, PDT, HPO_ADAM_L2, DEV, SDT, GDT, MST>, n_chunks, kBlock, stream, sv, sc,
+                         n_chunks);
 }
 
-template <bool DEV, int SDT>
+template <bool DEV, int SDT, int GDT>
 hipError_t launch_adam_s(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                          hipStream_t stream)
 {
     switch (sv.param_dtype) {
-    case HPO_PARAM_BF16: return launch_adam_p<DEV, SDT, HPO_PARAM_BF16>(sv, n_chunks, mode, sc, stream);
-    case HPO_PARAM_FP16: return launch_adam_p<DEV, SDT, HPO_PARAM_FP16>(sv, n_chunks, mode, sc, stream);
-    default: return launch_adam_p<DEV, SDT, HPO_PARAM_FP32>(sv, n_chunks, mode, sc, stream);
+    case HPO_PARAM_BF16:
+        return sv.master_fp16 ? launch_adam_p<DEV, SDT, GDT, HPO_PARAM_BF16, kF16>(sv, n_chunks, mode, sc, stream)
+                              : launch_adam_p<DEV, SDT, GDT, HPO_PARAM_BF16, kF32>(sv, n_chunks, mode, sc, stream);
+    case HPO_PARAM_FP16: return launch_adam_p<DEV, SDT, GDT, HPO_PARAM_FP16, kF32>(sv, n_chunks, mode, sc, stream);
+    default: return launch_adam_p<DEV, SDT, GDT, HPO_PARAM_FP32, kF32>(sv, n_chunks, mode, sc, stream);
     }
+}
+
+template <bool DEV, int SDT>
+hipError_t launch_adam_g(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+                         hipStream_t stream)
+{
+    return sv.grad_bf16 ? launch_adam_s<DEV, SDT, kBF16>(sv, n_chunks, mode, sc, stream)
+                        : launch_adam_s<DEV, SDT, kF32>(sv, n_chunks, mode, sc, stream);
 }
 
 template <bool DEV>
 hipError_t launch_adam_t(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                          hipStream_t stream)
 {
-    return sv.state_bf16 ? launch_adam_s<DEV, 1>(sv, n_chunks, mode, sc, stream)
-                         : launch_adam_s<DEV, 0>(sv, n_chunks, mode, sc, stream);
+    return sv.state_bf16 ? launch_adam_g<DEV, kBF16>(sv, n_chunks, mode, sc, stream)
+                         : launch_adam_g<DEV, kF32>(sv, n_chunks, mode, sc, stream);
 }
 
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
@@ -769,10 +826,13 @@ hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStr
     if (n_chunks == 0 || sv.param_dtype == HPO_PARAM_FP32)
         return hipSuccess;
     if (sv.param_dtype == HPO_PARAM_FP16)
-        return sv.is_flat ? launch(k_copy_main_to_model<true, HPO_PARAM_FP16>, n_chunks, kBlock, stream, sv)
-                          : launch(k_copy_main_to_model<false, HPO_PARAM_FP16>, n_chunks, kBlock, stream, sv);
-    return sv.is_flat ? launch(k_copy_main_to_model<true, HPO_PARAM_BF16>, n_chunks, kBlock, stream, sv)
-                      : launch(k_copy_main_to_model<false, HPO_PARAM_BF16>, n_chunks, kBlock, stream, sv);
+        return sv.is_flat ? launch(k_copy_main_to_model<true, HPO_PARAM_FP16, kF32>, n_chunks, kBlock, stream, sv)
+                          : launch(k_copy_main_to_model<false, HPO_PARAM_FP16, kF32>, n_chunks, kBlock, stream, sv);
+    if (sv.master_fp16)
+        return sv.is_flat ? launch(k_copy_main_to_model<true, HPO_PARAM_BF16, kF16>, n_chunks, kBlock, stream, sv)
+                          : launch(k_copy_main_to_model<false, HPO_PARAM_BF16, kF16>, n_chunks, kBlock, stream, sv);
+    return sv.is_flat ? launch(k_copy_main_to_model<true, HPO_PARAM_BF16, kF32>, n_chunks, kBlock, stream, sv)
+                      : launch(k_copy_main_to_model<false, HPO_PARAM_BF16, kF32>, n_chunks, kBlock, stream, sv);
 }
 
 }  // namespace hpo

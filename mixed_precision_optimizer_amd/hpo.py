@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libhpo.so")
 HPO_OK, HPO_EINVAL, HPO_EDTYPE, HPO_ENOMEM, HPO_EHIP, HPO_EDEVICE = 0, -1, -2, -3, -4, -5
 HPO_PARAM_BF16, HPO_PARAM_FP32, HPO_PARAM_FP16 = 0, 1, 2
 HPO_STATE_BF16 = 0x100
+HPO_GRAD_BF16 = 0x200
+HPO_MASTER_FP16 = 0x400
 HPO_ADAMW, HPO_ADAM_L2 = 0, 1
 HPO_MAX_GROUPS = 16
 
@@ -267,6 +269,25 @@ def _moments_flag(exp_avgs, exp_avg_sqs) -> int:
     raise TypeError(f"exp_avg / exp_avg_sq must all be float32 or all bfloat16, got {sorted(map(str, dts))}")
 
 
+def _storage_flags(main_params, main_grads, exp_avgs, exp_avg_sqs):
+    """(flags, master dtype, grad dtype, moment dtype) of a set's arrays: the
+    master fp32 or fp16 (HPO_MASTER_FP16), the grads fp32 or bf16
+    (HPO_GRAD_BF16), the moments fp32 or bf16 (HPO_STATE_BF16); each kind
+    shares one dtype over the whole set."""
+    flags = _moments_flag(exp_avgs, exp_avg_sqs)
+    mdt = torch.bfloat16 if flags else torch.float32
+    out = [flags, torch.float32, torch.float32, mdt]
+    for k, what, ts, low, flag in ((1, "main_param", main_params, torch.float16, HPO_MASTER_FP16),
+                                   (2, "main_grad", main_grads, torch.bfloat16, HPO_GRAD_BF16)):
+        dts = {t.dtype for t in ts}
+        if dts == {low}:
+            out[0] |= flag
+            out[k] = low
+        elif dts and dts != {torch.float32}:
+            raise TypeError(f"{what} tensors must all be float32 or all {low}, got {sorted(map(str, dts))}")
+    return tuple(out)
+
+
 # --------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # --------------------------------------------------------------------------
@@ -307,12 +328,11 @@ def hpo_set_create_list(params: Sequence[Optional[torch.Tensor]], main_params: S
     if param_dtype is None:
         first = next((p for p in params if p is not None), None)
         param_dtype = HPO_PARAM_FP32 if first is None else param_dtype_code(first.dtype)
-    mflag = _moments_flag(exp_avgs, exp_avg_sqs)
-    mdt = torch.bfloat16 if mflag else torch.float32
+    mflag, tdt, gdt, mdt = _storage_flags(main_params, main_grads, exp_avgs, exp_avg_sqs)
     _check_params(params, list(main_params) + list(main_grads) + list(exp_avgs) + list(exp_avg_sqs))
     numel = []
     for i in range(n):
-        for what, lst, dt in (("main_params", main_params, torch.float32), ("main_grads", main_grads, torch.float32),
+        for what, lst, dt in (("main_params", main_params, tdt), ("main_grads", main_grads, gdt),
                               ("exp_avgs", exp_avgs, mdt), ("exp_avg_sqs", exp_avg_sqs, mdt)):
             _require(lst[i], dt, what, i)
             if lst[i].numel() != main_params[i].numel():
@@ -340,9 +360,8 @@ def hpo_set_create_list(params: Sequence[Optional[torch.Tensor]], main_params: S
 def hpo_set_create_flat(param: Optional[torch.Tensor], main_param: torch.Tensor, main_grad: torch.Tensor,
                         exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, param_dtype: Optional[int] = None,
                         stream=None) -> HpoSet:
-    mflag = _moments_flag([exp_avg], [exp_avg_sq])
-    mdt = torch.bfloat16 if mflag else torch.float32
-    for what, t, dt in (("main_param", main_param, torch.float32), ("main_grad", main_grad, torch.float32),
+    mflag, tdt, gdt, mdt = _storage_flags([main_param], [main_grad], [exp_avg], [exp_avg_sq])
+    for what, t, dt in (("main_param", main_param, tdt), ("main_grad", main_grad, gdt),
                         ("exp_avg", exp_avg, mdt), ("exp_avg_sq", exp_avg_sq, mdt)):
         _require(t, dt, what, 0)
         if t.numel() != main_param.numel():
@@ -363,9 +382,8 @@ def hpo_set_create_flat(param: Optional[torch.Tensor], main_param: torch.Tensor,
 def hpo_set_create_flat_ranges(param: Optional[torch.Tensor], main_param: torch.Tensor, main_grad: torch.Tensor,
                                exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, range_start: Sequence[int],
                                range_group: Sequence[int], param_dtype: Optional[int] = None, stream=None) -> HpoSet:
-    mflag = _moments_flag([exp_avg], [exp_avg_sq])
-    mdt = torch.bfloat16 if mflag else torch.float32
-    for what, t, dt in (("main_param", main_param, torch.float32), ("main_grad", main_grad, torch.float32),
+    mflag, tdt, gdt, mdt = _storage_flags([main_param], [main_grad], [exp_avg], [exp_avg_sq])
+    for what, t, dt in (("main_param", main_param, tdt), ("main_grad", main_grad, gdt),
                         ("exp_avg", exp_avg, mdt), ("exp_avg_sq", exp_avg_sq, mdt)):
         _require(t, dt, what, 0)
         if t.numel() != main_param.numel():

@@ -37,6 +37,8 @@ class Workload:
     ndims: List[int]
     param_dtype: str = "bf16"          # "bf16", "fp16" or "fp32" (fp32 params are their own master)
     state_dtype: str = "fp32"          # exp_avg / exp_avg_sq storage: "fp32" or "bf16"
+    grad_dtype: str = "fp32"           # main grad storage: "fp32" or "bf16" (the bf16 image of the fp32 draw)
+    master_dtype: str = "fp32"         # master storage: "fp32" or "fp16" (the fp16 image of the fp32 draw)
     lr: float = 1e-3
     weight_decay: float = 0.1
     beta1: float = 0.9
@@ -122,12 +124,17 @@ def ragged(n: int = 20000, max_elems: int = 4 * 2 ** 20, steps: int = 8, inf_ste
                     loss_scale=65536.0, steps=steps, grad_std=[1e-3] * n, inf_step=inf_step)
 
 
-def zero_shard(numel: int = 8_750_000_000, state_dtype: str = "fp32", param_dtype: str = "bf16") -> Workload:
+def zero_shard(numel: int = 8_750_000_000, state_dtype: str = "fp32", param_dtype: str = "bf16",
+               grad_dtype: str = "fp32", master_dtype: str = "fp32") -> Workload:
     # a flat shard mixes every kind of param; it is stepped as one decaying group
     tag = "" if (state_dtype, param_dtype) == ("fp32", "bf16") else f"_{param_dtype}_params_{state_dtype}_moments"
+    if grad_dtype != "fp32":
+        tag += f"_{grad_dtype}_grads"
+    if master_dtype != "fp32":
+        tag += f"_{master_dtype}_master"
     return Workload(f"zero1_shard_70b_over_8{tag}", [numel], [1], lr=1e-3, weight_decay=0.1, max_norm=1.0,
                     steps=3, grad_std=[1e-4], flat=True, no_decay_1d=False, state_dtype=state_dtype,
-                    param_dtype=param_dtype)
+                    param_dtype=param_dtype, grad_dtype=grad_dtype, master_dtype=master_dtype)
 
 
 def llama70b_shapes():
@@ -230,10 +237,22 @@ class Buffers:
                 [self.view(self.exp_avg_sq, i) for i in range(w.n_tensors)])
 
 
+def _narrowed(x: torch.Tensor, dtype) -> torch.Tensor:
+    """A 16-bit copy of x made in FILL_CHUNK slices (torch's cast)."""
+    out = torch.empty(x.numel(), dtype=dtype, device=x.device)
+    for a in range(0, x.numel(), FILL_CHUNK):
+        b = min(x.numel(), a + FILL_CHUNK)
+        out[a:b].copy_(x[a:b])
+    return out
+
+
 def allocate(w: Workload, device) -> Buffers:
     """Allocate flat master/grad/m/v (+bf16 param) buffers and initialise the
     state: master N(0,1) from ``master_seed``, m = v = 0, param = bf16 cast of
-    the master (torch's cast; the param's initial value is an input)."""
+    the master (torch's cast; the param's initial value is an input).  An
+    fp16 master holds the fp16 image of the same draw, and the param is then
+    the cast of that fp16 master; bf16 grads are the bf16 image of the fp32
+    grads fill_grads_ draws."""
     if w.flat:
         # a flat shard, possibly cut into ranges of different groups: the
         # ranges are consecutive, with no gaps
@@ -251,7 +270,9 @@ def allocate(w: Workload, device) -> Buffers:
         master[offs[1]:offs[1] + m[1].numel()].copy_(m[1].reshape(-1))
     else:
         fill_normal_(master, w.master_seed)
-    grad = torch.zeros(total, **f32)
+    if w.master_dtype == "fp16":
+        master = _narrowed(master, torch.float16)
+    grad = torch.zeros(total, dtype=torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32, device=device)
     sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
     exp_avg = torch.zeros(total, dtype=sdt, device=device)
     exp_avg_sq = torch.zeros(total, dtype=sdt, device=device)
@@ -283,6 +304,15 @@ def fill_grads_(bufs: Buffers, k: int) -> None:
     multiplied by its std, then by the loss scale (exact for powers of two);
     at ``inf_step`` one element becomes +inf (see inf_position)."""
     w = bufs.workload
+    if bufs.grad.dtype != torch.float32:
+        # the 16-bit image of the fp32 grads below (torch's cast)
+        full = Buffers(w, bufs.offs, bufs.total, bufs.master, torch.empty(bufs.total, dtype=torch.float32,
+                       device=bufs.grad.device), bufs.exp_avg, bufs.exp_avg_sq, bufs.param)
+        fill_grads_(full, k)
+        for a in range(0, bufs.total, FILL_CHUNK):
+            b = min(bufs.total, a + FILL_CHUNK)
+            bufs.grad[a:b].copy_(full.grad[a:b])
+        return
     if w.name.startswith("toy"):
         bufs.grad[:2].copy_(torch.from_numpy(toy_grad(k)))
         return

@@ -50,6 +50,18 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+def widen_fp16(bits: np.ndarray) -> np.ndarray:
+    """torch's CPU fp16 -> fp32 cast of fp16 bit patterns."""
+    return torch.from_numpy(bits.view(np.int16)).view(torch.float16).float().numpy()
+
+
+def ordered16(bits: np.ndarray) -> np.ndarray:
+    """Sign-magnitude 16-bit float patterns mapped to integers in value order,
+    so that adjacent values differ by one."""
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
 def make_set(bufs, stream=None):
     from mixed_precision_optimizer_amd import hpo
     w = bufs.workload
@@ -81,9 +93,13 @@ def compare_tensor(tag, gpu, orc_new, orc_prev, G, *, inv, clip, C, c64, lr, wd,
     fp32 moments: the rel-1e-6 propagated bound; bf16 moments: within one bf16
     ulp (the master's bound then uses the widened moments)."""
     sbf16 = orc_new.m.dtype == np.uint16
+    t16 = getattr(orc_new, "master_fp16", False)
     m_prev = widen_bf16(orc_prev.m) if sbf16 else orc_prev.m
     v_prev = widen_bf16(orc_prev.v) if sbf16 else orc_prev.v
-    E_m, E_v, E_th = step_error_bounds(orc_prev.theta, m_prev, v_prev, G, inv=inv, C=c64, do_clip=clip,
+    th_prev = widen_fp16(orc_prev.theta) if t16 else orc_prev.theta
+    if G.dtype == np.uint16:
+        G = widen_bf16(G)
+    E_m, E_v, E_th = step_error_bounds(th_prev, m_prev, v_prev, G, inv=inv, C=c64, do_clip=clip,
                                        lr=lr, wd=wd, t=t, mode=mode)
     if sbf16:
         for key in ("m", "v"):
@@ -95,16 +111,23 @@ def compare_tensor(tag, gpu, orc_new, orc_prev, G, *, inv, clip, C, c64, lr, wd,
         check_within(f"{tag} v", gpu["v"], orc_new.v, E_v)
         eq_mv = int(np.sum(gpu["m"].view(np.uint32) == orc_new.m.view(np.uint32)))
         eq_mv += int(np.sum(gpu["v"].view(np.uint32) == orc_new.v.view(np.uint32)))
-    check_within(f"{tag} theta", gpu["theta"], orc_new.theta, E_th)
     n = gpu["theta"].size
-    eq = int(np.sum(gpu["theta"].view(np.uint32) == orc_new.theta.view(np.uint32))) + eq_mv
+    if t16:
+        # fp16 master: within one fp16 ulp of the oracle's stored master
+        d = np.abs(ordered16(gpu["theta"]) - ordered16(orc_new.theta))
+        assert np.all(d <= 1), f"{tag} theta: fp16 master more than 1 ulp from the oracle"
+        eq = int(np.sum(gpu["theta"] == orc_new.theta)) + eq_mv
+    else:
+        check_within(f"{tag} theta", gpu["theta"], orc_new.theta, E_th)
+        eq = int(np.sum(gpu["theta"].view(np.uint32) == orc_new.theta.view(np.uint32))) + eq_mv
     stats["bit_equal"] = stats.get("bit_equal", 0) + eq
     stats["compared"] = stats.get("compared", 0) + 3 * n
     if bf16 or fp16:
         p = gpu["p"]
         # the write-back of the GPU's own master is bit-exact (the pages' invariant)
-        want = fp16_of(gpu["theta"]) if fp16 else bf16_of(gpu["theta"])
-        isnan = np.isnan(gpu["theta"])
+        th = widen_fp16(gpu["theta"]) if t16 else gpu["theta"]
+        want = fp16_of(th) if fp16 else bf16_of(th)
+        isnan = np.isnan(th)
         assert np.array_equal(p[~isnan], want[~isnan]), f"{tag}: param != 16-bit(master)"
         # and within one ulp of the oracle's param
         d = np.abs(p.astype(np.int32) - orc_new.p.astype(np.int32))

@@ -80,9 +80,20 @@ def test_validation_happens_before_any_device_call(H):
     st, msg = _flat(H, -1, 0, [0] * 5)
     assert st == H.HPO_EINVAL and "negative" in msg
     # unsupported dtypes: an error, never a silent cast
-    for code in (3, 0x200, 0x101 | 0x1000, -1):
+    for code in (3, 0x800, 0x101 | 0x1000, -1):
         st, msg = _flat(H, 16, code, [0x1000] * 5)
         assert st == H.HPO_EDTYPE and "not supported" in msg, code
+    # an fp16 master only under bf16 params
+    for code in (0x401, 0x402, 0x501, 0x601):
+        st, msg = _flat(H, 16, code, [0x1000] * 5)
+        assert st == H.HPO_EDTYPE and "bf16 params" in msg, code
+    # 16-bit grads and masters need 2-byte alignment, fp32 ones 4-byte
+    st, msg = _flat(H, 16, 0x400, [0x1000, 0x1001, 0x2000, 0x3000, 0x4000])
+    assert st == H.HPO_EINVAL and "main_param must be 2-byte" in msg
+    st, msg = _flat(H, 16, 0x200, [0x1000, 0x1000, 0x2001, 0x3000, 0x4000])
+    assert st == H.HPO_EINVAL and "main_grad must be 2-byte" in msg
+    st, msg = _flat(H, 16, 0x400, [0x1000, 0x1000, 0x2002, 0x3000, 0x4000])
+    assert st == H.HPO_EINVAL and "main_grad must be 4-byte" in msg
     # bf16 moments need only 2-byte alignment; fp32 moments 4-byte
     st, msg = _flat(H, 16, 0, [0x1000, 0x2000, 0x3000, 0x4002, 0x5000])
     assert st == H.HPO_EINVAL and "exp_avg" in msg
@@ -226,8 +237,9 @@ def test_muon_set_validation(H):
     any device call."""
     st, msg = _muon(H, [(4, 8)], pdt=2)
     assert st == H.HPO_EDTYPE and "fp16" in msg
-    st, msg = _muon(H, [(4, 8)], pdt=0x100)
-    assert st == H.HPO_EDTYPE
+    for code in (0x100, 0x200, 0x400):
+        st, msg = _muon(H, [(4, 8)], pdt=code)
+        assert st == H.HPO_EDTYPE, code
     st, msg = _muon(H, [(4, -8)])
     assert st == H.HPO_EINVAL and "negative" in msg
     st, msg = _muon(H, [(4, 8)], groups=[16])
@@ -297,6 +309,20 @@ def test_binding_rejects_mixed_param_dtypes_and_devices(H):
         H._check_params([None], [m, torch.zeros(4, dtype=torch.float32, device="meta")])
     with pytest.raises(ValueError, match="device tensor"):
         H._check_params([a], [a.new_zeros(4, dtype=torch.float32)])
+
+
+def test_binding_storage_flags(H):
+    """The binding reads each array kind's storage from its tensors' dtype
+    and refuses sets that mix dtypes within a kind."""
+    f32, bf, fp = (torch.zeros(4, dtype=d) for d in (torch.float32, torch.bfloat16, torch.float16))
+    assert H._storage_flags([f32], [f32], [f32], [f32]) == (0, torch.float32, torch.float32, torch.float32)
+    fl = H._storage_flags([fp], [bf], [bf], [bf])
+    assert fl == (H.HPO_MASTER_FP16 | H.HPO_GRAD_BF16 | H.HPO_STATE_BF16, torch.float16, torch.bfloat16,
+                  torch.bfloat16)
+    with pytest.raises(TypeError, match="main_grad tensors must all be"):
+        H._storage_flags([f32, f32], [f32, bf], [f32] * 2, [f32] * 2)
+    with pytest.raises(TypeError, match="main_param tensors must all be"):
+        H._storage_flags([bf], [f32], [f32], [f32])
 
 
 def test_binding_refuses_host_tensors_as_device_buffers(H):

@@ -18,8 +18,8 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_update_bytes_per_element():
-    """Fused update: grad and master read, master written (12 B), both moments
-    read and written at their width, the 16-bit param written."""
+    """Fused update: grad read, master read and written, both moments read and
+    written, all at their widths, and the 16-bit param written."""
     import bench
 
     class W:
@@ -29,7 +29,14 @@ def test_update_bytes_per_element():
     assert bench.update_bytes(W) == 22
     W.state_dtype, W.param_dtype = "fp32", "fp32"
     assert bench.update_bytes(W) == 28
-    assert bench.GRADPASS_BYTES == 4
+    assert bench.gradpass_bytes(W) == 4
+    # bf16 main grads (2 B read) and an fp16 master (2 B read, 2 B written)
+    W.param_dtype, W.grad_dtype = "bf16", "bf16"
+    assert bench.update_bytes(W) == 28 and bench.gradpass_bytes(W) == 2
+    W.master_dtype = "fp16"
+    assert bench.update_bytes(W) == 24
+    W.state_dtype = "bf16"
+    assert bench.update_bytes(W) == 16
 
 
 def test_spread_of_kernel_times():

@@ -41,16 +41,18 @@ def _true_grads(k, rng_seed=500):
     return gs
 
 
-@pytest.mark.parametrize("mode,pdt", [(0, "bf16"), (1, "bf16"), (0, "fp16")])
-def test_device_step_sequence_matches_oracle(H, orc, mode, pdt):
-    banner(f"device-resident step sequence, mode {mode}, {pdt} params")
+@pytest.mark.parametrize("mode,pdt,lowp", [(0, "bf16", False), (1, "bf16", False), (0, "fp16", False),
+                                           (1, "bf16", True)])
+def test_device_step_sequence_matches_oracle(H, orc, mode, pdt, lowp):
+    """lowp: bf16 main grads and an fp16 master under the bf16 params."""
+    banner(f"device-resident step sequence, mode {mode}, {pdt} params, bf16 grads + fp16 master {lowp}")
     from mixed_precision_optimizer_amd import DeviceAdamW
     rng = np.random.default_rng(400)
     th0 = [rng.standard_normal(n).astype(np.float32) for n in SIZES]
-    ths = [torch.from_numpy(a.copy()).to(DEV) for a in th0]
+    ths = [torch.from_numpy(a.copy()).to(DEV).to(torch.float16 if lowp else torch.float32) for a in th0]
     tdt = torch.float16 if pdt == "fp16" else torch.bfloat16
     ps = [t.to(tdt) for t in ths]
-    gs = [torch.zeros(n, device=DEV) for n in SIZES]
+    gs = [torch.zeros(n, device=DEV, dtype=torch.bfloat16 if lowp else torch.float32) for n in SIZES]
     ms = [torch.zeros(n, device=DEV) for n in SIZES]
     vs = [torch.zeros(n, device=DEV) for n in SIZES]
     hset = H.hpo_set_create_list(ps, ths, gs, ms, vs, GROUPS)
@@ -58,8 +60,8 @@ def test_device_step_sequence_matches_oracle(H, orc, mode, pdt):
     kw = dict(loss_scale=2.0 ** 16, dynamic=True, growth_interval=5, hysteresis=2, min_scale=1.0,
               grad_norm_skip_threshold=50.0)
     opt = DeviceAdamW(hset, groups, mode=mode, max_norm=1.0, **kw)
-    T = [orc.OTensor(a.copy(), np.zeros_like(a), np.zeros_like(a), p.view(torch.int16).cpu().numpy().view(np.uint16).copy(), g,
-                     pdt == "fp16") for a, p, g in zip(th0, ps, GROUPS)]
+    T = [orc.OTensor(to_np(t), np.zeros_like(a), np.zeros_like(a), to_np(p), g, pdt == "fp16", lowp)
+         for a, t, p, g in zip(th0, ths, ps, GROUPS)]
     O = orc.OracleOptimizer(T, orc.Hyper(mode=mode), groups, max_norm=1.0)
     sc = orc.LossScaler(scale=2.0 ** 16, dynamic=True, growth_interval=5, hysteresis=2, min_scale=1.0)
     applied = skipped = 0
@@ -72,9 +74,14 @@ def test_device_step_sequence_matches_oracle(H, orc, mode, pdt):
             g.mul_(opt.loss_scale_tensor)
         if k in INF_STEPS:
             gs[2][-1] = float("inf")
-        stored = [(t * sc.scale).astype(np.float32) for t in true]
-        if k in INF_STEPS:
-            stored[2][-1] = np.inf
+        if lowp:   # the bf16 image of the true grads, times the power-of-two scale (exact)
+            stored = [to_np(torch.from_numpy(t).to(torch.bfloat16).mul_(sc.scale)) for t in true]
+            if k in INF_STEPS:
+                stored[2][-1] = 0x7F80
+        else:
+            stored = [(t * sc.scale).astype(np.float32) for t in true]
+            if k in INF_STEPS:
+                stored[2][-1] = np.inf
         r = O.step_scaled(stored, sc, skip_threshold=50.0)
         applied += int(r.applied)
         skipped += int(not r.applied)
@@ -89,7 +96,7 @@ def test_device_step_sequence_matches_oracle(H, orc, mode, pdt):
             if r.norm32 is not None:
                 assert st.grad_norm == r.norm32 or abs(st.grad_norm - r.norm64) <= 1e-5 * r.norm64
             for i in range(len(SIZES)):
-                assert np.array_equal(to_np(ths[i]).view(np.uint32), T[i].theta.view(np.uint32)), (k, i)
+                assert np.array_equal(to_np(ths[i]).view(np.uint8), T[i].theta.view(np.uint8)), (k, i)
                 assert np.array_equal(to_np(ms[i]).view(np.uint32), T[i].m.view(np.uint32)), (k, i)
                 assert np.array_equal(to_np(vs[i]).view(np.uint32), T[i].v.view(np.uint32)), (k, i)
                 assert np.array_equal(to_np(ps[i]), T[i].p), (k, i)

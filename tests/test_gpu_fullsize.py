@@ -135,13 +135,15 @@ def _run_fullsize(H, orc, w, picks_kw, steps=None, device_step=False):
     bf16 = w.param_dtype == "bf16"
     fp16 = w.param_dtype == "fp16"
     has_p = bf16 or fp16
+    t16 = w.master_dtype == "fp16"
     Ts = []
     lr_e = np.empty(S.n)
     wd_e = np.empty(S.n)
     for i, pos, n in S.seg:
         sl = slice(pos, pos + n)
         g = w.group_of(i)
-        Ts.append(orc.OTensor(big["theta"][sl], big["m"][sl], big["v"][sl], big["p"][sl] if has_p else None, g, fp16))
+        Ts.append(orc.OTensor(big["theta"][sl], big["m"][sl], big["v"][sl], big["p"][sl] if has_p else None, g, fp16,
+                              t16))
         lr_e[sl], wd_e[sl] = w.groups()[g]
     hset = make_set(bufs)
     opt = _DeviceStep(hset, w) if device_step else make_opt(hset, w)
@@ -174,11 +176,11 @@ def _run_fullsize(H, orc, w, picks_kw, steps=None, device_step=False):
         assert abs(norm - norm64) <= 1e-5 * norm64
         do_clip, C, c64 = orc.clip_coeff(w.max_norm, norm32)
         prev = orc.OTensor(big["theta"].copy(), big["m"].copy(), big["v"].copy(),
-                           big["p"].copy() if has_p else None, 0, fp16)
+                           big["p"].copy() if has_p else None, 0, fp16, t16)
         orc.apply_update(Ts, [Gs[pos:pos + n] for _, pos, n in S.seg], hyper, w.groups(), t_orc, inv,
                          do_clip, C, c64)
         assert opt.t == t_orc
-        now = orc.OTensor(big["theta"], big["m"], big["v"], big["p"] if has_p else None, 0, fp16)
+        now = orc.OTensor(big["theta"], big["m"], big["v"], big["p"] if has_p else None, 0, fp16, t16)
         compare_tensor(f"{w.name} step {k}", st, now, prev, Gs, inv=inv, clip=do_clip, C=C, c64=c64,
                        lr=lr_e, wd=wd_e, t=t_orc, mode=w.mode, bf16=bf16, fp16=fp16, stats=stats)
     banner(f"bit-equal {stats.get('bit_equal', 0)}/{stats.get('compared', 0)}; skipped {stats.get('skipped', [])}")
@@ -249,6 +251,19 @@ def test_zero_shard_bf16_moments(H, orc):
     element per update instead of 30), 3 steps."""
     from mixed_precision_optimizer_amd import inputs
     w = inputs.zero_shard(state_dtype="bf16")
+    stats = _run_fullsize(H, orc, w, dict(head=4096, windows_big=64, window=65536))
+    assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.timeout(900)
+def test_zero_shard_bf16_grads_fp16_master(H, orc):
+    """The 70B/8 flat shard with bf16 main grads and an fp16 master under the
+    bf16 params (the update moves 24 bytes per element instead of 30), 3
+    steps: the norm over all 8.75e9 widened grads, the sampled state within
+    one fp16 ulp (bit-equal in practice), every param the bf16 rounding of
+    its stored master."""
+    from mixed_precision_optimizer_amd import inputs
+    w = inputs.zero_shard(grad_dtype="bf16", master_dtype="fp16")
     stats = _run_fullsize(H, orc, w, dict(head=4096, windows_big=64, window=65536))
     assert stats["bit_equal"] == stats["compared"]
 

@@ -37,7 +37,8 @@ def _oracle_tensors(orc, bufs):
     out = []
     for i in range(w.n_tensors):
         st = read_state(bufs, i)
-        T = orc.OTensor(st["theta"], st["m"], st["v"], st.get("p"), w.group_of(i), w.param_dtype == "fp16")
+        T = orc.OTensor(st["theta"], st["m"], st["v"], st.get("p"), w.group_of(i), w.param_dtype == "fp16",
+                        w.master_dtype == "fp16")
         out.append(T)
     return out
 
@@ -115,13 +116,14 @@ def test_two_matrices_ten_steps(H, orc):
 
 
 def _edge_workload(mode, loss_scale, inf_step=None, max_norm=1.0, steps=4, param_dtype="bf16",
-                   state_dtype="fp32"):
+                   state_dtype="fp32", grad_dtype="fp32", master_dtype="fp32"):
     from mixed_precision_optimizer_amd.inputs import Workload
     sizes = [1, 3, 4, 5, 63, 64, 65, 255, 1023, 4095, 4096, 4097, 0, 12345, 70001, 131072, 300000, 2]
     ndims = [1 if n in (4095, 5, 63) else 2 for n in sizes]
     return Workload(f"edge_mode{mode}", sizes, ndims, lr=1e-3, weight_decay=0.1, mode=mode, max_norm=max_norm,
                     loss_scale=loss_scale, steps=steps, grad_std=[1e-3 * (1 + (i % 5)) for i in range(len(sizes))],
-                    inf_step=inf_step, param_dtype=param_dtype, state_dtype=state_dtype)
+                    inf_step=inf_step, param_dtype=param_dtype, state_dtype=state_dtype, grad_dtype=grad_dtype,
+                    master_dtype=master_dtype)
 
 
 @pytest.mark.parametrize("mode", [0, 1])
@@ -148,6 +150,60 @@ def test_reduced_precision_variants(H, orc, mode, pdt, sdt):
     stats, Ts, bufs = _run_parity(H, orc, w)
     assert stats["skipped"] == [3]
     assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("gdt,tdt,sdt", [("bf16", "fp32", "fp32"), ("fp32", "fp16", "fp32"), ("bf16", "fp16", "fp32"),
+                                         ("bf16", "fp16", "bf16")])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_lower_precision_grads_and_master(H, orc, mode, gdt, tdt, sdt, inplace):
+    """bf16 main grads and an fp16 master under bf16 params, alone and
+    together with bf16 moments, on the ragged edge sets (loss scale 1024,
+    clipping, a no-decay group, a skipped step), with the fused and the
+    in-place unscale, against the oracle's own trajectory."""
+    banner(f"lower precision: grads {gdt}, master {tdt}, moments {sdt}, mode {mode}, inplace {inplace}")
+    w = _edge_workload(mode, 1024.0, inf_step=3, steps=6, state_dtype=sdt, grad_dtype=gdt, master_dtype=tdt)
+    stats, Ts, bufs = _run_parity(H, orc, w, inplace=inplace)
+    assert stats["skipped"] == [3]
+    assert stats["bit_equal"] == stats["compared"]
+
+
+@pytest.mark.parametrize("grads", ["fp32", "bf16"])
+def test_inplace_unscale_against_oracle(H, orc, grads):
+    """hpo_unscale_check_inf over a ragged list (vector bodies, scalar tails,
+    a misaligned view) stores the oracle's unscaled grads bit for bit, for
+    inv_scale values that round (1/3) and that are exact (2^-13, 1), with
+    fp32 or bf16 grads; an inf anywhere sets the flag and is kept."""
+    banner(f"in-place unscale, {grads} grads")
+    gdt = torch.bfloat16 if grads == "bf16" else torch.float32
+    sizes = [1, 5, 4096, 70001, 3, 131075]
+    rng = np.random.default_rng(17)
+    for inv in (float(np.float32(1.0 / 3.0)), 2.0 ** -13, 1.0):
+        buf = torch.zeros(sum(sizes) + 8, dtype=gdt, device=DEV)
+        views, o = [], 1     # the first view starts one element in
+        for n in sizes:
+            views.append(buf[o:o + n])
+            o += n + 1
+        for k, v in enumerate(views):
+            v.copy_(torch.from_numpy((rng.standard_normal(v.numel()) * 3e4).astype(np.float32)))
+        views[3][777] = float("inf")
+        before = [to_np(v) for v in views]
+        ths = [torch.zeros(v.numel(), device=DEV) for v in views]
+        ms = [torch.zeros(v.numel(), device=DEV) for v in views]
+        vs = [torch.zeros(v.numel(), device=DEV) for v in views]
+        hset = H.hpo_set_create_list(None, ths, views, ms, vs)
+        flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+        H.hpo_unscale_check_inf(hset, inv, flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 1
+        for G0, v in zip(before, views):
+            want = G0.copy()
+            if grads == "bf16":
+                orc.unscale_inplace_bf16(want, inv)
+            else:
+                orc.unscale_inplace(want, inv)
+            assert np.array_equal(to_np(v).view(np.uint8), want.view(np.uint8))
+        hset.close()
 
 
 def test_fp16_writeback_exhaustive(H, orc):
@@ -353,25 +409,31 @@ def test_flat_and_list_sets_agree_bitwise(H):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
-@pytest.mark.parametrize("moments,param", [("fp32", "bf16"), ("bf16", "bf16"), ("bf16", "fp16")])
-def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param):
+@pytest.mark.parametrize("moments,param,grads,master", [("fp32", "bf16", "fp32", "fp32"), ("bf16", "bf16", "fp32", "fp32"),
+                                                        ("bf16", "fp16", "fp32", "fp32"), ("fp32", "bf16", "bf16", "fp32"),
+                                                        ("fp32", "bf16", "fp32", "fp16"), ("bf16", "bf16", "bf16", "fp16")])
+def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param, grads, master):
     """Views that start 1..3 elements into their buffers, as a list set and
     as a flat set: when all five pointers share the element offset (for
     16-bit moments and params, the offset within their own 4-element lines),
     the head is peeled and the body vectorized; when they do not, the whole
     tensor runs element by element.  Every layout and kind gives the same
-    bits, and the oracle's, for fp32 or bf16 moments and bf16 or fp16 params."""
-    banner(f"misaligned, {moments} moments, {param} params")
+    bits, and the oracle's, for fp32 or bf16 moments, bf16 or fp16 params,
+    fp32 or bf16 grads and an fp32 or fp16 master."""
+    banner(f"misaligned, {moments} moments, {param} params, {grads} grads, {master} master")
     n = 50_001
     rng = np.random.default_rng(6)
     th0 = rng.standard_normal(n).astype(np.float32)
     G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
     mdt = torch.bfloat16 if moments == "bf16" else torch.float32
     pdt = torch.float16 if param == "fp16" else torch.bfloat16
+    tdt = torch.float16 if master == "fp16" else torch.float32
+    gdt = torch.bfloat16 if grads == "bf16" else torch.float32
     res = []
     layouts = [(0, 0), (1, 1), (2, 2), (3, 3), (1, 2), (0, 3)]  # (shift of master/m/v/param, shift of grad)
     for (shift, gshift), kind in [(lay, kind) for lay in layouts for kind in ("list", "flat")]:
-        tb, gb = (torch.zeros(n + 4, device=DEV) for _ in range(2))
+        tb = torch.zeros(n + 4, dtype=tdt, device=DEV)
+        gb = torch.zeros(n + 4, dtype=gdt, device=DEV)
         mb, vb = (torch.zeros(n + 4, dtype=mdt, device=DEV) for _ in range(2))
         pb = torch.zeros(n + 4, dtype=pdt, device=DEV)
         th, m, v, p = (b[shift:shift + n] for b in (tb, mb, vb, pb))
@@ -389,12 +451,14 @@ def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param):
         H.hpo_adamw_step(hset, H.make_cfg(mode=1), [(1e-3, 0.1)], None, 1, 1.0, 1.0, norm, None)
         torch.cuda.synchronize()
         res.append((to_np(th), to_np(m), to_np(v), to_np(p)))
+        G_stored = to_np(g)     # bf16 grads: the patterns the set read
         hset.close()
     for r in res[1:]:
         for a, b in zip(res[0], r):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
-    T = orc.OTensor.fresh(th0, fp16_param=param == "fp16", state_bf16=moments == "bf16")
-    orc.OracleOptimizer([T], orc.Hyper(mode=1), [(1e-3, 0.1)], max_norm=1.0).step([G])
+    T = orc.OTensor.fresh(th0, fp16_param=param == "fp16", state_bf16=moments == "bf16",
+                          fp16_master=master == "fp16")
+    orc.OracleOptimizer([T], orc.Hyper(mode=1), [(1e-3, 0.1)], max_norm=1.0).step([G_stored])
     for got, want in zip(res[0], (T.theta, T.m, T.v, T.p)):
         assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
 
