@@ -52,7 +52,13 @@ def update_bytes(w) -> int:
     return gradpass_bytes(w) + 2 * mst + 4 * mom + par
 
 
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_hbm_traffic_zero_shard_70b_over_8.txt")
+def pmc_summary_path(workload_name):
+    """The committed counter summary of a flat-shard workload: the default
+    storage has pmc_hbm_traffic_zero_shard_70b_over_8.txt, and each other
+    storage the same name with its tag (for example
+    ..._bf16_grads_fp16_master.txt)."""
+    return os.path.join(ROOT, "profiles", "pmc_hbm_traffic_" + workload_name.replace("zero1_shard", "zero_shard", 1)
+                        + ".txt")
 # the sources of the AdamW-path kernels (the counters in profiles/ name this digest)
 KERNEL_SOURCES = ("mixed_precision_optimizer_amd/csrc/hpo_kernels.hip", "mixed_precision_optimizer_amd/csrc/hpo_impl.h",
                   "mixed_precision_optimizer_amd/csrc/hpo_device.h")
@@ -73,10 +79,13 @@ def measured_traffic(workload_name, numel):
     """HBM bytes per launch of the update kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary, or None when that summary was taken on
     another workload or on kernels that have changed since."""
-    if workload_name != "zero1_shard_70b_over_8" or numel != 8_750_000_000 or not os.path.exists(PMC_SUMMARY):
+    if not workload_name.startswith("zero1_shard_70b_over_8") or numel != 8_750_000_000:
+        return None
+    path = pmc_summary_path(workload_name)
+    if not os.path.exists(path):
         return None
     digest, traffic = None, None
-    with open(PMC_SUMMARY) as f:
+    with open(path) as f:
         for line in f:
             if "kernel source digest" in line:
                 digest = line.rsplit(":", 1)[1].strip()

@@ -72,6 +72,7 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 ld_stream(const float4* p)
 {
@@ -90,6 +91,26 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* p)
     return make_uint2(v.x, v.y);
 #else
     return *p;
+#endif
+}
+
+__device__ __forceinline__ uint4 ld_stream(const uint4* p)
+{
+#if HPO_NT_LOADS
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void st_stream(uint4* p, uint4 v)
+{
+#if HPO_NT_STORES
+    u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+#else
+    *p = v;
 #endif
 }
 
@@ -257,6 +278,29 @@ __device__ __forceinline__ void st1(void* base, int64_t e, float x)
         static_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(narrow16<S>(x));
 }
 
+/* 8 consecutive 16-bit elements at 8-element index i: one 16-byte access. */
+template <int S>
+__device__ __forceinline__ void ld8(const void* base, int64_t i, float (&x)[8])
+{
+    const uint4 w = ld_stream(static_cast<const uint4*>(base) + i);
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x[2 * j] = widen16<S>(q[j] & 0xFFFFu);
+        x[2 * j + 1] = widen16<S>(q[j] >> 16);
+    }
+}
+
+template <int S>
+__device__ __forceinline__ void st8(void* base, int64_t i, const float (&x)[8])
+{
+    uint32_t q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        q[j] = narrow16<S>(x[2 * j]) | (narrow16<S>(x[2 * j + 1]) << 16);
+    st_stream(static_cast<uint4*>(base) + i, make_uint4(q[0], q[1], q[2], q[3]));
+}
+
 /* Element `start` of an array of S elements. */
 template <int S>
 __device__ __forceinline__ void* at(void* base, int64_t start)
@@ -279,13 +323,47 @@ __device__ __forceinline__ void grad_elem(float& G, float inv, double& acc, int&
     }
 }
 
+/* The body of a 16-bit grad range whose start is 16-byte aligned: 8
+ * elements per lane access, so that each access moves as many bytes as an
+ * fp32 one.  Returns the elements it covered. */
+template <GradPass PASS, int GDT>
+__device__ __forceinline__ int64_t grad_body16(void* __restrict__ G, int64_t len, float inv, double& acc, int& bad)
+{
+    constexpr int U = HPO_GRAD_UNROLL;
+    const int tid = threadIdx.x;
+    const int64_t nv = len / 8;
+    for (int64_t base = tid; base < nv; base += kGradBlock * U) {
+        float x[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + static_cast<int64_t>(u) * kGradBlock;
+            if (i < nv)
+                ld8<GDT>(G, i, x[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + static_cast<int64_t>(u) * kGradBlock;
+            if (i < nv) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    grad_elem<PASS>(x[u][j], inv, acc, bad);
+                if constexpr (PASS == GradPass::kUnscale)
+                    st8<GDT>(G, i, x[u]);
+            }
+        }
+    }
+    return nv * 8;
+}
+
 template <GradPass PASS, int GDT>
 __device__ __forceinline__ void grad_range(const Range& r, float inv, double& acc, int& bad)
 {
     void* __restrict__ G = at<GDT>(r.d.grad, r.start);
     const int tid = threadIdx.x;
     int64_t done = 0;
-    if (r.d.vec_ok) {
+    if (GDT != kF32 && r.d.vec_ok && reinterpret_cast<uintptr_t>(G) % 16 == 0) {
+        done = grad_body16<PASS, GDT>(G, r.len, inv, acc, bad);
+    } else if (r.d.vec_ok) {
         constexpr int U = HPO_GRAD_UNROLL;
         const int64_t nv = r.len / kVec;
         for (int64_t base = tid; base < nv; base += kGradBlock * U) {
