@@ -231,6 +231,34 @@ def test_fp16_writeback_exhaustive(H, orc):
     hset.close()
 
 
+def test_fp16_master_copy_exhaustive(H, orc):
+    """hpo_copy_main_to_model on a set with an fp16 master and bf16 params,
+    over all 65536 fp16 master patterns, with aligned arrays (vector path)
+    and with views one element in (three elements on the element path, the
+    rest vectorized): each param is the oracle's bf16 RNE of the widened
+    master, NaN staying NaN."""
+    banner("exhaustive fp16-master copy")
+    n = 1 << 16
+    pats = torch.arange(n, dtype=torch.int32).to(torch.int16)
+    want = orc.bf16_rne(orc.widen_fp16(pats.numpy().view(np.uint16)))
+    nan = (pats.numpy().view(np.uint16) & 0x7FFF) > 0x7C00
+    for shift in (0, 1):
+        master = torch.zeros(n + 4, dtype=torch.float16, device=DEV)
+        grad = torch.zeros(n + 4, dtype=torch.float32, device=DEV)
+        m, v = (torch.zeros(n + 4, dtype=torch.float32, device=DEV) for _ in range(2))
+        param = torch.zeros(n + 4, dtype=torch.bfloat16, device=DEV)
+        t, g, mm, vv, p = (b[shift:shift + n] for b in (master, grad, m, v, param))
+        t.view(torch.int16).copy_(pats.to(DEV))
+        hset = H.hpo_set_create_list([p], [t], [g], [mm], [vv])
+        assert hset.info().n_vector == 1   # every array shares the shift: peeled head + vector body
+        H.hpo_copy_main_to_model(hset)
+        torch.cuda.synchronize()
+        got = to_np(p)
+        assert np.array_equal(got[~nan], want[~nan]), shift
+        assert np.all((got[nan] & 0x7FFF) > 0x7F80)
+        hset.close()
+
+
 @pytest.mark.parametrize("bad", [float("inf"), float("-inf"), float("nan")])
 @pytest.mark.parametrize("where", ["head", "middle", "tail"])
 def test_nonfinite_anywhere_skips(H, orc, bad, where):
