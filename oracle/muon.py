@@ -65,7 +65,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (ADAMW, Hyper, OTensor, StepResult, any_nonfinite, apply_update, bf16_rne, clip_coeff,
+from . import (ADAMW, Hyper, OTensor, StepResult, any_nonfinite, apply_update, bf16_rne, clip_coeff, grad_f32,
                norm_from_sumsq, sumsq)
 
 # (a, b, c) of the quintic the pages print (the original single set)
@@ -279,6 +279,7 @@ class ChainedOracle:
     def step(self, adam_grads: Sequence[np.ndarray], muon_grads: Sequence[np.ndarray],
              inv_scale: float = 1.0) -> StepResult:
         inv32 = float(F32(inv_scale))
+        adam_grads = [grad_f32(G) for G in adam_grads]   # bf16 AdamW grads are read as their fp32 values
         allg = list(adam_grads) + list(muon_grads)
         if any(G.size and any_nonfinite(np.ascontiguousarray(G, dtype=F32).ravel()) for G in allg):
             return StepResult(False, True, None, None)

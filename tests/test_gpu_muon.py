@@ -297,12 +297,14 @@ def test_muon_rejects_adam_calls_and_vice_versa(H, mu, I):
 # ---------------------------------------------------------------------------
 # The chain: AdamW + Muon, device-resident, with the loss scaler
 # ---------------------------------------------------------------------------
-def test_chained_device_step(H, mu, I):
+@pytest.mark.parametrize("lowp", [False, True])
+def test_chained_device_step(H, mu, I, lowp):
     """AdamW tensors (an embedding-like matrix and norm gains) and Muon
     matrices stepped by hpo_step_device_chain with a dynamic loss scaler:
     one norm over both, one skip, one counter.  AdamW state is bit-exact; the
-    Muon momentum is bit-exact; masters within the NS bound."""
-    banner("chained AdamW + Muon device step")
+    Muon momentum is bit-exact; masters within the NS bound.  lowp: the AdamW
+    set keeps bf16 main grads and an fp16 master."""
+    banner(f"chained AdamW + Muon device step, AdamW bf16 grads + fp16 master {lowp}")
     import oracle
     dev = torch.device("cuda")
     adam_shapes = [(3000,), (256,), (64 * 50,)]
@@ -310,16 +312,18 @@ def test_chained_device_step(H, mu, I):
     aidx = [0, 0, 1]
     A0 = [I.seeded_matrix(s, 500 + i, 0.02).ravel() for i, s in enumerate(adam_shapes)]
     am = [torch.from_numpy(a.copy()).to(dev) for a in A0]
+    if lowp:
+        am = [t.half() for t in am]
     ap = [t.to(torch.bfloat16) for t in am]
-    ag = [torch.zeros_like(t) for t in am]
-    a1 = [torch.zeros_like(t) for t in am]
-    a2 = [torch.zeros_like(t) for t in am]
+    ag = [torch.zeros(t.numel(), dtype=torch.bfloat16 if lowp else torch.float32, device=dev) for t in am]
+    a1 = [torch.zeros(t.numel(), device=dev) for t in am]
+    a2 = [torch.zeros(t.numel(), device=dev) for t in am]
     aset = H.hpo_set_create_list(ap, am, ag, a1, a2, aidx)
     shapes = [(128, 384), (384, 128), (300, 700), (37, 129)]
     case = MuonCase(H, mu, I, shapes, groups=[0, 1, 0, 1])
     mgroups = [(0.02, 0.1), (0.01, 0.0)]
     cfg_o = mu.MuonCfg()
-    chain = mu.ChainedOracle([oracle.OTensor.fresh(a, group=g) for a, g in zip(A0, aidx)], oracle.Hyper(),
+    chain = mu.ChainedOracle([oracle.OTensor.fresh(a, group=g, fp16_master=lowp) for a, g in zip(A0, aidx)], oracle.Hyper(),
                              groups, case.orc, cfg_o, mgroups, max_norm=1.0)
     scaler = oracle.LossScaler(scale=2.0 ** 16, growth_interval=3, hysteresis=1)
     d_state = H.new_scaler_state(dev)
@@ -336,13 +340,16 @@ def test_chained_device_step(H, mu, I):
             gm[1][3, 3] = np.inf
         for t, g in zip(ag, ga):
             t.copy_(torch.from_numpy(g))
+        if lowp:     # the oracle reads the bf16 patterns the set holds
+            ga = [to_np(t) for t in ag]
         case.set_grads(gm)
         st_before = H.read_scaler_state(d_state)
         H.hpo_step_device_chain(aset, acfg, groups, case.set, mcfg, mgroups, 1.0, scfg, d_state,
                                 st_before.applied_steps + 1, 1)
         torch.cuda.synchronize()
         inv = scaler.inv_scale()
-        found = any(not np.all(np.isfinite(g)) for g in ga + gm)
+        found = any(not np.all(np.isfinite(g)) for g in gm) or any(
+            not np.all(np.isfinite(oracle.grad_f32(g))) for g in ga)
         scaler.update(found)
         r = chain.step(ga, gm, inv)
         assert r.found_inf == found
@@ -355,7 +362,7 @@ def test_chained_device_step(H, mu, I):
             assert st.grad_norm == r.norm32, (k, st.grad_norm, r.norm32)
             _grow_bounds(case, mu, cfg_o, mgroups, chain.last)
         for i, T in enumerate(chain.adam):
-            assert np.array_equal(to_np(am[i]).view(np.uint32), T.theta.view(np.uint32)), f"step {k} adam {i}"
+            assert np.array_equal(to_np(am[i]).view(np.uint8), T.theta.view(np.uint8)), f"step {k} adam {i}"
             assert np.array_equal(to_np(a1[i]).view(np.uint32), T.m.view(np.uint32))
             assert np.array_equal(to_np(a2[i]).view(np.uint32), T.v.view(np.uint32))
             assert np.array_equal(to_np(ap[i]), T.p)
