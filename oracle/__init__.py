@@ -18,7 +18,7 @@ orders the steps of one optimizer step the way the pages order them:
     §9.2   the master is then written back to the 16-bit model params.
   [FP32-RFC] "支持FP32优化器" §7.2: fp32 params are their own master.
   [OPT-INFRA] §16: the precision-aware optimizer may keep exp_avg /
-           exp_avg_sq, the main grads and the master below fp32: bf16
+           exp_avg_sq, the main grads and the master below fp32: bf16 or fp16
            moments and bf16 grads are widened exactly on read; an fp16 master
            under bf16 params is widened, updated in fp32 and stored with the
            fp16 RNE, and the param is the bf16 RNE of the stored master.
@@ -250,32 +250,34 @@ class OTensor:
     group: int = 0
     param_fp16: bool = False          # p holds fp16 bits instead of bf16
     master_fp16: bool = False         # theta holds fp16 bits (uint16) under bf16 params
+    moments_fp16: bool = False        # m and v hold fp16 bits (uint16) instead of bf16
 
     @property
     def state_bf16(self) -> bool:
-        return self.m.dtype == np.uint16
+        return self.m.dtype == np.uint16 and not self.moments_fp16
 
     @staticmethod
     def fresh(theta: np.ndarray, bf16_param: bool = True, group: int = 0, fp16_param: bool = False,
-              state_bf16: bool = False, fp16_master: bool = False) -> "OTensor":
+              state_bf16: bool = False, fp16_master: bool = False, fp16_moments: bool = False) -> "OTensor":
         theta = np.ascontiguousarray(theta, dtype=np.float32).copy()
-        sdt = np.uint16 if state_bf16 else np.float32
+        sdt = np.uint16 if (state_bf16 or fp16_moments) else np.float32
         if fp16_master:
             # the master is the fp16 image of the draw; the bf16 param that of the master
             assert bf16_param and not fp16_param
             t16 = fp16_rne(theta)
             return OTensor(t16, np.zeros(theta.shape, sdt), np.zeros(theta.shape, sdt),
-                           bf16_rne(widen_fp16(t16)), group, False, True)
+                           bf16_rne(widen_fp16(t16)), group, False, True, fp16_moments)
         if fp16_param:
             p = fp16_rne(theta)
         else:
             p = bf16_rne(theta) if bf16_param else None
-        return OTensor(theta, np.zeros(theta.shape, sdt), np.zeros(theta.shape, sdt), p, group, fp16_param)
+        return OTensor(theta, np.zeros(theta.shape, sdt), np.zeros(theta.shape, sdt), p, group, fp16_param,
+                       False, fp16_moments)
 
     def copy(self) -> "OTensor":
         return OTensor(self.theta.copy(), self.m.copy(), self.v.copy(),
                        None if self.p is None else self.p.copy(), self.group, self.param_fp16,
-                       self.master_fp16)
+                       self.master_fp16, self.moments_fp16)
 
 
 @dataclass
@@ -332,7 +334,9 @@ def apply_update(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper:
     be kept below fp32): bf16 grads are widened exactly; an fp16 master is
     widened exactly, updated in fp32 like an fp32 master, stored back with the
     fp16 RNE, and the bf16 param is the bf16 RNE of that stored master (the
-    param is a copy of the master, [OPT-INFRA] §9.2)."""
+    param is a copy of the master, [OPT-INFRA] §9.2).  fp16 moments likewise:
+    widened exactly, updated in fp32, stored with the fp16 RNE (subnormals
+    kept; a v below half the smallest subnormal becomes 0)."""
     L = lib()
     fn = L.orc_update_f32 if variant == "f32" else L.orc_update_f64
     for T, G in zip(tensors, grads):
@@ -348,15 +352,27 @@ def apply_update(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper:
             assert variant == "f32", "bf16 moments are defined for the fp32-literal reading only"
             assert T.m.flags["C_CONTIGUOUS"] and T.v.flags["C_CONTIGUOUS"]
             mp, vp = _ptr(T.m), _ptr(T.v)
-        else:
+        elif not T.moments_fp16:
             mp, vp = _ptr(_f32(T.m)), _ptr(_f32(T.v))
-        if T.master_fp16:
-            assert variant == "f32", "an fp16 master is defined for the fp32-literal reading only"
-            assert T.p is not None and not T.param_fp16 and T.theta.dtype == np.uint16
-            th = widen_fp16(T.theta).copy()
-            fn(th.size, _ptr(th), mp, vp, _ptr(_f32(G)), None, ctypes.byref(args))
-            T.theta[...] = fp16_rne(th)
-            T.p[...] = bf16_rne(widen_fp16(T.theta))
+        if T.master_fp16 or T.moments_fp16:
+            assert variant == "f32", "fp16 storage is defined for the fp32-literal reading only"
+            if T.moments_fp16:
+                assert T.m.dtype == np.uint16 and T.v.dtype == np.uint16
+                m32, v32 = widen_fp16(T.m).copy(), widen_fp16(T.v).copy()
+                args.state_bf16 = 0
+                mp, vp = _ptr(m32), _ptr(v32)
+            if T.master_fp16:
+                assert T.p is not None and not T.param_fp16 and T.theta.dtype == np.uint16
+                th = widen_fp16(T.theta).copy()
+            else:
+                th = _f32(T.theta)
+            fn(th.size, _ptr(th), mp, vp, _ptr(_f32(G)), None if T.master_fp16 else _ptr(T.p), ctypes.byref(args))
+            if T.moments_fp16:
+                T.m[...] = fp16_rne(m32)
+                T.v[...] = fp16_rne(v32)
+            if T.master_fp16:
+                T.theta[...] = fp16_rne(th)
+                T.p[...] = bf16_rne(widen_fp16(T.theta))
             continue
         fn(T.theta.size, _ptr(_f32(T.theta)), mp, vp,
            _ptr(_f32(np.ascontiguousarray(G))), _ptr(T.p), ctypes.byref(args))

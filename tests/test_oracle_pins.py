@@ -685,3 +685,41 @@ def test_bf16_unscale_inplace_matches_torch(orc):
         orc.unscale_inplace_bf16(bits, float(np.float32(inv)))
         ref = x.clone().mul_(float(np.float32(inv)))
         assert np.array_equal(bits, _torch_bits(ref))
+
+
+@pytest.mark.parametrize("mode", [ADAMW, ADAM_L2])
+def test_fp16_moments_are_the_fp32_update_rounded(orc, mode):
+    """fp16 exp_avg / exp_avg_sq: one step equals the fp32-moment step from
+    the same (fp16-representable) moments, followed by torch's fp16 cast of
+    the new moments; the master and its bf16 param are those of that fp32
+    step.  Grads of unit scale keep v in fp16's normal range."""
+    th, m, v, G = _rand_state(100_003, 64)
+    m16 = torch.from_numpy(m * np.float32(300)).to(torch.float16)
+    v16 = torch.from_numpy(v * np.float32(1e4)).to(torch.float16)
+    G = G * np.float32(300)
+    for t in (1, 5):
+        a = orc.OTensor(th.copy(), _torch_bits(m16).copy(), _torch_bits(v16).copy(), orc.bf16_rne(th), 0,
+                        moments_fp16=True)
+        b = orc.OTensor(th.copy(), m16.float().numpy().copy(), v16.float().numpy().copy(), orc.bf16_rne(th), 0)
+        for T in (a, b):
+            orc.apply_update([T], [G], orc.Hyper(mode=mode), [(1e-3, 0.1)], t, 1.0, True, 0.5, 0.5)
+        assert np.array_equal(a.theta.view(np.uint32), b.theta.view(np.uint32))
+        assert np.array_equal(a.p, b.p)
+        assert np.array_equal(a.m, _torch_bits(torch.from_numpy(b.m).to(torch.float16)))
+        assert np.array_equal(a.v, _torch_bits(torch.from_numpy(b.v).to(torch.float16)))
+
+
+def test_fp16_second_moment_underflows_at_small_grads(orc):
+    """The format's limit, reproduced and not corrected: at t = 1 from zero
+    moments v = (1 - beta2) g^2.  For |g| = 2^-10 that is about 9.5e-10, below
+    half fp16's smallest subnormal (2^-25), so the stored v is +0; the update
+    that step used the fp32 v before the store (u = 1, the first-step closed
+    form), and the next step starts from v = 0."""
+    g = np.full(64, 2.0 ** -10, np.float32)
+    T = orc.OTensor.fresh(np.ones(64, np.float32), fp16_moments=True)
+    opt = orc.OracleOptimizer([T], orc.Hyper(eps=0.0), [(2.0 ** -9, 0.0)])
+    assert opt.step([g]).applied
+    assert np.all(T.v == 0)
+    # m = 0.1 g is an fp16 normal (about 9.8e-5 > 2^-14): stored with the RNE, not lost
+    assert np.all(T.m == _torch_bits(torch.tensor([0.1 * 2.0 ** -10], dtype=torch.float32).to(torch.float16)))
+    assert np.all(T.theta == np.float32(1.0 - 2.0 ** -9))
