@@ -46,7 +46,7 @@ def update_bytes(w) -> int:
     storage: the grad read, the master read and written, each moment read
     and written, all at their widths, and the 16-bit param written (none for
     fp32 params)."""
-    mom = 2 if w.state_dtype == "bf16" else 4
+    mom = 2 if w.state_dtype in ("bf16", "fp16") else 4
     mst = 2 if getattr(w, "master_dtype", "fp32") == "fp16" else 4
     par = 0 if w.param_dtype == "fp32" else 2
     return gradpass_bytes(w) + 2 * mst + 4 * mom + par
@@ -168,7 +168,7 @@ def parse():
     ap.add_argument("--muon-workspace", type=int, default=0,
                     help="Muon set workspace cap in bytes (0: the library default)")
     ap.add_argument("--numel", type=int, default=None, help="override the flat shard's size")
-    ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"],
+    ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16", "fp16"],
                     help="exp_avg / exp_avg_sq storage of the flat shard")
     ap.add_argument("--param-dtype", default="bf16", choices=["bf16", "fp16"],
                     help="model-param dtype of the flat shard")
@@ -247,7 +247,8 @@ def cpu_baseline(sample, w, steps):
     import oracle
     theta, m, v, p, G = sample
     n = theta.size
-    T = oracle.OTensor(theta, m, v, p, 0, w.param_dtype == "fp16", w.master_dtype == "fp16")
+    T = oracle.OTensor(theta, m, v, p, 0, w.param_dtype == "fp16", w.master_dtype == "fp16",
+                       w.state_dtype == "fp16")
     O = oracle.OracleOptimizer([T], oracle.Hyper(w.beta1, w.beta2, w.eps, w.mode), w.groups(),
                                max_norm=w.max_norm)
     times = []
@@ -281,7 +282,7 @@ def cpu_baseline_threads(sample, w, steps, threads):
     n = theta.size
     cuts = [n * k // threads for k in range(threads + 1)]
     parts = [(oracle.OTensor(theta[a:b], m[a:b], v[a:b], p[a:b], 0, w.param_dtype == "fp16",
-                             w.master_dtype == "fp16"), oracle.grad_f32(G[a:b]))
+                             w.master_dtype == "fp16", w.state_dtype == "fp16"), oracle.grad_f32(G[a:b]))
              for a, b in zip(cuts[:-1], cuts[1:])]
     hyper = oracle.Hyper(w.beta1, w.beta2, w.eps, w.mode)
     inv32 = float(np.float32(w.inv_scale()))

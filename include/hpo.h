@@ -80,6 +80,13 @@ typedef enum {
  * silently cast ([FP32-RFC] §7.2). */
 typedef enum { HPO_PARAM_BF16 = 0, HPO_PARAM_FP32 = 1, HPO_PARAM_FP16 = 2 } hpo_param_dtype;
 #define HPO_STATE_BF16 0x100
+/* The same with fp16 moments (IEEE binary16, rounded to nearest even,
+ * subnormals kept): the other 16-bit moment format of [OPT-INFRA] §16.  No
+ * per-tensor scaling is applied, so a second moment below half fp16's
+ * smallest subnormal (2^-25, about 3e-8) is stored as 0: at grad magnitudes
+ * under roughly 1e-2 (with beta2 = 0.999) v is lost or kept with few bits.
+ * Exclusive with HPO_STATE_BF16. */
+#define HPO_STATE_FP16 0x800
 
 /* The main grads and the master may be stored below fp32 as well ([OPT-INFRA]
  * §16 lists main_grads and main_params among the precision-aware optimizer's

@@ -106,26 +106,31 @@ hpo_status check_sizes(int32_t n_tensors, const int64_t* numel)
 struct Layout {
     int32_t pdt;         /* HPO_PARAM_BF16 / FP32 / FP16 */
     int32_t state_bf16;  /* exp_avg / exp_avg_sq are bf16 */
+    int32_t state_fp16;  /* exp_avg / exp_avg_sq are fp16 */
     int32_t grad_bf16;   /* main grads are bf16 */
     int32_t master_fp16; /* the master is fp16 (bf16 params only) */
-    int64_t mom_bytes() const { return state_bf16 ? 2 : 4; }
+    int64_t mom_bytes() const { return (state_bf16 || state_fp16) ? 2 : 4; }
+    int32_t state_store() const { return state_fp16 ? 2 : (state_bf16 ? 1 : 0); }
     int64_t grad_bytes() const { return grad_bf16 ? 2 : 4; }
     int64_t master_bytes() const { return master_fp16 ? 2 : 4; }
 };
 
 hpo_status decode_dtype(int32_t param_dtype, Layout& lay)
 {
-    constexpr int32_t kFlags = HPO_STATE_BF16 | HPO_GRAD_BF16 | HPO_MASTER_FP16;
+    constexpr int32_t kFlags = HPO_STATE_BF16 | HPO_STATE_FP16 | HPO_GRAD_BF16 | HPO_MASTER_FP16;
     lay.pdt = param_dtype & 0xFF;
     lay.state_bf16 = (param_dtype & HPO_STATE_BF16) ? 1 : 0;
+    lay.state_fp16 = (param_dtype & HPO_STATE_FP16) ? 1 : 0;
     lay.grad_bf16 = (param_dtype & HPO_GRAD_BF16) ? 1 : 0;
     lay.master_fp16 = (param_dtype & HPO_MASTER_FP16) ? 1 : 0;
     const bool pdt_ok = lay.pdt == HPO_PARAM_BF16 || lay.pdt == HPO_PARAM_FP32 || lay.pdt == HPO_PARAM_FP16;
     if (!pdt_ok || (param_dtype & ~(0xFF | kFlags)) != 0)
         return fail(HPO_EDTYPE,
                     "param dtype %d is not supported (bf16 = 0, fp32 = 1, fp16 = 2, optionally | HPO_STATE_BF16 "
-                    "| HPO_GRAD_BF16 | HPO_MASTER_FP16)",
+                    "or HPO_STATE_FP16, | HPO_GRAD_BF16, | HPO_MASTER_FP16)",
                     param_dtype);
+    if (lay.state_bf16 && lay.state_fp16)
+        return fail(HPO_EDTYPE, "HPO_STATE_BF16 and HPO_STATE_FP16 are exclusive (param dtype %d)", param_dtype);
     if (lay.master_fp16 && lay.pdt != HPO_PARAM_BF16)
         return fail(HPO_EDTYPE, "HPO_MASTER_FP16 needs bf16 params (param dtype %d)", param_dtype);
     return HPO_OK;
@@ -432,7 +437,7 @@ hpo_status create_from_pieces(hpo_set* out, int32_t param_dtype, const Layout& l
     s->view.chunks = s->d_chunks;
     s->view.is_flat = 0;
     s->view.param_dtype = lay.pdt;
-    s->view.state_bf16 = lay.state_bf16;
+    s->view.state_store = lay.state_store();
     s->view.grad_bf16 = static_cast<int16_t>(lay.grad_bf16);
     s->view.master_fp16 = static_cast<int16_t>(lay.master_fp16);
     *out = s;
@@ -580,7 +585,7 @@ hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype,
     s->view.chunk_elems = ch;
     s->view.is_flat = 1;
     s->view.param_dtype = lay.pdt;
-    s->view.state_bf16 = lay.state_bf16;
+    s->view.state_store = lay.state_store();
     s->view.grad_bf16 = static_cast<int16_t>(lay.grad_bf16);
     s->view.master_fp16 = static_cast<int16_t>(lay.master_fp16);
     st = alloc_partials(s);

@@ -80,7 +80,7 @@ struct SetView {
     int64_t chunk_elems;
     int32_t is_flat;
     int32_t param_dtype;  /* HPO_PARAM_BF16 / FP32 / FP16 */
-    int32_t state_bf16;   /* exp_avg / exp_avg_sq held as bf16 */
+    int32_t state_store;  /* exp_avg / exp_avg_sq storage: 0 fp32, 1 bf16, 2 fp16 */
     int16_t grad_bf16;    /* main grads held as bf16 */
     int16_t master_fp16;  /* master held as fp16 (bf16 params) */
 };

@@ -807,8 +807,11 @@ template <bool DEV>
 hipError_t launch_adam_t(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                          hipStream_t stream)
 {
-    return sv.state_bf16 ? launch_adam_g<DEV, kBF16>(sv, n_chunks, mode, sc, stream)
-                         : launch_adam_g<DEV, kF32>(sv, n_chunks, mode, sc, stream);
+    switch (sv.state_store) {
+    case kBF16: return launch_adam_g<DEV, kBF16>(sv, n_chunks, mode, sc, stream);
+    case kF16: return launch_adam_g<DEV, kF16>(sv, n_chunks, mode, sc, stream);
+    default: return launch_adam_g<DEV, kF32>(sv, n_chunks, mode, sc, stream);
+    }
 }
 
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,

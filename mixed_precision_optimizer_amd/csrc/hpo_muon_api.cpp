@@ -461,7 +461,7 @@ hpo_status hpo_muon_set_create(hpo_set* out, int32_t n_matrices, int32_t param_d
     s->view.chunks = s->d_chunks;
     s->view.is_flat = 0;
     s->view.param_dtype = param_dtype;
-    s->view.state_bf16 = 0;
+    s->view.state_store = 0;
     *out = s;
     return ok();
 }

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libhpo.so")
 HPO_OK, HPO_EINVAL, HPO_EDTYPE, HPO_ENOMEM, HPO_EHIP, HPO_EDEVICE = 0, -1, -2, -3, -4, -5
 HPO_PARAM_BF16, HPO_PARAM_FP32, HPO_PARAM_FP16 = 0, 1, 2
 HPO_STATE_BF16 = 0x100
+HPO_STATE_FP16 = 0x800
 HPO_GRAD_BF16 = 0x200
 HPO_MASTER_FP16 = 0x400
 HPO_ADAMW, HPO_ADAM_L2 = 0, 1
@@ -259,14 +260,18 @@ def param_dtype_code(dtype) -> int:
 
 
 def _moments_flag(exp_avgs, exp_avg_sqs) -> int:
-    """HPO_STATE_BF16 when the moments are bf16 tensors, 0 for fp32; both
-    moments of every tensor must share one of these dtypes."""
+    """HPO_STATE_BF16 / HPO_STATE_FP16 when the moments are bf16 / fp16
+    tensors, 0 for fp32; both moments of every tensor must share one of
+    these dtypes."""
     dts = {t.dtype for t in list(exp_avgs) + list(exp_avg_sqs)}
     if not dts or dts == {torch.float32}:
         return 0
     if dts == {torch.bfloat16}:
         return HPO_STATE_BF16
-    raise TypeError(f"exp_avg / exp_avg_sq must all be float32 or all bfloat16, got {sorted(map(str, dts))}")
+    if dts == {torch.float16}:
+        return HPO_STATE_FP16
+    raise TypeError(f"exp_avg / exp_avg_sq must all be float32, all bfloat16 or all float16, "
+                    f"got {sorted(map(str, dts))}")
 
 
 def _storage_flags(main_params, main_grads, exp_avgs, exp_avg_sqs):
@@ -275,7 +280,7 @@ def _storage_flags(main_params, main_grads, exp_avgs, exp_avg_sqs):
     (HPO_GRAD_BF16), the moments fp32 or bf16 (HPO_STATE_BF16); each kind
     shares one dtype over the whole set."""
     flags = _moments_flag(exp_avgs, exp_avg_sqs)
-    mdt = torch.bfloat16 if flags else torch.float32
+    mdt = {0: torch.float32, HPO_STATE_BF16: torch.bfloat16, HPO_STATE_FP16: torch.float16}[flags]
     out = [flags, torch.float32, torch.float32, mdt]
     for k, what, ts, low, flag in ((1, "main_param", main_params, torch.float16, HPO_MASTER_FP16),
                                    (2, "main_grad", main_grads, torch.bfloat16, HPO_GRAD_BF16)):

@@ -36,7 +36,7 @@ class Workload:
     numels: List[int]
     ndims: List[int]
     param_dtype: str = "bf16"          # "bf16", "fp16" or "fp32" (fp32 params are their own master)
-    state_dtype: str = "fp32"          # exp_avg / exp_avg_sq storage: "fp32" or "bf16"
+    state_dtype: str = "fp32"          # exp_avg / exp_avg_sq storage: "fp32", "bf16" or "fp16"
     grad_dtype: str = "fp32"           # main grad storage: "fp32" or "bf16" (the bf16 image of the fp32 draw)
     master_dtype: str = "fp32"         # master storage: "fp32" or "fp16" (the fp16 image of the fp32 draw)
     lr: float = 1e-3
@@ -273,7 +273,7 @@ def allocate(w: Workload, device) -> Buffers:
     if w.master_dtype == "fp16":
         master = _narrowed(master, torch.float16)
     grad = torch.zeros(total, dtype=torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32, device=device)
-    sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
+    sdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[w.state_dtype]
     exp_avg = torch.zeros(total, dtype=sdt, device=device)
     exp_avg_sq = torch.zeros(total, dtype=sdt, device=device)
     if w.param_dtype == "fp32":

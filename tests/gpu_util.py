@@ -92,19 +92,20 @@ def compare_tensor(tag, gpu, orc_new, orc_prev, G, *, inv, clip, C, c64, lr, wd,
     """gpu: dict theta/m/v[/p] numpy; orc_new / orc_prev: oracle OTensor after / before the step.
     fp32 moments: the rel-1e-6 propagated bound; bf16 moments: within one bf16
     ulp (the master's bound then uses the widened moments)."""
-    sbf16 = orc_new.m.dtype == np.uint16
+    s16 = orc_new.m.dtype == np.uint16
+    wid = widen_fp16 if getattr(orc_new, "moments_fp16", False) else widen_bf16
     t16 = getattr(orc_new, "master_fp16", False)
-    m_prev = widen_bf16(orc_prev.m) if sbf16 else orc_prev.m
-    v_prev = widen_bf16(orc_prev.v) if sbf16 else orc_prev.v
+    m_prev = wid(orc_prev.m) if s16 else orc_prev.m
+    v_prev = wid(orc_prev.v) if s16 else orc_prev.v
     th_prev = widen_fp16(orc_prev.theta) if t16 else orc_prev.theta
     if G.dtype == np.uint16:
         G = widen_bf16(G)
     E_m, E_v, E_th = step_error_bounds(th_prev, m_prev, v_prev, G, inv=inv, C=c64, do_clip=clip,
                                        lr=lr, wd=wd, t=t, mode=mode)
-    if sbf16:
+    if s16:
         for key in ("m", "v"):
-            d = np.abs(gpu[key].astype(np.int32) - getattr(orc_new, key).astype(np.int32))
-            assert np.all(d <= 1), f"{tag} {key}: bf16 moment more than 1 ulp from the oracle"
+            d = np.abs(ordered16(gpu[key]) - ordered16(getattr(orc_new, key)))
+            assert np.all(d <= 1), f"{tag} {key}: 16-bit moment more than 1 ulp from the oracle"
         eq_mv = int(np.sum(gpu["m"] == orc_new.m)) + int(np.sum(gpu["v"] == orc_new.v))
     else:
         check_within(f"{tag} m", gpu["m"], orc_new.m, E_m)

@@ -80,9 +80,12 @@ def test_validation_happens_before_any_device_call(H):
     st, msg = _flat(H, -1, 0, [0] * 5)
     assert st == H.HPO_EINVAL and "negative" in msg
     # unsupported dtypes: an error, never a silent cast
-    for code in (3, 0x800, 0x101 | 0x1000, -1):
+    for code in (3, 0x2000, 0x101 | 0x1000, -1):
         st, msg = _flat(H, 16, code, [0x1000] * 5)
         assert st == H.HPO_EDTYPE and "not supported" in msg, code
+    # one moment format at a time
+    st, msg = _flat(H, 16, 0x900, [0x1000] * 5)
+    assert st == H.HPO_EDTYPE and "exclusive" in msg
     # an fp16 master only under bf16 params
     for code in (0x401, 0x402, 0x501, 0x601):
         st, msg = _flat(H, 16, code, [0x1000] * 5)
@@ -237,7 +240,7 @@ def test_muon_set_validation(H):
     any device call."""
     st, msg = _muon(H, [(4, 8)], pdt=2)
     assert st == H.HPO_EDTYPE and "fp16" in msg
-    for code in (0x100, 0x200, 0x400):
+    for code in (0x100, 0x200, 0x400, 0x800):
         st, msg = _muon(H, [(4, 8)], pdt=code)
         assert st == H.HPO_EDTYPE, code
     st, msg = _muon(H, [(4, -8)])
@@ -316,6 +319,7 @@ def test_binding_storage_flags(H):
     and refuses sets that mix dtypes within a kind."""
     f32, bf, fp = (torch.zeros(4, dtype=d) for d in (torch.float32, torch.bfloat16, torch.float16))
     assert H._storage_flags([f32], [f32], [f32], [f32]) == (0, torch.float32, torch.float32, torch.float32)
+    assert H._storage_flags([f32], [f32], [fp], [fp])[0] == H.HPO_STATE_FP16
     fl = H._storage_flags([fp], [bf], [bf], [bf])
     assert fl == (H.HPO_MASTER_FP16 | H.HPO_GRAD_BF16 | H.HPO_STATE_BF16, torch.float16, torch.bfloat16,
                   torch.bfloat16)

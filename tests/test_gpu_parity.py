@@ -38,7 +38,7 @@ def _oracle_tensors(orc, bufs):
     for i in range(w.n_tensors):
         st = read_state(bufs, i)
         T = orc.OTensor(st["theta"], st["m"], st["v"], st.get("p"), w.group_of(i), w.param_dtype == "fp16",
-                        w.master_dtype == "fp16")
+                        w.master_dtype == "fp16", w.state_dtype == "fp16")
         out.append(T)
     return out
 
@@ -116,12 +116,13 @@ def test_two_matrices_ten_steps(H, orc):
 
 
 def _edge_workload(mode, loss_scale, inf_step=None, max_norm=1.0, steps=4, param_dtype="bf16",
-                   state_dtype="fp32", grad_dtype="fp32", master_dtype="fp32"):
+                   state_dtype="fp32", grad_dtype="fp32", master_dtype="fp32", grad_std_scale=1.0):
     from mixed_precision_optimizer_amd.inputs import Workload
     sizes = [1, 3, 4, 5, 63, 64, 65, 255, 1023, 4095, 4096, 4097, 0, 12345, 70001, 131072, 300000, 2]
     ndims = [1 if n in (4095, 5, 63) else 2 for n in sizes]
     return Workload(f"edge_mode{mode}", sizes, ndims, lr=1e-3, weight_decay=0.1, mode=mode, max_norm=max_norm,
-                    loss_scale=loss_scale, steps=steps, grad_std=[1e-3 * (1 + (i % 5)) for i in range(len(sizes))],
+                    loss_scale=loss_scale, steps=steps,
+                    grad_std=[1e-3 * grad_std_scale * (1 + (i % 5)) for i in range(len(sizes))],
                     inf_step=inf_step, param_dtype=param_dtype, state_dtype=state_dtype, grad_dtype=grad_dtype,
                     master_dtype=master_dtype)
 
@@ -154,18 +155,22 @@ def test_reduced_precision_variants(H, orc, mode, pdt, sdt):
 
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("gdt,tdt,sdt", [("bf16", "fp32", "fp32"), ("fp32", "fp16", "fp32"), ("bf16", "fp16", "fp32"),
-                                         ("bf16", "fp16", "bf16")])
+                                         ("bf16", "fp16", "bf16"), ("fp32", "fp32", "fp16"), ("bf16", "fp16", "fp16")])
 @pytest.mark.parametrize("inplace", [False, True])
 def test_lower_precision_grads_and_master(H, orc, mode, gdt, tdt, sdt, inplace):
     """bf16 main grads and an fp16 master under bf16 params, alone and
     together with bf16 moments, on the ragged edge sets (loss scale 1024,
     clipping, a no-decay group, a skipped step), with the fused and the
-    in-place unscale, against the oracle's own trajectory."""
+    in-place unscale, against the oracle's own trajectory.  fp16 moments run
+    with grads 300x larger as well, so that v sits in fp16's normal range
+    rather than underflowing."""
     banner(f"lower precision: grads {gdt}, master {tdt}, moments {sdt}, mode {mode}, inplace {inplace}")
-    w = _edge_workload(mode, 1024.0, inf_step=3, steps=6, state_dtype=sdt, grad_dtype=gdt, master_dtype=tdt)
-    stats, Ts, bufs = _run_parity(H, orc, w, inplace=inplace)
-    assert stats["skipped"] == [3]
-    assert stats["bit_equal"] == stats["compared"]
+    for scale in ((1.0, 300.0) if sdt == "fp16" else (1.0,)):
+        w = _edge_workload(mode, 1024.0, inf_step=3, steps=6, state_dtype=sdt, grad_dtype=gdt, master_dtype=tdt,
+                           grad_std_scale=scale)
+        stats, Ts, bufs = _run_parity(H, orc, w, inplace=inplace)
+        assert stats["skipped"] == [3]
+        assert stats["bit_equal"] == stats["compared"], scale
 
 
 @pytest.mark.parametrize("grads", ["fp32", "bf16"])
@@ -439,7 +444,8 @@ def test_flat_and_list_sets_agree_bitwise(H):
 
 @pytest.mark.parametrize("moments,param,grads,master", [("fp32", "bf16", "fp32", "fp32"), ("bf16", "bf16", "fp32", "fp32"),
                                                         ("bf16", "fp16", "fp32", "fp32"), ("fp32", "bf16", "bf16", "fp32"),
-                                                        ("fp32", "bf16", "fp32", "fp16"), ("bf16", "bf16", "bf16", "fp16")])
+                                                        ("fp32", "bf16", "fp32", "fp16"), ("bf16", "bf16", "bf16", "fp16"),
+                                                        ("fp16", "bf16", "fp32", "fp32"), ("fp16", "bf16", "bf16", "fp16")])
 def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param, grads, master):
     """Views that start 1..3 elements into their buffers, as a list set and
     as a flat set: when all five pointers share the element offset (for
@@ -453,7 +459,7 @@ def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param, grads, mas
     rng = np.random.default_rng(6)
     th0 = rng.standard_normal(n).astype(np.float32)
     G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
-    mdt = torch.bfloat16 if moments == "bf16" else torch.float32
+    mdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[moments]
     pdt = torch.float16 if param == "fp16" else torch.bfloat16
     tdt = torch.float16 if master == "fp16" else torch.float32
     gdt = torch.bfloat16 if grads == "bf16" else torch.float32
@@ -485,7 +491,7 @@ def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param, grads, mas
         for a, b in zip(res[0], r):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
     T = orc.OTensor.fresh(th0, fp16_param=param == "fp16", state_bf16=moments == "bf16",
-                          fp16_master=master == "fp16")
+                          fp16_master=master == "fp16", fp16_moments=moments == "fp16")
     orc.OracleOptimizer([T], orc.Hyper(mode=1), [(1e-3, 0.1)], max_norm=1.0).step([G_stored])
     for got, want in zip(res[0], (T.theta, T.m, T.v, T.p)):
         assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
