@@ -49,7 +49,8 @@
 extern "C" {
 #endif
 
-#define HPO_ABI_VERSION 2
+/* 3: param_dtype also takes HPO_STATE_FP16, HPO_GRAD_BF16 and HPO_MASTER_FP16. */
+#define HPO_ABI_VERSION 3
 /* Most parameter groups one step can take (per-group lr / weight decay). */
 #define HPO_MAX_GROUPS 16
 

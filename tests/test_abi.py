@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(H):
         assert hasattr(lib, n), n
         assert n in H.SIGNATURES, f"binding lacks {n}"
     assert set(H.SIGNATURES) == set(names)
-    assert H.hpo_abi_version() == 2
+    assert H.hpo_abi_version() == 3
 
 
 def test_struct_layouts(H):
