@@ -108,6 +108,8 @@ def lib():
         L.orc_unscale_inplace.argtypes = [P, I64, ctypes.c_float]
         L.orc_sumsq.argtypes = [P, I64, ctypes.c_float]
         L.orc_sumsq.restype = ctypes.c_double
+        L.orc_count_zeros.argtypes = [P, I64, ctypes.c_float]
+        L.orc_count_zeros.restype = ctypes.c_int64
         L.orc_clip_coeff.argtypes = [ctypes.c_double, ctypes.c_float,
                                      ctypes.POINTER(ctypes.c_float),
                                      ctypes.POINTER(ctypes.c_double)]
@@ -213,6 +215,14 @@ def sumsq(G: np.ndarray, inv_scale: float = 1.0) -> float:
     return float(lib().orc_sumsq(_ptr(G), G.size, ctypes.c_float(inv_scale)))
 
 
+def count_zeros(G: np.ndarray, inv_scale: float = 1.0) -> int:
+    """Number of elements whose unscaled value fp32(G * inv) is zero (either
+    sign); the step's num_zeros ([OPT-INFRA] §10.2 return value, §17
+    log_num_zeros_in_grad), counted over the same grads as the norm."""
+    G = _f32(G)
+    return int(lib().orc_count_zeros(_ptr(G), G.size, ctypes.c_float(inv_scale)))
+
+
 def clip_coeff(max_norm: float, norm32: float):
     """Returns (applies, C as fp32 value, c64)."""
     C = ctypes.c_float(1.0)
@@ -289,6 +299,7 @@ class StepResult:
     clip_applied: bool = False
     clip_C: float = 1.0
     extra: dict = field(default_factory=dict)
+    num_zeros: Optional[int] = None   # zeros of the unscaled grads; None on a non-finite step
 
 
 def oracle_step(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper: Hyper,
@@ -316,11 +327,16 @@ def oracle_step(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper: 
         if G.size:
             n2 = n2 + sumsq(G, inv32)
     norm64, norm32 = norm_from_sumsq(n2)
+    # the step's zero count, over the same unscaled grads as the norm
+    zeros = 0
+    for G in grads:
+        if G.size:
+            zeros = zeros + count_zeros(G, inv32)
     # a3: clip coefficient from the fp32 norm
     do_clip, C, c64 = clip_coeff(max_norm, norm32)
     # a4 + a5: the update, one call per tensor with its group's lr / wd
     apply_update(tensors, grads, hyper, groups, t, inv32, do_clip, C, c64, variant)
-    return StepResult(True, False, norm32, norm64, do_clip, C)
+    return StepResult(True, False, norm32, norm64, do_clip, C, num_zeros=zeros)
 
 
 def apply_update(tensors: Sequence[OTensor], grads: Sequence[np.ndarray], hyper: Hyper,
@@ -461,10 +477,14 @@ class OracleOptimizer:
             if G.size:
                 n2 = n2 + sumsq(G, inv)
         norm64, norm32 = norm_from_sumsq(n2)
+        zeros = 0
+        for G in grads:
+            if G.size:
+                zeros = zeros + count_zeros(G, inv)
         if norm32 > skip_threshold:
-            return StepResult(False, False, norm32, norm64, extra={"threshold_skip": True})
+            return StepResult(False, False, norm32, norm64, extra={"threshold_skip": True}, num_zeros=zeros)
         do_clip, C, c64 = clip_coeff(self.max_norm, norm32)
         apply_update(self.tensors, grads, self.hyper, self.groups, self.t + 1, inv, do_clip, C, c64,
                      self.variant)
         self.t += 1
-        return StepResult(True, False, norm32, norm64, do_clip, C)
+        return StepResult(True, False, norm32, norm64, do_clip, C, num_zeros=zeros)

@@ -197,6 +197,25 @@ double orc_sumsq(const float* G, int64_t n, float inv_scale)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Zero count of the step's gradient ([OPT-INFRA] §10.2: an applied step     */
+/* returns (success, grad_norm, num_zeros); §17: log_num_zeros_in_grad).     */
+/* The pages do not say which gradient is counted.  Reading: the unscaled    */
+/* fp32 grad g = fp32(G * inv_scale), the same vector whose norm the step    */
+/* returns; +0 and -0 both count (they compare equal), so a subnormal that   */
+/* the unscale rounds to zero counts too.  NaN and inf are not zero.         */
+/* ------------------------------------------------------------------------ */
+int64_t orc_count_zeros(const float* G, int64_t n, float inv_scale)
+{
+    int64_t zeros = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float g = G[i] * inv_scale;
+        if (g == 0.0f)
+            zeros = zeros + 1;
+    }
+    return zeros;
+}
+
+/* ------------------------------------------------------------------------ */
 /* a3: clip coefficient, [OPT-INFRA] §11.1: c = max_norm / (total + 1e-6),  */
 /* applied only when c < 1; a non-positive max_norm turns clipping off.     */
 /* The fp32 norm handed in is widened to binary64, c is formed in binary64  */

@@ -65,8 +65,8 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (ADAMW, Hyper, OTensor, StepResult, any_nonfinite, apply_update, bf16_rne, clip_coeff, grad_f32,
-               norm_from_sumsq, sumsq)
+from . import (ADAMW, Hyper, OTensor, StepResult, any_nonfinite, apply_update, bf16_rne, clip_coeff, count_zeros,
+               grad_f32, norm_from_sumsq, sumsq)
 
 # (a, b, c) of the quintic the pages print (the original single set)
 NS_SIMPLE = (3.4445, -4.7750, 2.0315)
@@ -288,6 +288,10 @@ class ChainedOracle:
             if G.size:
                 n2 = n2 + sumsq(np.ascontiguousarray(G, dtype=F32).ravel(), inv32)
         norm64, norm32 = norm_from_sumsq(n2)
+        zeros = 0
+        for G in allg:
+            if G.size:
+                zeros = zeros + count_zeros(np.ascontiguousarray(G, dtype=F32).ravel(), inv32)
         do_clip, C, c64 = clip_coeff(self.max_norm, norm32)
         t = self.t + 1
         if self.adam:
@@ -301,7 +305,7 @@ class ChainedOracle:
                 continue
             self.last.append(muon_matrix_step(T, G, self.cfg, lr, wd, inv32, do_clip, C, self.ns))
         self.t = t
-        return StepResult(True, False, norm32, norm64, do_clip, C)
+        return StepResult(True, False, norm32, norm64, do_clip, C, num_zeros=zeros)
 
 
 __all__ = ["NS_SIMPLE", "NS_EPS", "MOMENTUM_SUM", "MOMENTUM_EMA", "SCALE_SPECTRAL", "SCALE_SHAPE",

@@ -300,6 +300,100 @@ def test_skip_leaves_state_and_counter_alone(orc):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+# ---------------------------------------------------------------------------
+# the step's zero count ("02 · Optimizer：算法与 infra" §10.2 return value,
+# §17 log_num_zeros_in_grad): zeros of the unscaled grads
+# ---------------------------------------------------------------------------
+def _bits(u):
+    return np.array([u], dtype=np.uint32).view(np.float32)[0]
+
+
+# Stored grads around fp32's underflow threshold under an unscale by 2^-16,
+# each with whether fp32(G * 2^-16) is zero.  Round to nearest even: a product
+# below 2^-150 (half the smallest subnormal 2^-149) rounds to zero, exactly
+# 2^-150 is a tie that goes to the even neighbour 0, anything above rounds to
+# 2^-149.  Decided by hand from IEEE 754, not computed.
+_UNDERFLOW_CASES = [
+    (0.0, True),                                   # +0
+    (-0.0, True),                                  # -0 compares equal to 0
+    (_bits(0x00000001), True),                     # 2^-149 -> 2^-165
+    (-_bits(0x00000001), True),
+    (_bits(0x00000200), True),                     # 2^-140 -> 2^-156
+    (_bits(0x00008000), True),                     # 2^-134 -> 2^-150, the tie: even -> 0
+    (-_bits(0x00008000), True),
+    (_bits(0x00008001), False),                    # 2^-134 + 2^-149 -> just above 2^-150 -> 2^-149
+    (_bits(0x0000C000), False),                    # 1.5 * 2^-134 -> 0.75 * 2^-149 -> 2^-149
+    (_bits(0x00010000), False),                    # 2^-133 -> 2^-149 exactly
+    (_bits(0x00800000), False),                    # 2^-126 (smallest normal) -> 2^-142, subnormal
+    (np.float32(1e-3), False),
+    (np.float32(-65536.0), False),
+    (np.float32(np.nan), False),                   # NaN is not zero
+    (np.float32(np.inf), False),
+]
+
+
+def test_zero_count_known_underflow_cases(orc):
+    """Each case alone and all together: the count under 2^-16 is the number
+    of cases marked zero; under no scale only the two signed zeros count.
+    A count taken on the stored (scaled) grads, one that counts only +0's bit
+    pattern, or one that treats NaN as zero fails here."""
+    G = np.array([g for g, _ in _UNDERFLOW_CASES], dtype=np.float32)
+    want = sum(1 for _, z in _UNDERFLOW_CASES if z)
+    assert want == 7
+    assert orc.count_zeros(G, 2.0 ** -16) == want
+    assert orc.count_zeros(G, 1.0) == 2
+    for g, z in _UNDERFLOW_CASES:
+        assert orc.count_zeros(np.array([g], dtype=np.float32), 2.0 ** -16) == int(z), hex(
+            int(np.array([g], dtype=np.float32).view(np.uint32)[0]))
+
+
+def test_zero_count_against_numpy_products(orc):
+    """Brute force with numpy's own fp32 multiply and compare, on grads with
+    planted zeros of both signs and subnormals, at several scales; also
+    permutation invariance and additivity over a split."""
+    rng = np.random.default_rng(35)
+    n = 200_003
+    G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    idx = rng.choice(n, 5000, replace=False)
+    G[idx[:1000]] = 0.0
+    G[idx[1000:2000]] = -0.0
+    G[idx[2000:5000]] = (rng.integers(1, 1 << 20, 3000).astype(np.uint32)).view(np.float32)  # subnormals
+    for inv in (1.0, 2.0 ** -16, 2.0 ** -24, 1.0 / 3.0):
+        inv32 = np.float32(inv)
+        prod = G * inv32
+        assert prod.dtype == np.float32
+        want = int(n - np.count_nonzero(prod))
+        got = orc.count_zeros(G, inv)
+        assert got == want, (inv, got, want)
+        assert orc.count_zeros(G[rng.permutation(n)], inv) == got
+        assert orc.count_zeros(G[:77_777], inv) + orc.count_zeros(G[77_777:], inv) == got
+    assert orc.count_zeros(G, 1.0) == 2000
+
+
+def test_step_returns_zero_count_and_none_on_skip(orc):
+    """The applied step returns (success, grad_norm, num_zeros) and a skipped
+    one (False, None, None) ("02 · Optimizer：算法与 infra" §10.2): the oracle's
+    result carries the count over all tensors, and None on a non-finite step."""
+    rng = np.random.default_rng(36)
+    th = [rng.standard_normal(n).astype(np.float32) for n in (1000, 37, 4096)]
+    G = [(rng.standard_normal(x.size) * 1e-3 + 1e-2).astype(np.float32) for x in th]  # no accidental zeros
+    G[0][[3, 500, 999]] = [0.0, -0.0, 0.0]
+    G[2][:40] = 0.0
+    G[1][5] = _bits(0x00000003)   # 3 * 2^-149: not zero at S = 1, zero after * 2^-16
+    O = orc.OracleOptimizer([orc.OTensor.fresh(x) for x in th], orc.Hyper(), [(1e-3, 0.1)], max_norm=1.0)
+    assert all(np.all(g != 0) for g in (np.delete(G[0], [3, 500, 999]), np.delete(G[1], 5), G[2][40:]))
+    r = O.step(G)
+    assert r.applied and r.num_zeros == 43
+    scaled = [g * np.float32(65536.0) for g in G]
+    scaled[1][5] = _bits(0x00000003)   # stored 3 * 2^-149 underflows under the unscale
+    r = O.step(scaled, inv_scale=2.0 ** -16)
+    assert r.applied and r.num_zeros == 44
+    bad = [g.copy() for g in G]
+    bad[1][0] = np.nan
+    r = O.step(bad)
+    assert not r.applied and r.num_zeros is None and r.norm32 is None
+
+
 def test_unscale_power_of_two_is_exact(orc):
     """Multiplying by 2^-16 is exact for normal fp32 values, so the in-place
     unscale recovers the unscaled grads bit for bit."""
