@@ -168,7 +168,7 @@ def parse():
     ap.add_argument("--muon-workspace", type=int, default=0,
                     help="Muon set workspace cap in bytes (0: the library default)")
     ap.add_argument("--numel", type=int, default=None, help="override the flat shard's size")
-    ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16", "fp16"],
+    ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"],
                     help="exp_avg / exp_avg_sq storage of the flat shard")
     ap.add_argument("--param-dtype", default="bf16", choices=["bf16", "fp16"],
                     help="model-param dtype of the flat shard")
@@ -351,7 +351,7 @@ def main():
         buf.zero_()
         if evs:
             evs[0].record(stream)
-        hpo.hpo_grad_global_norm(hset, inv, norm, found, stream)
+        hpo.hpo_grad_global_norm(hset, inv, norm, found, stream=stream)
         if evs:
             evs[1].record(stream)
         hpo.hpo_adamw_step(hset, cfg, groups, n_groups, t_applied + 1, inv, w.max_norm, norm, found, stream)

@@ -30,7 +30,7 @@
  *   - The caller owns (allocates, frees) every tensor and every device
  *     result buffer.  The library never frees or resizes them.  A set holds
  *     only its own small device tables (one 64-byte descriptor per tensor,
- *     16 bytes per chunk, 12 bytes per grad-pass workgroup of reduction
+ *     16 bytes per chunk, 20 bytes per grad-pass workgroup of reduction
  *     partials); it never allocates per-element memory.
  *   - The tensors of a set must stay allocated while the set exists and must
  *     not overlap one another.  All element counts are int64.
@@ -49,8 +49,8 @@
 extern "C" {
 #endif
 
-/* 3: param_dtype also takes HPO_STATE_FP16, HPO_GRAD_BF16 and HPO_MASTER_FP16. */
-#define HPO_ABI_VERSION 3
+/* 4: the norm calls and the device step state report the grads' zero count. */
+#define HPO_ABI_VERSION 4
 /* Most parameter groups one step can take (per-group lr / weight decay). */
 #define HPO_MAX_GROUPS 16
 
@@ -81,12 +81,13 @@ typedef enum {
  * silently cast ([FP32-RFC] §7.2). */
 typedef enum { HPO_PARAM_BF16 = 0, HPO_PARAM_FP32 = 1, HPO_PARAM_FP16 = 2 } hpo_param_dtype;
 #define HPO_STATE_BF16 0x100
-/* The same with fp16 moments (IEEE binary16, rounded to nearest even,
- * subnormals kept): the other 16-bit moment format of [OPT-INFRA] §16.  No
- * per-tensor scaling is applied, so a second moment below half fp16's
- * smallest subnormal (2^-25, about 3e-8) is stored as 0: at grad magnitudes
- * under roughly 1e-2 (with beta2 = 0.999) v is lost or kept with few bits.
- * Exclusive with HPO_STATE_BF16. */
+/* fp16 moments are refused (HPO_EDTYPE).  [OPT-INFRA] §16 lets
+ * exp_avg_dtype / exp_avg_sq_dtype go below fp32 without fixing a format or a
+ * scale.  Without a per-tensor scale, fp16 cannot hold the second moment at
+ * ordinary grad magnitudes: (1 - beta2) g^2 falls below half fp16's smallest
+ * subnormal (2^-25) once |g| is under about 1.7e-4 and is stored as 0, and the
+ * first moment runs subnormal (few bits) below |g| of about 6e-4, so the
+ * update stops being Adam's.  bf16 has fp32's range and keeps both. */
 #define HPO_STATE_FP16 0x800
 
 /* The main grads and the master may be stored below fp32 as well ([OPT-INFRA]
@@ -227,9 +228,14 @@ hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_in
  * sum, so the result is deterministic).  The grads are not written.
  * d_found_inf (device int32, nullable) is set to 1 when any stored element is
  * inf or NaN (same rule as above) -- the same read serves both.  When a
- * non-finite value is present the norm is inf or NaN. */
+ * non-finite value is present the norm is inf or NaN.
+ * d_num_zeros (device int64, nullable) receives the number of elements whose
+ * g is zero, +0 or -0: the step's num_zeros ([OPT-INFRA] §10.2, an applied
+ * step returns (success, grad_norm, num_zeros); §17 log_num_zeros_in_grad),
+ * counted on the unscaled grads whose norm is taken, before the clip.  A
+ * stored value that the unscale rounds to zero counts; NaN and inf do not. */
 hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32_t* d_found_inf,
-                                void* stream);
+                                int64_t* d_num_zeros, void* stream);
 
 /* Clip + Adam/AdamW update + bf16 write-back, one fused pass
  * ([OPT-INFRA] §11.1, §2, §3, §9.2).  For every element, with fp32 arithmetic
@@ -266,7 +272,7 @@ hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* g
  * tables travel in the kernel arguments (2 KB at 256). */
 #define HPO_MAX_WINDOW 256
 
-/* Loss-scaler and step state kept in device memory (48 bytes, caller-owned,
+/* Loss-scaler and step state kept in device memory (56 bytes, caller-owned,
  * 8-byte aligned).  The caller multiplies its loss by loss_scale before
  * backward ([OPT-INFRA] §10.2: the loss is scaled, the grads are unscaled
  * before the step) and may read the struct back at any time after a sync. */
@@ -281,6 +287,7 @@ typedef struct {
     int32_t found_inf;          /* the last step saw an inf/NaN grad */
     int32_t applied;            /* the last step was applied */
     int32_t error;              /* sticky: a step's t fell outside the window it was given */
+    int64_t num_zeros;          /* zeros among the last step's unscaled grads (as hpo_grad_global_norm) */
 } hpo_scaler_state;
 
 /* Scaler and skip policy ([OPT-INFRA] §10.1 scaler rules and defaults; §11.4
@@ -428,9 +435,10 @@ hpo_status hpo_muon_step(hpo_set s, const hpo_muon_cfg* cfg, const hpo_group* gr
  * optimizers takes one norm over all of its grads): *d_norm receives
  * fp32(sqrt(sum over every element of every set of (G * inv_scale)^2)), the
  * sum in binary64, the sets' partial sums added in array order; d_found_inf
- * as in hpo_grad_global_norm.  1 <= n_sets <= 4, all on one device. */
+ * and d_num_zeros as in hpo_grad_global_norm, over all the sets.
+ * 1 <= n_sets <= 4, all on one device. */
 hpo_status hpo_grad_global_norm_sets(const hpo_set* sets, int32_t n_sets, float inv_scale, float* d_norm,
-                                     int32_t* d_found_inf, void* stream);
+                                     int32_t* d_found_inf, int64_t* d_num_zeros, void* stream);
 
 /* hpo_step_device for an AdamW set and a Muon set stepped as one chain
  * ([OPT-INFRA] §11.4): one grad pass over both, one norm (AdamW grads

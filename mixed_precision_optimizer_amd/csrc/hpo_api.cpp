@@ -83,11 +83,7 @@ int32_t grad_group_of(int32_t chunk_elems, int64_t n_chunks)
 int64_t parts_of(int64_t n_chunks, int32_t group) { return (n_chunks + group - 1) / group; }
 
 /* First-stage partials plus the second-stage ones of large sets. */
-int64_t partial_bytes(int64_t n_parts)
-{
-    const int64_t n = (n_parts > 0 ? n_parts : 1) + hpo::stage_parts(n_parts);
-    return n * static_cast<int64_t>(sizeof(double) + sizeof(int32_t));
-}
+int64_t partial_bytes(int64_t n_parts) { return hpo::partial_entries(n_parts) * hpo::kPartialBytes; }
 
 hpo_status check_sizes(int32_t n_tensors, const int64_t* numel)
 {
@@ -100,20 +96,6 @@ hpo_status check_sizes(int32_t n_tensors, const int64_t* numel)
             return fail(HPO_EINVAL, "numel[%d] = %lld is negative", i, (long long)numel[i]);
     return HPO_OK;
 }
-
-/* What a set stores: the model-param dtype and the widths of the moments,
- * the main grads and the master. */
-struct Layout {
-    int32_t pdt;         /* HPO_PARAM_BF16 / FP32 / FP16 */
-    int32_t state_bf16;  /* exp_avg / exp_avg_sq are bf16 */
-    int32_t state_fp16;  /* exp_avg / exp_avg_sq are fp16 */
-    int32_t grad_bf16;   /* main grads are bf16 */
-    int32_t master_fp16; /* the master is fp16 (bf16 params only) */
-    int64_t mom_bytes() const { return (state_bf16 || state_fp16) ? 2 : 4; }
-    int32_t state_store() const { return state_fp16 ? 2 : (state_bf16 ? 1 : 0); }
-    int64_t grad_bytes() const { return grad_bf16 ? 2 : 4; }
-    int64_t master_bytes() const { return master_fp16 ? 2 : 4; }
-};
 
 hpo_status decode_dtype(int32_t param_dtype, Layout& lay)
 {
@@ -129,8 +111,10 @@ hpo_status decode_dtype(int32_t param_dtype, Layout& lay)
                     "param dtype %d is not supported (bf16 = 0, fp32 = 1, fp16 = 2, optionally | HPO_STATE_BF16 "
                     "or HPO_STATE_FP16, | HPO_GRAD_BF16, | HPO_MASTER_FP16)",
                     param_dtype);
-    if (lay.state_bf16 && lay.state_fp16)
-        return fail(HPO_EDTYPE, "HPO_STATE_BF16 and HPO_STATE_FP16 are exclusive (param dtype %d)", param_dtype);
+    if (lay.state_fp16)
+        return fail(HPO_EDTYPE,
+                    "fp16 moments (HPO_STATE_FP16) are not supported: with no per-tensor scale fp16 stores "
+                    "exp_avg_sq = (1 - beta2) g^2 as 0 below |g| ~ 1.7e-4; use bf16 moments (HPO_STATE_BF16)");
     if (lay.master_fp16 && lay.pdt != HPO_PARAM_BF16)
         return fail(HPO_EDTYPE, "HPO_MASTER_FP16 needs bf16 params (param dtype %d)", param_dtype);
     return HPO_OK;
@@ -260,8 +244,7 @@ void free_set(hpo_set s)
         return;
     if (s->d_tensors) (void)hipFree(s->d_tensors);
     if (s->d_chunks) (void)hipFree(s->d_chunks);
-    if (s->d_part_sum) (void)hipFree(s->d_part_sum);
-    if (s->d_part_flag) (void)hipFree(s->d_part_flag);
+    if (s->d_parts) (void)hipFree(s->d_parts);
     free_muon(s->muon);
     delete s;
 }
@@ -270,14 +253,13 @@ hpo_status alloc_partials(hpo_set s)
 {
     s->grad_group = grad_group_of(static_cast<int32_t>(s->view.chunk_elems), s->n_chunks);
     s->n_parts = parts_of(s->n_chunks, s->grad_group);
-    const int64_t n = (s->n_parts > 0 ? s->n_parts : 1) + hpo::stage_parts(s->n_parts);
-    hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->d_part_sum), n * sizeof(double));
+    const int64_t bytes = partial_bytes(s->n_parts);
+    hipError_t e = hipMalloc(&s->d_parts, static_cast<size_t>(bytes));
     if (e != hipSuccess)
-        return fail(HPO_ENOMEM, "hipMalloc of %lld reduction partials: %s", (long long)n, hipGetErrorString(e));
-    e = hipMalloc(reinterpret_cast<void**>(&s->d_part_flag), n * sizeof(int32_t));
-    if (e != hipSuccess)
-        return fail(HPO_ENOMEM, "hipMalloc of %lld flag partials: %s", (long long)n, hipGetErrorString(e));
-    s->device_bytes += partial_bytes(s->n_parts);
+        return fail(HPO_ENOMEM, "hipMalloc of %lld reduction partials: %s", (long long)hpo::partial_entries(s->n_parts),
+                    hipGetErrorString(e));
+    s->parts = hpo::carve_partials(s->d_parts, s->n_parts);
+    s->device_bytes += bytes;
     return HPO_OK;
 }
 
@@ -296,16 +278,9 @@ hpo_status check_set(hpo_set s)
 
 hipStream_t as_stream(void* stream) { return static_cast<hipStream_t>(stream); }
 
-/* The second-stage partials sit right after the first-stage ones. */
-double* stage_sum(hpo_set s) { return s->d_part_sum + (s->n_parts > 0 ? s->n_parts : 1); }
-int32_t* stage_flag(hpo_set s) { return s->d_part_flag + (s->n_parts > 0 ? s->n_parts : 1); }
-
 bool is_finite(double x) { return std::isfinite(x); }
 
-hpo::Partials partials_of(hpo_set s)
-{
-    return hpo::Partials{s->d_part_sum, s->d_part_flag, s->n_parts, stage_sum(s), stage_flag(s)};
-}
+hpo::Partials partials_of(hpo_set s) { return s->parts; }
 
 }  // namespace hpo_host
 
@@ -634,13 +609,12 @@ hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_in
     if (!std::isfinite(inv_scale))
         return fail(HPO_EINVAL, "inv_scale must be finite");
     const hpo::GradPass pass = (inv_scale == 1.0f) ? hpo::GradPass::kCheck : hpo::GradPass::kUnscale;
-    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, pass, inv_scale, nullptr,
-                                         s->d_part_sum, s->d_part_flag, as_stream(stream));
+    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, pass, inv_scale, nullptr, s->parts,
+                                         as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch unscale/check pass");
     if (s->n_chunks > 0) {
-        e = hpo::launch_finalize(nullptr, s->d_part_flag, s->n_parts, stage_sum(s), stage_flag(s), nullptr,
-                                 d_found_inf, as_stream(stream));
+        e = hpo::launch_finalize_sets(&s->parts, 1, nullptr, d_found_inf, nullptr, as_stream(stream));
         if (e != hipSuccess)
             return hip_fail(e, "launch flag finalize");
     }
@@ -648,7 +622,7 @@ hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_in
 }
 
 hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32_t* d_found_inf,
-                                void* stream)
+                                int64_t* d_num_zeros, void* stream)
 {
     hpo_status st = check_set(s);
     if (st != HPO_OK)
@@ -657,13 +631,14 @@ hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32
         return fail(HPO_EINVAL, "d_norm is NULL");
     if (!std::isfinite(inv_scale))
         return fail(HPO_EINVAL, "inv_scale must be finite");
+    if (d_num_zeros && !aligned(d_num_zeros, 8))
+        return fail(HPO_EINVAL, "d_num_zeros must be 8-byte aligned");
     hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm,
-                                         inv_scale, nullptr, s->d_part_sum, s->d_part_flag, as_stream(stream));
+                                         inv_scale, nullptr, s->parts, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch norm pass");
-    /* with no chunks the finalizer still runs, so the norm reads 0 */
-    e = hpo::launch_finalize(s->d_part_sum, s->d_part_flag, s->n_parts, stage_sum(s), stage_flag(s), d_norm,
-                             d_found_inf, as_stream(stream));
+    /* with no chunks the finalizer still runs, so the norm and the count read 0 */
+    e = hpo::launch_finalize_sets(&s->parts, 1, d_norm, d_found_inf, d_num_zeros, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch norm finalize");
     return ok();
@@ -671,17 +646,13 @@ hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32
 
 }  // extern "C"
 
-namespace {
+namespace hpo_host {
 
-/* Argument rules shared by the two step calls. */
-hpo_status check_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
-                      double max_norm)
+/* Argument rules shared by the step calls: the configuration and the groups
+ * (max_group: the largest group index the stepped tensors use). */
+hpo_status check_step_args(const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups, int32_t max_group,
+                           double max_norm)
 {
-    hpo_status st = check_set(s);
-    if (st != HPO_OK)
-        return st;
-    if (s->kind != HPO_SET_ADAM)
-        return fail(HPO_EINVAL, "a Muon set takes hpo_muon_step / hpo_step_device_chain, not the AdamW step");
     if (!cfg)
         return fail(HPO_EINVAL, "cfg is NULL");
     if (cfg->mode != HPO_ADAMW && cfg->mode != HPO_ADAM_L2)
@@ -694,14 +665,25 @@ hpo_status check_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* group
         return fail(HPO_EINVAL, "n_groups must be in [1, %d] (got %d)", HPO_MAX_GROUPS, n_groups);
     if (!groups)
         return fail(HPO_EINVAL, "groups is NULL");
-    if (s->max_group >= n_groups)
-        return fail(HPO_EINVAL, "the set uses group %d but only %d groups were given", s->max_group, n_groups);
+    if (max_group >= n_groups)
+        return fail(HPO_EINVAL, "the set uses group %d but only %d groups were given", max_group, n_groups);
     for (int32_t k = 0; k < n_groups; ++k)
         if (!is_finite(groups[k].lr) || !is_finite(groups[k].weight_decay))
             return fail(HPO_EINVAL, "group %d: lr and weight_decay must be finite", k);
     if (std::isnan(max_norm))
         return fail(HPO_EINVAL, "max_norm is NaN");
     return HPO_OK;
+}
+
+hpo_status check_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                      double max_norm)
+{
+    hpo_status st = check_set(s);
+    if (st != HPO_OK)
+        return st;
+    if (s->kind != HPO_SET_ADAM)
+        return fail(HPO_EINVAL, "a Muon set takes hpo_muon_step / hpo_step_device_chain, not the AdamW step");
+    return check_step_args(cfg, groups, n_groups, s->max_group, max_norm);
 }
 
 /* 1 - beta^t, formed in binary64 and rounded once to fp32. */
@@ -724,7 +706,7 @@ hpo::AdamScalars base_scalars(const hpo_adam_cfg* cfg, const hpo_group* groups, 
     return sc;
 }
 
-}  // namespace
+}  // namespace hpo_host
 
 extern "C" {
 
@@ -770,7 +752,7 @@ hpo_status hpo_scaler_state_init(hpo_scaler_state* d_state, float loss_scale, in
 
 }  // extern "C"
 
-namespace {
+namespace hpo_host {
 
 hpo_status check_scaler_args(const hpo_scaler_cfg* scfg, const hpo_scaler_state* d_state, int64_t t_first,
                              int32_t window)
@@ -822,7 +804,7 @@ hpo::ScalerRule rule_of(const hpo_scaler_cfg* scfg)
     return rule;
 }
 
-}  // namespace
+}  // namespace hpo_host
 
 extern "C" {
 
@@ -840,11 +822,10 @@ hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* 
     const hpo::ScalerRule rule = rule_of(scfg);
     hipStream_t strm = as_stream(stream);
     hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, 1.0f,
-                                         &d_state->inv_scale, s->d_part_sum, s->d_part_flag, strm);
+                                         &d_state->inv_scale, s->parts, strm);
     if (e != hipSuccess)
         return hip_fail(e, "launch norm pass");
-    e = hpo::launch_finalize_state(s->d_part_sum, s->d_part_flag, s->n_parts, stage_sum(s), stage_flag(s), d_state,
-                                   scfg->grad_norm_skip_threshold, strm);
+    e = hpo::launch_finalize_state_sets(&s->parts, 1, d_state, scfg->grad_norm_skip_threshold, strm);
     if (e != hipSuccess)
         return hip_fail(e, "launch norm finalize");
     e = hpo::launch_adam(s->view, s->n_chunks, cfg->mode, sc, strm);
@@ -870,7 +851,7 @@ hpo_status hpo_copy_main_to_model(hpo_set s, void* stream)
 }
 
 hpo_status hpo_grad_global_norm_sets(const hpo_set* sets, int32_t n_sets, float inv_scale, float* d_norm,
-                                     int32_t* d_found_inf, void* stream)
+                                     int32_t* d_found_inf, int64_t* d_num_zeros, void* stream)
 {
     if (!sets || n_sets < 1 || n_sets > hpo::kMaxFoldSets)
         return fail(HPO_EINVAL, "sets must be an array of 1..%d sets (got %d)", hpo::kMaxFoldSets, n_sets);
@@ -878,6 +859,8 @@ hpo_status hpo_grad_global_norm_sets(const hpo_set* sets, int32_t n_sets, float 
         return fail(HPO_EINVAL, "d_norm is NULL");
     if (!std::isfinite(inv_scale))
         return fail(HPO_EINVAL, "inv_scale must be finite");
+    if (d_num_zeros && !aligned(d_num_zeros, 8))
+        return fail(HPO_EINVAL, "d_num_zeros must be 8-byte aligned");
     hpo::Partials p[hpo::kMaxFoldSets];
     for (int32_t k = 0; k < n_sets; ++k) {
         hpo_status st = check_set(sets[k]);
@@ -892,11 +875,11 @@ hpo_status hpo_grad_global_norm_sets(const hpo_set* sets, int32_t n_sets, float 
     for (int32_t k = 0; k < n_sets; ++k) {
         hpo_set s = sets[k];
         hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, inv_scale,
-                                             nullptr, s->d_part_sum, s->d_part_flag, strm);
+                                             nullptr, s->parts, strm);
         if (e != hipSuccess)
             return hip_fail(e, "launch norm pass");
     }
-    hipError_t e = hpo::launch_finalize_sets(p, n_sets, d_norm, d_found_inf, strm);
+    hipError_t e = hpo::launch_finalize_sets(p, n_sets, d_norm, d_found_inf, d_num_zeros, strm);
     if (e != hipSuccess)
         return hip_fail(e, "launch norm finalize");
     return ok();
@@ -934,7 +917,7 @@ hpo_status hpo_step_device_chain(hpo_set adam_set, const hpo_adam_cfg* cfg, cons
         if (!s)
             continue;
         hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, 1.0f,
-                                             &d_state->inv_scale, s->d_part_sum, s->d_part_flag, strm);
+                                             &d_state->inv_scale, s->parts, strm);
         if (e != hipSuccess)
             return hip_fail(e, "launch norm pass");
         p[n_sets++] = partials_of(s);

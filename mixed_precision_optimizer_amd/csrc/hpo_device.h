@@ -27,13 +27,14 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-/* Sum of one double per lane over an NT-lane workgroup: wavefront shuffles,
- * then the wavefront sums through LDS in a fixed order. */
-template <int NT>
-__device__ __forceinline__ double block_sum(double x)
+/* Sum of one value per lane over an NT-lane workgroup: wavefront shuffles,
+ * then the wavefront sums through LDS in a fixed order (T = double for the
+ * norm's partials, integers for counts). */
+template <int NT, typename T = double>
+__device__ __forceinline__ T block_sum(T x)
 {
     constexpr int kWaves = NT / 64;
-    __shared__ double wsum[kWaves];
+    __shared__ T wsum[kWaves];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         x += __shfl_down(x, off, 64);
@@ -42,7 +43,7 @@ __device__ __forceinline__ double block_sum(double x)
     if (lane == 0)
         wsum[wave] = x;
     __syncthreads();
-    double tot = 0.0;
+    T tot = 0;
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)

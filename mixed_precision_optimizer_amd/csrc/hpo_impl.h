@@ -46,7 +46,7 @@ constexpr int64_t kGradSpan = int64_t(1) << HPO_GRAD_SPAN_LOG2;
 constexpr int kFinalBlock = 1024;
 constexpr int64_t kFinalSpan = 8192;
 /* Second-stage partials a set needs for n first-stage partials. */
-inline int64_t stage_parts(int64_t n) { return n > kFinalSpan ? (n + kFinalSpan - 1) / kFinalSpan : 0; }
+constexpr int64_t stage_parts(int64_t n) { return n > kFinalSpan ? (n + kFinalSpan - 1) / kFinalSpan : 0; }
 
 /* One tensor of a set, as the kernels see it (64 bytes). */
 struct TensorDesc {
@@ -106,8 +106,9 @@ struct AdamScalars {
     float bc2_tab[HPO_MAX_WINDOW];
 };
 
-static_assert(sizeof(hpo_scaler_state) == 48, "hpo_scaler_state layout");
+static_assert(sizeof(hpo_scaler_state) == 56, "hpo_scaler_state layout");
 static_assert(offsetof(hpo_scaler_state, applied_steps) == 16, "hpo_scaler_state layout");
+static_assert(offsetof(hpo_scaler_state, num_zeros) == 48, "hpo_scaler_state layout");
 
 /* Scaler rule constants for the end-of-step kernel. */
 struct ScalerRule {
@@ -121,37 +122,50 @@ struct ScalerRule {
 
 enum class GradPass : int { kNorm = 0, kCheck = 1, kUnscale = 2 };
 
-/* The reduction partials of one set, for the finalizers that fold the
- * partials of several sets (an AdamW set and a Muon set stepped together
- * share one norm and one found_inf). */
+/* The reduction partials of one set: one entry per grad-pass workgroup (its
+ * binary64 sum of squares, non-finite flag and zero count), and the
+ * second-stage entries of sets with more than kFinalSpan of them.  The
+ * finalizers fold the partials of several sets (an AdamW set and a Muon set
+ * stepped together share one norm, one found_inf and one zero count). */
 struct Partials {
-    const double* sum;
-    const int32_t* flag;
+    double* sum;
+    int32_t* flag;
+    int64_t* zeros;
     int64_t n;
     double* stage_sum;    /* stage_parts(n) entries */
     int32_t* stage_flag;
+    int64_t* stage_zeros;
 };
 constexpr int kMaxFoldSets = 4;
+/* Device bytes of the partials of a pass with n workgroups (at least one
+ * entry, so an empty set still has a place for its finalize to read). */
+constexpr int64_t kPartialBytes = sizeof(double) + sizeof(int32_t) + sizeof(int64_t);
+inline int64_t partial_entries(int64_t n) { return (n > 0 ? n : 1) + stage_parts(n); }
+/* Carves the partials of an n-workgroup pass out of one buffer of
+ * partial_entries(n) * kPartialBytes bytes, 8-byte aligned. */
+inline Partials carve_partials(void* base, int64_t n)
+{
+    const int64_t first = n > 0 ? n : 1;
+    const int64_t e = partial_entries(n);
+    char* b = static_cast<char*>(base);
+    Partials p;
+    p.sum = reinterpret_cast<double*>(b);
+    p.zeros = reinterpret_cast<int64_t*>(b + e * sizeof(double));
+    p.flag = reinterpret_cast<int32_t*>(b + e * (sizeof(double) + sizeof(int64_t)));
+    p.n = n;
+    p.stage_sum = p.sum + first;
+    p.stage_zeros = p.zeros + first;
+    p.stage_flag = p.flag + first;
+    return p;
+}
 
 /* Launchers (hpo_kernels.hip).  Each enqueues on `stream` and returns the
  * launch status. */
 /* The grad pass runs one workgroup per group of `grad_group` consecutive
- * chunks (n_parts = ceil(n_chunks / grad_group) workgroups and partials). */
+ * chunks (n_parts = ceil(n_chunks / grad_group) workgroups and partials,
+ * written to p's first-stage entries). */
 hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
-                            float inv_scale, const float* d_inv, double* part_sum, int32_t* part_flag,
-                            hipStream_t stream);
-/* Folds n_parts partials into *d_norm = fp32(sqrt(sum)) (skipped when d_norm
- * is null, part_sum is then not read) and *d_found |= any flag; sets with
- * more than kFinalSpan partials go through stage_sum / stage_flag
- * (stage_parts(n_parts) entries). */
-hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
-                           double* stage_sum, int32_t* stage_flag, float* d_norm, int32_t* d_found,
-                           hipStream_t stream);
-/* Same folding, then writes the norm, found_inf and the apply decision
- * (finite and norm <= threshold) into the device step state. */
-hipError_t launch_finalize_state(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
-                                 double* stage_sum, int32_t* stage_flag, hpo_scaler_state* st,
-                                 double threshold, hipStream_t stream);
+                            float inv_scale, const float* d_inv, const Partials& p, hipStream_t stream);
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                        hipStream_t stream);
 hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hysteresis, int64_t applied,
@@ -159,8 +173,15 @@ hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hy
 hipError_t launch_step_end(hpo_scaler_state* st, ScalerRule rule, int64_t t_first, int32_t window,
                            hipStream_t stream);
 hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream);
-/* Folds the partials of n_sets sets (in order) into one norm / flag. */
-hipError_t launch_finalize_sets(const Partials* p, int n_sets, float* d_norm, int32_t* d_found, hipStream_t stream);
+/* Folds the partials of n_sets sets (in order) into *d_norm =
+ * fp32(sqrt(sum)) and the zero count *d_zeros (both skipped when d_norm is
+ * null: the sums and counts are then not read; d_zeros is nullable) and
+ * *d_found |= any flag.  Sets with more than kFinalSpan partials go through
+ * their second-stage entries first. */
+hipError_t launch_finalize_sets(const Partials* p, int n_sets, float* d_norm, int32_t* d_found, int64_t* d_zeros,
+                                hipStream_t stream);
+/* Same folding, then writes the norm, the zero count, found_inf and the
+ * apply decision (finite and norm <= threshold) into the device step state. */
 hipError_t launch_finalize_state_sets(const Partials* p, int n_sets, hpo_scaler_state* st, double threshold,
                                       hipStream_t stream);
 

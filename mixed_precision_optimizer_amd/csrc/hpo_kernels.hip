@@ -311,13 +311,18 @@ __device__ __forceinline__ void* at(void* base, int64_t start)
 /* ---------------------------------------------------------------------- */
 /* grad pass: non-finite flag + sum of squares, or in-place unscale        */
 /* ---------------------------------------------------------------------- */
+/* The norm pass also counts the unscaled grads that are zero (either sign):
+ * the step's num_zeros ([OPT-INFRA] §10.2 return value, §17
+ * log_num_zeros_in_grad), taken on the same values as the norm. */
 template <GradPass PASS>
-__device__ __forceinline__ void grad_elem(float& G, float inv, double& acc, int& bad)
+__device__ __forceinline__ void grad_elem(float& G, float inv, double& acc, int& bad, int& zeros)
 {
     bad |= !__builtin_isfinite(G);
     if constexpr (PASS == GradPass::kNorm) {
-        const double g = static_cast<double>(G * inv);
-        acc = __builtin_fma(g, g, acc); /* g*g is exact in binary64, so this is one rounding of acc + g^2 */
+        const float g = G * inv;
+        zeros += g == 0.0f ? 1 : 0;
+        const double gd = static_cast<double>(g);
+        acc = __builtin_fma(gd, gd, acc); /* gd*gd is exact in binary64, so this is one rounding of acc + g^2 */
     } else if constexpr (PASS == GradPass::kUnscale) {
         G = G * inv;
     }
@@ -327,7 +332,8 @@ __device__ __forceinline__ void grad_elem(float& G, float inv, double& acc, int&
  * elements per lane access, so that each access moves as many bytes as an
  * fp32 one.  Returns the elements it covered. */
 template <GradPass PASS, int GDT>
-__device__ __forceinline__ int64_t grad_body16(void* __restrict__ G, int64_t len, float inv, double& acc, int& bad)
+__device__ __forceinline__ int64_t grad_body16(void* __restrict__ G, int64_t len, float inv, double& acc, int& bad,
+                                               int& zeros)
 {
     constexpr int U = HPO_GRAD_UNROLL;
     const int tid = threadIdx.x;
@@ -346,7 +352,7 @@ __device__ __forceinline__ int64_t grad_body16(void* __restrict__ G, int64_t len
             if (i < nv) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    grad_elem<PASS>(x[u][j], inv, acc, bad);
+                    grad_elem<PASS>(x[u][j], inv, acc, bad, zeros);
                 if constexpr (PASS == GradPass::kUnscale)
                     st8<GDT>(G, i, x[u]);
             }
@@ -356,13 +362,13 @@ __device__ __forceinline__ int64_t grad_body16(void* __restrict__ G, int64_t len
 }
 
 template <GradPass PASS, int GDT>
-__device__ __forceinline__ void grad_range(const Range& r, float inv, double& acc, int& bad)
+__device__ __forceinline__ void grad_range(const Range& r, float inv, double& acc, int& bad, int& zeros)
 {
     void* __restrict__ G = at<GDT>(r.d.grad, r.start);
     const int tid = threadIdx.x;
     int64_t done = 0;
     if (GDT != kF32 && r.d.vec_ok && reinterpret_cast<uintptr_t>(G) % 16 == 0) {
-        done = grad_body16<PASS, GDT>(G, r.len, inv, acc, bad);
+        done = grad_body16<PASS, GDT>(G, r.len, inv, acc, bad, zeros);
     } else if (r.d.vec_ok) {
         constexpr int U = HPO_GRAD_UNROLL;
         const int64_t nv = r.len / kVec;
@@ -378,10 +384,10 @@ __device__ __forceinline__ void grad_range(const Range& r, float inv, double& ac
             for (int u = 0; u < U; ++u) {
                 const int64_t i = base + static_cast<int64_t>(u) * kGradBlock;
                 if (i < nv) {
-                    grad_elem<PASS>(x[u].x, inv, acc, bad);
-                    grad_elem<PASS>(x[u].y, inv, acc, bad);
-                    grad_elem<PASS>(x[u].z, inv, acc, bad);
-                    grad_elem<PASS>(x[u].w, inv, acc, bad);
+                    grad_elem<PASS>(x[u].x, inv, acc, bad, zeros);
+                    grad_elem<PASS>(x[u].y, inv, acc, bad, zeros);
+                    grad_elem<PASS>(x[u].z, inv, acc, bad, zeros);
+                    grad_elem<PASS>(x[u].w, inv, acc, bad, zeros);
                     if constexpr (PASS == GradPass::kUnscale)
                         st4<GDT>(G, i, x[u]);
                 }
@@ -391,33 +397,37 @@ __device__ __forceinline__ void grad_range(const Range& r, float inv, double& ac
     }
     for (int64_t i = done + tid; i < r.len; i += kGradBlock) {
         float x = ld1<GDT>(G, i);
-        grad_elem<PASS>(x, inv, acc, bad);
+        grad_elem<PASS>(x, inv, acc, bad, zeros);
         if constexpr (PASS == GradPass::kUnscale)
             st1<GDT>(G, i, x);
     }
 }
 
-/* One workgroup per group of consecutive chunks; one partial per workgroup. */
+/* One workgroup per group of consecutive chunks; one partial per workgroup:
+ * the flag, and for the norm pass the binary64 sum and the zero count. */
 template <bool FLAT, GradPass PASS, int GDT>
 __global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_chunks, int32_t group,
-                                                          float inv_arg, const float* d_inv, double* part_sum,
-                                                          int32_t* part_flag)
+                                                          float inv_arg, const float* d_inv, Partials p)
 {
     const float inv = d_inv != nullptr ? *d_inv : inv_arg;
     double acc = 0.0;
     int bad = 0;
+    int zeros = 0;
     const int64_t c0 = static_cast<int64_t>(blockIdx.x) * group;
     const int64_t c1 = c0 + group < n_chunks ? c0 + group : n_chunks;
     for (int64_t c = c0; c < c1; ++c)
-        grad_range<PASS, GDT>(chunk_range<FLAT>(sv, c), inv, acc, bad);
+        grad_range<PASS, GDT>(chunk_range<FLAT>(sv, c), inv, acc, bad, zeros);
     const int any_bad = __syncthreads_or(bad);
     if constexpr (PASS == GradPass::kNorm) {
         const double tot = block_sum<kGradBlock>(acc);
-        if (threadIdx.x == 0)
-            part_sum[blockIdx.x] = tot;
+        const int nz = block_sum<kGradBlock, int>(zeros);
+        if (threadIdx.x == 0) {
+            p.sum[blockIdx.x] = tot;
+            p.zeros[blockIdx.x] = nz;
+        }
     }
     if (threadIdx.x == 0)
-        part_flag[blockIdx.x] = any_bad ? 1 : 0;
+        p.flag[blockIdx.x] = any_bad ? 1 : 0;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -427,8 +437,11 @@ __global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_
  * independent accumulators so that kAcc loads are in flight at once; partial
  * i always lands in the same accumulator and the accumulators and lanes are
  * combined in a fixed tree, so the result is reproducible.  Valid in lane 0. */
+/* The zero counts are integers, so their order does not matter.
+ * want_sum == false: flags only (the check pass leaves no sums or counts). */
 __device__ __forceinline__ double reduce_partials(const double* part_sum, const int32_t* part_flag,
-                                                  int64_t lo, int64_t hi, bool want_sum, int& any_bad)
+                                                  const int64_t* part_zeros, int64_t lo, int64_t hi,
+                                                  bool want_sum, int& any_bad, int64_t& zeros)
 {
     constexpr int kAcc = 8;
     double acc[kAcc];
@@ -436,36 +449,42 @@ __device__ __forceinline__ double reduce_partials(const double* part_sum, const 
     for (int k = 0; k < kAcc; ++k)
         acc[k] = 0.0;
     int bad = 0;
+    int64_t nz = 0;
     for (int64_t base = lo + threadIdx.x; base < hi; base += static_cast<int64_t>(kFinalBlock) * kAcc) {
 #pragma unroll
         for (int k = 0; k < kAcc; ++k) {
             const int64_t i = base + static_cast<int64_t>(k) * kFinalBlock;
             if (i < hi) {
-                if (want_sum)
+                if (want_sum) {
                     acc[k] += part_sum[i];
+                    nz += part_zeros[i];
+                }
                 bad |= part_flag[i];
             }
         }
     }
     const double mine = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     any_bad = __syncthreads_or(bad);
-    return block_sum<kFinalBlock>(mine);
+    const double tot = block_sum<kFinalBlock>(mine);
+    zeros = block_sum<kFinalBlock, int64_t>(nz);
+    return tot;
 }
 
 /* First of two reduction stages for large sets: workgroup b folds partials
  * [b * kFinalSpan, (b + 1) * kFinalSpan) into one. */
-__global__ __launch_bounds__(kFinalBlock) void k_reduce_stage(const double* part_sum, const int32_t* part_flag,
-                                                              int64_t n, double* out_sum, int32_t* out_flag)
+__global__ __launch_bounds__(kFinalBlock) void k_reduce_stage(Partials in, int32_t want_sum)
 {
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * kFinalSpan;
-    const int64_t hi = lo + kFinalSpan < n ? lo + kFinalSpan : n;
-    const bool want_sum = part_sum != nullptr;
+    const int64_t hi = lo + kFinalSpan < in.n ? lo + kFinalSpan : in.n;
     int any_bad = 0;
-    const double tot = reduce_partials(part_sum, part_flag, lo, hi, want_sum, any_bad);
+    int64_t zeros = 0;
+    const double tot = reduce_partials(in.sum, in.flag, in.zeros, lo, hi, want_sum != 0, any_bad, zeros);
     if (threadIdx.x == 0) {
-        if (want_sum)
-            out_sum[blockIdx.x] = tot;
-        out_flag[blockIdx.x] = any_bad ? 1 : 0;
+        if (want_sum) {
+            in.stage_sum[blockIdx.x] = tot;
+            in.stage_zeros[blockIdx.x] = zeros;
+        }
+        in.stage_flag[blockIdx.x] = any_bad ? 1 : 0;
     }
 }
 
@@ -473,47 +492,58 @@ __global__ __launch_bounds__(kFinalBlock) void k_reduce_stage(const double* part
 struct Fold {
     const double* sum[kMaxFoldSets];
     const int32_t* flag[kMaxFoldSets];
+    const int64_t* zeros[kMaxFoldSets];
     int64_t n[kMaxFoldSets];
     int32_t count;
 };
 
-__device__ __forceinline__ double fold_sets(const Fold& f, bool want_sum, int& any_bad)
+__device__ __forceinline__ double fold_sets(const Fold& f, bool want_sum, int& any_bad, int64_t& zeros)
 {
     double tot = 0.0;
     any_bad = 0;
+    zeros = 0;
     for (int k = 0; k < f.count; ++k) {
         int bad = 0;
-        const double s = reduce_partials(f.sum[k], f.flag[k], 0, f.n[k], want_sum, bad);
+        int64_t nz = 0;
+        const double s = reduce_partials(f.sum[k], f.flag[k], f.zeros[k], 0, f.n[k], want_sum, bad, nz);
         tot = k == 0 ? s : tot + s;
         any_bad |= bad;
+        zeros += nz;
     }
     return tot;
 }
 
 /* Last stage: one workgroup over all remaining partials, then sqrt and the
- * flag.  d_norm == nullptr: flag only (the sums are not read). */
-__global__ __launch_bounds__(kFinalBlock) void k_finalize(Fold f, float* d_norm, int32_t* d_found)
+ * flag.  d_norm == nullptr: flag only (the sums are not read); d_zeros
+ * (nullable) receives the zero count. */
+__global__ __launch_bounds__(kFinalBlock) void k_finalize(Fold f, float* d_norm, int32_t* d_found, int64_t* d_zeros)
 {
     const bool want_norm = d_norm != nullptr;
     int any_bad = 0;
-    const double tot = fold_sets(f, want_norm, any_bad);
+    int64_t zeros = 0;
+    const double tot = fold_sets(f, want_norm, any_bad, zeros);
     if (threadIdx.x == 0) {
         if (want_norm)
             *d_norm = static_cast<float>(sqrt(tot));
+        if (want_norm && d_zeros != nullptr)
+            *d_zeros = zeros;
         if (d_found != nullptr && any_bad)
             *d_found = 1;
     }
 }
 
-/* Last stage of the device-resident step: norm, found_inf and whether the
- * step will be applied (finite grads, norm not above the skip threshold). */
+/* Last stage of the device-resident step: norm, zero count, found_inf and
+ * whether the step will be applied (finite grads, norm not above the skip
+ * threshold). */
 __global__ __launch_bounds__(kFinalBlock) void k_finalize_state(Fold f, hpo_scaler_state* st, double threshold)
 {
     int any_bad = 0;
-    const double tot = fold_sets(f, true, any_bad);
+    int64_t zeros = 0;
+    const double tot = fold_sets(f, true, any_bad, zeros);
     if (threadIdx.x == 0) {
         const float norm = static_cast<float>(sqrt(tot));
         st->grad_norm = norm;
+        st->num_zeros = zeros;
         st->found_inf = any_bad ? 1 : 0;
         /* the threshold test fails for a NaN norm, so "not above" is spelled out */
         st->applied = (!any_bad && !(static_cast<double>(norm) > threshold)) ? 1 : 0;
@@ -742,16 +772,14 @@ hipError_t launch(void (*kernel)(Args...), int64_t grid, int block, hipStream_t 
 }  // namespace
 
 hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
-                            float inv_scale, const float* d_inv, double* part_sum, int32_t* part_flag,
-                            hipStream_t stream)
+                            float inv_scale, const float* d_inv, const Partials& p, hipStream_t stream)
 {
     if (n_chunks == 0)
         return hipSuccess;
     const int64_t grid = (n_chunks + grad_group - 1) / grad_group;
     const bool flat = sv.is_flat != 0;
 #define HPO_GRAD_LAUNCH_G(F, P, G) \
-    launch(k_grad_pass<F, P, G>, grid, kGradBlock, stream, sv, n_chunks, grad_group, inv_scale, d_inv, part_sum, \
-           part_flag)
+    launch(k_grad_pass<F, P, G>, grid, kGradBlock, stream, sv, n_chunks, grad_group, inv_scale, d_inv, p)
 #define HPO_GRAD_LAUNCH(F, P) (sv.grad_bf16 ? HPO_GRAD_LAUNCH_G(F, P, kBF16) : HPO_GRAD_LAUNCH_G(F, P, kF32))
     switch (pass) {
     case GradPass::kNorm:
@@ -807,11 +835,9 @@ template <bool DEV>
 hipError_t launch_adam_t(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                          hipStream_t stream)
 {
-    switch (sv.state_store) {
-    case kBF16: return launch_adam_g<DEV, kBF16>(sv, n_chunks, mode, sc, stream);
-    case kF16: return launch_adam_g<DEV, kF16>(sv, n_chunks, mode, sc, stream);
-    default: return launch_adam_g<DEV, kF32>(sv, n_chunks, mode, sc, stream);
-    }
+    /* fp32 or bf16 moments (the host refuses fp16 ones) */
+    return sv.state_store == kBF16 ? launch_adam_g<DEV, kBF16>(sv, n_chunks, mode, sc, stream)
+                                   : launch_adam_g<DEV, kF32>(sv, n_chunks, mode, sc, stream);
 }
 
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
@@ -833,21 +859,23 @@ hipError_t fold_inputs(const Partials* p, int n_sets, bool want_sum, Fold& f, hi
         return hipErrorInvalidValue;
     f.count = n_sets;
     for (int k = 0; k < n_sets; ++k) {
-        const double* ps = want_sum ? p[k].sum : nullptr;
+        const double* ps = p[k].sum;
         const int32_t* pf = p[k].flag;
+        const int64_t* pz = p[k].zeros;
         int64_t n = p[k].n;
         if (n > kFinalSpan) {
             const int64_t n_stage = (n + kFinalSpan - 1) / kFinalSpan;
-            hipError_t e = launch(k_reduce_stage, n_stage, kFinalBlock, stream, ps, pf, n, p[k].stage_sum,
-                                  p[k].stage_flag);
+            hipError_t e = launch(k_reduce_stage, n_stage, kFinalBlock, stream, p[k], want_sum ? 1 : 0);
             if (e != hipSuccess)
                 return e;
-            ps = want_sum ? static_cast<const double*>(p[k].stage_sum) : nullptr;
+            ps = p[k].stage_sum;
             pf = p[k].stage_flag;
+            pz = p[k].stage_zeros;
             n = n_stage;
         }
         f.sum[k] = ps;
         f.flag[k] = pf;
+        f.zeros[k] = pz;
         f.n[k] = n;
     }
     return hipSuccess;
@@ -855,13 +883,14 @@ hipError_t fold_inputs(const Partials* p, int n_sets, bool want_sum, Fold& f, hi
 
 }  // namespace
 
-hipError_t launch_finalize_sets(const Partials* p, int n_sets, float* d_norm, int32_t* d_found, hipStream_t stream)
+hipError_t launch_finalize_sets(const Partials* p, int n_sets, float* d_norm, int32_t* d_found, int64_t* d_zeros,
+                                hipStream_t stream)
 {
     Fold f{};
     hipError_t e = fold_inputs(p, n_sets, d_norm != nullptr, f, stream);
     if (e != hipSuccess)
         return e;
-    return launch(k_finalize, 1, kFinalBlock, stream, f, d_norm, d_found);
+    return launch(k_finalize, 1, kFinalBlock, stream, f, d_norm, d_found, d_zeros);
 }
 
 hipError_t launch_finalize_state_sets(const Partials* p, int n_sets, hpo_scaler_state* st, double threshold,
@@ -872,22 +901,6 @@ hipError_t launch_finalize_state_sets(const Partials* p, int n_sets, hpo_scaler_
     if (e != hipSuccess)
         return e;
     return launch(k_finalize_state, 1, kFinalBlock, stream, f, st, threshold);
-}
-
-hipError_t launch_finalize(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
-                           double* stage_sum, int32_t* stage_flag, float* d_norm, int32_t* d_found,
-                           hipStream_t stream)
-{
-    const Partials p{part_sum, part_flag, n_parts, stage_sum, stage_flag};
-    return launch_finalize_sets(&p, 1, d_norm, d_found, stream);
-}
-
-hipError_t launch_finalize_state(const double* part_sum, const int32_t* part_flag, int64_t n_parts,
-                                 double* stage_sum, int32_t* stage_flag, hpo_scaler_state* st,
-                                 double threshold, hipStream_t stream)
-{
-    const Partials p{part_sum, part_flag, n_parts, stage_sum, stage_flag};
-    return launch_finalize_state_sets(&p, 1, st, threshold, stream);
 }
 
 hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hysteresis, int64_t applied,

@@ -48,12 +48,26 @@ struct hpo_set_ {
     int64_t device_bytes = 0;
     hpo::TensorDesc* d_tensors = nullptr;
     hpo::Chunk* d_chunks = nullptr;
-    double* d_part_sum = nullptr;
-    int32_t* d_part_flag = nullptr;
+    void* d_parts = nullptr;  /* the grad pass's reduction partials (hpo::carve_partials) */
+    hpo::Partials parts{};
     hpo_muon_part* muon = nullptr;
 };
 
 namespace hpo_host {
+
+/* What a set stores: the model-param dtype and the widths of the moments,
+ * the main grads and the master. */
+struct Layout {
+    int32_t pdt;         /* HPO_PARAM_BF16 / FP32 / FP16 */
+    int32_t state_bf16;  /* exp_avg / exp_avg_sq are bf16 */
+    int32_t state_fp16;  /* exp_avg / exp_avg_sq are fp16 (refused by decode_dtype) */
+    int32_t grad_bf16;   /* main grads are bf16 */
+    int32_t master_fp16; /* the master is fp16 (bf16 params only) */
+    int64_t mom_bytes() const { return (state_bf16 || state_fp16) ? 2 : 4; }
+    int32_t state_store() const { return state_fp16 ? 2 : (state_bf16 ? 1 : 0); }
+    int64_t grad_bytes() const { return grad_bf16 ? 2 : 4; }
+    int64_t master_bytes() const { return master_fp16 ? 2 : 4; }
+};
 
 hpo_status fail(hpo_status st, const char* fmt, ...);
 hpo_status hip_fail(hipError_t e, const char* what);
@@ -63,12 +77,29 @@ bool is_finite(double x);
 int64_t count_chunks(const int64_t* numel, int32_t n, int64_t ch);
 int32_t choose_chunk(const int64_t* numel, int32_t n);
 void build_chunks(const int64_t* numel, int32_t n, int64_t ch, std::vector<hpo::Chunk>& out);
+/* Chunks per grad-pass workgroup, and the workgroups (= partials) of a pass. */
+int32_t grad_group_of(int32_t chunk_elems, int64_t n_chunks);
+int64_t parts_of(int64_t n_chunks, int32_t group);
+int64_t partial_bytes(int64_t n_parts);
+hpo_status decode_dtype(int32_t param_dtype, Layout& lay);
+/* Pointer rules for one tensor (hpo.h, hpo_set_create_list). */
+hpo_status check_tensor(int32_t i, const Layout& lay, void* param, float* master, float* grad, void* m, void* v,
+                        int64_t numel);
+hpo::TensorDesc make_desc(const Layout& lay, void* param, float* master, float* grad, void* m, void* v,
+                          int64_t numel, int32_t group);
+/* Argument rules of the step calls (the configuration and the groups). */
+hpo_status check_step_args(const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups, int32_t max_group,
+                           double max_norm);
+hpo_status check_scaler_args(const hpo_scaler_cfg* scfg, const hpo_scaler_state* d_state, int64_t t_first,
+                             int32_t window);
+/* The update's scalars for a device-resident step over t_first .. t_first + window - 1. */
+hpo::AdamScalars device_scalars(const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
+                                double max_norm, hpo_scaler_state* d_state, int64_t t_first, int32_t window);
+hpo::ScalerRule rule_of(const hpo_scaler_cfg* scfg);
 hpo_status alloc_partials(hpo_set s);
 void free_set(hpo_set s);
 hpo_status check_set(hpo_set s);
 hipStream_t as_stream(void* stream);
-double* stage_sum(hpo_set s);
-int32_t* stage_flag(hpo_set s);
 hpo::Partials partials_of(hpo_set s);
 
 /* hpo_muon_api.cpp */

@@ -83,7 +83,7 @@ class hpo_scaler_state(ctypes.Structure):
                 ("growth_tracker", ctypes.c_int32), ("hysteresis_tracker", ctypes.c_int32),
                 ("applied_steps", ctypes.c_int64), ("skipped_steps", ctypes.c_int64),
                 ("grad_norm", ctypes.c_float), ("found_inf", ctypes.c_int32),
-                ("applied", ctypes.c_int32), ("error", ctypes.c_int32)]
+                ("applied", ctypes.c_int32), ("error", ctypes.c_int32), ("num_zeros", ctypes.c_int64)]
 
 
 class hpo_scaler_cfg(ctypes.Structure):
@@ -111,7 +111,7 @@ SIGNATURES = {
     "hpo_set_destroy": (_I32, [_P]),
     "hpo_set_info": (_I32, [_P, ctypes.POINTER(hpo_set_info_t)]),
     "hpo_unscale_check_inf": (_I32, [_P, ctypes.c_float, _P, _P]),
-    "hpo_grad_global_norm": (_I32, [_P, ctypes.c_float, _P, _P, _P]),
+    "hpo_grad_global_norm": (_I32, [_P, ctypes.c_float, _P, _P, _P, _P]),
     "hpo_adamw_step": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32,
                               _I64, ctypes.c_float, ctypes.c_double, _P, _P, _P]),
     "hpo_copy_main_to_model": (_I32, [_P, _P]),
@@ -122,7 +122,7 @@ SIGNATURES = {
                                    ctypes.POINTER(_I64), ctypes.POINTER(_I32), _I64, _P]),
     "hpo_muon_step": (_I32, [_P, ctypes.POINTER(hpo_muon_cfg), ctypes.POINTER(hpo_group), _I32, ctypes.c_float,
                              ctypes.c_double, _P, _P, _P]),
-    "hpo_grad_global_norm_sets": (_I32, [ctypes.POINTER(_P), _I32, ctypes.c_float, _P, _P, _P]),
+    "hpo_grad_global_norm_sets": (_I32, [ctypes.POINTER(_P), _I32, ctypes.c_float, _P, _P, _P, _P]),
     "hpo_step_device_chain": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32, _P,
                                      ctypes.POINTER(hpo_muon_cfg), ctypes.POINTER(hpo_group), _I32, ctypes.c_double,
                                      ctypes.POINTER(hpo_scaler_cfg), _P, _I64, _I32, _P]),
@@ -215,6 +215,10 @@ def _norm_ptr(t, what: str = "d_norm") -> ctypes.c_void_p:
     return _dptr(t, what, torch.float32, 4)
 
 
+def _zeros_ptr(t, what: str = "d_num_zeros") -> ctypes.c_void_p:
+    return _dptr(t, what, torch.int64, 8)
+
+
 def _state_ptr(t) -> ctypes.c_void_p:
     return _dptr(t, "d_state", None, SCALER_STATE_BYTES)
 
@@ -260,9 +264,9 @@ def param_dtype_code(dtype) -> int:
 
 
 def _moments_flag(exp_avgs, exp_avg_sqs) -> int:
-    """HPO_STATE_BF16 / HPO_STATE_FP16 when the moments are bf16 / fp16
-    tensors, 0 for fp32; both moments of every tensor must share one of
-    these dtypes."""
+    """HPO_STATE_BF16 when the moments are bf16 tensors, 0 for fp32; fp16
+    moments map to HPO_STATE_FP16, which the library refuses (HPO_EDTYPE).
+    Both moments of every tensor must share one of these dtypes."""
     dts = {t.dtype for t in list(exp_avgs) + list(exp_avg_sqs)}
     if not dts or dts == {torch.float32}:
         return 0
@@ -426,9 +430,11 @@ def hpo_unscale_check_inf(s: HpoSet, inv_scale: float, d_found_inf, stream=None)
     _check(load().hpo_unscale_check_inf(s.handle, inv_scale, flag, _stream(stream)), "hpo_unscale_check_inf")
 
 
-def hpo_grad_global_norm(s: HpoSet, inv_scale: float, d_norm, d_found_inf=None, stream=None) -> None:
-    norm, flag = _norm_ptr(d_norm), _flag_ptr(d_found_inf)
-    _check(load().hpo_grad_global_norm(s.handle, inv_scale, norm, flag, _stream(stream)), "hpo_grad_global_norm")
+def hpo_grad_global_norm(s: HpoSet, inv_scale: float, d_norm, d_found_inf=None, d_num_zeros=None,
+                         stream=None) -> None:
+    norm, flag, zeros = _norm_ptr(d_norm), _flag_ptr(d_found_inf), _zeros_ptr(d_num_zeros)
+    _check(load().hpo_grad_global_norm(s.handle, inv_scale, norm, flag, zeros, _stream(stream)),
+           "hpo_grad_global_norm")
 
 
 def make_cfg(beta1=0.9, beta2=0.999, eps=1e-8, mode=HPO_ADAMW) -> hpo_adam_cfg:
@@ -454,7 +460,7 @@ def hpo_adamw_step(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int]
 
 
 def new_scaler_state(device=None) -> torch.Tensor:
-    """Device buffer for one hpo_scaler_state (48 bytes, 8-byte aligned)."""
+    """Device buffer for one hpo_scaler_state (56 bytes, 8-byte aligned)."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     return torch.zeros(SCALER_STATE_BYTES // 8, dtype=torch.int64, device=dev)
 
@@ -563,10 +569,10 @@ def hpo_muon_step(s: HpoSet, cfg: hpo_muon_cfg, groups, n_groups: Optional[int],
 
 
 def hpo_grad_global_norm_sets(sets: Sequence[HpoSet], inv_scale: float, d_norm, d_found_inf=None,
-                              stream=None) -> None:
+                              d_num_zeros=None, stream=None) -> None:
     handles = (ctypes.c_void_p * max(len(sets), 1))(*[x.handle for x in sets])
-    norm, flag = _norm_ptr(d_norm), _flag_ptr(d_found_inf)
-    _check(load().hpo_grad_global_norm_sets(handles, len(sets), inv_scale, norm, flag, _stream(stream)),
+    norm, flag, zeros = _norm_ptr(d_norm), _flag_ptr(d_found_inf), _zeros_ptr(d_num_zeros)
+    _check(load().hpo_grad_global_norm_sets(handles, len(sets), inv_scale, norm, flag, zeros, _stream(stream)),
            "hpo_grad_global_norm_sets")
 
 

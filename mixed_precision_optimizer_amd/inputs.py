@@ -54,6 +54,7 @@ class Workload:
     inf_step: Optional[int] = None     # 1-based call index whose grads carry one +inf
     flat: bool = False                 # one flat shard instead of a tensor list
     no_decay_1d: bool = True           # 1-D tensors go to the weight_decay = 0 group
+    zero_every: int = 0                # > 0: plant exact zeros and tiny subnormals every this many elements
 
     @property
     def numel(self) -> int:
@@ -121,7 +122,7 @@ def ragged_sizes(n: int = 20000, max_elems: int = 4 * 2 ** 20, seed: int = 4) ->
 def ragged(n: int = 20000, max_elems: int = 4 * 2 ** 20, steps: int = 8, inf_step: int = 3) -> Workload:
     sizes = ragged_sizes(n, max_elems)
     return Workload(f"ragged_{n}", sizes, [2] * n, lr=1e-3, weight_decay=0.1, max_norm=1.0,
-                    loss_scale=65536.0, steps=steps, grad_std=[1e-3] * n, inf_step=inf_step)
+                    loss_scale=65536.0, steps=steps, grad_std=[1e-3] * n, inf_step=inf_step, zero_every=1009)
 
 
 def zero_shard(numel: int = 8_750_000_000, state_dtype: str = "fp32", param_dtype: str = "bf16",
@@ -134,7 +135,7 @@ def zero_shard(numel: int = 8_750_000_000, state_dtype: str = "fp32", param_dtyp
         tag += f"_{master_dtype}_master"
     return Workload(f"zero1_shard_70b_over_8{tag}", [numel], [1], lr=1e-3, weight_decay=0.1, max_norm=1.0,
                     steps=3, grad_std=[1e-4], flat=True, no_decay_1d=False, state_dtype=state_dtype,
-                    param_dtype=param_dtype, grad_dtype=grad_dtype, master_dtype=master_dtype)
+                    param_dtype=param_dtype, grad_dtype=grad_dtype, master_dtype=master_dtype, zero_every=4099)
 
 
 def llama70b_shapes():
@@ -331,9 +332,29 @@ def fill_grads_(bufs: Buffers, k: int) -> None:
                 bufs.view(bufs.grad, i).mul_(stds[i])
     if w.loss_scale is not None:
         bufs.grad.mul_(w.loss_scale)
+    if w.zero_every > 0:
+        plant_zeros_(bufs.grad, w.zero_every, k)
     if w.inf_step is not None and k == w.inf_step:
         ti, e = inf_position(w)
         bufs.grad[bufs.offs[ti] + e] = float("inf")
+
+
+# The stored value 3 * 2^-149, an fp32 subnormal: not zero as stored, zero
+# after an unscale by 2^-16 (3 * 2^-165 is below half the smallest subnormal).
+TINY_SUBNORMAL = float(np.array([3], dtype=np.uint32).view(np.float32)[0])
+
+
+def plant_zeros_(grad: torch.Tensor, every: int, k: int) -> None:
+    """Stored grads that are exactly zero, as real grads are where a weight
+    got no signal (embedding rows of unseen tokens, dead units): in call k,
+    elements o, o + every, o + 2 every, ... with o = (7919 k) mod every
+    become +0 and -0 alternately, and elements o + every/2 + j every become
+    TINY_SUBNORMAL, which is zero only after a 2^-16 unscale.  Written after
+    the loss-scale multiply, so these are the stored values."""
+    o = (7919 * k) % every
+    grad[o::2 * every] = 0.0
+    grad[o + every::2 * every] = -0.0
+    grad[o + every // 2::every] = TINY_SUBNORMAL
 
 
 # ---------------------------------------------------------------------------

@@ -3,11 +3,14 @@
 "02 · Optimizer：算法与 infra" §10.2 / §11.1: zero found_inf, unscale + check,
 global norm, clip, inner step, write-back; a found_inf step returns early,
 with no clip, no inner step and no advance of the step counter, and the
-caller gets (success, grad_norm) back.
+caller gets (success, grad_norm, num_zeros) back, (False, None, None) on a
+skipped step.  num_zeros is reported when log_num_zeros_in_grad is set
+(§17's config field, off by default), else None.
 
 Host logic only.  The computation is the library's: one norm pass that also
-checks for inf/NaN, one finalize, one fused update launched with the device
-flag so it skips itself, then a single 8-byte read of {found_inf, norm}.
+checks for inf/NaN and counts zeros, one finalize, one fused update launched
+with the device flag so it skips itself, then a single 16-byte read of
+{found_inf, norm, num_zeros}.
 """
 from __future__ import annotations
 
@@ -22,47 +25,53 @@ from . import hpo
 class MixedPrecisionAdamW:
     def __init__(self, hset: hpo.HpoSet, groups: Sequence[Tuple[float, float]], *, beta1: float = 0.9,
                  beta2: float = 0.999, eps: float = 1e-8, mode: int = hpo.HPO_ADAMW,
-                 max_norm: float = 1.0, loss_scale: Optional[float] = None, device=None):
+                 max_norm: float = 1.0, loss_scale: Optional[float] = None,
+                 log_num_zeros_in_grad: bool = False, device=None):
         self.set = hset
         self.cfg = hpo.make_cfg(beta1, beta2, eps, mode)
         self.groups, self.n_groups = hpo.make_groups(list(groups))
         self.max_norm = float(max_norm)
         self.loss_scale = loss_scale
+        self.log_num_zeros_in_grad = bool(log_num_zeros_in_grad)
         self.t = 0  # applied steps so far
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-        # [0] found_inf (int32), [1] norm (fp32 bits)
-        self._buf = torch.zeros(2, dtype=torch.int32, device=dev)
-        self._host = torch.zeros(2, dtype=torch.int32, pin_memory=True)
+        # [0] found_inf (int32), [1] norm (fp32 bits), [2:4] num_zeros (int64)
+        self._buf = torch.zeros(4, dtype=torch.int32, device=dev)
+        self._host = torch.zeros(4, dtype=torch.int32, pin_memory=True)
         self.found_inf = self._buf[0:1]
         self.norm = self._buf[1:2].view(torch.float32)
+        self.num_zeros = self._buf[2:4].view(torch.int64)
 
     def inv_scale(self) -> float:
         return 1.0 if self.loss_scale is None else float(np.float32(1.0 / self.loss_scale))
 
     def step(self, stream=None, inplace_unscale: bool = False):
-        """Returns (applied, grad_norm): (False, None) on a skipped step.
+        """Returns (applied, grad_norm, num_zeros): (False, None, None) on a
+        skipped step; num_zeros is None unless log_num_zeros_in_grad is set.
 
         inplace_unscale=True runs the pages' literal sequence (grads are
         unscaled in place first, then norm and step take inv_scale = 1)."""
         inv = self.inv_scale()
         s = torch.cuda.current_stream() if stream is None else stream
+        zeros = self.num_zeros if self.log_num_zeros_in_grad else None
         with torch.cuda.stream(s):
             self._buf.zero_()
             if inplace_unscale:
                 hpo.hpo_unscale_check_inf(self.set, inv, self.found_inf, s)
                 inv = 1.0
-                hpo.hpo_grad_global_norm(self.set, inv, self.norm, None, s)
+                hpo.hpo_grad_global_norm(self.set, inv, self.norm, None, zeros, stream=s)
             else:
-                hpo.hpo_grad_global_norm(self.set, inv, self.norm, self.found_inf, s)
+                hpo.hpo_grad_global_norm(self.set, inv, self.norm, self.found_inf, zeros, stream=s)
             hpo.hpo_adamw_step(self.set, self.cfg, self.groups, self.n_groups, self.t + 1, inv,
                                self.max_norm, self.norm, self.found_inf, s)
             self._host.copy_(self._buf, non_blocking=True)
         s.synchronize()
         found = int(self._host[0]) != 0
         if found:
-            return False, None
+            return False, None, None
         self.t += 1
-        return True, float(self._host[1:2].view(torch.float32)[0])
+        n_zeros = int(self._host[2:4].view(torch.int64)[0]) if self.log_num_zeros_in_grad else None
+        return True, float(self._host[1:2].view(torch.float32)[0]), n_zeros
 
 
 class DeviceAdamW:

@@ -84,7 +84,8 @@ def make_set(bufs, stream=None):
 def make_opt(hset, w, device=None):
     from mixed_precision_optimizer_amd import MixedPrecisionAdamW
     return MixedPrecisionAdamW(hset, w.groups(), beta1=w.beta1, beta2=w.beta2, eps=w.eps, mode=w.mode,
-                               max_norm=w.max_norm, loss_scale=w.loss_scale, device=device)
+                               max_norm=w.max_norm, loss_scale=w.loss_scale, log_num_zeros_in_grad=True,
+                               device=device)
 
 
 def compare_tensor(tag, gpu, orc_new, orc_prev, G, *, inv, clip, C, c64, lr, wd, t, mode, bf16, stats,
@@ -158,12 +159,21 @@ def oracle_sumsq_streamed(orc, grad: torch.Tensor, ranges, inv: float, chunk: in
     device grad buffer: each range is copied to pinned host memory in slices,
     each slice is summed by the oracle's plain loop (up to `threads` slices at
     once), and the slice sums are added in range order."""
+    return oracle_grad_stats_streamed(orc, grad, ranges, inv, chunk, threads)[0]
+
+
+def oracle_grad_stats_streamed(orc, grad: torch.Tensor, ranges, inv: float, chunk: int = 1 << 27,
+                               threads: int = 8):
+    """(sum of squares, zero count) of the unscaled grads over the given
+    ranges, both by the oracle's plain loops over pinned host slices; the
+    slice sums are added in range order, the counts are integers."""
     host = [torch.empty(chunk, dtype=torch.float32, pin_memory=True) for _ in range(threads)]
     pieces = []
     for off, n in ranges:
         for a in range(0, n, chunk):
             pieces.append((off + a, min(chunk, n - a)))
     sums = [0.0] * len(pieces)
+    zeros = [0] * len(pieces)
     busy = [None] * threads
     with cf.ThreadPoolExecutor(max_workers=threads) as pool:
         for k, (off, n) in enumerate(pieces):
@@ -175,6 +185,7 @@ def oracle_sumsq_streamed(orc, grad: torch.Tensor, ranges, inv: float, chunk: in
 
             def work(arr=arr, k=k):
                 sums[k] = orc.sumsq(arr, inv)
+                zeros[k] = orc.count_zeros(arr, inv)
             busy[slot] = pool.submit(work)
         for f in busy:
             if f is not None:
@@ -182,7 +193,7 @@ def oracle_sumsq_streamed(orc, grad: torch.Tensor, ranges, inv: float, chunk: in
     total = 0.0
     for x in sums:
         total = total + x
-    return total
+    return total, sum(zeros)
 
 
 def oracle_any_nonfinite_streamed(orc, grad: torch.Tensor, ranges, chunk: int = 1 << 28) -> bool:

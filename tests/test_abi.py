@@ -36,12 +36,12 @@ def test_exports_every_declared_symbol(H):
         assert hasattr(lib, n), n
         assert n in H.SIGNATURES, f"binding lacks {n}"
     assert set(H.SIGNATURES) == set(names)
-    assert H.hpo_abi_version() == 3
+    assert H.hpo_abi_version() == 4
 
 
 def test_struct_layouts(H):
     """The ctypes mirrors have the C sizes the header fixes."""
-    assert H.SCALER_STATE_BYTES == 48
+    assert H.SCALER_STATE_BYTES == 56
     assert ctypes.sizeof(H.hpo_set_info_t) == 64
     assert ctypes.sizeof(H.hpo_adam_cfg) == 32 and ctypes.sizeof(H.hpo_group) == 16
     assert ctypes.sizeof(H.hpo_scaler_cfg) == 32
@@ -83,9 +83,11 @@ def test_validation_happens_before_any_device_call(H):
     for code in (3, 0x2000, 0x101 | 0x1000, -1):
         st, msg = _flat(H, 16, code, [0x1000] * 5)
         assert st == H.HPO_EDTYPE and "not supported" in msg, code
-    # one moment format at a time
-    st, msg = _flat(H, 16, 0x900, [0x1000] * 5)
-    assert st == H.HPO_EDTYPE and "exclusive" in msg
+    # fp16 moments are refused, alone or with any other flag: without a
+    # per-tensor scale fp16 cannot hold exp_avg_sq at ordinary grad sizes
+    for code in (0x800, 0x900, 0xA00, 0xC00, 0x802):
+        st, msg = _flat(H, 16, code, [0x1000] * 5)
+        assert st == H.HPO_EDTYPE and "fp16 moments" in msg, code
     # an fp16 master only under bf16 params
     for code in (0x401, 0x402, 0x501, 0x601):
         st, msg = _flat(H, 16, code, [0x1000] * 5)
@@ -155,7 +157,7 @@ def test_step_calls_reject_null_set(H):
     cfg = H.make_cfg()
     groups, n = H.make_groups([(1e-3, 0.1)])
     assert L.hpo_adamw_step(None, ctypes.byref(cfg), groups, n, 1, 1.0, 1.0, None, None, None) == H.HPO_EINVAL
-    assert L.hpo_grad_global_norm(None, 1.0, None, None, None) == H.HPO_EINVAL
+    assert L.hpo_grad_global_norm(None, 1.0, None, None, None, None) == H.HPO_EINVAL
     assert L.hpo_unscale_check_inf(None, 1.0, None, None) == H.HPO_EINVAL
     assert L.hpo_copy_main_to_model(None, None) == H.HPO_EINVAL
     assert L.hpo_set_destroy(None) == H.HPO_OK
@@ -193,7 +195,7 @@ def test_chunk_plan_partitions_every_tensor(H, sizes):
     group = max(1, min(65536 // ch, nc // 1024))
     parts = (nc + group - 1) // group
     stage = (parts + 8191) // 8192 if parts > 8192 else 0
-    assert nb == 64 * len(sizes) + 16 * nc + 12 * (max(parts, 1) + stage)
+    assert nb == 64 * len(sizes) + 16 * nc + 20 * (max(parts, 1) + stage)
 
 
 def test_chunk_size_choice(H):
@@ -297,7 +299,7 @@ def test_muon_step_and_ns_validation(H):
     scfg = H.make_scaler_cfg()
     assert L.hpo_step_device_chain(None, None, None, 0, None, None, None, 0, 1.0, ctypes.byref(scfg),
                                    ctypes.c_void_p(0x1000), 1, 1, None) == H.HPO_EINVAL
-    assert L.hpo_grad_global_norm_sets(None, 1, 1.0, ctypes.c_void_p(0x1000), None, None) == H.HPO_EINVAL
+    assert L.hpo_grad_global_norm_sets(None, 1, 1.0, ctypes.c_void_p(0x1000), None, None, None) == H.HPO_EINVAL
 
 
 def test_binding_rejects_mixed_param_dtypes_and_devices(H):
@@ -353,3 +355,4 @@ def test_binding_refuses_host_tensors_as_device_buffers(H):
     g = torch.zeros(4, 4)
     with pytest.raises(ValueError, match="G must be a device tensor"):
         H.hpo_newton_schulz(g, g.clone(), H.make_muon_cfg(), torch.zeros(1 << 16, dtype=torch.uint8))
+

@@ -63,9 +63,12 @@ def _run_parity(H, orc, w, steps=None, stats=None, inplace=False):
         G = _grads_np(bufs)
         prev = [T.copy() for T in Ts]
         r = O.step(G, inv_scale=w.inv_scale())
-        applied, norm = opt.step(inplace_unscale=inplace)
+        applied, norm, zeros = opt.step(inplace_unscale=inplace)
         assert applied == r.applied, f"step {k}: skip decision differs"
         assert opt.t == O.t
+        assert zeros == r.num_zeros, f"step {k}: zero count {zeros} vs {r.num_zeros}"
+        if r.num_zeros:
+            stats.setdefault("zeros", []).append(r.num_zeros)
         if not r.applied:
             for i, T in enumerate(Ts):
                 st = read_state(bufs, i)
@@ -124,7 +127,7 @@ def _edge_workload(mode, loss_scale, inf_step=None, max_norm=1.0, steps=4, param
                     loss_scale=loss_scale, steps=steps,
                     grad_std=[1e-3 * grad_std_scale * (1 + (i % 5)) for i in range(len(sizes))],
                     inf_step=inf_step, param_dtype=param_dtype, state_dtype=state_dtype, grad_dtype=grad_dtype,
-                    master_dtype=master_dtype)
+                    master_dtype=master_dtype, zero_every=97)
 
 
 @pytest.mark.parametrize("mode", [0, 1])
@@ -138,6 +141,7 @@ def test_ragged_tails_groups_scale_and_skip(H, orc, mode, inplace):
     stats, Ts, bufs = _run_parity(H, orc, w, inplace=inplace)
     assert stats["skipped"] == [2]
     assert stats["bit_equal"] == stats["compared"]
+    assert len(stats["zeros"]) == 4   # planted zeros in every applied step, counted bit-exactly
 
 
 @pytest.mark.parametrize("mode", [0, 1])
@@ -155,22 +159,18 @@ def test_reduced_precision_variants(H, orc, mode, pdt, sdt):
 
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("gdt,tdt,sdt", [("bf16", "fp32", "fp32"), ("fp32", "fp16", "fp32"), ("bf16", "fp16", "fp32"),
-                                         ("bf16", "fp16", "bf16"), ("fp32", "fp32", "fp16"), ("bf16", "fp16", "fp16")])
+                                         ("bf16", "fp16", "bf16"), ("fp32", "fp32", "bf16")])
 @pytest.mark.parametrize("inplace", [False, True])
 def test_lower_precision_grads_and_master(H, orc, mode, gdt, tdt, sdt, inplace):
     """bf16 main grads and an fp16 master under bf16 params, alone and
     together with bf16 moments, on the ragged edge sets (loss scale 1024,
     clipping, a no-decay group, a skipped step), with the fused and the
-    in-place unscale, against the oracle's own trajectory.  fp16 moments run
-    with grads 300x larger as well, so that v sits in fp16's normal range
-    rather than underflowing."""
+    in-place unscale, against the oracle's own trajectory."""
     banner(f"lower precision: grads {gdt}, master {tdt}, moments {sdt}, mode {mode}, inplace {inplace}")
-    for scale in ((1.0, 300.0) if sdt == "fp16" else (1.0,)):
-        w = _edge_workload(mode, 1024.0, inf_step=3, steps=6, state_dtype=sdt, grad_dtype=gdt, master_dtype=tdt,
-                           grad_std_scale=scale)
-        stats, Ts, bufs = _run_parity(H, orc, w, inplace=inplace)
-        assert stats["skipped"] == [3]
-        assert stats["bit_equal"] == stats["compared"], scale
+    w = _edge_workload(mode, 1024.0, inf_step=3, steps=6, state_dtype=sdt, grad_dtype=gdt, master_dtype=tdt)
+    stats, Ts, bufs = _run_parity(H, orc, w, inplace=inplace)
+    assert stats["skipped"] == [3]
+    assert stats["bit_equal"] == stats["compared"]
 
 
 @pytest.mark.parametrize("grads", ["fp32", "bf16"])
@@ -279,8 +279,8 @@ def test_nonfinite_anywhere_skips(H, orc, bad, where):
                                        ("p", bufs.param))}
     hset = make_set(bufs)
     opt = make_opt(hset, w)
-    applied, norm = opt.step()
-    assert applied is False and opt.t == 0
+    applied, norm, zeros = opt.step()
+    assert applied is False and opt.t == 0 and norm is None and zeros is None
     assert int(opt.found_inf.item()) == 1
     for k, t in (("m", bufs.master), ("a", bufs.exp_avg), ("b", bufs.exp_avg_sq), ("p", bufs.param)):
         assert torch.equal(before[k].view(torch.int16) if k == "p" else before[k].view(torch.int32),
@@ -444,8 +444,7 @@ def test_flat_and_list_sets_agree_bitwise(H):
 
 @pytest.mark.parametrize("moments,param,grads,master", [("fp32", "bf16", "fp32", "fp32"), ("bf16", "bf16", "fp32", "fp32"),
                                                         ("bf16", "fp16", "fp32", "fp32"), ("fp32", "bf16", "bf16", "fp32"),
-                                                        ("fp32", "bf16", "fp32", "fp16"), ("bf16", "bf16", "bf16", "fp16"),
-                                                        ("fp16", "bf16", "fp32", "fp32"), ("fp16", "bf16", "bf16", "fp16")])
+                                                        ("fp32", "bf16", "fp32", "fp16"), ("bf16", "bf16", "bf16", "fp16")])
 def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param, grads, master):
     """Views that start 1..3 elements into their buffers, as a list set and
     as a flat set: when all five pointers share the element offset (for
@@ -459,7 +458,7 @@ def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param, grads, mas
     rng = np.random.default_rng(6)
     th0 = rng.standard_normal(n).astype(np.float32)
     G = (rng.standard_normal(n) * 1e-3).astype(np.float32)
-    mdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[moments]
+    mdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[moments]
     pdt = torch.float16 if param == "fp16" else torch.bfloat16
     tdt = torch.float16 if master == "fp16" else torch.float32
     gdt = torch.bfloat16 if grads == "bf16" else torch.float32
@@ -491,7 +490,7 @@ def test_misaligned_tensors_peel_or_go_scalar(H, orc, moments, param, grads, mas
         for a, b in zip(res[0], r):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
     T = orc.OTensor.fresh(th0, fp16_param=param == "fp16", state_bf16=moments == "bf16",
-                          fp16_master=master == "fp16", fp16_moments=moments == "fp16")
+                          fp16_master=master == "fp16")
     orc.OracleOptimizer([T], orc.Hyper(mode=1), [(1e-3, 0.1)], max_norm=1.0).step([G_stored])
     for got, want in zip(res[0], (T.theta, T.m, T.v, T.p)):
         assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
@@ -567,7 +566,7 @@ def test_flat_shard_with_param_ranges(H, orc, cut):
         for k in range(3):
             G = (grng.standard_normal(shard_len) * 1e-3 * 1024).astype(np.float32)
             g.copy_(torch.from_numpy(G))
-            applied, norm = opt.step()
+            applied, norm, _ = opt.step()
             assert applied
             states.append((to_np(th), to_np(m), to_np(v), to_np(p), norm))
         results[kind] = states
@@ -770,7 +769,7 @@ def test_zero_grads_leave_state_alone(H, orc):
         from mixed_precision_optimizer_amd import MixedPrecisionAdamW
         opt = MixedPrecisionAdamW(hset, [(1e-3, 0.0)], mode=mode, max_norm=1.0)
         for _ in range(4):
-            applied, norm = opt.step()
+            applied, norm, _ = opt.step()
             assert applied and norm == 0.0
         assert np.array_equal(to_np(th).view(np.uint32), th0.view(np.uint32))
         assert torch.equal(p.view(torch.int16), p0.view(torch.int16))
