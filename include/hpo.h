@@ -337,6 +337,30 @@ hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* 
                            double max_norm, const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state,
                            int64_t t_first, int32_t window, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * device-resident step of one flat shard with no set, so no call, first or
+ * later, allocates, copies or frees anything.  It computes exactly what
+ * hpo_set_create_flat over the same arrays followed by hpo_step_device with
+ * the one group *group (n_groups = 1) computes, bit for bit, with the same
+ * argument rules (pointers as for one tensor of a list set; the state,
+ * t_first and window as for hpo_step_device).  A shard whose pointers are
+ * not on their 4-element vector lines steps element by element (same bits,
+ * slower): there is no table to peel its head into.
+ * The grad pass's reduction partials live in a static device array of
+ * HPO_STATIC_MAX_PARTS entries (20 bytes each, about 5 MiB) that each GPU the
+ * library runs on holds until the process ends; a shard whose plan needs
+ * more partials (more than about HPO_STATIC_MAX_PARTS * 65536, i.e. 1.7e10
+ * elements) is refused with HPO_EINVAL before anything is enqueued.  All
+ * calls on one GPU share that array: calls that overlap on one GPU (two
+ * streams or two threads at once) race on it and must be ordered by the
+ * caller. */
+#define HPO_STATIC_MAX_PARTS (1 << 18)
+hpo_status hpo_step_device_flat_static(int64_t numel, int32_t param_dtype, void* param, float* main_param,
+                                       float* main_grad, void* exp_avg, void* exp_avg_sq, const hpo_adam_cfg* cfg,
+                                       const hpo_group* group, double max_norm, const hpo_scaler_cfg* scfg,
+                                       hpo_scaler_state* d_state, int64_t t_first, int32_t window, void* stream);
+
 /* Master -> model copy alone: param = bf16_rne(main_param) for every element
  * of a bf16 set ([OPT-INFRA] §9.2, the write-back row; the same conversion the
  * step fuses).  A no-op for fp32 sets. */

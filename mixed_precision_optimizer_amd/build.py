@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 
 # gfx950 kernel files and host files of libhpo
-DEVICE_SOURCES = ("hpo_kernels.hip", "hpo_muon.hip")
+DEVICE_SOURCES = ("hpo_kernels.hip", "hpo_muon.hip", "hpo_static.hip")
 HOST_SOURCES = ("hpo_api.cpp", "hpo_muon_api.cpp")
 
 

@@ -115,6 +115,9 @@ SIGNATURES = {
     "hpo_adamw_step": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32,
                               _I64, ctypes.c_float, ctypes.c_double, _P, _P, _P]),
     "hpo_copy_main_to_model": (_I32, [_P, _P]),
+    "hpo_step_device_flat_static": (_I32, [_I64, _I32, _P, _P, _P, _P, _P, ctypes.POINTER(hpo_adam_cfg),
+                                           ctypes.POINTER(hpo_group), ctypes.c_double, ctypes.POINTER(hpo_scaler_cfg),
+                                           _P, _I64, _I32, _P]),
     "hpo_scaler_state_init": (_I32, [_P, ctypes.c_float, _I32, _I64, _P]),
     "hpo_step_device": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32, ctypes.c_double,
                                ctypes.POINTER(hpo_scaler_cfg), _P, _I64, _I32, _P]),
@@ -490,6 +493,35 @@ def hpo_step_device(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int
     state = _state_ptr(d_state)
     _check(load().hpo_step_device(s.handle, ctypes.byref(cfg), groups, n_groups, max_norm, ctypes.byref(scfg),
                                   state, t_first, window, _stream(stream)), "hpo_step_device")
+
+
+HPO_STATIC_MAX_PARTS = 1 << 18
+
+
+def hpo_step_device_flat_static(param: Optional[torch.Tensor], main_param: torch.Tensor, main_grad: torch.Tensor,
+                                exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, cfg: hpo_adam_cfg, group: tuple,
+                                max_norm: float, scfg: hpo_scaler_cfg, d_state, t_first: int, window: int,
+                                param_dtype: Optional[int] = None, stream=None) -> None:
+    """hpo_set_create_flat + hpo_step_device over one group, with no set and
+    no device allocation (the library keeps the reduction partials in a
+    static device array); `group` is (lr, weight_decay)."""
+    mflag, tdt, gdt, mdt = _storage_flags([main_param], [main_grad], [exp_avg], [exp_avg_sq])
+    n = main_param.numel()
+    ptrs = []
+    for what, t, dt in (("main_param", main_param, tdt), ("main_grad", main_grad, gdt),
+                        ("exp_avg", exp_avg, mdt), ("exp_avg_sq", exp_avg_sq, mdt)):
+        if t.numel() != n:
+            raise ValueError(f"{what} has {t.numel()} elements, main_param {n}")
+        ptrs.append(_dptr(t, what, dt))
+    if param_dtype is None:
+        param_dtype = HPO_PARAM_FP32 if param is None else param_dtype_code(param.dtype)
+    if param is not None and param.numel() != n:
+        raise ValueError("param must have main_param's size")
+    p_ptr = _dptr(param, "param")
+    g = hpo_group(*group)
+    _check(load().hpo_step_device_flat_static(n, param_dtype | mflag, p_ptr, *ptrs, ctypes.byref(cfg), ctypes.byref(g),
+                                              max_norm, ctypes.byref(scfg), _state_ptr(d_state), t_first, window,
+                                              _stream(stream)), "hpo_step_device_flat_static")
 
 
 def hpo_copy_main_to_model(s: HpoSet, stream=None) -> None:

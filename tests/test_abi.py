@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(H):
     names = _declared()
-    assert len(names) == 24
+    assert len(names) == 25
     lib = H.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -356,3 +356,29 @@ def test_binding_refuses_host_tensors_as_device_buffers(H):
     with pytest.raises(ValueError, match="G must be a device tensor"):
         H.hpo_newton_schulz(g, g.clone(), H.make_muon_cfg(), torch.zeros(1 << 16, dtype=torch.uint8))
 
+
+def test_static_step_refuses_a_shard_beyond_its_partials(H):
+    """The no-allocation device step keeps its reduction partials in a static
+    array of HPO_STATIC_MAX_PARTS entries: a shard whose plan needs more is
+    refused on the host, before the device is touched."""
+    L = H.load()
+    assert H.HPO_STATIC_MAX_PARTS == 1 << 18
+    cfg = H.make_cfg()
+    grp = H.hpo_group(1e-3, 0.1)
+    scfg = H.make_scaler_cfg()
+    ptrs = [ctypes.c_void_p(0x1000 * k) for k in range(1, 6)]
+    for n, ok in ((H.HPO_STATIC_MAX_PARTS * 65536 + 65536 * 16, False), (-1, False)):
+        st = L.hpo_step_device_flat_static(n, 0, *ptrs, ctypes.byref(cfg), ctypes.byref(grp), 1.0,
+                                           ctypes.byref(scfg), ctypes.c_void_p(0x6000), 1, 1, None)
+        assert st == H.HPO_EINVAL, n
+    st = L.hpo_step_device_flat_static(H.HPO_STATIC_MAX_PARTS * 65536 + 65536 * 16, 0, *ptrs, ctypes.byref(cfg),
+                                       ctypes.byref(grp), 1.0, ctypes.byref(scfg), ctypes.c_void_p(0x6000), 1, 1,
+                                       None)
+    assert "static scratch holds at most" in H.hpo_last_error()
+    # the same argument rules as the set-based step
+    st = L.hpo_step_device_flat_static(1024, 0x800, *ptrs, ctypes.byref(cfg), ctypes.byref(grp), 1.0,
+                                       ctypes.byref(scfg), ctypes.c_void_p(0x6000), 1, 1, None)
+    assert st == H.HPO_EDTYPE
+    st = L.hpo_step_device_flat_static(1024, 0, *ptrs, ctypes.byref(cfg), ctypes.byref(grp), 1.0,
+                                       ctypes.byref(scfg), ctypes.c_void_p(0x6000), 1, 0, None)
+    assert st == H.HPO_EINVAL and "window" in H.hpo_last_error()
