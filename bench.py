@@ -16,9 +16,14 @@ clips to 1.0, lr 1e-3, wd 0.1.
 Prints ONE JSON line.  `value` is G params/s of the full step; HBM figures use
 34 algorithmic bytes per element per step (30 for the fused update, 4 for the
 grad pass).  The roofline block is for the dominant kernel (the fused update,
-30 B/elem), timed with HIP events on the stream it runs on.  cpu_baseline is
-the CPU oracle (single-threaded C, not tuned) on a bounded slice of the same
-inputs.
+30 B/elem), timed with HIP events on the stream it runs on, against the
+published 8 TB/s and against the practical ceiling of its read/write mix (the
+library's stream probe: the same accesses with no arithmetic, timed the same
+way); the shader clock under load comes from a committed counter summary.
+cpu_baseline is the CPU oracle (its C routines unchanged, over the host
+cores in disjoint slices) on a contiguous 1/8 slice of the same inputs, the
+median of 5 steps after 1 warm-up; cpu_baseline_1thread is the same on one
+core over a 1/64 slice.
 """
 from __future__ import annotations
 
@@ -94,6 +99,26 @@ def measured_traffic(workload_name, numel):
     return traffic if digest == kernel_digest() else None
 
 
+CLOCK_SUMMARY = os.path.join(ROOT, "profiles", "pmc_clock_zero_shard_70b_over_8.txt")
+
+
+def measured_clock(workload_name, numel):
+    """Shader clock (GHz) under the update kernel and the grad pass from the
+    committed rocprofv3 GRBM_GUI_ACTIVE summary of the default shard, or None
+    when it was taken on kernels that have changed since."""
+    if workload_name != "zero1_shard_70b_over_8" or numel != 8_750_000_000 or not os.path.exists(CLOCK_SUMMARY):
+        return None
+    digest, clk = None, {}
+    with open(CLOCK_SUMMARY) as f:
+        for line in f:
+            if "kernel source digest" in line:
+                digest = line.rsplit(":", 1)[1].strip()
+            if line.startswith("clock_GHz "):
+                _, kern, val = line.split()
+                clk[kern] = float(val)
+    return clk if digest == kernel_digest() and clk else None
+
+
 MUON_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_hbm_traffic_llama8b_adamw_muon_chain.txt")
 MUON_SOURCES = ("mixed_precision_optimizer_amd/csrc/hpo_muon.hip", "mixed_precision_optimizer_amd/csrc/hpo_muon_impl.h")
 
@@ -129,7 +154,10 @@ def measured_muon_traffic():
 
 
 def host_cpu_model() -> str:
-    """The host CPU's model name (Linux /proc/cpuinfo), for the CPU baselines."""
+    """The host CPU's model name (lscpu's, else /proc/cpuinfo's), for the CPU baselines."""
+    name = host_cpu().get("model_name")
+    if name:
+        return name
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -138,6 +166,39 @@ def host_cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def host_cpu() -> dict:
+    """lscpu's model name, sockets, physical cores and logical CPUs, and the
+    CPUs this process may run on."""
+    import subprocess
+    out = {}
+    try:
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        txt = ""
+    fields = {}
+    for line in txt.splitlines():
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if "Model name" in fields:
+        out["model_name"] = fields["Model name"]
+    try:
+        sockets = int(fields["Socket(s)"])
+        cores = int(fields["Core(s) per socket"])
+        out["sockets"] = sockets
+        out["physical_cores"] = sockets * cores
+        out["threads_per_core"] = int(fields.get("Thread(s) per core", "1"))
+    except (KeyError, ValueError):
+        pass
+    if "CPU(s)" in fields:
+        out["logical_cpus"] = fields["CPU(s)"]
+    try:
+        out["cpus_allowed"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        out["cpus_allowed"] = os.cpu_count()
+    return out
 
 
 def device_info(torch) -> dict:
@@ -176,9 +237,13 @@ def parse():
                     help="main grad storage of the flat shard")
     ap.add_argument("--master-dtype", default="fp32", choices=["fp32", "fp16"],
                     help="master storage of the flat shard (fp16 needs bf16 params)")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 28,
-                    help="elements of the workload the CPU oracle steps (0: skip)")
-    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-sample", type=int, default=-1,
+                    help="elements of the workload the CPU oracle steps on all cores (-1: a contiguous 1/8 "
+                         "of the workload; 0: skip); the one-core baseline takes 1/8 of that")
+    ap.add_argument("--cpu-steps", type=int, default=5, help="timed oracle steps (after one warm-up step)")
+    ap.add_argument("--cpu-threads", type=int, default=16,
+                    help="threads of the all-core oracle baseline (the host share of one GPU; capped to the "
+                         "CPUs this process may use)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="N",
                     help="only run a plain device copy of N fp32 elements (known bytes: 4N read, 4N "
                          "written) five times; used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -242,29 +307,35 @@ def cpu_sample(bufs, n_sample):
     return get(bufs.master), get(bufs.exp_avg), get(bufs.exp_avg_sq), bits(bufs.param), get(bufs.grad)
 
 
+def _sample_note(n, w):
+    frac = w.numel / n if n else 0
+    return (f"a contiguous 1/{frac:.0f} slice ({n} elements, the first of the set) of the same workload"
+            if abs(frac - round(frac)) < 1e-9 else f"the first {n} elements of the same workload")
+
+
 def cpu_baseline(sample, w, steps):
-    """The oracle's full step (check, norm, clip, update, RNE) on the sample."""
+    """The oracle's full step (check, norm, clip, update, RNE) on the sample,
+    on one core: one warm-up step, then the median of `steps` steps."""
     import oracle
     theta, m, v, p, G = sample
     n = theta.size
-    T = oracle.OTensor(theta, m, v, p, 0, w.param_dtype == "fp16", w.master_dtype == "fp16",
-                       w.state_dtype == "fp16")
+    T = oracle.OTensor(theta, m, v, p, 0, w.param_dtype == "fp16", w.master_dtype == "fp16", False)
     O = oracle.OracleOptimizer([T], oracle.Hyper(w.beta1, w.beta2, w.eps, w.mode), w.groups(),
                                max_norm=w.max_norm)
     times = []
-    for _ in range(steps):
+    for k in range(steps + 1):
         t0 = time.perf_counter()
         O.step([G], inv_scale=w.inv_scale())
-        times.append(time.perf_counter() - t0)
+        if k > 0:
+            times.append(time.perf_counter() - t0)
     dt = statistics.median(times)
-    gps = n / dt / 1e9
-    return {"value": round(gps, 4), "unit": "G params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} elements of the same workload (initial master/m/v, param, step-1 grads, "
-                      f"as stored), full step (inf check, binary64 norm, clip, AdamW, RNE stores), median of {steps} "
-                      f"steps, single-threaded C ({os.cpu_count()} host CPUs visible); "
-                      f"{(update_bytes(w) + gradpass_bytes(w)) * n / dt / 1e9:.2f} GB/s at "
-                      f"{update_bytes(w) + gradpass_bytes(w)} B/elem",
-            "ms_per_step": round(dt * 1e3, 2), "cpu_model": host_cpu_model()}
+    bpe = update_bytes(w) + gradpass_bytes(w)
+    return {"value": round(n / dt / 1e9, 4), "unit": "G params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{_sample_note(n, w)}: initial master/m/v, param and step-1 grads as stored; the full step "
+                      f"(inf check, binary64 norm, clip, AdamW, RNE stores) in single-threaded C; median of {steps} "
+                      f"steps after 1 warm-up; {bpe * n / dt / 1e9:.2f} GB/s at {bpe} B/elem",
+            "ms_per_step": round(dt * 1e3, 2), "ms_min": round(min(times) * 1e3, 2),
+            "ms_max": round(max(times) * 1e3, 2), "cpu_model": host_cpu_model()}
 
 
 def cpu_baseline_threads(sample, w, steps, threads):
@@ -272,7 +343,7 @@ def cpu_baseline_threads(sample, w, steps, threads):
     slices at once (ctypes releases the GIL in the oracle's C calls): the
     inf check and binary64 sums per slice, their sum in slice order, the
     clip decision, then each slice's update.  The oracle's code is unchanged;
-    only the work is split."""
+    only the work is split.  One warm-up step, then the median of `steps`."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -282,13 +353,13 @@ def cpu_baseline_threads(sample, w, steps, threads):
     n = theta.size
     cuts = [n * k // threads for k in range(threads + 1)]
     parts = [(oracle.OTensor(theta[a:b], m[a:b], v[a:b], p[a:b], 0, w.param_dtype == "fp16",
-                             w.master_dtype == "fp16", w.state_dtype == "fp16"), oracle.grad_f32(G[a:b]))
+                             w.master_dtype == "fp16", False), oracle.grad_f32(G[a:b]))
              for a, b in zip(cuts[:-1], cuts[1:])]
     hyper = oracle.Hyper(w.beta1, w.beta2, w.eps, w.mode)
     inv32 = float(np.float32(w.inv_scale()))
     times, t = [], 0
     with ThreadPoolExecutor(threads) as pool:
-        for _ in range(steps):
+        for k in range(steps + 1):
             t0 = time.perf_counter()
             found = any(pool.map(lambda tg: oracle.any_nonfinite(tg[1]), parts))
             if not found:
@@ -300,12 +371,19 @@ def cpu_baseline_threads(sample, w, steps, threads):
                 t += 1
                 list(pool.map(lambda tg: oracle.apply_update([tg[0]], [tg[1]], hyper, w.groups(), t, inv32,
                                                              do_clip, C, c64), parts))
-            times.append(time.perf_counter() - t0)
+            if k > 0:
+                times.append(time.perf_counter() - t0)
     dt = statistics.median(times)
+    bpe = update_bytes(w) + gradpass_bytes(w)
+    hc = host_cpu()
     return {"value": round(n / dt / 1e9, 4), "unit": "G params/s", "cores": threads, "kind": "oracle",
-            "sample": f"the same {n} elements, the oracle's inf check, binary64 sums and update over {threads} "
-                      f"slices in {threads} threads (the oracle's C routines unchanged), median of {steps} steps",
-            "ms_per_step": round(dt * 1e3, 2), "cpu_model": host_cpu_model()}
+            "sample": f"{_sample_note(n, w)}: the oracle's inf check, binary64 sums and update over {threads} "
+                      f"slices in {threads} threads (its C routines unchanged); median of {steps} steps after 1 "
+                      f"warm-up; {bpe * n / dt / 1e9:.2f} GB/s at {bpe} B/elem",
+            "ms_per_step": round(dt * 1e3, 2), "ms_min": round(min(times) * 1e3, 2),
+            "ms_max": round(max(times) * 1e3, 2), "cpu_model": host_cpu_model(),
+            "host": {k: hc[k] for k in ("physical_cores", "sockets", "threads_per_core", "logical_cpus",
+                                        "cpus_allowed") if k in hc}}
 
 
 def main():
@@ -332,7 +410,8 @@ def main():
     bufs = inputs.allocate(w, dev)
     inputs.fill_grads_(bufs, 1)
     torch.cuda.synchronize()
-    sample = cpu_sample(bufs, args.cpu_sample) if args.cpu_sample > 0 else None
+    n_cpu = N // 8 if args.cpu_sample < 0 else args.cpu_sample
+    sample = cpu_sample(bufs, n_cpu) if n_cpu > 0 else None
     hset = make_set(bufs)
     info = hset.info()
     log(f"set: chunk {info.chunk_elems} elements, {info.n_chunks} chunks, {info.device_bytes} B of tables")
@@ -365,6 +444,22 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the practical ceiling of the update's read/write mix: the library's probe
+    # with the same accesses and no arithmetic, on the same buffers (it leaves
+    # the state as it is), timed with HIP events on the same stream
+    probe_ms = None
+    try:
+        hpo.hpo_stream_probe(hset, stream)
+    except hpo.HpoError:
+        log("stream probe: not applicable to this storage")
+    else:
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in pev:
+            a.record(stream)
+            hpo.hpo_stream_probe(hset, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        probe_ms = statistics.median(a.elapsed_time(b) for a, b in pev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -383,6 +478,8 @@ def main():
     step_gbps = (ub + gradpass_bytes(w)) * N / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(w.name, N)
     traffic_gb = None if traffic is None else round(traffic / 1e9, 3)
+    ceil_gbps = None if probe_ms is None else ub * N / (probe_ms * 1e-3) / 1e9
+    clock = measured_clock(w.name, N)
     log(f"norm {norm_v:.6g}, applied steps {t_applied}; step {ms_step:.3f} ms, update {upd:.3f} ms "
         f"({upd_gbps:.0f} GB/s), grad pass {gp:.3f} ms ({gp_gbps:.0f} GB/s)")
     out = {
@@ -413,7 +510,17 @@ def main():
                      "frac": round(upd_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_gb,
                      "traffic_unit": "GB per launch of the update kernel (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, "
                                      "scales from a device copy of known size); algorithmic: "
-                                     f"{ub * N / 1e9:.1f} GB"},
+                                     f"{ub * N / 1e9:.1f} GB",
+                     "ceiling": None if ceil_gbps is None else round(ceil_gbps, 1),
+                     "frac_of_ceiling": None if ceil_gbps is None else round(upd_gbps / ceil_gbps, 4),
+                     "ceiling_unit": "GB/s of the library's stream probe: the update's accesses (same chunks, launch "
+                                     "shape, streaming loads/stores) with no arithmetic, same buffers, HIP events, "
+                                     "median of 5",
+                     "clock_GHz": clock,
+                     "clock_unit": "shader clock under each kernel, rocprofv3 GRBM_GUI_ACTIVE per XCD over the "
+                                   "dispatch time (committed summary of the same kernels, else null)",
+                     "target": {"frac_of_peak_full_step": 0.80,
+                                "met": bool(step_gbps / PEAK_HBM_GBPS >= 0.80)}},
         "device": device_info(torch),
     }
     # the same step with the scaler, skip decision and step counter on the
@@ -461,11 +568,13 @@ def main():
                                  "HIP graph (torch.cuda.CUDAGraph) and replayed; captures and state reads timed"}
     hset.close()
     if sample is not None:
-        log(f"cpu baseline on {sample[0].size} elements")
-        out["cpu_baseline"] = cpu_baseline(sample, w, args.cpu_steps)
-        threads = max(1, min(16, os.cpu_count() or 1))   # the host share of one GPU
-        log(f"cpu baseline, {threads} threads")
-        out["cpu_baseline_all_cores"] = cpu_baseline_threads(sample, w, args.cpu_steps, threads)
+        threads = max(1, min(args.cpu_threads, host_cpu().get("cpus_allowed") or 1))
+        log(f"cpu baseline on {sample[0].size} elements, {threads} threads")
+        out["cpu_baseline"] = cpu_baseline_threads(sample, w, args.cpu_steps, threads)
+        one = tuple(a[:max(1, a.size // 8)].copy() for a in sample)
+        del sample
+        log(f"cpu baseline on {one[0].size} elements, 1 thread")
+        out["cpu_baseline_1thread"] = cpu_baseline(one, w, args.cpu_steps)
     print(json.dumps(out), flush=True)
 
 
@@ -488,16 +597,17 @@ def muon_cpu_baseline(matrices, steps=1):
     G = inputs.seeded_matrix((r, c), 6, std)
     T = mu.OMatrix.fresh(W)
     times = []
-    for _ in range(steps):
+    for k in range(steps + 1):
         t0 = time.perf_counter()
         mu.muon_matrix_step(T, G, mu.MuonCfg(), 1e-3, 0.1, 1.0, False, 1.0, "bf16")
-        times.append(time.perf_counter() - t0)
+        if k > 0:
+            times.append(time.perf_counter() - t0)
     ms = 1e3 * statistics.median(times)
     threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
     return {"value": round(r * c / (ms * 1e-3) / 1e9, 5), "unit": "G params/s", "cores": threads, "kind": "oracle",
             "sample": f"one {r}x{c} Muon matrix ({name}) of the same workload: momentum, 5-step bf16-reading NS "
                       f"(numpy binary64 matmuls over bf16 values, {threads} BLAS threads), decayed scaled update, "
-                      f"bf16 write-back; median of {steps}", "ms_per_step": round(ms, 2),
+                      f"bf16 write-back; median of {steps} after 1 warm-up", "ms_per_step": round(ms, 2),
             "cpu_model": host_cpu_model()}
 
 
@@ -616,7 +726,7 @@ def main_muon(args, dev):
             f"of known size); algorithmic {tr[1] / 1e9:.3f} GB: B and X read once, X' and X'^T written")
     aset.close()
     mset.close()
-    if args.cpu_sample > 0:
+    if args.cpu_sample != 0:
         out["cpu_baseline"] = muon_cpu_baseline(mats, args.cpu_steps)
     print(json.dumps(out), flush=True)
 

@@ -49,8 +49,9 @@
 extern "C" {
 #endif
 
-/* 4: the norm calls and the device step state report the grads' zero count. */
-#define HPO_ABI_VERSION 4
+/* 5: the device step state (64 bytes) reports the grads' zero count and the
+ *    scale the step unscaled with; the norm calls report the zero count. */
+#define HPO_ABI_VERSION 5
 /* Most parameter groups one step can take (per-group lr / weight decay). */
 #define HPO_MAX_GROUPS 16
 
@@ -272,13 +273,15 @@ hpo_status hpo_adamw_step(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* g
  * tables travel in the kernel arguments (2 KB at 256). */
 #define HPO_MAX_WINDOW 256
 
-/* Loss-scaler and step state kept in device memory (56 bytes, caller-owned,
+/* Loss-scaler and step state kept in device memory (64 bytes, caller-owned,
  * 8-byte aligned).  The caller multiplies its loss by loss_scale before
  * backward ([OPT-INFRA] §10.2: the loss is scaled, the grads are unscaled
- * before the step) and may read the struct back at any time after a sync. */
+ * before the step) and may read the struct back at any time after a sync.
+ * After a step, loss_scale / inv_scale hold the scale for the next step
+ * and step_inv_scale the one this step's grads were unscaled with. */
 typedef struct {
     float loss_scale;           /* S */
-    float inv_scale;            /* fp32(1 / S), formed in binary64; what the passes multiply by */
+    float inv_scale;            /* fp32(1 / S), formed in binary64; what the next step multiplies by */
     int32_t growth_tracker;     /* clean steps since the last growth or non-finite step */
     int32_t hysteresis_tracker; /* non-finite steps still tolerated before a back-off */
     int64_t applied_steps;      /* steps applied so far = t of the last applied step */
@@ -288,6 +291,8 @@ typedef struct {
     int32_t applied;            /* the last step was applied */
     int32_t error;              /* sticky: a step's t fell outside the window it was given */
     int64_t num_zeros;          /* zeros among the last step's unscaled grads (as hpo_grad_global_norm) */
+    float step_inv_scale;       /* the inv_scale the last step's grads were unscaled with */
+    int32_t reserved;           /* 0 */
 } hpo_scaler_state;
 
 /* Scaler and skip policy ([OPT-INFRA] §10.1 scaler rules and defaults; §11.4
@@ -320,10 +325,11 @@ hpo_status hpo_scaler_state_init(hpo_scaler_state* d_state, float loss_scale, in
                                  int64_t applied_steps, void* stream);
 
 /* One whole step with everything decided on the device: the grad pass (check
- * + norm, multiplying by d_state->inv_scale), the finalize (norm, found_inf,
- * skip decision), the fused clip + update + write-back (run only when the
- * step is applied, with t = applied_steps + 1), and a one-lane kernel that
- * advances the counters and the scaler.  Nothing is read back.
+ * + norm + zero count, multiplying by d_state->inv_scale), the finalize
+ * (norm, found_inf, the skip decision, then the counters and the scaler
+ * rule), and the fused clip + update + write-back, run only when the step is
+ * applied, with t = the new applied_steps and the step's inv_scale.
+ * Nothing is read back.
  * The bias corrections 1 - beta^t are formed on the host in binary64 and
  * rounded to fp32 for t = t_first .. t_first + window - 1, where t_first is
  * applied_steps + 1 as of the caller's last read of the state and window
@@ -484,6 +490,20 @@ hpo_status hpo_step_device_chain(hpo_set adam_set, const hpo_adam_cfg* cfg, cons
 hpo_status hpo_newton_schulz(const float* d_G, int64_t rows, int64_t cols, const hpo_muon_cfg* cfg, float* d_out,
                              void* d_workspace, int64_t workspace_bytes, void* stream);
 hpo_status hpo_newton_schulz_workspace(int64_t rows, int64_t cols, int64_t* out_bytes);
+
+/* Measurement only, not part of a step: the fused update's memory traffic
+ * with none of its arithmetic, on a flat set of fp32 grads, master and
+ * moments with 16-bit params whose pointers are on their 4-element vector
+ * lines (else HPO_EINVAL).  Each chunk's grad, master, exp_avg and
+ * exp_avg_sq are read (16 bytes per element) and master, exp_avg, exp_avg_sq
+ * written back unchanged and the param written as the 16-bit rounding of
+ * the master (14 bytes), with the update's launch shape and streaming
+ * accesses; chunk tails that are not whole vectors are skipped.  The
+ * state is left as it was wherever param already equals the rounding of the
+ * master, which every step keeps.  Timing it gives the practical HBM
+ * ceiling of the update's read/write mix, which the roofline of the update
+ * is reported against besides the published peak. */
+hpo_status hpo_stream_probe(hpo_set s, void* stream);
 
 /* Opt-in timing of a Muon set's launches (for measurement, not for the
  * hot loop): while enabled, every Muon update of the set (hpo_muon_step,

@@ -609,15 +609,12 @@ hpo_status hpo_unscale_check_inf(hpo_set s, float inv_scale, int32_t* d_found_in
     if (!std::isfinite(inv_scale))
         return fail(HPO_EINVAL, "inv_scale must be finite");
     const hpo::GradPass pass = (inv_scale == 1.0f) ? hpo::GradPass::kCheck : hpo::GradPass::kUnscale;
-    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, pass, inv_scale, nullptr, s->parts,
-                                         as_stream(stream));
+    hpo::FinalOut out{};
+    out.d_found = d_found_inf;
+    hipError_t e = hpo::launch_grad_pass_final(s->view, s->n_chunks, s->grad_group, pass, inv_scale, nullptr,
+                                               s->parts, out, as_stream(stream));
     if (e != hipSuccess)
         return hip_fail(e, "launch unscale/check pass");
-    if (s->n_chunks > 0) {
-        e = hpo::launch_finalize_sets(&s->parts, 1, nullptr, d_found_inf, nullptr, as_stream(stream));
-        if (e != hipSuccess)
-            return hip_fail(e, "launch flag finalize");
-    }
     return ok();
 }
 
@@ -633,14 +630,14 @@ hpo_status hpo_grad_global_norm(hpo_set s, float inv_scale, float* d_norm, int32
         return fail(HPO_EINVAL, "inv_scale must be finite");
     if (d_num_zeros && !aligned(d_num_zeros, 8))
         return fail(HPO_EINVAL, "d_num_zeros must be 8-byte aligned");
-    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm,
-                                         inv_scale, nullptr, s->parts, as_stream(stream));
+    hpo::FinalOut out{};
+    out.d_norm = d_norm;
+    out.d_found = d_found_inf;
+    out.d_zeros = d_num_zeros;
+    hipError_t e = hpo::launch_grad_pass_final(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm,
+                                               inv_scale, nullptr, s->parts, out, as_stream(stream));
     if (e != hipSuccess)
-        return hip_fail(e, "launch norm pass");
-    /* with no chunks the finalizer still runs, so the norm and the count read 0 */
-    e = hpo::launch_finalize_sets(&s->parts, 1, d_norm, d_found_inf, d_num_zeros, as_stream(stream));
-    if (e != hipSuccess)
-        return hip_fail(e, "launch norm finalize");
+        return hip_fail(e, "launch norm pass and finalize");
     return ok();
 }
 
@@ -792,6 +789,17 @@ hpo::AdamScalars device_scalars(const hpo_adam_cfg* cfg, const hpo_group* groups
     return sc;
 }
 
+hpo::FinalOut state_out(const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state, int64_t t_first, int32_t window)
+{
+    hpo::FinalOut o{};
+    o.st = d_state;
+    o.threshold = scfg->grad_norm_skip_threshold;
+    o.rule = rule_of(scfg);
+    o.t_first = t_first;
+    o.window = window;
+    return o;
+}
+
 hpo::ScalerRule rule_of(const hpo_scaler_cfg* scfg)
 {
     hpo::ScalerRule rule{};
@@ -819,21 +827,31 @@ hpo_status hpo_step_device(hpo_set s, const hpo_adam_cfg* cfg, const hpo_group* 
     if (st != HPO_OK)
         return st;
     const hpo::AdamScalars sc = device_scalars(cfg, groups, n_groups, max_norm, d_state, t_first, window);
-    const hpo::ScalerRule rule = rule_of(scfg);
     hipStream_t strm = as_stream(stream);
-    hipError_t e = hpo::launch_grad_pass(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, 1.0f,
-                                         &d_state->inv_scale, s->parts, strm);
+    const hpo::FinalOut out = state_out(scfg, d_state, t_first, window);
+    hipError_t e = hpo::launch_grad_pass_final(s->view, s->n_chunks, s->grad_group, hpo::GradPass::kNorm, 1.0f,
+                                               &d_state->inv_scale, s->parts, out, strm);
     if (e != hipSuccess)
-        return hip_fail(e, "launch norm pass");
-    e = hpo::launch_finalize_state_sets(&s->parts, 1, d_state, scfg->grad_norm_skip_threshold, strm);
-    if (e != hipSuccess)
-        return hip_fail(e, "launch norm finalize");
+        return hip_fail(e, "launch norm pass and finalize");
     e = hpo::launch_adam(s->view, s->n_chunks, cfg->mode, sc, strm);
     if (e != hipSuccess)
         return hip_fail(e, "launch adam update");
-    e = hpo::launch_step_end(d_state, rule, t_first, window, strm);
+    return ok();
+}
+
+hpo_status hpo_stream_probe(hpo_set s, void* stream)
+{
+    hpo_status st = check_set(s);
+    if (st != HPO_OK)
+        return st;
+    const hpo::SetView& v = s->view;
+    if (!v.is_flat || !v.flat.vec_ok || v.param_dtype == HPO_PARAM_FP32 || v.state_store != 0 || v.grad_bf16 ||
+        v.master_fp16 || s->kind != HPO_SET_ADAM)
+        return fail(HPO_EINVAL, "the probe takes flat sets with fp32 grads, master and moments, 16-bit params and "
+                                "pointers on their vector lines");
+    hipError_t e = hpo::launch_stream_probe(v, s->n_chunks, as_stream(stream));
     if (e != hipSuccess)
-        return hip_fail(e, "launch step end");
+        return hip_fail(e, "launch stream probe");
     return ok();
 }
 
@@ -909,7 +927,6 @@ hpo_status hpo_step_device_chain(hpo_set adam_set, const hpo_adam_cfg* cfg, cons
     st = check_scaler_args(scfg, d_state, t_first, window);
     if (st != HPO_OK)
         return st;
-    const hpo::ScalerRule rule = rule_of(scfg);
     hipStream_t strm = as_stream(stream);
     hpo::Partials p[2];
     int n_sets = 0;
@@ -922,7 +939,7 @@ hpo_status hpo_step_device_chain(hpo_set adam_set, const hpo_adam_cfg* cfg, cons
             return hip_fail(e, "launch norm pass");
         p[n_sets++] = partials_of(s);
     }
-    hipError_t e = hpo::launch_finalize_state_sets(p, n_sets, d_state, scfg->grad_norm_skip_threshold, strm);
+    hipError_t e = hpo::launch_finalize_state_sets(p, n_sets, state_out(scfg, d_state, t_first, window), strm);
     if (e != hipSuccess)
         return hip_fail(e, "launch norm finalize");
     if (adam_set) {
@@ -941,9 +958,6 @@ hpo_status hpo_step_device_chain(hpo_set adam_set, const hpo_adam_cfg* cfg, cons
         if (st != HPO_OK)
             return st;
     }
-    e = hpo::launch_step_end(d_state, rule, t_first, window, strm);
-    if (e != hipSuccess)
-        return hip_fail(e, "launch step end");
     return ok();
 }
 

@@ -106,11 +106,12 @@ struct AdamScalars {
     float bc2_tab[HPO_MAX_WINDOW];
 };
 
-static_assert(sizeof(hpo_scaler_state) == 56, "hpo_scaler_state layout");
+static_assert(sizeof(hpo_scaler_state) == 64, "hpo_scaler_state layout");
+static_assert(offsetof(hpo_scaler_state, step_inv_scale) == 56, "hpo_scaler_state layout");
 static_assert(offsetof(hpo_scaler_state, applied_steps) == 16, "hpo_scaler_state layout");
 static_assert(offsetof(hpo_scaler_state, num_zeros) == 48, "hpo_scaler_state layout");
 
-/* Scaler rule constants for the end-of-step kernel. */
+/* Scaler rule constants for the end of a device-resident step. */
 struct ScalerRule {
     int32_t dynamic;
     int32_t growth_interval;
@@ -140,7 +141,7 @@ constexpr int kMaxFoldSets = 4;
 /* Device bytes of the partials of a pass with n workgroups (at least one
  * entry, so an empty set still has a place for its finalize to read). */
 constexpr int64_t kPartialBytes = sizeof(double) + sizeof(int32_t) + sizeof(int64_t);
-inline int64_t partial_entries(int64_t n) { return (n > 0 ? n : 1) + stage_parts(n); }
+constexpr int64_t partial_entries(int64_t n) { return (n > 0 ? n : 1) + stage_parts(n); }
 /* Carves the partials of an n-workgroup pass out of one buffer of
  * partial_entries(n) * kPartialBytes bytes, 8-byte aligned. */
 inline Partials carve_partials(void* base, int64_t n)
@@ -159,6 +160,21 @@ inline Partials carve_partials(void* base, int64_t n)
     return p;
 }
 
+/* Where the finalize of a grad pass writes (both nullable per field):
+ * host-driven calls get the norm, found_inf and the zero count; the
+ * device-resident step gets the state and the end-of-step rule. */
+struct FinalOut {
+    float* d_norm;
+    int32_t* d_found;
+    int64_t* d_zeros;
+    hpo_scaler_state* st;
+    double threshold;
+    ScalerRule rule;
+    int64_t t_first;
+    int32_t window;
+};
+
+
 /* Launchers (hpo_kernels.hip).  Each enqueues on `stream` and returns the
  * launch status. */
 /* The grad pass runs one workgroup per group of `grad_group` consecutive
@@ -166,13 +182,20 @@ inline Partials carve_partials(void* base, int64_t n)
  * written to p's first-stage entries). */
 hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
                             float inv_scale, const float* d_inv, const Partials& p, hipStream_t stream);
+/* The grad pass followed by its finalize kernels (one stage, or two for
+ * sets with more than kFinalSpan partials).  out.st set: the
+ * device-resident step's finalize (state, skip decision, counters, scaler);
+ * else the norm (when out.d_norm is set), found_inf and the zero count. */
+hipError_t launch_grad_pass_final(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
+                                  float inv_scale, const float* d_inv, const Partials& p, const FinalOut& out,
+                                  hipStream_t stream);
 hipError_t launch_adam(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                        hipStream_t stream);
 hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hysteresis, int64_t applied,
                               hipStream_t stream);
-hipError_t launch_step_end(hpo_scaler_state* st, ScalerRule rule, int64_t t_first, int32_t window,
-                           hipStream_t stream);
 hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream);
+/* The update's memory traffic with no arithmetic (fp32 flat sets with 16-bit params). */
+hipError_t launch_stream_probe(const SetView& sv, int64_t n_chunks, hipStream_t stream);
 /* Folds the partials of n_sets sets (in order) into *d_norm =
  * fp32(sqrt(sum)) and the zero count *d_zeros (both skipped when d_norm is
  * null: the sums and counts are then not read; d_zeros is nullable) and
@@ -180,10 +203,10 @@ hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStr
  * their second-stage entries first. */
 hipError_t launch_finalize_sets(const Partials* p, int n_sets, float* d_norm, int32_t* d_found, int64_t* d_zeros,
                                 hipStream_t stream);
-/* Same folding, then writes the norm, the zero count, found_inf and the
- * apply decision (finite and norm <= threshold) into the device step state. */
-hipError_t launch_finalize_state_sets(const Partials* p, int n_sets, hpo_scaler_state* st, double threshold,
-                                      hipStream_t stream);
+/* Same folding, then the device step state: the norm, the zero count,
+ * found_inf, the apply decision (finite, norm <= threshold and t in the
+ * window), the counters and the scaler rule, and the step's inv_scale. */
+hipError_t launch_finalize_state_sets(const Partials* p, int n_sets, const FinalOut& out, hipStream_t stream);
 
 }  // namespace hpo
 

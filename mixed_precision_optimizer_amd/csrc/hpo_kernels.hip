@@ -403,33 +403,6 @@ __device__ __forceinline__ void grad_range(const Range& r, float inv, double& ac
     }
 }
 
-/* One workgroup per group of consecutive chunks; one partial per workgroup:
- * the flag, and for the norm pass the binary64 sum and the zero count. */
-template <bool FLAT, GradPass PASS, int GDT>
-__global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_chunks, int32_t group,
-                                                          float inv_arg, const float* d_inv, Partials p)
-{
-    const float inv = d_inv != nullptr ? *d_inv : inv_arg;
-    double acc = 0.0;
-    int bad = 0;
-    int zeros = 0;
-    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * group;
-    const int64_t c1 = c0 + group < n_chunks ? c0 + group : n_chunks;
-    for (int64_t c = c0; c < c1; ++c)
-        grad_range<PASS, GDT>(chunk_range<FLAT>(sv, c), inv, acc, bad, zeros);
-    const int any_bad = __syncthreads_or(bad);
-    if constexpr (PASS == GradPass::kNorm) {
-        const double tot = block_sum<kGradBlock>(acc);
-        const int nz = block_sum<kGradBlock, int>(zeros);
-        if (threadIdx.x == 0) {
-            p.sum[blockIdx.x] = tot;
-            p.zeros[blockIdx.x] = nz;
-        }
-    }
-    if (threadIdx.x == 0)
-        p.flag[blockIdx.x] = any_bad ? 1 : 0;
-}
-
 /* ---------------------------------------------------------------------- */
 /* finalize: one workgroup, fixed-order sum of the per-chunk partials       */
 /* ---------------------------------------------------------------------- */
@@ -513,41 +486,114 @@ __device__ __forceinline__ double fold_sets(const Fold& f, bool want_sum, int& a
     return tot;
 }
 
-/* Last stage: one workgroup over all remaining partials, then sqrt and the
- * flag.  d_norm == nullptr: flag only (the sums are not read); d_zeros
- * (nullable) receives the zero count. */
-__global__ __launch_bounds__(kFinalBlock) void k_finalize(Fold f, float* d_norm, int32_t* d_found, int64_t* d_zeros)
+/* Host-driven outputs of a finalize (thread 0): the norm and the zero count
+ * when the sums were folded, found_inf or-ed in. */
+__device__ __forceinline__ void write_norm_outputs(const FinalOut& o, double tot, int any_bad, int64_t zeros)
 {
-    const bool want_norm = d_norm != nullptr;
-    int any_bad = 0;
-    int64_t zeros = 0;
-    const double tot = fold_sets(f, want_norm, any_bad, zeros);
-    if (threadIdx.x == 0) {
-        if (want_norm)
-            *d_norm = static_cast<float>(sqrt(tot));
-        if (want_norm && d_zeros != nullptr)
-            *d_zeros = zeros;
-        if (d_found != nullptr && any_bad)
-            *d_found = 1;
+    if (o.d_norm != nullptr) {
+        *o.d_norm = static_cast<float>(sqrt(tot));
+        if (o.d_zeros != nullptr)
+            *o.d_zeros = zeros;
     }
+    if (o.d_found != nullptr && any_bad)
+        *o.d_found = 1;
 }
 
-/* Last stage of the device-resident step: norm, zero count, found_inf and
- * whether the step will be applied (finite grads, norm not above the skip
- * threshold). */
-__global__ __launch_bounds__(kFinalBlock) void k_finalize_state(Fold f, hpo_scaler_state* st, double threshold)
+/* The end of a device-resident step (thread 0), once the partials are
+ * folded: the norm, the zero count and found_inf; the step is applied when
+ * the grads are finite, the norm is not above the skip threshold and its t
+ * (applied_steps + 1) lies in the window of bias corrections it was given
+ * (a t outside sets the sticky error instead); then the counters and the
+ * loss-scale rule of [OPT-INFRA] §10.1.  step_inv_scale keeps the scale this
+ * step's grads were unscaled with, for the update that follows; inv_scale
+ * becomes the next step's. */
+__device__ __forceinline__ void write_step_state(const FinalOut& o, double tot, int any_bad, int64_t zeros)
+{
+    hpo_scaler_state s = *o.st;
+    const float norm = static_cast<float>(sqrt(tot));
+    s.grad_norm = norm;
+    s.num_zeros = zeros;
+    s.found_inf = any_bad ? 1 : 0;
+    s.step_inv_scale = s.inv_scale;
+    /* the threshold test fails for a NaN norm, so "not above" is spelled out */
+    const bool ok = !any_bad && !(static_cast<double>(norm) > o.threshold);
+    const int64_t j = s.applied_steps + 1 - o.t_first;
+    const bool in_window = j >= 0 && j < o.window;
+    if (ok && !in_window)
+        s.error = 1;
+    s.applied = (ok && in_window) ? 1 : 0;
+    if (s.applied)
+        s.applied_steps += 1;
+    else
+        s.skipped_steps += 1;
+    const ScalerRule& rule = o.rule;
+    if (rule.dynamic) {
+        if (s.found_inf) {
+            s.growth_tracker = 0;
+            s.hysteresis_tracker -= 1;
+            if (s.hysteresis_tracker <= 0) {
+                const float backed = s.loss_scale * rule.backoff_factor;
+                s.loss_scale = backed > rule.min_scale ? backed : rule.min_scale;
+            }
+        } else {
+            s.growth_tracker += 1;
+            if (s.growth_tracker == rule.growth_interval) {
+                s.growth_tracker = 0;
+                s.hysteresis_tracker = rule.hysteresis;
+                s.loss_scale = s.loss_scale * rule.growth_factor;
+            }
+        }
+        s.inv_scale = static_cast<float>(1.0 / static_cast<double>(s.loss_scale));
+    }
+    *o.st = s;
+}
+
+/* Last stage: one workgroup over all remaining partials, then the outputs.
+ * d_norm == nullptr: flag only (the sums are not read). */
+__global__ __launch_bounds__(kFinalBlock) void k_finalize(Fold f, FinalOut o)
+{
+    int any_bad = 0;
+    int64_t zeros = 0;
+    const double tot = fold_sets(f, o.d_norm != nullptr, any_bad, zeros);
+    if (threadIdx.x == 0)
+        write_norm_outputs(o, tot, any_bad, zeros);
+}
+
+/* Last stage of the device-resident step. */
+__global__ __launch_bounds__(kFinalBlock) void k_finalize_state(Fold f, FinalOut o)
 {
     int any_bad = 0;
     int64_t zeros = 0;
     const double tot = fold_sets(f, true, any_bad, zeros);
-    if (threadIdx.x == 0) {
-        const float norm = static_cast<float>(sqrt(tot));
-        st->grad_norm = norm;
-        st->num_zeros = zeros;
-        st->found_inf = any_bad ? 1 : 0;
-        /* the threshold test fails for a NaN norm, so "not above" is spelled out */
-        st->applied = (!any_bad && !(static_cast<double>(norm) > threshold)) ? 1 : 0;
+    if (threadIdx.x == 0)
+        write_step_state(o, tot, any_bad, zeros);
+}
+
+/* One workgroup per group of consecutive chunks; one partial per workgroup:
+ * the flag, and for the norm pass the binary64 sum and the zero count. */
+template <bool FLAT, GradPass PASS, int GDT>
+__global__ __launch_bounds__(kGradBlock) void k_grad_pass(SetView sv, int64_t n_chunks, int32_t group,
+                                                          float inv_arg, const float* d_inv, Partials p)
+{
+    const float inv = d_inv != nullptr ? *d_inv : inv_arg;
+    double acc = 0.0;
+    int bad = 0;
+    int zeros = 0;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * group;
+    const int64_t c1 = c0 + group < n_chunks ? c0 + group : n_chunks;
+    for (int64_t c = c0; c < c1; ++c)
+        grad_range<PASS, GDT>(chunk_range<FLAT>(sv, c), inv, acc, bad, zeros);
+    const int any_bad = __syncthreads_or(bad);
+    if constexpr (PASS == GradPass::kNorm) {
+        const double tot = block_sum<kGradBlock>(acc);
+        const int nz = block_sum<kGradBlock, int>(zeros);
+        if (threadIdx.x == 0) {
+            p.sum[blockIdx.x] = tot;
+            p.zeros[blockIdx.x] = nz;
+        }
     }
+    if (threadIdx.x == 0)
+        p.flag[blockIdx.x] = any_bad ? 1 : 0;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -602,12 +648,13 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
         const hpo_scaler_state* st = sc.d_state;
         if (!st->applied)
             return;
-        const int64_t j = st->applied_steps + 1 - sc.t_first;
+        /* the finalize has counted this step: t = applied_steps, in the window */
+        const int64_t j = st->applied_steps - sc.t_first;
         if (j < 0 || j >= sc.window)
-            return; /* outside the window: the end kernel records the error */
+            return;
         k.bc1 = sc.bc1_tab[j];
         k.bc2 = sc.bc2_tab[j];
-        k.inv_scale = st->inv_scale;
+        k.inv_scale = st->step_inv_scale;
         norm = st->grad_norm;
     } else {
         if (sc.d_found != nullptr && *sc.d_found != 0)
@@ -686,6 +733,58 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
 }
 
 /* ---------------------------------------------------------------------- */
+/* bandwidth probe (measurement only)                                     */
+/* ---------------------------------------------------------------------- */
+/* The update's access pattern on an fp32 flat shard with a 16-bit param --
+ * the same chunks, workgroups, unroll and streaming accesses -- with none of
+ * its arithmetic: grad, master, exp_avg, exp_avg_sq read, the three state
+ * arrays written back as read and the param written as the RNE of the
+ * master.  The state is left as it was (param == bf16 / fp16 of the master
+ * holds after every step), so this times the practical ceiling of the
+ * update's 16-byte-read / 14-byte-write mix on the very buffers it steps.
+ * The empty asm statements keep the grad loads and the stores from being
+ * optimized away. */
+template <int PDT>
+__global__ HPO_ADAM_BOUNDS void k_stream_probe(SetView sv, int64_t n_chunks)
+{
+    const Range r = chunk_range<true>(sv, update_chunk(n_chunks));
+    const float4* __restrict__ G = reinterpret_cast<const float4*>(r.d.grad + r.start);
+    float4* __restrict__ T = reinterpret_cast<float4*>(r.d.master + r.start);
+    float4* __restrict__ M = static_cast<float4*>(r.d.exp_avg) + r.start / kVec;
+    float4* __restrict__ V = static_cast<float4*>(r.d.exp_avg_sq) + r.start / kVec;
+    uint2* __restrict__ P = reinterpret_cast<uint2*>(static_cast<uint16_t*>(r.d.param) + r.start);
+    const int64_t nv = r.len / kVec;  /* flat chunks start on vector lines; the tail is not probed */
+    constexpr int U = HPO_ADAM_UNROLL;
+    for (int64_t base = threadIdx.x; base < nv; base += kBlock * U) {
+        float4 g[U], th[U], m[U], v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + static_cast<int64_t>(u) * kBlock;
+            if (i < nv) {
+                g[u] = ld_stream(G + i);
+                th[u] = ld_stream(T + i);
+                m[u] = ld_stream(M + i);
+                v[u] = ld_stream(V + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + static_cast<int64_t>(u) * kBlock;
+            if (i < nv) {
+                asm volatile("" : "+v"(g[u].x), "+v"(g[u].y), "+v"(g[u].z), "+v"(g[u].w));
+                asm volatile("" : "+v"(th[u].x), "+v"(th[u].y), "+v"(th[u].z), "+v"(th[u].w));
+                asm volatile("" : "+v"(m[u].x), "+v"(m[u].y), "+v"(m[u].z), "+v"(m[u].w));
+                asm volatile("" : "+v"(v[u].x), "+v"(v[u].y), "+v"(v[u].z), "+v"(v[u].w));
+                st_stream(T + i, th[u]);
+                st_stream(M + i, m[u]);
+                st_stream(V + i, v[u]);
+                st_stream(P + i, pack_param4<PDT>(th[u]));
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* master -> model copy                                                   */
 /* ---------------------------------------------------------------------- */
 template <bool FLAT, int PDT, int MST>
@@ -719,45 +818,9 @@ __global__ __launch_bounds__(64) void k_scaler_init(hpo_scaler_state* st, float 
         s.inv_scale = static_cast<float>(1.0 / static_cast<double>(loss_scale));
         s.hysteresis_tracker = hysteresis;
         s.applied_steps = applied;
+        s.step_inv_scale = s.inv_scale;
         *st = s;
     }
-}
-
-/* Counters and the dynamic loss-scale rule ([OPT-INFRA] §10.1), one lane. */
-__global__ __launch_bounds__(64) void k_step_end(hpo_scaler_state* st, ScalerRule rule, int64_t t_first,
-                                                 int32_t window)
-{
-    if (threadIdx.x != 0)
-        return;
-    hpo_scaler_state s = *st;
-    const int64_t j = s.applied_steps + 1 - t_first;
-    const bool in_window = j >= 0 && j < window;
-    if (s.applied && !in_window)
-        s.error = 1;
-    s.applied = (s.applied && in_window) ? 1 : 0;
-    if (s.applied)
-        s.applied_steps += 1;
-    else
-        s.skipped_steps += 1;
-    if (rule.dynamic) {
-        if (s.found_inf) {
-            s.growth_tracker = 0;
-            s.hysteresis_tracker -= 1;
-            if (s.hysteresis_tracker <= 0) {
-                const float backed = s.loss_scale * rule.backoff_factor;
-                s.loss_scale = backed > rule.min_scale ? backed : rule.min_scale;
-            }
-        } else {
-            s.growth_tracker += 1;
-            if (s.growth_tracker == rule.growth_interval) {
-                s.growth_tracker = 0;
-                s.hysteresis_tracker = rule.hysteresis;
-                s.loss_scale = s.loss_scale * rule.growth_factor;
-            }
-        }
-        s.inv_scale = static_cast<float>(1.0 / static_cast<double>(s.loss_scale));
-    }
-    *st = s;
 }
 
 template <typename... Args>
@@ -890,17 +953,32 @@ hipError_t launch_finalize_sets(const Partials* p, int n_sets, float* d_norm, in
     hipError_t e = fold_inputs(p, n_sets, d_norm != nullptr, f, stream);
     if (e != hipSuccess)
         return e;
-    return launch(k_finalize, 1, kFinalBlock, stream, f, d_norm, d_found, d_zeros);
+    FinalOut o{};
+    o.d_norm = d_norm;
+    o.d_found = d_found;
+    o.d_zeros = d_zeros;
+    return launch(k_finalize, 1, kFinalBlock, stream, f, o);
 }
 
-hipError_t launch_finalize_state_sets(const Partials* p, int n_sets, hpo_scaler_state* st, double threshold,
-                                      hipStream_t stream)
+hipError_t launch_finalize_state_sets(const Partials* p, int n_sets, const FinalOut& out, hipStream_t stream)
 {
     Fold f{};
     hipError_t e = fold_inputs(p, n_sets, true, f, stream);
     if (e != hipSuccess)
         return e;
-    return launch(k_finalize_state, 1, kFinalBlock, stream, f, st, threshold);
+    return launch(k_finalize_state, 1, kFinalBlock, stream, f, out);
+}
+
+hipError_t launch_grad_pass_final(const SetView& sv, int64_t n_chunks, int32_t grad_group, GradPass pass,
+                                  float inv_scale, const float* d_inv, const Partials& p, const FinalOut& out,
+                                  hipStream_t stream)
+{
+    hipError_t e = launch_grad_pass(sv, n_chunks, grad_group, pass, inv_scale, d_inv, p, stream);
+    if (e != hipSuccess)
+        return e;
+    /* an empty set still finalizes, so the norm and the count read 0 */
+    return out.st != nullptr ? launch_finalize_state_sets(&p, 1, out, stream)
+                             : launch_finalize_sets(&p, 1, out.d_norm, out.d_found, out.d_zeros, stream);
 }
 
 hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hysteresis, int64_t applied,
@@ -909,10 +987,12 @@ hipError_t launch_scaler_init(hpo_scaler_state* st, float loss_scale, int32_t hy
     return launch(k_scaler_init, 1, 64, stream, st, loss_scale, hysteresis, applied);
 }
 
-hipError_t launch_step_end(hpo_scaler_state* st, ScalerRule rule, int64_t t_first, int32_t window,
-                           hipStream_t stream)
+hipError_t launch_stream_probe(const SetView& sv, int64_t n_chunks, hipStream_t stream)
 {
-    return launch(k_step_end, 1, 64, stream, st, rule, t_first, window);
+    if (n_chunks == 0)
+        return hipSuccess;
+    return sv.param_dtype == HPO_PARAM_FP16 ? launch(k_stream_probe<HPO_PARAM_FP16>, n_chunks, kBlock, stream, sv, n_chunks)
+                                            : launch(k_stream_probe<HPO_PARAM_BF16>, n_chunks, kBlock, stream, sv, n_chunks);
 }
 
 hipError_t launch_copy_main_to_model(const SetView& sv, int64_t n_chunks, hipStream_t stream)

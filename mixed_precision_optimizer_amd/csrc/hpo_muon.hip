@@ -145,10 +145,11 @@ constexpr int kTile = 64;              /* transpose tile of the input kernel */
 __device__ __forceinline__ bool gate_open(const MuonGate& g)
 {
     if (g.dev) {
+        /* the finalize has decided and counted the step (t = applied_steps, in the window) */
         if (!g.st->applied)
             return false;
-        const int64_t j = g.st->applied_steps + 1 - g.t_first;
-        return j >= 0 && j < g.window;  /* outside the window the end kernel records the error */
+        const int64_t j = g.st->applied_steps - g.t_first;
+        return j >= 0 && j < g.window;
     }
     return !(g.d_found != nullptr && *g.d_found != 0);
 }
@@ -166,7 +167,7 @@ __device__ __forceinline__ GradVals grad_vals(const MuonScalars& sc)
     GradVals v;
     float norm = 0.0f;
     if (sc.gate.dev) {
-        v.inv_scale = sc.gate.st->inv_scale;
+        v.inv_scale = sc.gate.st->step_inv_scale;
         norm = sc.gate.st->grad_norm;
     } else {
         v.inv_scale = sc.inv_scale;

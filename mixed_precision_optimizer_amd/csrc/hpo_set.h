@@ -96,6 +96,8 @@ hpo_status check_scaler_args(const hpo_scaler_cfg* scfg, const hpo_scaler_state*
 hpo::AdamScalars device_scalars(const hpo_adam_cfg* cfg, const hpo_group* groups, int32_t n_groups,
                                 double max_norm, hpo_scaler_state* d_state, int64_t t_first, int32_t window);
 hpo::ScalerRule rule_of(const hpo_scaler_cfg* scfg);
+/* The finalize outputs of a device-resident step: the state and its end-of-step rule. */
+hpo::FinalOut state_out(const hpo_scaler_cfg* scfg, hpo_scaler_state* d_state, int64_t t_first, int32_t window);
 hpo_status alloc_partials(hpo_set s);
 void free_set(hpo_set s);
 hpo_status check_set(hpo_set s);

@@ -33,6 +33,8 @@ constexpr size_t kScratchBytes =
     static_cast<size_t>(HPO_STATIC_MAX_PARTS + hpo::stage_parts(HPO_STATIC_MAX_PARTS)) * hpo::kPartialBytes;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static_assert(hpo::partial_entries(HPO_STATIC_MAX_PARTS) * hpo::kPartialBytes <= static_cast<int64_t>(kScratchBytes),
+              "the largest plan's partials fit");
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -117,19 +119,13 @@ extern "C" hpo_status hpo_step_device_flat_static(int64_t numel, int32_t param_d
     const hpo::Partials parts = hpo::carve_partials(base, n_parts);
 
     const hpo::AdamScalars sc = device_scalars(cfg, group, 1, max_norm, d_state, t_first, window);
-    const hpo::ScalerRule rule = rule_of(scfg);
     hipStream_t strm = as_stream(stream);
-    e = hpo::launch_grad_pass(sv, n_chunks, gg, hpo::GradPass::kNorm, 1.0f, &d_state->inv_scale, parts, strm);
+    e = hpo::launch_grad_pass_final(sv, n_chunks, gg, hpo::GradPass::kNorm, 1.0f, &d_state->inv_scale, parts,
+                                    state_out(scfg, d_state, t_first, window), strm);
     if (e != hipSuccess)
-        return hip_fail(e, "launch norm pass");
-    e = hpo::launch_finalize_state_sets(&parts, 1, d_state, scfg->grad_norm_skip_threshold, strm);
-    if (e != hipSuccess)
-        return hip_fail(e, "launch norm finalize");
+        return hip_fail(e, "launch norm pass and finalize");
     e = hpo::launch_adam(sv, n_chunks, cfg->mode, sc, strm);
     if (e != hipSuccess)
         return hip_fail(e, "launch adam update");
-    e = hpo::launch_step_end(d_state, rule, t_first, window, strm);
-    if (e != hipSuccess)
-        return hip_fail(e, "launch step end");
     return ok();
 }

@@ -83,7 +83,8 @@ class hpo_scaler_state(ctypes.Structure):
                 ("growth_tracker", ctypes.c_int32), ("hysteresis_tracker", ctypes.c_int32),
                 ("applied_steps", ctypes.c_int64), ("skipped_steps", ctypes.c_int64),
                 ("grad_norm", ctypes.c_float), ("found_inf", ctypes.c_int32),
-                ("applied", ctypes.c_int32), ("error", ctypes.c_int32), ("num_zeros", ctypes.c_int64)]
+                ("applied", ctypes.c_int32), ("error", ctypes.c_int32), ("num_zeros", ctypes.c_int64),
+                ("step_inv_scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
 
 
 class hpo_scaler_cfg(ctypes.Structure):
@@ -115,6 +116,7 @@ SIGNATURES = {
     "hpo_adamw_step": (_I32, [_P, ctypes.POINTER(hpo_adam_cfg), ctypes.POINTER(hpo_group), _I32,
                               _I64, ctypes.c_float, ctypes.c_double, _P, _P, _P]),
     "hpo_copy_main_to_model": (_I32, [_P, _P]),
+    "hpo_stream_probe": (_I32, [_P, _P]),
     "hpo_step_device_flat_static": (_I32, [_I64, _I32, _P, _P, _P, _P, _P, ctypes.POINTER(hpo_adam_cfg),
                                            ctypes.POINTER(hpo_group), ctypes.c_double, ctypes.POINTER(hpo_scaler_cfg),
                                            _P, _I64, _I32, _P]),
@@ -463,7 +465,7 @@ def hpo_adamw_step(s: HpoSet, cfg: hpo_adam_cfg, groups, n_groups: Optional[int]
 
 
 def new_scaler_state(device=None) -> torch.Tensor:
-    """Device buffer for one hpo_scaler_state (56 bytes, 8-byte aligned)."""
+    """Device buffer for one hpo_scaler_state (64 bytes, 8-byte aligned)."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     return torch.zeros(SCALER_STATE_BYTES // 8, dtype=torch.int64, device=dev)
 
@@ -522,6 +524,10 @@ def hpo_step_device_flat_static(param: Optional[torch.Tensor], main_param: torch
     _check(load().hpo_step_device_flat_static(n, param_dtype | mflag, p_ptr, *ptrs, ctypes.byref(cfg), ctypes.byref(g),
                                               max_norm, ctypes.byref(scfg), _state_ptr(d_state), t_first, window,
                                               _stream(stream)), "hpo_step_device_flat_static")
+
+
+def hpo_stream_probe(s: HpoSet, stream=None) -> None:
+    _check(load().hpo_stream_probe(s.handle, _stream(stream)), "hpo_stream_probe")
 
 
 def hpo_copy_main_to_model(s: HpoSet, stream=None) -> None:

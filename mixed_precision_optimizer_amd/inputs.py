@@ -433,6 +433,15 @@ class MuonBuffers:
         return [buf[o:o + r * c].view(r, c) for o, (r, c) in zip(self.offs, self.shapes)]
 
 
+def fill_muon_grads_(mb: MuonBuffers, matrices, k: int, grad_seed: int = 2001) -> None:
+    """fp32 grads of call k of a Muon matrix list: N(0, 1) from seed
+    grad_seed + 1000 (k - 1) over the flat buffer, then matrix i's slice
+    times its std (call 1 repeats the draw allocate_muon makes)."""
+    fill_normal_(mb.grad, grad_seed + 1000 * (k - 1))
+    for (_, (r, c), std), o in zip(matrices, mb.offs):
+        mb.grad[o:o + r * c].mul_(std)
+
+
 def allocate_muon(matrices, device, master_seed: int = 7, grad_seed: int = 2001) -> MuonBuffers:
     """fp32 master N(0, 1), fp32 momentum 0, bf16 param = cast of the master,
     fp32 grads N(0, std_i) for matrix i (one seeded fill, then per-matrix

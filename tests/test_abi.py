@@ -30,18 +30,18 @@ def _declared():
 
 def test_exports_every_declared_symbol(H):
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 26
     lib = H.load()
     for n in names:
         assert hasattr(lib, n), n
         assert n in H.SIGNATURES, f"binding lacks {n}"
     assert set(H.SIGNATURES) == set(names)
-    assert H.hpo_abi_version() == 4
+    assert H.hpo_abi_version() == 5
 
 
 def test_struct_layouts(H):
     """The ctypes mirrors have the C sizes the header fixes."""
-    assert H.SCALER_STATE_BYTES == 56
+    assert H.SCALER_STATE_BYTES == 64
     assert ctypes.sizeof(H.hpo_set_info_t) == 64
     assert ctypes.sizeof(H.hpo_adam_cfg) == 32 and ctypes.sizeof(H.hpo_group) == 16
     assert ctypes.sizeof(H.hpo_scaler_cfg) == 32

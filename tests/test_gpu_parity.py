@@ -375,6 +375,63 @@ def test_norm_over_several_sets(H, orc):
         s.close()
 
 
+def test_norm_paths_agree_across_the_two_stage_boundary(H, orc):
+    """The single-set norm call, the multi-set call on that one set and the
+    device step's finalize give the same norm, zero count and flag bits,
+    call after call, on both sides of the 8192-workgroup boundary where the
+    finalize takes a second stage; the count equals torch's own count of
+    zero grads."""
+    banner("norm paths across the two-stage boundary")
+    rng = np.random.default_rng(19)
+    inv = float(np.float32(1 / 1024))
+    for n in (1, 4097, 3_000_001, 8192 * 65536, 8192 * 65536 + 3 * 65536):
+        g = torch.randn(n, device=DEV).mul_(1e-2 * 1024)
+        g[::97] = 0.0
+        t = torch.zeros(n, device=DEV)
+        hset = H.hpo_set_create_flat(None, t, g, torch.zeros_like(t), torch.zeros_like(t))
+        parts = hset.info().n_grad_parts
+        out = torch.zeros(4, dtype=torch.int32, device=DEV)
+        ref = torch.zeros(4, dtype=torch.int32, device=DEV)
+        norm, flag, zeros = out[0:1].view(torch.float32), out[1:2], out[2:4].view(torch.int64)
+        rnorm, rflag, rzeros = ref[0:1].view(torch.float32), ref[1:2], ref[2:4].view(torch.int64)
+        H.hpo_grad_global_norm_sets([hset], inv, rnorm, rflag, rzeros)
+        for rep in range(3):
+            out.zero_()
+            H.hpo_grad_global_norm(hset, inv, norm, flag, zeros)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), (n, parts, rep, out.tolist(), ref.tolist())
+        assert int(zeros.item()) == int((g == 0).sum().item()), (n, zeros.item())   # torch's own count
+        if n < 10_000:
+            want = orc.sumsq(to_np(g), inv)
+            assert norm.item() == float(np.float32(math.sqrt(want)))
+        # a non-finite grad: the folded flag, the norm of the check pass
+        g[n // 2] = float("inf")
+        out.zero_()
+        H.hpo_grad_global_norm(hset, inv, norm, flag, zeros)
+        f2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+        H.hpo_unscale_check_inf(hset, 1.0, f2)
+        torch.cuda.synchronize()
+        assert flag.item() == 1 and f2.item() == 1 and not math.isfinite(norm.item()), n
+        g[n // 2] = 0.0
+        # the device step's folded finalize writes the same norm and count into the state
+        d_state = H.new_scaler_state()
+        H.hpo_scaler_state_init(d_state, 1024.0, 1)
+        H.hpo_step_device(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1.0, H.make_scaler_cfg(dynamic=False), d_state,
+                          1, 1)
+        st = H.read_scaler_state(d_state)
+        assert st.applied == 1 and st.applied_steps == 1 and st.error == 0
+        d_norm = torch.zeros(1, device=DEV)
+        d_zeros = torch.zeros(1, dtype=torch.int64, device=DEV)
+        H.hpo_grad_global_norm_sets([hset], inv, d_norm, None, d_zeros)   # the grads as the step saw them
+        torch.cuda.synchronize()
+        assert st.grad_norm == d_norm.item() and st.num_zeros == int(d_zeros.item())
+        assert st.step_inv_scale == inv and st.inv_scale == inv
+        print(f"[norm paths] n={n} workgroups={parts} norm={rnorm.item()} zeros={int(rzeros.item())}", flush=True)
+        hset.close()
+        del g, t
+        torch.cuda.empty_cache()
+
+
 def test_empty_set_and_zero_sizes(H):
     banner("empty set")
     hset = H.hpo_set_create_list([], [], [], [], [], param_dtype=H.HPO_PARAM_BF16)

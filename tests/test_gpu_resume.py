@@ -4,7 +4,7 @@
 weights, the Muon and AdamW states and the fp32 main params, build a new
 trainer from the saved files, continue on the same next batch, and compare
 with a run that never stopped.  Here everything a step depends on lives in
-caller-owned buffers plus the 48-byte device scaler state (which holds the
+caller-owned buffers plus the 64-byte device scaler state (which holds the
 applied-step counter), so "save" is a host copy of those buffers, "load"
 builds fresh device buffers and fresh sets from the copies, and the
 continued run must match the uninterrupted one bit for bit: AdamW master, m,
