@@ -134,6 +134,10 @@ typedef struct {
 /* Opaque handle on a set of parameters stepped together. */
 typedef struct hpo_set_* hpo_set;
 
+/* A set whose arrays take at most 192 MiB in all stays in the GPU's on-die
+ * cache between steps; its update then reads and writes through the caches
+ * (the same results), while larger sets use streaming accesses that go
+ * around them. */
 typedef struct {
     int32_t n_tensors;
     int32_t param_dtype;

@@ -415,6 +415,7 @@ hpo_status create_from_pieces(hpo_set* out, int32_t param_dtype, const Layout& l
     s->view.state_store = lay.state_store();
     s->view.grad_bf16 = static_cast<int16_t>(lay.grad_bf16);
     s->view.master_fp16 = static_cast<int16_t>(lay.master_fp16);
+    s->view.cached = lay.cached(s->numel);
     *out = s;
     return ok();
 }
@@ -563,6 +564,7 @@ hpo_status hpo_set_create_flat(hpo_set* out, int64_t numel, int32_t param_dtype,
     s->view.state_store = lay.state_store();
     s->view.grad_bf16 = static_cast<int16_t>(lay.grad_bf16);
     s->view.master_fp16 = static_cast<int16_t>(lay.master_fp16);
+    s->view.cached = lay.cached(numel);
     st = alloc_partials(s);
     if (st != HPO_OK) { free_set(s); return st; }
     *out = s;

@@ -83,7 +83,12 @@ struct SetView {
     int32_t state_store;  /* exp_avg / exp_avg_sq storage: 0 fp32, 1 bf16, 2 fp16 */
     int16_t grad_bf16;    /* main grads held as bf16 */
     int16_t master_fp16;  /* master held as fp16 (bf16 params) */
+    int32_t cached;       /* the update takes cached (not streaming) accesses: the set fits the on-die cache */
 };
+/* A set whose five arrays take at most this many bytes stays in MI355X's
+ * 256 MB on-die cache from one step to the next, so its update reads and
+ * writes through the caches; larger sets stream around them. */
+constexpr int64_t kCachedMaxBytes = int64_t(192) << 20;
 
 /* Per-step scalars of the update, all formed on the host in binary64 and
  * rounded to fp32 once. */

@@ -74,64 +74,74 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+/* 16-, 8- and 16-byte accesses, nontemporal (streaming) when NT: data that
+ * is touched once per pass goes around the caches.  Sets small enough to sit
+ * in the on-die cache from one step to the next take cached accesses in the
+ * update instead (SetView::cached). */
+template <bool NT = HPO_NT_LOADS>
 __device__ __forceinline__ float4 ld_stream(const float4* p)
 {
-#if HPO_NT_LOADS
-    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-    return make_float4(v.x, v.y, v.z, v.w);
-#else
-    return *p;
-#endif
+    if constexpr (NT) {
+        const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
 }
 
+template <bool NT = HPO_NT_LOADS>
 __device__ __forceinline__ uint2 ld_stream(const uint2* p)
 {
-#if HPO_NT_LOADS
-    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-    return make_uint2(v.x, v.y);
-#else
-    return *p;
-#endif
+    if constexpr (NT) {
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        return make_uint2(v.x, v.y);
+    } else {
+        return *p;
+    }
 }
 
+template <bool NT = HPO_NT_LOADS>
 __device__ __forceinline__ uint4 ld_stream(const uint4* p)
 {
-#if HPO_NT_LOADS
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-#else
-    return *p;
-#endif
+    if constexpr (NT) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
 }
 
+template <bool NT = HPO_NT_STORES>
 __device__ __forceinline__ void st_stream(uint4* p, uint4 v)
 {
-#if HPO_NT_STORES
-    u32x4_t w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
-#else
-    *p = v;
-#endif
+    if constexpr (NT) {
+        u32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+    } else {
+        *p = v;
+    }
 }
 
+template <bool NT = HPO_NT_STORES>
 __device__ __forceinline__ void st_stream(float4* p, float4 v)
 {
-#if HPO_NT_STORES
-    f32x4_t w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(p));
-#else
-    *p = v;
-#endif
+    if constexpr (NT) {
+        f32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(p));
+    } else {
+        *p = v;
+    }
 }
 
+template <bool NT = HPO_NT_STORES>
 __device__ __forceinline__ void st_stream(uint2* p, uint2 v)
 {
-#if HPO_NT_STORES
-    u32x2_t w = {v.x, v.y};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
-#else
-    *p = v;
-#endif
+    if constexpr (NT) {
+        u32x2_t w = {v.x, v.y};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+    } else {
+        *p = v;
+    }
 }
 
 /* Chunk handled by this workgroup of an n-workgroup update launch. */
@@ -237,25 +247,25 @@ __device__ __forceinline__ float stored(float x)
 }
 
 /* 4 consecutive elements at 4-element index i of base. */
-template <int S>
+template <int S, bool NT = HPO_NT_LOADS>
 __device__ __forceinline__ float4 ld4(const void* base, int64_t i)
 {
     if constexpr (S == kF32) {
-        return ld_stream(static_cast<const float4*>(base) + i);
+        return ld_stream<NT>(static_cast<const float4*>(base) + i);
     } else {
-        const uint2 w = ld_stream(static_cast<const uint2*>(base) + i);
+        const uint2 w = ld_stream<NT>(static_cast<const uint2*>(base) + i);
         return make_float4(widen16<S>(w.x & 0xFFFFu), widen16<S>(w.x >> 16), widen16<S>(w.y & 0xFFFFu),
                            widen16<S>(w.y >> 16));
     }
 }
 
-template <int S>
+template <int S, bool NT = HPO_NT_STORES>
 __device__ __forceinline__ void st4(void* base, int64_t i, float4 x)
 {
     if constexpr (S == kF32)
-        st_stream(static_cast<float4*>(base) + i, x);
+        st_stream<NT>(static_cast<float4*>(base) + i, x);
     else
-        st_stream(static_cast<uint2*>(base) + i, make_uint2(narrow16<S>(x.x) | (narrow16<S>(x.y) << 16),
+        st_stream<NT>(static_cast<uint2*>(base) + i, make_uint2(narrow16<S>(x.x) | (narrow16<S>(x.y) << 16),
                                                             narrow16<S>(x.z) | (narrow16<S>(x.w) << 16)));
 }
 
@@ -637,7 +647,7 @@ __device__ __forceinline__ void adam_elem(float G, float& th, float& m, float& v
 /* SDT, GDT, MST: storage (Store) of the moments, the main grads and the
  * master.  The param written back is the 16-bit rounding of the master as
  * stored, so an fp16 master and its bf16 param agree with a later copy. */
-template <bool FLAT, int PDT, int MODE, bool DEV, int SDT, int GDT, int MST>
+template <bool FLAT, int PDT, int MODE, bool DEV, int SDT, int GDT, int MST, bool NT>
 __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chunks)
 {
     StepVals k;
@@ -694,10 +704,10 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
             for (int u = 0; u < U; ++u) {
                 const int64_t i = base + static_cast<int64_t>(u) * kBlock;
                 if (i < nv) {
-                    g[u] = ld4<GDT>(G, i);
-                    th[u] = ld4<MST>(T, i);
-                    m[u] = ld4<SDT>(M, i);
-                    v[u] = ld4<SDT>(V, i);
+                    g[u] = ld4<GDT, NT>(G, i);
+                    th[u] = ld4<MST, NT>(T, i);
+                    m[u] = ld4<SDT, NT>(M, i);
+                    v[u] = ld4<SDT, NT>(V, i);
                 }
             }
 #pragma unroll
@@ -710,11 +720,11 @@ __global__ HPO_ADAM_BOUNDS void k_adam(SetView sv, AdamScalars sc, int64_t n_chu
                     adam_elem<MODE>(g[u].w, th[u].w, m[u].w, v[u].w, sc, k, lr, wd);
                     th[u] = make_float4(stored<MST>(th[u].x), stored<MST>(th[u].y), stored<MST>(th[u].z),
                                         stored<MST>(th[u].w));
-                    st4<MST>(T, i, th[u]);
-                    st4<SDT>(M, i, m[u]);
-                    st4<SDT>(V, i, v[u]);
+                    st4<MST, NT>(T, i, th[u]);
+                    st4<SDT, NT>(M, i, m[u]);
+                    st4<SDT, NT>(V, i, v[u]);
                     if constexpr (PDT != HPO_PARAM_FP32)
-                        st_stream(P4 + i, pack_param4<PDT>(th[u]));
+                        st_stream<NT>(P4 + i, pack_param4<PDT>(th[u]));
                 }
             }
         }
@@ -857,20 +867,28 @@ hipError_t launch_grad_pass(const SetView& sv, int64_t n_chunks, int32_t grad_gr
     return hipErrorInvalidValue;
 }
 
-template <bool DEV, int SDT, int GDT, int PDT, int MST>
-hipError_t launch_adam_p(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+template <bool DEV, int SDT, int GDT, int PDT, int MST, bool NT>
+hipError_t launch_adam_n(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
                          hipStream_t stream)
 {
     const bool flat = sv.is_flat != 0;
     if (mode == HPO_ADAMW)
-        return flat ? launch(k_adam<true, PDT, HPO_ADAMW, DEV, SDT, GDT, MST>, n_chunks, kBlock, stream, sv, sc,
+        return flat ? launch(k_adam<true, PDT, HPO_ADAMW, DEV, SDT, GDT, MST, NT>, n_chunks, kBlock, stream, sv, sc,
                              n_chunks)
-                    : launch(k_adam<false, PDT, HPO_ADAMW, DEV, SDT, GDT, MST>, n_chunks, kBlock, stream, sv, sc,
+                    : launch(k_adam<false, PDT, HPO_ADAMW, DEV, SDT, GDT, MST, NT>, n_chunks, kBlock, stream, sv, sc,
                              n_chunks);
-    return flat ? launch(k_adam<true, PDT, HPO_ADAM_L2, DEV, SDT, GDT, MST>, n_chunks, kBlock, stream, sv, sc,
+    return flat ? launch(k_adam<true, PDT, HPO_ADAM_L2, DEV, SDT, GDT, MST, NT>, n_chunks, kBlock, stream, sv, sc,
                          n_chunks)
-                : launch(k_adam<false, PDT, HPO_ADAM_L2, DEV, SDT, GDT, MST>, n_chunks, kBlock, stream, sv, sc,
+                : launch(k_adam<false, PDT, HPO_ADAM_L2, DEV, SDT, GDT, MST, NT>, n_chunks, kBlock, stream, sv, sc,
                          n_chunks);
+}
+
+template <bool DEV, int SDT, int GDT, int PDT, int MST>
+hipError_t launch_adam_p(const SetView& sv, int64_t n_chunks, int32_t mode, const AdamScalars& sc,
+                         hipStream_t stream)
+{
+    return sv.cached ? launch_adam_n<DEV, SDT, GDT, PDT, MST, false>(sv, n_chunks, mode, sc, stream)
+                     : launch_adam_n<DEV, SDT, GDT, PDT, MST, true>(sv, n_chunks, mode, sc, stream);
 }
 
 template <bool DEV, int SDT, int GDT>

@@ -67,6 +67,13 @@ struct Layout {
     int32_t state_store() const { return state_fp16 ? 2 : (state_bf16 ? 1 : 0); }
     int64_t grad_bytes() const { return grad_bf16 ? 2 : 4; }
     int64_t master_bytes() const { return master_fp16 ? 2 : 4; }
+    /* bytes of the five arrays per element (the param's none for fp32 params) */
+    int64_t elem_bytes() const
+    {
+        return (pdt == HPO_PARAM_FP32 ? 0 : 2) + master_bytes() + grad_bytes() + 2 * mom_bytes();
+    }
+    /* whether a set of numel elements takes the update's cached accesses */
+    int32_t cached(int64_t numel) const { return numel * elem_bytes() <= hpo::kCachedMaxBytes ? 1 : 0; }
 };
 
 hpo_status fail(hpo_status st, const char* fmt, ...);

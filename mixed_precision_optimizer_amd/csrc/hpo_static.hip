@@ -116,6 +116,7 @@ extern "C" hpo_status hpo_step_device_flat_static(int64_t numel, int32_t param_d
     sv.state_store = lay.state_store();
     sv.grad_bf16 = static_cast<int16_t>(lay.grad_bf16);
     sv.master_fp16 = static_cast<int16_t>(lay.master_fp16);
+    sv.cached = lay.cached(numel);
     const hpo::Partials parts = hpo::carve_partials(base, n_parts);
 
     const hpo::AdamScalars sc = device_scalars(cfg, group, 1, max_norm, d_state, t_first, window);
