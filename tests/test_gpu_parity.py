@@ -432,6 +432,61 @@ def test_norm_paths_agree_across_the_two_stage_boundary(H, orc):
         torch.cuda.empty_cache()
 
 
+def test_norm_calls_agree_call_after_call(H):
+    """The single-set norm call and the multi-set call on that set, 300 times
+    each, with the grads rescaled, given an inf or a zero in between on the
+    same stream and no host synchronisation: norm, zero count and flag are
+    bit-identical every time, and the flag is set exactly on the calls that
+    saw an inf (a partial left over from an earlier call would show as a
+    difference).  List and flat sets, fp32 and bf16 grads, and 1 to 8192
+    grad-pass workgroups (the most that one finalize stage folds)."""
+    banner("norm calls, 300 per set")
+    inv = float(np.float32(1 / 512))
+    cases = [("list two 4096x1024", [4096 * 1024, 1024 * 4096], torch.float32),
+             ("flat 8192 workgroups", [8192 * 65536], torch.float32),
+             ("flat one workgroup", [3000], torch.float32),
+             ("list ragged bf16 grads", [1_000_003, 77, 65536 * 5 + 1], torch.bfloat16)]
+    for name, sizes, gdt in cases:
+        gen = torch.Generator(device=DEV).manual_seed(23)
+        grads = [torch.randn(n, device=DEV, generator=gen).mul_(1e-2).to(gdt) for n in sizes]
+        for g in grads:
+            g[::89] = 0
+        masters = [torch.zeros(n, device=DEV) for n in sizes]
+        m1 = [torch.zeros(n, device=DEV) for n in sizes]
+        m2 = [torch.zeros(n, device=DEV) for n in sizes]
+        if len(sizes) == 1 and gdt == torch.float32:
+            hset = H.hpo_set_create_flat(None, masters[0], grads[0], m1[0], m2[0])
+        else:   # the grads' dtype selects bf16 grads
+            hset = H.hpo_set_create_list([None] * len(sizes), masters, grads, m1, m2, [0] * len(sizes),
+                                         param_dtype=H.HPO_PARAM_FP32)
+        parts = hset.info().n_grad_parts
+        calls = 300
+        got = torch.zeros(calls, 4, dtype=torch.int32, device=DEV)
+        ref = torch.zeros(calls, 4, dtype=torch.int32, device=DEV)
+        for k in range(calls):
+            if k % 7 == 3:
+                grads[k % len(grads)][(k * 131) % sizes[k % len(grads)]] = float("inf")
+            elif k % 7 == 4:
+                grads[(k - 1) % len(grads)][((k - 1) * 131) % sizes[(k - 1) % len(grads)]] = 0.0
+            else:
+                for g in grads:
+                    g.mul_(1.0 + (k % 5) / 64.0)
+            for out, call in ((got[k], "one"), (ref[k], "sets")):
+                norm, flag, zeros = out[0:1].view(torch.float32), out[1:2], out[2:4].view(torch.int64)
+                if call == "one":
+                    H.hpo_grad_global_norm(hset, inv, norm, flag, zeros)
+                else:
+                    H.hpo_grad_global_norm_sets([hset], inv, norm, flag, zeros)
+        torch.cuda.synchronize()
+        bad = (got != ref).any(dim=1).nonzero().flatten().tolist()
+        print(f"[norm calls] {name}: {parts} workgroups, {calls} calls, mismatches {len(bad)}", flush=True)
+        assert not bad, (name, bad[:5], got[bad[0]].tolist(), ref[bad[0]].tolist())
+        assert int(got[:, 1].sum().item()) == sum(1 for k in range(calls) if k % 7 == 3)
+        hset.close()
+        del grads, masters, m1, m2
+        torch.cuda.empty_cache()
+
+
 def test_empty_set_and_zero_sizes(H):
     banner("empty set")
     hset = H.hpo_set_create_list([], [], [], [], [], param_dtype=H.HPO_PARAM_BF16)
