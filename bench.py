@@ -427,7 +427,6 @@ def main():
 
     def step(evs=None):
         nonlocal t_applied
-        buf.zero_()
         if evs:
             evs[0].record(stream)
         hpo.hpo_grad_global_norm(hset, inv, norm, found, stream=stream)
@@ -437,6 +436,7 @@ def main():
         if evs:
             evs[2].record(stream)
         host.copy_(buf, non_blocking=True)
+        buf.zero_()   # found_inf starts the next step at 0; enqueued here, it runs while the host waits
         stream.synchronize()
         if int(host[0]) == 0:
             t_applied += 1

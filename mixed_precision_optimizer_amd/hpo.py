@@ -186,10 +186,11 @@ def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
 
 
 def _on_current_device(t: torch.Tensor, what: str) -> None:
-    if not t.is_cuda:
+    d = t.get_device()   # -1 for a host tensor
+    if d < 0:
         raise ValueError(f"{what} must be a device tensor")
     cur = torch.cuda.current_device()
-    if t.device.index != cur:
+    if d != cur:
         raise ValueError(f"{what} is on {t.device} but the current device is cuda:{cur}")
 
 

@@ -35,12 +35,26 @@ class MixedPrecisionAdamW:
         self.log_num_zeros_in_grad = bool(log_num_zeros_in_grad)
         self.t = 0  # applied steps so far
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-        # [0] found_inf (int32), [1] norm (fp32 bits), [2:4] num_zeros (int64)
-        self._buf = torch.zeros(4, dtype=torch.int32, device=dev)
+        # two step buffers, used in turn: [0] found_inf (int32), [1] norm (fp32
+        # bits), [2:4] num_zeros (int64).  A step clears the other one for the
+        # next step while the host waits, and its own keeps its results.
+        self._bufs = torch.zeros(2, 4, dtype=torch.int32, device=dev)
         self._host = torch.zeros(4, dtype=torch.int32, pin_memory=True)
-        self.found_inf = self._buf[0:1]
-        self.norm = self._buf[1:2].view(torch.float32)
-        self.num_zeros = self._buf[2:4].view(torch.int64)
+        self._cur = 0      # buffer of the last step (the attributes below)
+        self._next = 0     # buffer the next step writes
+        self._cleared = False   # the zeros above may still be in flight on the constructing stream
+
+    @property
+    def found_inf(self) -> torch.Tensor:
+        return self._bufs[self._cur, 0:1]
+
+    @property
+    def norm(self) -> torch.Tensor:
+        return self._bufs[self._cur, 1:2].view(torch.float32)
+
+    @property
+    def num_zeros(self) -> torch.Tensor:
+        return self._bufs[self._cur, 2:4].view(torch.int64)
 
     def inv_scale(self) -> float:
         return 1.0 if self.loss_scale is None else float(np.float32(1.0 / self.loss_scale))
@@ -53,19 +67,28 @@ class MixedPrecisionAdamW:
         unscaled in place first, then norm and step take inv_scale = 1)."""
         inv = self.inv_scale()
         s = torch.cuda.current_stream() if stream is None else stream
-        zeros = self.num_zeros if self.log_num_zeros_in_grad else None
+        buf = self._bufs[self._next]
+        found_inf, norm = buf[0:1], buf[1:2].view(torch.float32)
+        zeros = buf[2:4].view(torch.int64) if self.log_num_zeros_in_grad else None
         with torch.cuda.stream(s):
-            self._buf.zero_()
+            if not self._cleared:
+                buf.zero_()
             if inplace_unscale:
-                hpo.hpo_unscale_check_inf(self.set, inv, self.found_inf, s)
+                hpo.hpo_unscale_check_inf(self.set, inv, found_inf, s)
                 inv = 1.0
-                hpo.hpo_grad_global_norm(self.set, inv, self.norm, None, zeros, stream=s)
+                hpo.hpo_grad_global_norm(self.set, inv, norm, None, zeros, stream=s)
             else:
-                hpo.hpo_grad_global_norm(self.set, inv, self.norm, self.found_inf, zeros, stream=s)
+                hpo.hpo_grad_global_norm(self.set, inv, norm, found_inf, zeros, stream=s)
             hpo.hpo_adamw_step(self.set, self.cfg, self.groups, self.n_groups, self.t + 1, inv,
-                               self.max_norm, self.norm, self.found_inf, s)
-            self._host.copy_(self._buf, non_blocking=True)
+                               self.max_norm, norm, found_inf, s)
+            self._host.copy_(buf, non_blocking=True)
+            # the next step's buffer starts at 0; enqueued here, the clear runs
+            # while the host waits, and the synchronisation below completes it
+            # for every stream
+            self._bufs[self._next ^ 1].zero_()
         s.synchronize()
+        self._cleared = True
+        self._cur, self._next = self._next, self._next ^ 1
         found = int(self._host[0]) != 0
         if found:
             return False, None, None
