@@ -487,6 +487,47 @@ def test_norm_calls_agree_call_after_call(H):
         torch.cuda.empty_cache()
 
 
+def test_cached_and_streaming_updates_agree(H):
+    """A set whose arrays take at most 192 MiB takes cached loads and stores in
+    the update; a larger one takes streaming ones.  The same 12M elements
+    stepped as one flat set (216 MB: streaming) and as two flat sets of half
+    the size over the same storage (108 MB each: cached) end bit-identical
+    over three steps (no clip, so that the two norm folds do not enter)."""
+    banner("cached vs streaming update accesses")
+    n = 12 * 1024 * 1024
+    gen = torch.Generator(device=DEV).manual_seed(31)
+    th0 = torch.randn(n, device=DEV, generator=gen)
+    grads = [torch.randn(n, device=DEV, generator=gen).mul_(1e-3) for _ in range(3)]
+    cfg = H.make_cfg()
+    groups, ng = H.make_groups([(1e-3, 0.1)])
+    out = {}
+    for kind in ("one", "halves"):
+        th = th0.clone()
+        p = th.to(torch.bfloat16)
+        g = torch.zeros(n, device=DEV)
+        m = torch.zeros(n, device=DEV)
+        v = torch.zeros(n, device=DEV)
+        if kind == "one":
+            sets = [H.hpo_set_create_flat(p, th, g, m, v)]
+        else:
+            h = n // 2
+            sets = [H.hpo_set_create_flat(p[a:a + h], th[a:a + h], g[a:a + h], m[a:a + h], v[a:a + h])
+                    for a in (0, h)]
+        for k in range(3):
+            g.copy_(grads[k])
+            for hs in sets:
+                H.hpo_adamw_step(hs, cfg, groups, ng, k + 1, 1.0, 0.0, None, None)
+        torch.cuda.synchronize()
+        out[kind] = (th.clone(), m.clone(), v.clone(), p.clone())
+        for hs in sets:
+            hs.close()
+    a, b = out["one"], out["halves"]
+    assert not torch.equal(a[0], th0)   # the steps moved the master
+    for x, y, name in zip(a, b, ("master", "exp_avg", "exp_avg_sq", "param")):
+        assert torch.equal(x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32),
+                           y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32)), name
+
+
 def test_empty_set_and_zero_sizes(H):
     banner("empty set")
     hset = H.hpo_set_create_list([], [], [], [], [], param_dtype=H.HPO_PARAM_BF16)
