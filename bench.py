@@ -184,6 +184,12 @@ def host_cpu() -> dict:
             fields[k.strip()] = v.strip()
     if "Model name" in fields:
         out["model_name"] = fields["Model name"]
+    # a virtual machine may show a generic model name: the family / model /
+    # stepping numbers and the hypervisor still identify the part
+    for key, name in (("CPU family", "cpu_family"), ("Model", "model"), ("Stepping", "stepping"),
+                      ("Hypervisor vendor", "hypervisor"), ("L3 cache", "l3_cache")):
+        if key in fields:
+            out[name] = fields[key]
     try:
         sockets = int(fields["Socket(s)"])
         cores = int(fields["Core(s) per socket"])
