@@ -253,6 +253,22 @@ def test_zero_shard_70b_over_8(H, orc):
 
 
 @pytest.mark.timeout(900)
+def test_zero_shard_70b_over_8_device_resident(H, orc):
+    """The same 8.75e9-element shard through the device-resident step, the
+    configuration of the bench's device-resident leg: the two-stage finalize
+    (133,515 partials) writes the norm, the zero count and the apply decision
+    into the device state, and the update (streaming accesses) takes t and
+    the unscale factor from it; the sampled elements match the oracle bit for
+    bit and every param equals bf16(master)."""
+    from mixed_precision_optimizer_amd import inputs
+    w = inputs.zero_shard()
+    stats = _run_fullsize(H, orc, w, dict(head=4096, windows_big=0, window=1 << 20, windows_total=256),
+                          device_step=True)
+    assert stats["bit_equal"] == stats["compared"]
+    assert len(stats["zeros"]) == 3 and min(stats["zeros"]) > 0
+
+
+@pytest.mark.timeout(900)
 def test_llama8b_shaped_list(H, orc):
     """291 tensors (65 1-D in the no-decay group), per-tensor grad scales
     log-uniform in [1e-5, 1e-2], clip 1.0, 5 steps."""
