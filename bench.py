@@ -389,7 +389,8 @@ def cpu_baseline_threads(sample, w, steps, threads):
             "ms_per_step": round(dt * 1e3, 2), "ms_min": round(min(times) * 1e3, 2),
             "ms_max": round(max(times) * 1e3, 2), "cpu_model": host_cpu_model(),
             "host": {k: hc[k] for k in ("physical_cores", "sockets", "threads_per_core", "logical_cpus",
-                                        "cpus_allowed") if k in hc}}
+                                        "cpus_allowed", "cpu_family", "model", "stepping", "hypervisor",
+                                        "l3_cache") if k in hc}}
 
 
 def main():
