@@ -394,6 +394,23 @@ def test_step_returns_zero_count_and_none_on_skip(orc):
     assert not r.applied and r.num_zeros is None and r.norm32 is None
 
 
+def test_zero_count_is_taken_before_the_clip(orc):
+    """R40: the count is of the unscaled grads whose norm is taken, before the
+    clip.  One grad of 1e15 makes the clip coefficient about 1e-15, which
+    would round the ten stored subnormals (2^-130) to zero if they were
+    counted after it; only the three true zeros count."""
+    th = np.linspace(-1, 1, 14).astype(np.float32)
+    G = np.full(14, _bits(0x00010000), dtype=np.float32)   # 2^-133 each
+    G[0] = np.float32(1e15)
+    G[[5, 9, 13]] = [0.0, -0.0, 0.0]
+    assert orc.count_zeros(G, 1.0) == 3
+    _, C, _ = orc.clip_coeff(1.0, np.float32(1e15))
+    assert np.count_nonzero(G[1:] * np.float32(C)) == 0   # after the clip they would all be zero
+    O = orc.OracleOptimizer([orc.OTensor.fresh(th)], orc.Hyper(), [(1e-3, 0.1)], max_norm=1.0)
+    r = O.step([G])
+    assert r.applied and r.clip_applied and r.num_zeros == 3
+
+
 def test_unscale_power_of_two_is_exact(orc):
     """Multiplying by 2^-16 is exact for normal fp32 values, so the in-place
     unscale recovers the unscaled grads bit for bit."""
