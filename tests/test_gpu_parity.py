@@ -528,6 +528,37 @@ def test_cached_and_streaming_updates_agree(H):
                            y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32)), name
 
 
+def test_zero_count_is_taken_before_the_clip(H, orc):
+    """R40 on the GPU: one grad of 1e15 sets the clip coefficient near 1e-15,
+    which would round the stored subnormals to zero; the host-driven and the
+    device-resident steps both count only the true zeros, as the oracle."""
+    banner("zero count before the clip")
+    n = 5000
+    g = torch.full((n,), 2.0 ** -133, device=DEV)
+    g[0] = 1e15
+    g[1234::1000] = 0.0
+    want = int((g == 0).sum().item())
+    assert want == 4 and orc.count_zeros(to_np(g), 1.0) == want
+    for kind in ("host", "device"):
+        th = torch.linspace(-1, 1, n, device=DEV)
+        p = th.to(torch.bfloat16)
+        m, v = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+        hset = H.hpo_set_create_flat(p, th, g.clone(), m, v)
+        if kind == "host":
+            from mixed_precision_optimizer_amd import MixedPrecisionAdamW
+            opt = MixedPrecisionAdamW(hset, [(1e-3, 0.1)], max_norm=1.0, log_num_zeros_in_grad=True)
+            applied, norm, zeros = opt.step()
+            assert applied and zeros == want, (applied, zeros)
+        else:
+            d_state = H.new_scaler_state()
+            H.hpo_scaler_state_init(d_state, 1.0, 1)
+            H.hpo_step_device(hset, H.make_cfg(), [(1e-3, 0.1)], None, 1.0, H.make_scaler_cfg(dynamic=False),
+                              d_state, 1, 1)
+            st = H.read_scaler_state(d_state)
+            assert st.applied == 1 and st.num_zeros == want, (st.applied, st.num_zeros)
+        hset.close()
+
+
 def test_empty_set_and_zero_sizes(H):
     banner("empty set")
     hset = H.hpo_set_create_list([], [], [], [], [], param_dtype=H.HPO_PARAM_BF16)
